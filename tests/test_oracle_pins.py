@@ -1,0 +1,452 @@
+"""Pins of the CPU oracle to closed forms, hand-worked examples and invariants.
+
+Every function of the oracle is checked here against something other than
+itself, so that a dropped term, a wrong sign or index, or a transposed operand
+fails at least one test.  Hand-worked values live in tests/golden/ with their
+derivation.  No GPU is needed.
+"""
+import dataclasses
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import (OracleModel, rmsnorm, rope_rotate, causal_gqa_attention, silu, swiglu_mlp,
+                    argmax_lowest, quantize_int4_g128, dequantize_int4_g128, splitmix64_output,
+                    uniform_for_step, sample_top_k_top_p)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def tiny_shape(**kw):
+    base = dict(name="pin", n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16,
+                intermediate=96, vocab=80, max_pos=32)
+    base.update(kw)
+    return synth.ModelShape(**base)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_worked_example():
+    g = golden("rmsnorm_worked.json")
+    x = np.array(g["x"], dtype=np.float64)
+    np.testing.assert_allclose(rmsnorm(x, np.ones(2), 0.0), g["want_unit_gain"], rtol=1e-14)
+    np.testing.assert_allclose(rmsnorm(x, np.array(g["gain"]), 0.0), g["want_gain"], rtol=1e-14)
+
+
+def test_rmsnorm_output_rms_closed_form():
+    rng = np.random.default_rng(5)
+    for m in (4, 128, 1024):
+        x = rng.standard_normal((3, m)) * rng.uniform(0.01, 10, (3, 1))
+        eps = 1e-6
+        y = rmsnorm(x, np.ones(m), eps)
+        ms = np.mean(x * x, axis=1)
+        want = np.sqrt(ms / (ms + eps))
+        np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), want, rtol=1e-13)
+
+
+def test_rmsnorm_is_per_row_and_per_head():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((2, 3, 8))
+    x[:, 1] *= 100.0
+    y = rmsnorm(x, np.ones(8), 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), np.ones((2, 3)), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_worked_examples():
+    g = golden("rope_worked.json")
+    for c in g["cases"]:
+        x = np.array(c["x"], dtype=np.float64).reshape(1, 1, g["d"])
+        y = rope_rotate(x, np.array([c["pos"]]), g["theta"])
+        np.testing.assert_allclose(y.reshape(-1), c["want"], rtol=0, atol=1e-15)
+
+
+def test_rope_position_zero_is_identity_bit_exact():
+    x = np.random.default_rng(1).standard_normal((1, 3, 128))
+    assert np.array_equal(rope_rotate(x, np.array([0]), 1e6), x)
+
+
+def test_rope_preserves_pair_norms():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 2, 128))
+    pos = np.array([1, 7, 100, 2047, 16383])
+    y = rope_rotate(x, pos, 1e6)
+    nx = x[..., :64] ** 2 + x[..., 64:] ** 2
+    ny = y[..., :64] ** 2 + y[..., 64:] ** 2
+    np.testing.assert_allclose(ny, nx, rtol=1e-12)
+
+
+def test_rope_relative_position_invariance():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 1, 128))
+    k = rng.standard_normal((1, 1, 128))
+    for m, n, shift in ((5, 2, 11), (100, 0, 900), (3000, 2999, 13000)):
+        a = np.sum(rope_rotate(q, np.array([m]), 1e6) * rope_rotate(k, np.array([n]), 1e6))
+        b = np.sum(rope_rotate(q, np.array([m + shift]), 1e6) * rope_rotate(k, np.array([n + shift]), 1e6))
+        assert abs(a - b) <= 1e-9 * (1 + abs(a))
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_two_position_worked_example():
+    g = golden("attention_two_position.json")
+    d = g["d"]
+    q = np.array([g["q"], g["q"]], dtype=np.float64).reshape(2, 1, d)
+    k = np.array(g["k"], dtype=np.float64).reshape(2, 1, d)
+    v = np.array(g["v"], dtype=np.float64).reshape(2, 1, d)
+    o = causal_gqa_attention(q, k, v, np.array([0, 1]))
+    np.testing.assert_allclose(o[0, 0], g["want_pos0"], rtol=1e-14)
+    np.testing.assert_allclose(o[1, 0], g["want_pos1"], rtol=1e-14)
+
+
+def test_attention_single_position_returns_v_exactly():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 4, 16))
+    k = rng.standard_normal((1, 2, 16))
+    v = rng.standard_normal((1, 2, 16))
+    o = causal_gqa_attention(q, k, v, np.array([0]))
+    assert np.array_equal(o[0, 0], v[0, 0]) and np.array_equal(o[0, 3], v[0, 1])
+
+
+def test_attention_gqa_head_mapping_consecutive():
+    # kv head 0 carries value 1, kv head 1 carries value 2; q heads 0,1 -> kv 0; 2,3 -> kv 1
+    rng = np.random.default_rng(7)
+    T, d = 5, 8
+    q = rng.standard_normal((T, 4, d))
+    k = rng.standard_normal((T, 2, d))
+    v = np.zeros((T, 2, d))
+    v[:, 0] = 1.0
+    v[:, 1] = 2.0
+    o = causal_gqa_attention(q, k, v, np.arange(T))
+    np.testing.assert_allclose(o[:, :2], 1.0, rtol=1e-14)
+    np.testing.assert_allclose(o[:, 2:], 2.0, rtol=1e-14)
+
+
+def test_attention_equal_scores_average_visible_values():
+    T, d = 6, 8
+    q = np.zeros((T, 2, d))
+    k = np.random.default_rng(8).standard_normal((T, 1, d))
+    v = np.arange(T, dtype=np.float64)[:, None, None] * np.ones((T, 1, d))
+    o = causal_gqa_attention(q, k, v, np.arange(T))
+    for p in range(T):
+        np.testing.assert_allclose(o[p, :, 0], np.mean(np.arange(p + 1)), rtol=1e-14)
+
+
+def test_attention_is_causal():
+    rng = np.random.default_rng(9)
+    T, d = 7, 16
+    q = rng.standard_normal((T, 4, d))
+    k = rng.standard_normal((T, 2, d))
+    v = rng.standard_normal((T, 2, d))
+    o1 = causal_gqa_attention(q, k, v, np.arange(T))
+    k2, v2 = k.copy(), v.copy()
+    k2[4:] += 3.0
+    v2[4:] -= 5.0
+    o2 = causal_gqa_attention(q, k2, v2, np.arange(T))
+    assert np.array_equal(o1[:4], o2[:4])
+    assert not np.allclose(o1[4:], o2[4:])
+
+
+def test_attention_softmax_shift_invariance_and_brute_force():
+    # brute force with an explicit TxT masked score matrix in pure Python, tiny sizes
+    rng = np.random.default_rng(10)
+    T, nq, nkv, d = 4, 2, 1, 3
+    q = rng.standard_normal((T, nq, d))
+    k = rng.standard_normal((T, nkv, d))
+    v = rng.standard_normal((T, nkv, d))
+    o = causal_gqa_attention(q, k, v, np.arange(T))
+    for h in range(nq):
+        for i in range(T):
+            scores = [sum(q[i, h, c] * k[j, 0, c] for c in range(d)) / math.sqrt(d) if j <= i else -math.inf
+                      for j in range(T)]
+            w = [math.exp(s) for s in scores]
+            tot = sum(w)
+            want = [sum(w[j] * v[j, 0, c] for j in range(T)) / tot for c in range(d)]
+            np.testing.assert_allclose(o[i, h], want, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- SiLU / MLP
+
+def test_silu_and_mlp_worked_examples():
+    g = golden("silu_worked.json")
+    for z, want in g["silu"]:
+        assert silu(np.array(float(z))) == pytest.approx(want, rel=1e-15, abs=0)
+    got = swiglu_mlp(np.array([[1.0]]), np.array([[1.0]]), np.array([[2.0]]), np.array([[1.0]]))
+    assert got[0, 0] == pytest.approx(g["mlp_gate1_up2_down1_h1"], rel=1e-15)
+    assert got[0, 0] != pytest.approx(g["mlp_swapped"], rel=1e-6)
+
+
+def test_silu_limits():
+    assert silu(np.array(60.0)) == pytest.approx(60.0, rel=1e-15)
+    assert abs(silu(np.array(-800.0))) < 1e-300
+
+
+# ---------------------------------------------------------------- whole model
+
+def _model(shape, weights, **kw):
+    return OracleModel(shape, weights, **kw)
+
+
+def test_zero_layer_model_is_tied_head_of_normalised_embedding():
+    # Hadamard rows: orthogonal, all of norm 2 -> logits[t] = 4/sqrt(1+eps), others 0
+    shape = tiny_shape(n_layers=0, hidden=4, vocab=4, n_q_heads=1, n_kv_heads=1, head_dim=4, intermediate=4)
+    had = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], dtype=np.float32)
+    w = {"embed": synth.bf16_round(had), "final_norm": synth.bf16_round(np.ones(4, np.float32)), "layers": []}
+    m = _model(shape, w)
+    logits = m.forward([2])
+    want = np.zeros(4)
+    want[2] = 4.0 / math.sqrt(1.0 + shape.rms_eps)
+    np.testing.assert_allclose(logits[0], want, rtol=1e-15, atol=1e-15)
+    assert argmax_lowest(logits[0]) == 2
+
+
+def test_zero_layer_model_applies_final_norm_gains():
+    shape = tiny_shape(n_layers=0, hidden=4, vocab=4, n_q_heads=1, n_kv_heads=1, head_dim=4, intermediate=4)
+    had = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], dtype=np.float32)
+    gains = np.array([0.5, 2.0, 1.5, 3.0], dtype=np.float32)
+    w = {"embed": synth.bf16_round(had), "final_norm": synth.bf16_round(gains), "layers": []}
+    logits = _model(shape, w).forward([1])[0]
+    want = np.array([sum(float(had[v, j]) * float(gains[j]) * float(had[1, j]) for j in range(4))
+                     for v in range(4)]) / math.sqrt(1.0 + shape.rms_eps)
+    np.testing.assert_allclose(logits, want, rtol=1e-15, atol=1e-15)
+
+
+def test_mlp_wiring_single_position():
+    # With o_proj zero, a layer is x + down(SiLU(gate h2) * up h2), h2 = RMSNorm(x; mlp gains).
+    shape = tiny_shape(n_layers=1)
+    w = synth.make_weights(shape, seed=29, random_gains=True)
+    w["layers"][0]["wo"] = np.zeros_like(w["layers"][0]["wo"])
+    cap = {}
+    _model(shape, w).forward([3], capture=cap)
+    f = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    lw = w["layers"][0]
+    x = f(w["embed"])[3]
+    h2 = x / np.sqrt(np.mean(x * x) + shape.rms_eps) * f(lw["mlp_norm"])
+    g = f(lw["w_gate"]) @ h2
+    u = f(lw["w_up"]) @ h2
+    want = x + f(lw["w_down"]) @ (g / (1.0 + np.exp(-g)) * u)
+    np.testing.assert_allclose(cap["layer_out"][0][0], want, rtol=1e-12, atol=1e-14)
+
+
+def test_zero_projection_layers_are_identity_on_the_bus():
+    shape = tiny_shape()
+    w = synth.make_weights(shape, seed=11)
+    base = _model(dataclasses.replace(shape, n_layers=0), {"embed": w["embed"], "final_norm": w["final_norm"],
+                                                             "layers": []})
+    for lw in w["layers"]:
+        for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+            lw[name] = np.zeros_like(lw[name])
+    full = _model(shape, w)
+    toks = synth.make_prompt(shape.vocab, 6, seed=12)
+    np.testing.assert_allclose(full.forward(toks), base.forward(toks), rtol=1e-14, atol=1e-14)
+
+
+def test_single_position_layer_closed_form():
+    # At position 0 attention returns v exactly, so one layer with zero MLP is
+    # x + Wo (Wv rmsnorm(x) + bv): pins V (not K or Q), bias, o_proj orientation, residual base.
+    shape = tiny_shape(n_layers=1, qkv_bias=True, qk_norm=False)
+    w = synth.make_weights(shape, seed=13, random_gains=True)
+    for name in ("w_gate", "w_up", "w_down"):
+        w["layers"][0][name] = np.zeros_like(w["layers"][0][name])
+    m = _model(shape, w)
+    cap = {}
+    m.forward([7], capture=cap)
+    f = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    lw = w["layers"][0]
+    x = f(w["embed"])[7]
+    h = x / np.sqrt(np.mean(x * x) + shape.rms_eps) * f(lw["attn_norm"])
+    v = f(lw["wv"]) @ h + f(lw["bv"])
+    vrep = np.repeat(v.reshape(shape.n_kv_heads, shape.head_dim), shape.n_q_heads // shape.n_kv_heads, axis=0)
+    want = x + f(lw["wo"]) @ vrep.reshape(-1)
+    np.testing.assert_allclose(cap["layer_out"][0][0], want, rtol=1e-12, atol=1e-14)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    shape = tiny_shape(n_q_heads=4, n_kv_heads=2)
+    w = synth.make_weights(shape, seed=14, random_gains=True)
+    mha_shape = dataclasses.replace(shape, n_kv_heads=4)
+    w2 = {"embed": w["embed"], "final_norm": w["final_norm"], "layers": []}
+    d = shape.head_dim
+    for lw in w["layers"]:
+        l2 = dict(lw)
+        for name in ("wk", "wv"):
+            heads = lw[name].reshape(2, d, shape.hidden)
+            l2[name] = np.repeat(heads, 2, axis=0).reshape(4 * d, shape.hidden)
+        w2["layers"].append(l2)
+    toks = synth.make_prompt(shape.vocab, 9, seed=15)
+    np.testing.assert_allclose(_model(shape, w).forward(toks), _model(mha_shape, w2).forward(toks),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_qk_norm_makes_logits_invariant_to_scaling_q_and_k_weights():
+    shape = tiny_shape()
+    w = synth.make_weights(shape, seed=16)
+    toks = synth.make_prompt(shape.vocab, 8, seed=17)
+    ref = _model(shape, w).forward(toks)
+    for lw in w["layers"]:
+        for name in ("wq", "wk"):
+            lw[name] = synth.bf16_round(synth.bf16_to_f32(lw[name]) * np.float32(4.0))  # exact power-of-two scale
+    got = _model(shape, w).forward(toks)
+    np.testing.assert_allclose(got, ref, rtol=1e-4, atol=1e-5)
+    no_norm = dataclasses.replace(shape, qk_norm=False)
+    w2 = synth.make_weights(no_norm, seed=16)
+    a = _model(no_norm, w2).forward(toks)
+    for lw in w2["layers"]:
+        for name in ("wq", "wk"):
+            lw[name] = synth.bf16_round(synth.bf16_to_f32(lw[name]) * np.float32(4.0))
+    b = _model(no_norm, w2).forward(toks)
+    assert np.max(np.abs(a - b)) > 1e-4
+
+
+def test_incremental_equals_cacheless_prefill():
+    shape = tiny_shape(qkv_bias=True)
+    w = synth.make_weights(shape, seed=18, random_gains=True)
+    m = _model(shape, w)
+    toks = synth.make_prompt(shape.vocab, 12, seed=19)
+    full = m.forward(toks)
+    cache = m.new_cache()
+    rows = [m.forward(toks[:5], cache)]
+    for t in toks[5:]:
+        rows.append(m.forward([t], cache))
+    inc = np.concatenate(rows, axis=0)
+    np.testing.assert_allclose(inc, full, rtol=1e-12, atol=1e-13)
+
+
+def test_model_is_causal():
+    shape = tiny_shape()
+    m = _model(shape, synth.make_weights(shape, seed=20))
+    toks = synth.make_prompt(shape.vocab, 10, seed=21)
+    a = m.forward(toks)
+    toks2 = toks.copy()
+    toks2[6:] = (toks2[6:] + 1) % shape.vocab
+    b = m.forward(toks2)
+    np.testing.assert_allclose(a[:6], b[:6], rtol=1e-13, atol=1e-14)
+    assert not np.allclose(a[6:], b[6:])
+
+
+def test_lora_equals_merged_weights_and_zero_b_is_base():
+    shape = tiny_shape(qk_norm=False, qkv_bias=True)
+    w = synth.make_weights(shape, seed=22)
+    lora = synth.make_lora(shape, rank=4, seed=23)
+    toks = synth.make_prompt(shape.vocab, 7, seed=24)
+    alpha = 8.0
+    with_lora = _model(shape, w, lora=lora, lora_alpha=alpha).forward(toks)
+    # merged: W' = W + (alpha/r) B A, computed in float64 by patching the oracle's widened weights
+    merged = _model(shape, w)
+    for li, lw in enumerate(lora):
+        f = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa
+        merged.layers[li]["wq"] = merged.layers[li]["wq"] + (alpha / 4) * f(lw["b_q"]) @ f(lw["a_q"])
+        merged.layers[li]["wv"] = merged.layers[li]["wv"] + (alpha / 4) * f(lw["b_v"]) @ f(lw["a_v"])
+    np.testing.assert_allclose(with_lora, merged.forward(toks), rtol=1e-11, atol=1e-12)
+    zero_b = [dict(lw, b_q=np.zeros_like(lw["b_q"]), b_v=np.zeros_like(lw["b_v"])) for lw in lora]
+    base = _model(shape, w).forward(toks)
+    assert np.array_equal(_model(shape, w, lora=zero_b, lora_alpha=alpha).forward(toks), base)
+    assert not np.allclose(with_lora, base)
+
+
+def test_int4_model_uses_dequantised_projections():
+    shape = tiny_shape(qk_norm=False, qkv_bias=True, hidden=128, intermediate=256, head_dim=32,
+                       weight_format=synth.W_INT4_G128)
+    w = synth.make_weights(shape, seed=25)
+    m = _model(shape, w)
+    f32 = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)  # noqa: E731
+    codes, scales = quantize_int4_g128(f32(w["layers"][1]["w_down"]))
+    np.testing.assert_array_equal(m.layers[1]["w_down"], codes.astype(np.float64) *
+                                  np.repeat(scales.astype(np.float64), 128, axis=1))
+    # biases, norms and the embedding stay bf16
+    np.testing.assert_array_equal(m.layers[0]["bq"], f32(w["layers"][0]["bq"]).astype(np.float64))
+
+
+# ---------------------------------------------------------------- greedy / sampling
+
+def test_argmax_ties_go_to_lowest_index():
+    assert argmax_lowest(np.array([1.0, 3.0, 2.0, 3.0])) == 1
+    assert argmax_lowest(np.array([-1.0, -1.0])) == 0
+
+
+def test_splitmix64_published_vectors():
+    g = golden("splitmix64_vectors.json")
+    got = [splitmix64_output(g["seed"], i + 1) for i in range(len(g["outputs_hex"]))]
+    assert got == [int(h, 16) for h in g["outputs_hex"]]
+    u = [uniform_for_step(2, s) for s in range(1000)]
+    assert min(u) >= 0.0 and max(u) < 1.0 and abs(np.mean(u) - 0.5) < 0.03
+
+
+def test_sampling_worked_examples():
+    g = golden("sampling_worked.json")
+    logits = np.array(g["logits"])
+    for c in g["cases"]:
+        assert sample_top_k_top_p(logits, c["T"], c["top_k"], c["top_p"], c["u"]) == c["want"], c
+
+
+def test_sampling_reduces_to_greedy():
+    rng = np.random.default_rng(26)
+    logits = rng.standard_normal(1000)
+    best = argmax_lowest(logits)
+    for u in (0.0, 0.3, 0.999):
+        assert sample_top_k_top_p(logits, 0.7, 1, 0.9, u) == best
+        assert sample_top_k_top_p(logits, 1e-6, 40, 0.9, u) == best
+        assert sample_top_k_top_p(logits, 0.7, 40, 1e-9, u) == best
+
+
+def test_sampling_distribution_matches_truncated_softmax():
+    rng = np.random.default_rng(27)
+    logits = rng.standard_normal(200) * 2.0
+    T, k, p = 0.7, 40, 0.9
+    n = 200000
+    counts = {}
+    for i in range(n):
+        t = sample_top_k_top_p(logits, T, k, p, (i + 0.5) / n)
+        counts[t] = counts.get(t, 0) + 1
+    order = sorted(range(200), key=lambda i: (-logits[i], i))[:k]
+    w = np.array([math.exp((logits[i] - logits[order[0]]) / T) for i in order])
+    pi = w / w.sum()
+    kept, before = [], 0.0
+    for i, pr in zip(order, pi):
+        if before < p or not kept:
+            kept.append((i, pr))
+        before += pr
+    z = sum(pr for _, pr in kept)
+    assert set(counts) == {i for i, _ in kept}
+    for i, pr in kept:
+        assert abs(counts[i] / n - pr / z) < 2.0 / n + 1e-12
+
+
+# ---------------------------------------------------------------- int4 group-128
+
+def test_int4_worked_example():
+    g = golden("int4_worked.json")
+    w = np.zeros((2, 128), dtype=np.float32)
+    w[0, :len(g["values"])] = np.array(g["values"], dtype=np.float32)
+    codes, scales = quantize_int4_g128(w)
+    assert float(scales[0, 0]) == g["scale"]
+    assert list(codes[0, :len(g["codes"])]) == g["codes"]
+    assert np.all(codes[0, len(g["codes"]):] == 0)
+    assert float(scales[1, 0]) == 0.0 and np.all(codes[1] == 0)
+
+
+def test_int4_properties():
+    rng = np.random.default_rng(28)
+    w = synth.bf16_to_f32(synth.bf16_round(rng.standard_normal((64, 512)).astype(np.float32) * 0.02))
+    codes, scales = quantize_int4_g128(w)
+    assert codes.min() >= -7 and codes.max() <= 7
+    s = np.repeat(scales.astype(np.float32), 128, axis=1)
+    what = dequantize_int4_g128(codes, scales)
+    # error within half a step (plus the float32 rounding of the division)
+    assert np.all(np.abs(w - what) <= s * (0.5 + 1e-3))
+    # the largest magnitude in each group maps to +-7
+    g = np.abs(codes.reshape(64, 4, 128)).max(axis=2)
+    assert np.all(g == 7)
+    # idempotent: quantising the dequantised weights returns the same codes and scales
+    c2, s2 = quantize_int4_g128(what.astype(np.float32))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
