@@ -1,0 +1,158 @@
+"""Benchmark: single-sequence decode (and prefill) of a Qwen3-style decoder on one MI355X.
+
+One timed step = one whole generation job of the workload: reset the KV cache,
+batched prefill of the prompt, then the workload's greedy decode steps, all
+through the C ABI on one HIP stream, with weights and inputs resident in HBM.
+
+Prints ONE JSON line.  `value` = generated tokens per second over the whole
+job (prefill token + decode tokens); decode-only and prefill rates, the
+effective HBM bandwidth and the dominant kernel's roofline fraction are
+reported beside it.  The CPU oracle is timed on a bounded sample of the same
+workload on the host cores (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3-0.6b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-steps", type=int, default=8)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, weights, prompt, n_steps):
+    """Time the oracle (as it stands) on the host: prompt + n_steps incremental greedy steps."""
+    import numpy as np
+    from oracle import OracleModel, argmax_lowest
+    t_build = time.perf_counter()
+    m = OracleModel(wl.shape, weights)
+    t_build = time.perf_counter() - t_build
+    cache = m.new_cache(len(prompt) + n_steps + 1)
+    t0 = time.perf_counter()
+    logits = m.forward(prompt, cache, logits_rows="last")[-1]
+    toks = 1
+    for _ in range(n_steps):
+        logits = m.forward([argmax_lowest(logits)], cache, logits_rows="last")[-1]
+        toks += 1
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": toks / dt, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{wl.name}: float64 numpy oracle, prefill {len(prompt)} tokens + {n_steps} greedy decode "
+                      f"steps with its own KV cache ({toks} tokens in {dt:.1f} s; weight widening {t_build:.1f} s "
+                      f"not counted); BLAS threads = all {cores} host cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synth
+    import decoder_only_token_amd as qd
+
+    wl = synth.WORKLOADS[args.workload]
+    shape = wl.shape
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    weights = synth.make_weights(shape)
+    prompt = synth.make_prompt(shape.vocab, wl.prompt_len)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
+    dw = {"embed": to_dev(weights["embed"]), "final_norm": to_dev(weights["final_norm"]),
+          "layers": [{k: to_dev(v) for k, v in lw.items()} for lw in weights["layers"]]}
+    torch.cuda.synchronize()
+    dec = qd.Decoder(qd.make_config(shape, max_prefill=wl.max_prefill), stream.cuda_stream)
+    dec.load_weights(dw)
+    del dw
+    torch.cuda.synchronize()
+    n_dec = wl.decode_steps
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def job(marks=None):
+        dec.reset_kv()
+        if marks:
+            marks[0].record(stream)
+        dec.prefill(prompt)
+        if marks:
+            marks[1].record(stream)
+        for _ in range(n_dec):
+            dec.decode_step()
+        if marks:
+            marks[2].record(stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            job()
+        torch.cuda.synchronize()
+        marks = [[ev(), ev(), ev()] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            job(marks[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    prefill_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
+    decode_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_job = 1 + n_dec
+    value = tokens_per_job * args.steps / wall
+
+    wb = synth.weight_bytes(shape)
+    kvp = synth.kv_bytes_per_position(shape)
+    # algorithmic HBM bytes of one decode step at context c: all weights once
+    # (layers + tied head + one gathered row), KV read for c positions, KV write of one position
+    ctx0 = wl.prompt_len
+    dec_bytes = sum((wb["layers"] + wb["lm_head"] + wb["embed_row"]) + kvp * (ctx0 + i + 1)
+                    for i in range(n_dec))
+    decode_step_us = decode_ms * 1e3 / n_dec
+    achieved = dec_bytes / n_dec / (decode_step_us * 1e-6) / 1e9
+    out = {
+        "metric": "decode tok/s + achieved HBM GB/s (% of peak); prefill tok/s, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights, f32 activations/accumulation/KV",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform random prompt ids)",
+        "config": {"workload": wl.name, "model": shape.name, "layers": shape.n_layers, "hidden": shape.hidden,
+                   "heads": [shape.n_q_heads, shape.n_kv_heads], "vocab": shape.vocab,
+                   "prompt_len": wl.prompt_len, "decode_steps": n_dec, "global_batch": 1,
+                   "parallelism": "single GPU"},
+        "decode_tok_s": round(n_dec / (decode_ms * 1e-3), 2),
+        "decode_step_us": round(decode_step_us, 2),
+        "prefill_tok_s": round(wl.prompt_len / (prefill_ms * 1e-3), 2),
+        "prefill_ms": round(prefill_ms, 3),
+        "decode_hbm_gbs_effective": round(achieved, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode step (captured graph), algorithmic bytes = weights + KV read + KV write"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, weights, prompt, args.cpu_sample_steps)
+    dec.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

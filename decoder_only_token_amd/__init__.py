@@ -1,0 +1,240 @@
+"""Python binding of libqd, the MI355X (gfx950) single-sequence decoder-step library.
+
+This module only marshals arguments (ctypes mirrors of the structs in
+include/qd.h, device pointers taken from torch tensors, the current HIP
+stream).  Every step of the forward pass runs in the HIP kernels of
+libqd.so; there is no Python or CPU fallback, and importing the binding
+without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqd.so")
+
+QD_ABI_VERSION = 1
+QD_W_BF16, QD_W_INT4_G128 = 0, 1
+QD_CAP_EMBED, QD_CAP_LAYER_OUT, QD_CAP_FINAL_NORM, QD_CAP_LOGITS = 0, 1, 2, 3
+STATUS = {0: "QD_OK", -1: "QD_E_ARG", -2: "QD_E_ABI", -3: "QD_E_STATE", -4: "QD_E_RANGE", -5: "QD_E_OOM",
+          -6: "QD_E_HIP"}
+
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class QdConfig(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("abi_version", ctypes.c_uint32),
+                ("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("qk_norm", ctypes.c_uint8), ("qkv_bias", ctypes.c_uint8), ("tie_embeddings", ctypes.c_uint8),
+                ("weight_format", ctypes.c_uint8), ("max_pos", ctypes.c_int32), ("max_prefill", ctypes.c_int32),
+                ("lora_rank_max", ctypes.c_int32)]
+
+
+class QdWeights(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("embed", _P), ("final_norm", _P), ("lm_head", _P)] + \
+               [(n, _PP) for n in ("attn_norm", "mlp_norm", "q_norm", "k_norm", "wq", "wk", "wv", "wo", "bq", "bk",
+                                   "bv", "w_gate", "w_up", "w_down")]
+
+
+class QdSampling(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("top_p", ctypes.c_float), ("seed", ctypes.c_uint64)]
+
+
+class QdLora(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("rank", ctypes.c_int32), ("alpha", ctypes.c_float),
+                ("a_q", _PP), ("b_q", _PP), ("a_v", _PP), ("b_v", _PP)]
+
+
+EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_decode_step", "qd_set_lora",
+           "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_sync_token", "qd_get_position",
+           "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
+           "qd_sizeof_lora"]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libqd.so (built by decoder_only_token_amd.build) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libqd.so not built: {path} is missing (run decoder_only_token_amd/build.py)")
+    L = ctypes.CDLL(path)
+    i32, u64, sz = ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+    H = _P
+    sig = {
+        "qd_create": (i32, [ctypes.POINTER(QdConfig), _P, ctypes.POINTER(H)]),
+        "qd_load_weights": (i32, [H, ctypes.POINTER(QdWeights)]),
+        "qd_reset_kv": (i32, [H]),
+        "qd_prefill": (i32, [H, ctypes.POINTER(ctypes.c_int32), i32, ctypes.POINTER(QdSampling), _P, _P]),
+        "qd_decode_step": (i32, [H, ctypes.POINTER(QdSampling), _P, _P]),
+        "qd_set_lora": (i32, [H, ctypes.POINTER(QdLora)]),
+        "qd_clear_lora": (i32, [H]),
+        "qd_enable_capture": (i32, [H, i32]),
+        "qd_get_capture": (i32, [H, i32, i32, ctypes.POINTER(ctypes.c_float), sz, ctypes.POINTER(sz)]),
+        "qd_sync_token": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
+        "qd_get_position": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
+        "qd_last_error": (ctypes.c_char_p, [H]),
+        "qd_destroy": (None, [H]),
+        "qd_sizeof_config": (sz, []),
+        "qd_sizeof_weights": (sz, []),
+        "qd_sizeof_sampling": (sz, []),
+        "qd_sizeof_lora": (sz, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    for name, cls in (("qd_sizeof_config", QdConfig), ("qd_sizeof_weights", QdWeights),
+                      ("qd_sizeof_sampling", QdSampling), ("qd_sizeof_lora", QdLora)):
+        if getattr(L, name)() != ctypes.sizeof(cls):
+            raise ImportError(f"ctypes mirror of {cls.__name__} does not match the C struct size")
+    _lib = L
+    return L
+
+
+class QdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Optional[int] = None) -> QdConfig:
+    """Fill a QdConfig from any object with the model-shape attribute names."""
+    c = QdConfig()
+    c.struct_size = ctypes.sizeof(QdConfig)
+    c.abi_version = QD_ABI_VERSION
+    for f in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "intermediate", "vocab"):
+        setattr(c, f, int(getattr(shape, f)))
+    c.rope_theta = float(shape.rope_theta)
+    c.rms_eps = float(shape.rms_eps)
+    c.qk_norm = int(bool(shape.qk_norm))
+    c.qkv_bias = int(bool(shape.qkv_bias))
+    c.tie_embeddings = 1
+    c.weight_format = int(shape.weight_format)
+    c.max_pos = int(max_pos if max_pos is not None else shape.max_pos)
+    c.max_prefill = int(max_prefill)
+    c.lora_rank_max = int(lora_rank_max)
+    return c
+
+
+def make_sampling(temperature: float, top_k: int, top_p: float, seed: int) -> QdSampling:
+    s = QdSampling()
+    s.struct_size = ctypes.sizeof(QdSampling)
+    s.temperature, s.top_k, s.top_p, s.seed = float(temperature), int(top_k), float(top_p), int(seed)
+    return s
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _ptr_array(ts: Sequence) -> ctypes.Array:
+    return (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+
+
+class Decoder:
+    """One model on the current GPU behind the C ABI.
+
+    Device tensors (torch, on the current CUDA/HIP device) supply the memory the
+    library reads and writes; the current torch stream is the stream every call
+    enqueues on.  Weights are dicts of bf16 tensors (any 16-bit dtype holding
+    bf16 bit patterns).
+    """
+
+    def __init__(self, cfg: QdConfig, stream_ptr: int):
+        self.lib = load_library()
+        self.cfg = cfg
+        h = ctypes.c_void_p()
+        rc = self.lib.qd_create(ctypes.byref(cfg), ctypes.c_void_p(stream_ptr), ctypes.byref(h))
+        if rc != 0:
+            raise QdError(rc, "qd_create failed (reason printed on stderr)")
+        self.h = h
+
+    def _check(self, rc: int):
+        if rc != 0:
+            raise QdError(rc, self.lib.qd_last_error(self.h).decode())
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.qd_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def load_weights(self, w: Dict):
+        """w = {"embed", "final_norm", "layers": [ {name: tensor} ]} of device tensors."""
+        layers = w["layers"]
+        qw = QdWeights()
+        qw.struct_size = ctypes.sizeof(QdWeights)
+        qw.embed = _ptr(w["embed"])
+        qw.final_norm = _ptr(w["final_norm"])
+        qw.lm_head = None
+        keep = []
+        for name in ("attn_norm", "mlp_norm", "q_norm", "k_norm", "wq", "wk", "wv", "wo", "bq", "bk", "bv",
+                     "w_gate", "w_up", "w_down"):
+            if name in layers[0]:
+                arr = _ptr_array([lw[name] for lw in layers])
+                keep.append(arr)
+                setattr(qw, name, ctypes.cast(arr, _PP))
+        self._check(self.lib.qd_load_weights(self.h, ctypes.byref(qw)))
+
+    def reset_kv(self):
+        self._check(self.lib.qd_reset_kv(self.h))
+
+    def prefill(self, tokens: Sequence[int], sampling: Optional[QdSampling] = None, logits_out=None, token_out=None):
+        arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+        self._check(self.lib.qd_prefill(self.h, arr, len(tokens), ctypes.byref(sampling) if sampling else None,
+                                        ctypes.c_void_p(_ptr(logits_out)), ctypes.c_void_p(_ptr(token_out))))
+
+    def decode_step(self, sampling: Optional[QdSampling] = None, logits_out=None, token_out=None):
+        self._check(self.lib.qd_decode_step(self.h, ctypes.byref(sampling) if sampling else None,
+                                            ctypes.c_void_p(_ptr(logits_out)), ctypes.c_void_p(_ptr(token_out))))
+
+    def set_lora(self, lora_layers: List[Dict], rank: int, alpha: float):
+        q = QdLora()
+        q.struct_size = ctypes.sizeof(QdLora)
+        q.rank, q.alpha = int(rank), float(alpha)
+        keep = []
+        for name in ("a_q", "b_q", "a_v", "b_v"):
+            arr = _ptr_array([lw[name] for lw in lora_layers])
+            keep.append(arr)
+            setattr(q, name, ctypes.cast(arr, _PP))
+        self._check(self.lib.qd_set_lora(self.h, ctypes.byref(q)))
+
+    def clear_lora(self):
+        self._check(self.lib.qd_clear_lora(self.h))
+
+    def enable_capture(self, on: bool = True):
+        self._check(self.lib.qd_enable_capture(self.h, int(on)))
+
+    def get_capture(self, what: int, layer: int, capacity: int):
+        import numpy as np
+        out = np.empty(capacity, dtype=np.float32)
+        written = ctypes.c_size_t()
+        self._check(self.lib.qd_get_capture(self.h, what, layer,
+                                            out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), capacity,
+                                            ctypes.byref(written)))
+        return out[:written.value]
+
+    def sync_token(self) -> int:
+        t = ctypes.c_int32()
+        self._check(self.lib.qd_sync_token(self.h, ctypes.byref(t)))
+        return t.value
+
+    @property
+    def position(self) -> int:
+        p = ctypes.c_int32()
+        self._check(self.lib.qd_get_position(self.h, ctypes.byref(p)))
+        return p.value

@@ -1,0 +1,509 @@
+// Engine and C ABI of libqd (declared in include/qd.h).
+//
+// One handle = one model on one GPU: engine-owned weights (bf16, or int4
+// group-128 codes + fp16 scales), an f32 KV cache laid out
+// [layer][kv_head][position][head_dim] (head-major, so a kv head's rows are
+// contiguous for the attention scan), host-baked f32 RoPE tables, workspaces
+// and the device-resident step state {pos, token, step}.  Every step is
+// enqueued on the caller's stream; a decode step is one replay of a captured
+// hipGraph that reads pos/token from device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/qd.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kAttnChunk = 64;  // cache positions per split-K attention block
+
+struct Layer {
+  uint16_t* wqkv = nullptr;  // [(nq + 2 nkv) d, H]
+  float* bqkv = nullptr;     // [(nq + 2 nkv) d] or null
+  float* attn_norm = nullptr;
+  float* mlp_norm = nullptr;
+  float* q_norm = nullptr;
+  float* k_norm = nullptr;
+  uint16_t* wo = nullptr;  // [H, nq d]
+  uint16_t* wg = nullptr;  // [I, H]
+  uint16_t* wu = nullptr;  // [I, H]
+  uint16_t* wd = nullptr;  // [H, I]
+};
+
+__global__ void k_widen_bf16(const uint16_t* __restrict__ src, float* __restrict__ dst, size_t n) {
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = __uint_as_float(((uint32_t)src[i]) << 16);
+}
+
+}  // namespace
+
+struct qd_handle {
+  qd_config cfg{};
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+  int device = 0;
+  std::string err;
+  bool weights = false;
+  int32_t pos = 0;        // host mirror of DevState::pos
+  bool have_token = false;
+  std::vector<void*> allocs;
+
+  uint16_t* embed = nullptr;
+  float* final_norm = nullptr;
+  std::vector<Layer> layers;
+
+  float* Kc = nullptr;  // [L][nkv][max_pos][d]
+  float* Vc = nullptr;
+  float* rope_cos = nullptr;  // [max_pos][d/2]
+  float* rope_sin = nullptr;
+
+  // workspaces (rows = max_prefill)
+  float* x = nullptr;    // [rows][H]
+  float* qkv = nullptr;  // [rows][(nq + 2 nkv) d]
+  float* q = nullptr;    // [rows][nq][d]
+  float* o = nullptr;    // [rows][nq d]
+  float* act = nullptr;  // [rows][I]
+  float* part = nullptr; // attention partials
+  size_t part_floats = 0;
+  float* logits = nullptr;  // [V]
+  float* pval = nullptr;
+  int32_t* pidx = nullptr;
+  int32_t* tokens_dev = nullptr;  // [max_prefill]
+  int32_t* tokens_pinned = nullptr;
+  DevState* st = nullptr;
+
+  hipGraphExec_t decode_exec = nullptr;
+  hipGraph_t decode_graph = nullptr;
+
+  bool capture_on = false;
+  float* cap = nullptr;  // [(L + 1)][rows][H] + [H] + [V]
+  int32_t cap_rows = 0;  // rows of the last captured prefill (0 = none)
+
+  int set_err(int code, const std::string& m) {
+    err = m;
+    return code;
+  }
+};
+
+namespace {
+
+#define HIP_TRY(h, call)                                                                   \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess)                                                                  \
+      return (h)->set_err(QD_E_HIP, std::string(#call) + ": " + hipGetErrorString(e_));    \
+  } while (0)
+
+template <typename T>
+int dev_alloc(qd_handle* h, T** p, size_t n) {
+  void* v = nullptr;
+  hipError_t e = hipMalloc(&v, n * sizeof(T) + 16);
+  if (e != hipSuccess) return h->set_err(QD_E_OOM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  h->allocs.push_back(v);
+  *p = static_cast<T*>(v);
+  return QD_OK;
+}
+
+int qkv_rows(const qd_config& c) { return (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim; }
+
+int attn_splits(int ctx) { return (ctx + kAttnChunk - 1) / kAttnChunk; }
+
+// Rows of attention partials the workspace holds at once for a prefill.
+int attn_row_chunk(const qd_config& c) {
+  const size_t per_row = (size_t)c.n_q_heads * attn_splits(c.max_pos) * (c.head_dim + 2);
+  size_t rows = ((size_t)64 << 20) / sizeof(float) / per_row;  // 64 MiB budget
+  if (rows < 1) rows = 1;
+  if (rows > (size_t)c.max_prefill) rows = c.max_prefill;
+  return (int)rows;
+}
+
+int gemv_t_tile(int K) {
+  int t = (16384 - 64) / K;  // keep the staged input (plus the reduction slots) within 64 KiB of LDS
+  if (t > GEMV_MAX_T) t = GEMV_MAX_T;
+  if (t < 1) t = 1;
+  return t;
+}
+
+int validate_config(const qd_config* c, std::string& why) {
+  if (!c) { why = "config is NULL"; return QD_E_ARG; }
+  if (c->struct_size != sizeof(qd_config)) { why = "qd_config.struct_size does not match this library"; return QD_E_ABI; }
+  if (c->abi_version != QD_ABI_VERSION) { why = "qd_config.abi_version does not match this library"; return QD_E_ABI; }
+  if (c->n_layers < 1 || c->hidden < 256 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->intermediate < 8 ||
+      c->vocab < 1) { why = "non-positive or too small model dimension"; return QD_E_ARG; }
+  if (c->head_dim != 128) { why = "head_dim must be 128"; return QD_E_ARG; }
+  if (c->n_q_heads % c->n_kv_heads) { why = "n_q_heads must be a multiple of n_kv_heads"; return QD_E_ARG; }
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) { why = "n_q_heads / n_kv_heads must be 1, 2, 4 or 8"; return QD_E_ARG; }
+  if (c->hidden % 512 || (c->n_q_heads * c->head_dim) % 512) { why = "hidden and n_q_heads*head_dim must be multiples of 512"; return QD_E_ARG; }
+  if (c->intermediate % 128) { why = "intermediate must be a multiple of 128"; return QD_E_ARG; }
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) { why = "rope_theta must be > 0 and rms_eps >= 0"; return QD_E_ARG; }
+  if (c->tie_embeddings != 1) { why = "only tied embeddings are supported (tie_embeddings must be 1)"; return QD_E_ARG; }
+  if (c->weight_format != QD_W_BF16) { why = "weight_format not supported by this build"; return QD_E_ARG; }
+  if (c->max_pos < 1 || c->max_pos > (1 << 20)) { why = "max_pos out of range"; return QD_E_ARG; }
+  if (c->max_prefill < 1 || c->max_prefill > c->max_pos) { why = "max_prefill must be in [1, max_pos]"; return QD_E_ARG; }
+  if (c->lora_rank_max != 0) { why = "LoRA not supported by this build"; return QD_E_ARG; }
+  return QD_OK;
+}
+
+int build_rope_tables(qd_handle* h) {
+  const qd_config& c = h->cfg;
+  const int half = c.head_dim / 2;
+  std::vector<float> cs((size_t)c.max_pos * half), sn((size_t)c.max_pos * half);
+  for (int j = 0; j < half; ++j) {
+    const double inv = std::pow((double)c.rope_theta, -2.0 * j / c.head_dim);
+    for (int p = 0; p < c.max_pos; ++p) {
+      const double a = (double)p * inv;
+      cs[(size_t)p * half + j] = (float)std::cos(a);
+      sn[(size_t)p * half + j] = (float)std::sin(a);
+    }
+  }
+  HIP_TRY(h, hipMemcpy(h->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(h, hipMemcpy(h->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+  return QD_OK;
+}
+
+void free_all(qd_handle* h) {
+  if (h->decode_exec) (void)hipGraphExecDestroy(h->decode_exec);
+  if (h->decode_graph) (void)hipGraphDestroy(h->decode_graph);
+  h->decode_exec = nullptr;
+  h->decode_graph = nullptr;
+  for (void* p : h->allocs) (void)hipFree(p);
+  h->allocs.clear();
+  if (h->tokens_pinned) (void)hipHostFree(h->tokens_pinned);
+  h->tokens_pinned = nullptr;
+  if (h->own_stream && h->stream) (void)hipStreamDestroy(h->stream);
+  h->stream = nullptr;
+}
+
+// Enqueue the whole forward for T new rows whose ids are at `tok` (device),
+// at positions st->pos .. st->pos + T - 1, and choose the next token from the
+// last row.  Captures are written only when `capture` is set.
+void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
+  const qd_config& c = h->cfg;
+  hipStream_t s = h->stream;
+  const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, I = c.intermediate;
+  const int NQKV = qkv_rows(c);
+  const size_t layer_kv = (size_t)nkv * c.max_pos * d;
+  launch_embed(s, h->embed, tok, T, H, h->x);
+  if (capture) (void)hipMemcpyAsync(h->cap, h->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice, s);
+  const int att_rows = T == 1 ? 1 : attn_row_chunk(c);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const Layer& L = h->layers[l];
+    for (int t0 = 0, tt = gemv_t_tile(H); t0 < T; t0 += tt) {
+      const int tn = std::min(tt, T - t0);
+      launch_gemv_bf16(s, L.wqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
+                       h->qkv + (size_t)t0 * NQKV, NQKV, 0);
+    }
+    launch_qk_rope_kv(s, h->qkv, NQKV, T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin, h->st,
+                      h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
+    if (T == 1) {
+      launch_attention(s, h->q, 1, nq, nkv, d, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st,
+                       kAttnChunk, attn_splits(c.max_pos), h->part, h->o, nq * d, 0);
+    } else {
+      for (int t0 = 0; t0 < T; t0 += att_rows) {
+        const int tn = std::min(att_rows, T - t0);
+        const int S = attn_splits(h->pos + t0 + tn);
+        launch_attention(s, h->q + (size_t)t0 * nq * d, tn, nq, nkv, d, h->Kc + l * layer_kv, h->Vc + l * layer_kv,
+                         c.max_pos, h->st, kAttnChunk, S, h->part, h->o + (size_t)t0 * nq * d, nq * d, t0);
+      }
+    }
+    for (int t0 = 0, tt = gemv_t_tile(nq * d); t0 < T; t0 += tt) {
+      const int tn = std::min(tt, T - t0);
+      launch_gemv_bf16(s, L.wo, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
+                       h->x + (size_t)t0 * H, H, 1);
+    }
+    for (int t0 = 0, tt = gemv_t_tile(H); t0 < T; t0 += tt) {
+      const int tn = std::min(tt, T - t0);
+      launch_gemv_gateup_bf16(s, L.wg, L.wu, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
+                              h->act + (size_t)t0 * I, I);
+    }
+    for (int t0 = 0, tt = gemv_t_tile(I); t0 < T; t0 += tt) {
+      const int tn = std::min(tt, T - t0);
+      launch_gemv_bf16(s, L.wd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr, h->x + (size_t)t0 * H,
+                       H, 1);
+    }
+    if (capture)
+      (void)hipMemcpyAsync(h->cap + (size_t)(l + 1) * c.max_prefill * H, h->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice,
+                     s);
+  }
+  float* xf_cap = capture ? h->cap + (size_t)(c.n_layers + 1) * c.max_prefill * H : nullptr;
+  launch_lmhead_bf16(s, h->embed, c.vocab, H, h->x + (size_t)(T - 1) * H, h->final_norm, c.rms_eps, h->logits,
+                     h->pval, h->pidx, xf_cap);
+  launch_argmax_final(s, h->pval, h->pidx, lmhead_blocks(c.vocab), h->st, T, nullptr);
+  if (capture)
+    (void)hipMemcpyAsync(xf_cap + H, h->logits, (size_t)c.vocab * 4, hipMemcpyDeviceToDevice, s);
+}
+
+int copy_outputs(qd_handle* h, float* logits_dev, int32_t* token_dev) {
+  if (logits_dev)
+    HIP_TRY(h, hipMemcpyAsync(logits_dev, h->logits, (size_t)h->cfg.vocab * 4, hipMemcpyDeviceToDevice, h->stream));
+  if (token_dev)
+    HIP_TRY(h, hipMemcpyAsync(token_dev, &h->st->token, 4, hipMemcpyDeviceToDevice, h->stream));
+  return QD_OK;
+}
+
+int check_sampling(qd_handle* h, const qd_sampling* sp) {
+  if (!sp) return QD_OK;
+  if (sp->struct_size != sizeof(qd_sampling)) return h->set_err(QD_E_ABI, "qd_sampling.struct_size mismatch");
+  if (sp->temperature > 0.f) return h->set_err(QD_E_ARG, "sampling not supported by this build");
+  return QD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qd_sizeof_config(void) { return sizeof(qd_config); }
+size_t qd_sizeof_weights(void) { return sizeof(qd_weights); }
+size_t qd_sizeof_sampling(void) { return sizeof(qd_sampling); }
+size_t qd_sizeof_lora(void) { return sizeof(qd_lora); }
+
+const char* qd_last_error(const qd_handle* h) { return h ? h->err.c_str() : "NULL handle"; }
+
+int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
+  if (!out) return QD_E_ARG;
+  *out = nullptr;
+  std::string why;
+  int rc = validate_config(cfg, why);
+  if (rc != QD_OK) {
+    fprintf(stderr, "qd_create: %s\n", why.c_str());
+    return rc;
+  }
+  qd_handle* h = new qd_handle();
+  h->cfg = *cfg;
+  const qd_config& c = h->cfg;
+  auto fail = [&](int code) {
+    fprintf(stderr, "qd_create: %s\n", h->err.c_str());
+    free_all(h);
+    delete h;
+    return code;
+  };
+  if (hipGetDevice(&h->device) != hipSuccess) return fail(h->set_err(QD_E_HIP, "hipGetDevice failed"));
+  if (hip_stream) {
+    h->stream = (hipStream_t)hip_stream;
+  } else {
+    if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess)
+      return fail(h->set_err(QD_E_HIP, "hipStreamCreate failed"));
+    h->own_stream = true;
+  }
+  const size_t H = c.hidden, d = c.head_dim, I = c.intermediate, rows = c.max_prefill;
+  const size_t kv = (size_t)c.n_layers * c.n_kv_heads * c.max_pos * d;
+  h->part_floats = (size_t)(c.max_prefill > 1 ? attn_row_chunk(c) : 1) * c.n_q_heads * attn_splits(c.max_pos) * (d + 2);
+  if ((rc = dev_alloc(h, &h->Kc, kv)) || (rc = dev_alloc(h, &h->Vc, kv)) ||
+      (rc = dev_alloc(h, &h->rope_cos, (size_t)c.max_pos * d / 2)) ||
+      (rc = dev_alloc(h, &h->rope_sin, (size_t)c.max_pos * d / 2)) || (rc = dev_alloc(h, &h->x, rows * H)) ||
+      (rc = dev_alloc(h, &h->qkv, rows * qkv_rows(c))) || (rc = dev_alloc(h, &h->q, rows * c.n_q_heads * d)) ||
+      (rc = dev_alloc(h, &h->o, rows * c.n_q_heads * d)) || (rc = dev_alloc(h, &h->act, rows * I)) ||
+      (rc = dev_alloc(h, &h->part, h->part_floats)) || (rc = dev_alloc(h, &h->logits, (size_t)c.vocab)) ||
+      (rc = dev_alloc(h, &h->pval, (size_t)lmhead_blocks(c.vocab))) ||
+      (rc = dev_alloc(h, &h->pidx, (size_t)lmhead_blocks(c.vocab))) ||
+      (rc = dev_alloc(h, &h->tokens_dev, rows)) || (rc = dev_alloc(h, &h->st, 1)))
+    return fail(rc);
+  if (hipHostMalloc((void**)&h->tokens_pinned, rows * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
+    return fail(h->set_err(QD_E_OOM, "hipHostMalloc failed"));
+  if ((rc = build_rope_tables(h))) return fail(rc);
+  if (hipMemset(h->st, 0, sizeof(DevState)) != hipSuccess) return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
+  h->layers.resize(c.n_layers);
+  *out = h;
+  return QD_OK;
+}
+
+int qd_load_weights(qd_handle* h, const qd_weights* w) {
+  if (!h) return QD_E_ARG;
+  if (!w) return h->set_err(QD_E_ARG, "weights is NULL");
+  if (w->struct_size != sizeof(qd_weights)) return h->set_err(QD_E_ABI, "qd_weights.struct_size mismatch");
+  const qd_config& c = h->cfg;
+  if (w->lm_head) return h->set_err(QD_E_ARG, "lm_head must be NULL for tied embeddings");
+  if (!w->embed || !w->final_norm || !w->attn_norm || !w->mlp_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+      !w->w_gate || !w->w_up || !w->w_down)
+    return h->set_err(QD_E_ARG, "a required weight array is NULL");
+  if (c.qk_norm && (!w->q_norm || !w->k_norm)) return h->set_err(QD_E_ARG, "q_norm/k_norm required");
+  if (c.qkv_bias && (!w->bq || !w->bk || !w->bv)) return h->set_err(QD_E_ARG, "bq/bk/bv required");
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (!w->attn_norm[l] || !w->mlp_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->w_gate[l] ||
+        !w->w_up[l] || !w->w_down[l] || (c.qk_norm && (!w->q_norm[l] || !w->k_norm[l])) ||
+        (c.qkv_bias && (!w->bq[l] || !w->bk[l] || !w->bv[l])))
+      return h->set_err(QD_E_ARG, "NULL pointer in layer " + std::to_string(l));
+  }
+  const size_t H = c.hidden, d = c.head_dim, I = c.intermediate, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const size_t NQKV = qkv_rows(c);
+  hipStream_t s = h->stream;
+  int rc;
+  auto widen = [&](const void* src, float* dst, size_t n) {
+    hipLaunchKernelGGL(k_widen_bf16, dim3((n + 255) / 256), dim3(256), 0, s, (const uint16_t*)src, dst, n);
+  };
+  if (!h->weights) {  // first load: allocate engine-owned weight buffers
+    if ((rc = dev_alloc(h, &h->embed, (size_t)c.vocab * H)) || (rc = dev_alloc(h, &h->final_norm, H))) return rc;
+    for (auto& L : h->layers) {
+      if ((rc = dev_alloc(h, &L.wqkv, NQKV * H)) || (rc = dev_alloc(h, &L.attn_norm, H)) ||
+          (rc = dev_alloc(h, &L.mlp_norm, H)) || (rc = dev_alloc(h, &L.wo, H * nq * d)) ||
+          (rc = dev_alloc(h, &L.wg, I * H)) || (rc = dev_alloc(h, &L.wu, I * H)) || (rc = dev_alloc(h, &L.wd, H * I)))
+        return rc;
+      if (c.qk_norm && ((rc = dev_alloc(h, &L.q_norm, d)) || (rc = dev_alloc(h, &L.k_norm, d)))) return rc;
+      if (c.qkv_bias && (rc = dev_alloc(h, &L.bqkv, NQKV))) return rc;
+    }
+  }
+  HIP_TRY(h, hipMemcpyAsync(h->embed, w->embed, (size_t)c.vocab * H * 2, hipMemcpyDeviceToDevice, s));
+  widen(w->final_norm, h->final_norm, H);
+  for (int l = 0; l < c.n_layers; ++l) {
+    Layer& L = h->layers[l];
+    HIP_TRY(h, hipMemcpyAsync(L.wqkv, w->wq[l], nq * d * H * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(L.wqkv + nq * d * H, w->wk[l], nkv * d * H * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(L.wqkv + (nq + nkv) * d * H, w->wv[l], nkv * d * H * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(L.wo, w->wo[l], H * nq * d * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(L.wg, w->w_gate[l], I * H * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(L.wu, w->w_up[l], I * H * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(L.wd, w->w_down[l], H * I * 2, hipMemcpyDeviceToDevice, s));
+    widen(w->attn_norm[l], L.attn_norm, H);
+    widen(w->mlp_norm[l], L.mlp_norm, H);
+    if (c.qk_norm) {
+      widen(w->q_norm[l], L.q_norm, d);
+      widen(w->k_norm[l], L.k_norm, d);
+    }
+    if (c.qkv_bias) {
+      widen(w->bq[l], L.bqkv, nq * d);
+      widen(w->bk[l], L.bqkv + nq * d, nkv * d);
+      widen(w->bv[l], L.bqkv + (nq + nkv) * d, nkv * d);
+    }
+  }
+  HIP_TRY(h, hipGetLastError());
+  HIP_TRY(h, hipStreamSynchronize(s));
+  h->weights = true;
+  return qd_reset_kv(h);
+}
+
+int qd_reset_kv(qd_handle* h) {
+  if (!h) return QD_E_ARG;
+  HIP_TRY(h, hipMemsetAsync(h->st, 0, sizeof(DevState), h->stream));
+  h->pos = 0;
+  h->have_token = false;
+  h->cap_rows = 0;
+  return QD_OK;
+}
+
+int qd_prefill(qd_handle* h, const int32_t* tokens_host, int32_t n, const qd_sampling* sampling, float* logits_dev,
+               int32_t* token_dev) {
+  if (!h) return QD_E_ARG;
+  if (!h->weights) return h->set_err(QD_E_STATE, "weights not loaded");
+  if (!tokens_host) return h->set_err(QD_E_ARG, "tokens is NULL");
+  if (n <= 0) return h->set_err(QD_E_ARG, "empty prompt (n <= 0)");
+  if (n > h->cfg.max_prefill) return h->set_err(QD_E_RANGE, "n exceeds max_prefill");
+  if ((int64_t)h->pos + n > h->cfg.max_pos) return h->set_err(QD_E_RANGE, "position would exceed max_pos");
+  for (int i = 0; i < n; ++i)
+    if (tokens_host[i] < 0 || tokens_host[i] >= h->cfg.vocab) return h->set_err(QD_E_ARG, "token id out of range");
+  int rc = check_sampling(h, sampling);
+  if (rc) return rc;
+  // the pinned staging buffer may still feed an earlier async copy
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  memcpy(h->tokens_pinned, tokens_host, (size_t)n * sizeof(int32_t));
+  HIP_TRY(h, hipMemcpyAsync(h->tokens_dev, h->tokens_pinned, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice,
+                            h->stream));
+  enqueue_forward(h, n, h->tokens_dev, h->capture_on);
+  HIP_TRY(h, hipGetLastError());
+  h->pos += n;
+  h->have_token = true;
+  h->cap_rows = h->capture_on ? n : 0;
+  return copy_outputs(h, logits_dev, token_dev);
+}
+
+int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev, int32_t* token_dev) {
+  if (!h) return QD_E_ARG;
+  if (!h->weights) return h->set_err(QD_E_STATE, "weights not loaded");
+  if (!h->have_token) return h->set_err(QD_E_STATE, "decode before prefill");
+  if (h->pos + 1 > h->cfg.max_pos) return h->set_err(QD_E_RANGE, "position would exceed max_pos");
+  int rc = check_sampling(h, sampling);
+  if (rc) return rc;
+  if (!h->decode_exec) {
+    HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+    enqueue_forward(h, 1, &h->st->token, false);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(h->stream, &g);
+    if (e != hipSuccess) return h->set_err(QD_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    h->decode_graph = g;
+    HIP_TRY(h, hipGraphInstantiate(&h->decode_exec, g, nullptr, nullptr, 0));
+  }
+  HIP_TRY(h, hipGraphLaunch(h->decode_exec, h->stream));
+  h->pos += 1;
+  return copy_outputs(h, logits_dev, token_dev);
+}
+
+int qd_set_lora(qd_handle* h, const qd_lora* lora) {
+  if (!h) return QD_E_ARG;
+  if (!lora) return h->set_err(QD_E_ARG, "lora is NULL");
+  if (lora->struct_size != sizeof(qd_lora)) return h->set_err(QD_E_ABI, "qd_lora.struct_size mismatch");
+  return h->set_err(QD_E_STATE, "LoRA not enabled (lora_rank_max = 0)");
+}
+
+int qd_clear_lora(qd_handle* h) {
+  if (!h) return QD_E_ARG;
+  return QD_OK;
+}
+
+int qd_enable_capture(qd_handle* h, int32_t enable) {
+  if (!h) return QD_E_ARG;
+  if (enable && !h->cap) {
+    const qd_config& c = h->cfg;
+    size_t n = (size_t)(c.n_layers + 1) * c.max_prefill * c.hidden + c.hidden + c.vocab;
+    int rc = dev_alloc(h, &h->cap, n);
+    if (rc) return rc;
+  }
+  h->capture_on = enable != 0;
+  return QD_OK;
+}
+
+int qd_get_capture(qd_handle* h, int32_t what, int32_t layer, float* out_host, size_t capacity_elems,
+                   size_t* written_elems) {
+  if (!h) return QD_E_ARG;
+  if (!out_host) return h->set_err(QD_E_ARG, "out_host is NULL");
+  if (h->cap_rows == 0 || !h->cap) return h->set_err(QD_E_STATE, "nothing captured");
+  const qd_config& c = h->cfg;
+  const size_t H = c.hidden, rows = h->cap_rows;
+  const float* src = nullptr;
+  size_t n = 0;
+  switch (what) {
+    case QD_CAP_EMBED: src = h->cap; n = rows * H; break;
+    case QD_CAP_LAYER_OUT:
+      if (layer < 0 || layer >= c.n_layers) return h->set_err(QD_E_ARG, "layer out of range");
+      src = h->cap + (size_t)(layer + 1) * c.max_prefill * H;
+      n = rows * H;
+      break;
+    case QD_CAP_FINAL_NORM: src = h->cap + (size_t)(c.n_layers + 1) * c.max_prefill * H; n = H; break;
+    case QD_CAP_LOGITS: src = h->cap + (size_t)(c.n_layers + 1) * c.max_prefill * H + H; n = c.vocab; break;
+    default: return h->set_err(QD_E_ARG, "unknown capture point");
+  }
+  if (capacity_elems < n) return h->set_err(QD_E_ARG, "capacity smaller than the capture");
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipMemcpy(out_host, src, n * 4, hipMemcpyDeviceToHost));
+  if (written_elems) *written_elems = n;
+  return QD_OK;
+}
+
+int qd_sync_token(qd_handle* h, int32_t* token_host) {
+  if (!h) return QD_E_ARG;
+  if (!token_host) return h->set_err(QD_E_ARG, "token_host is NULL");
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  DevState st;
+  HIP_TRY(h, hipMemcpy(&st, h->st, sizeof(st), hipMemcpyDeviceToHost));
+  *token_host = st.token;
+  return QD_OK;
+}
+
+int qd_get_position(const qd_handle* h, int32_t* pos_out) {
+  if (!h || !pos_out) return QD_E_ARG;
+  *pos_out = h->pos;
+  return QD_OK;
+}
+
+void qd_destroy(qd_handle* h) {
+  if (!h) return;
+  if (h->stream) (void)hipStreamSynchronize(h->stream);
+  free_all(h);
+  delete h;
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Host-side launchers of the gfx950 decoder-step kernels (internal to libqd).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Device-resident step state: the decode graph reads pos/token from here, so
+// one captured graph serves every position.
+struct DevState {
+  int32_t pos;    // tokens already in the KV cache
+  int32_t token;  // last chosen token (input of the next decode step)
+  int32_t step;   // tokens chosen since the last reset (sampling counter)
+  int32_t pad;
+};
+
+#define GEMV_MAX_T 8   // input rows handled per GEMV launch
+#define GEMV_RPW 4     // output rows per wave (plain GEMV)
+#define GATEUP_RPW 2   // output rows per wave (gate/up pair)
+#define LMHEAD_RPW 4   // vocabulary rows per wave (LM head)
+
+void launch_embed(hipStream_t s, const uint16_t* E, const int32_t* tok, int T, int H, float* x);
+void launch_gemv_bf16(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
+                      const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate);
+void launch_gemv_gateup_bf16(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
+                             int ldx, int T, const float* gain, float eps, float* a, int lda);
+int lmhead_blocks(int V);
+void launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
+                        float* logits, float* part_val, int32_t* part_idx, float* xf_out);
+void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* part_idx, int nparts, DevState* st,
+                         int advance, int32_t* token_out);
+void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq, int nkv, int d, const float* qn,
+                       const float* kn, float eps, const float* cos_t, const float* sin_t, const DevState* st,
+                       float* q_out, float* Kc, float* Vc, int max_pos);
+void launch_attention(hipStream_t s, const float* q, int T, int nq, int nkv, int d, const float* Kc, const float* Vc,
+                      int max_pos, const DevState* st, int chunk, int S, float* part, float* o_out, int ldo,
+                      int row0);

@@ -1,0 +1,485 @@
+// Decoder-step kernels for gfx950 (wave64, 160 KB LDS per CU).
+//
+// Activations, accumulators and the KV cache are f32; weights are bf16 (or int4
+// group-128 codes with fp16 scales) widened in registers.  Every reduction has
+// a fixed order (no float atomics), so results are bit-identical run to run.
+#include "common.h"
+#include "kernels.h"
+
+// ---------------------------------------------------------------------------
+// Embedding gather: x[t, :] = E[tok[t], :] widened to f32.
+// "Failed Star / fs — Forward pass → logits", GATHER step (IDs -> residual rows).
+__global__ __launch_bounds__(256) void k_embed(const uint16_t* __restrict__ E, const int32_t* __restrict__ tok,
+                                               int H, float* __restrict__ x) {
+  const int t = blockIdx.x;
+  const int id = tok[t];
+  const uint16_t* row = E + (size_t)id * H;
+  for (int k = threadIdx.x * 4; k < H; k += 256 * 4) {
+    u32x2 w = *reinterpret_cast<const u32x2*>(row + k);
+    f32x4 o = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+    *reinterpret_cast<f32x4*>(x + (size_t)t * H + k) = o;
+  }
+}
+
+void launch_embed(hipStream_t s, const uint16_t* E, const int32_t* tok, int T, int H, float* x) {
+  hipLaunchKernelGGL(k_embed, dim3(T), dim3(256), 0, s, E, tok, H, x);
+}
+
+// ---------------------------------------------------------------------------
+// Input staging shared by the GEMV kernels: rows [T][K] of the input into LDS,
+// optionally RMS-normalised with gains (RMSNorm as a GEMV prologue).
+// h[t][k] = x[t][k] * g[k] / sqrt(mean_k x[t][k]^2 + eps)
+__device__ __forceinline__ void stage_input(const float* __restrict__ x, int ldx, int T, int K,
+                                            const float* __restrict__ gain, float eps, float* h, float* red) {
+  for (int t = 0; t < T; ++t) {
+    const float* xr = x + (size_t)t * ldx;
+    float ss = 0.f;
+    for (int k = threadIdx.x * 4; k < K; k += 1024) {
+      f32x4 v = *reinterpret_cast<const f32x4*>(xr + k);
+      *reinterpret_cast<f32x4*>(h + t * K + k) = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    if (gain) {
+      float tot = block_sum_256(ss, red);
+      float r = 1.0f / sqrtf(tot / (float)K + eps);
+      for (int k = threadIdx.x * 4; k < K; k += 1024) {
+        f32x4 v = *reinterpret_cast<f32x4*>(h + t * K + k);
+        f32x4 g = *reinterpret_cast<const f32x4*>(gain + k);
+        v = v * r * g;
+        *reinterpret_cast<f32x4*>(h + t * K + k) = v;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Dot of one bf16 weight row chunk (8 values in a u32x4) with 8 staged inputs.
+__device__ __forceinline__ float dot8(u32x4 w, const float* hk) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(hk);
+  f32x4 b = *reinterpret_cast<const f32x4*>(hk + 4);
+  float s = bf16_lo(w.x) * a.x;
+  s = fmaf(bf16_hi(w.x), a.y, s);
+  s = fmaf(bf16_lo(w.y), a.z, s);
+  s = fmaf(bf16_hi(w.y), a.w, s);
+  s = fmaf(bf16_lo(w.z), b.x, s);
+  s = fmaf(bf16_hi(w.z), b.y, s);
+  s = fmaf(bf16_lo(w.w), b.z, s);
+  s = fmaf(bf16_hi(w.w), b.w, s);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 GEMV / skinny GEMM for T <= GEMV_MAX_T input rows:
+//   y[t][n] (=|+=) sum_k W[n][k] * h[t][k] (+ bias[n])
+// W row-major [N][K] (the [out, in] layout of the pages).  Each wave owns RPW
+// consecutive output rows; each lane streams 16-byte chunks of those rows.
+// The wave-wide sum of a row is taken in a fixed order.
+template <int RPW>
+__global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ W, int N, int K,
+                                                   const float* __restrict__ x, int ldx, int T,
+                                                   const float* __restrict__ gain, float eps,
+                                                   const float* __restrict__ bias,
+                                                   float* __restrict__ y, int ldy, int accumulate) {
+  extern __shared__ float smem[];
+  float* red = smem;
+  float* h = smem + 8;
+  stage_input(x, ldx, T, K, gain, eps, h, red);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * RPW;
+  if (n0 >= N) return;
+  float acc[RPW][GEMV_MAX_T];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int t = 0; t < GEMV_MAX_T; ++t) acc[i][t] = 0.f;
+  for (int k = lane * 8; k < K; k += 512) {
+    u32x4 w[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int n = min(n0 + i, N - 1);
+      w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)n * K + k));
+    }
+#pragma unroll
+    for (int t = 0; t < GEMV_MAX_T; ++t) {
+      if (t < T) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) acc[i][t] += dot8(w[i], h + t * K + k);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+#pragma unroll
+    for (int t = 0; t < GEMV_MAX_T; ++t) {
+      if (t < T) {
+        float s = wave_sum(acc[i][t]);
+        const int n = n0 + i;
+        if (lane == 0 && n < N) {
+          float* yp = y + (size_t)t * ldy + n;
+          float v = s + (bias ? bias[n] : 0.f);
+          *yp = accumulate ? (*yp + v) : v;
+        }
+      }
+    }
+  }
+}
+
+int gemv_rows_per_block() { return 4 * GEMV_RPW; }
+
+void launch_gemv_bf16(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
+                      const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate) {
+  const int rows_per_block = 4 * GEMV_RPW;
+  dim3 grid((N + rows_per_block - 1) / rows_per_block);
+  size_t lds = (8 + (size_t)T * K) * sizeof(float);
+  hipLaunchKernelGGL(k_gemv_bf16<GEMV_RPW>, grid, dim3(256), lds, s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy,
+                     accumulate);
+}
+
+// ---------------------------------------------------------------------------
+// Fused gate/up GEMV with the SiLU(gate) * up epilogue and an RMSNorm prologue:
+//   a[t][i] = SiLU(sum_k Wg[i][k] h[t][k]) * (sum_k Wu[i][k] h[t][k])
+// "Failed Star / fs" block figure (SwiGLU); the gated product is formed in
+// registers and never stored separately.
+template <int RPW>
+__global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __restrict__ Wg,
+                                                          const uint16_t* __restrict__ Wu, int N, int K,
+                                                          const float* __restrict__ x, int ldx, int T,
+                                                          const float* __restrict__ gain, float eps,
+                                                          float* __restrict__ a, int lda) {
+  extern __shared__ float smem[];
+  float* red = smem;
+  float* h = smem + 8;
+  stage_input(x, ldx, T, K, gain, eps, h, red);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * RPW;
+  if (n0 >= N) return;
+  float ag[RPW][GEMV_MAX_T], au[RPW][GEMV_MAX_T];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int t = 0; t < GEMV_MAX_T; ++t) ag[i][t] = au[i][t] = 0.f;
+  for (int k = lane * 8; k < K; k += 512) {
+    u32x4 wg[RPW], wu[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int n = min(n0 + i, N - 1);
+      wg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wg + (size_t)n * K + k));
+      wu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wu + (size_t)n * K + k));
+    }
+#pragma unroll
+    for (int t = 0; t < GEMV_MAX_T; ++t) {
+      if (t < T) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          ag[i][t] += dot8(wg[i], h + t * K + k);
+          au[i][t] += dot8(wu[i], h + t * K + k);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+#pragma unroll
+    for (int t = 0; t < GEMV_MAX_T; ++t) {
+      if (t < T) {
+        float g = wave_sum(ag[i][t]);
+        float u = wave_sum(au[i][t]);
+        const int n = n0 + i;
+        if (lane == 0 && n < N) a[(size_t)t * lda + n] = silu_f(g) * u;
+      }
+    }
+  }
+}
+
+void launch_gemv_gateup_bf16(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
+                             int ldx, int T, const float* gain, float eps, float* a, int lda) {
+  const int rows_per_block = 4 * GATEUP_RPW;
+  dim3 grid((N + rows_per_block - 1) / rows_per_block);
+  size_t lds = (8 + (size_t)T * K) * sizeof(float);
+  hipLaunchKernelGGL(k_gemv_gateup_bf16<GATEUP_RPW>, grid, dim3(256), lds, s, Wg, Wu, N, K, x, ldx, T, gain, eps,
+                     a, lda);
+}
+
+// ---------------------------------------------------------------------------
+// Final RMSNorm + tied LM head for one row, with per-block argmax partials.
+//   logits[v] = sum_k E[v][k] * xf[k];  partial[b] = (max logit, lowest id) over the block's rows.
+// "Failed Star / fs", LAST ROW step (tied table as the [V, H] output linear).
+__global__ __launch_bounds__(256) void k_lmhead_bf16(const uint16_t* __restrict__ E, int V, int H,
+                                                     const float* __restrict__ x, const float* __restrict__ gain,
+                                                     float eps, float* __restrict__ logits,
+                                                     float* __restrict__ part_val, int32_t* __restrict__ part_idx,
+                                                     float* __restrict__ xf_out) {
+  extern __shared__ float smem[];
+  float* red = smem;
+  float* h = smem + 8;
+  __shared__ float bval[4];
+  __shared__ int32_t bidx[4];
+  stage_input(x, H, 1, H, gain, eps, h, red);
+  if (xf_out && blockIdx.x == 0)
+    for (int k = threadIdx.x; k < H; k += 256) xf_out[k] = h[k];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * LMHEAD_RPW;
+  float acc[LMHEAD_RPW];
+#pragma unroll
+  for (int i = 0; i < LMHEAD_RPW; ++i) acc[i] = 0.f;
+  if (n0 < V) {
+    for (int k = lane * 8; k < H; k += 512) {
+      u32x4 w[LMHEAD_RPW];
+#pragma unroll
+      for (int i = 0; i < LMHEAD_RPW; ++i) {
+        const int n = min(n0 + i, V - 1);
+        w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(E + (size_t)n * H + k));
+      }
+#pragma unroll
+      for (int i = 0; i < LMHEAD_RPW; ++i) acc[i] += dot8(w[i], h + k);
+    }
+  }
+  float best = -INFINITY;
+  int32_t bi = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < LMHEAD_RPW; ++i) {
+    float s = wave_sum(acc[i]);
+    const int n = n0 + i;
+    if (n < V) {
+      if (lane == 0) logits[n] = s;
+      if (s > best) { best = s; bi = n; }  // rows visited in increasing id: ties keep the lowest
+    }
+  }
+  if (lane == 0) { bval[wave] = best; bidx[wave] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bv = bval[0];
+    int32_t bj = bidx[0];
+    for (int w = 1; w < 4; ++w)
+      if (bval[w] > bv || (bval[w] == bv && bidx[w] < bj)) { bv = bval[w]; bj = bidx[w]; }
+    part_val[blockIdx.x] = bv;
+    part_idx[blockIdx.x] = bj;
+  }
+}
+
+int lmhead_blocks(int V) { return (V + 4 * LMHEAD_RPW - 1) / (4 * LMHEAD_RPW); }
+
+void launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
+                        float* logits, float* part_val, int32_t* part_idx, float* xf_out) {
+  dim3 grid(lmhead_blocks(V));
+  size_t lds = (8 + (size_t)H) * sizeof(float);
+  hipLaunchKernelGGL(k_lmhead_bf16, grid, dim3(256), lds, s, E, V, H, x, gain, eps, logits, part_val, part_idx,
+                     xf_out);
+}
+
+// ---------------------------------------------------------------------------
+// Final greedy choice over the per-block partials (ties -> lowest id), then
+// advance the device-resident step state: token := choice, pos += advance, step += 1.
+// "flashmoon demo/README.md", Performance notes: argmax stays on the GPU and
+// only the token id crosses to the host.
+__global__ __launch_bounds__(256) void k_argmax_final(const float* __restrict__ part_val,
+                                                      const int32_t* __restrict__ part_idx, int nparts,
+                                                      DevState* st, int advance, int32_t* token_out) {
+  __shared__ float sv[256];
+  __shared__ int32_t si[256];
+  float bv = -INFINITY;
+  int32_t bj = 0x7fffffff;
+  for (int i = threadIdx.x; i < nparts; i += 256) {
+    float v = part_val[i];
+    int32_t j = part_idx[i];
+    if (v > bv || (v == bv && j < bj)) { bv = v; bj = j; }
+  }
+  sv[threadIdx.x] = bv;
+  si[threadIdx.x] = bj;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) {
+      float v = sv[threadIdx.x + off];
+      int32_t j = si[threadIdx.x + off];
+      if (v > sv[threadIdx.x] || (v == sv[threadIdx.x] && j < si[threadIdx.x])) {
+        sv[threadIdx.x] = v;
+        si[threadIdx.x] = j;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int32_t tok = si[0];
+    if (tok == 0x7fffffff) tok = 0;  // only if every logit was NaN
+    st->token = tok;
+    st->pos += advance;
+    st->step += 1;
+    if (token_out) *token_out = tok;
+  }
+}
+
+void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* part_idx, int nparts, DevState* st,
+                         int advance, int32_t* token_out) {
+  hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(256), 0, s, part_val, part_idx, nparts, st, advance, token_out);
+}
+
+// ---------------------------------------------------------------------------
+// Per-head QK-RMSNorm, RoPE and the KV-cache write for T rows at positions
+// pos .. pos+T-1 (pos read from the device state).
+// "flashmoon demo/README.md", decode invariants: RoPE is applied as K is
+// written, so the cache holds rotated keys.  "Failed Star / fs" block figure:
+// QK-norm comes before RoPE.  Pairs are (j, j + d/2).
+// grid (T, nq + nkv), block d/2 threads (one per rotation pair).
+__global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, int nkv, int d,
+                             const float* __restrict__ qn, const float* __restrict__ kn, float eps,
+                             const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+                             const DevState* __restrict__ st, float* __restrict__ q_out,
+                             float* __restrict__ Kc, float* __restrict__ Vc, int max_pos) {
+  const int t = blockIdx.x, head = blockIdx.y, j = threadIdx.x, half = d >> 1;
+  const int pos = st->pos + t;
+  const float* row = qkv + (size_t)t * ldqkv;
+  const bool is_q = head < nq;
+  const int g = head - nq;
+  const float* src = is_q ? row + head * d : row + nq * d + g * d;
+  float a = src[j], b = src[j + half];
+  const float* gain = is_q ? qn : kn;
+  if (gain) {
+    __shared__ float red[4];
+    float ss = a * a + b * b;
+    ss = wave_sum(ss);
+    if (half > 64) {  // more than one wave per head
+      if ((j & 63) == 0) red[j >> 6] = ss;
+      __syncthreads();
+      ss = 0.f;
+      for (int w = 0; w < (half + 63) / 64; ++w) ss += red[w];
+    }
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    a = a * r * gain[j];
+    b = b * r * gain[j + half];
+  }
+  const float c = cos_t[(size_t)pos * half + j], s = sin_t[(size_t)pos * half + j];
+  const float ra = a * c - b * s, rb = b * c + a * s;
+  if (is_q) {
+    float* qo = q_out + ((size_t)t * nq + head) * d;
+    qo[j] = ra;
+    qo[j + half] = rb;
+  } else {
+    float* kr = Kc + ((size_t)g * max_pos + pos) * d;
+    kr[j] = ra;
+    kr[j + half] = rb;
+    const float* vsrc = row + (nq + nkv) * d + g * d;
+    float* vr = Vc + ((size_t)g * max_pos + pos) * d;
+    vr[j] = vsrc[j];
+    vr[j + half] = vsrc[j + half];
+  }
+}
+
+void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq, int nkv, int d, const float* qn,
+                       const float* kn, float eps, const float* cos_t, const float* sin_t, const DevState* st,
+                       float* q_out, float* Kc, float* Vc, int max_pos) {
+  hipLaunchKernelGGL(k_qk_rope_kv, dim3(T, nq + nkv), dim3(d / 2), 0, s, qkv, ldqkv, nq, nkv, d, qn, kn, eps, cos_t,
+                     sin_t, st, q_out, Kc, Vc, max_pos);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K decode attention (query row t sits at position pos+row0+t), GQA.
+// grid (nkv, S, T), block 256.  Block (g, s, t) covers cache positions
+// [s*chunk, min((s+1)*chunk, ctx)), ctx = pos + t + 1, for the G = nq/nkv query
+// heads of kv head g, so each K/V row is read once for the whole group.
+// Each half-wave holds one position per iteration (32 lanes x 4 dims = 128);
+// the running maximum / sum / weighted V (online softmax) stay in registers,
+// then the 8 half-wave states are merged in a fixed order through LDS.
+// Writes partials part[t][h][s] = {m, l, o[0..d)} (o not yet divided by l).
+// "EMBERGLASS README", split-K flash-style decode attention.
+template <int G>
+__global__ __launch_bounds__(256) void k_attn_splitk(const float* __restrict__ q, int nq, int nkv,
+                                                     const float* __restrict__ Kc, const float* __restrict__ Vc,
+                                                     int max_pos, const DevState* __restrict__ st, int chunk,
+                                                     int S, float scale, float* __restrict__ part, int row0) {
+  constexpr int D = 128;
+  const int g = blockIdx.x, sp = blockIdx.y, t = blockIdx.z;
+  const int ctx = st->pos + row0 + t + 1;
+  const int p_begin = sp * chunk;
+  const int p_end = min(p_begin + chunk, ctx);
+  if (p_begin >= p_end) return;  // the merge only reads splits below ceil(ctx/chunk)
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hw = wave * 2 + (lane >> 5);  // half-wave id 0..7
+  const int sub = lane & 31;              // dims 4*sub .. 4*sub+3
+  f32x4 qv[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+    qv[j] = *reinterpret_cast<const f32x4*>(q + ((size_t)t * nq + g * G + j) * D + sub * 4);
+  float m[G], l[G];
+  f32x4 o[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) { m[j] = -INFINITY; l[j] = 0.f; o[j] = f32x4{0, 0, 0, 0}; }
+  const float* Kg = Kc + (size_t)g * max_pos * D;
+  const float* Vg = Vc + (size_t)g * max_pos * D;
+  for (int p = p_begin + hw; p < p_end; p += 8) {
+    f32x4 kv = *reinterpret_cast<const f32x4*>(Kg + (size_t)p * D + sub * 4);
+    f32x4 vv = *reinterpret_cast<const f32x4*>(Vg + (size_t)p * D + sub * 4);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float sdot = qv[j].x * kv.x + qv[j].y * kv.y + qv[j].z * kv.z + qv[j].w * kv.w;
+      sdot = group_sum<32>(sdot) * scale;
+      const float mn = fmaxf(m[j], sdot);
+      const float corr = __expf(m[j] - mn);
+      const float pw = __expf(sdot - mn);
+      l[j] = l[j] * corr + pw;
+      o[j] = o[j] * corr + vv * pw;
+      m[j] = mn;
+    }
+  }
+  // merge the 8 half-wave states: LDS [8][G][D + 2]
+  __shared__ float sm[8 * G * (D + 2)];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float* e = sm + (hw * G + j) * (D + 2);
+    *reinterpret_cast<f32x4*>(e + 2 + sub * 4) = o[j];
+    if (sub == 0) { e[0] = m[j]; e[1] = l[j]; }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int j = idx / D, dd = idx % D;
+    float M = -INFINITY;
+    for (int w = 0; w < 8; ++w) M = fmaxf(M, sm[(w * G + j) * (D + 2)]);
+    float L = 0.f, acc = 0.f;
+    for (int w = 0; w < 8; ++w) {
+      const float* e = sm + (w * G + j) * (D + 2);
+      if (e[0] == -INFINITY) continue;  // half-wave saw no position
+      const float f = __expf(e[0] - M);
+      L += e[1] * f;
+      acc += e[2 + dd] * f;
+    }
+    float* out = part + (((size_t)t * nq + g * G + j) * S + sp) * (D + 2);
+    out[2 + dd] = acc;
+    if (dd == 0) { out[0] = M; out[1] = L; }
+  }
+}
+
+// Merge the split partials of each (t, head): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M},
+// splits taken in increasing order.  grid (nq, T), block D.
+__global__ void k_attn_merge(const float* __restrict__ part, int nq, int S, int chunk, const DevState* __restrict__ st,
+                             float* __restrict__ o_out, int ldo, int row0) {
+  constexpr int D = 128;
+  const int h = blockIdx.x, t = blockIdx.y, dd = threadIdx.x;
+  const int ctx = st->pos + row0 + t + 1;
+  const int s_act = min(S, (ctx + chunk - 1) / chunk);
+  const float* base = part + ((size_t)t * nq + h) * S * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < s_act; ++s) M = fmaxf(M, base[s * (D + 2)]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < s_act; ++s) {
+    const float* e = base + s * (D + 2);
+    const float f = __expf(e[0] - M);
+    L += e[1] * f;
+    acc += e[2 + dd] * f;
+  }
+  o_out[(size_t)t * ldo + h * D + dd] = acc / L;
+}
+
+void launch_attention(hipStream_t s, const float* q, int T, int nq, int nkv, int d, const float* Kc, const float* Vc,
+                      int max_pos, const DevState* st, int chunk, int S, float* part, float* o_out, int ldo,
+                      int row0) {
+  const float scale = 1.0f / sqrtf((float)d);
+  dim3 grid(nkv, S, T);
+  const int G = nq / nkv;
+  switch (G) {
+    case 1: hipLaunchKernelGGL(k_attn_splitk<1>, grid, dim3(256), 0, s, q, nq, nkv, Kc, Vc, max_pos, st, chunk, S, scale, part, row0); break;
+    case 2: hipLaunchKernelGGL(k_attn_splitk<2>, grid, dim3(256), 0, s, q, nq, nkv, Kc, Vc, max_pos, st, chunk, S, scale, part, row0); break;
+    case 4: hipLaunchKernelGGL(k_attn_splitk<4>, grid, dim3(256), 0, s, q, nq, nkv, Kc, Vc, max_pos, st, chunk, S, scale, part, row0); break;
+    case 8: hipLaunchKernelGGL(k_attn_splitk<8>, grid, dim3(256), 0, s, q, nq, nkv, Kc, Vc, max_pos, st, chunk, S, scale, part, row0); break;
+    default: break;  // rejected by the host before any launch
+  }
+  hipLaunchKernelGGL(k_attn_merge, dim3(nq, T), dim3(d), 0, s, part, nq, S, chunk, st, o_out, ldo, row0);
+}

@@ -1,0 +1,207 @@
+/*
+ * qd.h — C ABI of the MI355X (gfx950) single-sequence decoder-step library.
+ *
+ * The library computes the forward step of a Qwen3-style decoder-only
+ * transformer for one sequence: embedding gather, then per layer RMSNorm,
+ * Q/K/V projection (+bias, +LoRA), per-head QK-RMSNorm, RoPE applied as K is
+ * written to an f32 KV cache, causal grouped-query attention, o_proj and
+ * residual, RMSNorm, SwiGLU gate/up/down and residual; then the final norm,
+ * the tied-embedding LM head and an on-GPU argmax or top-k/top-p draw.
+ *
+ * Sources (page title, section):
+ *   - "Failed Star / fs — Forward pass → logits": the block order, [out,in]
+ *     weight rows, the tied head borrowing the embedding table, the last-row
+ *     projection, rejection of empty or over-long prompts before any work.
+ *   - "flashmoon demo/README.md — Qwen3-0.6B inference": f32 KV cache, RoPE
+ *     fused into the cache write, in-place SiLU and residual, argmax on the GPU
+ *     so only the token crosses to the host; temperature 0 means greedy;
+ *     MAXPOS sizing of the cache.
+ *   - "EMBERGLASS (qwen-webgpu-lora) README": int4 group-128 weights quantised
+ *     on the way to the GPU, split-K decode attention, live LoRA that restores
+ *     the base bit-for-bit when cleared, maxCtx / maxPrefillT options.
+ *   - "SuperKittens PR #7 (qwen3: 0.6B correctness + 2.6x decode speedup)":
+ *     a C ABI of config and weight structs behind a ctypes binding (and the
+ *     struct-size mismatches that motivate struct_size / abi_version here),
+ *     the capture call that must fail for what was not captured and must not
+ *     overrun the caller's buffer, seq-major vs head-major layout at T >= 2.
+ *
+ * Conventions
+ *   - Every call returns an int status: QD_OK (0) or a negative QD_E_* code.
+ *     qd_last_error() returns a text reason for the last failure on a handle.
+ *   - Arguments are checked before any state change or GPU work; a failed
+ *     call leaves the handle as it was.
+ *   - "device pointer" = memory allocated on the handle's GPU (hipMalloc or
+ *     a torch CUDA tensor).  "host pointer" = ordinary process memory.
+ *   - GPU work is enqueued on the hipStream_t given to qd_create and is
+ *     asynchronous unless stated; qd_sync_token() synchronises.
+ *   - Not thread-safe: one handle must not be used by two threads at once.
+ */
+#ifndef QD_H
+#define QD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QD_ABI_VERSION 1
+
+typedef struct qd_handle qd_handle; /* opaque; owns every device buffer it allocates */
+
+enum {
+  QD_OK = 0,
+  QD_E_ARG = -1,   /* bad argument: NULL pointer, bad shape, n <= 0, capacity too small */
+  QD_E_ABI = -2,   /* struct_size or abi_version does not match this library */
+  QD_E_STATE = -3, /* call not valid now (no weights, decode before prefill, nothing captured) */
+  QD_E_RANGE = -4, /* position would exceed max_pos, or n exceeds max_prefill */
+  QD_E_OOM = -5,   /* device allocation failed */
+  QD_E_HIP = -6    /* a HIP runtime call failed */
+};
+
+enum { QD_W_BF16 = 0, QD_W_INT4_G128 = 1 };
+
+/* Model and engine shape.  Copied by qd_create. */
+typedef struct {
+  uint32_t struct_size; /* = sizeof(qd_config) */
+  uint32_t abi_version; /* = QD_ABI_VERSION */
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
+  float rope_theta; /* RoPE base; pair j of a head turns by pos * theta^(-2j/head_dim) */
+  float rms_eps;    /* epsilon inside the RMSNorm square root */
+  uint8_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE */
+  uint8_t qkv_bias;       /* 1: q/k/v projections carry a bias */
+  uint8_t tie_embeddings; /* must be 1: the LM head is the embedding table */
+  uint8_t weight_format;  /* QD_W_BF16 or QD_W_INT4_G128 (projections only; E stays bf16) */
+  int32_t max_pos;        /* KV-cache capacity in positions */
+  int32_t max_prefill;    /* largest n accepted by one qd_prefill call */
+  int32_t lora_rank_max;  /* 0 disables LoRA; else the largest rank qd_set_lora accepts */
+} qd_config;
+
+/* Weights: device pointers to bf16 (uint16 bit patterns), row-major [out, in].
+ * Per-layer fields are HOST arrays of n_layers device pointers.  Shapes:
+ *   embed [vocab, hidden], final_norm [hidden], attn_norm/mlp_norm [hidden],
+ *   q_norm/k_norm [head_dim] (read only when qk_norm), wq [nq*d, hidden],
+ *   wk/wv [nkv*d, hidden], bq [nq*d], bk/bv [nkv*d] (read only when qkv_bias),
+ *   wo [hidden, nq*d], w_gate/w_up [intermediate, hidden], w_down [hidden, intermediate].
+ * Everything is copied (or, for QD_W_INT4_G128, quantised) into buffers the
+ * handle owns; the caller's memory is only borrowed during the call. */
+typedef struct {
+  uint32_t struct_size; /* = sizeof(qd_weights) */
+  const void* embed;
+  const void* final_norm;
+  const void* lm_head; /* must be NULL (tied) */
+  const void* const* attn_norm;
+  const void* const* mlp_norm;
+  const void* const* q_norm;
+  const void* const* k_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
+  const void* const* bq;
+  const void* const* bk;
+  const void* const* bv;
+  const void* const* w_gate;
+  const void* const* w_up;
+  const void* const* w_down;
+} qd_weights;
+
+/* Token choice.  temperature <= 0 (or a NULL qd_sampling*) means greedy argmax
+ * with ties to the lowest id.  Otherwise: keep the top_k logits (by value, then
+ * lowest id; top_k <= 0 or > 64 is rejected), softmax at `temperature`, keep
+ * the shortest prefix whose mass before each kept entry is < top_p, and pick
+ * with the uniform u = (SplitMix64 output number (step+1) from state `seed`) >> 40
+ * divided by 2^24, where step counts tokens chosen since the last qd_reset_kv
+ * (0 = the token chosen by the first qd_prefill). */
+typedef struct {
+  uint32_t struct_size; /* = sizeof(qd_sampling) */
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  uint64_t seed;
+} qd_sampling;
+
+/* Rank-r LoRA on q_proj and v_proj: q += (alpha/r) B_q (A_q h), v += (alpha/r) B_v (A_v h),
+ * h = the attention-normed input.  HOST arrays of n_layers device pointers to bf16:
+ * a_q/a_v [r, hidden], b_q [nq*d, r], b_v [nkv*d, r].  Copied into the handle. */
+typedef struct {
+  uint32_t struct_size; /* = sizeof(qd_lora) */
+  int32_t rank;
+  float alpha;
+  const void* const* a_q;
+  const void* const* b_q;
+  const void* const* a_v;
+  const void* const* b_v;
+} qd_lora;
+
+/* Capture points for layer-by-layer comparison (what argument of qd_get_capture). */
+enum {
+  QD_CAP_EMBED = 0,      /* f32 [n, hidden]: gathered rows of the last prefill */
+  QD_CAP_LAYER_OUT = 1,  /* f32 [n, hidden]: residual after layer `layer` */
+  QD_CAP_FINAL_NORM = 2, /* f32 [hidden]: final-normed last row */
+  QD_CAP_LOGITS = 3      /* f32 [vocab]: logits of the last row */
+};
+
+/* Validate *cfg (before any HIP call), then allocate the KV cache
+ * ([n_layers][n_kv_heads][max_pos][head_dim] f32 for K and for V), workspaces
+ * and RoPE tables on the current HIP device.  hip_stream is a hipStream_t
+ * (NULL = the default stream); all later work is enqueued on it.
+ * On success *out receives a new handle.  Errors: QD_E_ARG, QD_E_ABI, QD_E_OOM, QD_E_HIP. */
+int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out);
+
+/* Copy (or quantise) every weight into the handle; synchronous with respect to
+ * the caller's pointers (they may be freed on return).  Resets the KV cache.
+ * Errors: QD_E_ARG (NULL field, lm_head not NULL), QD_E_ABI, QD_E_HIP. */
+int qd_load_weights(qd_handle* h, const qd_weights* w);
+
+/* Empty the KV cache: position := 0, step := 0.  The LoRA state is kept. */
+int qd_reset_kv(qd_handle* h);
+
+/* Append n prompt tokens (host int32 array, ids in [0, vocab)) at the current
+ * position in one batched pass, then choose the next token from the last
+ * row's logits.  Requires 1 <= n <= max_prefill and position + n <= max_pos.
+ * logits_dev (device f32 [vocab]) and token_dev (device int32 [1]) are
+ * optional outputs, written asynchronously.  The chosen token stays on the
+ * device as the input of the next qd_decode_step.
+ * Errors: QD_E_ARG (NULL tokens, n <= 0, id out of range), QD_E_RANGE, QD_E_STATE (no weights). */
+int qd_prefill(qd_handle* h, const int32_t* tokens_host, int32_t n, const qd_sampling* sampling,
+               float* logits_dev, int32_t* token_dev);
+
+/* One decode step: consume the device-resident last token at the current
+ * position, write its K/V, and choose the next token.  Needs a prior
+ * qd_prefill since the last reset and position + 1 <= max_pos.
+ * Errors: QD_E_STATE, QD_E_RANGE, QD_E_ARG (bad sampling). */
+int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev, int32_t* token_dev);
+
+/* Install (copy) a LoRA adapter; rank must be 1..lora_rank_max.  Clearing
+ * restores the base model bit-for-bit (the adapter's kernels are not run). */
+int qd_set_lora(qd_handle* h, const qd_lora* lora);
+int qd_clear_lora(qd_handle* h);
+
+/* Copy a capture point of the most recent qd_prefill into out_host (host
+ * f32, capacity_elems elements).  Captures are recorded only while enabled
+ * with qd_enable_capture(h, 1).  Errors: QD_E_STATE if that point was not
+ * captured, QD_E_ARG if capacity_elems is smaller than the capture. */
+int qd_enable_capture(qd_handle* h, int32_t enable);
+int qd_get_capture(qd_handle* h, int32_t what, int32_t layer, float* out_host, size_t capacity_elems,
+                   size_t* written_elems);
+
+/* Synchronise the stream and read the device-resident last token. */
+int qd_sync_token(qd_handle* h, int32_t* token_host);
+
+/* Current position (number of tokens in the KV cache), host-side mirror. */
+int qd_get_position(const qd_handle* h, int32_t* pos_out);
+
+const char* qd_last_error(const qd_handle* h);
+void qd_destroy(qd_handle* h);
+
+size_t qd_sizeof_config(void);
+size_t qd_sizeof_weights(void);
+size_t qd_sizeof_sampling(void);
+size_t qd_sizeof_lora(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QD_H */

@@ -1,0 +1,81 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/qd.h declares, the ctypes mirrors match the C struct sizes, and
+qd_create rejects bad configurations before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+import decoder_only_token_amd as qd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(qd_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = qd.load_library()
+    names = declared_functions()
+    assert {"qd_create", "qd_load_weights", "qd_prefill", "qd_decode_step", "qd_reset_kv"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(qd.EXPORTS) == names
+
+
+def test_struct_sizes_match_ctypes_mirrors():
+    lib = qd.load_library()
+    assert lib.qd_sizeof_config() == ctypes.sizeof(qd.QdConfig)
+    assert lib.qd_sizeof_weights() == ctypes.sizeof(qd.QdWeights)
+    assert lib.qd_sizeof_sampling() == ctypes.sizeof(qd.QdSampling)
+    assert lib.qd_sizeof_lora() == ctypes.sizeof(qd.QdLora)
+
+
+def _create(cfg):
+    lib = qd.load_library()
+    h = ctypes.c_void_p()
+    return lib.qd_create(ctypes.byref(cfg), None, ctypes.byref(h)), h
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda c: setattr(c, "struct_size", c.struct_size - 4), -2),
+    (lambda c: setattr(c, "abi_version", 99), -2),
+    (lambda c: setattr(c, "head_dim", 64), -1),
+    (lambda c: setattr(c, "n_kv_heads", 3), -1),
+    (lambda c: setattr(c, "n_layers", 0), -1),
+    (lambda c: setattr(c, "max_prefill", 0), -1),
+    (lambda c: setattr(c, "max_prefill", c.max_pos + 1), -1),
+    (lambda c: setattr(c, "tie_embeddings", 0), -1),
+    (lambda c: setattr(c, "rope_theta", 0.0), -1),
+])
+def test_create_rejects_bad_config_before_any_hip_call(mutate, code):
+    cfg = qd.make_config(synth.TINY, max_prefill=16)
+    mutate(cfg)
+    rc, h = _create(cfg)
+    assert rc == code
+    assert not h.value
+
+
+def test_create_rejects_null_config():
+    lib = qd.load_library()
+    h = ctypes.c_void_p()
+    assert lib.qd_create(None, None, ctypes.byref(h)) == -1
+
+
+def test_null_handle_calls_fail_cleanly():
+    lib = qd.load_library()
+    assert lib.qd_reset_kv(None) == -1
+    assert lib.qd_decode_step(None, None, None, None) == -1
+    assert lib.qd_prefill(None, None, 0, None, None, None) == -1
+    assert lib.qd_last_error(None) == b"NULL handle"
+    lib.qd_destroy(None)

@@ -1,0 +1,177 @@
+"""GPU parity: the HIP library against the float64 oracle on seeded inputs.
+
+Bar: every logit within |got - want| <= 2e-3 + 2e-3 |want|, and the GPU's
+greedy token equal to the oracle's argmax except at near-ties (two candidates
+within that tolerance on the oracle's logits), which are counted and must stay rare.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import OracleModel
+
+from gpu_util import lockstep_greedy, logits_within_tol, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def make_decoder(torch_cuda, shape, max_prefill, lora_rank_max=0):
+    import decoder_only_token_amd as qd
+    cfg = qd.make_config(shape, max_prefill=max_prefill, lora_rank_max=lora_rank_max)
+    return qd.Decoder(cfg, torch_cuda.cuda.current_stream().cuda_stream)
+
+
+def assert_records(recs, max_forced=0):
+    bad = [r for r in recs if r.n_bad]
+    assert not bad, f"logits out of tolerance at steps {[(r.step, r.max_err_ratio, r.n_bad) for r in bad[:5]]}"
+    forced = [r for r in recs if r.forced]
+    assert len(forced) <= max_forced, f"token mismatches (near-ties) at {[(r.step, r.gpu_token, r.oracle_token) for r in forced]}"
+
+
+@pytest.mark.parametrize("random_gains", [False, True])
+def test_tiny_prefill_and_decode(torch_cuda, random_gains):
+    """8-token prompt then 16 greedy steps on the 2-layer tiny model; every step checked."""
+    wl = synth.WORKLOADS["tiny"]
+    shape = wl.shape
+    log(f"tiny random_gains={random_gains}")
+    w = synth.make_weights(shape, random_gains=random_gains)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, wl.max_prefill)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = synth.make_prompt(shape.vocab, wl.prompt_len)
+    recs = lockstep_greedy(dec, oracle, prompt, wl.decode_steps, log=log)
+    assert_records(recs)
+
+
+def test_tiny_capture_checkpoints(torch_cuda):
+    """Embedding, every layer's output, final norm and logits of a 13-token prefill."""
+    import decoder_only_token_amd as qd
+    shape = synth.TINY
+    w = synth.make_weights(shape, seed=5, random_gains=True)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 16)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    dec.enable_capture(True)
+    prompt = synth.make_prompt(shape.vocab, 13, seed=6)
+    dec.prefill(prompt)
+    cap = {}
+    oracle.forward(prompt, capture=cap)
+    H = shape.hidden
+    got = dec.get_capture(qd.QD_CAP_EMBED, 0, 13 * H).reshape(13, H)
+    assert np.array_equal(got, cap["embed"].astype(np.float32))
+    for l in range(shape.n_layers):
+        got = dec.get_capture(qd.QD_CAP_LAYER_OUT, l, 13 * H).reshape(13, H)
+        np.testing.assert_allclose(got, cap["layer_out"][l], rtol=1e-3, atol=1e-3)
+    got = dec.get_capture(qd.QD_CAP_FINAL_NORM, 0, H)
+    np.testing.assert_allclose(got, cap["final_norm"][-1], rtol=1e-3, atol=1e-3)
+    got = dec.get_capture(qd.QD_CAP_LOGITS, 0, shape.vocab)
+    ok, ratio, nbad = logits_within_tol(got, cap["logits"][-1])
+    assert ok, (ratio, nbad)
+    with pytest.raises(qd.QdError):
+        dec.get_capture(qd.QD_CAP_LOGITS, 0, shape.vocab - 1)  # capacity too small
+
+
+def test_tiny_errors_leave_state_unchanged(torch_cuda):
+    import decoder_only_token_amd as qd
+    shape = synth.TINY
+    dec = make_decoder(torch_cuda, shape, 16)
+    with pytest.raises(qd.QdError) as e:
+        dec.prefill([1, 2, 3])
+    assert e.value.code == -3  # no weights
+    w = synth.make_weights(shape, seed=7)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    with pytest.raises(qd.QdError) as e:
+        dec.decode_step()
+    assert e.value.code == -3  # decode before prefill
+    with pytest.raises(qd.QdError) as e:
+        dec.prefill([])
+    assert e.value.code == -1
+    with pytest.raises(qd.QdError) as e:
+        dec.prefill(list(range(17)))
+    assert e.value.code == -4  # > max_prefill
+    with pytest.raises(qd.QdError) as e:
+        dec.prefill([shape.vocab])
+    assert e.value.code == -1
+    assert dec.position == 0
+    dec.prefill([1, 2])
+    assert dec.position == 2
+
+
+def test_tiny_runs_are_bit_identical(torch_cuda):
+    import torch
+    shape = synth.TINY
+    w = synth.make_weights(shape, seed=8)
+    dec = make_decoder(torch_cuda, shape, 16)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    outs = []
+    for _ in range(2):
+        logits = torch.empty((6, shape.vocab), dtype=torch.float32, device="cuda")
+        dec.reset_kv()
+        dec.prefill([5, 6, 7, 8], logits_out=logits[0])
+        for i in range(1, 6):
+            dec.decode_step(logits_out=logits[i])
+        torch.cuda.synchronize()
+        outs.append(logits.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_tiny_prefill_equals_sequential_decode(torch_cuda):
+    """Batched prefill of 12 tokens vs 1-token prefill + forced 1-token appends: logits agree."""
+    import torch
+    shape = synth.TINY
+    w = synth.make_weights(shape, seed=9)
+    dec = make_decoder(torch_cuda, shape, 16)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    toks = synth.make_prompt(shape.vocab, 12, seed=10)
+    a = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    b = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    dec.prefill(toks, logits_out=a)
+    dec.reset_kv()
+    for t in toks:
+        dec.prefill([t], logits_out=b)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(a.cpu().numpy(), b.cpu().numpy(), rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.slow
+def test_qwen3_06b_prompt5_decode128(torch_cuda):
+    """The Qwen3-0.6B-shaped workload: 5-token prompt, 128 greedy decode steps, every step checked."""
+    wl = synth.WORKLOADS["qwen3-0.6b"]
+    shape = wl.shape
+    log("qwen3-0.6b: drawing weights")
+    w = synth.make_weights(shape)
+    dec = make_decoder(torch_cuda, shape, wl.max_prefill)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    log("qwen3-0.6b: building oracle")
+    oracle = OracleModel(shape, w)
+    del w
+    prompt = synth.make_prompt(shape.vocab, wl.prompt_len)
+    recs = lockstep_greedy(dec, oracle, prompt, wl.decode_steps, log=log)
+    assert_records(recs, max_forced=2)
