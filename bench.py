@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--workload", default="qwen3-0.6b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=8)
+    ap.add_argument("--path", choices=["persistent", "graph"], default="persistent",
+                    help="decode step as one persistent kernel, or as per-operation kernels in a hipGraph")
     return ap.parse_args()
 
 
@@ -77,7 +79,8 @@ def main():
     dw = {"embed": to_dev(weights["embed"]), "final_norm": to_dev(weights["final_norm"]),
           "layers": [{k: to_dev(v) for k, v in lw.items()} for lw in weights["layers"]]}
     torch.cuda.synchronize()
-    dec = qd.Decoder(qd.make_config(shape, max_prefill=wl.max_prefill), stream.cuda_stream)
+    path = qd.QD_DECODE_PERSISTENT if args.path == "persistent" else qd.QD_DECODE_GRAPH
+    dec = qd.Decoder(qd.make_config(shape, max_prefill=wl.max_prefill, decode_path=path), stream.cuda_stream)
     dec.load_weights(dw)
     del dw
     torch.cuda.synchronize()
@@ -107,6 +110,7 @@ def main():
             job(marks[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+    dec.sync_token()  # raises if any decode step was abandoned
     prefill_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
     decode_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
     ms_per_step = wall * 1e3 / args.steps
@@ -138,7 +142,7 @@ def main():
         "config": {"workload": wl.name, "model": shape.name, "layers": shape.n_layers, "hidden": shape.hidden,
                    "heads": [shape.n_q_heads, shape.n_kv_heads], "vocab": shape.vocab,
                    "prompt_len": wl.prompt_len, "decode_steps": n_dec, "global_batch": 1,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "decode_path": args.path},
         "decode_tok_s": round(n_dec / (decode_ms * 1e-3), 2),
         "decode_step_us": round(decode_step_us, 2),
         "prefill_tok_s": round(wl.prompt_len / (prefill_ms * 1e-3), 2),
@@ -146,7 +150,9 @@ def main():
         "decode_hbm_gbs_effective": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode step (captured graph), algorithmic bytes = weights + KV read + KV write"},
+                     "kernel": ("k_decode_persistent (one launch = one decode step)" if args.path == "persistent"
+                                else "decode step (captured graph of per-operation kernels)") +
+                               "; algorithmic bytes = weights + KV read + KV write"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, weights, prompt, args.cpu_sample_steps)

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libqd.so")
 
 QD_ABI_VERSION = 1
 QD_W_BF16, QD_W_INT4_G128 = 0, 1
+QD_DECODE_PERSISTENT, QD_DECODE_GRAPH = 0, 1
 QD_CAP_EMBED, QD_CAP_LAYER_OUT, QD_CAP_FINAL_NORM, QD_CAP_LOGITS = 0, 1, 2, 3
 STATUS = {0: "QD_OK", -1: "QD_E_ARG", -2: "QD_E_ABI", -3: "QD_E_STATE", -4: "QD_E_RANGE", -5: "QD_E_OOM",
           -6: "QD_E_HIP"}
@@ -32,7 +33,7 @@ class QdConfig(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("qk_norm", ctypes.c_uint8), ("qkv_bias", ctypes.c_uint8), ("tie_embeddings", ctypes.c_uint8),
                 ("weight_format", ctypes.c_uint8), ("max_pos", ctypes.c_int32), ("max_prefill", ctypes.c_int32),
-                ("lora_rank_max", ctypes.c_int32)]
+                ("lora_rank_max", ctypes.c_int32), ("decode_path", ctypes.c_int32)]
 
 
 class QdWeights(ctypes.Structure):
@@ -52,7 +53,8 @@ class QdLora(ctypes.Structure):
 
 
 EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_decode_step", "qd_set_lora",
-           "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_sync_token", "qd_get_position",
+           "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_enable_phase_trace", "qd_get_phase_trace",
+           "qd_sync_token", "qd_get_position",
            "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
            "qd_sizeof_lora"]
 
@@ -79,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qd_clear_lora": (i32, [H]),
         "qd_enable_capture": (i32, [H, i32]),
         "qd_get_capture": (i32, [H, i32, i32, ctypes.POINTER(ctypes.c_float), sz, ctypes.POINTER(sz)]),
+        "qd_enable_phase_trace": (i32, [H, i32]),
+        "qd_get_phase_trace": (i32, [H, ctypes.POINTER(ctypes.c_uint64), sz, ctypes.POINTER(sz),
+                                     ctypes.POINTER(ctypes.c_int32)]),
         "qd_sync_token": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
         "qd_get_position": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
         "qd_last_error": (ctypes.c_char_p, [H]),
@@ -106,7 +111,8 @@ class QdError(RuntimeError):
         self.code = code
 
 
-def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Optional[int] = None) -> QdConfig:
+def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Optional[int] = None,
+                decode_path: int = QD_DECODE_PERSISTENT) -> QdConfig:
     """Fill a QdConfig from any object with the model-shape attribute names."""
     c = QdConfig()
     c.struct_size = ctypes.sizeof(QdConfig)
@@ -122,6 +128,7 @@ def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Option
     c.max_pos = int(max_pos if max_pos is not None else shape.max_pos)
     c.max_prefill = int(max_prefill)
     c.lora_rank_max = int(lora_rank_max)
+    c.decode_path = int(decode_path)
     return c
 
 
@@ -227,6 +234,19 @@ class Decoder:
                                             out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), capacity,
                                             ctypes.byref(written)))
         return out[:written.value]
+
+    def enable_phase_trace(self, on: bool = True):
+        self._check(self.lib.qd_enable_phase_trace(self.h, int(on)))
+
+    def get_phase_trace(self):
+        """Stamps of the last decode step as a uint64 array [n_cu, 1 + 2 (5 L + 2)] (100 MHz ticks)."""
+        import numpy as np
+        n = 4096 * (1 + 2 * (5 * self.cfg.n_layers + 2))
+        out = np.empty(n, dtype=np.uint64)
+        written, ncu = ctypes.c_size_t(), ctypes.c_int32()
+        self._check(self.lib.qd_get_phase_trace(self.h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n,
+                                                ctypes.byref(written), ctypes.byref(ncu)))
+        return out[:written.value].reshape(ncu.value, -1)
 
     def sync_token(self) -> int:
         t = ctypes.c_int32()

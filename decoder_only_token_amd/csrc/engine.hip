@@ -17,6 +17,7 @@
 
 #include "../../include/qd.h"
 #include "kernels.h"
+#include "persist.h"
 
 namespace {
 
@@ -79,6 +80,22 @@ struct qd_handle {
 
   hipGraphExec_t decode_exec = nullptr;
   hipGraph_t decode_graph = nullptr;
+
+  // persistent single-kernel decode step
+  bool persistent = false;
+  int grid = 0;   // one workgroup per CU
+  int hseg = 0;   // hidden / 512
+  uint32_t seq = 0;
+  PersistConst* pconst = nullptr;  // device copy
+  LayerPtrs* layer_ptrs = nullptr; // device array [L]
+  uint64_t *X0 = nullptr, *X1 = nullptr, *QKVx = nullptr, *PART = nullptr, *Ox = nullptr, *ACT = nullptr;
+  uint64_t *AMV = nullptr, *AMI = nullptr;
+  uint32_t* err_dev = nullptr;
+  bool failed = false;  // a decode step was abandoned; needs qd_reset_kv
+  PersistConst pc_host{};
+  uint64_t* trace = nullptr;
+  bool trace_on = false;
+  bool traced_step = false;
 
   bool capture_on = false;
   float* cap = nullptr;  // [(L + 1)][rows][H] + [H] + [V]
@@ -147,6 +164,11 @@ int validate_config(const qd_config* c, std::string& why) {
   if (c->max_pos < 1 || c->max_pos > (1 << 20)) { why = "max_pos out of range"; return QD_E_ARG; }
   if (c->max_prefill < 1 || c->max_prefill > c->max_pos) { why = "max_prefill must be in [1, max_pos]"; return QD_E_ARG; }
   if (c->lora_rank_max != 0) { why = "LoRA not supported by this build"; return QD_E_ARG; }
+  if (c->decode_path != QD_DECODE_PERSISTENT && c->decode_path != QD_DECODE_GRAPH) { why = "unknown decode_path"; return QD_E_ARG; }
+  if (c->decode_path == QD_DECODE_PERSISTENT) {
+    if (c->hidden != 1024 && c->hidden != 2048) { why = "the persistent decode step needs hidden 1024 or 2048"; return QD_E_ARG; }
+    if (c->intermediate + c->hidden > 16384 || c->n_q_heads * c->head_dim > 8192) { why = "model too wide for the persistent decode step"; return QD_E_ARG; }
+  }
   return QD_OK;
 }
 
@@ -307,6 +329,33 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if (hipHostMalloc((void**)&h->tokens_pinned, rows * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
     return fail(h->set_err(QD_E_OOM, "hipHostMalloc failed"));
   if ((rc = build_rope_tables(h))) return fail(rc);
+  if (c.decode_path == QD_DECODE_PERSISTENT) {
+    h->persistent = true;
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || ncu < 1)
+      return fail(h->set_err(QD_E_HIP, "cannot query the CU count"));
+    h->grid = ncu > 1024 ? 1024 : ncu;
+    h->hseg = c.hidden / 512;
+    const int G = c.n_q_heads / c.n_kv_heads;
+    if (persist_prepare(G, h->hseg) != 0) return fail(h->set_err(QD_E_HIP, "persistent decode kernel unavailable"));
+    if (2 * ((c.intermediate + h->grid - 1) / h->grid) > 128 || (qkv_rows(c) + h->grid - 1) / h->grid > 128)
+      return fail(h->set_err(QD_E_ARG, "too many rows per CU for the persistent decode step"));
+    const size_t smax = (size_t)h->grid / c.n_kv_heads;
+    if ((rc = dev_alloc(h, &h->X0, H)) || (rc = dev_alloc(h, &h->X1, H)) ||
+        (rc = dev_alloc(h, &h->QKVx, (size_t)qkv_rows(c))) ||
+        (rc = dev_alloc(h, &h->PART, (size_t)c.n_q_heads * smax * (d + 2))) ||
+        (rc = dev_alloc(h, &h->Ox, (size_t)c.n_q_heads * d)) || (rc = dev_alloc(h, &h->ACT, I)) ||
+        (rc = dev_alloc(h, &h->AMV, (size_t)h->grid)) || (rc = dev_alloc(h, &h->AMI, (size_t)h->grid)) ||
+        (rc = dev_alloc(h, &h->err_dev, 4)) || (rc = dev_alloc(h, &h->pconst, 1)) ||
+        (rc = dev_alloc(h, &h->layer_ptrs, (size_t)c.n_layers)))
+      return fail(rc);
+    // tags start at 0; every step uses seq >= 1, so stale words never match
+    if (hipMemset(h->X0, 0, H * 8) || hipMemset(h->X1, 0, H * 8) || hipMemset(h->QKVx, 0, qkv_rows(c) * 8) ||
+        hipMemset(h->PART, 0, (size_t)c.n_q_heads * smax * (d + 2) * 8) || hipMemset(h->Ox, 0, c.n_q_heads * d * 8) ||
+        hipMemset(h->ACT, 0, I * 8) || hipMemset(h->AMV, 0, h->grid * 8) || hipMemset(h->AMI, 0, h->grid * 8) ||
+        hipMemset(h->err_dev, 0, 16))
+      return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
+  }
   if (hipMemset(h->st, 0, sizeof(DevState)) != hipSuccess) return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
   h->layers.resize(c.n_layers);
   *out = h;
@@ -372,6 +421,24 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
     }
   }
   HIP_TRY(h, hipGetLastError());
+  if (h->persistent) {
+    std::vector<LayerPtrs> lp(c.n_layers);
+    for (int l = 0; l < c.n_layers; ++l) {
+      const Layer& L = h->layers[l];
+      lp[l] = LayerPtrs{L.wqkv, L.bqkv, L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm, L.wo, L.wg, L.wu, L.wd};
+    }
+    PersistConst pc{};
+    pc.L = c.n_layers; pc.H = c.hidden; pc.nq = c.n_q_heads; pc.nkv = c.n_kv_heads; pc.I = c.intermediate;
+    pc.V = c.vocab; pc.nqkv = (int)NQKV; pc.max_pos = c.max_pos; pc.eps = c.rms_eps;
+    pc.embed = h->embed; pc.final_norm = h->final_norm; pc.layers = h->layer_ptrs;
+    pc.Kc = h->Kc; pc.Vc = h->Vc; pc.rope_cos = h->rope_cos; pc.rope_sin = h->rope_sin;
+    pc.X0 = h->X0; pc.X1 = h->X1; pc.QKV = h->QKVx; pc.PART = h->PART; pc.O = h->Ox; pc.ACT = h->ACT;
+    pc.AMV = h->AMV; pc.AMI = h->AMI; pc.logits = h->logits; pc.xf_out = nullptr; pc.st = h->st; pc.err = h->err_dev;
+    pc.trace = h->trace_on ? h->trace : nullptr;
+    h->pc_host = pc;
+    HIP_TRY(h, hipMemcpyAsync(h->layer_ptrs, lp.data(), lp.size() * sizeof(LayerPtrs), hipMemcpyHostToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(h->pconst, &pc, sizeof(pc), hipMemcpyHostToDevice, s));
+  }
   HIP_TRY(h, hipStreamSynchronize(s));
   h->weights = true;
   return qd_reset_kv(h);
@@ -380,6 +447,8 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
 int qd_reset_kv(qd_handle* h) {
   if (!h) return QD_E_ARG;
   HIP_TRY(h, hipMemsetAsync(h->st, 0, sizeof(DevState), h->stream));
+  if (h->err_dev) HIP_TRY(h, hipMemsetAsync(h->err_dev, 0, 16, h->stream));
+  h->failed = false;
   h->pos = 0;
   h->have_token = false;
   h->cap_rows = 0;
@@ -418,6 +487,22 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
   if (h->pos + 1 > h->cfg.max_pos) return h->set_err(QD_E_RANGE, "position would exceed max_pos");
   int rc = check_sampling(h, sampling);
   if (rc) return rc;
+  if (h->failed) return h->set_err(QD_E_STATE, "an earlier decode step was abandoned; call qd_reset_kv");
+  if (h->persistent) {
+    const int ctx = h->pos + 1;
+    const int cap = h->grid / h->cfg.n_kv_heads;
+    int S = (ctx + 63) / 64;
+    if (S > cap) S = cap;
+    const int chunk = (ctx + S - 1) / S;
+    S = (ctx + chunk - 1) / chunk;  // every split holds at least one position
+    if (++h->seq >= (1u << 24)) h->seq = 1;
+    const int G = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+    int e = persist_launch(h->pconst, G, h->hseg, h->grid, h->pos, h->seq, S, chunk, h->stream);
+    if (e != 0) return h->set_err(QD_E_HIP, "persistent decode launch failed: " + std::to_string(e));
+    h->pos += 1;
+    h->traced_step = h->trace_on;
+    return copy_outputs(h, logits_dev, token_dev);
+  }
   if (!h->decode_exec) {
     HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
     enqueue_forward(h, 1, &h->st->token, false);
@@ -483,10 +568,48 @@ int qd_get_capture(qd_handle* h, int32_t what, int32_t layer, float* out_host, s
   return QD_OK;
 }
 
+int qd_enable_phase_trace(qd_handle* h, int32_t enable) {
+  if (!h) return QD_E_ARG;
+  if (!h->persistent) return h->set_err(QD_E_STATE, "phase trace needs the persistent decode step");
+  if (!h->weights) return h->set_err(QD_E_STATE, "weights not loaded");
+  if (enable && !h->trace) {
+    int rc = dev_alloc(h, &h->trace, (size_t)h->grid * persist_trace_slots(h->cfg.n_layers));
+    if (rc) return rc;
+  }
+  h->trace_on = enable != 0;
+  h->pc_host.trace = h->trace_on ? h->trace : nullptr;
+  HIP_TRY(h, hipMemcpyAsync(h->pconst, &h->pc_host, sizeof(PersistConst), hipMemcpyHostToDevice, h->stream));
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  h->traced_step = false;
+  return QD_OK;
+}
+
+int qd_get_phase_trace(qd_handle* h, uint64_t* out_host, size_t capacity_elems, size_t* written_elems,
+                       int32_t* n_cu) {
+  if (!h) return QD_E_ARG;
+  if (!out_host) return h->set_err(QD_E_ARG, "out_host is NULL");
+  if (!h->persistent || !h->trace || !h->traced_step) return h->set_err(QD_E_STATE, "no traced decode step");
+  const size_t n = (size_t)h->grid * persist_trace_slots(h->cfg.n_layers);
+  if (capacity_elems < n) return h->set_err(QD_E_ARG, "capacity smaller than the trace");
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipMemcpy(out_host, h->trace, n * 8, hipMemcpyDeviceToHost));
+  if (written_elems) *written_elems = n;
+  if (n_cu) *n_cu = h->grid;
+  return QD_OK;
+}
+
 int qd_sync_token(qd_handle* h, int32_t* token_host) {
   if (!h) return QD_E_ARG;
   if (!token_host) return h->set_err(QD_E_ARG, "token_host is NULL");
   HIP_TRY(h, hipStreamSynchronize(h->stream));
+  if (h->persistent) {
+    uint32_t e = 0;
+    HIP_TRY(h, hipMemcpy(&e, h->err_dev, 4, hipMemcpyDeviceToHost));
+    if (e) {
+      h->failed = true;
+      return h->set_err(QD_E_HIP, "a decode step was abandoned (device-side wait timed out)");
+    }
+  }
   DevState st;
   HIP_TRY(h, hipMemcpy(&st, h->st, sizeof(st), hipMemcpyDeviceToHost));
   *token_host = st.token;

@@ -53,21 +53,6 @@ __device__ __forceinline__ void stage_input(const float* __restrict__ x, int ldx
   __syncthreads();
 }
 
-// Dot of one bf16 weight row chunk (8 values in a u32x4) with 8 staged inputs.
-__device__ __forceinline__ float dot8(u32x4 w, const float* hk) {
-  f32x4 a = *reinterpret_cast<const f32x4*>(hk);
-  f32x4 b = *reinterpret_cast<const f32x4*>(hk + 4);
-  float s = bf16_lo(w.x) * a.x;
-  s = fmaf(bf16_hi(w.x), a.y, s);
-  s = fmaf(bf16_lo(w.y), a.z, s);
-  s = fmaf(bf16_hi(w.y), a.w, s);
-  s = fmaf(bf16_lo(w.z), b.x, s);
-  s = fmaf(bf16_hi(w.z), b.y, s);
-  s = fmaf(bf16_lo(w.w), b.z, s);
-  s = fmaf(bf16_hi(w.w), b.w, s);
-  return s;
-}
-
 // ---------------------------------------------------------------------------
 // bf16 GEMV / skinny GEMM for T <= GEMV_MAX_T input rows:
 //   y[t][n] (=|+=) sum_k W[n][k] * h[t][k] (+ bias[n])

@@ -1,0 +1,54 @@
+// Persistent single-kernel decode step (internal to libqd).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+// Per-layer weight pointers, stored in device memory for the persistent kernel.
+struct LayerPtrs {
+  const uint16_t* wqkv;  // [(nq + 2 nkv) d][H] bf16
+  const float* bqkv;     // [(nq + 2 nkv) d] or null
+  const float* attn_norm;
+  const float* mlp_norm;
+  const float* q_norm;  // [d] or null (no QK-norm)
+  const float* k_norm;
+  const uint16_t* wo;  // [H][nq d]
+  const uint16_t* wg;  // [I][H]
+  const uint16_t* wu;  // [I][H]
+  const uint16_t* wd;  // [H][I]
+};
+
+// Everything the decode kernel needs that does not change from step to step.
+// The exchange buffers hold 64-bit words {f32 value | tag << 32}.
+struct PersistConst {
+  int L, H, nq, nkv, I, V, nqkv, max_pos;
+  float eps;
+  const uint16_t* embed;
+  const float* final_norm;
+  const LayerPtrs* layers;
+  float* Kc;  // [L][nkv][max_pos][128]
+  float* Vc;
+  const float* rope_cos;  // [max_pos][64]
+  const float* rope_sin;
+  uint64_t* X0;    // [H] residual entering a layer
+  uint64_t* X1;    // [H] residual after attention
+  uint64_t* QKV;   // [nqkv]
+  uint64_t* PART;  // [nq][S][130] split partials {m, l, o[128]}
+  uint64_t* O;     // [nq * 128] attention output
+  uint64_t* ACT;   // [I]
+  uint64_t* AMV;   // [grid] per-CU best logit
+  uint64_t* AMI;   // [grid] per-CU best id (bit pattern)
+  float* logits;   // [V]
+  float* xf_out;   // [H] final-normed row (optional)
+  DevState* st;
+  uint32_t* err;   // err[0] != 0: a wait timed out; the step was abandoned
+  uint64_t* trace; // optional [grid][1 + 2 * (5 L + 2)] real-time stamps of the last step
+};
+
+__host__ __device__ inline int persist_trace_slots(int L) { return 1 + 2 * (5 * L + 2); }
+
+size_t persist_smem_bytes();
+int persist_prepare(int G, int hseg);
+int persist_launch(const PersistConst* dev_const, int G, int hseg, int grid, int pos, uint32_t seq, int S, int chunk,
+                   hipStream_t s);

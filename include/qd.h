@@ -76,7 +76,11 @@ typedef struct {
   int32_t max_pos;        /* KV-cache capacity in positions */
   int32_t max_prefill;    /* largest n accepted by one qd_prefill call */
   int32_t lora_rank_max;  /* 0 disables LoRA; else the largest rank qd_set_lora accepts */
+  int32_t decode_path;    /* QD_DECODE_PERSISTENT (one cooperative kernel per decode step)
+                             or QD_DECODE_GRAPH (one kernel per operation, replayed as a hipGraph) */
 } qd_config;
+
+enum { QD_DECODE_PERSISTENT = 0, QD_DECODE_GRAPH = 1 };
 
 /* Weights: device pointers to bf16 (uint16 bit patterns), row-major [out, in].
  * Per-layer fields are HOST arrays of n_layers device pointers.  Shapes:
@@ -186,6 +190,19 @@ int qd_clear_lora(qd_handle* h);
 int qd_enable_capture(qd_handle* h, int32_t enable);
 int qd_get_capture(qd_handle* h, int32_t what, int32_t layer, float* out_host, size_t capacity_elems,
                    size_t* written_elems);
+
+/* Phase trace of the persistent decode step (diagnostics).  While enabled,
+ * every CU records 100 MHz real-time counter stamps: slot 0 = kernel start,
+ * then for phase p (per layer l: 5l = QKV, 5l+1 = attention, 5l+2 = o_proj,
+ * 5l+3 = gate/up, 5l+4 = down; then 5L = LM head, 5L+1 = final argmax)
+ * slot 1+2p = input ready and slot 2+2p = outputs written.  qd_get_phase_trace
+ * copies the stamps of the last decode step, laid out [cu][1 + 2(5L+2)], into
+ * out_host (uint64, capacity_elems elements) and reports the CU count.
+ * Errors: QD_E_STATE when the handle does not use the persistent decode step
+ * or no traced step has run; QD_E_ARG when capacity_elems is too small. */
+int qd_enable_phase_trace(qd_handle* h, int32_t enable);
+int qd_get_phase_trace(qd_handle* h, uint64_t* out_host, size_t capacity_elems, size_t* written_elems,
+                       int32_t* n_cu);
 
 /* Synchronise the stream and read the device-resident last token. */
 int qd_sync_token(qd_handle* h, int32_t* token_host);

@@ -73,6 +73,7 @@ def lockstep_greedy(dec, oracle, prompt, steps: int, check_every: int = 1, sampl
     for step in range(steps + 1):
         torch.cuda.synchronize()
         got_tok = int(tok_dev.item())
+        assert dec.sync_token() == got_tok  # also raises if a decode step was abandoned
         if sampling_params is None:
             o_tok = argmax_lowest(want)
         else:

@@ -30,9 +30,12 @@ def torch_cuda():
     return torch
 
 
-def make_decoder(torch_cuda, shape, max_prefill, lora_rank_max=0):
+PATHS = {"persistent": 0, "graph": 1}
+
+
+def make_decoder(torch_cuda, shape, max_prefill, lora_rank_max=0, path="persistent"):
     import decoder_only_token_amd as qd
-    cfg = qd.make_config(shape, max_prefill=max_prefill, lora_rank_max=lora_rank_max)
+    cfg = qd.make_config(shape, max_prefill=max_prefill, lora_rank_max=lora_rank_max, decode_path=PATHS[path])
     return qd.Decoder(cfg, torch_cuda.cuda.current_stream().cuda_stream)
 
 
@@ -43,15 +46,16 @@ def assert_records(recs, max_forced=0):
     assert len(forced) <= max_forced, f"token mismatches (near-ties) at {[(r.step, r.gpu_token, r.oracle_token) for r in forced]}"
 
 
+@pytest.mark.parametrize("path", ["persistent", "graph"])
 @pytest.mark.parametrize("random_gains", [False, True])
-def test_tiny_prefill_and_decode(torch_cuda, random_gains):
+def test_tiny_prefill_and_decode(torch_cuda, random_gains, path):
     """8-token prompt then 16 greedy steps on the 2-layer tiny model; every step checked."""
     wl = synth.WORKLOADS["tiny"]
     shape = wl.shape
-    log(f"tiny random_gains={random_gains}")
+    log(f"tiny random_gains={random_gains} path={path}")
     w = synth.make_weights(shape, random_gains=random_gains)
     oracle = OracleModel(shape, w)
-    dec = make_decoder(torch_cuda, shape, wl.max_prefill)
+    dec = make_decoder(torch_cuda, shape, wl.max_prefill, path=path)
     dw = to_device(w)
     torch_cuda.cuda.synchronize()
     dec.load_weights(dw)
@@ -118,11 +122,12 @@ def test_tiny_errors_leave_state_unchanged(torch_cuda):
     assert dec.position == 2
 
 
-def test_tiny_runs_are_bit_identical(torch_cuda):
+@pytest.mark.parametrize("path", ["persistent", "graph"])
+def test_tiny_runs_are_bit_identical(torch_cuda, path):
     import torch
     shape = synth.TINY
     w = synth.make_weights(shape, seed=8)
-    dec = make_decoder(torch_cuda, shape, 16)
+    dec = make_decoder(torch_cuda, shape, 16, path=path)
     dw = to_device(w)
     torch_cuda.cuda.synchronize()
     dec.load_weights(dw)
@@ -159,13 +164,14 @@ def test_tiny_prefill_equals_sequential_decode(torch_cuda):
 
 
 @pytest.mark.slow
-def test_qwen3_06b_prompt5_decode128(torch_cuda):
+@pytest.mark.parametrize("path", ["persistent", "graph"])
+def test_qwen3_06b_prompt5_decode128(torch_cuda, path):
     """The Qwen3-0.6B-shaped workload: 5-token prompt, 128 greedy decode steps, every step checked."""
     wl = synth.WORKLOADS["qwen3-0.6b"]
     shape = wl.shape
-    log("qwen3-0.6b: drawing weights")
+    log(f"qwen3-0.6b path={path}: drawing weights")
     w = synth.make_weights(shape)
-    dec = make_decoder(torch_cuda, shape, wl.max_prefill)
+    dec = make_decoder(torch_cuda, shape, wl.max_prefill, path=path)
     dw = to_device(w)
     torch_cuda.cuda.synchronize()
     dec.load_weights(dw)
