@@ -89,7 +89,7 @@ struct qd_handle {
   PersistConst* pconst = nullptr;  // device copy
   LayerPtrs* layer_ptrs = nullptr; // device array [L]
   uint64_t *X0 = nullptr, *X1 = nullptr, *QKVx = nullptr, *PART = nullptr, *Ox = nullptr, *ACT = nullptr;
-  uint64_t *AMV = nullptr, *AMI = nullptr;
+  uint64_t* AM = nullptr;
   uint32_t* err_dev = nullptr;
   bool failed = false;  // a decode step was abandoned; needs qd_reset_kv
   PersistConst pc_host{};
@@ -167,7 +167,7 @@ int validate_config(const qd_config* c, std::string& why) {
   if (c->decode_path != QD_DECODE_PERSISTENT && c->decode_path != QD_DECODE_GRAPH) { why = "unknown decode_path"; return QD_E_ARG; }
   if (c->decode_path == QD_DECODE_PERSISTENT) {
     if (c->hidden != 1024 && c->hidden != 2048) { why = "the persistent decode step needs hidden 1024 or 2048"; return QD_E_ARG; }
-    if (c->intermediate + c->hidden > 16384 || c->n_q_heads * c->head_dim > 8192) { why = "model too wide for the persistent decode step"; return QD_E_ARG; }
+    if (c->intermediate > 11264 || c->n_q_heads * c->head_dim > 11264) { why = "model too wide for the persistent decode step"; return QD_E_ARG; }
   }
   return QD_OK;
 }
@@ -338,21 +338,23 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     h->hseg = c.hidden / 512;
     const int G = c.n_q_heads / c.n_kv_heads;
     if (persist_prepare(G, h->hseg) != 0) return fail(h->set_err(QD_E_HIP, "persistent decode kernel unavailable"));
-    if (2 * ((c.intermediate + h->grid - 1) / h->grid) > 128 || (qkv_rows(c) + h->grid - 1) / h->grid > 128)
-      return fail(h->set_err(QD_E_ARG, "too many rows per CU for the persistent decode step"));
+    if ((c.hidden + h->grid - 1) / h->grid > 64)
+      return fail(h->set_err(QD_E_ARG, "too many hidden rows per CU for the persistent decode step"));
+    if (c.hidden < h->grid || c.intermediate < h->grid || qkv_rows(c) < h->grid || c.vocab < h->grid)
+      return fail(h->set_err(QD_E_ARG, "the persistent decode step needs at least one row of every projection per CU"));
     const size_t smax = (size_t)h->grid / c.n_kv_heads;
     if ((rc = dev_alloc(h, &h->X0, H)) || (rc = dev_alloc(h, &h->X1, H)) ||
         (rc = dev_alloc(h, &h->QKVx, (size_t)qkv_rows(c))) ||
         (rc = dev_alloc(h, &h->PART, (size_t)c.n_q_heads * smax * (d + 2))) ||
         (rc = dev_alloc(h, &h->Ox, (size_t)c.n_q_heads * d)) || (rc = dev_alloc(h, &h->ACT, I)) ||
-        (rc = dev_alloc(h, &h->AMV, (size_t)h->grid)) || (rc = dev_alloc(h, &h->AMI, (size_t)h->grid)) ||
+        (rc = dev_alloc(h, &h->AM, (size_t)2 * h->grid)) ||
         (rc = dev_alloc(h, &h->err_dev, 4)) || (rc = dev_alloc(h, &h->pconst, 1)) ||
         (rc = dev_alloc(h, &h->layer_ptrs, (size_t)c.n_layers)))
       return fail(rc);
     // tags start at 0; every step uses seq >= 1, so stale words never match
     if (hipMemset(h->X0, 0, H * 8) || hipMemset(h->X1, 0, H * 8) || hipMemset(h->QKVx, 0, qkv_rows(c) * 8) ||
         hipMemset(h->PART, 0, (size_t)c.n_q_heads * smax * (d + 2) * 8) || hipMemset(h->Ox, 0, c.n_q_heads * d * 8) ||
-        hipMemset(h->ACT, 0, I * 8) || hipMemset(h->AMV, 0, h->grid * 8) || hipMemset(h->AMI, 0, h->grid * 8) ||
+        hipMemset(h->ACT, 0, I * 8) || hipMemset(h->AM, 0, h->grid * 16) ||
         hipMemset(h->err_dev, 0, 16))
       return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
   }
@@ -380,7 +382,7 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
       return h->set_err(QD_E_ARG, "NULL pointer in layer " + std::to_string(l));
   }
   const size_t H = c.hidden, d = c.head_dim, I = c.intermediate, nq = c.n_q_heads, nkv = c.n_kv_heads;
-  const size_t NQKV = qkv_rows(c);
+  const size_t NQKV = qkv_rows(c), G = nq / nkv;
   hipStream_t s = h->stream;
   int rc;
   auto widen = [&](const void* src, float* dst, size_t n) {
@@ -401,9 +403,16 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
   widen(w->final_norm, h->final_norm, H);
   for (int l = 0; l < c.n_layers; ++l) {
     Layer& L = h->layers[l];
-    HIP_TRY(h, hipMemcpyAsync(L.wqkv, w->wq[l], nq * d * H * 2, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, hipMemcpyAsync(L.wqkv + nq * d * H, w->wk[l], nkv * d * H * 2, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, hipMemcpyAsync(L.wqkv + (nq + nkv) * d * H, w->wv[l], nkv * d * H * 2, hipMemcpyDeviceToDevice, s));
+    // fused q|k|v rows, group-major: [kv head g][q heads g*G .. g*G+G-1 | k_g | v_g] x d rows
+    for (size_t g = 0; g < nkv; ++g) {
+      uint16_t* dst = L.wqkv + g * (G + 2) * d * H;
+      HIP_TRY(h, hipMemcpyAsync(dst, (const uint16_t*)w->wq[l] + g * G * d * H, G * d * H * 2,
+                                hipMemcpyDeviceToDevice, s));
+      HIP_TRY(h, hipMemcpyAsync(dst + G * d * H, (const uint16_t*)w->wk[l] + g * d * H, d * H * 2,
+                                hipMemcpyDeviceToDevice, s));
+      HIP_TRY(h, hipMemcpyAsync(dst + (G + 1) * d * H, (const uint16_t*)w->wv[l] + g * d * H, d * H * 2,
+                                hipMemcpyDeviceToDevice, s));
+    }
     HIP_TRY(h, hipMemcpyAsync(L.wo, w->wo[l], H * nq * d * 2, hipMemcpyDeviceToDevice, s));
     HIP_TRY(h, hipMemcpyAsync(L.wg, w->w_gate[l], I * H * 2, hipMemcpyDeviceToDevice, s));
     HIP_TRY(h, hipMemcpyAsync(L.wu, w->w_up[l], I * H * 2, hipMemcpyDeviceToDevice, s));
@@ -415,9 +424,12 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
       widen(w->k_norm[l], L.k_norm, d);
     }
     if (c.qkv_bias) {
-      widen(w->bq[l], L.bqkv, nq * d);
-      widen(w->bk[l], L.bqkv + nq * d, nkv * d);
-      widen(w->bv[l], L.bqkv + (nq + nkv) * d, nkv * d);
+      for (size_t g = 0; g < nkv; ++g) {
+        float* dst = L.bqkv + g * (G + 2) * d;
+        widen((const uint16_t*)w->bq[l] + g * G * d, dst, G * d);
+        widen((const uint16_t*)w->bk[l] + g * d, dst + G * d, d);
+        widen((const uint16_t*)w->bv[l] + g * d, dst + (G + 1) * d, d);
+      }
     }
   }
   HIP_TRY(h, hipGetLastError());
@@ -433,7 +445,7 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
     pc.embed = h->embed; pc.final_norm = h->final_norm; pc.layers = h->layer_ptrs;
     pc.Kc = h->Kc; pc.Vc = h->Vc; pc.rope_cos = h->rope_cos; pc.rope_sin = h->rope_sin;
     pc.X0 = h->X0; pc.X1 = h->X1; pc.QKV = h->QKVx; pc.PART = h->PART; pc.O = h->Ox; pc.ACT = h->ACT;
-    pc.AMV = h->AMV; pc.AMI = h->AMI; pc.logits = h->logits; pc.xf_out = nullptr; pc.st = h->st; pc.err = h->err_dev;
+    pc.AM = h->AM; pc.logits = h->logits; pc.xf_out = nullptr; pc.st = h->st; pc.err = h->err_dev;
     pc.trace = h->trace_on ? h->trace : nullptr;
     h->pc_host = pc;
     HIP_TRY(h, hipMemcpyAsync(h->layer_ptrs, lp.data(), lp.size() * sizeof(LayerPtrs), hipMemcpyHostToDevice, s));
@@ -573,8 +585,10 @@ int qd_enable_phase_trace(qd_handle* h, int32_t enable) {
   if (!h->persistent) return h->set_err(QD_E_STATE, "phase trace needs the persistent decode step");
   if (!h->weights) return h->set_err(QD_E_STATE, "weights not loaded");
   if (enable && !h->trace) {
-    int rc = dev_alloc(h, &h->trace, (size_t)h->grid * persist_trace_slots(h->cfg.n_layers));
+    const size_t n = (size_t)h->grid * persist_trace_slots(h->cfg.n_layers);
+    int rc = dev_alloc(h, &h->trace, n);
     if (rc) return rc;
+    HIP_TRY(h, hipMemset(h->trace, 0, n * 8));
   }
   h->trace_on = enable != 0;
   h->pc_host.trace = h->trace_on ? h->trace : nullptr;

@@ -302,7 +302,8 @@ void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* pa
 // Per-head QK-RMSNorm, RoPE and the KV-cache write for T rows at positions
 // pos .. pos+T-1 (pos read from the device state).
 // "flashmoon demo/README.md", decode invariants: RoPE is applied as K is
-// written, so the cache holds rotated keys.  "Failed Star / fs" block figure:
+// written, so the cache holds rotated keys.  The fused projection rows are
+// group-major: [kv head g][q heads of g | k_g | v_g].  "Failed Star / fs" block figure:
 // QK-norm comes before RoPE.  Pairs are (j, j + d/2).
 // grid (T, nq + nkv), block d/2 threads (one per rotation pair).
 __global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, int nkv, int d,
@@ -314,8 +315,11 @@ __global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, i
   const int pos = st->pos + t;
   const float* row = qkv + (size_t)t * ldqkv;
   const bool is_q = head < nq;
-  const int g = head - nq;
-  const float* src = is_q ? row + head * d : row + nq * d + g * d;
+  const int G = nq / nkv;
+  const int g = is_q ? head / G : head - nq;  // kv group of this head
+  // group-major rows: [kv head g][q heads g*G .. g*G+G-1 | k_g | v_g] x d
+  const float* grp = row + (size_t)g * (G + 2) * d;
+  const float* src = is_q ? grp + (head % G) * d : grp + G * d;
   float a = src[j], b = src[j + half];
   const float* gain = is_q ? qn : kn;
   if (gain) {
@@ -342,7 +346,7 @@ __global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, i
     float* kr = Kc + ((size_t)g * max_pos + pos) * d;
     kr[j] = ra;
     kr[j + half] = rb;
-    const float* vsrc = row + (nq + nkv) * d + g * d;
+    const float* vsrc = grp + (G + 1) * d;
     float* vr = Vc + ((size_t)g * max_pos + pos) * d;
     vr[j] = vsrc[j];
     vr[j + half] = vsrc[j + half];

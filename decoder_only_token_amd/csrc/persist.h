@@ -37,16 +37,20 @@ struct PersistConst {
   uint64_t* PART;  // [nq][S][130] split partials {m, l, o[128]}
   uint64_t* O;     // [nq * 128] attention output
   uint64_t* ACT;   // [I]
-  uint64_t* AMV;   // [grid] per-CU best logit
-  uint64_t* AMI;   // [grid] per-CU best id (bit pattern)
+  uint64_t* AM;    // [grid][2] per-CU {best logit, best id (bit pattern)}
   float* logits;   // [V]
   float* xf_out;   // [H] final-normed row (optional)
   DevState* st;
   uint32_t* err;   // err[0] != 0: a wait timed out; the step was abandoned
-  uint64_t* trace; // optional [grid][1 + 2 * (5 L + 2)] real-time stamps of the last step
+  uint64_t* trace; // optional [grid][(5 L + 2) * 8] real-time stamps of the last step
 };
 
-__host__ __device__ inline int persist_trace_slots(int L) { return 1 + 2 * (5 * L + 2); }
+// Trace stamps per phase (100 MHz real-time counter), per CU, by thread 0:
+//   0 starts polling the phase input       1 the input is in LDS (after the barrier)
+//   3 finished its dot products            5 finished the phase (outputs written)
+//   7 kernel start (phase 0 only)          2, 4, 6 unused
+constexpr int kTraceSlots = 8;
+__host__ __device__ inline int persist_trace_slots(int L) { return (5 * L + 2) * kTraceSlots; }
 
 size_t persist_smem_bytes();
 int persist_prepare(int G, int hseg);

@@ -192,12 +192,14 @@ int qd_get_capture(qd_handle* h, int32_t what, int32_t layer, float* out_host, s
                    size_t* written_elems);
 
 /* Phase trace of the persistent decode step (diagnostics).  While enabled,
- * every CU records 100 MHz real-time counter stamps: slot 0 = kernel start,
- * then for phase p (per layer l: 5l = QKV, 5l+1 = attention, 5l+2 = o_proj,
- * 5l+3 = gate/up, 5l+4 = down; then 5L = LM head, 5L+1 = final argmax)
- * slot 1+2p = input ready and slot 2+2p = outputs written.  qd_get_phase_trace
- * copies the stamps of the last decode step, laid out [cu][1 + 2(5L+2)], into
- * out_host (uint64, capacity_elems elements) and reports the CU count.
+ * every CU records 100 MHz real-time counter stamps, 8 slots per phase p
+ * (per layer l: 5l = QKV, 5l+1 = attention, 5l+2 = o_proj, 5l+3 = gate/up,
+ * 5l+4 = down; then 5L = LM head, 5L+1 = final argmax on CU 0): slot 8p+0 =
+ * starts waiting for the phase input, 8p+1 = input ready, 8p+3 = dot products
+ * done, 8p+5 = phase outputs written; slot 7 = kernel start; other slots are
+ * left zero.  qd_get_phase_trace copies the stamps of the last decode step,
+ * laid out [cu][8 (5L+2)], into out_host (uint64, capacity_elems elements)
+ * and reports the CU count.
  * Errors: QD_E_STATE when the handle does not use the persistent decode step
  * or no traced step has run; QD_E_ARG when capacity_elems is too small. */
 int qd_enable_phase_trace(qd_handle* h, int32_t enable);
