@@ -31,10 +31,72 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen3-0.6b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-steps", type=int, default=8)
+    ap.add_argument("--cpu-sample-steps", type=int, default=128)
     ap.add_argument("--path", choices=["persistent", "graph"], default="persistent",
                     help="decode step as one persistent kernel, or as per-operation kernels in a hipGraph")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 launches): the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+# Sources of the persistent decode kernel: HBM traffic measured with counters
+# is reported only while these are unchanged since the counters were taken.
+KERNEL_SOURCES = ["decoder_only_token_amd/csrc/persist.hip", "decoder_only_token_amd/csrc/persist.h",
+                  "decoder_only_token_amd/csrc/common.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the persistent decode kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor),
+    or None when there is none for this workload or the kernel has changed since."""
+    path = os.path.join(ROOT, "profiles", f"k_decode_persistent.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib: int):
+    import torch
+    n = mib * 1024 * 1024 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4, "launches": 5}), flush=True)
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
 
 
 def cpu_baseline(wl, weights, prompt, n_steps):
@@ -52,11 +114,11 @@ def cpu_baseline(wl, weights, prompt, n_steps):
         logits = m.forward([argmax_lowest(logits)], cache, logits_rows="last")[-1]
         toks += 1
     dt = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0))
+    cores = blas_threads()
     return {"value": toks / dt, "unit": "tok/s", "cores": cores, "kind": "oracle",
             "sample": f"{wl.name}: float64 numpy oracle, prefill {len(prompt)} tokens + {n_steps} greedy decode "
                       f"steps with its own KV cache ({toks} tokens in {dt:.1f} s; weight widening {t_build:.1f} s "
-                      f"not counted); BLAS threads = all {cores} host cores"}
+                      f"not counted); {cores} BLAS threads"}
 
 
 def main():
@@ -64,6 +126,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     import numpy as np
     import torch
     import synth
@@ -126,6 +191,7 @@ def main():
                     for i in range(n_dec))
     decode_step_us = decode_ms * 1e3 / n_dec
     achieved = dec_bytes / n_dec / (decode_step_us * 1e-6) / 1e9
+    traffic = measured_traffic(wl.name) if args.path == "persistent" else None
     out = {
         "metric": "decode tok/s + achieved HBM GB/s (% of peak); prefill tok/s, 1 MI355X",
         "value": round(value, 2),
@@ -149,7 +215,7 @@ def main():
         "prefill_ms": round(prefill_ms, 3),
         "decode_hbm_gbs_effective": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": ("k_decode_persistent (one launch = one decode step)" if args.path == "persistent"
                                 else "decode step (captured graph of per-operation kernels)") +
                                "; algorithmic bytes = weights + KV read + KV write"},

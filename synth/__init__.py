@@ -86,9 +86,16 @@ WORKLOADS: Dict[str, Workload] = {
 def bf16_round(a: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round-to-nearest-even (input preparation only)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    u = a.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)  # wraps only for NaN bit patterns, fixed below
+    r >>= 16
+    out = r.astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)  # keep NaN a (quiet) NaN
+    return out
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
