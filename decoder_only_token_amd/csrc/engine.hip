@@ -74,6 +74,8 @@ struct qd_handle {
   float* logits = nullptr;  // [V]
   float* pval = nullptr;
   int32_t* pidx = nullptr;
+  float* spv = nullptr;      // sampling: per-slice sorted top-k lists
+  int32_t* spi = nullptr;
   int32_t* tokens_dev = nullptr;  // [max_prefill]
   int32_t* tokens_pinned = nullptr;
   DevState* st = nullptr;
@@ -272,7 +274,22 @@ int copy_outputs(qd_handle* h, float* logits_dev, int32_t* token_dev) {
 int check_sampling(qd_handle* h, const qd_sampling* sp) {
   if (!sp) return QD_OK;
   if (sp->struct_size != sizeof(qd_sampling)) return h->set_err(QD_E_ABI, "qd_sampling.struct_size mismatch");
-  if (sp->temperature > 0.f) return h->set_err(QD_E_ARG, "sampling not supported by this build");
+  if (!(sp->temperature <= 0.f) && !(sp->temperature > 0.f && std::isfinite(sp->temperature)))
+    return h->set_err(QD_E_ARG, "temperature must be finite");
+  if (sp->temperature <= 0.f) return QD_OK;
+  if (sp->top_k < 1 || sp->top_k > 64) return h->set_err(QD_E_ARG, "top_k must be in [1, 64]");
+  if (!sample_supported(h->cfg.vocab, sp->top_k)) return h->set_err(QD_E_ARG, "top_k too large for this vocabulary");
+  if (!(sp->top_p > 0.f && sp->top_p <= 1.f)) return h->set_err(QD_E_ARG, "top_p must be in (0, 1]");
+  return QD_OK;
+}
+
+// After the greedy pass has written the logits and counted the token: replace
+// its choice by a draw when sampling is asked for (top_k == 1 is greedy).
+int maybe_sample(qd_handle* h, const qd_sampling* sp) {
+  if (!sp || sp->temperature <= 0.f || sp->top_k == 1) return QD_OK;
+  launch_sample(h->stream, h->logits, h->cfg.vocab, sp->top_k, sp->temperature, sp->top_p, sp->seed, h->spv, h->spi,
+                h->st, nullptr);
+  HIP_TRY(h, hipGetLastError());
   return QD_OK;
 }
 
@@ -324,11 +341,15 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
       (rc = dev_alloc(h, &h->part, h->part_floats)) || (rc = dev_alloc(h, &h->logits, (size_t)c.vocab)) ||
       (rc = dev_alloc(h, &h->pval, (size_t)lmhead_blocks(c.vocab))) ||
       (rc = dev_alloc(h, &h->pidx, (size_t)lmhead_blocks(c.vocab))) ||
+      (rc = dev_alloc(h, &h->spv, (size_t)sample_lists(c.vocab) * 64)) ||
+      (rc = dev_alloc(h, &h->spi, (size_t)sample_lists(c.vocab) * 64)) ||
       (rc = dev_alloc(h, &h->tokens_dev, rows)) || (rc = dev_alloc(h, &h->st, 1)))
     return fail(rc);
   if (hipHostMalloc((void**)&h->tokens_pinned, rows * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
     return fail(h->set_err(QD_E_OOM, "hipHostMalloc failed"));
   if ((rc = build_rope_tables(h))) return fail(rc);
+  if (sample_supported(c.vocab, 1) && sample_prepare(c.vocab, c.vocab < 64 ? c.vocab : 64) != 0)
+    return fail(h->set_err(QD_E_HIP, "sampling kernel unavailable"));
   if (c.decode_path == QD_DECODE_PERSISTENT) {
     h->persistent = true;
     int ncu = 0;
@@ -486,6 +507,7 @@ int qd_prefill(qd_handle* h, const int32_t* tokens_host, int32_t n, const qd_sam
                             h->stream));
   enqueue_forward(h, n, h->tokens_dev, h->capture_on);
   HIP_TRY(h, hipGetLastError());
+  if ((rc = maybe_sample(h, sampling))) return rc;
   h->pos += n;
   h->have_token = true;
   h->cap_rows = h->capture_on ? n : 0;
@@ -511,6 +533,7 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
     const int G = h->cfg.n_q_heads / h->cfg.n_kv_heads;
     int e = persist_launch(h->pconst, G, h->hseg, h->grid, h->pos, h->seq, S, chunk, h->stream);
     if (e != 0) return h->set_err(QD_E_HIP, "persistent decode launch failed: " + std::to_string(e));
+    if ((rc = maybe_sample(h, sampling))) return rc;
     h->pos += 1;
     h->traced_step = h->trace_on;
     return copy_outputs(h, logits_dev, token_dev);
@@ -525,6 +548,7 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
     HIP_TRY(h, hipGraphInstantiate(&h->decode_exec, g, nullptr, nullptr, 0));
   }
   HIP_TRY(h, hipGraphLaunch(h->decode_exec, h->stream));
+  if ((rc = maybe_sample(h, sampling))) return rc;
   h->pos += 1;
   return copy_outputs(h, logits_dev, token_dev);
 }

@@ -33,3 +33,11 @@ void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq
 void launch_attention(hipStream_t s, const float* q, int T, int nq, int nkv, int d, const float* Kc, const float* Vc,
                       int max_pos, const DevState* st, int chunk, int S, float* part, float* o_out, int ldo,
                       int row0);
+
+// Top-k / temperature / top-p sampling over the logits (sample.hip); the token
+// goes to the device step state, which the greedy pass has already advanced.
+int sample_lists(int V);
+bool sample_supported(int V, int K);
+int sample_prepare(int V, int K);
+void launch_sample(hipStream_t s, const float* logits, int V, int K, float temperature, float top_p, uint64_t seed,
+                   float* part_val, int32_t* part_idx, DevState* st, int32_t* token_out);

@@ -57,7 +57,7 @@ class StepRecord:
 
 
 def lockstep_greedy(dec, oracle, prompt, steps: int, check_every: int = 1, sampling=None, sampling_params=None,
-                    log=None) -> List[StepRecord]:
+                    log=None, want_log: Optional[Dict] = None) -> List[StepRecord]:
     """Prefill `prompt`, then `steps` decode steps, comparing every checked step."""
     import torch
     from oracle import argmax_lowest, sample_top_k_top_p, uniform_for_step
@@ -79,6 +79,8 @@ def lockstep_greedy(dec, oracle, prompt, steps: int, check_every: int = 1, sampl
         else:
             T, k, p, seed = sampling_params
             o_tok = sample_top_k_top_p(want, T, k, p, uniform_for_step(seed, step))
+        if want_log is not None:
+            want_log[step] = want
         ok, ratio, nbad = True, 0.0, 0
         if step % check_every == 0 or step == steps:
             got = logits_dev.cpu().numpy()
@@ -95,3 +97,27 @@ def lockstep_greedy(dec, oracle, prompt, steps: int, check_every: int = 1, sampl
             dec.decode_step(sampling=sampling, logits_out=logits_dev, token_out=tok_dev)
         want = oracle.forward([o_tok], cache, logits_rows="last")[-1]
     return recs
+
+
+def sampling_mismatch_explained(want: np.ndarray, params, step: int, got_tok: int, delta: float = 1e-3) -> bool:
+    """Whether a sampled token that differs from the oracle's is still a correct draw.
+
+    The GPU draws from its own f32 logits, which may differ from the oracle's
+    within the logit tolerance.  A different token is accepted when moving the
+    uniform by at most `delta` (a CDF boundary between the two tokens), or
+    moving the logits by at most the tolerance at the kept-set cut, gives it.
+    """
+    from oracle import sample_top_k_top_p, uniform_for_step
+    T, k, p, seed = params
+    u = uniform_for_step(seed, step)
+    for uu in (max(0.0, u - delta), min(1.0 - 1e-12, u + delta)):
+        if sample_top_k_top_p(want, T, k, p, uu) == got_tok:
+            return True
+    # a token at the edge of the kept set: its logit within tolerance of the
+    # k-th largest, and the draw landing past the end of the kept set
+    order = np.lexsort((np.arange(want.shape[0]), -want))
+    kth = float(want[order[min(k, want.shape[0]) - 1]])
+    tol = ATOL + RTOL * abs(kth)
+    if abs(float(want[got_tok]) - kth) <= tol:
+        return True
+    return False

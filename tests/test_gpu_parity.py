@@ -13,7 +13,7 @@ import pytest
 import synth
 from oracle import OracleModel
 
-from gpu_util import lockstep_greedy, logits_within_tol, to_device
+from gpu_util import lockstep_greedy, logits_within_tol, sampling_mismatch_explained, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -181,3 +181,85 @@ def test_qwen3_06b_prompt5_decode128(torch_cuda, path):
     prompt = synth.make_prompt(shape.vocab, wl.prompt_len)
     recs = lockstep_greedy(dec, oracle, prompt, wl.decode_steps, log=log)
     assert_records(recs, max_forced=2)
+
+
+@pytest.mark.parametrize("path", ["persistent", "graph"])
+def test_tiny_sampling_topk_topp(torch_cuda, path):
+    """T = 0.7, top-k 40, top-p 0.9 with a fixed seed on the tiny model, 24 steps.
+
+    Every step: logits within tolerance, and the drawn token equal to the
+    oracle's draw with the same uniform, except where the draw sits within
+    1e-3 of a CDF boundary or the token is at the top-k cut (then the oracle's
+    token is forced and the case is counted)."""
+    import decoder_only_token_amd as qd
+    shape = synth.TINY
+    params = (0.7, 40, 0.9, 1234567)
+    log(f"tiny sampling path={path}")
+    w = synth.make_weights(shape, seed=11)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 16, path=path)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    sp = qd.make_sampling(*params)
+    prompt = synth.make_prompt(shape.vocab, 8, seed=12)
+    wants = {}
+
+    def keep(msg):
+        log(msg)
+
+    recs = lockstep_greedy(dec, oracle, prompt, 24, sampling=sp, sampling_params=params, log=keep,
+                           want_log=wants)
+    bad = [r for r in recs if r.n_bad]
+    assert not bad, [(r.step, r.max_err_ratio) for r in bad]
+    distinct = {r.oracle_token for r in recs}
+    assert len(distinct) > 3, "sampling produced too few distinct tokens to exercise the draw"
+    for r in recs:
+        if r.forced:
+            assert sampling_mismatch_explained(wants[r.step], params, r.step, r.gpu_token), \
+                f"step {r.step}: gpu drew {r.gpu_token}, oracle {r.oracle_token}"
+    assert sum(r.forced for r in recs) <= 2
+
+
+@pytest.mark.parametrize("top_k", [1, 64])
+def test_tiny_sampling_limits(torch_cuda, top_k):
+    """top_k = 1 is greedy; a tiny top_p keeps only the best token (greedy too)."""
+    import torch
+    import decoder_only_token_amd as qd
+    shape = synth.TINY
+    w = synth.make_weights(shape, seed=13)
+    dec = make_decoder(torch_cuda, shape, 16)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = [3, 1, 4, 1, 5]
+    sp = qd.make_sampling(0.9, top_k, 1e-6, 99)
+    toks = []
+    for s in (None, sp):
+        dec.reset_kv()
+        out = torch.empty(1, dtype=torch.int32, device="cuda")
+        seq = []
+        dec.prefill(prompt, sampling=s, token_out=out)
+        seq.append(dec.sync_token())
+        for _ in range(6):
+            dec.decode_step(sampling=s, token_out=out)
+            seq.append(dec.sync_token())
+        toks.append(seq)
+    assert toks[0] == toks[1]
+
+
+def test_sampling_argument_errors(torch_cuda):
+    import decoder_only_token_amd as qd
+    shape = synth.TINY
+    dec = make_decoder(torch_cuda, shape, 16)
+    w = synth.make_weights(shape, seed=14)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    for bad in (qd.make_sampling(0.7, 0, 0.9, 1), qd.make_sampling(0.7, 65, 0.9, 1),
+                qd.make_sampling(0.7, 40, 0.0, 1), qd.make_sampling(0.7, 40, 1.5, 1),
+                qd.make_sampling(float("inf"), 40, 0.9, 1), qd.make_sampling(float("nan"), 40, 0.9, 1)):
+        with pytest.raises(qd.QdError) as e:
+            dec.prefill([1, 2], sampling=bad)
+        assert e.value.code == -1
+    assert dec.position == 0
