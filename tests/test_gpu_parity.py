@@ -263,3 +263,22 @@ def test_sampling_argument_errors(torch_cuda):
             dec.prefill([1, 2], sampling=bad)
         assert e.value.code == -1
     assert dec.position == 0
+
+
+@pytest.mark.parametrize("path", ["persistent", "graph"])
+def test_tiny_long_context_splits(torch_cuda, path):
+    """A 200-token prefill then 90 decode steps on the tiny model with a 512-position
+    cache: the decode attention runs with 2 and then 3 position splits (the split
+    boundary at 256 is crossed); logits checked every 10th step and the last."""
+    import dataclasses
+    shape = dataclasses.replace(synth.TINY, max_pos=512)
+    log(f"tiny long context path={path}")
+    w = synth.make_weights(shape, seed=21)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 256, path=path)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = synth.make_prompt(shape.vocab, 200, seed=22)
+    recs = lockstep_greedy(dec, oracle, prompt, 90, check_every=10, log=log)
+    assert_records(recs, max_forced=1)
