@@ -22,6 +22,7 @@
 namespace {
 
 constexpr int kAttnChunk = 64;  // cache positions per split-K attention block
+constexpr int kGemmMinRows = 16;  // prefills of at least this many rows use the matrix-core projections
 
 struct Layer {
   uint16_t* wqkv = nullptr;  // [(nq + 2 nkv) d, H]
@@ -69,6 +70,8 @@ struct qd_handle {
   float* q = nullptr;    // [rows][nq][d]
   float* o = nullptr;    // [rows][nq d]
   float* act = nullptr;  // [rows][I]
+  uint16_t* xh = nullptr;  // [rows][max(H, nq d, I)] bf16 halves of a projection input
+  uint16_t* xl = nullptr;
   float* part = nullptr; // attention partials
   size_t part_floats = 0;
   float* logits = nullptr;  // [V]
@@ -160,6 +163,11 @@ int validate_config(const qd_config* c, std::string& why) {
   if (G != 1 && G != 2 && G != 4 && G != 8) { why = "n_q_heads / n_kv_heads must be 1, 2, 4 or 8"; return QD_E_ARG; }
   if (c->hidden % 512 || (c->n_q_heads * c->head_dim) % 512) { why = "hidden and n_q_heads*head_dim must be multiples of 512"; return QD_E_ARG; }
   if (c->intermediate % 128) { why = "intermediate must be a multiple of 128"; return QD_E_ARG; }
+  if (c->max_prefill >= kGemmMinRows && (!gemm_supported(c->hidden) || !gemm_supported(c->intermediate) ||
+                                         !gemm_supported(c->n_q_heads * c->head_dim))) {
+    why = "hidden, intermediate and n_q_heads*head_dim must be multiples of 64 for batched prefill";
+    return QD_E_ARG;
+  }
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) { why = "rope_theta must be > 0 and rms_eps >= 0"; return QD_E_ARG; }
   if (c->tie_embeddings != 1) { why = "only tied embeddings are supported (tie_embeddings must be 1)"; return QD_E_ARG; }
   if (c->weight_format != QD_W_BF16) { why = "weight_format not supported by this build"; return QD_E_ARG; }
@@ -204,18 +212,83 @@ void free_all(qd_handle* h) {
   h->stream = nullptr;
 }
 
+void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows);
+void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows);
+
 // Enqueue the whole forward for T new rows whose ids are at `tok` (device),
 // at positions st->pos .. st->pos + T - 1, and choose the next token from the
 // last row.  Captures are written only when `capture` is set.
 void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
   const qd_config& c = h->cfg;
   hipStream_t s = h->stream;
-  const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, I = c.intermediate;
-  const int NQKV = qkv_rows(c);
-  const size_t layer_kv = (size_t)nkv * c.max_pos * d;
+  const int H = c.hidden;
   launch_embed(s, h->embed, tok, T, H, h->x);
   if (capture) (void)hipMemcpyAsync(h->cap, h->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice, s);
   const int att_rows = T == 1 ? 1 : attn_row_chunk(c);
+  if (T >= kGemmMinRows) {
+    enqueue_layers_gemm(h, T, capture, att_rows);
+  } else {
+    enqueue_layers_gemv(h, T, capture, att_rows);
+  }
+  float* xf_cap = capture ? h->cap + (size_t)(c.n_layers + 1) * c.max_prefill * H : nullptr;
+  launch_lmhead_bf16(s, h->embed, c.vocab, H, h->x + (size_t)(T - 1) * H, h->final_norm, c.rms_eps, h->logits,
+                     h->pval, h->pidx, xf_cap);
+  launch_argmax_final(s, h->pval, h->pidx, lmhead_blocks(c.vocab), h->st, T, nullptr);
+  if (capture)
+    (void)hipMemcpyAsync(xf_cap + H, h->logits, (size_t)c.vocab * 4, hipMemcpyDeviceToDevice, s);
+}
+
+// Attention for T new rows (shared by both projection paths).
+void enqueue_attention(qd_handle* h, int l, int T, int att_rows) {
+  const qd_config& c = h->cfg;
+  hipStream_t s = h->stream;
+  const int d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const size_t layer_kv = (size_t)nkv * c.max_pos * d;
+  const Layer& L = h->layers[l];
+  launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
+                    h->st, h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
+  if (T == 1) {
+    launch_attention(s, h->q, 1, nq, nkv, d, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, kAttnChunk,
+                     attn_splits(c.max_pos), h->part, h->o, nq * d, 0);
+  } else {
+    for (int t0 = 0; t0 < T; t0 += att_rows) {
+      const int tn = std::min(att_rows, T - t0);
+      const int S = attn_splits(h->pos + t0 + tn);
+      launch_attention(s, h->q + (size_t)t0 * nq * d, tn, nq, nkv, d, h->Kc + l * layer_kv, h->Vc + l * layer_kv,
+                       c.max_pos, h->st, kAttnChunk, S, h->part, h->o + (size_t)t0 * nq * d, nq * d, t0);
+    }
+  }
+}
+
+// Layers with the matrix-core projections (T >= kGemmMinRows).
+void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows) {
+  const qd_config& c = h->cfg;
+  hipStream_t s = h->stream;
+  const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, I = c.intermediate;
+  const int NQKV = qkv_rows(c);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const Layer& L = h->layers[l];
+    launch_split_rows(s, h->x, H, T, H, L.attn_norm, c.rms_eps, h->xh, h->xl);
+    launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, L.wqkv, nullptr, NQKV, L.bqkv, h->qkv, NQKV);
+    enqueue_attention(h, l, T, att_rows);
+    launch_split_rows(s, h->o, nq * d, T, nq * d, nullptr, 0.f, h->xh, h->xl);
+    launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.wo, nullptr, H, nullptr, h->x, H);
+    launch_split_rows(s, h->x, H, T, H, L.mlp_norm, c.rms_eps, h->xh, h->xl);
+    launch_gemm_hilo(s, GEMM_GATEUP, h->xh, h->xl, T, H, L.wg, L.wu, I, nullptr, h->act, I);
+    launch_split_rows(s, h->act, I, T, I, nullptr, 0.f, h->xh, h->xl);
+    launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, I, L.wd, nullptr, H, nullptr, h->x, H);
+    if (capture)
+      (void)hipMemcpyAsync(h->cap + (size_t)(l + 1) * c.max_prefill * H, h->x, (size_t)T * H * 4,
+                           hipMemcpyDeviceToDevice, s);
+  }
+}
+
+// Layers with the T-row GEMV projections (decode and short prefills).
+void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
+  const qd_config& c = h->cfg;
+  hipStream_t s = h->stream;
+  const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, I = c.intermediate;
+  const int NQKV = qkv_rows(c);
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = h->layers[l];
     for (int t0 = 0, tt = gemv_t_tile(H); t0 < T; t0 += tt) {
@@ -223,19 +296,7 @@ void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
       launch_gemv_bf16(s, L.wqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
                        h->qkv + (size_t)t0 * NQKV, NQKV, 0);
     }
-    launch_qk_rope_kv(s, h->qkv, NQKV, T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin, h->st,
-                      h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
-    if (T == 1) {
-      launch_attention(s, h->q, 1, nq, nkv, d, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st,
-                       kAttnChunk, attn_splits(c.max_pos), h->part, h->o, nq * d, 0);
-    } else {
-      for (int t0 = 0; t0 < T; t0 += att_rows) {
-        const int tn = std::min(att_rows, T - t0);
-        const int S = attn_splits(h->pos + t0 + tn);
-        launch_attention(s, h->q + (size_t)t0 * nq * d, tn, nq, nkv, d, h->Kc + l * layer_kv, h->Vc + l * layer_kv,
-                         c.max_pos, h->st, kAttnChunk, S, h->part, h->o + (size_t)t0 * nq * d, nq * d, t0);
-      }
-    }
+    enqueue_attention(h, l, T, att_rows);
     for (int t0 = 0, tt = gemv_t_tile(nq * d); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
       launch_gemv_bf16(s, L.wo, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
@@ -255,12 +316,6 @@ void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
       (void)hipMemcpyAsync(h->cap + (size_t)(l + 1) * c.max_prefill * H, h->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice,
                      s);
   }
-  float* xf_cap = capture ? h->cap + (size_t)(c.n_layers + 1) * c.max_prefill * H : nullptr;
-  launch_lmhead_bf16(s, h->embed, c.vocab, H, h->x + (size_t)(T - 1) * H, h->final_norm, c.rms_eps, h->logits,
-                     h->pval, h->pidx, xf_cap);
-  launch_argmax_final(s, h->pval, h->pidx, lmhead_blocks(c.vocab), h->st, T, nullptr);
-  if (capture)
-    (void)hipMemcpyAsync(xf_cap + H, h->logits, (size_t)c.vocab * 4, hipMemcpyDeviceToDevice, s);
 }
 
 int copy_outputs(qd_handle* h, float* logits_dev, int32_t* token_dev) {
@@ -338,6 +393,8 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
       (rc = dev_alloc(h, &h->rope_sin, (size_t)c.max_pos * d / 2)) || (rc = dev_alloc(h, &h->x, rows * H)) ||
       (rc = dev_alloc(h, &h->qkv, rows * qkv_rows(c))) || (rc = dev_alloc(h, &h->q, rows * c.n_q_heads * d)) ||
       (rc = dev_alloc(h, &h->o, rows * c.n_q_heads * d)) || (rc = dev_alloc(h, &h->act, rows * I)) ||
+      (rc = dev_alloc(h, &h->xh, rows * std::max(std::max(H, (size_t)c.n_q_heads * d), I))) ||
+      (rc = dev_alloc(h, &h->xl, rows * std::max(std::max(H, (size_t)c.n_q_heads * d), I))) ||
       (rc = dev_alloc(h, &h->part, h->part_floats)) || (rc = dev_alloc(h, &h->logits, (size_t)c.vocab)) ||
       (rc = dev_alloc(h, &h->pval, (size_t)lmhead_blocks(c.vocab))) ||
       (rc = dev_alloc(h, &h->pidx, (size_t)lmhead_blocks(c.vocab))) ||

@@ -1,0 +1,210 @@
+// Batched prefill projections on the matrix cores of gfx950.
+//
+// A prompt of T rows makes every projection a dense contraction
+// C[T, N] = X[T, K] W[N, K]^T ("Failed Star / fs — Forward pass → logits":
+// one [out, in] matrix per projection, applied to every row).  X is f32; W is
+// bf16.  X is split into two bf16 halves, X = Xh + Xl (Xh = X rounded to
+// bf16, Xl = the rounded remainder), and both are multiplied with W on the
+// matrix cores with f32 accumulation, so the product keeps about 16 bits of
+// X's mantissa instead of 8.  The RMSNorm of the rows (with its gains) is
+// applied before the split.
+//
+// Tiles: 128 rows of X by 128 output columns per 256-thread block, K in
+// steps of 64; each wave owns a 64 x 64 quarter as 4 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16.  The K-step tiles of Xh, Xl and W go through
+// padded LDS rows (144-byte stride: the 16 rows of a fragment read land on
+// distinct banks), and the next K-step is loaded into registers while the
+// current one is multiplied.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDR = BK + 8;  // padded LDS row (bf16): 144 bytes
+constexpr int kThreads = 256;
+
+// f32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One block per row: optional RMSNorm with gains, then the hi/lo split.
+__global__ __launch_bounds__(256) void k_split_rows(const float* __restrict__ x, int ldx, int K,
+                                                    const float* __restrict__ gain, float eps,
+                                                    uint16_t* __restrict__ xh, uint16_t* __restrict__ xl) {
+  __shared__ float red[8];
+  const int t = blockIdx.x;
+  const float* xr = x + (size_t)t * ldx;
+  float r = 1.0f;
+  if (gain) {
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < K; k += 256) ss += xr[k] * xr[k];
+    r = 1.0f / sqrtf(block_sum_256(ss, red) / (float)K + eps);
+  }
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const float v = gain ? xr[k] * r * gain[k] : xr[k];
+    const uint32_t h = bf16_rne(v);
+    const float rest = v - __uint_as_float(h << 16);
+    xh[(size_t)t * K + k] = (uint16_t)h;
+    xl[(size_t)t * K + k] = (uint16_t)bf16_rne(rest);
+  }
+}
+
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_GATEUP = 2 };
+
+// C tile of block (bm, bn).  EPI_STORE: C = acc (+ bias); EPI_ADD: C += acc;
+// EPI_GATEUP: the block's B rows are 64 gate rows and the same 64 up rows,
+// C[t][n] = SiLU(gate) * up.
+template <int EPI>
+__global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al,
+                                                        int T, int K, const uint16_t* __restrict__ B,
+                                                        const uint16_t* __restrict__ B2, int N,
+                                                        const float* __restrict__ bias, float* __restrict__ C,
+                                                        int ldc) {
+  __shared__ __align__(16) uint16_t sA[2][BM * LDR];  // [hi, lo]
+  __shared__ __align__(16) uint16_t sB[BN * LDR];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.x * BM;
+  const int n0 = blockIdx.y * (EPI == EPI_GATEUP ? BN / 2 : BN);
+
+  // global -> register staging: each tile is 128 rows x 8 chunks of 16 bytes,
+  // 4 chunks per thread (row = idx / 8, chunk = idx % 8)
+  u32x4 ra[2][4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
+      const int t = min(m0 + row, T - 1);
+      const size_t off = (size_t)t * K + k0 + ch * 8;
+      ra[0][j] = *reinterpret_cast<const u32x4*>(Ah + off);
+      ra[1][j] = *reinterpret_cast<const u32x4*>(Al + off);
+      int n;
+      const uint16_t* src;
+      if (EPI == EPI_GATEUP) {
+        n = min(n0 + (row & 63), N - 1);
+        src = row < 64 ? B : B2;
+      } else {
+        n = min(n0 + row, N - 1);
+        src = B;
+      }
+      rb[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)n * K + k0 + ch * 8));
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(&sA[0][row * LDR + ch * 8]) = ra[0][j];
+      *reinterpret_cast<u32x4*>(&sA[1][row * LDR + ch * 8]) = ra[1][j];
+      *reinterpret_cast<u32x4*>(&sB[row * LDR + ch * 8]) = rb[j];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // B rows of this wave's 4 column tiles
+  int brow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    brow[j] = EPI == EPI_GATEUP ? (j < 2 ? 0 : 64) + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16;
+
+  const int nk = K / BK;
+  gload(0);
+  sstore();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload((kt + 1) * BK);  // the next K-step flies during this one
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      // fragments: lane holds row (lane % 16), k = kk + (lane / 16) * 8 .. + 8
+      const int fr = lane & 15, fk = kk + (lane >> 4) * 8;
+      bf16x8 bh[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bh[j] = *reinterpret_cast<const bf16x8*>(&sB[(brow[j] + fr) * LDR + fk]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ar = wm * 64 + i * 16 + fr;
+        const bf16x8 a_hi = *reinterpret_cast<const bf16x8*>(&sA[0][ar * LDR + fk]);
+        const bf16x8 a_lo = *reinterpret_cast<const bf16x8*>(&sA[1][ar * LDR + fk]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, bh[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, bh[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+    if (kt + 1 < nk) {
+      __syncthreads();  // every wave is done with this K-step's tiles
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  // epilogue: acc[i][j] element e of lane is C[row 4 (lane / 16) + e][col lane % 16]
+  // of the (i, j) 16 x 16 tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+      if (t >= T) continue;
+      if (EPI == EPI_GATEUP) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wn * 32 + j * 16 + (lane & 15);
+          if (n < N) {
+            const float g = acc[i][j][e], u = acc[i][j + 2][e];
+            C[(size_t)t * ldc + n] = silu_f(g) * u;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * 64 + j * 16 + (lane & 15);
+          if (n < N) {
+            float* cp = C + (size_t)t * ldc + n;
+            if (EPI == EPI_ADD) {
+              *cp += acc[i][j][e];
+            } else {
+              *cp = acc[i][j][e] + (bias ? bias[n] : 0.f);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool gemm_supported(int K) { return K % BK == 0; }
+
+void launch_split_rows(hipStream_t s, const float* x, int ldx, int T, int K, const float* gain, float eps,
+                       uint16_t* xh, uint16_t* xl) {
+  hipLaunchKernelGGL(k_split_rows, dim3(T), dim3(256), 0, s, x, ldx, K, gain, eps, xh, xl);
+}
+
+void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
+                      const uint16_t* W2, int N, const float* bias, float* C, int ldc) {
+  const dim3 grid((T + BM - 1) / BM, epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN);
+  switch (epi) {
+    case EPI_STORE:
+      hipLaunchKernelGGL(k_gemm_hilo<EPI_STORE>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc);
+      break;
+    case EPI_ADD:
+      hipLaunchKernelGGL(k_gemm_hilo<EPI_ADD>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc);
+      break;
+    default:
+      hipLaunchKernelGGL(k_gemm_hilo<EPI_GATEUP>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc);
+      break;
+  }
+}

@@ -41,3 +41,13 @@ bool sample_supported(int V, int K);
 int sample_prepare(int V, int K);
 void launch_sample(hipStream_t s, const float* logits, int V, int K, float temperature, float top_p, uint64_t seed,
                    float* part_val, int32_t* part_idx, DevState* st, int32_t* token_out);
+
+// Batched prefill projections on the matrix cores (gemm.hip).  X rows are
+// split into bf16 hi/lo halves (after RMSNorm with gains when `gain` is set),
+// then C[T, N] = (Xh + Xl) W[N, K]^T with one of three epilogues.
+enum { GEMM_STORE = 0, GEMM_ADD = 1, GEMM_GATEUP = 2 };
+bool gemm_supported(int K);
+void launch_split_rows(hipStream_t s, const float* x, int ldx, int T, int K, const float* gain, float eps,
+                       uint16_t* xh, uint16_t* xl);
+void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
+                      const uint16_t* W2, int N, const float* bias, float* C, int ldc);

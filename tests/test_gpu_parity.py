@@ -282,3 +282,38 @@ def test_tiny_long_context_splits(torch_cuda, path):
     prompt = synth.make_prompt(shape.vocab, 200, seed=22)
     recs = lockstep_greedy(dec, oracle, prompt, 90, check_every=10, log=log)
     assert_records(recs, max_forced=1)
+
+
+@pytest.mark.parametrize("n", [16, 137])
+def test_tiny_batched_prefill_matrix_cores(torch_cuda, n):
+    """Prefills of >= 16 rows run the projections on the matrix cores (bf16 hi/lo
+    split of the inputs).  Every layer's output for every row, the final norm
+    and the logits are checked against the oracle; 137 rows leave a ragged
+    second row tile."""
+    import dataclasses
+    import decoder_only_token_amd as qd
+    shape = dataclasses.replace(synth.TINY, max_pos=256)
+    w = synth.make_weights(shape, seed=31, random_gains=True)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 160)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    dec.enable_capture(True)
+    prompt = synth.make_prompt(shape.vocab, n, seed=32)
+    log(f"batched prefill n={n}")
+    dec.prefill(prompt)
+    cap = {}
+    oracle.forward(prompt, capture=cap)
+    H = shape.hidden
+    for l in range(shape.n_layers):
+        got = dec.get_capture(qd.QD_CAP_LAYER_OUT, l, n * H).reshape(n, H)
+        np.testing.assert_allclose(got, cap["layer_out"][l], rtol=1e-3, atol=1e-3)
+    got = dec.get_capture(qd.QD_CAP_FINAL_NORM, 0, H)
+    np.testing.assert_allclose(got, cap["final_norm"][-1], rtol=1e-3, atol=1e-3)
+    got = dec.get_capture(qd.QD_CAP_LOGITS, 0, shape.vocab)
+    ok, ratio, nbad = logits_within_tol(got, cap["logits"][-1])
+    assert ok, (ratio, nbad)
+    # the next token continues from the batched cache
+    assert dec.sync_token() == int(np.argmax(cap["logits"][-1])) or \
+        cap["logits"][-1][dec.sync_token()] >= np.max(cap["logits"][-1]) - 4e-3
