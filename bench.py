@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_BF16_TFLOPS = 2500.0
 
 
 def parse():
@@ -31,6 +32,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen3-0.6b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-rows", type=int, default=512,
+                    help="also time one batched prefill of this many random tokens (0: skip)")
     ap.add_argument("--cpu-sample-steps", type=int, default=128)
     ap.add_argument("--path", choices=["persistent", "graph"], default="persistent",
                     help="decode step as one persistent kernel, or as per-operation kernels in a hipGraph")
@@ -121,6 +124,44 @@ def cpu_baseline(wl, weights, prompt, n_steps):
                       f"not counted); {cores} BLAS threads"}
 
 
+def measure_long_prefill(dec, stream, shape, wl, args):
+    """Time a batched prefill of args.prefill_rows seeded random tokens on the
+    same model (the projections run on the matrix cores).  FLOP counts are the
+    algorithmic ones: 2 per weight per row for the projections, plus the causal
+    attention products (2 * 2 * d per visible key per q head)."""
+    import numpy as np
+    import torch
+    import synth
+    n = args.prefill_rows
+    if n > wl.max_prefill or n > shape.max_pos:
+        return None
+    toks = synth.make_prompt(shape.vocab, n, seed=7)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    times = []
+    with torch.cuda.stream(stream):
+        for i in range(4):
+            dec.reset_kv()
+            a, b = ev(), ev()
+            a.record(stream)
+            dec.prefill(toks)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                times.append(a.elapsed_time(b))
+    dec.sync_token()
+    ms = float(np.median(times))
+    H, d, I, L = shape.hidden, shape.head_dim, shape.intermediate, shape.n_layers
+    nq, nkv = shape.n_q_heads, shape.n_kv_heads
+    lin = (nq * d + 2 * nkv * d) * H + H * nq * d + 2 * I * H + H * I
+    proj = 2.0 * n * lin * L
+    attn = 2.0 * 2.0 * d * nq * L * (n * (n + 1) / 2)
+    return {"rows": n, "ms": round(ms, 3), "tok_s": round(n / (ms * 1e-3), 1),
+            "projection_tflops": round(proj / (ms * 1e-3) / 1e12, 2),
+            "mfma_util_lower_bound": round(proj / (ms * 1e-3) / (MFMA_PEAK_BF16_TFLOPS * 1e12), 4),
+            "note": "whole prefill time (projections, attention, norms, LM head row); projection FLOPs "
+                    "counted once although the hi/lo input split issues each product twice"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -176,6 +217,7 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     dec.sync_token()  # raises if any decode step was abandoned
+    long_prefill = measure_long_prefill(dec, stream, shape, wl, args) if args.prefill_rows else None
     prefill_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
     decode_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
     ms_per_step = wall * 1e3 / args.steps
@@ -220,6 +262,8 @@ def main():
                                 else "decode step (captured graph of per-operation kernels)") +
                                "; algorithmic bytes = weights + KV read + KV write"},
     }
+    if long_prefill:
+        out["prefill_batched"] = long_prefill
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, weights, prompt, args.cpu_sample_steps)
     dec.close()

@@ -72,6 +72,9 @@ struct qd_handle {
   float* act = nullptr;  // [rows][I]
   uint16_t* xh = nullptr;  // [rows][max(H, nq d, I)] bf16 halves of a projection input
   uint16_t* xl = nullptr;
+  float* gws = nullptr;  // split-K workspace of the batched projections
+  size_t gws_floats = 0;
+  int ncu = 0;
   float* part = nullptr; // attention partials
   size_t part_floats = 0;
   float* logits = nullptr;  // [V]
@@ -182,6 +185,24 @@ int validate_config(const qd_config* c, std::string& why) {
   return QD_OK;
 }
 
+// Split-K workspace for the batched projections: the largest need over the
+// prefill lengths that use them and the four products of a layer.
+int alloc_gemm_workspace(qd_handle* h) {
+  const qd_config& c = h->cfg;
+  if (c.max_prefill < kGemmMinRows) return QD_OK;
+  size_t need = 0;
+  const int NQKV = qkv_rows(c);
+  // the need s(T) * T * N peaks at the end of each 128-row tile count
+  for (int T = std::min(128, c.max_prefill); T <= c.max_prefill; T = T < c.max_prefill ? std::min(T + 128, c.max_prefill) : T + 1) {
+    need = std::max(need, gemm_workspace_floats(T, c.hidden, NQKV, h->ncu));
+    need = std::max(need, gemm_workspace_floats(T, c.n_q_heads * c.head_dim, c.hidden, h->ncu));
+    need = std::max(need, gemm_workspace_floats(T, c.hidden, c.intermediate, h->ncu));
+    need = std::max(need, gemm_workspace_floats(T, c.intermediate, c.hidden, h->ncu));
+  }
+  h->gws_floats = need;
+  return need ? dev_alloc(h, &h->gws, need) : QD_OK;
+}
+
 int build_rope_tables(qd_handle* h) {
   const qd_config& c = h->cfg;
   const int half = c.head_dim / 2;
@@ -269,14 +290,18 @@ void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows) {
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = h->layers[l];
     launch_split_rows(s, h->x, H, T, H, L.attn_norm, c.rms_eps, h->xh, h->xl);
-    launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, L.wqkv, nullptr, NQKV, L.bqkv, h->qkv, NQKV);
+    launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, L.wqkv, nullptr, NQKV, L.bqkv, h->qkv, NQKV, h->gws,
+                     h->gws_floats, h->ncu);
     enqueue_attention(h, l, T, att_rows);
     launch_split_rows(s, h->o, nq * d, T, nq * d, nullptr, 0.f, h->xh, h->xl);
-    launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.wo, nullptr, H, nullptr, h->x, H);
+    launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.wo, nullptr, H, nullptr, h->x, H, h->gws, h->gws_floats,
+                     h->ncu);
     launch_split_rows(s, h->x, H, T, H, L.mlp_norm, c.rms_eps, h->xh, h->xl);
-    launch_gemm_hilo(s, GEMM_GATEUP, h->xh, h->xl, T, H, L.wg, L.wu, I, nullptr, h->act, I);
+    launch_gemm_hilo(s, GEMM_GATEUP, h->xh, h->xl, T, H, L.wg, L.wu, I, nullptr, h->act, I, h->gws, h->gws_floats,
+                     h->ncu);
     launch_split_rows(s, h->act, I, T, I, nullptr, 0.f, h->xh, h->xl);
-    launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, I, L.wd, nullptr, H, nullptr, h->x, H);
+    launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, I, L.wd, nullptr, H, nullptr, h->x, H, h->gws, h->gws_floats,
+                     h->ncu);
     if (capture)
       (void)hipMemcpyAsync(h->cap + (size_t)(l + 1) * c.max_prefill * H, h->x, (size_t)T * H * 4,
                            hipMemcpyDeviceToDevice, s);
@@ -378,6 +403,8 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     return code;
   };
   if (hipGetDevice(&h->device) != hipSuccess) return fail(h->set_err(QD_E_HIP, "hipGetDevice failed"));
+  if (hipDeviceGetAttribute(&h->ncu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || h->ncu < 1)
+    return fail(h->set_err(QD_E_HIP, "cannot query the CU count"));
   if (hip_stream) {
     h->stream = (hipStream_t)hip_stream;
   } else {
@@ -395,6 +422,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
       (rc = dev_alloc(h, &h->o, rows * c.n_q_heads * d)) || (rc = dev_alloc(h, &h->act, rows * I)) ||
       (rc = dev_alloc(h, &h->xh, rows * std::max(std::max(H, (size_t)c.n_q_heads * d), I))) ||
       (rc = dev_alloc(h, &h->xl, rows * std::max(std::max(H, (size_t)c.n_q_heads * d), I))) ||
+      (rc = alloc_gemm_workspace(h)) ||
       (rc = dev_alloc(h, &h->part, h->part_floats)) || (rc = dev_alloc(h, &h->logits, (size_t)c.vocab)) ||
       (rc = dev_alloc(h, &h->pval, (size_t)lmhead_blocks(c.vocab))) ||
       (rc = dev_alloc(h, &h->pidx, (size_t)lmhead_blocks(c.vocab))) ||

@@ -18,6 +18,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -59,12 +61,18 @@ enum { EPI_STORE = 0, EPI_ADD = 1, EPI_GATEUP = 2 };
 // C tile of block (bm, bn).  EPI_STORE: C = acc (+ bias); EPI_ADD: C += acc;
 // EPI_GATEUP: the block's B rows are 64 gate rows and the same 64 up rows,
 // C[t][n] = SiLU(gate) * up.
+//
+// Split-K: with gridDim.z = S > 1, block z multiplies the K range [z Kc,
+// (z + 1) Kc) and writes its raw tile to part[z][T][ldp] (ldp = N, or 2 N for
+// gate | up); k_splitk_epilogue then sums the S partials in order and applies
+// the epilogue.  Small grids (few row tiles times few column tiles) fill the
+// GPU this way.
 template <int EPI>
 __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al,
                                                         int T, int K, const uint16_t* __restrict__ B,
                                                         const uint16_t* __restrict__ B2, int N,
                                                         const float* __restrict__ bias, float* __restrict__ C,
-                                                        int ldc) {
+                                                        int ldc, int Kc, float* __restrict__ part) {
   __shared__ __align__(16) uint16_t sA[2][BM * LDR];  // [hi, lo]
   __shared__ __align__(16) uint16_t sB[BN * LDR];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -117,12 +125,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   for (int j = 0; j < 4; ++j)
     brow[j] = EPI == EPI_GATEUP ? (j < 2 ? 0 : 64) + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16;
 
-  const int nk = K / BK;
-  gload(0);
+  const int kbeg = blockIdx.z * Kc;
+  const int nk = min(Kc, K - kbeg) / BK;
+  auto gload_k = [&](int kt) { gload(kbeg + kt * BK); };
+  gload_k(0);
   sstore();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * BK);  // the next K-step flies during this one
+    if (kt + 1 < nk) gload_k(kt + 1);  // the next K-step flies during this one
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       // fragments: lane holds row (lane % 16), k = kk + (lane / 16) * 8 .. + 8
@@ -151,6 +161,30 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
 
   // epilogue: acc[i][j] element e of lane is C[row 4 (lane / 16) + e][col lane % 16]
   // of the (i, j) 16 x 16 tile
+  if (gridDim.z > 1) {
+    const int ldp = EPI == EPI_GATEUP ? 2 * N : N;
+    float* P = part + (size_t)blockIdx.z * T * ldp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int n;
+          if (EPI == EPI_GATEUP) {
+            n = n0 + wn * 32 + (j & 1) * 16 + (lane & 15);
+            if (n < N) P[(size_t)t * ldp + (j < 2 ? 0 : N) + n] = acc[i][j][e];
+          } else {
+            n = n0 + wn * 64 + j * 16 + (lane & 15);
+            if (n < N) P[(size_t)t * ldp + n] = acc[i][j][e];
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -184,9 +218,53 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   }
 }
 
+// Sum of the S split partials in split order, then the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_splitk_epilogue(const float* __restrict__ part, int S, int T, int N,
+                                                         const float* __restrict__ bias, float* __restrict__ C,
+                                                         int ldc) {
+  const size_t total = (size_t)T * N;
+  const int ldp = EPI == EPI_GATEUP ? 2 * N : N;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i / N), n = (int)(i % N);
+    float a = 0.f, b = 0.f;
+    for (int z = 0; z < S; ++z) {
+      const float* P = part + (size_t)z * T * ldp + (size_t)t * ldp;
+      a += P[n];
+      if (EPI == EPI_GATEUP) b += P[N + n];
+    }
+    float* cp = C + (size_t)t * ldc + n;
+    if (EPI == EPI_GATEUP) {
+      *cp = silu_f(a) * b;
+    } else if (EPI == EPI_ADD) {
+      *cp += a;
+    } else {
+      *cp = a + (bias ? bias[n] : 0.f);
+    }
+  }
+}
+
+// K splits for a T x N product: enough blocks to cover the GPU twice, each
+// split at least two K-steps long, at most 8 splits.
+int splits_for(int T, int K, int N, int epi, int ncu) {
+  const int tiles = ((T + BM - 1) / BM) * (epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN);
+  int s = (2 * ncu + tiles - 1) / tiles;
+  s = std::min(s, std::max(1, K / BK / 2));
+  return std::max(1, std::min(s, 8));
+}
+
 }  // namespace
 
 bool gemm_supported(int K) { return K % BK == 0; }
+
+size_t gemm_workspace_floats(int T, int K, int N, int ncu) {
+  size_t best = 0;
+  for (int epi : {EPI_STORE, EPI_GATEUP}) {
+    const int s = splits_for(T, K, N, epi, ncu);
+    if (s > 1) best = std::max(best, (size_t)s * T * (epi == EPI_GATEUP ? 2 * N : N));
+  }
+  return best;
+}
 
 void launch_split_rows(hipStream_t s, const float* x, int ldx, int T, int K, const float* gain, float eps,
                        uint16_t* xh, uint16_t* xl) {
@@ -194,17 +272,36 @@ void launch_split_rows(hipStream_t s, const float* x, int ldx, int T, int K, con
 }
 
 void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
-                      const uint16_t* W2, int N, const float* bias, float* C, int ldc) {
-  const dim3 grid((T + BM - 1) / BM, epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN);
+                      const uint16_t* W2, int N, const float* bias, float* C, int ldc, float* ws, size_t ws_floats,
+                      int ncu) {
+  int S = splits_for(T, K, N, epi, ncu);
+  if ((size_t)S * T * (epi == EPI_GATEUP ? 2 * N : N) > ws_floats || !ws) S = 1;
+  const int Kc = (K / BK + S - 1) / S * BK;
+  S = (K + Kc - 1) / Kc;  // every split holds at least one K-step
+  const dim3 grid((T + BM - 1) / BM, epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN, S);
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL(k_gemm_hilo<EPI_STORE>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc);
+      hipLaunchKernelGGL(k_gemm_hilo<EPI_STORE>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc, Kc, ws);
       break;
     case EPI_ADD:
-      hipLaunchKernelGGL(k_gemm_hilo<EPI_ADD>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc);
+      hipLaunchKernelGGL(k_gemm_hilo<EPI_ADD>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc, Kc, ws);
       break;
     default:
-      hipLaunchKernelGGL(k_gemm_hilo<EPI_GATEUP>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc);
+      hipLaunchKernelGGL(k_gemm_hilo<EPI_GATEUP>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc, Kc,
+                         ws);
+      break;
+  }
+  if (S == 1) return;
+  const int blocks = (int)std::min<size_t>(((size_t)T * N + 255) / 256, 4096);
+  switch (epi) {
+    case EPI_STORE:
+      hipLaunchKernelGGL(k_splitk_epilogue<EPI_STORE>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc);
+      break;
+    case EPI_ADD:
+      hipLaunchKernelGGL(k_splitk_epilogue<EPI_ADD>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc);
+      break;
+    default:
+      hipLaunchKernelGGL(k_splitk_epilogue<EPI_GATEUP>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc);
       break;
   }
 }

@@ -49,5 +49,9 @@ enum { GEMM_STORE = 0, GEMM_ADD = 1, GEMM_GATEUP = 2 };
 bool gemm_supported(int K);
 void launch_split_rows(hipStream_t s, const float* x, int ldx, int T, int K, const float* gain, float eps,
                        uint16_t* xh, uint16_t* xl);
+// ws: split-K workspace of ws_floats floats (gemm_workspace_floats of the
+// largest product); ncu = compute units of the GPU.
+size_t gemm_workspace_floats(int T, int K, int N, int ncu);
 void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
-                      const uint16_t* W2, int N, const float* bias, float* C, int ldc);
+                      const uint16_t* W2, int N, const float* bias, float* C, int ldc, float* ws, size_t ws_floats,
+                      int ncu);
