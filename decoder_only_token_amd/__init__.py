@@ -19,6 +19,7 @@ QD_ABI_VERSION = 1
 QD_W_BF16, QD_W_INT4_G128 = 0, 1
 QD_DECODE_PERSISTENT, QD_DECODE_GRAPH = 0, 1
 QD_CAP_EMBED, QD_CAP_LAYER_OUT, QD_CAP_FINAL_NORM, QD_CAP_LOGITS = 0, 1, 2, 3
+QD_PROJ = {"wq": 0, "wk": 1, "wv": 2, "wo": 3, "w_gate": 4, "w_up": 5, "w_down": 6}
 STATUS = {0: "QD_OK", -1: "QD_E_ARG", -2: "QD_E_ABI", -3: "QD_E_STATE", -4: "QD_E_RANGE", -5: "QD_E_OOM",
           -6: "QD_E_HIP"}
 
@@ -54,7 +55,7 @@ class QdLora(ctypes.Structure):
 
 EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_decode_step", "qd_set_lora",
            "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_enable_phase_trace", "qd_get_phase_trace",
-           "qd_sync_token", "qd_get_position",
+           "qd_get_quantized", "qd_sync_token", "qd_get_position",
            "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
            "qd_sizeof_lora"]
 
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qd_enable_phase_trace": (i32, [H, i32]),
         "qd_get_phase_trace": (i32, [H, ctypes.POINTER(ctypes.c_uint64), sz, ctypes.POINTER(sz),
                                      ctypes.POINTER(ctypes.c_int32)]),
+        "qd_get_quantized": (i32, [H, i32, i32, ctypes.POINTER(ctypes.c_int8), sz, ctypes.POINTER(ctypes.c_uint16),
+                                   sz]),
         "qd_sync_token": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
         "qd_get_position": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
         "qd_last_error": (ctypes.c_char_p, [H]),
@@ -247,6 +250,18 @@ class Decoder:
         self._check(self.lib.qd_get_phase_trace(self.h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n,
                                                 ctypes.byref(written), ctypes.byref(ncu)))
         return out[:written.value].reshape(ncu.value, -1)
+
+    def get_quantized(self, layer: int, name: str, shape):
+        """int4 encoding of projection `name` ("wq", ..., "w_down") of `layer`:
+        (codes int8 [N, K], scales float16 [N, K / 128])."""
+        import numpy as np
+        n, k = shape
+        codes = np.empty((n, k), dtype=np.int8)
+        scales = np.empty((n, k // 128), dtype=np.uint16)
+        self._check(self.lib.qd_get_quantized(self.h, layer, QD_PROJ[name],
+                                              codes.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), codes.size,
+                                              scales.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), scales.size))
+        return codes, scales.view(np.float16)
 
     def sync_token(self) -> int:
         t = ctypes.c_int32()

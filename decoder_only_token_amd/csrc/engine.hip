@@ -35,6 +35,10 @@ struct Layer {
   uint16_t* wg = nullptr;  // [I, H]
   uint16_t* wu = nullptr;  // [I, H]
   uint16_t* wd = nullptr;  // [H, I]
+  // int4 group-128 format: codes [rows][in / 2] and fp16 scales [rows][in / 128]
+  // of the same five matrices (the bf16 pointers above stay null)
+  uint8_t *cqkv = nullptr, *co = nullptr, *cg = nullptr, *cu = nullptr, *cd = nullptr;
+  uint16_t *sqkv = nullptr, *so = nullptr, *sg = nullptr, *su = nullptr, *sd = nullptr;
 };
 
 __global__ void k_widen_bf16(const uint16_t* __restrict__ src, float* __restrict__ dst, size_t n) {
@@ -173,12 +177,13 @@ int validate_config(const qd_config* c, std::string& why) {
   }
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) { why = "rope_theta must be > 0 and rms_eps >= 0"; return QD_E_ARG; }
   if (c->tie_embeddings != 1) { why = "only tied embeddings are supported (tie_embeddings must be 1)"; return QD_E_ARG; }
-  if (c->weight_format != QD_W_BF16) { why = "weight_format not supported by this build"; return QD_E_ARG; }
+  if (c->weight_format != QD_W_BF16 && c->weight_format != QD_W_INT4_G128) { why = "unknown weight_format"; return QD_E_ARG; }
   if (c->max_pos < 1 || c->max_pos > (1 << 20)) { why = "max_pos out of range"; return QD_E_ARG; }
   if (c->max_prefill < 1 || c->max_prefill > c->max_pos) { why = "max_prefill must be in [1, max_pos]"; return QD_E_ARG; }
   if (c->lora_rank_max != 0) { why = "LoRA not supported by this build"; return QD_E_ARG; }
   if (c->decode_path != QD_DECODE_PERSISTENT && c->decode_path != QD_DECODE_GRAPH) { why = "unknown decode_path"; return QD_E_ARG; }
   if (c->decode_path == QD_DECODE_PERSISTENT) {
+    if (c->weight_format != QD_W_BF16) { why = "int4 weights need decode_path QD_DECODE_GRAPH"; return QD_E_ARG; }
     if (c->hidden != 1024 && c->hidden != 2048) { why = "the persistent decode step needs hidden 1024 or 2048"; return QD_E_ARG; }
     if (c->intermediate > 11264 || c->n_q_heads * c->head_dim > 11264) { why = "model too wide for the persistent decode step"; return QD_E_ARG; }
   }
@@ -284,24 +289,41 @@ void enqueue_attention(qd_handle* h, int l, int T, int att_rows) {
 // Layers with the matrix-core projections (T >= kGemmMinRows).
 void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows) {
   const qd_config& c = h->cfg;
+  const bool q4 = c.weight_format == QD_W_INT4_G128;
   hipStream_t s = h->stream;
   const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, I = c.intermediate;
   const int NQKV = qkv_rows(c);
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = h->layers[l];
     launch_split_rows(s, h->x, H, T, H, L.attn_norm, c.rms_eps, h->xh, h->xl);
-    launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, L.wqkv, nullptr, NQKV, L.bqkv, h->qkv, NQKV, h->gws,
-                     h->gws_floats, h->ncu);
+    if (q4)
+      launch_gemm_q4(s, GEMM_STORE, h->xh, h->xl, T, H, L.cqkv, L.sqkv, nullptr, nullptr, NQKV, L.bqkv, h->qkv, NQKV,
+                     h->gws, h->gws_floats, h->ncu);
+    else
+      launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, L.wqkv, nullptr, NQKV, L.bqkv, h->qkv, NQKV, h->gws,
+                       h->gws_floats, h->ncu);
     enqueue_attention(h, l, T, att_rows);
     launch_split_rows(s, h->o, nq * d, T, nq * d, nullptr, 0.f, h->xh, h->xl);
-    launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.wo, nullptr, H, nullptr, h->x, H, h->gws, h->gws_floats,
-                     h->ncu);
+    if (q4)
+      launch_gemm_q4(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.co, L.so, nullptr, nullptr, H, nullptr, h->x, H, h->gws,
+                     h->gws_floats, h->ncu);
+    else
+      launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.wo, nullptr, H, nullptr, h->x, H, h->gws,
+                       h->gws_floats, h->ncu);
     launch_split_rows(s, h->x, H, T, H, L.mlp_norm, c.rms_eps, h->xh, h->xl);
-    launch_gemm_hilo(s, GEMM_GATEUP, h->xh, h->xl, T, H, L.wg, L.wu, I, nullptr, h->act, I, h->gws, h->gws_floats,
-                     h->ncu);
+    if (q4)
+      launch_gemm_q4(s, GEMM_GATEUP, h->xh, h->xl, T, H, L.cg, L.sg, L.cu, L.su, I, nullptr, h->act, I, h->gws,
+                     h->gws_floats, h->ncu);
+    else
+      launch_gemm_hilo(s, GEMM_GATEUP, h->xh, h->xl, T, H, L.wg, L.wu, I, nullptr, h->act, I, h->gws, h->gws_floats,
+                       h->ncu);
     launch_split_rows(s, h->act, I, T, I, nullptr, 0.f, h->xh, h->xl);
-    launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, I, L.wd, nullptr, H, nullptr, h->x, H, h->gws, h->gws_floats,
-                     h->ncu);
+    if (q4)
+      launch_gemm_q4(s, GEMM_ADD, h->xh, h->xl, T, I, L.cd, L.sd, nullptr, nullptr, H, nullptr, h->x, H, h->gws,
+                     h->gws_floats, h->ncu);
+    else
+      launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, I, L.wd, nullptr, H, nullptr, h->x, H, h->gws, h->gws_floats,
+                       h->ncu);
     if (capture)
       (void)hipMemcpyAsync(h->cap + (size_t)(l + 1) * c.max_prefill * H, h->x, (size_t)T * H * 4,
                            hipMemcpyDeviceToDevice, s);
@@ -314,28 +336,46 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
   hipStream_t s = h->stream;
   const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, I = c.intermediate;
   const int NQKV = qkv_rows(c);
+  const bool q4 = c.weight_format == QD_W_INT4_G128;
+  auto tile = [&](int K) { return q4 ? q4_gemv_t_tile(K) : gemv_t_tile(K); };
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = h->layers[l];
-    for (int t0 = 0, tt = gemv_t_tile(H); t0 < T; t0 += tt) {
+    for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      launch_gemv_bf16(s, L.wqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
-                       h->qkv + (size_t)t0 * NQKV, NQKV, 0);
+      if (q4)
+        launch_gemv_q4(s, L.cqkv, L.sqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
+                       h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
+      else
+        launch_gemv_bf16(s, L.wqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
+                         h->qkv + (size_t)t0 * NQKV, NQKV, 0);
     }
     enqueue_attention(h, l, T, att_rows);
-    for (int t0 = 0, tt = gemv_t_tile(nq * d); t0 < T; t0 += tt) {
+    for (int t0 = 0, tt = tile(nq * d); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      launch_gemv_bf16(s, L.wo, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
-                       h->x + (size_t)t0 * H, H, 1);
+      if (q4)
+        launch_gemv_q4(s, L.co, L.so, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
+                       h->x + (size_t)t0 * H, H, 1, h->ncu);
+      else
+        launch_gemv_bf16(s, L.wo, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
+                         h->x + (size_t)t0 * H, H, 1);
     }
-    for (int t0 = 0, tt = gemv_t_tile(H); t0 < T; t0 += tt) {
+    for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      launch_gemv_gateup_bf16(s, L.wg, L.wu, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
-                              h->act + (size_t)t0 * I, I);
+      if (q4)
+        launch_gemv_gateup_q4(s, L.cg, L.sg, L.cu, L.su, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
+                              h->act + (size_t)t0 * I, I, h->ncu);
+      else
+        launch_gemv_gateup_bf16(s, L.wg, L.wu, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
+                                h->act + (size_t)t0 * I, I);
     }
-    for (int t0 = 0, tt = gemv_t_tile(I); t0 < T; t0 += tt) {
+    for (int t0 = 0, tt = tile(I); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      launch_gemv_bf16(s, L.wd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr, h->x + (size_t)t0 * H,
-                       H, 1);
+      if (q4)
+        launch_gemv_q4(s, L.cd, L.sd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
+                       h->x + (size_t)t0 * H, H, 1, h->ncu);
+      else
+        launch_gemv_bf16(s, L.wd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
+                         h->x + (size_t)t0 * H, H, 1);
     }
     if (capture)
       (void)hipMemcpyAsync(h->cap + (size_t)(l + 1) * c.max_prefill * H, h->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice,
@@ -494,13 +534,23 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
   auto widen = [&](const void* src, float* dst, size_t n) {
     hipLaunchKernelGGL(k_widen_bf16, dim3((n + 255) / 256), dim3(256), 0, s, (const uint16_t*)src, dst, n);
   };
+  const bool q4 = c.weight_format == QD_W_INT4_G128;
   if (!h->weights) {  // first load: allocate engine-owned weight buffers
     if ((rc = dev_alloc(h, &h->embed, (size_t)c.vocab * H)) || (rc = dev_alloc(h, &h->final_norm, H))) return rc;
     for (auto& L : h->layers) {
-      if ((rc = dev_alloc(h, &L.wqkv, NQKV * H)) || (rc = dev_alloc(h, &L.attn_norm, H)) ||
-          (rc = dev_alloc(h, &L.mlp_norm, H)) || (rc = dev_alloc(h, &L.wo, H * nq * d)) ||
-          (rc = dev_alloc(h, &L.wg, I * H)) || (rc = dev_alloc(h, &L.wu, I * H)) || (rc = dev_alloc(h, &L.wd, H * I)))
+      if ((rc = dev_alloc(h, &L.attn_norm, H)) || (rc = dev_alloc(h, &L.mlp_norm, H))) return rc;
+      if (q4) {
+        if ((rc = dev_alloc(h, &L.cqkv, NQKV * H / 2)) || (rc = dev_alloc(h, &L.sqkv, NQKV * H / 128)) ||
+            (rc = dev_alloc(h, &L.co, H * nq * d / 2)) || (rc = dev_alloc(h, &L.so, H * nq * d / 128)) ||
+            (rc = dev_alloc(h, &L.cg, I * H / 2)) || (rc = dev_alloc(h, &L.sg, I * H / 128)) ||
+            (rc = dev_alloc(h, &L.cu, I * H / 2)) || (rc = dev_alloc(h, &L.su, I * H / 128)) ||
+            (rc = dev_alloc(h, &L.cd, H * I / 2)) || (rc = dev_alloc(h, &L.sd, H * I / 128)))
+          return rc;
+      } else if ((rc = dev_alloc(h, &L.wqkv, NQKV * H)) || (rc = dev_alloc(h, &L.wo, H * nq * d)) ||
+                 (rc = dev_alloc(h, &L.wg, I * H)) || (rc = dev_alloc(h, &L.wu, I * H)) ||
+                 (rc = dev_alloc(h, &L.wd, H * I))) {
         return rc;
+      }
       if (c.qk_norm && ((rc = dev_alloc(h, &L.q_norm, d)) || (rc = dev_alloc(h, &L.k_norm, d)))) return rc;
       if (c.qkv_bias && (rc = dev_alloc(h, &L.bqkv, NQKV))) return rc;
     }
@@ -509,8 +559,26 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
   widen(w->final_norm, h->final_norm, H);
   for (int l = 0; l < c.n_layers; ++l) {
     Layer& L = h->layers[l];
+    if (q4) {
+      // rows [row0, row0 + nrows) of a source matrix [*, K] -> rows from dst_row of the engine's matrix
+      auto quant = [&](const void* src, size_t row0, size_t nrows, size_t K, uint8_t* codes, uint16_t* scales,
+                       size_t dst_row) {
+        launch_quantize_q4(s, (const uint16_t*)src + row0 * K, (int)nrows, (int)K, codes + dst_row * (K / 2),
+                           scales + dst_row * (K / 128));
+      };
+      for (size_t g = 0; g < nkv; ++g) {
+        const size_t r = g * (G + 2) * d;
+        quant(w->wq[l], g * G * d, G * d, H, L.cqkv, L.sqkv, r);
+        quant(w->wk[l], g * d, d, H, L.cqkv, L.sqkv, r + G * d);
+        quant(w->wv[l], g * d, d, H, L.cqkv, L.sqkv, r + (G + 1) * d);
+      }
+      quant(w->wo[l], 0, H, nq * d, L.co, L.so, 0);
+      quant(w->w_gate[l], 0, I, H, L.cg, L.sg, 0);
+      quant(w->w_up[l], 0, I, H, L.cu, L.su, 0);
+      quant(w->w_down[l], 0, H, I, L.cd, L.sd, 0);
+    }
     // fused q|k|v rows, group-major: [kv head g][q heads g*G .. g*G+G-1 | k_g | v_g] x d rows
-    for (size_t g = 0; g < nkv; ++g) {
+    for (size_t g = 0; !q4 && g < nkv; ++g) {
       uint16_t* dst = L.wqkv + g * (G + 2) * d * H;
       HIP_TRY(h, hipMemcpyAsync(dst, (const uint16_t*)w->wq[l] + g * G * d * H, G * d * H * 2,
                                 hipMemcpyDeviceToDevice, s));
@@ -519,10 +587,12 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
       HIP_TRY(h, hipMemcpyAsync(dst + (G + 1) * d * H, (const uint16_t*)w->wv[l] + g * d * H, d * H * 2,
                                 hipMemcpyDeviceToDevice, s));
     }
-    HIP_TRY(h, hipMemcpyAsync(L.wo, w->wo[l], H * nq * d * 2, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, hipMemcpyAsync(L.wg, w->w_gate[l], I * H * 2, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, hipMemcpyAsync(L.wu, w->w_up[l], I * H * 2, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(h, hipMemcpyAsync(L.wd, w->w_down[l], H * I * 2, hipMemcpyDeviceToDevice, s));
+    if (!q4) {
+      HIP_TRY(h, hipMemcpyAsync(L.wo, w->wo[l], H * nq * d * 2, hipMemcpyDeviceToDevice, s));
+      HIP_TRY(h, hipMemcpyAsync(L.wg, w->w_gate[l], I * H * 2, hipMemcpyDeviceToDevice, s));
+      HIP_TRY(h, hipMemcpyAsync(L.wu, w->w_up[l], I * H * 2, hipMemcpyDeviceToDevice, s));
+      HIP_TRY(h, hipMemcpyAsync(L.wd, w->w_down[l], H * I * 2, hipMemcpyDeviceToDevice, s));
+    }
     widen(w->attn_norm[l], L.attn_norm, H);
     widen(w->mlp_norm[l], L.mlp_norm, H);
     if (c.qk_norm) {
@@ -718,6 +788,50 @@ int qd_get_phase_trace(qd_handle* h, uint64_t* out_host, size_t capacity_elems, 
   HIP_TRY(h, hipMemcpy(out_host, h->trace, n * 8, hipMemcpyDeviceToHost));
   if (written_elems) *written_elems = n;
   if (n_cu) *n_cu = h->grid;
+  return QD_OK;
+}
+
+int qd_get_quantized(qd_handle* h, int32_t layer, int32_t which, int8_t* codes_host, size_t codes_capacity,
+                     uint16_t* scales_host, size_t scales_capacity) {
+  if (!h) return QD_E_ARG;
+  const qd_config& c = h->cfg;
+  if (c.weight_format != QD_W_INT4_G128) return h->set_err(QD_E_STATE, "the handle does not hold int4 weights");
+  if (!h->weights) return h->set_err(QD_E_STATE, "weights not loaded");
+  if (!codes_host || !scales_host) return h->set_err(QD_E_ARG, "output pointer is NULL");
+  if (layer < 0 || layer >= c.n_layers) return h->set_err(QD_E_ARG, "layer out of range");
+  const size_t H = c.hidden, d = c.head_dim, I = c.intermediate, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const size_t G = nq / nkv;
+  const Layer& L = h->layers[layer];
+  // (source matrix, its rows, K) and, for q/k/v, where each kv group's rows sit in the fused matrix
+  const uint8_t* cs = nullptr;
+  const uint16_t* ss = nullptr;
+  size_t N = 0, K = 0, src_rows = 0, per_group = 0, group_off = 0;
+  switch (which) {
+    case QD_PROJ_Q: cs = L.cqkv; ss = L.sqkv; N = nq * d; K = H; per_group = G * d; group_off = 0; break;
+    case QD_PROJ_K: cs = L.cqkv; ss = L.sqkv; N = nkv * d; K = H; per_group = d; group_off = G * d; break;
+    case QD_PROJ_V: cs = L.cqkv; ss = L.sqkv; N = nkv * d; K = H; per_group = d; group_off = (G + 1) * d; break;
+    case QD_PROJ_O: cs = L.co; ss = L.so; N = H; K = nq * d; break;
+    case QD_PROJ_GATE: cs = L.cg; ss = L.sg; N = I; K = H; break;
+    case QD_PROJ_UP: cs = L.cu; ss = L.su; N = I; K = H; break;
+    case QD_PROJ_DOWN: cs = L.cd; ss = L.sd; N = H; K = I; break;
+    default: return h->set_err(QD_E_ARG, "unknown projection");
+  }
+  if (codes_capacity < N * K || scales_capacity < N * (K / 128))
+    return h->set_err(QD_E_ARG, "capacity smaller than the matrix");
+  src_rows = per_group ? (size_t)qkv_rows(c) : N;
+  std::vector<uint8_t> codes(src_rows * K / 2);
+  std::vector<uint16_t> scales(src_rows * K / 128);
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipMemcpy(codes.data(), cs, codes.size(), hipMemcpyDeviceToHost));
+  HIP_TRY(h, hipMemcpy(scales.data(), ss, scales.size() * 2, hipMemcpyDeviceToHost));
+  for (size_t n = 0; n < N; ++n) {
+    const size_t r = per_group ? (n / per_group) * (G + 2) * d + group_off + n % per_group : n;
+    for (size_t k = 0; k < K; ++k) {
+      const uint8_t b = codes[r * (K / 2) + k / 2];
+      codes_host[n * K + k] = (int8_t)((k & 1 ? b >> 4 : b & 15) - 8);
+    }
+    for (size_t g = 0; g < K / 128; ++g) scales_host[n * (K / 128) + g] = scales[r * (K / 128) + g];
+  }
   return QD_OK;
 }
 

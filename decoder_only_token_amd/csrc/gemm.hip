@@ -15,6 +15,14 @@
 // padded LDS rows (144-byte stride: the 16 rows of a fragment read land on
 // distinct banks), and the next K-step is loaded into registers while the
 // current one is multiplied.
+//
+// int4 group-128 weights ("EMBERGLASS (qwen-webgpu-lora) README", "Note on
+// weights") go through the same tiles: the 32 codes a thread loads become 32
+// exact bf16 integers in the W tile, the products of one 128-column group are
+// accumulated apart, and at the end of the group each output column's partial
+// is multiplied by its fp16 scale and added to the running sum.
+#include <hip/hip_fp16.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -67,10 +75,14 @@ enum { EPI_STORE = 0, EPI_ADD = 1, EPI_GATEUP = 2 };
 // gate | up); k_splitk_epilogue then sums the S partials in order and applies
 // the epilogue.  Small grids (few row tiles times few column tiles) fill the
 // GPU this way.
-template <int EPI>
+//
+// Q4: B / B2 are int4 codes [N][K / 2] with fp16 scales SB / SB2 [N][K / 128]
+// (the layout of the int4 GEMVs); Kc is then a multiple of 128.
+template <int EPI, bool Q4>
 __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al,
-                                                        int T, int K, const uint16_t* __restrict__ B,
-                                                        const uint16_t* __restrict__ B2, int N,
+                                                        int T, int K, const void* __restrict__ B,
+                                                        const void* __restrict__ B2, const uint16_t* __restrict__ SB,
+                                                        const uint16_t* __restrict__ SB2, int N,
                                                         const float* __restrict__ bias, float* __restrict__ C,
                                                         int ldc, int Kc, float* __restrict__ part) {
   __shared__ __align__(16) uint16_t sA[2][BM * LDR];  // [hi, lo]
@@ -82,7 +94,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
 
   // global -> register staging: each tile is 128 rows x 8 chunks of 16 bytes,
   // 4 chunks per thread (row = idx / 8, chunk = idx % 8)
-  u32x4 ra[2][4], rb[4];
+  // (an int4 W tile is 128 rows x 32 bytes: one 16-byte load per thread,
+  // row = tid / 2, columns 32 (tid % 2) .. + 31)
+  u32x4 ra[2][4], rb[Q4 ? 1 : 4];
+  auto b_row = [&](int row, int& n) -> const void* {
+    if (EPI == EPI_GATEUP) {
+      n = min(n0 + (row & 63), N - 1);
+      return row < 64 ? B : B2;
+    }
+    n = min(n0 + row, N - 1);
+    return B;
+  };
   auto gload = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -91,16 +113,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
       const size_t off = (size_t)t * K + k0 + ch * 8;
       ra[0][j] = *reinterpret_cast<const u32x4*>(Ah + off);
       ra[1][j] = *reinterpret_cast<const u32x4*>(Al + off);
-      int n;
-      const uint16_t* src;
-      if (EPI == EPI_GATEUP) {
-        n = min(n0 + (row & 63), N - 1);
-        src = row < 64 ? B : B2;
-      } else {
-        n = min(n0 + row, N - 1);
-        src = B;
+      if (!Q4) {
+        int n;
+        const uint16_t* src = static_cast<const uint16_t*>(b_row(row, n));
+        rb[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)n * K + k0 + ch * 8));
       }
-      rb[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)n * K + k0 + ch * 8));
+    }
+    if (Q4) {
+      int n;
+      const uint8_t* src = static_cast<const uint8_t*>(b_row(tid >> 1, n));
+      rb[0] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(src + (size_t)n * (K / 2) + k0 / 2 + (tid & 1) * 16));
     }
   };
   auto sstore = [&]() {
@@ -109,15 +132,37 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
       const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
       *reinterpret_cast<u32x4*>(&sA[0][row * LDR + ch * 8]) = ra[0][j];
       *reinterpret_cast<u32x4*>(&sA[1][row * LDR + ch * 8]) = ra[1][j];
-      *reinterpret_cast<u32x4*>(&sB[row * LDR + ch * 8]) = rb[j];
+      if (!Q4) *reinterpret_cast<u32x4*>(&sB[row * LDR + ch * 8]) = rb[j];
+    }
+    if (Q4) {
+      // byte b of dword m: columns 8 m + 2 b (low nibble) and 8 m + 2 b + 1
+      // (high nibble), each code + 8; bf16 of a small integer is exact
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t w = rb[0][m];
+        u32x4 o;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float f0 = (float)((w >> (8 * b)) & 0xFu) - 8.0f;
+          const float f1 = (float)((w >> (8 * b + 4)) & 0xFu) - 8.0f;
+          o[b] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+        }
+        *reinterpret_cast<u32x4*>(&sB[(tid >> 1) * LDR + (tid & 1) * 32 + m * 8]) = o;
+      }
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][4], tot[Q4 ? 4 : 1][Q4 ? 4 : 1];  // Q4: acc holds the current group, tot the scaled sum
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (Q4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tot[Q4 ? i : 0][Q4 ? j : 0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // B rows of this wave's 4 column tiles
   int brow[4];
@@ -131,8 +176,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   gload_k(0);
   sstore();
   __syncthreads();
+  float scl[4];  // Q4: fp16 scales of this lane's 4 output columns in the current group
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) gload_k(kt + 1);  // the next K-step flies during this one
+    if (Q4 && (kt & 1) == 0) {
+      const int g = (kbeg + kt * BK) / 128;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int n;
+        const uint16_t* S;
+        if (EPI == EPI_GATEUP) {
+          n = n0 + wn * 32 + (j & 1) * 16 + (lane & 15);
+          S = j < 2 ? SB : SB2;
+        } else {
+          n = n0 + wn * 64 + j * 16 + (lane & 15);
+          S = SB;
+        }
+        scl[j] = __half2float(__ushort_as_half(S[(size_t)min(n, N - 1) * (K / 128) + g]));
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       // fragments: lane holds row (lane % 16), k = kk + (lane / 16) * 8 .. + 8
@@ -152,11 +214,26 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
         }
       }
     }
+    if (Q4 && (kt & 1) == 1) {  // end of a 128-column group
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          tot[Q4 ? i : 0][Q4 ? j : 0] += scl[j] * acc[i][j];
+          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     if (kt + 1 < nk) {
       __syncthreads();  // every wave is done with this K-step's tiles
       sstore();
       __syncthreads();
     }
+  }
+  if (Q4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = tot[Q4 ? i : 0][Q4 ? j : 0];
   }
 
   // epilogue: acc[i][j] element e of lane is C[row 4 (lane / 16) + e][col lane % 16]
@@ -271,24 +348,30 @@ void launch_split_rows(hipStream_t s, const float* x, int ldx, int T, int K, con
   hipLaunchKernelGGL(k_split_rows, dim3(T), dim3(256), 0, s, x, ldx, K, gain, eps, xh, xl);
 }
 
-void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
-                      const uint16_t* W2, int N, const float* bias, float* C, int ldc, float* ws, size_t ws_floats,
-                      int ncu) {
+namespace {
+
+template <bool Q4>
+void launch_gemm(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const void* W,
+                 const void* W2, const uint16_t* SW, const uint16_t* SW2, int N, const float* bias, float* C, int ldc,
+                 float* ws, size_t ws_floats, int ncu) {
   int S = splits_for(T, K, N, epi, ncu);
   if ((size_t)S * T * (epi == EPI_GATEUP ? 2 * N : N) > ws_floats || !ws) S = 1;
-  const int Kc = (K / BK + S - 1) / S * BK;
+  const int step = Q4 ? 128 : BK;  // an int4 split holds whole groups
+  const int Kc = (K / step + S - 1) / S * step;
   S = (K + Kc - 1) / Kc;  // every split holds at least one K-step
   const dim3 grid((T + BM - 1) / BM, epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN, S);
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL(k_gemm_hilo<EPI_STORE>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc, Kc, ws);
+      hipLaunchKernelGGL((k_gemm_hilo<EPI_STORE, Q4>), grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, SW, SW2, N,
+                         bias, C, ldc, Kc, ws);
       break;
     case EPI_ADD:
-      hipLaunchKernelGGL(k_gemm_hilo<EPI_ADD>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc, Kc, ws);
+      hipLaunchKernelGGL((k_gemm_hilo<EPI_ADD, Q4>), grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, SW, SW2, N,
+                         bias, C, ldc, Kc, ws);
       break;
     default:
-      hipLaunchKernelGGL(k_gemm_hilo<EPI_GATEUP>, grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, N, bias, C, ldc, Kc,
-                         ws);
+      hipLaunchKernelGGL((k_gemm_hilo<EPI_GATEUP, Q4>), grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, SW, SW2, N,
+                         bias, C, ldc, Kc, ws);
       break;
   }
   if (S == 1) return;
@@ -304,4 +387,18 @@ void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t
       hipLaunchKernelGGL(k_splitk_epilogue<EPI_GATEUP>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc);
       break;
   }
+}
+
+}  // namespace
+
+void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
+                      const uint16_t* W2, int N, const float* bias, float* C, int ldc, float* ws, size_t ws_floats,
+                      int ncu) {
+  launch_gemm<false>(s, epi, xh, xl, T, K, W, W2, nullptr, nullptr, N, bias, C, ldc, ws, ws_floats, ncu);
+}
+
+void launch_gemm_q4(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint8_t* W,
+                    const uint16_t* SW, const uint8_t* W2, const uint16_t* SW2, int N, const float* bias, float* C,
+                    int ldc, float* ws, size_t ws_floats, int ncu) {
+  launch_gemm<true>(s, epi, xh, xl, T, K, W, W2, SW, SW2, N, bias, C, ldc, ws, ws_floats, ncu);
 }

@@ -55,3 +55,20 @@ size_t gemm_workspace_floats(int T, int K, int N, int ncu);
 void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
                       const uint16_t* W2, int N, const float* bias, float* C, int ldc, float* ws, size_t ws_floats,
                       int ncu);
+// W given as int4 group-128 codes [N][K / 2] and fp16 scales [N][K / 128]
+// (q4.hip layout); K a multiple of 128.  W2 / SW2: the up matrix of GEMM_GATEUP.
+void launch_gemm_q4(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint8_t* W,
+                    const uint16_t* SW, const uint8_t* W2, const uint16_t* SW2, int N, const float* bias, float* C,
+                    int ldc, float* ws, size_t ws_floats, int ncu);
+
+// int4 group-128 weights (q4.hip): quantiser run at weight load, and the
+// GEMVs of decode and short prefills (same contracts as the bf16 GEMVs;
+// ncu = compute units, used to size the grid).
+void launch_quantize_q4(hipStream_t s, const uint16_t* src, int nrows, int K, uint8_t* codes, uint16_t* scales);
+int q4_gemv_t_tile(int K);
+void launch_gemv_q4(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
+                    int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate,
+                    int ncu);
+void launch_gemv_gateup_q4(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su,
+                           int N, int K, const float* x, int ldx, int T, const float* gain, float eps, float* a,
+                           int lda, int ncu);

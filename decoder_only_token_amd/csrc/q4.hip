@@ -1,0 +1,308 @@
+// int4 group-128 projection weights: the quantiser that runs while weights
+// are loaded, the decode / short-prefill GEMVs that dequantise in registers,
+// and the code layout both share.
+//
+// "EMBERGLASS (qwen-webgpu-lora) README", "Why it's hard" and "Note on
+// weights": projection weights are quantised to symmetric int4 in groups of
+// 128 on their way to the GPU.  For output row n and group g (input columns
+// 128 g .. 128 g + 127):
+//   s    = fp16(absmax / 7)            f32 divide, round to nearest even
+//   code = rint(w / s) in [-7, 7]      f32 divide, ties to even; 0 when s = 0
+// and the model's weight is code * s.
+//
+// Layout (private to the library): codes u8 [N][K / 2], byte j of a row holds
+// column 2 j in its low nibble and column 2 j + 1 in its high nibble, each as
+// code + 8; scales are fp16 bit patterns [N][K / 128].  A 16-byte load holds
+// 32 consecutive columns of one group.
+#include <hip/hip_fp16.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+// One wave per (row, group); lane l quantises columns 128 g + 2 l and 2 l + 1.
+__global__ __launch_bounds__(256) void k_quantize_q4(const uint16_t* __restrict__ src, int nrows, int K,
+                                                     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+  const int groups = K / 128;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (item >= nrows * groups) return;
+  const int n = item / groups, g = item % groups;
+  const uint32_t pair = *reinterpret_cast<const uint32_t*>(src + (size_t)n * K + g * 128 + 2 * lane);
+  const float w0 = bf16_lo(pair), w1 = bf16_hi(pair);
+  const float amax = wave_max(fmaxf(fabsf(w0), fabsf(w1)));
+  const __half sh = __float2half_rn(amax / 7.0f);
+  const float s = __half2float(sh);
+  auto code = [&](float w) -> int {
+    if (!(s > 0.f)) return 0;
+    const float q = rintf(w / s);
+    return (int)fminf(fmaxf(q, -7.f), 7.f);
+  };
+  const int q0 = code(w0), q1 = code(w1);
+  codes[(size_t)n * (K / 2) + g * 64 + lane] = (uint8_t)((q0 + 8) | ((q1 + 8) << 4));
+  if (lane == 0) scales[(size_t)n * groups + g] = __half_as_ushort(sh);
+}
+
+__device__ __forceinline__ float f16_bits_to_f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+
+// Staged inputs in LDS are permuted so that the 64 lanes of a wave read them
+// without bank conflicts: within each 2048-column pass, lane l owns columns
+// 32 l .. 32 l + 31 (its 16 bytes of codes), and its j-th quadruple of inputs
+// (columns 32 l + 4 j .. + 3) sits at float offset (64 j + l) 4 of the pass.
+// Rows of the staged block are q4_stride(K) floats apart.
+__host__ __device__ inline int q4_stride(int K) { return (K + 2047) / 2048 * 2048; }
+
+__device__ __forceinline__ int q4_perm(int k) {
+  const int p = k >> 11, r = k & 2047, l = r >> 5, j = (r >> 2) & 7;
+  return (p << 11) + ((j * 64 + l) << 2) + (k & 3);
+}
+
+// h[t][perm(k)] = x[t][k] (* g[k] / rms(x[t])); K a multiple of 128.
+__device__ __forceinline__ void stage_input_q4(const float* __restrict__ x, int ldx, int T, int K,
+                                               const float* __restrict__ gain, float eps, float* h, float* red) {
+  const int ks = q4_stride(K);
+  for (int t = 0; t < T; ++t) {
+    const float* xr = x + (size_t)t * ldx;
+    float ss = 0.f;
+    for (int k = threadIdx.x * 4; k < K; k += 1024) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xr + k);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    const float r = gain ? 1.0f / sqrtf(block_sum_256(ss, red) / (float)K + eps) : 1.0f;
+    for (int k = threadIdx.x * 4; k < K; k += 1024) {
+      f32x4 v = *reinterpret_cast<const f32x4*>(xr + k);
+      if (gain) v = v * r * *reinterpret_cast<const f32x4*>(gain + k);
+      *reinterpret_cast<f32x4*>(h + t * ks + q4_perm(k)) = v;
+    }
+  }
+  __syncthreads();
+}
+
+// sum over one lane's 32 columns of code * x, with u = code + 8 in the nibbles:
+// sum u x - 8 sum x.  Dword m holds columns 8 m .. 8 m + 7; v[2 m], v[2 m + 1]
+// are their inputs.
+__device__ __forceinline__ float dot32_q4(u32x4 c, const f32x4* v, float sx) {
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t w = c[m];
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const f32x4 a = v[2 * m], b = v[2 * m + 1];
+    s = fmaf((float)(lo & 0xFF), a.x, s);
+    s = fmaf((float)(hi & 0xFF), a.y, s);
+    s = fmaf((float)((lo >> 8) & 0xFF), a.z, s);
+    s = fmaf((float)((hi >> 8) & 0xFF), a.w, s);
+    s = fmaf((float)((lo >> 16) & 0xFF), b.x, s);
+    s = fmaf((float)((hi >> 16) & 0xFF), b.y, s);
+    s = fmaf((float)(lo >> 24), b.z, s);
+    s = fmaf((float)(hi >> 24), b.w, s);
+  }
+  return fmaf(-8.0f, sx, s);
+}
+
+__device__ __forceinline__ void load_x32(const float* hp, f32x4* v, float& sx) {
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[j] = *reinterpret_cast<const f32x4*>(hp + j * 256);
+    a += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  }
+  sx = a;
+}
+
+// y[t][n] (=|+=) sum_g s[n][g] sum_{k in g} code[n][k] h[t][k] (+ bias[n]) for
+// T <= TM rows.  Each wave owns RPW output rows; in each 2048-column pass a
+// lane takes 16 bytes (32 codes) of each row.  TM = 1 (decode) keeps the
+// register count low enough for several waves per SIMD.
+template <int RPW, int TM>
+__global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4, const uint16_t* __restrict__ S4,
+                                                 int N, int K, const float* __restrict__ x, int ldx, int T,
+                                                 const float* __restrict__ gain, float eps,
+                                                 const float* __restrict__ bias, float* __restrict__ y, int ldy,
+                                                 int accumulate) {
+  extern __shared__ float smem[];
+  float* red = smem;
+  float* h = smem + 8;
+  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * RPW;
+  if (n0 >= N) return;
+  const int groups = K / 128, ks = q4_stride(K);
+  float acc[RPW][TM];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[i][t] = 0.f;
+  for (int p = 0; p * 2048 + lane * 32 < K; ++p) {
+    const int k = p * 2048 + lane * 32;
+    u32x4 c[RPW];
+    float sc[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int n = min(n0 + i, N - 1);
+      c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(C4 + (size_t)n * (K / 2) + k / 2));
+      sc[i] = f16_bits_to_f(S4[(size_t)n * groups + k / 128]);
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < T) {
+        f32x4 v[8];
+        float sx;
+        load_x32(h + t * ks + p * 2048 + lane * 4, v, sx);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) acc[i][t] = fmaf(sc[i], dot32_q4(c[i], v, sx), acc[i][t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < T) {
+        const float s = wave_sum(acc[i][t]);
+        const int n = n0 + i;
+        if (lane == 0 && n < N) {
+          float* yp = y + (size_t)t * ldy + n;
+          const float v = s + (bias ? bias[n] : 0.f);
+          *yp = accumulate ? (*yp + v) : v;
+        }
+      }
+    }
+  }
+}
+
+// a[t][n] = SiLU(gate row n . h[t]) * (up row n . h[t]), both rows int4.
+template <int RPW, int TM>
+__global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restrict__ Cg, const uint16_t* __restrict__ Sg,
+                                                        const uint8_t* __restrict__ Cu, const uint16_t* __restrict__ Su,
+                                                        int N, int K, const float* __restrict__ x, int ldx, int T,
+                                                        const float* __restrict__ gain, float eps,
+                                                        float* __restrict__ a, int lda) {
+  extern __shared__ float smem[];
+  float* red = smem;
+  float* h = smem + 8;
+  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * RPW;
+  if (n0 >= N) return;
+  const int groups = K / 128, ks = q4_stride(K);
+  float ag[RPW][TM], au[RPW][TM];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) ag[i][t] = au[i][t] = 0.f;
+  for (int p = 0; p * 2048 + lane * 32 < K; ++p) {
+    const int k = p * 2048 + lane * 32;
+    u32x4 cg[RPW], cu[RPW];
+    float sg[RPW], su[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int n = min(n0 + i, N - 1);
+      cg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cg + (size_t)n * (K / 2) + k / 2));
+      cu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cu + (size_t)n * (K / 2) + k / 2));
+      sg[i] = f16_bits_to_f(Sg[(size_t)n * groups + k / 128]);
+      su[i] = f16_bits_to_f(Su[(size_t)n * groups + k / 128]);
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < T) {
+        f32x4 v[8];
+        float sx;
+        load_x32(h + t * ks + p * 2048 + lane * 4, v, sx);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          ag[i][t] = fmaf(sg[i], dot32_q4(cg[i], v, sx), ag[i][t]);
+          au[i][t] = fmaf(su[i], dot32_q4(cu[i], v, sx), au[i][t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < T) {
+        const float g = wave_sum(ag[i][t]);
+        const float u = wave_sum(au[i][t]);
+        const int n = n0 + i;
+        if (lane == 0 && n < N) a[(size_t)t * lda + n] = silu_f(g) * u;
+      }
+    }
+  }
+}
+
+// Output rows per wave: as many as max_rpw while the grid (four waves per
+// block) still gives every CU at least two blocks.
+int q4_rpw(int N, int ncu, int max_rpw) {
+  int r = max_rpw;
+  while (r > 1 && (N + 4 * r - 1) / (4 * r) < 2 * ncu) r >>= 1;
+  return r;
+}
+
+}  // namespace
+
+int q4_gemv_t_tile(int K) {
+  int t = (16384 - 64) / q4_stride(K);  // staged rows (plus the reduction slots) within 64 KiB of LDS
+  if (t > GEMV_MAX_T) t = GEMV_MAX_T;
+  if (t < 1) t = 1;
+  return t;
+}
+
+void launch_quantize_q4(hipStream_t s, const uint16_t* src, int nrows, int K, uint8_t* codes, uint16_t* scales) {
+  const int items = nrows * (K / 128);
+  hipLaunchKernelGGL(k_quantize_q4, dim3((items + 3) / 4), dim3(256), 0, s, src, nrows, K, codes, scales);
+}
+
+namespace {
+
+template <int RPW>
+void gemv_q4_t(hipStream_t s, dim3 grid, size_t lds, const uint8_t* codes, const uint16_t* scales, int N, int K,
+               const float* x, int ldx, int T, const float* gain, float eps, const float* bias, float* y, int ldy,
+               int accumulate) {
+  if (T == 1)
+    hipLaunchKernelGGL((k_gemv_q4<RPW, 1>), grid, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain, eps, bias,
+                       y, ldy, accumulate);
+  else
+    hipLaunchKernelGGL((k_gemv_q4<RPW, GEMV_MAX_T>), grid, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain,
+                       eps, bias, y, ldy, accumulate);
+}
+
+template <int RPW>
+void gateup_q4_t(hipStream_t s, dim3 grid, size_t lds, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu,
+                 const uint16_t* su, int N, int K, const float* x, int ldx, int T, const float* gain, float eps,
+                 float* a, int lda) {
+  if (T == 1)
+    hipLaunchKernelGGL((k_gemv_gateup_q4<RPW, 1>), grid, dim3(256), lds, s, cg, sg, cu, su, N, K, x, ldx, T, gain, eps,
+                       a, lda);
+  else
+    hipLaunchKernelGGL((k_gemv_gateup_q4<RPW, GEMV_MAX_T>), grid, dim3(256), lds, s, cg, sg, cu, su, N, K, x, ldx, T,
+                       gain, eps, a, lda);
+}
+
+}  // namespace
+
+void launch_gemv_q4(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
+                    int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate,
+                    int ncu) {
+  const size_t lds = (8 + (size_t)T * q4_stride(K)) * sizeof(float);
+  const int r = q4_rpw(N, ncu, 4);
+  const dim3 grid((N + 4 * r - 1) / (4 * r));
+  if (r == 4)
+    gemv_q4_t<4>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+  else if (r == 2)
+    gemv_q4_t<2>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+  else
+    gemv_q4_t<1>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+}
+
+void launch_gemv_gateup_q4(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su,
+                           int N, int K, const float* x, int ldx, int T, const float* gain, float eps, float* a,
+                           int lda, int ncu) {
+  const size_t lds = (8 + (size_t)T * q4_stride(K)) * sizeof(float);
+  const int r = q4_rpw(N, ncu, 2);
+  const dim3 grid((N + 4 * r - 1) / (4 * r));
+  if (r == 2)
+    gateup_q4_t<2>(s, grid, lds, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, a, lda);
+  else
+    gateup_q4_t<1>(s, grid, lds, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, a, lda);
+}

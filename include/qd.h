@@ -206,6 +206,23 @@ int qd_enable_phase_trace(qd_handle* h, int32_t enable);
 int qd_get_phase_trace(qd_handle* h, uint64_t* out_host, size_t capacity_elems, size_t* written_elems,
                        int32_t* n_cu);
 
+/* Projections of a layer, for qd_get_quantized. */
+enum { QD_PROJ_Q = 0, QD_PROJ_K = 1, QD_PROJ_V = 2, QD_PROJ_O = 3, QD_PROJ_GATE = 4, QD_PROJ_UP = 5, QD_PROJ_DOWN = 6 };
+
+/* Read back the int4 group-128 encoding that qd_load_weights made of one
+ * projection of layer `layer` ("EMBERGLASS (qwen-webgpu-lora) README", "Note
+ * on weights": int4 in groups of 128, quantised on the way to the GPU), in the
+ * caller's [out, in] order whatever the library's own layout:
+ *   codes_host  int8 [N][K], values in [-7, 7]            (codes_capacity >= N K)
+ *   scales_host fp16 bit patterns [N][K / 128]           (scales_capacity >= N K / 128)
+ * with N x K the shape of that projection (qd_weights); the weight of row n,
+ * column k is codes[n][k] * scale[n][k / 128].  Synchronises the stream.
+ * Errors: QD_E_STATE (weights not loaded, or weight_format is not
+ * QD_W_INT4_G128), QD_E_ARG (NULL output, bad layer or projection, capacity
+ * too small), QD_E_HIP. */
+int qd_get_quantized(qd_handle* h, int32_t layer, int32_t which, int8_t* codes_host, size_t codes_capacity,
+                     uint16_t* scales_host, size_t scales_capacity);
+
 /* Synchronise the stream and read the device-resident last token. */
 int qd_sync_token(qd_handle* h, int32_t* token_host);
 

@@ -65,6 +65,13 @@ QWEN3_06B = ModelShape("qwen3-0.6b", 28, 1024, 16, 8, 128, 3072, 151936, max_pos
 QWEN25_3B_INT4 = ModelShape("qwen2.5-3b-int4g128", 36, 2048, 16, 2, 128, 11008, 151936,
                             qk_norm=False, qkv_bias=True, weight_format=W_INT4_G128, max_pos=4096)
 QWEN25_3B_INT4_16K = dataclasses.replace(QWEN25_3B_INT4, name="qwen2.5-3b-int4g128-16k", max_pos=16384)
+# Small int4 models of the 3B family's structure (8 query heads per kv head,
+# q/k/v bias, no QK-norm).  Their projection widths end partway into a
+# 2048-column pass (1024, 1408) or run one pass and a ragged rest (2432).
+TINY_INT4 = ModelShape("tiny-int4g128", 2, 1024, 16, 2, 128, 1408, 4096, qk_norm=False, qkv_bias=True,
+                       weight_format=W_INT4_G128, max_pos=256)
+TINY_INT4_WIDE = ModelShape("tiny-int4g128-wide", 2, 2048, 16, 2, 128, 2432, 4096, qk_norm=False, qkv_bias=True,
+                            weight_format=W_INT4_G128, max_pos=256)
 
 WORKLOADS: Dict[str, Workload] = {
     # 8-token prompt, 16 greedy decode steps
