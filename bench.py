@@ -245,7 +245,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 weights, f32 activations/accumulation/KV",
+        "dtype": ("int4-g128 projection weights with fp16 scales, bf16 tied embedding"
+                  if shape.weight_format == synth.W_INT4_G128 else "bf16 weights") +
+                 ", f32 activations/accumulation/KV",
         "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform random prompt ids)",
         "config": {"workload": wl.name, "model": shape.name, "layers": shape.n_layers, "hidden": shape.hidden,
                    "heads": [shape.n_q_heads, shape.n_kv_heads], "vocab": shape.vocab,

@@ -1,0 +1,221 @@
+// Split-K flash-decode attention for one new row (the decode step), GQA.
+//
+// "EMBERGLASS (qwen-webgpu-lora) README", split-K decode attention: the cache
+// positions 0 .. ctx-1 are cut into S splits; each split produces the
+// unnormalised softmax state {max m, sum l, weighted values o} of its
+// positions, and a merge combines the splits.  Here a block of 256 threads
+// owns one kv head g and one split, and handles the G = nq / nkv query heads
+// of g together, so each K/V row is read from HBM once for the whole group.
+//
+// The split count S is fixed for the life of the engine (so one captured
+// graph serves every position); the split length is C = max(cmin, ceil(ctx /
+// S)), computed on the device from the step state, and splits past the end of
+// the context do nothing.  Within a split, positions go in tiles of 64:
+//   1. each thread loads 32 dims of K and of V of one position (4 threads per
+//      position, 16-byte loads, a wave reads 16 consecutive rows);
+//   2. scores s = q_j . k / sqrt(d) from K in registers and q in LDS;
+//   3. per head, the running max / sum are updated (online softmax) and the
+//      tile's probabilities written to LDS;
+//   4. each thread rescales and accumulates its (head, dim) outputs from the V
+//      tile in LDS.
+// Every sum has a fixed order, so results are identical run to run.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int D = 128;
+constexpr int TP = 64;  // positions per tile
+
+__device__ __forceinline__ float block_max_256(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  const float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ int split_len(int ctx, int S, int cmin) { return max(cmin, (ctx + S - 1) / S); }
+
+// grid (nkv, S), block 256.  Partials part[h][s] = {m, l, o[0..D)} for query
+// head h = g G + j (o not divided by l).
+template <int G>
+__global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q, const float* __restrict__ Kc,
+                                                     const float* __restrict__ Vc, int max_pos,
+                                                     const DevState* __restrict__ st, int S, int cmin, float scale,
+                                                     float* __restrict__ part) {
+  const int g = blockIdx.x, sp = blockIdx.y;
+  const int ctx = st->pos + 1;
+  const int C = split_len(ctx, S, cmin);
+  const int p_begin = sp * C;
+  if (p_begin >= ctx) return;  // the merge reads only the splits that hold positions
+  const int p_end = min(p_begin + C, ctx);
+
+  __shared__ __align__(16) float qs[G * D];
+  __shared__ __align__(16) float vs[TP * D];
+  __shared__ __align__(16) float ps[G * TP];  // scores, then probabilities
+  __shared__ float cs[G];                     // per-head rescale of this tile
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < G * D / 4; i += 256)
+    reinterpret_cast<f32x4*>(qs)[i] = reinterpret_cast<const f32x4*>(q + (size_t)g * G * D)[i];
+
+  const int pl = tid >> 2, sub = tid & 3;  // load / score mapping: position, quarter of the dims
+  const int dd = tid & 127, jh = tid >> 7; // output mapping: dim, head parity
+  constexpr int JPT = G >= 2 ? G / 2 : 1;  // output heads per thread
+  constexpr int HPW = G >= 4 ? G / 4 : 1;  // softmax heads per wave
+  float acc[JPT];
+#pragma unroll
+  for (int i = 0; i < JPT; ++i) acc[i] = 0.f;
+  float M[HPW], L[HPW];
+#pragma unroll
+  for (int r = 0; r < HPW; ++r) { M[r] = -INFINITY; L[r] = 0.f; }
+
+  const float* Kg = Kc + (size_t)g * max_pos * D;
+  const float* Vg = Vc + (size_t)g * max_pos * D;
+  for (int t0 = p_begin; t0 < p_end; t0 += TP) {
+    const int n = min(TP, p_end - t0);
+    f32x4 kr[8], vr[8];
+    if (pl < n) {
+      const size_t off = (size_t)(t0 + pl) * D + sub * 32;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Kg + off) + i);
+        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Vg + off) + i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kr[i] = vr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();  // q staged; the previous tile's V and probabilities consumed
+    if (pl < n) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) reinterpret_cast<f32x4*>(vs + pl * D + sub * 32)[i] = vr[i];
+    }
+    float sj[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const f32x4* qv = reinterpret_cast<const f32x4*>(qs + j * D + sub * 32);
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const f32x4 b = qv[i];
+        a = fmaf(kr[i].x, b.x, a);
+        a = fmaf(kr[i].y, b.y, a);
+        a = fmaf(kr[i].z, b.z, a);
+        a = fmaf(kr[i].w, b.w, a);
+      }
+      sj[j] = group_sum<4>(a);
+    }
+    if (sub == 0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) ps[j * TP + pl] = pl < n ? sj[j] * scale : -INFINITY;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < HPW; ++r) {
+      const int j = wave + 4 * r;
+      if (j < G) {
+        const float s = ps[j * TP + lane];
+        const float mn = fmaxf(M[r], wave_max(s));
+        const float p = __expf(s - mn);
+        const float c = __expf(M[r] - mn);
+        L[r] = L[r] * c + wave_sum(p);
+        M[r] = mn;
+        ps[j * TP + lane] = p;
+        if (lane == 0) cs[j] = c;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < JPT; ++i) {
+      const int j = G >= 2 ? jh + 2 * i : 0;
+      if (G >= 2 || jh == 0) {
+        float a = acc[i] * cs[j];
+        const float* pj = ps + j * TP;
+        for (int p = 0; p < n; ++p) a = fmaf(pj[p], vs[p * D + dd], a);
+        acc[i] = a;
+      }
+    }
+  }
+  float* base = part + ((size_t)g * G * S + sp) * (D + 2);
+#pragma unroll
+  for (int i = 0; i < JPT; ++i) {
+    const int j = G >= 2 ? jh + 2 * i : 0;
+    if (G >= 2 || jh == 0) base[(size_t)j * S * (D + 2) + 2 + dd] = acc[i];
+  }
+#pragma unroll
+  for (int r = 0; r < HPW; ++r) {
+    const int j = wave + 4 * r;
+    if (j < G && lane == 0) {
+      base[(size_t)j * S * (D + 2)] = M[r];
+      base[(size_t)j * S * (D + 2) + 1] = L[r];
+    }
+  }
+}
+
+// o_h = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M} over the splits that hold
+// positions, in split order.  grid (nq, D / 32), block 256: 32 dims x 8 split
+// classes (s mod 8), summed in class order at the end.
+constexpr int kMaxSplits = 1024;
+
+__global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restrict__ part, int S, int cmin,
+                                                           const DevState* __restrict__ st, float* __restrict__ o_out) {
+  __shared__ float f[kMaxSplits];
+  __shared__ float red[8];
+  __shared__ float acc_s[8][33];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int ctx = st->pos + 1;
+  const int C = split_len(ctx, S, cmin);
+  const int s_act = min(S, (ctx + C - 1) / C);
+  const float* base = part + (size_t)h * S * (D + 2);
+  float m = -INFINITY;
+  for (int s = tid; s < s_act; s += 256) m = fmaxf(m, base[(size_t)s * (D + 2)]);
+  const float M = block_max_256(m, red);
+  float lsum = 0.f;
+  for (int s = tid; s < s_act; s += 256) {
+    const float e = __expf(base[(size_t)s * (D + 2)] - M);
+    f[s] = e;
+    lsum = fmaf(base[(size_t)s * (D + 2) + 1], e, lsum);
+  }
+  const float Lt = block_sum_256(lsum, red);  // its barrier also publishes f[]
+  const int d = blockIdx.y * 32 + (tid & 31), sg = tid >> 5;
+  float a = 0.f;
+#pragma unroll 4
+  for (int s = sg; s < s_act; s += 8) a = fmaf(f[s], base[(size_t)s * (D + 2) + 2 + d], a);
+  acc_s[sg][tid & 31] = a;
+  __syncthreads();
+  if (sg == 0) {
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o += acc_s[k][tid & 31];
+    o_out[(size_t)h * D + d] = o / Lt;
+  }
+}
+
+}  // namespace
+
+int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin) {
+  int s = 2 * ncu / nkv;
+  s = std::min(s, (max_pos + cmin - 1) / cmin);
+  s = std::min(s, kMaxSplits);
+  return std::max(s, 1);
+}
+
+void launch_attention_decode(hipStream_t s, const float* q, int nq, int nkv, const float* Kc, const float* Vc,
+                             int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const dim3 grid(nkv, S);
+  switch (nq / nkv) {
+    case 1: hipLaunchKernelGGL(k_attn_decode<1>, grid, dim3(256), 0, s, q, Kc, Vc, max_pos, st, S, cmin, scale, part); break;
+    case 2: hipLaunchKernelGGL(k_attn_decode<2>, grid, dim3(256), 0, s, q, Kc, Vc, max_pos, st, S, cmin, scale, part); break;
+    case 4: hipLaunchKernelGGL(k_attn_decode<4>, grid, dim3(256), 0, s, q, Kc, Vc, max_pos, st, S, cmin, scale, part); break;
+    case 8: hipLaunchKernelGGL(k_attn_decode<8>, grid, dim3(256), 0, s, q, Kc, Vc, max_pos, st, S, cmin, scale, part); break;
+    default: return;  // rejected by the host before any launch
+  }
+  hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32), dim3(256), 0, s, part, S, cmin, st, o_out);
+}

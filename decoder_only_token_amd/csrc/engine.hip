@@ -21,7 +21,8 @@
 
 namespace {
 
-constexpr int kAttnChunk = 64;  // cache positions per split-K attention block
+constexpr int kAttnChunk = 64;  // cache positions per split-K attention block (prefill)
+constexpr int kDecodeMinSplit = 16;  // shortest split of the decode attention
 constexpr int kGemmMinRows = 16;  // prefills of at least this many rows use the matrix-core projections
 
 struct Layer {
@@ -81,6 +82,7 @@ struct qd_handle {
   int ncu = 0;
   float* part = nullptr; // attention partials
   size_t part_floats = 0;
+  int dec_splits = 1;    // splits of the decode attention
   float* logits = nullptr;  // [V]
   float* pval = nullptr;
   int32_t* pidx = nullptr;
@@ -274,8 +276,8 @@ void enqueue_attention(qd_handle* h, int l, int T, int att_rows) {
   launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
                     h->st, h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
   if (T == 1) {
-    launch_attention(s, h->q, 1, nq, nkv, d, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, kAttnChunk,
-                     attn_splits(c.max_pos), h->part, h->o, nq * d, 0);
+    launch_attention_decode(s, h->q, nq, nkv, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st,
+                            h->dec_splits, kDecodeMinSplit, h->part, h->o);
   } else {
     for (int t0 = 0; t0 < T; t0 += att_rows) {
       const int tn = std::min(att_rows, T - t0);
@@ -347,7 +349,7 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
                        h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
       else
         launch_gemv_bf16(s, L.wqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
-                         h->qkv + (size_t)t0 * NQKV, NQKV, 0);
+                         h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
     }
     enqueue_attention(h, l, T, att_rows);
     for (int t0 = 0, tt = tile(nq * d); t0 < T; t0 += tt) {
@@ -357,7 +359,7 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
                        h->x + (size_t)t0 * H, H, 1, h->ncu);
       else
         launch_gemv_bf16(s, L.wo, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
-                         h->x + (size_t)t0 * H, H, 1);
+                         h->x + (size_t)t0 * H, H, 1, h->ncu);
     }
     for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
@@ -366,7 +368,7 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
                               h->act + (size_t)t0 * I, I, h->ncu);
       else
         launch_gemv_gateup_bf16(s, L.wg, L.wu, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
-                                h->act + (size_t)t0 * I, I);
+                                h->act + (size_t)t0 * I, I, h->ncu);
     }
     for (int t0 = 0, tt = tile(I); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
@@ -375,7 +377,7 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
                        h->x + (size_t)t0 * H, H, 1, h->ncu);
       else
         launch_gemv_bf16(s, L.wd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
-                         h->x + (size_t)t0 * H, H, 1);
+                         h->x + (size_t)t0 * H, H, 1, h->ncu);
     }
     if (capture)
       (void)hipMemcpyAsync(h->cap + (size_t)(l + 1) * c.max_prefill * H, h->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice,
@@ -455,6 +457,8 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   const size_t H = c.hidden, d = c.head_dim, I = c.intermediate, rows = c.max_prefill;
   const size_t kv = (size_t)c.n_layers * c.n_kv_heads * c.max_pos * d;
   h->part_floats = (size_t)(c.max_prefill > 1 ? attn_row_chunk(c) : 1) * c.n_q_heads * attn_splits(c.max_pos) * (d + 2);
+  h->dec_splits = attn_decode_splits(c.max_pos, c.n_kv_heads, h->ncu, kDecodeMinSplit);
+  h->part_floats = std::max(h->part_floats, (size_t)c.n_q_heads * h->dec_splits * (d + 2));
   if ((rc = dev_alloc(h, &h->Kc, kv)) || (rc = dev_alloc(h, &h->Vc, kv)) ||
       (rc = dev_alloc(h, &h->rope_cos, (size_t)c.max_pos * d / 2)) ||
       (rc = dev_alloc(h, &h->rope_sin, (size_t)c.max_pos * d / 2)) || (rc = dev_alloc(h, &h->x, rows * H)) ||

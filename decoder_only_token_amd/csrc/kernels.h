@@ -18,10 +18,11 @@ struct DevState {
 #define LMHEAD_RPW 4   // vocabulary rows per wave (LM head)
 
 void launch_embed(hipStream_t s, const uint16_t* E, const int32_t* tok, int T, int H, float* x);
+// (ncu = compute units of the GPU, used to size the grid)
 void launch_gemv_bf16(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
-                      const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate);
+                      const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate, int ncu);
 void launch_gemv_gateup_bf16(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
-                             int ldx, int T, const float* gain, float eps, float* a, int lda);
+                             int ldx, int T, const float* gain, float eps, float* a, int lda, int ncu);
 int lmhead_blocks(int V);
 void launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
                         float* logits, float* part_val, int32_t* part_idx, float* xf_out);
@@ -33,6 +34,11 @@ void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq
 void launch_attention(hipStream_t s, const float* q, int T, int nq, int nkv, int d, const float* Kc, const float* Vc,
                       int max_pos, const DevState* st, int chunk, int S, float* part, float* o_out, int ldo,
                       int row0);
+// Decode attention for one new row (attn.hip): S splits of length
+// max(cmin, ceil(ctx / S)); part holds nq * S * (d + 2) floats.
+int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin);
+void launch_attention_decode(hipStream_t s, const float* q, int nq, int nkv, const float* Kc, const float* Vc,
+                             int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out);
 
 // Top-k / temperature / top-p sampling over the logits (sample.hip); the token
 // goes to the device step state, which the greedy pass has already advanced.

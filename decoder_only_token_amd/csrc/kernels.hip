@@ -57,9 +57,13 @@ __device__ __forceinline__ void stage_input(const float* __restrict__ x, int ldx
 // bf16 GEMV / skinny GEMM for T <= GEMV_MAX_T input rows:
 //   y[t][n] (=|+=) sum_k W[n][k] * h[t][k] (+ bias[n])
 // W row-major [N][K] (the [out, in] layout of the pages).  Each wave owns RPW
-// consecutive output rows; each lane streams 16-byte chunks of those rows.
-// The wave-wide sum of a row is taken in a fixed order.
-template <int RPW>
+// consecutive output rows; each lane streams 16-byte chunks of those rows,
+// 512 columns per pass of the wave.  The first pass's weights are requested
+// before the input is staged and each later pass is requested while the
+// previous one is multiplied, so HBM latency overlaps the staging and the
+// arithmetic.  The wave-wide sum of a row is taken in a fixed order.
+// TM = 1 (decode) keeps the register count low.
+template <int RPW, int TM>
 __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ W, int N, int K,
                                                    const float* __restrict__ x, int ldx, int T,
                                                    const float* __restrict__ gain, float eps,
@@ -68,34 +72,42 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
   extern __shared__ float smem[];
   float* red = smem;
   float* h = smem + 8;
-  stage_input(x, ldx, T, K, gain, eps, h, red);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  if (n0 >= N) return;
-  float acc[RPW][GEMV_MAX_T];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i)
-#pragma unroll
-    for (int t = 0; t < GEMV_MAX_T; ++t) acc[i][t] = 0.f;
-  for (int k = lane * 8; k < K; k += 512) {
-    u32x4 w[RPW];
+  u32x4 w[RPW];
+  auto load = [&](u32x4* dst, int k) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int n = min(n0 + i, N - 1);
-      w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)n * K + k));
+      dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)n * K + k));
     }
+  };
+  int k = lane * 8;
+  if (n0 < N && k < K) load(w, k);
+  stage_input(x, ldx, T, K, gain, eps, h, red);
+  if (n0 >= N) return;
+  float acc[RPW][TM];
 #pragma unroll
-    for (int t = 0; t < GEMV_MAX_T; ++t) {
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[i][t] = 0.f;
+  for (; k < K; k += 512) {
+    u32x4 wn[RPW];
+    if (k + 512 < K) load(wn, k + 512);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
       if (t < T) {
 #pragma unroll
         for (int i = 0; i < RPW; ++i) acc[i][t] += dot8(w[i], h + t * K + k);
       }
     }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) w[i] = wn[i];
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
 #pragma unroll
-    for (int t = 0; t < GEMV_MAX_T; ++t) {
+    for (int t = 0; t < TM; ++t) {
       if (t < T) {
         float s = wave_sum(acc[i][t]);
         const int n = n0 + i;
@@ -109,23 +121,42 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
   }
 }
 
-int gemv_rows_per_block() { return 4 * GEMV_RPW; }
+// Rows per wave: as many as max_rpw while the grid (four waves per block)
+// still gives every CU at least two blocks.
+static int rows_per_wave(int N, int ncu, int max_rpw) {
+  int r = max_rpw;
+  while (r > 1 && (N + 4 * r - 1) / (4 * r) < 2 * ncu) r >>= 1;
+  return r;
+}
+
+template <int RPW>
+static void gemv_bf16_t(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
+                        const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate) {
+  const dim3 grid((N + 4 * RPW - 1) / (4 * RPW));
+  const size_t lds = (8 + (size_t)T * K) * sizeof(float);
+  if (T == 1)
+    hipLaunchKernelGGL((k_gemv_bf16<RPW, 1>), grid, dim3(256), lds, s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy,
+                       accumulate);
+  else
+    hipLaunchKernelGGL((k_gemv_bf16<RPW, GEMV_MAX_T>), grid, dim3(256), lds, s, W, N, K, x, ldx, T, gain, eps, bias,
+                       y, ldy, accumulate);
+}
 
 void launch_gemv_bf16(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
-                      const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate) {
-  const int rows_per_block = 4 * GEMV_RPW;
-  dim3 grid((N + rows_per_block - 1) / rows_per_block);
-  size_t lds = (8 + (size_t)T * K) * sizeof(float);
-  hipLaunchKernelGGL(k_gemv_bf16<GEMV_RPW>, grid, dim3(256), lds, s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy,
-                     accumulate);
+                      const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate, int ncu) {
+  switch (rows_per_wave(N, ncu, GEMV_RPW)) {
+    case 4: gemv_bf16_t<4>(s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    case 2: gemv_bf16_t<2>(s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    default: gemv_bf16_t<1>(s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Fused gate/up GEMV with the SiLU(gate) * up epilogue and an RMSNorm prologue:
 //   a[t][i] = SiLU(sum_k Wg[i][k] h[t][k]) * (sum_k Wu[i][k] h[t][k])
 // "Failed Star / fs" block figure (SwiGLU); the gated product is formed in
-// registers and never stored separately.
-template <int RPW>
+// registers and never stored separately.  Loads are issued as in k_gemv_bf16.
+template <int RPW, int TM>
 __global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __restrict__ Wg,
                                                           const uint16_t* __restrict__ Wu, int N, int K,
                                                           const float* __restrict__ x, int ldx, int T,
@@ -134,25 +165,31 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __rest
   extern __shared__ float smem[];
   float* red = smem;
   float* h = smem + 8;
-  stage_input(x, ldx, T, K, gain, eps, h, red);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  if (n0 >= N) return;
-  float ag[RPW][GEMV_MAX_T], au[RPW][GEMV_MAX_T];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i)
-#pragma unroll
-    for (int t = 0; t < GEMV_MAX_T; ++t) ag[i][t] = au[i][t] = 0.f;
-  for (int k = lane * 8; k < K; k += 512) {
-    u32x4 wg[RPW], wu[RPW];
+  u32x4 wg[RPW], wu[RPW];
+  auto load = [&](u32x4* dg, u32x4* du, int k) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int n = min(n0 + i, N - 1);
-      wg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wg + (size_t)n * K + k));
-      wu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wu + (size_t)n * K + k));
+      dg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wg + (size_t)n * K + k));
+      du[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wu + (size_t)n * K + k));
     }
+  };
+  int k = lane * 8;
+  if (n0 < N && k < K) load(wg, wu, k);
+  stage_input(x, ldx, T, K, gain, eps, h, red);
+  if (n0 >= N) return;
+  float ag[RPW][TM], au[RPW][TM];
 #pragma unroll
-    for (int t = 0; t < GEMV_MAX_T; ++t) {
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) ag[i][t] = au[i][t] = 0.f;
+  for (; k < K; k += 512) {
+    u32x4 gn[RPW], un[RPW];
+    if (k + 512 < K) load(gn, un, k + 512);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
       if (t < T) {
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
@@ -161,11 +198,13 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __rest
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) { wg[i] = gn[i]; wu[i] = un[i]; }
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
 #pragma unroll
-    for (int t = 0; t < GEMV_MAX_T; ++t) {
+    for (int t = 0; t < TM; ++t) {
       if (t < T) {
         float g = wave_sum(ag[i][t]);
         float u = wave_sum(au[i][t]);
@@ -176,13 +215,25 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __rest
   }
 }
 
+template <int RPW>
+static void gateup_bf16_t(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
+                          int ldx, int T, const float* gain, float eps, float* a, int lda) {
+  const dim3 grid((N + 4 * RPW - 1) / (4 * RPW));
+  const size_t lds = (8 + (size_t)T * K) * sizeof(float);
+  if (T == 1)
+    hipLaunchKernelGGL((k_gemv_gateup_bf16<RPW, 1>), grid, dim3(256), lds, s, Wg, Wu, N, K, x, ldx, T, gain, eps, a,
+                       lda);
+  else
+    hipLaunchKernelGGL((k_gemv_gateup_bf16<RPW, GEMV_MAX_T>), grid, dim3(256), lds, s, Wg, Wu, N, K, x, ldx, T, gain,
+                       eps, a, lda);
+}
+
 void launch_gemv_gateup_bf16(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
-                             int ldx, int T, const float* gain, float eps, float* a, int lda) {
-  const int rows_per_block = 4 * GATEUP_RPW;
-  dim3 grid((N + rows_per_block - 1) / rows_per_block);
-  size_t lds = (8 + (size_t)T * K) * sizeof(float);
-  hipLaunchKernelGGL(k_gemv_gateup_bf16<GATEUP_RPW>, grid, dim3(256), lds, s, Wg, Wu, N, K, x, ldx, T, gain, eps,
-                     a, lda);
+                             int ldx, int T, const float* gain, float eps, float* a, int lda, int ncu) {
+  if (rows_per_wave(N, ncu, GATEUP_RPW) == 2)
+    gateup_bf16_t<2>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda);
+  else
+    gateup_bf16_t<1>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda);
 }
 
 // ---------------------------------------------------------------------------

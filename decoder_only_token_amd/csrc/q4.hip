@@ -123,26 +123,34 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
   extern __shared__ float smem[];
   float* red = smem;
   float* h = smem + 8;
-  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  if (n0 >= N) return;
   const int groups = K / 128, ks = q4_stride(K);
+  // the first pass's codes are requested before the input is staged, each
+  // later pass while the previous one is multiplied
+  u32x4 c[RPW];
+  float sc[RPW];
+  auto load = [&](u32x4* dc, float* ds, int k) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int n = min(n0 + i, N - 1);
+      dc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(C4 + (size_t)n * (K / 2) + k / 2));
+      ds[i] = f16_bits_to_f(S4[(size_t)n * groups + k / 128]);
+    }
+  };
+  int k = lane * 32;
+  if (n0 < N && k < K) load(c, sc, k);
+  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  if (n0 >= N) return;
   float acc[RPW][TM];
 #pragma unroll
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[i][t] = 0.f;
-  for (int p = 0; p * 2048 + lane * 32 < K; ++p) {
-    const int k = p * 2048 + lane * 32;
-    u32x4 c[RPW];
-    float sc[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int n = min(n0 + i, N - 1);
-      c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(C4 + (size_t)n * (K / 2) + k / 2));
-      sc[i] = f16_bits_to_f(S4[(size_t)n * groups + k / 128]);
-    }
+  for (int p = 0; k < K; ++p, k += 2048) {
+    u32x4 cn[RPW];
+    float sn[RPW];
+    if (k + 2048 < K) load(cn, sn, k + 2048);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       if (t < T) {
@@ -153,6 +161,8 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
         for (int i = 0; i < RPW; ++i) acc[i][t] = fmaf(sc[i], dot32_q4(c[i], v, sx), acc[i][t]);
       }
     }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) { c[i] = cn[i]; sc[i] = sn[i]; }
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -181,28 +191,34 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restric
   extern __shared__ float smem[];
   float* red = smem;
   float* h = smem + 8;
-  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  if (n0 >= N) return;
   const int groups = K / 128, ks = q4_stride(K);
+  u32x4 cg[RPW], cu[RPW];
+  float sg[RPW], su[RPW];
+  auto load = [&](u32x4* dg, float* dsg, u32x4* du, float* dsu, int k) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int n = min(n0 + i, N - 1);
+      dg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cg + (size_t)n * (K / 2) + k / 2));
+      du[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cu + (size_t)n * (K / 2) + k / 2));
+      dsg[i] = f16_bits_to_f(Sg[(size_t)n * groups + k / 128]);
+      dsu[i] = f16_bits_to_f(Su[(size_t)n * groups + k / 128]);
+    }
+  };
+  int k = lane * 32;
+  if (n0 < N && k < K) load(cg, sg, cu, su, k);
+  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  if (n0 >= N) return;
   float ag[RPW][TM], au[RPW][TM];
 #pragma unroll
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int t = 0; t < TM; ++t) ag[i][t] = au[i][t] = 0.f;
-  for (int p = 0; p * 2048 + lane * 32 < K; ++p) {
-    const int k = p * 2048 + lane * 32;
-    u32x4 cg[RPW], cu[RPW];
-    float sg[RPW], su[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int n = min(n0 + i, N - 1);
-      cg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cg + (size_t)n * (K / 2) + k / 2));
-      cu[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cu + (size_t)n * (K / 2) + k / 2));
-      sg[i] = f16_bits_to_f(Sg[(size_t)n * groups + k / 128]);
-      su[i] = f16_bits_to_f(Su[(size_t)n * groups + k / 128]);
-    }
+  for (int p = 0; k < K; ++p, k += 2048) {
+    u32x4 gn[RPW], un[RPW];
+    float sgn[RPW], sun[RPW];
+    if (k + 2048 < K) load(gn, sgn, un, sun, k + 2048);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       if (t < T) {
@@ -216,6 +232,8 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restric
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) { cg[i] = gn[i]; cu[i] = un[i]; sg[i] = sgn[i]; su[i] = sun[i]; }
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
