@@ -42,6 +42,14 @@ struct Layer {
   uint16_t *sqkv = nullptr, *so = nullptr, *sg = nullptr, *su = nullptr, *sd = nullptr;
 };
 
+// Adapter of one layer: stacked down matrices [A_q; A_v] [2 r, H] and the up
+// matrices B_q [nq d, r], B_v [nkv d, r] (bf16, r = the installed rank).
+struct LoraLayer {
+  uint16_t* a = nullptr;
+  uint16_t* bq = nullptr;
+  uint16_t* bv = nullptr;
+};
+
 __global__ void k_widen_bf16(const uint16_t* __restrict__ src, float* __restrict__ dst, size_t n) {
   size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   if (i < n) dst[i] = __uint_as_float(((uint32_t)src[i]) << 16);
@@ -63,6 +71,10 @@ struct qd_handle {
   uint16_t* embed = nullptr;
   float* final_norm = nullptr;
   std::vector<Layer> layers;
+  std::vector<LoraLayer> lora;  // sized for lora_rank_max
+  int lora_rank = 0;            // 0: no adapter installed
+  float lora_scale = 0.f;       // alpha / rank
+  float* lu = nullptr;          // [rows][2 lora_rank_max] down products
 
   float* Kc = nullptr;  // [L][nkv][max_pos][d]
   float* Vc = nullptr;
@@ -182,9 +194,10 @@ int validate_config(const qd_config* c, std::string& why) {
   if (c->weight_format != QD_W_BF16 && c->weight_format != QD_W_INT4_G128) { why = "unknown weight_format"; return QD_E_ARG; }
   if (c->max_pos < 1 || c->max_pos > (1 << 20)) { why = "max_pos out of range"; return QD_E_ARG; }
   if (c->max_prefill < 1 || c->max_prefill > c->max_pos) { why = "max_prefill must be in [1, max_pos]"; return QD_E_ARG; }
-  if (c->lora_rank_max != 0) { why = "LoRA not supported by this build"; return QD_E_ARG; }
+  if (c->lora_rank_max < 0 || c->lora_rank_max > 64) { why = "lora_rank_max must be in [0, 64]"; return QD_E_ARG; }
   if (c->decode_path != QD_DECODE_PERSISTENT && c->decode_path != QD_DECODE_GRAPH) { why = "unknown decode_path"; return QD_E_ARG; }
   if (c->decode_path == QD_DECODE_PERSISTENT) {
+    if (c->lora_rank_max != 0) { why = "LoRA needs decode_path QD_DECODE_GRAPH"; return QD_E_ARG; }
     if (c->weight_format != QD_W_BF16) { why = "int4 weights need decode_path QD_DECODE_GRAPH"; return QD_E_ARG; }
     if (c->hidden != 1024 && c->hidden != 2048) { why = "the persistent decode step needs hidden 1024 or 2048"; return QD_E_ARG; }
     if (c->intermediate > 11264 || c->n_q_heads * c->head_dim > 11264) { why = "model too wide for the persistent decode step"; return QD_E_ARG; }
@@ -205,6 +218,7 @@ int alloc_gemm_workspace(qd_handle* h) {
     need = std::max(need, gemm_workspace_floats(T, c.n_q_heads * c.head_dim, c.hidden, h->ncu));
     need = std::max(need, gemm_workspace_floats(T, c.hidden, c.intermediate, h->ncu));
     need = std::max(need, gemm_workspace_floats(T, c.intermediate, c.hidden, h->ncu));
+    if (c.lora_rank_max) need = std::max(need, gemm_workspace_floats(T, c.hidden, 2 * c.lora_rank_max, h->ncu));
   }
   h->gws_floats = need;
   return need ? dev_alloc(h, &h->gws, need) : QD_OK;
@@ -227,11 +241,15 @@ int build_rope_tables(qd_handle* h) {
   return QD_OK;
 }
 
-void free_all(qd_handle* h) {
+void drop_decode_graph(qd_handle* h) {
   if (h->decode_exec) (void)hipGraphExecDestroy(h->decode_exec);
   if (h->decode_graph) (void)hipGraphDestroy(h->decode_graph);
   h->decode_exec = nullptr;
   h->decode_graph = nullptr;
+}
+
+void free_all(qd_handle* h) {
+  drop_decode_graph(h);
   for (void* p : h->allocs) (void)hipFree(p);
   h->allocs.clear();
   if (h->tokens_pinned) (void)hipHostFree(h->tokens_pinned);
@@ -304,6 +322,13 @@ void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows) {
     else
       launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, L.wqkv, nullptr, NQKV, L.bqkv, h->qkv, NQKV, h->gws,
                        h->gws_floats, h->ncu);
+    if (h->lora_rank) {  // the normed input halves are still in xh / xl
+      const int r2 = 2 * h->lora_rank;
+      launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, h->lora[l].a, nullptr, r2, nullptr, h->lu, r2, h->gws,
+                       h->gws_floats, h->ncu);
+      launch_lora_up(s, h->lu, r2, T, h->lora_rank, h->lora[l].bq, h->lora[l].bv, nq, c.n_kv_heads, d,
+                     h->lora_scale, h->qkv, NQKV);
+    }
     enqueue_attention(h, l, T, att_rows);
     launch_split_rows(s, h->o, nq * d, T, nq * d, nullptr, 0.f, h->xh, h->xl);
     if (q4)
@@ -350,6 +375,16 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
       else
         launch_gemv_bf16(s, L.wqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
                          h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
+    }
+    if (h->lora_rank) {
+      const int r2 = 2 * h->lora_rank;
+      for (int t0 = 0, tt = gemv_t_tile(H); t0 < T; t0 += tt) {
+        const int tn = std::min(tt, T - t0);
+        launch_gemv_bf16(s, h->lora[l].a, r2, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, nullptr,
+                         h->lu + (size_t)t0 * r2, r2, 0, h->ncu);
+      }
+      launch_lora_up(s, h->lu, r2, T, h->lora_rank, h->lora[l].bq, h->lora[l].bv, nq, c.n_kv_heads, d,
+                     h->lora_scale, h->qkv, NQKV);
     }
     enqueue_attention(h, l, T, att_rows);
     for (int t0 = 0, tt = tile(nq * d); t0 < T; t0 += tt) {
@@ -510,6 +545,15 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   }
   if (hipMemset(h->st, 0, sizeof(DevState)) != hipSuccess) return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
   h->layers.resize(c.n_layers);
+  if (c.lora_rank_max) {
+    const size_t r = c.lora_rank_max;
+    h->lora.resize(c.n_layers);
+    if ((rc = dev_alloc(h, &h->lu, rows * 2 * r))) return fail(rc);
+    for (auto& A : h->lora)
+      if ((rc = dev_alloc(h, &A.a, 2 * r * H)) || (rc = dev_alloc(h, &A.bq, (size_t)c.n_q_heads * d * r)) ||
+          (rc = dev_alloc(h, &A.bv, (size_t)c.n_kv_heads * d * r)))
+        return fail(rc);
+  }
   *out = h;
   return QD_OK;
 }
@@ -716,11 +760,37 @@ int qd_set_lora(qd_handle* h, const qd_lora* lora) {
   if (!h) return QD_E_ARG;
   if (!lora) return h->set_err(QD_E_ARG, "lora is NULL");
   if (lora->struct_size != sizeof(qd_lora)) return h->set_err(QD_E_ABI, "qd_lora.struct_size mismatch");
-  return h->set_err(QD_E_STATE, "LoRA not enabled (lora_rank_max = 0)");
+  const qd_config& c = h->cfg;
+  if (c.lora_rank_max == 0) return h->set_err(QD_E_STATE, "LoRA not enabled (lora_rank_max = 0)");
+  if (lora->rank < 1 || lora->rank > c.lora_rank_max) return h->set_err(QD_E_ARG, "rank must be in [1, lora_rank_max]");
+  if (!std::isfinite(lora->alpha)) return h->set_err(QD_E_ARG, "alpha must be finite");
+  if (!lora->a_q || !lora->b_q || !lora->a_v || !lora->b_v) return h->set_err(QD_E_ARG, "a LoRA array is NULL");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!lora->a_q[l] || !lora->b_q[l] || !lora->a_v[l] || !lora->b_v[l])
+      return h->set_err(QD_E_ARG, "NULL LoRA pointer in layer " + std::to_string(l));
+  const size_t r = lora->rank, H = c.hidden, d = c.head_dim;
+  hipStream_t s = h->stream;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LoraLayer& A = h->lora[l];
+    HIP_TRY(h, hipMemcpyAsync(A.a, lora->a_q[l], r * H * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(A.a + r * H, lora->a_v[l], r * H * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(A.bq, lora->b_q[l], (size_t)c.n_q_heads * d * r * 2, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(h, hipMemcpyAsync(A.bv, lora->b_v[l], (size_t)c.n_kv_heads * d * r * 2, hipMemcpyDeviceToDevice, s));
+  }
+  HIP_TRY(h, hipStreamSynchronize(s));
+  h->lora_rank = (int)r;
+  h->lora_scale = lora->alpha / (float)r;
+  drop_decode_graph(h);  // the next decode step captures the adapter's kernels
+  return QD_OK;
 }
 
 int qd_clear_lora(qd_handle* h) {
   if (!h) return QD_E_ARG;
+  if (h->lora_rank) {
+    HIP_TRY(h, hipStreamSynchronize(h->stream));  // the captured step may still be running
+    h->lora_rank = 0;
+    drop_decode_graph(h);
+  }
   return QD_OK;
 }
 

@@ -78,3 +78,8 @@ void launch_gemv_q4(hipStream_t s, const uint8_t* codes, const uint16_t* scales,
 void launch_gemv_gateup_q4(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su,
                            int N, int K, const float* x, int ldx, int T, const float* gain, float eps, float* a,
                            int lda, int ncu);
+
+// LoRA up products (lora.hip): for rows t < T, q rows of the fused q|k|v
+// output += scale B_q u[t][0, r), v rows += scale B_v u[t][r, 2 r).
+void launch_lora_up(hipStream_t s, const float* u, int ldu, int T, int r, const uint16_t* Bq, const uint16_t* Bv,
+                    int nq, int nkv, int d, float scale, float* qkv, int ldqkv);

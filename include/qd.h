@@ -150,7 +150,11 @@ enum {
 /* Validate *cfg (before any HIP call), then allocate the KV cache
  * ([n_layers][n_kv_heads][max_pos][head_dim] f32 for K and for V), workspaces
  * and RoPE tables on the current HIP device.  hip_stream is a hipStream_t
- * (NULL = the default stream); all later work is enqueued on it.
+ * that all later work is enqueued on; NULL makes the handle create (and own)
+ * a non-blocking stream of its own, which the legacy default stream does not
+ * wait for: then read outputs after qd_sync_token() or a device-wide
+ * synchronisation.  (A decode step is captured as a graph, which the legacy
+ * default stream cannot hold.)
  * On success *out receives a new handle.  Errors: QD_E_ARG, QD_E_ABI, QD_E_OOM, QD_E_HIP. */
 int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out);
 
@@ -178,8 +182,15 @@ int qd_prefill(qd_handle* h, const int32_t* tokens_host, int32_t n, const qd_sam
  * Errors: QD_E_STATE, QD_E_RANGE, QD_E_ARG (bad sampling). */
 int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev, int32_t* token_dev);
 
-/* Install (copy) a LoRA adapter; rank must be 1..lora_rank_max.  Clearing
- * restores the base model bit-for-bit (the adapter's kernels are not run). */
+/* Install (copy) a LoRA adapter ("EMBERGLASS (qwen-webgpu-lora) README", LoRA
+ * sections: a live low-rank adapter on q_proj and v_proj).  Needs
+ * lora_rank_max in 1..64 at qd_create (and decode_path QD_DECODE_GRAPH); rank
+ * must be in 1..lora_rank_max and alpha finite.  The adapter applies to every
+ * later prefill and decode step; the KV cache is kept.  Synchronises the
+ * stream.  qd_clear_lora removes it: the adapter's kernels no longer run, so
+ * outputs are bit-for-bit those of the base model.
+ * Errors: QD_E_STATE (lora_rank_max = 0), QD_E_ARG (rank, alpha, NULL array
+ * or layer pointer), QD_E_ABI, QD_E_HIP. */
 int qd_set_lora(qd_handle* h, const qd_lora* lora);
 int qd_clear_lora(qd_handle* h);
 

@@ -76,6 +76,15 @@ def test_int4_needs_the_graph_decode_path():
     assert rc == -1 and not h.value
 
 
+def test_lora_needs_the_graph_decode_path_and_a_bounded_rank():
+    cfg = qd.make_config(synth.TINY, max_prefill=16, lora_rank_max=16, decode_path=qd.QD_DECODE_PERSISTENT)
+    rc, h = _create(cfg)
+    assert rc == -1 and not h.value
+    cfg = qd.make_config(synth.TINY, max_prefill=16, lora_rank_max=65, decode_path=qd.QD_DECODE_GRAPH)
+    rc, h = _create(cfg)
+    assert rc == -1 and not h.value
+
+
 def test_create_rejects_null_config():
     lib = qd.load_library()
     h = ctypes.c_void_p()
