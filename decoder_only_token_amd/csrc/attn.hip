@@ -197,6 +197,153 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Causal attention for a prefill of T >= 2 rows (flash style, f32 on the VALU).
+// Query row t sits at position pos + t (pos = the step state's position) and
+// sees cache positions 0 .. pos + t, its own included.
+//
+// grid (nkv, ceil(T / (64 / G))), block 256.  A block owns kv head g and 64
+// query vectors: 64 / G consecutive rows times the G query heads of g, so a
+// K/V tile in LDS serves all of them.  Per tile of 32 cache positions:
+//   scores: each thread forms a 2 (query) x 4 (position) tile of dot products
+//           from LDS (queries pre-scaled by 1 / sqrt(d));
+//   online softmax: the 8 threads that share a query pair reduce the tile's
+//           max and sum with shuffles, rescale the running state and write the
+//           probabilities (transposed) to LDS;
+//   values: each thread accumulates an 8 (query) x 4 (dim) tile of outputs.
+// K and V of a tile share one LDS buffer (V is held in registers while the
+// scores are formed), which keeps the block under 64 KiB of LDS.
+// Blocks with the longest causal ranges start first.
+template <int G>
+__global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q, int T, int nq,
+                                                      const float* __restrict__ Kc, const float* __restrict__ Vc,
+                                                      int max_pos, const DevState* __restrict__ st, float scale,
+                                                      float* __restrict__ o_out, int ldo) {
+  constexpr int QV = 64, R = QV / G, BK = 32, RS = D + 4;
+  __shared__ __align__(16) float Qs[QV * RS];
+  __shared__ __align__(16) float KVs[BK * RS];  // K of the tile, then its V
+  __shared__ __align__(16) float Pt[BK * QV];
+  __shared__ float cs[QV];
+  __shared__ float ls[QV];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int t0 = (gridDim.y - 1 - blockIdx.y) * R;
+  const int pos0 = st->pos;
+  const int nrows = min(R, T - t0);
+  const int kv_end = pos0 + t0 + nrows;  // one past the last row's position
+
+  for (int i = tid; i < QV * D / 4; i += 256) {
+    const int v = i / (D / 4), c4 = i % (D / 4), r = v / G, j = v % G;
+    f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (r < nrows) val = *reinterpret_cast<const f32x4*>(q + ((size_t)(t0 + r) * nq + g * G + j) * D + c4 * 4) * scale;
+    *reinterpret_cast<f32x4*>(Qs + v * RS + c4 * 4) = val;
+  }
+  const int qi = tid >> 3, kj = tid & 7;  // score mapping: queries 2 qi, 2 qi + 1; positions 4 kj .. + 3
+  const int qg = tid >> 5, dg = tid & 31; // value mapping: queries 8 qg .. + 7; dims 4 dg .. + 3
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  int qpos[2];
+  bool live[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int r = (2 * qi + a) / G;
+    live[a] = r < nrows;
+    qpos[a] = pos0 + t0 + r;
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) o[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* Kg = Kc + (size_t)g * max_pos * D;
+  const float* Vg = Vc + (size_t)g * max_pos * D;
+
+  for (int k0 = 0; k0 < kv_end; k0 += BK) {
+    const int nk = min(BK, kv_end - k0);
+    f32x4 vr[BK * D / 4 / 256];
+    __syncthreads();  // queries staged; the previous tile consumed
+#pragma unroll
+    for (int u = 0; u < BK * D / 4 / 256; ++u) {
+      const int i = tid + u * 256, p = i / (D / 4), c4 = i % (D / 4);
+      f32x4 kv = f32x4{0.f, 0.f, 0.f, 0.f};
+      vr[u] = kv;
+      if (p < nk) {
+        kv = *reinterpret_cast<const f32x4*>(Kg + (size_t)(k0 + p) * D + c4 * 4);
+        vr[u] = *reinterpret_cast<const f32x4*>(Vg + (size_t)(k0 + p) * D + c4 * 4);
+      }
+      *reinterpret_cast<f32x4*>(KVs + p * RS + c4 * 4) = kv;
+    }
+    __syncthreads();
+    float sc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) sc[a][b] = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < D; c += 4) {
+      const f32x4 qa = *reinterpret_cast<const f32x4*>(Qs + (2 * qi) * RS + c);
+      const f32x4 qb = *reinterpret_cast<const f32x4*>(Qs + (2 * qi + 1) * RS + c);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(KVs + (4 * kj + b) * RS + c);
+        sc[0][b] = fmaf(qa.x, kv.x, fmaf(qa.y, kv.y, fmaf(qa.z, kv.z, fmaf(qa.w, kv.w, sc[0][b]))));
+        sc[1][b] = fmaf(qb.x, kv.x, fmaf(qb.y, kv.y, fmaf(qb.z, kv.z, fmaf(qb.w, kv.w, sc[1][b]))));
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int pl = 4 * kj + b;
+        if (!live[a] || pl >= nk || k0 + pl > qpos[a]) sc[a][b] = -INFINITY;
+        tmax = fmaxf(tmax, sc[a][b]);
+      }
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off, QD_WAVE));
+      const float mn = fmaxf(m[a], tmax);
+      const float mref = mn == -INFINITY ? 0.f : mn;  // a query with nothing visible yet
+      float ps = 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float p = __expf(sc[a][b] - mref);
+        Pt[(4 * kj + b) * QV + 2 * qi + a] = p;
+        ps += p;
+      }
+      ps = group_sum<8>(ps);
+      const float c = __expf(m[a] - mref);
+      l[a] = l[a] * c + ps;
+      m[a] = mn;
+      if (kj == 0) cs[2 * qi + a] = c;
+    }
+    __syncthreads();  // every score formed: the buffer takes V
+#pragma unroll
+    for (int u = 0; u < BK * D / 4 / 256; ++u) {
+      const int i = tid + u * 256, p = i / (D / 4), c4 = i % (D / 4);
+      *reinterpret_cast<f32x4*>(KVs + p * RS + c4 * 4) = vr[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 8; ++a) o[a] = o[a] * cs[8 * qg + a];
+    for (int p = 0; p < nk; ++p) {
+      const f32x4 vv = *reinterpret_cast<const f32x4*>(KVs + p * RS + 4 * dg);
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(Pt + p * QV + 8 * qg);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(Pt + p * QV + 8 * qg + 4);
+      o[0] += pa.x * vv; o[1] += pa.y * vv; o[2] += pa.z * vv; o[3] += pa.w * vv;
+      o[4] += pb.x * vv; o[5] += pb.y * vv; o[6] += pb.z * vv; o[7] += pb.w * vv;
+    }
+  }
+  if (kj == 0) {
+    ls[2 * qi] = l[0];
+    ls[2 * qi + 1] = l[1];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int v = 8 * qg + a, r = v / G, j = v % G;
+    if (r < nrows)
+      *reinterpret_cast<f32x4*>(o_out + (size_t)(t0 + r) * ldo + (g * G + j) * D + 4 * dg) = o[a] * (1.0f / ls[v]);
+  }
+}
+
 }  // namespace
 
 int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin) {
@@ -218,4 +365,18 @@ void launch_attention_decode(hipStream_t s, const float* q, int nq, int nkv, con
     default: return;  // rejected by the host before any launch
   }
   hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32), dim3(256), 0, s, part, S, cmin, st, o_out);
+}
+
+void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const float* Kc, const float* Vc,
+                              int max_pos, const DevState* st, float* o_out, int ldo) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const int G = nq / nkv;
+  const dim3 grid(nkv, (T + 64 / G - 1) / (64 / G));
+  switch (G) {
+    case 1: hipLaunchKernelGGL(k_attn_prefill<1>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, ldo); break;
+    case 2: hipLaunchKernelGGL(k_attn_prefill<2>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, ldo); break;
+    case 4: hipLaunchKernelGGL(k_attn_prefill<4>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, ldo); break;
+    case 8: hipLaunchKernelGGL(k_attn_prefill<8>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, ldo); break;
+    default: break;  // rejected by the host before any launch
+  }
 }

@@ -21,7 +21,6 @@
 
 namespace {
 
-constexpr int kAttnChunk = 64;  // cache positions per split-K attention block (prefill)
 constexpr int kDecodeMinSplit = 16;  // shortest split of the decode attention
 constexpr int kGemmMinRows = 16;  // prefills of at least this many rows use the matrix-core projections
 
@@ -154,17 +153,6 @@ int dev_alloc(qd_handle* h, T** p, size_t n) {
 
 int qkv_rows(const qd_config& c) { return (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim; }
 
-int attn_splits(int ctx) { return (ctx + kAttnChunk - 1) / kAttnChunk; }
-
-// Rows of attention partials the workspace holds at once for a prefill.
-int attn_row_chunk(const qd_config& c) {
-  const size_t per_row = (size_t)c.n_q_heads * attn_splits(c.max_pos) * (c.head_dim + 2);
-  size_t rows = ((size_t)64 << 20) / sizeof(float) / per_row;  // 64 MiB budget
-  if (rows < 1) rows = 1;
-  if (rows > (size_t)c.max_prefill) rows = c.max_prefill;
-  return (int)rows;
-}
-
 int gemv_t_tile(int K) {
   int t = (16384 - 64) / K;  // keep the staged input (plus the reduction slots) within 64 KiB of LDS
   if (t > GEMV_MAX_T) t = GEMV_MAX_T;
@@ -258,8 +246,8 @@ void free_all(qd_handle* h) {
   h->stream = nullptr;
 }
 
-void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows);
-void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows);
+void enqueue_layers_gemm(qd_handle* h, int T, bool capture);
+void enqueue_layers_gemv(qd_handle* h, int T, bool capture);
 
 // Enqueue the whole forward for T new rows whose ids are at `tok` (device),
 // at positions st->pos .. st->pos + T - 1, and choose the next token from the
@@ -270,11 +258,10 @@ void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
   const int H = c.hidden;
   launch_embed(s, h->embed, tok, T, H, h->x);
   if (capture) (void)hipMemcpyAsync(h->cap, h->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice, s);
-  const int att_rows = T == 1 ? 1 : attn_row_chunk(c);
   if (T >= kGemmMinRows) {
-    enqueue_layers_gemm(h, T, capture, att_rows);
+    enqueue_layers_gemm(h, T, capture);
   } else {
-    enqueue_layers_gemv(h, T, capture, att_rows);
+    enqueue_layers_gemv(h, T, capture);
   }
   float* xf_cap = capture ? h->cap + (size_t)(c.n_layers + 1) * c.max_prefill * H : nullptr;
   launch_lmhead_bf16(s, h->embed, c.vocab, H, h->x + (size_t)(T - 1) * H, h->final_norm, c.rms_eps, h->logits,
@@ -285,7 +272,7 @@ void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
 }
 
 // Attention for T new rows (shared by both projection paths).
-void enqueue_attention(qd_handle* h, int l, int T, int att_rows) {
+void enqueue_attention(qd_handle* h, int l, int T) {
   const qd_config& c = h->cfg;
   hipStream_t s = h->stream;
   const int d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
@@ -297,17 +284,13 @@ void enqueue_attention(qd_handle* h, int l, int T, int att_rows) {
     launch_attention_decode(s, h->q, nq, nkv, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st,
                             h->dec_splits, kDecodeMinSplit, h->part, h->o);
   } else {
-    for (int t0 = 0; t0 < T; t0 += att_rows) {
-      const int tn = std::min(att_rows, T - t0);
-      const int S = attn_splits(h->pos + t0 + tn);
-      launch_attention(s, h->q + (size_t)t0 * nq * d, tn, nq, nkv, d, h->Kc + l * layer_kv, h->Vc + l * layer_kv,
-                       c.max_pos, h->st, kAttnChunk, S, h->part, h->o + (size_t)t0 * nq * d, nq * d, t0);
-    }
+    launch_attention_prefill(s, h->q, T, nq, nkv, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, h->o,
+                             nq * d);
   }
 }
 
 // Layers with the matrix-core projections (T >= kGemmMinRows).
-void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows) {
+void enqueue_layers_gemm(qd_handle* h, int T, bool capture) {
   const qd_config& c = h->cfg;
   const bool q4 = c.weight_format == QD_W_INT4_G128;
   hipStream_t s = h->stream;
@@ -329,7 +312,7 @@ void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows) {
       launch_lora_up(s, h->lu, r2, T, h->lora_rank, h->lora[l].bq, h->lora[l].bv, nq, c.n_kv_heads, d,
                      h->lora_scale, h->qkv, NQKV);
     }
-    enqueue_attention(h, l, T, att_rows);
+    enqueue_attention(h, l, T);
     launch_split_rows(s, h->o, nq * d, T, nq * d, nullptr, 0.f, h->xh, h->xl);
     if (q4)
       launch_gemm_q4(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.co, L.so, nullptr, nullptr, H, nullptr, h->x, H, h->gws,
@@ -358,7 +341,7 @@ void enqueue_layers_gemm(qd_handle* h, int T, bool capture, int att_rows) {
 }
 
 // Layers with the T-row GEMV projections (decode and short prefills).
-void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
+void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
   const qd_config& c = h->cfg;
   hipStream_t s = h->stream;
   const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, I = c.intermediate;
@@ -386,7 +369,7 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture, int att_rows) {
       launch_lora_up(s, h->lu, r2, T, h->lora_rank, h->lora[l].bq, h->lora[l].bv, nq, c.n_kv_heads, d,
                      h->lora_scale, h->qkv, NQKV);
     }
-    enqueue_attention(h, l, T, att_rows);
+    enqueue_attention(h, l, T);
     for (int t0 = 0, tt = tile(nq * d); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
       if (q4)
@@ -491,9 +474,8 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   }
   const size_t H = c.hidden, d = c.head_dim, I = c.intermediate, rows = c.max_prefill;
   const size_t kv = (size_t)c.n_layers * c.n_kv_heads * c.max_pos * d;
-  h->part_floats = (size_t)(c.max_prefill > 1 ? attn_row_chunk(c) : 1) * c.n_q_heads * attn_splits(c.max_pos) * (d + 2);
   h->dec_splits = attn_decode_splits(c.max_pos, c.n_kv_heads, h->ncu, kDecodeMinSplit);
-  h->part_floats = std::max(h->part_floats, (size_t)c.n_q_heads * h->dec_splits * (d + 2));
+  h->part_floats = (size_t)c.n_q_heads * h->dec_splits * (d + 2);
   if ((rc = dev_alloc(h, &h->Kc, kv)) || (rc = dev_alloc(h, &h->Vc, kv)) ||
       (rc = dev_alloc(h, &h->rope_cos, (size_t)c.max_pos * d / 2)) ||
       (rc = dev_alloc(h, &h->rope_sin, (size_t)c.max_pos * d / 2)) || (rc = dev_alloc(h, &h->x, rows * H)) ||

@@ -411,115 +411,3 @@ void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq
                      sin_t, st, q_out, Kc, Vc, max_pos);
 }
 
-// ---------------------------------------------------------------------------
-// Split-K decode attention (query row t sits at position pos+row0+t), GQA.
-// grid (nkv, S, T), block 256.  Block (g, s, t) covers cache positions
-// [s*chunk, min((s+1)*chunk, ctx)), ctx = pos + t + 1, for the G = nq/nkv query
-// heads of kv head g, so each K/V row is read once for the whole group.
-// Each half-wave holds one position per iteration (32 lanes x 4 dims = 128);
-// the running maximum / sum / weighted V (online softmax) stay in registers,
-// then the 8 half-wave states are merged in a fixed order through LDS.
-// Writes partials part[t][h][s] = {m, l, o[0..d)} (o not yet divided by l).
-// "EMBERGLASS README", split-K flash-style decode attention.
-template <int G>
-__global__ __launch_bounds__(256) void k_attn_splitk(const float* __restrict__ q, int nq, int nkv,
-                                                     const float* __restrict__ Kc, const float* __restrict__ Vc,
-                                                     int max_pos, const DevState* __restrict__ st, int chunk,
-                                                     int S, float scale, float* __restrict__ part, int row0) {
-  constexpr int D = 128;
-  const int g = blockIdx.x, sp = blockIdx.y, t = blockIdx.z;
-  const int ctx = st->pos + row0 + t + 1;
-  const int p_begin = sp * chunk;
-  const int p_end = min(p_begin + chunk, ctx);
-  if (p_begin >= p_end) return;  // the merge only reads splits below ceil(ctx/chunk)
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int hw = wave * 2 + (lane >> 5);  // half-wave id 0..7
-  const int sub = lane & 31;              // dims 4*sub .. 4*sub+3
-  f32x4 qv[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j)
-    qv[j] = *reinterpret_cast<const f32x4*>(q + ((size_t)t * nq + g * G + j) * D + sub * 4);
-  float m[G], l[G];
-  f32x4 o[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) { m[j] = -INFINITY; l[j] = 0.f; o[j] = f32x4{0, 0, 0, 0}; }
-  const float* Kg = Kc + (size_t)g * max_pos * D;
-  const float* Vg = Vc + (size_t)g * max_pos * D;
-  for (int p = p_begin + hw; p < p_end; p += 8) {
-    f32x4 kv = *reinterpret_cast<const f32x4*>(Kg + (size_t)p * D + sub * 4);
-    f32x4 vv = *reinterpret_cast<const f32x4*>(Vg + (size_t)p * D + sub * 4);
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float sdot = qv[j].x * kv.x + qv[j].y * kv.y + qv[j].z * kv.z + qv[j].w * kv.w;
-      sdot = group_sum<32>(sdot) * scale;
-      const float mn = fmaxf(m[j], sdot);
-      const float corr = __expf(m[j] - mn);
-      const float pw = __expf(sdot - mn);
-      l[j] = l[j] * corr + pw;
-      o[j] = o[j] * corr + vv * pw;
-      m[j] = mn;
-    }
-  }
-  // merge the 8 half-wave states: LDS [8][G][D + 2]
-  __shared__ float sm[8 * G * (D + 2)];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float* e = sm + (hw * G + j) * (D + 2);
-    *reinterpret_cast<f32x4*>(e + 2 + sub * 4) = o[j];
-    if (sub == 0) { e[0] = m[j]; e[1] = l[j]; }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int j = idx / D, dd = idx % D;
-    float M = -INFINITY;
-    for (int w = 0; w < 8; ++w) M = fmaxf(M, sm[(w * G + j) * (D + 2)]);
-    float L = 0.f, acc = 0.f;
-    for (int w = 0; w < 8; ++w) {
-      const float* e = sm + (w * G + j) * (D + 2);
-      if (e[0] == -INFINITY) continue;  // half-wave saw no position
-      const float f = __expf(e[0] - M);
-      L += e[1] * f;
-      acc += e[2 + dd] * f;
-    }
-    float* out = part + (((size_t)t * nq + g * G + j) * S + sp) * (D + 2);
-    out[2 + dd] = acc;
-    if (dd == 0) { out[0] = M; out[1] = L; }
-  }
-}
-
-// Merge the split partials of each (t, head): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M},
-// splits taken in increasing order.  grid (nq, T), block D.
-__global__ void k_attn_merge(const float* __restrict__ part, int nq, int S, int chunk, const DevState* __restrict__ st,
-                             float* __restrict__ o_out, int ldo, int row0) {
-  constexpr int D = 128;
-  const int h = blockIdx.x, t = blockIdx.y, dd = threadIdx.x;
-  const int ctx = st->pos + row0 + t + 1;
-  const int s_act = min(S, (ctx + chunk - 1) / chunk);
-  const float* base = part + ((size_t)t * nq + h) * S * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < s_act; ++s) M = fmaxf(M, base[s * (D + 2)]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < s_act; ++s) {
-    const float* e = base + s * (D + 2);
-    const float f = __expf(e[0] - M);
-    L += e[1] * f;
-    acc += e[2 + dd] * f;
-  }
-  o_out[(size_t)t * ldo + h * D + dd] = acc / L;
-}
-
-void launch_attention(hipStream_t s, const float* q, int T, int nq, int nkv, int d, const float* Kc, const float* Vc,
-                      int max_pos, const DevState* st, int chunk, int S, float* part, float* o_out, int ldo,
-                      int row0) {
-  const float scale = 1.0f / sqrtf((float)d);
-  dim3 grid(nkv, S, T);
-  const int G = nq / nkv;
-  switch (G) {
-    case 1: hipLaunchKernelGGL(k_attn_splitk<1>, grid, dim3(256), 0, s, q, nq, nkv, Kc, Vc, max_pos, st, chunk, S, scale, part, row0); break;
-    case 2: hipLaunchKernelGGL(k_attn_splitk<2>, grid, dim3(256), 0, s, q, nq, nkv, Kc, Vc, max_pos, st, chunk, S, scale, part, row0); break;
-    case 4: hipLaunchKernelGGL(k_attn_splitk<4>, grid, dim3(256), 0, s, q, nq, nkv, Kc, Vc, max_pos, st, chunk, S, scale, part, row0); break;
-    case 8: hipLaunchKernelGGL(k_attn_splitk<8>, grid, dim3(256), 0, s, q, nq, nkv, Kc, Vc, max_pos, st, chunk, S, scale, part, row0); break;
-    default: break;  // rejected by the host before any launch
-  }
-  hipLaunchKernelGGL(k_attn_merge, dim3(nq, T), dim3(d), 0, s, part, nq, S, chunk, st, o_out, ldo, row0);
-}

@@ -317,3 +317,36 @@ def test_tiny_batched_prefill_matrix_cores(torch_cuda, n):
     # the next token continues from the batched cache
     assert dec.sync_token() == int(np.argmax(cap["logits"][-1])) or \
         cap["logits"][-1][dec.sync_token()] >= np.max(cap["logits"][-1]) - 4e-3
+
+
+@pytest.mark.parametrize("shape_name,chunks", [("TINY", (100, 137, 63, 1, 40)), ("TINY_INT4", (200, 17, 2, 150))])
+def test_chunked_prefill_attention(torch_cuda, shape_name, chunks):
+    """Prompts fed in several prefill calls: each call's rows attend to the cache
+    of the earlier calls plus their own causal prefix (flash prefill tiles of
+    32 positions; 64 query vectors per block).  The logits after every call
+    are checked against the oracle."""
+    import dataclasses
+    import torch
+    base = getattr(synth, shape_name)
+    shape = dataclasses.replace(base, max_pos=512)
+    log(f"chunked prefill {shape.name} {chunks}")
+    w = synth.make_weights(shape, seed=71, random_gains=True)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 256, path="graph")
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = synth.make_prompt(shape.vocab, sum(chunks), seed=72)
+    cache = oracle.new_cache(sum(chunks) + 16)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    dec.reset_kv()
+    at = 0
+    for n in chunks:
+        dec.prefill(prompt[at:at + n], logits_out=logits)
+        want = oracle.forward(prompt[at:at + n], cache, logits_rows="last")[-1]
+        at += n
+        torch.cuda.synchronize()
+        ok, ratio, nbad = logits_within_tol(logits.cpu().numpy(), want)
+        log(f"after {at} rows: err/tol {ratio:.3f}")
+        assert ok, (at, ratio, nbad)
+    assert dec.position == at
