@@ -10,7 +10,14 @@
 // The split count S is fixed for the life of the engine (so one captured
 // graph serves every position); the split length is C = max(cmin, ceil(ctx /
 // S)), computed on the device from the step state, and splits past the end of
-// the context do nothing.  Within a split, positions go in tiles of 64:
+// the context do nothing.
+//
+// The block also finishes the new row's q and k: the raw q|k|v projection of
+// its group is read, q and k get the per-head RMSNorm (when the model has it)
+// and RoPE at the new position ("flashmoon demo/README.md", RoPE applied as K
+// is written), and the block whose split ends at the new position writes k
+// and v into the cache for later steps and uses them from LDS for this one.
+// Within a split, positions go in tiles of 64:
 //   1. each thread loads 32 dims of K and of V of one position (4 threads per
 //      position, 16-byte loads, a wave reads 16 consecutive rows);
 //   2. scores s = q_j . k / sqrt(d) from K in registers and q in LDS;
@@ -43,13 +50,33 @@ __device__ __forceinline__ int split_len(int ctx, int S, int cmin) { return max(
 
 // grid (nkv, S), block 256.  Partials part[h][s] = {m, l, o[0..D)} for query
 // head h = g G + j (o not divided by l).
+// One head of the new row: optional RMSNorm over its D values (gain), then
+// RoPE with the half-split pairing (j, j + D/2) at table row `pos`.  Lane l of
+// the wave holds dims l and l + 64; the results go to out[l], out[l + 64].
+__device__ __forceinline__ void norm_rope_head(const float* __restrict__ src, const float* __restrict__ gain,
+                                               float eps, const float* __restrict__ cos_t,
+                                               const float* __restrict__ sin_t, int pos, float* out) {
+  const int l = threadIdx.x & 63;
+  float a = src[l], b = src[l + 64];
+  if (gain) {
+    const float r = 1.0f / sqrtf(wave_sum(a * a + b * b) / (float)D + eps);
+    a = a * r * gain[l];
+    b = b * r * gain[l + 64];
+  }
+  const float c = cos_t[(size_t)pos * (D / 2) + l], s = sin_t[(size_t)pos * (D / 2) + l];
+  out[l] = a * c - b * s;
+  out[l + 64] = b * c + a * s;
+}
+
 template <int G>
-__global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q, const float* __restrict__ Kc,
-                                                     const float* __restrict__ Vc, int max_pos,
+__global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ qkv, const float* __restrict__ qn,
+                                                     const float* __restrict__ kn, float eps,
+                                                     const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+                                                     float* __restrict__ Kc, float* __restrict__ Vc, int max_pos,
                                                      const DevState* __restrict__ st, int S, int cmin, float scale,
                                                      float* __restrict__ part) {
   const int g = blockIdx.x, sp = blockIdx.y;
-  const int ctx = st->pos + 1;
+  const int ctx = st->pos + 1, pos = ctx - 1;
   const int C = split_len(ctx, S, cmin);
   const int p_begin = sp * C;
   if (p_begin >= ctx) return;  // the merge reads only the splits that hold positions
@@ -59,10 +86,24 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
   __shared__ __align__(16) float vs[TP * D];
   __shared__ __align__(16) float ps[G * TP];  // scores, then probabilities
   __shared__ float cs[G];                     // per-head rescale of this tile
+  __shared__ __align__(16) float kv_new[2 * D];  // k (normed, rotated) and v of the new row
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < G * D / 4; i += 256)
-    reinterpret_cast<f32x4*>(qs)[i] = reinterpret_cast<const f32x4*>(q + (size_t)g * G * D)[i];
+  // group-major projection rows: [q heads g G .. g G + G - 1 | k_g | v_g] x D
+  const float* grp = qkv + (size_t)g * (G + 2) * D;
+  for (int j = wave; j < G; j += 4) norm_rope_head(grp + j * D, qn, eps, cos_t, sin_t, pos, qs + j * D);
+  const bool owns_new = p_end == ctx;
+  if (owns_new && wave == 3) {  // wave 3 has the fewest q heads
+    norm_rope_head(grp + G * D, kn, eps, cos_t, sin_t, pos, kv_new);
+    kv_new[D + lane] = grp[(G + 1) * D + lane];
+    kv_new[D + 64 + lane] = grp[(G + 1) * D + 64 + lane];
+    float* kr = Kc + ((size_t)g * max_pos + pos) * D;
+    float* vr = Vc + ((size_t)g * max_pos + pos) * D;
+    kr[lane] = kv_new[lane];
+    kr[lane + 64] = kv_new[lane + 64];
+    vr[lane] = kv_new[D + lane];
+    vr[lane + 64] = kv_new[D + 64 + lane];
+  }
 
   const int pl = tid >> 2, sub = tid & 3;  // load / score mapping: position, quarter of the dims
   const int dd = tid & 127, jh = tid >> 7; // output mapping: dim, head parity
@@ -80,7 +121,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
   for (int t0 = p_begin; t0 < p_end; t0 += TP) {
     const int n = min(TP, p_end - t0);
     f32x4 kr[8], vr[8];
-    if (pl < n) {
+    const bool fresh = owns_new && t0 + pl == pos;  // the new row: from LDS, not the cache
+    if (pl < n && !fresh) {
       const size_t off = (size_t)(t0 + pl) * D + sub * 32;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -91,7 +133,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
 #pragma unroll
       for (int i = 0; i < 8; ++i) kr[i] = vr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();  // q staged; the previous tile's V and probabilities consumed
+    __syncthreads();  // q (and the new k, v) staged; the previous tile's V and probabilities consumed
+    if (fresh) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kr[i] = reinterpret_cast<const f32x4*>(kv_new + sub * 32)[i];
+        vr[i] = reinterpret_cast<const f32x4*>(kv_new + D + sub * 32)[i];
+      }
+    }
     if (pl < n) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) reinterpret_cast<f32x4*>(vs + pl * D + sub * 32)[i] = vr[i];
@@ -297,8 +346,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
         if (!live[a] || pl >= nk || k0 + pl > qpos[a]) sc[a][b] = -INFINITY;
         tmax = fmaxf(tmax, sc[a][b]);
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off, QD_WAVE));
+      tmax = group_max<8>(tmax);
       const float mn = fmaxf(m[a], tmax);
       const float mref = mn == -INFINITY ? 0.f : mn;  // a query with nothing visible yet
       float ps = 0.f;
@@ -353,17 +401,22 @@ int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin) {
   return std::max(s, 1);
 }
 
-void launch_attention_decode(hipStream_t s, const float* q, int nq, int nkv, const float* Kc, const float* Vc,
+void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, const float* kn, float eps,
+                             const float* cos_t, const float* sin_t, int nq, int nkv, float* Kc, float* Vc,
                              int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out) {
   const float scale = 1.0f / sqrtf((float)D);
   const dim3 grid(nkv, S);
+#define QD_ATTN_DECODE(G_)                                                                                          \
+  hipLaunchKernelGGL(k_attn_decode<G_>, grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, Kc, Vc, max_pos, st, \
+                     S, cmin, scale, part)
   switch (nq / nkv) {
-    case 1: hipLaunchKernelGGL(k_attn_decode<1>, grid, dim3(256), 0, s, q, Kc, Vc, max_pos, st, S, cmin, scale, part); break;
-    case 2: hipLaunchKernelGGL(k_attn_decode<2>, grid, dim3(256), 0, s, q, Kc, Vc, max_pos, st, S, cmin, scale, part); break;
-    case 4: hipLaunchKernelGGL(k_attn_decode<4>, grid, dim3(256), 0, s, q, Kc, Vc, max_pos, st, S, cmin, scale, part); break;
-    case 8: hipLaunchKernelGGL(k_attn_decode<8>, grid, dim3(256), 0, s, q, Kc, Vc, max_pos, st, S, cmin, scale, part); break;
+    case 1: QD_ATTN_DECODE(1); break;
+    case 2: QD_ATTN_DECODE(2); break;
+    case 4: QD_ATTN_DECODE(4); break;
+    case 8: QD_ATTN_DECODE(8); break;
     default: return;  // rejected by the host before any launch
   }
+#undef QD_ATTN_DECODE
   hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32), dim3(256), 0, s, part, S, cmin, st, o_out);
 }
 

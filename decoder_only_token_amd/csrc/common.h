@@ -14,25 +14,58 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Sum over the 64 lanes of a wave; every lane receives the total.
+// Lane exchange within rows of 16 lanes through DPP (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7 - i within each 8
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15 - i within each 16
+
+// Sum over the 64 lanes of a wave (all lanes active); every lane receives the
+// total.  Fixed order: pairs, quads, halves and rows of 16 by DPP, then the
+// four rows.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, QD_WAVE);
-  return v;
+  v += dpp_f<kDppQuadSwap1>(v);
+  v += dpp_f<kDppQuadSwap2>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  v += dpp_f<kDppRowMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+// Sum / maximum over aligned groups of WIDTH lanes (2, 4, 8 or 16), all lanes
+// active; every lane of a group receives its group's result.
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = WIDTH / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, QD_WAVE);
+  static_assert(WIDTH == 2 || WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "group width");
+  v += dpp_f<kDppQuadSwap1>(v);
+  if (WIDTH >= 4) v += dpp_f<kDppQuadSwap2>(v);
+  if (WIDTH >= 8) v += dpp_f<kDppRowHalfMirror>(v);
+  if (WIDTH >= 16) v += dpp_f<kDppRowMirror>(v);
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(WIDTH == 2 || WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "group width");
+  v = fmaxf(v, dpp_f<kDppQuadSwap1>(v));
+  if (WIDTH >= 4) v = fmaxf(v, dpp_f<kDppQuadSwap2>(v));
+  if (WIDTH >= 8) v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  if (WIDTH >= 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
   return v;
 }
 
+// Maximum over the 64 lanes of a wave (all lanes active), to every lane.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, QD_WAVE));
-  return v;
+  v = fmaxf(v, dpp_f<kDppQuadSwap1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // Block-wide sum for blockDim.x == 256 (4 waves); all threads get the result.

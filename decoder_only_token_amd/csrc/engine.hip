@@ -278,12 +278,13 @@ void enqueue_attention(qd_handle* h, int l, int T) {
   const int d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const size_t layer_kv = (size_t)nkv * c.max_pos * d;
   const Layer& L = h->layers[l];
-  launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
-                    h->st, h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
-  if (T == 1) {
-    launch_attention_decode(s, h->q, nq, nkv, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st,
-                            h->dec_splits, kDecodeMinSplit, h->part, h->o);
+  if (T == 1) {  // QK-norm, RoPE and the cache write happen inside the decode attention
+    launch_attention_decode(s, h->qkv, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin, nq, nkv,
+                            h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, h->dec_splits,
+                            kDecodeMinSplit, h->part, h->o);
   } else {
+    launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
+                      h->st, h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
     launch_attention_prefill(s, h->q, T, nq, nkv, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, h->o,
                              nq * d);
   }

@@ -31,10 +31,13 @@ void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* pa
 void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq, int nkv, int d, const float* qn,
                        const float* kn, float eps, const float* cos_t, const float* sin_t, const DevState* st,
                        float* q_out, float* Kc, float* Vc, int max_pos);
-// Decode attention for one new row (attn.hip): S splits of length
-// max(cmin, ceil(ctx / S)); part holds nq * S * (d + 2) floats.
+// Decode attention for one new row (attn.hip), from the raw q|k|v projection
+// row (group-major): QK-norm (gains may be null), RoPE, the cache write of the
+// new k / v, then S splits of length max(cmin, ceil(ctx / S)); part holds
+// nq * S * (d + 2) floats.
 int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin);
-void launch_attention_decode(hipStream_t s, const float* q, int nq, int nkv, const float* Kc, const float* Vc,
+void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, const float* kn, float eps,
+                             const float* cos_t, const float* sin_t, int nq, int nkv, float* Kc, float* Vc,
                              int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out);
 
 // Causal attention of T >= 2 new rows (attn.hip), rows at positions pos .. pos + T - 1.

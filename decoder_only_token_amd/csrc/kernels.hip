@@ -29,17 +29,32 @@ void launch_embed(hipStream_t s, const uint16_t* E, const int32_t* tok, int T, i
 // Input staging shared by the GEMV kernels: rows [T][K] of the input into LDS,
 // optionally RMS-normalised with gains (RMSNorm as a GEMV prologue).
 // h[t][k] = x[t][k] * g[k] / sqrt(mean_k x[t][k]^2 + eps)
+// Each thread requests up to kStageBatch 16-byte pieces before storing any, so
+// a row costs one L2 round trip per 4096 (or 12288) columns, not one per 1024.
+constexpr int kStageBatch = 12;
+
 __device__ __forceinline__ void stage_input(const float* __restrict__ x, int ldx, int T, int K,
                                             const float* __restrict__ gain, float eps, float* h, float* red) {
   for (int t = 0; t < T; ++t) {
     const float* xr = x + (size_t)t * ldx;
     float ss = 0.f;
-    for (int k = threadIdx.x * 4; k < K; k += 1024) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(xr + k);
-      *reinterpret_cast<f32x4*>(h + t * K + k) = v;
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    for (int k0 = 0; k0 < K; k0 += kStageBatch * 1024) {
+      f32x4 v[kStageBatch];
+#pragma unroll
+      for (int i = 0; i < kStageBatch; ++i) {
+        const int k = k0 + (threadIdx.x + i * 256) * 4;
+        if (k < K) v[i] = *reinterpret_cast<const f32x4*>(xr + k);
+      }
+#pragma unroll
+      for (int i = 0; i < kStageBatch; ++i) {
+        const int k = k0 + (threadIdx.x + i * 256) * 4;
+        if (k < K) {
+          *reinterpret_cast<f32x4*>(h + t * K + k) = v[i];
+          ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+        }
+      }
     }
-    if (gain) {
+    if (gain) {  // each thread rescales the pieces it stored
       float tot = block_sum_256(ss, red);
       float r = 1.0f / sqrtf(tot / (float)K + eps);
       for (int k = threadIdx.x * 4; k < K; k += 1024) {
@@ -58,12 +73,11 @@ __device__ __forceinline__ void stage_input(const float* __restrict__ x, int ldx
 //   y[t][n] (=|+=) sum_k W[n][k] * h[t][k] (+ bias[n])
 // W row-major [N][K] (the [out, in] layout of the pages).  Each wave owns RPW
 // consecutive output rows; each lane streams 16-byte chunks of those rows,
-// 512 columns per pass of the wave.  The first pass's weights are requested
-// before the input is staged and each later pass is requested while the
-// previous one is multiplied, so HBM latency overlaps the staging and the
-// arithmetic.  The wave-wide sum of a row is taken in a fixed order.
-// TM = 1 (decode) keeps the register count low.
-template <int RPW, int TM>
+// 512 columns per pass of the wave.  The weights of NP passes are requested
+// together (the first NP before the input is staged), so a row of up to
+// NP * 512 columns costs one HBM round trip.  The wave-wide sum of a row is
+// taken in a fixed order.  TM = 1 (decode) keeps the register count low.
+template <int RPW, int TM, int NP>
 __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ W, int N, int K,
                                                    const float* __restrict__ x, int ldx, int T,
                                                    const float* __restrict__ gain, float eps,
@@ -74,16 +88,22 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
   float* h = smem + 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  u32x4 w[RPW];
-  auto load = [&](u32x4* dst, int k) {
+  const int np = (K + 511) / 512;
+  u32x4 w[NP][RPW];
+  auto load = [&](int pb) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int n = min(n0 + i, N - 1);
-      dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)n * K + k));
+    for (int p = 0; p < NP; ++p) {
+      const int k = (pb + p) * 512 + lane * 8;
+      if (k < K) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          const int n = min(n0 + i, N - 1);
+          w[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (size_t)n * K + k));
+        }
+      }
     }
   };
-  int k = lane * 8;
-  if (n0 < N && k < K) load(w, k);
+  if (n0 < N) load(0);
   stage_input(x, ldx, T, K, gain, eps, h, red);
   if (n0 >= N) return;
   float acc[RPW][TM];
@@ -91,18 +111,21 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const uint16_t* __restrict__ 
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[i][t] = 0.f;
-  for (; k < K; k += 512) {
-    u32x4 wn[RPW];
-    if (k + 512 < K) load(wn, k + 512);
+  for (int pb = 0; pb < np; pb += NP) {
+    if (pb) load(pb);
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (t < T) {
+    for (int p = 0; p < NP; ++p) {
+      const int k = (pb + p) * 512 + lane * 8;
+      if (k < K) {
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) acc[i][t] += dot8(w[i], h + t * K + k);
+        for (int t = 0; t < TM; ++t) {
+          if (t < T) {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) acc[i][t] += dot8(w[p][i], h + t * K + k);
+          }
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) w[i] = wn[i];
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -129,17 +152,34 @@ static int rows_per_wave(int N, int ncu, int max_rpw) {
   return r;
 }
 
-template <int RPW>
-static void gemv_bf16_t(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
-                        const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate) {
+// Passes requested together: the row's pass count rounded up to 1, 2, 4 or 8.
+static int bf16_np(int K) {
+  const int np = (K + 511) / 512;
+  return np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : 8;
+}
+
+template <int RPW, int NP>
+static void gemv_bf16_np(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
+                         const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate) {
   const dim3 grid((N + 4 * RPW - 1) / (4 * RPW));
   const size_t lds = (8 + (size_t)T * K) * sizeof(float);
   if (T == 1)
-    hipLaunchKernelGGL((k_gemv_bf16<RPW, 1>), grid, dim3(256), lds, s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy,
-                       accumulate);
+    hipLaunchKernelGGL((k_gemv_bf16<RPW, 1, NP>), grid, dim3(256), lds, s, W, N, K, x, ldx, T, gain, eps, bias, y,
+                       ldy, accumulate);
   else
-    hipLaunchKernelGGL((k_gemv_bf16<RPW, GEMV_MAX_T>), grid, dim3(256), lds, s, W, N, K, x, ldx, T, gain, eps, bias,
-                       y, ldy, accumulate);
+    hipLaunchKernelGGL((k_gemv_bf16<RPW, GEMV_MAX_T, 1>), grid, dim3(256), lds, s, W, N, K, x, ldx, T, gain, eps,
+                       bias, y, ldy, accumulate);
+}
+
+template <int RPW>
+static void gemv_bf16_t(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
+                        const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate) {
+  switch (bf16_np(K)) {
+    case 1: gemv_bf16_np<RPW, 1>(s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    case 2: gemv_bf16_np<RPW, 2>(s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    case 4: gemv_bf16_np<RPW, 4>(s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    default: gemv_bf16_np<RPW, 8>(s, W, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+  }
 }
 
 void launch_gemv_bf16(hipStream_t s, const uint16_t* W, int N, int K, const float* x, int ldx, int T,
@@ -156,7 +196,7 @@ void launch_gemv_bf16(hipStream_t s, const uint16_t* W, int N, int K, const floa
 //   a[t][i] = SiLU(sum_k Wg[i][k] h[t][k]) * (sum_k Wu[i][k] h[t][k])
 // "Failed Star / fs" block figure (SwiGLU); the gated product is formed in
 // registers and never stored separately.  Loads are issued as in k_gemv_bf16.
-template <int RPW, int TM>
+template <int RPW, int TM, int NP>
 __global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __restrict__ Wg,
                                                           const uint16_t* __restrict__ Wu, int N, int K,
                                                           const float* __restrict__ x, int ldx, int T,
@@ -167,17 +207,23 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __rest
   float* h = smem + 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  u32x4 wg[RPW], wu[RPW];
-  auto load = [&](u32x4* dg, u32x4* du, int k) {
+  const int np = (K + 511) / 512;
+  u32x4 wg[NP][RPW], wu[NP][RPW];
+  auto load = [&](int pb) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int n = min(n0 + i, N - 1);
-      dg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wg + (size_t)n * K + k));
-      du[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wu + (size_t)n * K + k));
+    for (int p = 0; p < NP; ++p) {
+      const int k = (pb + p) * 512 + lane * 8;
+      if (k < K) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          const int n = min(n0 + i, N - 1);
+          wg[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wg + (size_t)n * K + k));
+          wu[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wu + (size_t)n * K + k));
+        }
+      }
     }
   };
-  int k = lane * 8;
-  if (n0 < N && k < K) load(wg, wu, k);
+  if (n0 < N) load(0);
   stage_input(x, ldx, T, K, gain, eps, h, red);
   if (n0 >= N) return;
   float ag[RPW][TM], au[RPW][TM];
@@ -185,21 +231,24 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __rest
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int t = 0; t < TM; ++t) ag[i][t] = au[i][t] = 0.f;
-  for (; k < K; k += 512) {
-    u32x4 gn[RPW], un[RPW];
-    if (k + 512 < K) load(gn, un, k + 512);
+  for (int pb = 0; pb < np; pb += NP) {
+    if (pb) load(pb);
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (t < T) {
+    for (int p = 0; p < NP; ++p) {
+      const int k = (pb + p) * 512 + lane * 8;
+      if (k < K) {
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-          ag[i][t] += dot8(wg[i], h + t * K + k);
-          au[i][t] += dot8(wu[i], h + t * K + k);
+        for (int t = 0; t < TM; ++t) {
+          if (t < T) {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+              ag[i][t] += dot8(wg[p][i], h + t * K + k);
+              au[i][t] += dot8(wu[p][i], h + t * K + k);
+            }
+          }
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) { wg[i] = gn[i]; wu[i] = un[i]; }
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -215,25 +264,35 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_bf16(const uint16_t* __rest
   }
 }
 
-template <int RPW>
-static void gateup_bf16_t(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
-                          int ldx, int T, const float* gain, float eps, float* a, int lda) {
+template <int RPW, int NP>
+static void gateup_bf16_np(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
+                           int ldx, int T, const float* gain, float eps, float* a, int lda) {
   const dim3 grid((N + 4 * RPW - 1) / (4 * RPW));
   const size_t lds = (8 + (size_t)T * K) * sizeof(float);
   if (T == 1)
-    hipLaunchKernelGGL((k_gemv_gateup_bf16<RPW, 1>), grid, dim3(256), lds, s, Wg, Wu, N, K, x, ldx, T, gain, eps, a,
-                       lda);
+    hipLaunchKernelGGL((k_gemv_gateup_bf16<RPW, 1, NP>), grid, dim3(256), lds, s, Wg, Wu, N, K, x, ldx, T, gain, eps,
+                       a, lda);
   else
-    hipLaunchKernelGGL((k_gemv_gateup_bf16<RPW, GEMV_MAX_T>), grid, dim3(256), lds, s, Wg, Wu, N, K, x, ldx, T, gain,
-                       eps, a, lda);
+    hipLaunchKernelGGL((k_gemv_gateup_bf16<RPW, GEMV_MAX_T, 1>), grid, dim3(256), lds, s, Wg, Wu, N, K, x, ldx, T,
+                       gain, eps, a, lda);
+}
+
+template <int RPW>
+static void gateup_bf16_t(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
+                          int ldx, int T, const float* gain, float eps, float* a, int lda) {
+  switch (bf16_np(K)) {
+    case 1: gateup_bf16_np<RPW, 1>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda); break;
+    case 2: gateup_bf16_np<RPW, 2>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda); break;
+    default: gateup_bf16_np<RPW, 4>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda); break;
+  }
 }
 
 void launch_gemv_gateup_bf16(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
                              int ldx, int T, const float* gain, float eps, float* a, int lda, int ncu) {
-  if (rows_per_wave(N, ncu, GATEUP_RPW) == 2)
-    gateup_bf16_t<2>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda);
-  else
-    gateup_bf16_t<1>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda);
+  switch (rows_per_wave(N, ncu, GATEUP_RPW)) {
+    case 2: gateup_bf16_t<2>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda); break;
+    default: gateup_bf16_t<1>(s, Wg, Wu, N, K, x, ldx, T, gain, eps, a, lda); break;
+  }
 }
 
 // ---------------------------------------------------------------------------

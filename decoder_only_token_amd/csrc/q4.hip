@@ -57,22 +57,37 @@ __device__ __forceinline__ int q4_perm(int k) {
   return (p << 11) + ((j * 64 + l) << 2) + (k & 3);
 }
 
-// h[t][perm(k)] = x[t][k] (* g[k] / rms(x[t])); K a multiple of 128.
+// h[t][perm(k)] = x[t][k] (* g[k] / rms(x[t])); K a multiple of 128.  Each
+// thread requests up to 12 pieces of 16 bytes before storing any.
 __device__ __forceinline__ void stage_input_q4(const float* __restrict__ x, int ldx, int T, int K,
                                                const float* __restrict__ gain, float eps, float* h, float* red) {
+  constexpr int B = 12;
   const int ks = q4_stride(K);
   for (int t = 0; t < T; ++t) {
     const float* xr = x + (size_t)t * ldx;
     float ss = 0.f;
-    for (int k = threadIdx.x * 4; k < K; k += 1024) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(xr + k);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    for (int k0 = 0; k0 < K; k0 += B * 1024) {
+      f32x4 v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int k = k0 + (threadIdx.x + i * 256) * 4;
+        if (k < K) v[i] = *reinterpret_cast<const f32x4*>(xr + k);
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int k = k0 + (threadIdx.x + i * 256) * 4;
+        if (k < K) {
+          *reinterpret_cast<f32x4*>(h + t * ks + q4_perm(k)) = v[i];
+          ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+        }
+      }
     }
-    const float r = gain ? 1.0f / sqrtf(block_sum_256(ss, red) / (float)K + eps) : 1.0f;
-    for (int k = threadIdx.x * 4; k < K; k += 1024) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(xr + k);
-      if (gain) v = v * r * *reinterpret_cast<const f32x4*>(gain + k);
-      *reinterpret_cast<f32x4*>(h + t * ks + q4_perm(k)) = v;
+    if (gain) {  // each thread rescales the pieces it stored
+      const float r = 1.0f / sqrtf(block_sum_256(ss, red) / (float)K + eps);
+      for (int k = threadIdx.x * 4; k < K; k += 1024) {
+        f32x4* hp = reinterpret_cast<f32x4*>(h + t * ks + q4_perm(k));
+        *hp = *hp * r * *reinterpret_cast<const f32x4*>(gain + k);
+      }
     }
   }
   __syncthreads();
@@ -112,9 +127,11 @@ __device__ __forceinline__ void load_x32(const float* hp, f32x4* v, float& sx) {
 
 // y[t][n] (=|+=) sum_g s[n][g] sum_{k in g} code[n][k] h[t][k] (+ bias[n]) for
 // T <= TM rows.  Each wave owns RPW output rows; in each 2048-column pass a
-// lane takes 16 bytes (32 codes) of each row.  TM = 1 (decode) keeps the
-// register count low enough for several waves per SIMD.
-template <int RPW, int TM>
+// lane takes 16 bytes (32 codes) of each row.  The codes of NP passes are
+// requested together (the first NP before the input is staged), so a row of
+// up to NP * 2048 columns costs one HBM round trip.  TM = 1 (decode) keeps
+// the register count low enough for several waves per SIMD.
+template <int RPW, int TM, int NP>
 __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4, const uint16_t* __restrict__ S4,
                                                  int N, int K, const float* __restrict__ x, int ldx, int T,
                                                  const float* __restrict__ gain, float eps,
@@ -125,21 +142,24 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
   float* h = smem + 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  const int groups = K / 128, ks = q4_stride(K);
-  // the first pass's codes are requested before the input is staged, each
-  // later pass while the previous one is multiplied
-  u32x4 c[RPW];
-  float sc[RPW];
-  auto load = [&](u32x4* dc, float* ds, int k) {
+  const int groups = K / 128, ks = q4_stride(K), np = (K + 2047) / 2048;
+  u32x4 c[NP][RPW];
+  float sc[NP][RPW];
+  auto load = [&](int pb) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int n = min(n0 + i, N - 1);
-      dc[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(C4 + (size_t)n * (K / 2) + k / 2));
-      ds[i] = f16_bits_to_f(S4[(size_t)n * groups + k / 128]);
+    for (int p = 0; p < NP; ++p) {
+      const int k = (pb + p) * 2048 + lane * 32;
+      if (k < K) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          const int n = min(n0 + i, N - 1);
+          c[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(C4 + (size_t)n * (K / 2) + k / 2));
+          sc[p][i] = f16_bits_to_f(S4[(size_t)n * groups + k / 128]);
+        }
+      }
     }
   };
-  int k = lane * 32;
-  if (n0 < N && k < K) load(c, sc, k);
+  if (n0 < N) load(0);
   stage_input_q4(x, ldx, T, K, gain, eps, h, red);
   if (n0 >= N) return;
   float acc[RPW][TM];
@@ -147,22 +167,23 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[i][t] = 0.f;
-  for (int p = 0; k < K; ++p, k += 2048) {
-    u32x4 cn[RPW];
-    float sn[RPW];
-    if (k + 2048 < K) load(cn, sn, k + 2048);
+  for (int pb = 0; pb < np; pb += NP) {
+    if (pb) load(pb);
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (t < T) {
-        f32x4 v[8];
-        float sx;
-        load_x32(h + t * ks + p * 2048 + lane * 4, v, sx);
+    for (int p = 0; p < NP; ++p) {
+      if ((pb + p) * 2048 + lane * 32 < K) {
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) acc[i][t] = fmaf(sc[i], dot32_q4(c[i], v, sx), acc[i][t]);
+        for (int t = 0; t < TM; ++t) {
+          if (t < T) {
+            f32x4 v[8];
+            float sx;
+            load_x32(h + t * ks + (pb + p) * 2048 + lane * 4, v, sx);
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) acc[i][t] = fmaf(sc[p][i], dot32_q4(c[p][i], v, sx), acc[i][t]);
+          }
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) { c[i] = cn[i]; sc[i] = sn[i]; }
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -181,8 +202,9 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
   }
 }
 
-// a[t][n] = SiLU(gate row n . h[t]) * (up row n . h[t]), both rows int4.
-template <int RPW, int TM>
+// a[t][n] = SiLU(gate row n . h[t]) * (up row n . h[t]), both rows int4;
+// loads as in k_gemv_q4.
+template <int RPW, int TM, int NP>
 __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restrict__ Cg, const uint16_t* __restrict__ Sg,
                                                         const uint8_t* __restrict__ Cu, const uint16_t* __restrict__ Su,
                                                         int N, int K, const float* __restrict__ x, int ldx, int T,
@@ -193,21 +215,26 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restric
   float* h = smem + 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
-  const int groups = K / 128, ks = q4_stride(K);
-  u32x4 cg[RPW], cu[RPW];
-  float sg[RPW], su[RPW];
-  auto load = [&](u32x4* dg, float* dsg, u32x4* du, float* dsu, int k) {
+  const int groups = K / 128, ks = q4_stride(K), np = (K + 2047) / 2048;
+  u32x4 cg[NP][RPW], cu[NP][RPW];
+  float sg[NP][RPW], su[NP][RPW];
+  auto load = [&](int pb) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int n = min(n0 + i, N - 1);
-      dg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cg + (size_t)n * (K / 2) + k / 2));
-      du[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cu + (size_t)n * (K / 2) + k / 2));
-      dsg[i] = f16_bits_to_f(Sg[(size_t)n * groups + k / 128]);
-      dsu[i] = f16_bits_to_f(Su[(size_t)n * groups + k / 128]);
+    for (int p = 0; p < NP; ++p) {
+      const int k = (pb + p) * 2048 + lane * 32;
+      if (k < K) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          const int n = min(n0 + i, N - 1);
+          cg[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cg + (size_t)n * (K / 2) + k / 2));
+          cu[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cu + (size_t)n * (K / 2) + k / 2));
+          sg[p][i] = f16_bits_to_f(Sg[(size_t)n * groups + k / 128]);
+          su[p][i] = f16_bits_to_f(Su[(size_t)n * groups + k / 128]);
+        }
+      }
     }
   };
-  int k = lane * 32;
-  if (n0 < N && k < K) load(cg, sg, cu, su, k);
+  if (n0 < N) load(0);
   stage_input_q4(x, ldx, T, K, gain, eps, h, red);
   if (n0 >= N) return;
   float ag[RPW][TM], au[RPW][TM];
@@ -215,25 +242,26 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restric
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
     for (int t = 0; t < TM; ++t) ag[i][t] = au[i][t] = 0.f;
-  for (int p = 0; k < K; ++p, k += 2048) {
-    u32x4 gn[RPW], un[RPW];
-    float sgn[RPW], sun[RPW];
-    if (k + 2048 < K) load(gn, sgn, un, sun, k + 2048);
+  for (int pb = 0; pb < np; pb += NP) {
+    if (pb) load(pb);
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (t < T) {
-        f32x4 v[8];
-        float sx;
-        load_x32(h + t * ks + p * 2048 + lane * 4, v, sx);
+    for (int p = 0; p < NP; ++p) {
+      if ((pb + p) * 2048 + lane * 32 < K) {
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-          ag[i][t] = fmaf(sg[i], dot32_q4(cg[i], v, sx), ag[i][t]);
-          au[i][t] = fmaf(su[i], dot32_q4(cu[i], v, sx), au[i][t]);
+        for (int t = 0; t < TM; ++t) {
+          if (t < T) {
+            f32x4 v[8];
+            float sx;
+            load_x32(h + t * ks + (pb + p) * 2048 + lane * 4, v, sx);
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+              ag[i][t] = fmaf(sg[p][i], dot32_q4(cg[p][i], v, sx), ag[i][t]);
+              au[i][t] = fmaf(su[p][i], dot32_q4(cu[p][i], v, sx), au[i][t]);
+            }
+          }
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) { cg[i] = gn[i]; cu[i] = un[i]; sg[i] = sgn[i]; su[i] = sun[i]; }
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -257,6 +285,59 @@ int q4_rpw(int N, int ncu, int max_rpw) {
   return r;
 }
 
+// Passes requested together: the row's pass count rounded up to 1, 2, 4 or 8.
+int q4_np(int K) {
+  const int np = (K + 2047) / 2048;
+  return np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : 8;
+}
+
+template <int RPW, int NP>
+void gemv_q4_np(hipStream_t s, dim3 grid, size_t lds, const uint8_t* codes, const uint16_t* scales, int N, int K,
+                const float* x, int ldx, int T, const float* gain, float eps, const float* bias, float* y, int ldy,
+                int accumulate) {
+  if (T == 1)
+    hipLaunchKernelGGL((k_gemv_q4<RPW, 1, NP>), grid, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain, eps,
+                       bias, y, ldy, accumulate);
+  else
+    hipLaunchKernelGGL((k_gemv_q4<RPW, GEMV_MAX_T, 1>), grid, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain,
+                       eps, bias, y, ldy, accumulate);
+}
+
+template <int RPW>
+void gemv_q4_t(hipStream_t s, dim3 grid, size_t lds, const uint8_t* codes, const uint16_t* scales, int N, int K,
+               const float* x, int ldx, int T, const float* gain, float eps, const float* bias, float* y, int ldy,
+               int accumulate) {
+  switch (q4_np(K)) {
+    case 1: gemv_q4_np<RPW, 1>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    case 2: gemv_q4_np<RPW, 2>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    case 4: gemv_q4_np<RPW, 4>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    default: gemv_q4_np<RPW, 8>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+  }
+}
+
+template <int RPW, int NP>
+void gateup_q4_np(hipStream_t s, dim3 grid, size_t lds, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu,
+                  const uint16_t* su, int N, int K, const float* x, int ldx, int T, const float* gain, float eps,
+                  float* a, int lda) {
+  if (T == 1)
+    hipLaunchKernelGGL((k_gemv_gateup_q4<RPW, 1, NP>), grid, dim3(256), lds, s, cg, sg, cu, su, N, K, x, ldx, T, gain,
+                       eps, a, lda);
+  else
+    hipLaunchKernelGGL((k_gemv_gateup_q4<RPW, GEMV_MAX_T, 1>), grid, dim3(256), lds, s, cg, sg, cu, su, N, K, x, ldx,
+                       T, gain, eps, a, lda);
+}
+
+template <int RPW>
+void gateup_q4_t(hipStream_t s, dim3 grid, size_t lds, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu,
+                 const uint16_t* su, int N, int K, const float* x, int ldx, int T, const float* gain, float eps,
+                 float* a, int lda) {
+  switch (q4_np(K)) {
+    case 1: gateup_q4_np<RPW, 1>(s, grid, lds, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, a, lda); break;
+    case 2: gateup_q4_np<RPW, 2>(s, grid, lds, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, a, lda); break;
+    default: gateup_q4_np<RPW, 4>(s, grid, lds, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, a, lda); break;
+  }
+}
+
 }  // namespace
 
 int q4_gemv_t_tile(int K) {
@@ -270,34 +351,6 @@ void launch_quantize_q4(hipStream_t s, const uint16_t* src, int nrows, int K, ui
   const int items = nrows * (K / 128);
   hipLaunchKernelGGL(k_quantize_q4, dim3((items + 3) / 4), dim3(256), 0, s, src, nrows, K, codes, scales);
 }
-
-namespace {
-
-template <int RPW>
-void gemv_q4_t(hipStream_t s, dim3 grid, size_t lds, const uint8_t* codes, const uint16_t* scales, int N, int K,
-               const float* x, int ldx, int T, const float* gain, float eps, const float* bias, float* y, int ldy,
-               int accumulate) {
-  if (T == 1)
-    hipLaunchKernelGGL((k_gemv_q4<RPW, 1>), grid, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain, eps, bias,
-                       y, ldy, accumulate);
-  else
-    hipLaunchKernelGGL((k_gemv_q4<RPW, GEMV_MAX_T>), grid, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain,
-                       eps, bias, y, ldy, accumulate);
-}
-
-template <int RPW>
-void gateup_q4_t(hipStream_t s, dim3 grid, size_t lds, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu,
-                 const uint16_t* su, int N, int K, const float* x, int ldx, int T, const float* gain, float eps,
-                 float* a, int lda) {
-  if (T == 1)
-    hipLaunchKernelGGL((k_gemv_gateup_q4<RPW, 1>), grid, dim3(256), lds, s, cg, sg, cu, su, N, K, x, ldx, T, gain, eps,
-                       a, lda);
-  else
-    hipLaunchKernelGGL((k_gemv_gateup_q4<RPW, GEMV_MAX_T>), grid, dim3(256), lds, s, cg, sg, cu, su, N, K, x, ldx, T,
-                       gain, eps, a, lda);
-}
-
-}  // namespace
 
 void launch_gemv_q4(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
                     int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate,
@@ -317,9 +370,11 @@ void launch_gemv_gateup_q4(hipStream_t s, const uint8_t* cg, const uint16_t* sg,
                            int N, int K, const float* x, int ldx, int T, const float* gain, float eps, float* a,
                            int lda, int ncu) {
   const size_t lds = (8 + (size_t)T * q4_stride(K)) * sizeof(float);
-  const int r = q4_rpw(N, ncu, 2);
+  const int r = q4_rpw(N, ncu, 4);
   const dim3 grid((N + 4 * r - 1) / (4 * r));
-  if (r == 2)
+  if (r == 4)
+    gateup_q4_t<4>(s, grid, lds, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, a, lda);
+  else if (r == 2)
     gateup_q4_t<2>(s, grid, lds, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, a, lda);
   else
     gateup_q4_t<1>(s, grid, lds, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, a, lda);
