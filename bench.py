@@ -35,8 +35,11 @@ def parse():
     ap.add_argument("--prefill-rows", type=int, default=512,
                     help="also time one batched prefill of this many random tokens (0: skip)")
     ap.add_argument("--cpu-sample-steps", type=int, default=128)
-    ap.add_argument("--path", choices=["persistent", "graph"], default="persistent",
-                    help="decode step as one persistent kernel, or as per-operation kernels in a hipGraph")
+    ap.add_argument("--path", choices=["auto", "persistent", "graph"], default="auto",
+                    help="decode step as one persistent kernel, or as per-operation kernels in a hipGraph "
+                         "(auto: persistent where the model allows it: bf16 weights, no adapter)")
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="decode steps per job (0: the workload's own count)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 launches): the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -185,24 +188,35 @@ def main():
     dw = {"embed": to_dev(weights["embed"]), "final_norm": to_dev(weights["final_norm"]),
           "layers": [{k: to_dev(v) for k, v in lw.items()} for lw in weights["layers"]]}
     torch.cuda.synchronize()
+    if args.path == "auto":
+        args.path = "persistent" if shape.weight_format == synth.W_BF16 and not wl.lora_rank else "graph"
     path = qd.QD_DECODE_PERSISTENT if args.path == "persistent" else qd.QD_DECODE_GRAPH
-    dec = qd.Decoder(qd.make_config(shape, max_prefill=wl.max_prefill, decode_path=path), stream.cuda_stream)
+    dec = qd.Decoder(qd.make_config(shape, max_prefill=wl.max_prefill, lora_rank_max=wl.lora_rank,
+                                    decode_path=path), stream.cuda_stream)
     dec.load_weights(dw)
     del dw
+    if wl.lora_rank:
+        lora = synth.make_lora(shape, wl.lora_rank)
+        dl = [{k: to_dev(v) for k, v in lw.items()} for lw in lora]
+        torch.cuda.synchronize()
+        dec.set_lora(dl, wl.lora_rank, wl.lora_alpha)
+        del dl
     torch.cuda.synchronize()
-    n_dec = wl.decode_steps
+    n_dec = args.decode_steps or wl.decode_steps
+    sampling = (qd.make_sampling(wl.temperature, wl.top_k, wl.top_p, synth.SEED_SAMPLING)
+                if wl.temperature > 0 else None)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def job(marks=None):
+    def job(marks=None, samp=None):
         dec.reset_kv()
         if marks:
             marks[0].record(stream)
-        dec.prefill(prompt)
+        dec.prefill(prompt, sampling=samp)
         if marks:
             marks[1].record(stream)
         for _ in range(n_dec):
-            dec.decode_step()
+            dec.decode_step(sampling=samp)
         if marks:
             marks[2].record(stream)
 
@@ -217,6 +231,17 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     dec.sync_token()  # raises if any decode step was abandoned
+    sampled = None
+    if sampling is not None:
+        with torch.cuda.stream(stream):
+            m = [ev(), ev(), ev()]
+            job(m, sampling)
+            torch.cuda.synchronize()
+        dec.sync_token()
+        s_ms = m[1].elapsed_time(m[2])
+        sampled = {"temperature": wl.temperature, "top_k": wl.top_k, "top_p": wl.top_p, "seed": synth.SEED_SAMPLING,
+                   "decode_tok_s": round(n_dec / (s_ms * 1e-3), 2), "decode_step_us": round(s_ms * 1e3 / n_dec, 2),
+                   "note": "one job with on-GPU top-k / temperature / top-p draws (greedy is the headline)"}
     long_prefill = measure_long_prefill(dec, stream, shape, wl, args) if args.prefill_rows else None
     prefill_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
     decode_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
@@ -224,12 +249,12 @@ def main():
     tokens_per_job = 1 + n_dec
     value = tokens_per_job * args.steps / wall
 
-    wb = synth.weight_bytes(shape)
     kvp = synth.kv_bytes_per_position(shape)
     # algorithmic HBM bytes of one decode step at context c: all weights once
     # (layers + tied head + one gathered row), KV read for c positions, KV write of one position
     ctx0 = wl.prompt_len
-    dec_bytes = sum((wb["layers"] + wb["lm_head"] + wb["embed_row"]) + kvp * (ctx0 + i + 1)
+    wb = synth.weight_bytes(shape, wl.lora_rank)
+    dec_bytes = sum((wb["layers"] + wb["lora"] + wb["lm_head"] + wb["embed_row"]) + kvp * (ctx0 + i + 1)
                     for i in range(n_dec))
     decode_step_us = decode_ms * 1e3 / n_dec
     achieved = dec_bytes / n_dec / (decode_step_us * 1e-6) / 1e9
@@ -252,7 +277,8 @@ def main():
         "config": {"workload": wl.name, "model": shape.name, "layers": shape.n_layers, "hidden": shape.hidden,
                    "heads": [shape.n_q_heads, shape.n_kv_heads], "vocab": shape.vocab,
                    "prompt_len": wl.prompt_len, "decode_steps": n_dec, "global_batch": 1,
-                   "parallelism": "single GPU", "decode_path": args.path},
+                   "parallelism": "single GPU", "decode_path": args.path,
+                   "lora": {"rank": wl.lora_rank, "alpha": wl.lora_alpha} if wl.lora_rank else None},
         "decode_tok_s": round(n_dec / (decode_ms * 1e-3), 2),
         "decode_step_us": round(decode_step_us, 2),
         "prefill_tok_s": round(wl.prompt_len / (prefill_ms * 1e-3), 2),
@@ -266,6 +292,8 @@ def main():
     }
     if long_prefill:
         out["prefill_batched"] = long_prefill
+    if sampled:
+        out["sampled"] = sampled
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, weights, prompt, args.cpu_sample_steps)
     dec.close()

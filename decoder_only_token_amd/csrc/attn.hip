@@ -395,7 +395,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
 }  // namespace
 
 int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin) {
-  int s = 2 * ncu / nkv;
+  int s = ncu / nkv;
   s = std::min(s, (max_pos + cmin - 1) / cmin);
   s = std::min(s, kMaxSplits);
   return std::max(s, 1);
