@@ -153,6 +153,49 @@ class OracleModel:
             self.lora_scale = lora_alpha / rank
             self.lora = [{k: widen_bf16(v) for k, v in lw.items()} for lw in lora]
 
+    def layer_rows(self, li: int, x: np.ndarray, rows) -> np.ndarray:
+        """Layer ``li`` applied to a prefix of rows, output only for ``rows``.
+
+        x [n, H] holds the layer's input for positions 0..n-1 (a prompt from an
+        empty cache).  Keys and values are formed for every position (each row
+        attends to all earlier ones); queries, attention, o_proj and the MLP
+        only for the selected rows.  The arithmetic is that of ``forward``
+        restricted to those rows ("Failed Star / fs" block figure), so a
+        layer's output can be checked on sampled rows at full model size.
+        """
+        s = self.shape
+        w = self.layers[li]
+        x = np.asarray(x, dtype=np.float64)
+        rows = np.asarray(rows, dtype=np.int64)
+        n = x.shape[0]
+        nq, nkv, d = s.n_q_heads, s.n_kv_heads, s.head_dim
+        pos = np.arange(n)
+        h = rmsnorm(x, w["attn_norm"], s.rms_eps)
+        k = h @ w["wk"].T
+        v = h @ w["wv"].T
+        hr = h[rows]
+        q = hr @ w["wq"].T
+        if s.qkv_bias:
+            q = q + w["bq"]
+            k = k + w["bk"]
+            v = v + w["bv"]
+        if self.lora is not None:
+            lw = self.lora[li]
+            q = q + self.lora_scale * ((hr @ lw["a_q"].T) @ lw["b_q"].T)
+            v = v + self.lora_scale * ((h @ lw["a_v"].T) @ lw["b_v"].T)
+        q = q.reshape(len(rows), nq, d)
+        k = k.reshape(n, nkv, d)
+        v = v.reshape(n, nkv, d)
+        if s.qk_norm:
+            q = rmsnorm(q, w["q_norm"], s.rms_eps)
+            k = rmsnorm(k, w["k_norm"], s.rms_eps)
+        q = rope_rotate(q, rows, s.rope_theta)
+        k = rope_rotate(k, pos, s.rope_theta)
+        o = causal_gqa_attention(q, k, v, rows)
+        xr = x[rows] + o.reshape(len(rows), nq * d) @ w["wo"].T
+        h2 = rmsnorm(xr, w["mlp_norm"], s.rms_eps)
+        return xr + swiglu_mlp(h2, w["w_gate"], w["w_up"], w["w_down"])
+
     def new_cache(self, capacity: Optional[int] = None) -> KVCache:
         s = self.shape
         return KVCache(s.n_layers, s.n_kv_heads, s.head_dim, capacity or s.max_pos)

@@ -450,3 +450,23 @@ def test_int4_properties():
     # idempotent: quantising the dequantised weights returns the same codes and scales
     c2, s2 = quantize_int4_g128(what.astype(np.float32))
     assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+@pytest.mark.parametrize("shape_name,lora", [("TINY", False), ("TINY_INT4", True)])
+def test_layer_rows_matches_the_full_forward(shape_name, lora):
+    """The row-sampled single-layer oracle used for full-size GPU checks gives,
+    for the selected rows, exactly the layer outputs of the whole forward
+    (same inputs, same definition restricted to those rows)."""
+    import dataclasses
+    shape = dataclasses.replace(getattr(synth, shape_name), n_layers=2)
+    w = synth.make_weights(shape, seed=81, random_gains=True)
+    lo = synth.make_lora(shape, 4, seed=82) if lora else None
+    m = OracleModel(shape, w, lora=lo, lora_alpha=8.0 if lora else 0.0)
+    prompt = synth.make_prompt(shape.vocab, 23, seed=83)
+    cap = {}
+    m.forward(prompt, capture=cap)
+    rows = [0, 5, 22, 11]
+    for li in range(shape.n_layers):
+        x_in = cap["embed"] if li == 0 else cap["layer_out"][li - 1]
+        got = m.layer_rows(li, x_in, rows)
+        np.testing.assert_allclose(got, cap["layer_out"][li][rows], rtol=1e-12, atol=1e-12)
