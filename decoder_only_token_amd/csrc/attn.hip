@@ -252,24 +252,26 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
 // Query row t sits at position pos + t (pos = the step state's position) and
 // sees cache positions 0 .. pos + t, its own included.
 //
-// grid (nkv, ceil(T / (64 / G))), block 256.  A block owns kv head g and 64
-// query vectors: 64 / G consecutive rows times the G query heads of g, so a
-// K/V tile in LDS serves all of them.  Per tile of 32 cache positions:
+// grid (nkv, ceil(T / (QV / G))), block 256.  A block owns kv head g and QV
+// query vectors (QV / G consecutive rows times the G query heads of g), so a
+// K/V tile in LDS serves all of them.  Per tile of BK = 2048 / QV positions:
 //   scores: each thread forms a 2 (query) x 4 (position) tile of dot products
 //           from LDS (queries pre-scaled by 1 / sqrt(d));
-//   online softmax: the 8 threads that share a query pair reduce the tile's
-//           max and sum with shuffles, rescale the running state and write the
-//           probabilities (transposed) to LDS;
-//   values: each thread accumulates an 8 (query) x 4 (dim) tile of outputs.
+//   online softmax: the BK / 4 threads that share a query pair reduce the
+//           tile's max and sum with DPP, rescale the running state and write
+//           the probabilities (transposed) to LDS;
+//   values: each thread accumulates a (QV / 8) (query) x 4 (dim) output tile.
 // K and V of a tile share one LDS buffer (V is held in registers while the
-// scores are formed), which keeps the block under 64 KiB of LDS.
-// Blocks with the longest causal ranges start first.
-template <int G>
+// scores are formed), which keeps the block under 64 KiB of LDS.  QV = 32
+// doubles the block count of short prompts.  Blocks with the longest causal
+// ranges start first.
+template <int G, int QV>
 __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q, int T, int nq,
                                                       const float* __restrict__ Kc, const float* __restrict__ Vc,
                                                       int max_pos, const DevState* __restrict__ st, float scale,
                                                       float* __restrict__ o_out, int ldo) {
-  constexpr int QV = 64, R = QV / G, BK = 32, RS = D + 4;
+  constexpr int R = QV / G, BK = 2048 / QV, KG = BK / 4, QPT = QV / 8, RS = D + 4;
+  constexpr int VPT = BK * D / 4 / 256;  // V pieces per thread
   __shared__ __align__(16) float Qs[QV * RS];
   __shared__ __align__(16) float KVs[BK * RS];  // K of the tile, then its V
   __shared__ __align__(16) float Pt[BK * QV];
@@ -288,8 +290,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
     if (r < nrows) val = *reinterpret_cast<const f32x4*>(q + ((size_t)(t0 + r) * nq + g * G + j) * D + c4 * 4) * scale;
     *reinterpret_cast<f32x4*>(Qs + v * RS + c4 * 4) = val;
   }
-  const int qi = tid >> 3, kj = tid & 7;  // score mapping: queries 2 qi, 2 qi + 1; positions 4 kj .. + 3
-  const int qg = tid >> 5, dg = tid & 31; // value mapping: queries 8 qg .. + 7; dims 4 dg .. + 3
+  const int qi = tid / KG, kj = tid % KG;  // score mapping: queries 2 qi, 2 qi + 1; positions 4 kj .. + 3
+  const int qg = tid >> 5, dg = tid & 31;  // value mapping: queries QPT qg .. + QPT - 1; dims 4 dg .. + 3
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   int qpos[2];
   bool live[2];
@@ -299,18 +301,18 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
     live[a] = r < nrows;
     qpos[a] = pos0 + t0 + r;
   }
-  f32x4 o[8];
+  f32x4 o[QPT];
 #pragma unroll
-  for (int a = 0; a < 8; ++a) o[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < QPT; ++a) o[a] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float* Kg = Kc + (size_t)g * max_pos * D;
   const float* Vg = Vc + (size_t)g * max_pos * D;
 
   for (int k0 = 0; k0 < kv_end; k0 += BK) {
     const int nk = min(BK, kv_end - k0);
-    f32x4 vr[BK * D / 4 / 256];
+    f32x4 vr[VPT];
     __syncthreads();  // queries staged; the previous tile consumed
 #pragma unroll
-    for (int u = 0; u < BK * D / 4 / 256; ++u) {
+    for (int u = 0; u < VPT; ++u) {
       const int i = tid + u * 256, p = i / (D / 4), c4 = i % (D / 4);
       f32x4 kv = f32x4{0.f, 0.f, 0.f, 0.f};
       vr[u] = kv;
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
         if (!live[a] || pl >= nk || k0 + pl > qpos[a]) sc[a][b] = -INFINITY;
         tmax = fmaxf(tmax, sc[a][b]);
       }
-      tmax = group_max<8>(tmax);
+      tmax = group_max<KG>(tmax);
       const float mn = fmaxf(m[a], tmax);
       const float mref = mn == -INFINITY ? 0.f : mn;  // a query with nothing visible yet
       float ps = 0.f;
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
         Pt[(4 * kj + b) * QV + 2 * qi + a] = p;
         ps += p;
       }
-      ps = group_sum<8>(ps);
+      ps = group_sum<KG>(ps);
       const float c = __expf(m[a] - mref);
       l[a] = l[a] * c + ps;
       m[a] = mn;
@@ -364,19 +366,23 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
     }
     __syncthreads();  // every score formed: the buffer takes V
 #pragma unroll
-    for (int u = 0; u < BK * D / 4 / 256; ++u) {
+    for (int u = 0; u < VPT; ++u) {
       const int i = tid + u * 256, p = i / (D / 4), c4 = i % (D / 4);
       *reinterpret_cast<f32x4*>(KVs + p * RS + c4 * 4) = vr[u];
     }
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 8; ++a) o[a] = o[a] * cs[8 * qg + a];
+    for (int a = 0; a < QPT; ++a) o[a] = o[a] * cs[QPT * qg + a];
     for (int p = 0; p < nk; ++p) {
       const f32x4 vv = *reinterpret_cast<const f32x4*>(KVs + p * RS + 4 * dg);
-      const f32x4 pa = *reinterpret_cast<const f32x4*>(Pt + p * QV + 8 * qg);
-      const f32x4 pb = *reinterpret_cast<const f32x4*>(Pt + p * QV + 8 * qg + 4);
-      o[0] += pa.x * vv; o[1] += pa.y * vv; o[2] += pa.z * vv; o[3] += pa.w * vv;
-      o[4] += pb.x * vv; o[5] += pb.y * vv; o[6] += pb.z * vv; o[7] += pb.w * vv;
+#pragma unroll
+      for (int a4 = 0; a4 < QPT; a4 += 4) {
+        const f32x4 pa = *reinterpret_cast<const f32x4*>(Pt + p * QV + QPT * qg + a4);
+        o[a4] += pa.x * vv;
+        o[a4 + 1] += pa.y * vv;
+        o[a4 + 2] += pa.z * vv;
+        o[a4 + 3] += pa.w * vv;
+      }
     }
   }
   if (kj == 0) {
@@ -385,8 +391,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
   }
   __syncthreads();
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int v = 8 * qg + a, r = v / G, j = v % G;
+  for (int a = 0; a < QPT; ++a) {
+    const int v = QPT * qg + a, r = v / G, j = v % G;
     if (r < nrows)
       *reinterpret_cast<f32x4*>(o_out + (size_t)(t0 + r) * ldo + (g * G + j) * D + 4 * dg) = o[a] * (1.0f / ls[v]);
   }
@@ -421,15 +427,24 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
 }
 
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const float* Kc, const float* Vc,
-                              int max_pos, const DevState* st, float* o_out, int ldo) {
+                              int max_pos, const DevState* st, float* o_out, int ldo, int ncu) {
   const float scale = 1.0f / sqrtf((float)D);
   const int G = nq / nkv;
-  const dim3 grid(nkv, (T + 64 / G - 1) / (64 / G));
-  switch (G) {
-    case 1: hipLaunchKernelGGL(k_attn_prefill<1>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, ldo); break;
-    case 2: hipLaunchKernelGGL(k_attn_prefill<2>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, ldo); break;
-    case 4: hipLaunchKernelGGL(k_attn_prefill<4>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, ldo); break;
-    case 8: hipLaunchKernelGGL(k_attn_prefill<8>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, ldo); break;
+  // 64 query vectors per block, or 32 when that leaves the GPU under two blocks per CU
+  const bool small = (size_t)nkv * ((T + 64 / G - 1) / (64 / G)) < (size_t)2 * ncu;
+#define QD_ATTN_PREFILL(G_, QV_)                                                                                    \
+  hipLaunchKernelGGL((k_attn_prefill<G_, QV_>), dim3(nkv, (T + QV_ / G_ - 1) / (QV_ / G_)), dim3(256), 0, s, q, T, nq, \
+                     Kc, Vc, max_pos, st, scale, o_out, ldo)
+  switch (G * (small ? -1 : 1)) {
+    case 1: QD_ATTN_PREFILL(1, 64); break;
+    case 2: QD_ATTN_PREFILL(2, 64); break;
+    case 4: QD_ATTN_PREFILL(4, 64); break;
+    case 8: QD_ATTN_PREFILL(8, 64); break;
+    case -1: QD_ATTN_PREFILL(1, 32); break;
+    case -2: QD_ATTN_PREFILL(2, 32); break;
+    case -4: QD_ATTN_PREFILL(4, 32); break;
+    case -8: QD_ATTN_PREFILL(8, 32); break;
     default: break;  // rejected by the host before any launch
   }
+#undef QD_ATTN_PREFILL
 }

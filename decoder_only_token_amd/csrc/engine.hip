@@ -286,7 +286,7 @@ void enqueue_attention(qd_handle* h, int l, int T) {
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
                       h->st, h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
     launch_attention_prefill(s, h->q, T, nq, nkv, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, h->o,
-                             nq * d);
+                             nq * d, h->ncu);
   }
 }
 

@@ -42,7 +42,7 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
 
 // Causal attention of T >= 2 new rows (attn.hip), rows at positions pos .. pos + T - 1.
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const float* Kc, const float* Vc,
-                              int max_pos, const DevState* st, float* o_out, int ldo);
+                              int max_pos, const DevState* st, float* o_out, int ldo, int ncu);
 
 // Top-k / temperature / top-p sampling over the logits (sample.hip); the token
 // goes to the device step state, which the greedy pass has already advanced.
