@@ -105,26 +105,29 @@ def blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(wl, weights, prompt, n_steps):
-    """Time the oracle (as it stands) on the host: prompt + n_steps incremental greedy steps."""
-    import numpy as np
+def cpu_baseline(wl, weights, prompt, n_steps, min_seconds=10.0, max_jobs=8):
+    """Time the oracle (as it stands) on the host: jobs of prompt + n_steps
+    incremental greedy steps, repeated until about min_seconds of CPU work."""
     from oracle import OracleModel, argmax_lowest
     t_build = time.perf_counter()
     m = OracleModel(wl.shape, weights)
     t_build = time.perf_counter() - t_build
-    cache = m.new_cache(len(prompt) + n_steps + 1)
+    toks, jobs = 0, 0
     t0 = time.perf_counter()
-    logits = m.forward(prompt, cache, logits_rows="last")[-1]
-    toks = 1
-    for _ in range(n_steps):
-        logits = m.forward([argmax_lowest(logits)], cache, logits_rows="last")[-1]
+    while jobs < max_jobs and (jobs == 0 or time.perf_counter() - t0 < min_seconds):
+        cache = m.new_cache(len(prompt) + n_steps + 1)
+        logits = m.forward(prompt, cache, logits_rows="last")[-1]
         toks += 1
+        for _ in range(n_steps):
+            logits = m.forward([argmax_lowest(logits)], cache, logits_rows="last")[-1]
+            toks += 1
+        jobs += 1
     dt = time.perf_counter() - t0
     cores = blas_threads()
     return {"value": toks / dt, "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{wl.name}: float64 numpy oracle, prefill {len(prompt)} tokens + {n_steps} greedy decode "
-                      f"steps with its own KV cache ({toks} tokens in {dt:.1f} s; weight widening {t_build:.1f} s "
-                      f"not counted); {cores} BLAS threads"}
+            "sample": f"{wl.name}: float64 numpy oracle, {jobs} job(s) of prefill {len(prompt)} tokens + {n_steps} "
+                      f"greedy decode steps with its own KV cache ({toks} tokens in {dt:.1f} s; weight widening "
+                      f"{t_build:.1f} s not counted); {cores} BLAS threads"}
 
 
 def measure_long_prefill(dec, stream, shape, wl, args):
