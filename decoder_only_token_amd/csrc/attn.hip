@@ -256,7 +256,9 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
 // query vectors (QV / G consecutive rows times the G query heads of g), so a
 // K/V tile in LDS serves all of them.  Per tile of BK = 2048 / QV positions:
 //   scores: each thread forms a 2 (query) x 4 (position) tile of dot products
-//           from LDS (queries pre-scaled by 1 / sqrt(d));
+//           from LDS (queries pre-scaled by 1 / sqrt(d)); its positions are
+//           kj + b BK / 4, so the lanes of a wave read consecutive K rows
+//           (distinct LDS banks);
 //   online softmax: the BK / 4 threads that share a query pair reduce the
 //           tile's max and sum with DPP, rescale the running state and write
 //           the probabilities (transposed) to LDS;
@@ -270,11 +272,11 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
                                                       const float* __restrict__ Kc, const float* __restrict__ Vc,
                                                       int max_pos, const DevState* __restrict__ st, float scale,
                                                       float* __restrict__ o_out, int ldo) {
-  constexpr int R = QV / G, BK = 2048 / QV, KG = BK / 4, QPT = QV / 8, RS = D + 4;
+  constexpr int R = QV / G, BK = 2048 / QV, KG = BK / 4, QPT = QV / 8, RS = D + 4, PS = QV + 4;
   constexpr int VPT = BK * D / 4 / 256;  // V pieces per thread
   __shared__ __align__(16) float Qs[QV * RS];
   __shared__ __align__(16) float KVs[BK * RS];  // K of the tile, then its V
-  __shared__ __align__(16) float Pt[BK * QV];
+  __shared__ __align__(16) float Pt[BK * PS];  // probabilities [position][query]
   __shared__ float cs[QV];
   __shared__ float ls[QV];
   const int tid = threadIdx.x;
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
     if (r < nrows) val = *reinterpret_cast<const f32x4*>(q + ((size_t)(t0 + r) * nq + g * G + j) * D + c4 * 4) * scale;
     *reinterpret_cast<f32x4*>(Qs + v * RS + c4 * 4) = val;
   }
-  const int qi = tid / KG, kj = tid % KG;  // score mapping: queries 2 qi, 2 qi + 1; positions 4 kj .. + 3
+  const int qi = tid / KG, kj = tid % KG;  // score mapping: queries 2 qi, 2 qi + 1; positions kj + KG b
   const int qg = tid >> 5, dg = tid & 31;  // value mapping: queries QPT qg .. + QPT - 1; dims 4 dg .. + 3
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   int qpos[2];
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
       const f32x4 qb = *reinterpret_cast<const f32x4*>(Qs + (2 * qi + 1) * RS + c);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(KVs + (4 * kj + b) * RS + c);
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(KVs + (kj + KG * b) * RS + c);
         sc[0][b] = fmaf(qa.x, kv.x, fmaf(qa.y, kv.y, fmaf(qa.z, kv.z, fmaf(qa.w, kv.w, sc[0][b]))));
         sc[1][b] = fmaf(qb.x, kv.x, fmaf(qb.y, kv.y, fmaf(qb.z, kv.z, fmaf(qb.w, kv.w, sc[1][b]))));
       }
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
       float tmax = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int pl = 4 * kj + b;
+        const int pl = kj + KG * b;
         if (!live[a] || pl >= nk || k0 + pl > qpos[a]) sc[a][b] = -INFINITY;
         tmax = fmaxf(tmax, sc[a][b]);
       }
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const float p = __expf(sc[a][b] - mref);
-        Pt[(4 * kj + b) * QV + 2 * qi + a] = p;
+        Pt[(kj + KG * b) * PS + 2 * qi + a] = p;
         ps += p;
       }
       ps = group_sum<KG>(ps);
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
       const f32x4 vv = *reinterpret_cast<const f32x4*>(KVs + p * RS + 4 * dg);
 #pragma unroll
       for (int a4 = 0; a4 < QPT; a4 += 4) {
-        const f32x4 pa = *reinterpret_cast<const f32x4*>(Pt + p * QV + QPT * qg + a4);
+        const f32x4 pa = *reinterpret_cast<const f32x4*>(Pt + p * PS + QPT * qg + a4);
         o[a4] += pa.x * vv;
         o[a4 + 1] += pa.y * vv;
         o[a4 + 2] += pa.z * vv;
