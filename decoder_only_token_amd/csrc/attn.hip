@@ -248,155 +248,183 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
 
 
 // ---------------------------------------------------------------------------
-// Causal attention for a prefill of T >= 2 rows (flash style, f32 on the VALU).
-// Query row t sits at position pos + t (pos = the step state's position) and
-// sees cache positions 0 .. pos + t, its own included.
+// Causal attention for a prefill of T >= 2 rows (flash style).  Query row t
+// sits at position pos + t (pos = the step state's position) and sees cache
+// positions 0 .. pos + t, its own included.  S = Q K^T and O += P V are dense
+// contractions per tile, so they run as v_mfma_f32_16x16x32_bf16 with
+// every f32 operand split into bf16 halves (x = hi + lo, both rounded to
+// nearest even) and three products (hi.hi + hi.lo + lo.hi, the lo.lo term is
+// below f32 rounding of the result); accumulation is f32.
 //
-// grid (nkv, ceil(T / (QV / G))), block 256.  A block owns kv head g and QV
-// query vectors (QV / G consecutive rows times the G query heads of g), so a
-// K/V tile in LDS serves all of them.  Per tile of BK = 2048 / QV positions:
-//   scores: each thread forms a 2 (query) x 4 (position) tile of dot products
-//           from LDS (queries pre-scaled by 1 / sqrt(d)); its positions are
-//           kj + b BK / 4, so the lanes of a wave read consecutive K rows
-//           (distinct LDS banks);
-//   online softmax: the BK / 4 threads that share a query pair reduce the
-//           tile's max and sum with DPP, rescale the running state and write
-//           the probabilities (transposed) to LDS;
-//   values: each thread accumulates a (QV / 8) (query) x 4 (dim) output tile.
-// K and V of a tile share one LDS buffer (V is held in registers while the
-// scores are formed), which keeps the block under 64 KiB of LDS.  QV = 32
-// doubles the block count of short prompts.  Blocks with the longest causal
-// ranges start first.
-template <int G, int QV>
-__global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ q, int T, int nq,
-                                                      const float* __restrict__ Kc, const float* __restrict__ Vc,
-                                                      int max_pos, const DevState* __restrict__ st, float scale,
-                                                      float* __restrict__ o_out, int ldo) {
-  constexpr int R = QV / G, BK = 2048 / QV, KG = BK / 4, QPT = QV / 8, RS = D + 4, PS = QV + 4;
-  constexpr int VPT = BK * D / 4 / 256;  // V pieces per thread
-  __shared__ __align__(16) float Qs[QV * RS];
-  __shared__ __align__(16) float KVs[BK * RS];  // K of the tile, then its V
-  __shared__ __align__(16) float Pt[BK * PS];  // probabilities [position][query]
-  __shared__ float cs[QV];
-  __shared__ float ls[QV];
-  const int tid = threadIdx.x;
+// grid (nkv, ceil(T / (64 / G))), block 256 = 4 waves.  A block owns 64 query
+// vectors of kv head g; wave w owns 16 of them (the A operand of S, kept in
+// registers for the whole kernel).  Per tile of 32 cache positions the block
+// stages K (row-major) and V (transposed) as bf16 halves in LDS; each wave
+// forms its 16 x 32 score tile, updates the online softmax of its rows
+// (row maxima and sums over the 16 lanes that hold a row, by DPP), writes
+// P's halves to its own LDS slice in the A-operand layout, and accumulates
+// its 16 x 128 output tile.
+template <int G>
+__global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restrict__ q, int T, int nq,
+                                                           const float* __restrict__ Kc,
+                                                           const float* __restrict__ Vc, int max_pos,
+                                                           const DevState* __restrict__ st, float scale,
+                                                           float* __restrict__ o_out, int ldo) {
+  constexpr int QV = 64, R = QV / G, BK = 32;
+  constexpr int KS = D + 8;   // K row stride (bf16)
+  constexpr int VS = BK + 8;  // V^T row stride (bf16)
+  constexpr int PS = BK + 8;  // P row stride (bf16)
+  __shared__ __align__(16) uint16_t Kh[BK * KS], Kl[BK * KS];
+  __shared__ __align__(16) uint16_t Vth[D * VS], Vtl[D * VS];
+  __shared__ __align__(16) uint16_t Ph[4][16 * PS], Pl[4][16 * PS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;  // fragment row / column, k-quarter
   const int g = blockIdx.x;
   const int t0 = (gridDim.y - 1 - blockIdx.y) * R;
   const int pos0 = st->pos;
   const int nrows = min(R, T - t0);
   const int kv_end = pos0 + t0 + nrows;  // one past the last row's position
 
-  for (int i = tid; i < QV * D / 4; i += 256) {
-    const int v = i / (D / 4), c4 = i % (D / 4), r = v / G, j = v % G;
-    f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (r < nrows) val = *reinterpret_cast<const f32x4*>(q + ((size_t)(t0 + r) * nq + g * G + j) * D + c4 * 4) * scale;
-    *reinterpret_cast<f32x4*>(Qs + v * RS + c4 * 4) = val;
-  }
-  const int qi = tid / KG, kj = tid % KG;  // score mapping: queries 2 qi, 2 qi + 1; positions kj + KG b
-  const int qg = tid >> 5, dg = tid & 31;  // value mapping: queries QPT qg .. + QPT - 1; dims 4 dg .. + 3
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  int qpos[2];
-  bool live[2];
+  // this lane's query fragment: vector wave*16 + lr, dims 32 ks + 8 lq .. + 8
+  bf16x8 qh[4], ql[4];
+  {
+    const int v = wave * 16 + lr, r = v / G, j = v % G;
+    const float* src = q + ((size_t)(t0 + r) * nq + g * G + j) * D + 8 * lq;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int r = (2 * qi + a) / G;
-    live[a] = r < nrows;
-    qpos[a] = pos0 + t0 + r;
-  }
-  f32x4 o[QPT];
+    for (int ks = 0; ks < 4; ++ks) {
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, b = a;
+      if (r < nrows) {
+        a = *reinterpret_cast<const f32x4*>(src + 32 * ks) * scale;
+        b = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4) * scale;
+      }
+      const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-  for (int a = 0; a < QPT; ++a) o[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t h = bf16_rne(x[i]);
+        qh[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)h);
+        ql[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)bf16_rne(x[i] - __uint_as_float(h << 16)));
+      }
+    }
+  }
+  // softmax state of this lane's 4 rows (rows 4 lq + e of the wave's 16)
+  float m[4], l[4];
+  int qpos[4];
+  bool live[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = (wave * 16 + 4 * lq + e) / G;
+    m[e] = -INFINITY;
+    l[e] = 0.f;
+    live[e] = r < nrows;
+    qpos[e] = pos0 + t0 + r;
+  }
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float* Kg = Kc + (size_t)g * max_pos * D;
   const float* Vg = Vc + (size_t)g * max_pos * D;
+  // staging map: positions 4 p4 .. + 3, dims 4 c4 .. + 3
+  const int p4 = tid & 7, c4 = tid >> 3;
 
   for (int k0 = 0; k0 < kv_end; k0 += BK) {
     const int nk = min(BK, kv_end - k0);
-    f32x4 vr[VPT];
-    __syncthreads();  // queries staged; the previous tile consumed
+    f32x4 kr[4], vr[4];
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int i = tid + u * 256, p = i / (D / 4), c4 = i % (D / 4);
-      f32x4 kv = f32x4{0.f, 0.f, 0.f, 0.f};
-      vr[u] = kv;
+    for (int pp = 0; pp < 4; ++pp) {
+      const int p = 4 * p4 + pp;
+      kr[pp] = vr[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (p < nk) {
-        kv = *reinterpret_cast<const f32x4*>(Kg + (size_t)(k0 + p) * D + c4 * 4);
-        vr[u] = *reinterpret_cast<const f32x4*>(Vg + (size_t)(k0 + p) * D + c4 * 4);
+        kr[pp] = *reinterpret_cast<const f32x4*>(Kg + (size_t)(k0 + p) * D + 4 * c4);
+        vr[pp] = *reinterpret_cast<const f32x4*>(Vg + (size_t)(k0 + p) * D + 4 * c4);
       }
-      *reinterpret_cast<f32x4*>(KVs + p * RS + c4 * 4) = kv;
+    }
+    __syncthreads();  // the previous tile's K, V and P are consumed
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const float x[4] = {kr[pp].x, kr[pp].y, kr[pp].z, kr[pp].w};
+      uint32_t h[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = bf16_rne(x[i]);
+        lo[i] = bf16_rne(x[i] - __uint_as_float(h[i] << 16));
+      }
+      *reinterpret_cast<u32x2*>(&Kh[(4 * p4 + pp) * KS + 4 * c4]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<u32x2*>(&Kl[(4 * p4 + pp) * KS + 4 * c4]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // dim 4 c4 + i: its 4 positions 4 p4 .. + 3, transposed
+      uint32_t h[4], lo[4];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const float x = vr[pp][i];
+        h[pp] = bf16_rne(x);
+        lo[pp] = bf16_rne(x - __uint_as_float(h[pp] << 16));
+      }
+      *reinterpret_cast<u32x2*>(&Vth[(4 * c4 + i) * VS + 4 * p4]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<u32x2*>(&Vtl[(4 * c4 + i) * VS + 4 * p4]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     }
     __syncthreads();
-    float sc[2][4];
+    // S = Q K^T: 16 queries x 32 positions (two 16 x 16 tiles)
+    f32x4 sc[2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int nt = 0; nt < 2; ++nt) {
+      sc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) sc[a][b] = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < D; c += 4) {
-      const f32x4 qa = *reinterpret_cast<const f32x4*>(Qs + (2 * qi) * RS + c);
-      const f32x4 qb = *reinterpret_cast<const f32x4*>(Qs + (2 * qi + 1) * RS + c);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(KVs + (kj + KG * b) * RS + c);
-        sc[0][b] = fmaf(qa.x, kv.x, fmaf(qa.y, kv.y, fmaf(qa.z, kv.z, fmaf(qa.w, kv.w, sc[0][b]))));
-        sc[1][b] = fmaf(qb.x, kv.x, fmaf(qb.y, kv.y, fmaf(qb.z, kv.z, fmaf(qb.w, kv.w, sc[1][b]))));
+      for (int ks = 0; ks < 4; ++ks) {
+        const int off = (nt * 16 + lr) * KS + 32 * ks + 8 * lq;
+        const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&Kh[off]);
+        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&Kl[off]);
+        sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kh, sc[nt], 0, 0, 0);
+        sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kl, sc[nt], 0, 0, 0);
+        sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kh, sc[nt], 0, 0, 0);
       }
     }
+    // online softmax; element e of sc[nt] is row 4 lq + e, position nt * 16 + lr
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      float tmax = -INFINITY;
+    for (int e = 0; e < 4; ++e) {
+      float s0 = sc[0][e], s1 = sc[1][e];
+      if (!live[e] || lr >= nk || k0 + lr > qpos[e]) s0 = -INFINITY;
+      if (!live[e] || 16 + lr >= nk || k0 + 16 + lr > qpos[e]) s1 = -INFINITY;
+      const float mn = fmaxf(m[e], group_max<16>(fmaxf(s0, s1)));
+      const float mref = mn == -INFINITY ? 0.f : mn;  // a row with nothing visible yet
+      const float e0 = __expf(s0 - mref), e1 = __expf(s1 - mref);
+      const float c = __expf(m[e] - mref);
+      l[e] = l[e] * c + group_sum<16>(e0 + e1);
+      m[e] = mn;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int pl = kj + KG * b;
-        if (!live[a] || pl >= nk || k0 + pl > qpos[a]) sc[a][b] = -INFINITY;
-        tmax = fmaxf(tmax, sc[a][b]);
-      }
-      tmax = group_max<KG>(tmax);
-      const float mn = fmaxf(m[a], tmax);
-      const float mref = mn == -INFINITY ? 0.f : mn;  // a query with nothing visible yet
-      float ps = 0.f;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float p = __expf(sc[a][b] - mref);
-        Pt[(kj + KG * b) * PS + 2 * qi + a] = p;
-        ps += p;
-      }
-      ps = group_sum<KG>(ps);
-      const float c = __expf(m[a] - mref);
-      l[a] = l[a] * c + ps;
-      m[a] = mn;
-      if (kj == 0) cs[2 * qi + a] = c;
+      for (int dt = 0; dt < D / 16; ++dt) oacc[dt][e] *= c;
+      const uint32_t h0 = bf16_rne(e0), h1 = bf16_rne(e1);
+      uint16_t* ph = &Ph[wave][(4 * lq + e) * PS];
+      uint16_t* pl = &Pl[wave][(4 * lq + e) * PS];
+      ph[lr] = (uint16_t)h0;
+      ph[16 + lr] = (uint16_t)h1;
+      pl[lr] = (uint16_t)bf16_rne(e0 - __uint_as_float(h0 << 16));
+      pl[16 + lr] = (uint16_t)bf16_rne(e1 - __uint_as_float(h1 << 16));
     }
-    __syncthreads();  // every score formed: the buffer takes V
+    __syncthreads();  // P written (each wave reads back only its own slice)
+    // O += P V: A = P (16 queries x 32 positions), B = V^T fragments of 8 dim tiles
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ph[wave][lr * PS + 8 * lq]);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Pl[wave][lr * PS + 8 * lq]);
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int i = tid + u * 256, p = i / (D / 4), c4 = i % (D / 4);
-      *reinterpret_cast<f32x4*>(KVs + p * RS + c4 * 4) = vr[u];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < QPT; ++a) o[a] = o[a] * cs[QPT * qg + a];
-    for (int p = 0; p < nk; ++p) {
-      const f32x4 vv = *reinterpret_cast<const f32x4*>(KVs + p * RS + 4 * dg);
-#pragma unroll
-      for (int a4 = 0; a4 < QPT; a4 += 4) {
-        const f32x4 pa = *reinterpret_cast<const f32x4*>(Pt + p * PS + QPT * qg + a4);
-        o[a4] += pa.x * vv;
-        o[a4 + 1] += pa.y * vv;
-        o[a4 + 2] += pa.z * vv;
-        o[a4 + 3] += pa.w * vv;
-      }
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int off = (dt * 16 + lr) * VS + 8 * lq;
+      const bf16x8 vh = *reinterpret_cast<const bf16x8*>(&Vth[off]);
+      const bf16x8 vl = *reinterpret_cast<const bf16x8*>(&Vtl[off]);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vh, oacc[dt], 0, 0, 0);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vl, oacc[dt], 0, 0, 0);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, vh, oacc[dt], 0, 0, 0);
     }
   }
-  if (kj == 0) {
-    ls[2 * qi] = l[0];
-    ls[2 * qi + 1] = l[1];
-  }
-  __syncthreads();
+  // element e of oacc[dt]: row 4 lq + e, dim dt * 16 + lr
 #pragma unroll
-  for (int a = 0; a < QPT; ++a) {
-    const int v = QPT * qg + a, r = v / G, j = v % G;
-    if (r < nrows)
-      *reinterpret_cast<f32x4*>(o_out + (size_t)(t0 + r) * ldo + (g * G + j) * D + 4 * dg) = o[a] * (1.0f / ls[v]);
+  for (int e = 0; e < 4; ++e) {
+    const int v = wave * 16 + 4 * lq + e, r = v / G, j = v % G;
+    if (r < nrows) {
+      const float inv = 1.0f / l[e];
+      float* dst = o_out + (size_t)(t0 + r) * ldo + (g * G + j) * D + lr;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) dst[dt * 16] = oacc[dt][e] * inv;
+    }
   }
 }
 
@@ -432,21 +460,17 @@ void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int 
                               int max_pos, const DevState* st, float* o_out, int ldo, int ncu) {
   const float scale = 1.0f / sqrtf((float)D);
   const int G = nq / nkv;
-  // 64 query vectors per block, or 32 when that leaves the GPU under two blocks per CU
-  const bool small = (size_t)nkv * ((T + 64 / G - 1) / (64 / G)) < (size_t)2 * ncu;
-#define QD_ATTN_PREFILL(G_, QV_)                                                                                    \
-  hipLaunchKernelGGL((k_attn_prefill<G_, QV_>), dim3(nkv, (T + QV_ / G_ - 1) / (QV_ / G_)), dim3(256), 0, s, q, T, nq, \
-                     Kc, Vc, max_pos, st, scale, o_out, ldo)
-  switch (G * (small ? -1 : 1)) {
-    case 1: QD_ATTN_PREFILL(1, 64); break;
-    case 2: QD_ATTN_PREFILL(2, 64); break;
-    case 4: QD_ATTN_PREFILL(4, 64); break;
-    case 8: QD_ATTN_PREFILL(8, 64); break;
-    case -1: QD_ATTN_PREFILL(1, 32); break;
-    case -2: QD_ATTN_PREFILL(2, 32); break;
-    case -4: QD_ATTN_PREFILL(4, 32); break;
-    case -8: QD_ATTN_PREFILL(8, 32); break;
+  const dim3 grid(nkv, (T + 64 / G - 1) / (64 / G));
+#define QD_ATTN_PREFILL(G_)                                                                                   \
+  hipLaunchKernelGGL(k_attn_prefill_mfma<G_>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, \
+                     ldo)
+  switch (G) {
+    case 1: QD_ATTN_PREFILL(1); break;
+    case 2: QD_ATTN_PREFILL(2); break;
+    case 4: QD_ATTN_PREFILL(4); break;
+    case 8: QD_ATTN_PREFILL(8); break;
     default: break;  // rejected by the host before any launch
   }
 #undef QD_ATTN_PREFILL
+  (void)ncu;
 }

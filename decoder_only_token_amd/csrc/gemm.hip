@@ -30,17 +30,9 @@
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int LDR = BK + 8;  // padded LDS row (bf16): 144 bytes
 constexpr int kThreads = 256;
-
-// f32 -> bf16 bit pattern, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 // One block per row: optional RMSNorm with gains, then the hi/lo split.
 __global__ __launch_bounds__(256) void k_split_rows(const float* __restrict__ x, int ldx, int K,
