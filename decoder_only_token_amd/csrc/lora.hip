@@ -14,12 +14,20 @@
 
 namespace {
 
-// grid (ceil((nq + nkv) d / 256), min(T, 65535)), block 256: one thread per
-// adapted output row (q rows, then v rows), rows of the input strided by gridDim.y.
+constexpr int kRowsPerBlock = 32;  // input rows per block of the up product
+constexpr int kMaxRank = 64;
+
+// grid (ceil((nq + nkv) d / 256), ceil(T / kRowsPerBlock)), block 256: one
+// thread per adapted output row (q rows, then v rows) holding its row of B in
+// registers; the block's input rows of u are staged in LDS.
 __global__ __launch_bounds__(256) void k_lora_up(const float* __restrict__ u, int ldu, int T, int r,
                                                  const uint16_t* __restrict__ Bq, const uint16_t* __restrict__ Bv,
                                                  int nq, int nkv, int d, float scale, float* __restrict__ qkv,
                                                  int ldqkv) {
+  __shared__ float us[kRowsPerBlock * 2 * kMaxRank];
+  const int t0 = blockIdx.y * kRowsPerBlock, nt = min(kRowsPerBlock, T - t0);
+  for (int i = threadIdx.x; i < nt * 2 * r; i += 256) us[i] = u[(size_t)(t0 + i / (2 * r)) * ldu + i % (2 * r)];
+  __syncthreads();
   const int row = blockIdx.x * 256 + threadIdx.x;
   const int G = nq / nkv;
   if (row >= (nq + nkv) * d) return;
@@ -36,11 +44,16 @@ __global__ __launch_bounds__(256) void k_lora_up(const float* __restrict__ u, in
     uoff = r;
     dst = g * (G + 2) * d + (G + 1) * d + j;
   }
-  for (int t = blockIdx.y; t < T; t += gridDim.y) {
-    const float* ut = u + (size_t)t * ldu + uoff;
+  float b[kMaxRank];
+#pragma unroll
+  for (int i = 0; i < kMaxRank; ++i) b[i] = i < r ? bf16_to_f(B[i]) : 0.f;
+  for (int t = 0; t < nt; ++t) {
+    const float* ut = us + t * 2 * r + uoff;
     float a = 0.f;
-    for (int i = 0; i < r; ++i) a = fmaf(bf16_to_f(B[i]), ut[i], a);
-    qkv[(size_t)t * ldqkv + dst] += scale * a;
+#pragma unroll
+    for (int i = 0; i < kMaxRank; ++i)
+      if (i < r) a = fmaf(b[i], ut[i], a);
+    qkv[(size_t)(t0 + t) * ldqkv + dst] += scale * a;
   }
 }
 
@@ -48,6 +61,6 @@ __global__ __launch_bounds__(256) void k_lora_up(const float* __restrict__ u, in
 
 void launch_lora_up(hipStream_t s, const float* u, int ldu, int T, int r, const uint16_t* Bq, const uint16_t* Bv,
                     int nq, int nkv, int d, float scale, float* qkv, int ldqkv) {
-  const dim3 grid(((nq + nkv) * d + 255) / 256, T < 65535 ? T : 65535);
+  const dim3 grid(((nq + nkv) * d + 255) / 256, (T + kRowsPerBlock - 1) / kRowsPerBlock);
   hipLaunchKernelGGL(k_lora_up, grid, dim3(256), 0, s, u, ldu, T, r, Bq, Bv, nq, nkv, d, scale, qkv, ldqkv);
 }
