@@ -18,9 +18,10 @@
 //
 // int4 group-128 weights ("EMBERGLASS (qwen-webgpu-lora) README", "Note on
 // weights") go through the same tiles: the 32 codes a thread loads become 32
-// exact bf16 integers in the W tile, the products of one 128-column group are
-// accumulated apart, and at the end of the group each output column's partial
-// is multiplied by its fp16 scale and added to the running sum.
+// exact bf16 integers in the W tile and the matrix cores accumulate code x
+// products; the fp16 group scales enter as a running rescale of each output
+// column's accumulator (by previous scale / new scale at a group change, by
+// the last scale at the end), so no second accumulator set is needed.
 #include <hip/hip_fp16.h>
 
 #include "common.h"
@@ -144,17 +145,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
     }
   };
 
-  f32x4 acc[4][4], tot[Q4 ? 4 : 1][Q4 ? 4 : 1];  // Q4: acc holds the current group, tot the scaled sum
+  // Q4: acc holds sum_groups code.x * e_g / e_cur, where e_g is the group's
+  // scale (a zero scale keeps the previous one: its codes are all zero);
+  // entering a group multiplies acc by e_prev / e_new, and the end by e_last.
+  f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (Q4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tot[Q4 ? i : 0][Q4 ? j : 0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
 
   // B rows of this wave's 4 column tiles
   int brow[4];
@@ -168,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   gload_k(0);
   sstore();
   __syncthreads();
-  float scl[4];  // Q4: fp16 scales of this lane's 4 output columns in the current group
+  float scl[4] = {1.f, 1.f, 1.f, 1.f};  // Q4: current scale e of this lane's 4 output columns
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) gload_k(kt + 1);  // the next K-step flies during this one
     if (Q4 && (kt & 1) == 0) {
@@ -184,7 +182,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
           n = n0 + wn * 64 + j * 16 + (lane & 15);
           S = SB;
         }
-        scl[j] = __half2float(__ushort_as_half(S[(size_t)min(n, N - 1) * (K / 128) + g]));
+        const float e = __half2float(__ushort_as_half(S[(size_t)min(n, N - 1) * (K / 128) + g]));
+        if (e > 0.f) {
+          const float r = scl[j] / e;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i][j] *= r;
+          scl[j] = e;
+        }
       }
     }
 #pragma unroll
@@ -206,15 +210,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
         }
       }
     }
-    if (Q4 && (kt & 1) == 1) {  // end of a 128-column group
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          tot[Q4 ? i : 0][Q4 ? j : 0] += scl[j] * acc[i][j];
-          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
     if (kt + 1 < nk) {
       __syncthreads();  // every wave is done with this K-step's tiles
       sstore();
@@ -225,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = tot[Q4 ? i : 0][Q4 ? j : 0];
+      for (int j = 0; j < 4; ++j) acc[i][j] *= scl[j];
   }
 
   // epilogue: acc[i][j] element e of lane is C[row 4 (lane / 16) + e][col lane % 16]

@@ -154,3 +154,34 @@ def test_int4_readback_errors(torch_cuda):
     with pytest.raises(qd.QdError) as e:
         bf.get_quantized(0, "wq", (shape.n_q_heads * 128, shape.hidden))
     assert e.value.code == -3
+
+
+def test_int4_edge_groups_through_both_paths(torch_cuda):
+    """Weights with an all-zero group (scale 0), an fp16-subnormal scale and
+    round-half-even ties, through the matrix-core prefill (40 rows: zero
+    scales keep the running rescale unchanged) and the GEMV decode."""
+    import decoder_only_token_amd as qd
+    shape = synth.TINY_INT4
+    w = plant_edge_groups(synth.make_weights(shape, seed=47, random_gains=True))
+    # a whole zero row group in a second matrix as well, first and last group
+    wo = synth.bf16_to_f32(w["layers"][1]["wo"]).copy()
+    wo[5, :128] = 0.0
+    wo[6, -128:] = 0.0
+    w["layers"][1]["wo"] = synth.bf16_round(wo)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 64)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    dec.enable_capture(True)
+    prompt = synth.make_prompt(shape.vocab, 40, seed=48)
+    dec.prefill(prompt)
+    cap = {}
+    oracle.forward(prompt, capture=cap)
+    H = shape.hidden
+    for l in range(shape.n_layers):
+        got = dec.get_capture(qd.QD_CAP_LAYER_OUT, l, 40 * H).reshape(40, H)
+        np.testing.assert_allclose(got, cap["layer_out"][l], rtol=1e-3, atol=1e-3)
+    dec.enable_capture(False)
+    recs = lockstep_greedy(dec, oracle, prompt[:6], 6, log=log)
+    assert not [r for r in recs if r.n_bad]
