@@ -106,12 +106,17 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
   }
 
   const int pl = tid >> 2, sub = tid & 3;  // load / score mapping: position, quarter of the dims
-  const int dd = tid & 127, jh = tid >> 7; // output mapping: dim, head parity
-  constexpr int JPT = G >= 2 ? G / 2 : 1;  // output heads per thread
+  // output mapping: G < 8: dim dd of heads jh, jh + 2, ...; G = 8: dims
+  // 4 dq .. + 3 of head hq (one 16-byte V read feeds four products)
+  const int dd = tid & 127, jh = tid >> 7;
+  const int dq = tid & 31, hq = tid >> 5;
+  constexpr bool QUAD = G == 8;
+  constexpr int JPT = QUAD ? 1 : (G >= 2 ? G / 2 : 1);  // output heads per thread
   constexpr int HPW = G >= 4 ? G / 4 : 1;  // softmax heads per wave
   float acc[JPT];
 #pragma unroll
   for (int i = 0; i < JPT; ++i) acc[i] = 0.f;
+  f32x4 acc4 = f32x4{0.f, 0.f, 0.f, 0.f};
   float M[HPW], L[HPW];
 #pragma unroll
   for (int r = 0; r < HPW; ++r) { M[r] = -INFINITY; L[r] = 0.f; }
@@ -180,22 +185,37 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
       }
     }
     __syncthreads();
+    if (QUAD) {
+      f32x4 a = acc4 * cs[hq];
+      const float* pj = ps + hq * TP;
+      for (int p = 0; p < n; ++p) a += pj[p] * *reinterpret_cast<const f32x4*>(vs + p * D + 4 * dq);
+      acc4 = a;
+    } else {
 #pragma unroll
-    for (int i = 0; i < JPT; ++i) {
-      const int j = G >= 2 ? jh + 2 * i : 0;
-      if (G >= 2 || jh == 0) {
-        float a = acc[i] * cs[j];
-        const float* pj = ps + j * TP;
-        for (int p = 0; p < n; ++p) a = fmaf(pj[p], vs[p * D + dd], a);
-        acc[i] = a;
+      for (int i = 0; i < JPT; ++i) {
+        const int j = G >= 2 ? jh + 2 * i : 0;
+        if (G >= 2 || jh == 0) {
+          float a = acc[i] * cs[j];
+          const float* pj = ps + j * TP;
+          for (int p = 0; p < n; ++p) a = fmaf(pj[p], vs[p * D + dd], a);
+          acc[i] = a;
+        }
       }
     }
   }
   float* base = part + ((size_t)g * G * S + sp) * (D + 2);
+  if (QUAD) {
+    float* o = base + (size_t)hq * S * (D + 2) + 2 + 4 * dq;
+    o[0] = acc4.x;
+    o[1] = acc4.y;
+    o[2] = acc4.z;
+    o[3] = acc4.w;
+  } else {
 #pragma unroll
-  for (int i = 0; i < JPT; ++i) {
-    const int j = G >= 2 ? jh + 2 * i : 0;
-    if (G >= 2 || jh == 0) base[(size_t)j * S * (D + 2) + 2 + dd] = acc[i];
+    for (int i = 0; i < JPT; ++i) {
+      const int j = G >= 2 ? jh + 2 * i : 0;
+      if (G >= 2 || jh == 0) base[(size_t)j * S * (D + 2) + 2 + dd] = acc[i];
+    }
   }
 #pragma unroll
   for (int r = 0; r < HPW; ++r) {
