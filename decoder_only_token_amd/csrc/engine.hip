@@ -144,7 +144,9 @@ namespace {
 template <typename T>
 int dev_alloc(qd_handle* h, T** p, size_t n) {
   void* v = nullptr;
-  hipError_t e = hipMalloc(&v, n * sizeof(T) + 16);
+  // 1 KiB of tail padding: a kernel may read (and ignore) up to one 512-value
+  // bf16 segment past the last row of a matrix
+  hipError_t e = hipMalloc(&v, n * sizeof(T) + 1024);
   if (e != hipSuccess) return h->set_err(QD_E_OOM, std::string("hipMalloc: ") + hipGetErrorString(e));
   h->allocs.push_back(v);
   *p = static_cast<T*>(v);
@@ -477,7 +479,9 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   const size_t kv = (size_t)c.n_layers * c.n_kv_heads * c.max_pos * d;
   h->dec_splits = attn_decode_splits(c.max_pos, c.n_kv_heads, h->ncu, kDecodeMinSplit);
   h->part_floats = (size_t)c.n_q_heads * h->dec_splits * (d + 2);
-  if ((rc = dev_alloc(h, &h->Kc, kv)) || (rc = dev_alloc(h, &h->Vc, kv)) ||
+  // the caches carry 256 rows of tail padding: the persistent decode step reads
+  // (and ignores) up to 192 positions past the end of a split
+  if ((rc = dev_alloc(h, &h->Kc, kv + 256 * d)) || (rc = dev_alloc(h, &h->Vc, kv + 256 * d)) ||
       (rc = dev_alloc(h, &h->rope_cos, (size_t)c.max_pos * d / 2)) ||
       (rc = dev_alloc(h, &h->rope_sin, (size_t)c.max_pos * d / 2)) || (rc = dev_alloc(h, &h->x, rows * H)) ||
       (rc = dev_alloc(h, &h->qkv, rows * qkv_rows(c))) || (rc = dev_alloc(h, &h->q, rows * c.n_q_heads * d)) ||
@@ -492,6 +496,11 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
       (rc = dev_alloc(h, &h->spi, (size_t)sample_lists(c.vocab) * 64)) ||
       (rc = dev_alloc(h, &h->tokens_dev, rows)) || (rc = dev_alloc(h, &h->st, 1)))
     return fail(rc);
+  // caches start as zeros, padding included (rows are read past a split's end
+  // and discarded; zeros keep even the discarded values finite)
+  if (hipMemset(h->Kc, 0, (kv + 256 * d) * sizeof(float)) != hipSuccess ||
+      hipMemset(h->Vc, 0, (kv + 256 * d) * sizeof(float)) != hipSuccess)
+    return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
   if (hipHostMalloc((void**)&h->tokens_pinned, rows * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
     return fail(h->set_err(QD_E_OOM, "hipHostMalloc failed"));
   if ((rc = build_rope_tables(h))) return fail(rc);
@@ -506,10 +515,15 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     h->hseg = c.hidden / 512;
     const int G = c.n_q_heads / c.n_kv_heads;
     if (persist_prepare(G, h->hseg) != 0) return fail(h->set_err(QD_E_HIP, "persistent decode kernel unavailable"));
-    if ((c.hidden + h->grid - 1) / h->grid > 64)
-      return fail(h->set_err(QD_E_ARG, "too many hidden rows per CU for the persistent decode step"));
-    if (c.hidden < h->grid || c.intermediate < h->grid || qkv_rows(c) < h->grid || c.vocab < h->grid)
-      return fail(h->set_err(QD_E_ARG, "the persistent decode step needs at least one row of every projection per CU"));
+    {  // the role plan must exist at the shortest and the longest context
+      PersistConst shape{};
+      shape.H = c.hidden; shape.nq = c.n_q_heads; shape.nkv = c.n_kv_heads; shape.I = c.intermediate;
+      shape.nqkv = (int)qkv_rows(c); shape.max_pos = c.max_pos; shape.V = c.vocab;
+      PersistStep st;
+      if (c.vocab < h->grid || persist_plan(shape, h->grid, 0, 1, &st) != 0 ||
+          persist_plan(shape, h->grid, c.max_pos - 1, 1, &st) != 0)
+        return fail(h->set_err(QD_E_ARG, "the model does not fit the CU roles of the persistent decode step"));
+    }
     const size_t smax = (size_t)h->grid / c.n_kv_heads;
     if ((rc = dev_alloc(h, &h->X0, H)) || (rc = dev_alloc(h, &h->X1, H)) ||
         (rc = dev_alloc(h, &h->QKVx, (size_t)qkv_rows(c))) ||
@@ -578,9 +592,10 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
             (rc = dev_alloc(h, &L.cd, H * I / 2)) || (rc = dev_alloc(h, &L.sd, H * I / 128)))
           return rc;
       } else if ((rc = dev_alloc(h, &L.wqkv, NQKV * H)) || (rc = dev_alloc(h, &L.wo, H * nq * d)) ||
-                 (rc = dev_alloc(h, &L.wg, I * H)) || (rc = dev_alloc(h, &L.wu, I * H)) ||
-                 (rc = dev_alloc(h, &L.wd, H * I))) {
+                 (rc = dev_alloc(h, &L.wg, 2 * I * H)) || (rc = dev_alloc(h, &L.wd, H * I))) {
         return rc;
+      } else {
+        L.wu = L.wg + I * H;  // gate and up rows share one allocation
       }
       if (c.qk_norm && ((rc = dev_alloc(h, &L.q_norm, d)) || (rc = dev_alloc(h, &L.k_norm, d)))) return rc;
       if (c.qkv_bias && (rc = dev_alloc(h, &L.bqkv, NQKV))) return rc;
@@ -709,15 +724,14 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
   if (rc) return rc;
   if (h->failed) return h->set_err(QD_E_STATE, "an earlier decode step was abandoned; call qd_reset_kv");
   if (h->persistent) {
-    const int ctx = h->pos + 1;
-    const int cap = h->grid / h->cfg.n_kv_heads;
-    int S = (ctx + 63) / 64;
-    if (S > cap) S = cap;
-    const int chunk = (ctx + S - 1) / S;
-    S = (ctx + chunk - 1) / chunk;  // every split holds at least one position
     if (++h->seq >= (1u << 24)) h->seq = 1;
+    PersistStep st;
+    if (persist_plan(h->pc_host, h->grid, h->pos, h->seq, &st) != 0)
+      return h->set_err(QD_E_HIP, "no CU role plan for this decode step");
     const int G = h->cfg.n_q_heads / h->cfg.n_kv_heads;
-    int e = persist_launch(h->pconst, G, h->hseg, h->grid, h->pos, h->seq, S, chunk, h->stream);
+    if (h->trace_on)  // a traced step writes only the stamps of its CUs' phases
+      HIP_TRY(h, hipMemsetAsync(h->trace, 0, (size_t)h->grid * persist_trace_slots(h->cfg.n_layers) * 8, h->stream));
+    int e = persist_launch(h->pconst, G, h->hseg, h->grid, st, h->stream);
     if (e != 0) return h->set_err(QD_E_HIP, "persistent decode launch failed: " + std::to_string(e));
     if ((rc = maybe_sample(h, sampling))) return rc;
     h->pos += 1;

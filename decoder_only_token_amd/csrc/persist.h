@@ -47,12 +47,26 @@ struct PersistConst {
 
 // Trace stamps per phase (100 MHz real-time counter), per CU, by thread 0:
 //   0 starts polling the phase input       1 the input is in LDS (after the barrier)
-//   3 finished its dot products            5 finished the phase (outputs written)
-//   7 kernel start (phase 0 only)          2, 4, 6 unused
+//   2 finished its dot products            3 outputs published
+//   5 next slice requested (phase done)    7 kernel start (phase 0 only); 4, 6 unused
 constexpr int kTraceSlots = 8;
 __host__ __device__ inline int persist_trace_slots(int L) { return (5 * L + 2) * kTraceSlots; }
 
+// One decode step's launch plan: the attention splits and the CU ranges of
+// the five roles (role r runs on blocks [start[r], start[r + 1]): QKV rows,
+// attention items (kv head, head group, split), o_proj rows, gate/up row
+// pairs, down rows).
+struct PersistStep {
+  int pos;       // position of the new token
+  uint32_t seq;  // step number in the tags (1 .. 2^24 - 1)
+  int S, chunk;  // splits per kv head, positions per split
+  int X;         // head groups per kv head: attention items = nkv X S
+  int start[6];
+};
+
 size_t persist_smem_bytes();
 int persist_prepare(int G, int hseg);
-int persist_launch(const PersistConst* dev_const, int G, int hseg, int grid, int pos, uint32_t seq, int S, int chunk,
-                   hipStream_t s);
+// Plans the step at position pos for `grid` CUs; 0 on success, -1 if the
+// grid cannot hold the five roles.
+int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, PersistStep* out);
+int persist_launch(const PersistConst* dev_const, int G, int hseg, int grid, const PersistStep& st, hipStream_t s);

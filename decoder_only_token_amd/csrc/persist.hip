@@ -1,7 +1,7 @@
 // Persistent decode step for gfx950: the whole single-token forward in ONE
 // cooperative kernel launch, one 512-thread workgroup (8 waves) per CU.
 //
-// A decode step is a chain of ~5 dependent phases per layer.  As separate
+// A decode step is a chain of 5 dependent phases per layer.  As separate
 // kernels every dependency costs a launch gap plus the ramp and tail of the
 // next kernel; here each dependency is a device-scope handshake instead.
 // Producers publish every value as a 64-bit word {f32 value | tag << 32} with
@@ -9,31 +9,42 @@
 // until every word carries the tag they expect.  No fences, no shared
 // counters, no L2 writeback/invalidate: the tag itself says the value is there.
 //
-// Phases of layer l (tag = seq << 8 | l unless noted):
-//   A  rows of q|k|v = W_qkv RMSNorm(x0) + b                       -> QKV
-//   B  attention item (kv head g, split s): QK-norm, RoPE, KV-cache write,
-//      online softmax over its positions; split partials merged     -> O
-//   C  rows of x1 = x0 + W_o o                                       -> X1
-//   D1 rows of act = SiLU(W_g h2) * (W_u h2), h2 = RMSNorm(x1)        -> ACT
-//   D2 rows of x0' = x1 + W_d act                                    -> X0 (tag l+1)
-// then the final RMSNorm + tied LM head with per-CU argmax partials, and the
-// argmax over the partials by CU 0, which advances the step state.
+// Roles.  Every CU serves ONE phase kind in every layer (the host sizes the
+// five groups of CUs in proportion to their bytes per layer):
+//   Q   rows of q|k|v = W_qkv RMSNorm(x0) + b                          -> QKV
+//   A   attention item (kv head g, split s): QK-norm, RoPE, KV-cache write,
+//       online softmax over its positions; split partials merged        -> O
+//   O   rows of x1 = x0 + W_o o                                          -> X1
+//   GU  rows of act = SiLU(W_g h2) * (W_u h2), h2 = RMSNorm(x1)           -> ACT
+//   D   rows of x0' = x1 + W_d act                                       -> X0
+// (tag = seq << 8 | l; D publishes x0' with the tag of layer l + 1.)
+// A CU that has finished its phase of layer l has four handshakes of time
+// before its input of layer l + 1 can exist, so it loads its whole slice of
+// layer l + 1 (weights, or the cached K/V rows of its item) into registers
+// right away: the weight stream runs beside the chain of handshakes instead of
+// inside it, and each buffer is polled by one group of CUs only.  After the
+// last layer every CU loads the first batch of its LM-head rows the same way;
+// then all CUs take the final RMSNorm + tied LM head with per-CU argmax
+// partials, and CU 0 the argmax over the partials, advancing the step state.
 //
 // Every phase: all 512 threads poll the input (a few values each) into LDS,
-// one workgroup barrier, then each wave computes whole output rows from
-// weights that were loaded into registers at the end of the PREVIOUS phase, so
-// the weight stream overlaps the handshake.  RMSNorm is folded in: the LDS
-// input is gain * x and each row sum is scaled by 1/RMS(x) afterwards.
+// one workgroup barrier, then each wave computes whole output rows.  RMSNorm
+// is folded in: the LDS input is gain * x and each row sum is scaled by
+// 1/RMS(x) afterwards.
 //
 // The fused QKV rows are stored group-major ([kv head g][q heads of g | k_g |
 // v_g] x 128), so one attention item reads one contiguous run.
 //
-// Reusing a buffer across phases is safe: every reader of a buffer instance
+// Reusing a buffer across layers is safe: every reader of a buffer instance
 // is, through the dataflow, a required producer of what the next writer of
-// that buffer waits for.  This needs every CU to own at least one row of the
-// QKV, hidden and intermediate projections (the host checks it), and every
-// LDS input slot is rewritten only after a workgroup barrier that all waves
-// reach after their last read of it.
+// that buffer waits for.  This needs every CU of a role to own at least one
+// output row (the host plans it so), and every LDS input slot is rewritten
+// only after a workgroup barrier that all waves reach after their last read
+// of it (slots alternate by layer).
+
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "persist.h"
 
@@ -42,10 +53,15 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = 8;
 constexpr int kSeg = 512;  // bf16 per segment: 64 lanes x 8 values (16 bytes)
-constexpr int kBatch = 8;  // segments per wave per load batch
+constexpr int kBatch = 8;  // segments per wave per streamed batch
+constexpr int kFirst = 24; // segments per wave loaded ahead (one layer slice, or the first LM-head rows)
 constexpr int D = 128;     // head_dim
 constexpr int kVecMax = 11264;
+constexpr int kResMax = 512;  // residual rows of one CU (O and D roles)
+constexpr int kOutMax = 4096; // output units of one CU in a phase (and LM-head rows)
+constexpr int kTraceL = 64;   // layers covered by the phase trace
 constexpr int kAttStride = D + 4;  // {m, l, -, -, o[128]}: o stays 16-byte aligned
+constexpr int kRedStride = 68;     // row stride of the GEMV row-sum scratch (floats)
 constexpr int kPE = 8;             // tagged values per thread per poll pass (4096 per pass)
 constexpr uint64_t kTimeoutTicks = 20000000ull;  // 200 ms of the 100 MHz real-time counter
 
@@ -103,34 +119,54 @@ __device__ __forceinline__ float half_total(float v) {  // the sum of this lane'
 }
 
 struct Smem {
-  float vec[2][kVecMax];  // phase inputs (gain * x for normed phases), slot = phase & 1
-  float xres[2][64];      // residual rows of this CU, slot = phase & 1
-  float att[kWaves * 8 * kAttStride];
+  float vec[2][kVecMax];    // phase inputs (gain * x for normed phases), slot = layer & 1
+  float xres[2][kResMax];   // residual rows of this CU, slot = layer & 1
+  float att[kWaves * 8 * kAttStride > kWaves * 16 * kRedStride ? kWaves * 8 * kAttStride : kWaves * 16 * kRedStride];
   float qk[10 * D];  // rotated q heads, k, v of one kv group
-  float red[48];     // [0, 16): RMS partials by phase parity; [32, 48): LM-head argmax
+  float red[48];     // [0, 16): RMS partials by slot; [32, 48): LM-head argmax
+  float outv[kOutMax];  // this CU's results of a phase, published together at its end
+  uint64_t ts[kTraceL + 2][8];  // phase-trace stamps of this CU's phases (written out at the end)
   int abort_flag;
 };
 
+static_assert(sizeof(Smem) <= 160 * 1024, "the workgroup's LDS holds Smem");
+
+enum { kQKV = 0, kAttn = 1, kOproj = 2, kGateUp = 3, kDown = 4 };
+
 struct Ctx {
   const AS4 PersistConst* a;
-  int pos, S, chunk;
+  int pos, S, chunk, X;  // X: head groups per kv head (attention items = nkv X S)
   uint32_t seq;
   uint64_t t0;
-  // this CU's row ranges, computed once: fused qkv rows, hidden rows,
-  // intermediate rows, vocabulary rows
-  int q0, q1, h0, h1, i0, i1, v0, v1;
+  int role, rank, nrole;  // this CU's role, its index among the CUs of the role, their number
+  int r0, r1;             // the role's output units of this CU (rows; gate/up row pairs)
+  int v0, v1;             // vocabulary rows of this CU (every CU)
 };
 
-// rows [r0, r1) of N split evenly over the grid (32-bit: N * grid < 2^31)
-__device__ __forceinline__ void cu_rows(int N, int& r0, int& r1) {
-  r0 = (int)(((uint32_t)N * blockIdx.x) / gridDim.x);
-  r1 = (int)(((uint32_t)N * (blockIdx.x + 1)) / gridDim.x);
+// Phase-trace stamps go to LDS (a global store here would make later waits on
+// the memory counter also wait for it) and are written out when the step ends.
+// Local phase index: layer l, then L (LM head) and L + 1 (final argmax);
+// slots 0..5 of the trace layout.
+__device__ __forceinline__ void stamp(const Ctx& c, Smem& sm, int ph, int what, bool who) {
+  if (c.a->trace && who) {
+    const int L = c.a->L;
+    const int li = ph < 5 * L ? ph / 5 : L + (ph - 5 * L);
+    if (li < kTraceL + 2) sm.ts[li][what] = __builtin_amdgcn_s_memrealtime();
+  }
 }
 
-__device__ __forceinline__ void stamp(const Ctx& c, int ph, int what, bool who) {
-  if (c.a->trace && who)
-    *gl(c.a->trace + (size_t)blockIdx.x * persist_trace_slots(c.a->L) + ph * kTraceSlots + what) =
-        __builtin_amdgcn_s_memrealtime();
+__device__ __forceinline__ void trace_flush(const Ctx& c, Smem& sm) {
+  const AS4 PersistConst& a = *c.a;
+  const int n = (min(a.L, kTraceL) + 2) * 8;
+  uint64_t* out = a.trace + (size_t)blockIdx.x * persist_trace_slots(a.L);
+  if (threadIdx.x == 0) *gl(out + 7) = c.t0;  // kernel start: phase 0, slot 7
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int li = i / 8, k = i % 8;
+    const uint64_t v = sm.ts[li][k];
+    if (v == 0) continue;
+    const int ph = li < a.L ? 5 * li + c.role : 5 * a.L + (li - a.L);
+    *gl(out + ph * kTraceSlots + k) = v;
+  }
 }
 
 __device__ __forceinline__ bool timed_out(const Ctx& c) {
@@ -138,13 +174,16 @@ __device__ __forceinline__ bool timed_out(const Ctx& c) {
 }
 
 // ------------------------------------------------------------------ polling
-// All 512 threads: copy n tagged values src[0..n) (and n2 <= 64 values
+// All 512 threads: copy n tagged values src[0..n) (and n2 <= 512 values
 // src2[0..n2) to dst2) into LDS once every tag equals `tag`.  With `gain`, the
 // LDS copy is gain[k] * x[k] and *rs receives 1 / sqrt(mean(x^2) + eps), the
 // RMSNorm scale, applied to the row sums later.  Ends with a workgroup
-// barrier; returns false on every thread when the step is abandoned.
-__device__ bool poll(const Ctx& c, Smem& sm, int ph, const uint64_t* src, int n, uint32_t tag, float* dst,
-                     const float* gain, float* rs, const uint64_t* src2, int n2, float* dst2) {
+// barrier; returns false on every thread when the step is abandoned.  With
+// `split`, the LDS copy is the bf16 pair (hi, lo) with hi + lo = the value to
+// about 16 significant bits, stored per 8 values as hi[8] then lo[8] (the
+// same 32 bytes as 8 floats), for the bf16 dot-product path.
+__device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint64_t* src, int n, uint32_t tag, float* dst,
+                     const float* gain, float* rs, const uint64_t* src2, int n2, float* dst2, bool split = false) {
   const int tid = threadIdx.x;
   bool ok = !sm.abort_flag;
   float ss = 0.f;
@@ -185,7 +224,15 @@ __device__ bool poll(const Ctx& c, Smem& sm, int ph, const uint64_t* src, int n,
       const int i = base + e * kThreads + tid;
       if (i < n) {
         const float x = __uint_as_float((uint32_t)v[e]);
-        dst[i] = gain ? x * gv[e] : x;
+        const float y = gain ? x * gv[e] : x;
+        if (split) {  // bf16 halves y = hi + lo; 8 values per 32 bytes: hi[8] then lo[8]
+          uint16_t* d = reinterpret_cast<uint16_t*>(dst) + (i >> 3) * 16 + (i & 7);
+          const uint32_t hb = bf16_rne(y);
+          d[0] = (uint16_t)hb;
+          d[8] = (uint16_t)bf16_rne(y - __uint_as_float(hb << 16));
+        } else {
+          dst[i] = y;
+        }
         ss += x * x;
       }
     }
@@ -208,35 +255,56 @@ __device__ bool poll(const Ctx& c, Smem& sm, int ph, const uint64_t* src, int n,
   return true;
 }
 
-// ------------------------------------------------------------ phase geometry
-enum { kQKV = 0, kAttn = 1, kOproj = 2, kGateUp = 3, kDown = 4 };
+// Attention item of an A-role CU: kv head g, head group x (q heads j0 ..
+// j0 + gi - 1 of the group), split s.
+struct Item {
+  int g, x, s, j0, gi;
+};
+template <int G>
+__device__ __forceinline__ Item item_of(const Ctx& c) {
+  const int per = c.X * c.S;
+  Item it;
+  it.g = c.rank / per;
+  it.x = (c.rank % per) / c.S;
+  it.s = c.rank % c.S;
+  it.gi = G / c.X;
+  it.j0 = it.x * it.gi;
+  return it;
+}
 
-// A GEMV phase: units (one row, or a gate/up row pair) [0, nunits) of this
-// CU; unit u belongs to wave u % 8 and covers `rpu` rows of K values, read in
-// segments of 512.
+// ------------------------------------------------------------ role geometry
+// A GEMV role: units [0, nunits) of this CU; unit u belongs to wave u % 8 and
+// covers `rpu` rows of K values, read in segments of 512.
 struct Gemv {
   const uint16_t* a;  // first row of this CU's slice (gate rows for pairs)
   long delta;         // up rows - gate rows, in elements (pairs only)
-  int K, nseg, rpu, nunits, r0;
+  int K, nseg, rpu, nunits;
 };
 
-__device__ __forceinline__ Gemv gemv_of(const Ctx& c, int l, int kind) {
+__device__ __forceinline__ Gemv gemv_of(const Ctx& c, int l) {
   const AS4 PersistConst& a = *c.a;
   const AS4 LayerPtrs& L = ((const AS4 LayerPtrs*)a.layers)[l];
   Gemv g;
   g.delta = 0;
   g.rpu = 1;
-  switch (kind) {
-    case kQKV: g.r0 = c.q0; g.nunits = c.q1 - c.q0; g.K = a.H; g.a = L.wqkv; break;
-    case kOproj: g.r0 = c.h0; g.nunits = c.h1 - c.h0; g.K = a.nq * D; g.a = L.wo; break;
-    case kGateUp:
-      g.r0 = c.i0; g.nunits = c.i1 - c.i0; g.K = a.H; g.a = L.wg; g.delta = (long)(L.wu - L.wg); g.rpu = 2;
-      break;
-    default: g.r0 = c.h0; g.nunits = c.h1 - c.h0; g.K = a.I; g.a = L.wd; break;
+  g.nunits = c.r1 - c.r0;
+  switch (c.role) {
+    case kQKV: g.K = a.H; g.a = L.wqkv; break;
+    case kOproj: g.K = a.nq * D; g.a = L.wo; break;
+    case kGateUp: g.K = a.H; g.a = L.wg; g.delta = (long)(L.wu - L.wg); g.rpu = 2; break;
+    default: g.K = a.I; g.a = L.wd; break;
   }
-  g.a += (size_t)g.r0 * g.K;
+  g.a += (size_t)c.r0 * g.K;
   g.nseg = (g.K + kSeg - 1) / kSeg;
   return g;
+}
+
+// Whether this CU's GEMV role takes the whole-segment path (rows of 2, 4 or 6
+// full segments), which stages its input as bf16 halves.
+__device__ __forceinline__ bool whole_segments(const Ctx& c) {
+  const AS4 PersistConst& a = *c.a;
+  const int K = c.role == kOproj ? a.nq * D : c.role == kDown ? a.I : a.H;
+  return c.role != kAttn && K % kSeg == 0 && (K == 2 * kSeg || K == 4 * kSeg || K == 6 * kSeg);
 }
 
 // A wave's walk over its segments: unit u (= wave + 8 j), row-in-unit t, segment sg.
@@ -256,141 +324,305 @@ __device__ __forceinline__ void walk_next(const Gemv& g, Walk& w) {
   }
 }
 
-// Always inside this CU's rows (nunits >= 1): a wave without units, and the
-// tail of a row shorter than a whole segment, re-read valid data.
-__device__ __forceinline__ const uint16_t* seg_ptr(const Gemv& g, const Walk& w) {
-  const int lane = threadIdx.x & 63;
-  const int k = min(w.sg * kSeg + lane * 8, g.K - 8);
-  return g.a + (long)w.t * g.delta + (long)min(w.u, g.nunits - 1) * g.K + k;
-}
-
 // ----------------------------------------------------------------- registers
-// The phase's first batch (weight segments, or the K/V rows of the attention
-// item: K in R[0..3], V in R[4..7]) is loaded at ONE program point of the
-// phase loop; each phase only computes addresses.  Values defined on several
-// paths would be merged with register copies, and a copy waits for its load.
+// The slice loaded ahead (weight segments, or the K/V rows of the attention
+// item: K in the first half, V in the second) is loaded at ONE program point
+// of the layer loop; each role only computes addresses.  Values defined on
+// several paths would be merged with register copies, and a copy waits for
+// its load.
+template <int N>
 struct Regs {
-  u32x4 R[kBatch];
-};
-struct Addr {
-  const u32x4* p[kBatch];
+  u32x4 R[N];
 };
 
-__device__ __forceinline__ void load_regs(Regs& rg, const Addr& ad) {
-#pragma unroll
-  for (int i = 0; i < kBatch; ++i) rg.R[i] = __builtin_nontemporal_load(gl(ad.p[i]));
+// N loads of 16 bytes per lane from buffer records: slot i reads
+// base[i < N/2 ? 0 : 1] + voff + soff[i], where voff is the lane's part and
+// soff[i] is wave-uniform (a scalar register), so a batch costs one vector
+// register of addressing.  Every byte read lies inside its allocation: the
+// uniform offsets stay inside the matrix or cache block, and the lane part of
+// a row or position past the end lands in the allocations' tail padding.
+template <int N>
+struct Addr {
+  __amdgpu_buffer_rsrc_t rs[2];
+  int voff;
+  int soff[N];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
-// Addresses of the next 8 segments from walk position w (the last valid
-// segment repeats past the end, so every register is loaded).
-__device__ __forceinline__ void gemv_addr(Addr& ad, const Gemv& g, Walk w) {
+template <int N>
+__device__ __forceinline__ void load_regs(Regs<N>& rg, const Addr<N>& ad) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    rg.R[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.rs[i < N / 2 ? 0 : 1], ad.voff, ad.soff[i], 2 /* nt */));
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// The next N segments from walk position w (the last valid segment repeats
+// past the end, so every register is loaded).  A row's last segment may run
+// past K: those lanes read the next row or the padding, and the dot product
+// skips them.
+template <int N>
+__device__ __forceinline__ void gemv_addr(Addr<N>& ad, const Gemv& g, Walk w) {
+  ad.rs[0] = ad.rs[1] = rsrc_of(g.a);
+  ad.voff = (int)(threadIdx.x & 63) * 16;
   Walk last = w;
 #pragma unroll
-  for (int i = 0; i < kBatch; ++i) {
+  for (int i = 0; i < N; ++i) {
     if (walk_valid(g, w)) last = w;
-    ad.p[i] = reinterpret_cast<const u32x4*>(seg_ptr(g, last));
+    ad.soff[i] = (int)(((long)last.t * g.delta + (long)min(last.u, g.nunits - 1) * g.K + last.sg * kSeg) * 2);
     walk_next(g, w);
   }
 }
 
-// Attention batch b: positions p_begin + hw + 16 (b + i), i < 4, for the 16
-// half-waves hw (clamped into the split).
-__device__ __forceinline__ void kv_addr(Addr& ad, const float* Kg, const float* Vg, int p_begin, int p_end, int b) {
-  const int hw = threadIdx.x >> 5, sub = threadIdx.x & 31;
+// Attention batch b: positions p_begin + hw + 16 (b + i), i < N / 2, for the
+// 16 half-waves hw; K rows in [0, N/2), V in [N/2, N).  Positions past the
+// split are read (inside the cache block or its padding) and not used.
+template <int N>
+__device__ __forceinline__ void kv_addr(Addr<N>& ad, const float* Kg, const float* Vg, int p_begin, int b) {
+  ad.rs[0] = rsrc_of(Kg);
+  ad.rs[1] = rsrc_of(Vg);
+  ad.voff = (int)((threadIdx.x >> 5) & 1) * D * 4 + (int)(threadIdx.x & 31) * 16;
+  const int p0 = p_begin + 2 * wave_id();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = min(p_begin + hw + 16 * (b + i), p_end - 1);
-    ad.p[i] = reinterpret_cast<const u32x4*>(Kg + (size_t)p * D + sub * 4);
-    ad.p[4 + i] = reinterpret_cast<const u32x4*>(Vg + (size_t)p * D + sub * 4);
-  }
+  for (int i = 0; i < N / 2; ++i) ad.soff[i] = ad.soff[N / 2 + i] = (p0 + 16 * (b + i)) * D * 4;
 }
 
-// LM head: rows rb, rb + 8, ... (kBatch / HS rows of HS segments) of this
-// CU's vocabulary slice, clamped into it.
-template <int HS>
-__device__ __forceinline__ void lm_addr(Addr& ad, const uint16_t* E, int rb, int nrows) {
+// LM head: rows rb, rb + 8, ... (N / HS rows of HS segments) of this CU's
+// vocabulary slice E (first row), clamped into it.
+template <int N, int HS>
+__device__ __forceinline__ void lm_addr(Addr<N>& ad, const uint16_t* E, int rb, int nrows) {
+  ad.rs[0] = ad.rs[1] = rsrc_of(E);
+  ad.voff = (int)(threadIdx.x & 63) * 16;
 #pragma unroll
-  for (int i = 0; i < kBatch / HS; ++i) {
+  for (int i = 0; i < N / HS; ++i) {
     const int rr = min(rb + i * kWaves, nrows - 1);
 #pragma unroll
-    for (int sg = 0; sg < HS; ++sg)
-      ad.p[i * HS + sg] = reinterpret_cast<const u32x4*>(E + (size_t)rr * HS * kSeg + sg * kSeg);
+    for (int sg = 0; sg < HS; ++sg) ad.soff[i * HS + sg] = (rr * HS + sg) * kSeg * 2;
   }
 }
 
-__device__ __forceinline__ bool has_item(const Ctx& c) { return (int)blockIdx.x < c.a->nkv * c.S; }
+// K and V cache rows of (layer l, kv head g).
+__device__ __forceinline__ float* k_rows(const AS4 PersistConst& a, int l, int g) {
+  return a.Kc + ((size_t)l * a.nkv + g) * a.max_pos * D;
+}
+__device__ __forceinline__ float* v_rows(const AS4 PersistConst& a, int l, int g) {
+  return a.Vc + ((size_t)l * a.nkv + g) * a.max_pos * D;
+}
 
-// First-batch addresses of phase ph (ph == 5 L: the LM head).
+// The slice this CU loads ahead for layer l (l == L: its first LM-head rows).
 template <int HS>
-__device__ __forceinline__ Addr phase_addr(const Ctx& c, int ph) {
+__device__ __forceinline__ Addr<kFirst> ahead_addr(const Ctx& c, int l) {
   const AS4 PersistConst& a = *c.a;
-  const int l = ph / 5, kind = ph % 5, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  Addr ad;
+  const int wave = wave_id();
+  Addr<kFirst> ad;
   if (l >= a.L) {
-    lm_addr<HS>(ad, a.embed + (size_t)c.v0 * HS * kSeg + lane * 8, wave, c.v1 - c.v0);
-  } else if (kind == kAttn) {
-    if (!has_item(c)) {  // no item: same-address loads keep the registers defined
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) ad.p[i] = reinterpret_cast<const u32x4*>(a.Kc);
-    } else {
-      const int g = blockIdx.x / c.S, s = blockIdx.x % c.S;
-      const int p_begin = s * c.chunk, p_end = min(p_begin + c.chunk, c.pos + 1);
-      kv_addr(ad, a.Kc + ((size_t)l * a.nkv + g) * a.max_pos * D, a.Vc + ((size_t)l * a.nkv + g) * a.max_pos * D,
-              p_begin, p_end, 0);
-    }
+    lm_addr<kFirst, HS>(ad, a.embed + (size_t)c.v0 * HS * kSeg, wave, c.v1 - c.v0);
+  } else if (c.role == kAttn) {
+    const int g = c.rank / (c.X * c.S), s = c.rank % c.S;
+    kv_addr<kFirst>(ad, k_rows(a, l, g), v_rows(a, l, g), s * c.chunk, 0);
   } else {
-    const Gemv g = gemv_of(c, l, kind);
-    gemv_addr(ad, g, Walk{wave, 0, 0});
+    gemv_addr<kFirst>(ad, gemv_of(c, l), Walk{wave, 0, 0});
   }
   return ad;
 }
 
 // ------------------------------------------------------------------- phases
-// GEMV phase: this wave's units, the first batch from rg and further batches
-// through a local array; each finished row goes straight to its output word.
-__device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, int kind, const Regs& rg, float rs) {
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Dot of 8 bf16 weights with 8 inputs given as bf16 halves (hi + lo): eight
+// bf16 pair products accumulated in f32.
+__device__ __forceinline__ float dot8_split(u32x4 w, u32x4 hi, u32x4 lo, float acc) {
+// (the vector elements are converted to plain values before the bit cast: a
+// bit cast applied to an element expression itself reads element 0 here)
+#define QD_DOT2(a, b, c) \
+  __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, (uint32_t)(a)), __builtin_bit_cast(bf16x2_t, (uint32_t)(b)), c, false)
+  acc = QD_DOT2(w.x, hi.x, acc);
+  acc = QD_DOT2(w.x, lo.x, acc);
+  acc = QD_DOT2(w.y, hi.y, acc);
+  acc = QD_DOT2(w.y, lo.y, acc);
+  acc = QD_DOT2(w.z, hi.z, acc);
+  acc = QD_DOT2(w.z, lo.z, acc);
+  acc = QD_DOT2(w.w, hi.w, acc);
+  acc = QD_DOT2(w.w, lo.w, acc);
+#undef QD_DOT2
+  return acc;
+}
+
+// GEMV units held in the registers loaded ahead, for rows of exactly NSEG
+// whole segments (input staged as bf16 halves): the wave's NSEG input
+// fragments are read from LDS once, each valid unit's dot products run without
+// further branches, and the row sums of all units are finished together.
+// Returns the units per wave covered (kFirst / (RPU NSEG)).
+template <int RPU, int NSEG>
+__device__ __forceinline__ int gemv_ahead(const Ctx& c, Smem& sm, const Gemv& g, const Regs<kFirst>& rg,
+                                          const float* h, float rs, int l) {
+  const int ph = 5 * l + c.role;
+  constexpr int UPW = kFirst / (RPU * NSEG);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  u32x4 hh[NSEG], hl[NSEG];
+#pragma unroll
+  for (int sg = 0; sg < NSEG; ++sg) {
+    const u32x4* blk = reinterpret_cast<const u32x4*>(h + sg * kSeg + lane * 8);  // 32 bytes: hi[8], lo[8]
+    hh[sg] = blk[0];
+    hl[sg] = blk[1];
+  }
+  float p[UPW * RPU];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+#pragma unroll
+    for (int t = 0; t < RPU; ++t) p[j * RPU + t] = 0.f;
+    if (wave + kWaves * j < g.nunits) {  // wave-uniform
+#pragma unroll
+      for (int t = 0; t < RPU; ++t) {
+        float acc = 0.f;
+#pragma unroll
+        for (int sg = 0; sg < NSEG; ++sg) acc = dot8_split(rg.R[(j * RPU + t) * NSEG + sg], hh[sg], hl[sg], acc);
+        p[j * RPU + t] = acc;
+      }
+    }
+  }
+  stamp(c, sm, ph, 6, threadIdx.x == 0);
+  // Row sums through LDS: the wave writes its row partials [row][lane], then
+  // lanes 4r .. 4r + 3 add row r's 64 partials (16 each) and finish with two
+  // quad exchanges; one pass serves every row of the wave.  The attention
+  // scratch is free on CUs that run a GEMV role.
+  constexpr int NR = UPW * RPU;  // rows of the wave, at most 16
+  static_assert(NR <= 16, "one reduction pass covers 16 rows");
+  float* red = sm.att + wave * (16 * kRedStride);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) red[i * kRedStride + lane] = p[i];
+  const int row = lane >> 2;
+  float t = 0.f;
+  if (row < NR) {
+    const float* src = red + row * kRedStride + (lane & 3) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
+      t += (v.x + v.y) + (v.z + v.w);
+    }
+  }
+  t += DPPF(t, 0xB1, 0xF);  // quad_perm [1,0,3,2]
+  t += DPPF(t, 0x4E, 0xF);  // quad_perm [2,3,0,1]: every lane of the quad holds row `row`
+  t *= rs;
+  if (RPU == 1) {
+    const int u = wave + kWaves * row;
+    if ((lane & 3) == 0 && row < NR && u < g.nunits) sm.outv[u] = t;
+  } else {
+    // unit j: gate row 2j in lanes 8j .. 8j + 3, up row 2j + 1 in lanes 8j + 4 .. 8j + 7
+    const float gate = DPPF(t, 0x114, 0xF);  // row_shr:4
+    const int j = lane >> 3, u = wave + kWaves * j;
+    if ((lane & 7) == 4 && j < UPW && u < g.nunits)
+      sm.outv[u] = t * gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
+  }
+  return UPW;
+}
+
+// GEMV role: this wave's units, the slice loaded ahead first and any rest in
+// streamed batches; each finished row goes straight to its output word.
+__device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, float rs) {
   const AS4 PersistConst& a = *c.a;
   const AS4 LayerPtrs& Lw = ((const AS4 LayerPtrs*)a.layers)[l];
-  const int ph = 5 * l + kind, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const Gemv g = gemv_of(c, l, kind);
-  const float* h = sm.vec[ph & 1];
-  const float* xr = sm.xres[ph & 1];
+  const int lane = threadIdx.x & 63, wave = wave_id(), kind = c.role;
+  const Gemv g = gemv_of(c, l);
+  const float* h = sm.vec[l & 1];
+  const float* xr = sm.xres[l & 1];
   const uint32_t tag = tag_of(c.seq, l);
+  stamp(c, sm, 5 * l + kind, 4, threadIdx.x == 0);
   Walk w{wave, 0, 0};
   float acc = 0.f, first = 0.f;
-  auto consume = [&](const Regs& r) {
+  const bool split = whole_segments(c);  // the input is staged as bf16 halves
+  auto consume = [&](const auto& r, auto n) {
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
+    for (int i = 0; i < decltype(n)::value; ++i) {
       if (walk_valid(g, w)) {  // wave-uniform
         const int k = w.sg * kSeg + lane * 8;
-        if (k < g.K) acc += dot8(r.R[i], h + k);
+        if (split) {
+          const u32x4* blk = reinterpret_cast<const u32x4*>(h + k);
+          acc = dot8_split(r.R[i], blk[0], blk[1], acc);
+        } else if (k < g.K) {
+          acc += dot8(r.R[i], h + k);
+        }
         if (w.sg + 1 == g.nseg) {  // row finished
           const float t = wave_total(acc) * rs;
           acc = 0.f;
           if (w.t + 1 < g.rpu) {
             first = t;  // gate row of a pair
           } else if (lane == 0) {
-            const int r = g.r0 + w.u;
-            switch (kind) {
-              case kQKV: st_tagged(a.QKV + r, Lw.bqkv ? t + ld_f(Lw.bqkv + r) : t, tag); break;
-              case kOproj: st_tagged(a.X1 + r, xr[w.u] + t, tag); break;
-              case kGateUp: st_tagged(a.ACT + r, silu_f(first) * t, tag); break;
-              default: st_tagged(a.X0 + r, xr[w.u] + t, tag_of(c.seq, l + 1)); break;
-            }
+            sm.outv[w.u] = kind == kGateUp ? t * first * __builtin_amdgcn_rcpf(1.0f + __expf(-first)) : t;
           }
         }
         walk_next(g, w);
       }
     }
   };
-  consume(rg);
-  while (walk_valid(g, w)) {  // more than one batch
-    Addr ad;
-    gemv_addr(ad, g, w);
-    Regs r2;
-    load_regs(r2, ad);
-    consume(r2);
+  int upw = 0;  // units per wave taken by the whole-segment path
+  if (split) {
+    if (g.rpu == 1) {
+      switch (g.nseg) {
+        case 2: upw = gemv_ahead<1, 2>(c, sm, g, rg, h, rs, l); break;
+        case 4: upw = gemv_ahead<1, 4>(c, sm, g, rg, h, rs, l); break;
+        case 6: upw = gemv_ahead<1, 6>(c, sm, g, rg, h, rs, l); break;
+      }
+    } else {
+      switch (g.nseg) {
+        case 2: upw = gemv_ahead<2, 2>(c, sm, g, rg, h, rs, l); break;
+        case 4: upw = gemv_ahead<2, 4>(c, sm, g, rg, h, rs, l); break;
+        case 6: upw = gemv_ahead<2, 6>(c, sm, g, rg, h, rs, l); break;
+      }
+    }
   }
+  if (upw > 0)
+    w.u += kWaves * upw;  // the rest (if any) streams below
+  else
+    consume(rg, std::integral_constant<int, kFirst>{});
+  while (walk_valid(g, w)) {  // a slice larger than the registers loaded ahead
+    Addr<kBatch> ad;
+    gemv_addr<kBatch>(ad, g, w);
+    Regs<kBatch> r2;
+    load_regs(r2, ad);
+    consume(r2, std::integral_constant<int, kBatch>{});
+  }
+  stamp(c, sm, 5 * l + kind, 2, threadIdx.x == 0);
+  // Publish every unit at once, one word per thread, so a wave's stores cover
+  // whole cache lines (single-word stores spread over lines reach the pollers
+  // much later), and no wait on the memory counter follows them inside the
+  // dot products.
+  __syncthreads();
+  for (int u = threadIdx.x; u < g.nunits; u += kThreads) {
+    const int r = c.r0 + u;
+    const float t = sm.outv[u];
+    switch (kind) {
+      case kQKV: st_tagged(a.QKV + r, Lw.bqkv ? t + ld_f(Lw.bqkv + r) : t, tag); break;
+      case kOproj: st_tagged(a.X1 + r, xr[u] + t, tag); break;
+      case kGateUp: st_tagged(a.ACT + r, t, tag); break;
+      default: st_tagged(a.X0 + r, xr[u] + t, tag_of(c.seq, l + 1)); break;
+    }
+  }
+}
+
+// The attention item's per-lane constants that do not depend on the phase
+// input (RoPE row of the position, QK-norm gains): loaded before the input
+// poll, so their latency hides behind the handshake.
+struct AttnPre {
+  float ct, st, gq0, gq1, gk0, gk1;
+};
+__device__ __forceinline__ AttnPre attn_pre(const Ctx& c, int l) {
+  const AS4 PersistConst& a = *c.a;
+  const AS4 LayerPtrs& Lw = ((const AS4 LayerPtrs*)a.layers)[l];
+  const int lane = threadIdx.x & 63;
+  AttnPre p;
+  p.ct = ld_f(a.rope_cos + (size_t)c.pos * (D / 2) + lane);
+  p.st = ld_f(a.rope_sin + (size_t)c.pos * (D / 2) + lane);
+  p.gq0 = Lw.q_norm ? ld_f(Lw.q_norm + lane) : 1.f;
+  p.gq1 = Lw.q_norm ? ld_f(Lw.q_norm + lane + 64) : 1.f;
+  p.gk0 = Lw.k_norm ? ld_f(Lw.k_norm + lane) : 1.f;
+  p.gk1 = Lw.k_norm ? ld_f(Lw.k_norm + lane + 64) : 1.f;
+  return p;
 }
 
 // Attention item (kv head g, split s), part 1: QK-norm + RoPE of the q heads
@@ -398,42 +630,43 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, int ki
 // p_begin + hw + 16 i (hw = the 16 half-waves; a lane holds 4 of the 128
 // dims), the two half-waves merged, per-wave state into LDS.
 template <int G>
-__device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const Regs& rg) {
+__device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, const AttnPre& pre) {
   const AS4 PersistConst& a = *c.a;
   const AS4 LayerPtrs& Lw = ((const AS4 LayerPtrs*)a.layers)[l];
-  const int S = c.S, pos = c.pos, ctx = pos + 1;
-  const int g = blockIdx.x / S, s = blockIdx.x % S;
-  const int p_begin = s * c.chunk, p_end = min(p_begin + c.chunk, ctx);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, hw = threadIdx.x >> 5, sub = lane & 31;
-  float* Kg = a.Kc + ((size_t)l * a.nkv + g) * a.max_pos * D;
-  float* Vg = a.Vc + ((size_t)l * a.nkv + g) * a.max_pos * D;
+  const int pos = c.pos, ctx = pos + 1;
+  const Item it = item_of<G>(c);
+  const int g = it.g, gi = it.gi;
+  const int p_begin = it.s * c.chunk, p_end = min(p_begin + c.chunk, ctx);
+  const int wave = wave_id(), lane = threadIdx.x & 63, hw = threadIdx.x >> 5, sub = lane & 31;
+  float* Kg = k_rows(a, l, g);
+  float* Vg = v_rows(a, l, g);
   float* qk = sm.qk;
-  // QK-norm (optional) and RoPE; wave hd handles head hd (lane j: the pair (j, j + 64))
-  for (int hd = wave; hd < G + 1; hd += kWaves) {
-    float* v = qk + hd * D;
+  // QK-norm (optional) and RoPE of the item's q heads and k; wave hd handles
+  // one of them (lane j: the pair (j, j + 64))
+  for (int hd = wave; hd < gi + 1; hd += kWaves) {
+    float* v = qk + (hd < gi ? it.j0 + hd : G) * D;
     float x0 = v[lane], x1 = v[lane + 64];
-    const float* gain = hd < G ? Lw.q_norm : Lw.k_norm;
-    if (gain) {
+    if (Lw.q_norm) {  // QK-norm present (q and k gains together)
       const float r = rsqrtf(wave_total(x0 * x0 + x1 * x1) / (float)D + a.eps);
-      x0 = x0 * r * ld_f(gain + lane);
-      x1 = x1 * r * ld_f(gain + lane + 64);
+      x0 = x0 * r * (hd < gi ? pre.gq0 : pre.gk0);
+      x1 = x1 * r * (hd < gi ? pre.gq1 : pre.gk1);
     }
-    const float ct = ld_f(a.rope_cos + (size_t)pos * (D / 2) + lane);
-    const float st = ld_f(a.rope_sin + (size_t)pos * (D / 2) + lane);
-    v[lane] = x0 * ct - x1 * st;
-    v[lane + 64] = x1 * ct + x0 * st;
+    v[lane] = x0 * pre.ct - x1 * pre.st;
+    v[lane + 64] = x1 * pre.ct + x0 * pre.st;
   }
   __syncthreads();
+  stamp(c, sm, 5 * l + kAttn, 4, threadIdx.x == 0);
   const float* knew = qk + G * D;
   const float* vnew = qk + (G + 1) * D;
-  if (pos >= p_begin && pos < p_end && threadIdx.x < D) {  // this split holds the new position
+  if (it.x == 0 && pos >= p_begin && pos < p_end && threadIdx.x < D) {  // this split holds the new position
     st_f(Kg + (size_t)pos * D + threadIdx.x, knew[threadIdx.x]);
     st_f(Vg + (size_t)pos * D + threadIdx.x, vnew[threadIdx.x]);
   }
   const float scale = 1.0f / sqrtf((float)D);
-  f32x4 qv[G];
+  f32x4 qv[G];  // heads j < gi of the item
 #pragma unroll
-  for (int j = 0; j < G; ++j) qv[j] = *reinterpret_cast<const f32x4*>(qk + j * D + sub * 4);
+  for (int j = 0; j < G; ++j)
+    qv[j] = j < gi ? *reinterpret_cast<const f32x4*>(qk + (it.j0 + j) * D + sub * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
   float m[G], ls[G];
   f32x4 o[G];
 #pragma unroll
@@ -443,41 +676,68 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
     o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int wave_first = p_begin + 2 * wave;  // this wave's lower-half position in batch 0
-  auto consume = [&](const Regs& r, int b) {
+  // Positions in blocks of 4 per half-wave: the 4 G scores first (their
+  // cross-lane sums overlap), then one online-softmax update per head.
+  auto consume = [&](const auto& r, auto n, int b) {
+    constexpr int NP = decltype(n)::value / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (wave_first + 16 * (b + i) < p_end) {  // wave-uniform: the lower half has a position
-        const int p = p_begin + hw + 16 * (b + i);
-        const bool valid = p < p_end;
-        // the cache row of the new position was prefetched before it was written
-        const f32x4 kv = p == pos ? *reinterpret_cast<const f32x4*>(knew + sub * 4) : as_f4(r.R[i]);
-        const f32x4 vv = p == pos ? *reinterpret_cast<const f32x4*>(vnew + sub * 4) : as_f4(r.R[4 + i]);
+    for (int i0 = 0; i0 < NP; i0 += 4) {
+      if (wave_first + 16 * (b + i0) < p_end) {  // wave-uniform: the lower half has a position
+        float sc[4][G];
+        f32x4 vv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = i0 + q;
+          const int p = p_begin + hw + 16 * (b + i);
+          // the cache row of the new position was loaded before it was written;
+          // rows past the split were read but are not data (a zero weight
+          // times a stale NaN would still be NaN): their V is replaced by 0
+          const f32x4 kv = p == pos ? *reinterpret_cast<const f32x4*>(knew + sub * 4) : as_f4(r.R[i]);
+          vv[q] = p >= p_end ? f32x4{0.f, 0.f, 0.f, 0.f}
+                  : p == pos ? *reinterpret_cast<const f32x4*>(vnew + sub * 4)
+                             : as_f4(r.R[NP + i]);
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            if (j < gi) {  // wave-uniform
+              const float sd = qv[j].x * kv.x + qv[j].y * kv.y + qv[j].z * kv.z + qv[j].w * kv.w;
+              sc[q][j] = p < p_end ? half_total(sd) * scale : -INFINITY;
+            } else {
+              sc[q][j] = -INFINITY;
+            }
+          }
+        }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-          float sd = qv[j].x * kv.x + qv[j].y * kv.y + qv[j].z * kv.z + qv[j].w * kv.w;
-          sd = half_total(sd) * scale;
-          if (valid) {
-            const float mn = fmaxf(m[j], sd);
-            const float corr = __expf(m[j] - mn), pw = __expf(sd - mn);
-            ls[j] = ls[j] * corr + pw;
-            o[j] = o[j] * corr + vv * pw;
-            m[j] = mn;
+          const float mx = fmaxf(fmaxf(m[j], fmaxf(sc[0][j], sc[1][j])), fmaxf(sc[2][j], sc[3][j]));
+          if (mx != -INFINITY) {
+            const float corr = __expf(m[j] - mx);
+            ls[j] *= corr;
+            o[j] = o[j] * corr;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float pw = __expf(sc[q][j] - mx);
+              ls[j] += pw;
+              o[j] = o[j] + vv[q] * pw;
+            }
+            m[j] = mx;
           }
         }
       }
     }
   };
-  consume(rg, 0);
-  for (int b = 4; wave_first + b * 16 < p_end; b += 4) {
-    Addr ad;
-    kv_addr(ad, Kg, Vg, p_begin, p_end, b);
-    Regs r2;
+  consume(rg, std::integral_constant<int, kFirst>{}, 0);
+  for (int b = kFirst / 2; wave_first + b * 16 < p_end; b += kBatch / 2) {  // a split longer than the slice loaded ahead
+    Addr<kBatch> ad;
+    kv_addr<kBatch>(ad, Kg, Vg, p_begin, b);
+    Regs<kBatch> r2;
     load_regs(r2, ad);
-    consume(r2, b);
+    consume(r2, std::integral_constant<int, kBatch>{}, b);
   }
+  stamp(c, sm, 5 * l + kAttn, 6, threadIdx.x == 0);
   // merge the two half-waves of this wave, lower half first (same order in both halves)
 #pragma unroll
   for (int j = 0; j < G; ++j) {
+    if (j >= gi) break;  // wave-uniform
     const float m2 = __shfl_xor(m[j], 32, 64), l2 = __shfl_xor(ls[j], 32, 64);
     f32x4 o2;
     o2.x = __shfl_xor(o[j].x, 32, 64);
@@ -506,27 +766,37 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
 }
 
 // Attention item, part 2: combine the 8 wave states in a fixed order into this
-// split's partial (with one split, into the output); then the heads j with
-// j % S == s fold the S split partials in split order.
+// split's partial (with one split, into the output); then the item's heads j
+// with j % S == s fold the S split partials in split order.
 template <int G>
 __device__ __forceinline__ bool attn_finish(const Ctx& c, Smem& sm, int l) {
   const AS4 PersistConst& a = *c.a;
-  const int S = c.S, g = blockIdx.x / S, s = blockIdx.x % S;
+  const Item it = item_of<G>(c);
+  const int S = c.S, s = it.s, gi = it.gi, h0 = it.g * G + it.j0;  // h0: the item's first q head
   const uint32_t tag = tag_of(c.seq, l);
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  stamp(c, sm, 5 * l + kAttn, 7, threadIdx.x == 0);
+  for (int idx = threadIdx.x; idx < gi * D; idx += kThreads) {
     const int j = idx / D, dd = idx % D;
-    float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.att[(w * G + j) * kAttStride]);
-    float Ls = 0.f, acc = 0.f;
+    float mw[kWaves], lw[kWaves], ow[kWaves];
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float* e = sm.att + (w * G + j) * kAttStride;
-      if (e[0] == -INFINITY) continue;  // a wave without positions
-      const float f = __expf(e[0] - M);
-      Ls += e[1] * f;
-      acc += e[4 + dd] * f;
+      mw[w] = e[0];
+      lw[w] = e[1];
+      ow[w] = e[4 + dd];
     }
-    const int h = g * G + j;
+    float M = mw[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
+    float Ls = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {  // a wave without positions has m = -inf: weight 0
+      const float f = __expf(mw[w] - M);
+      Ls += lw[w] * f;
+      acc += ow[w] * f;
+    }
+    const int h = h0 + j;
     if (S == 1) {
       st_tagged(a.O + h * D + dd, acc / Ls, tag);
     } else {
@@ -539,13 +809,13 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, Smem& sm, int l) {
     }
   }
   if (S == 1) return true;
-  const int nmerge = s < G ? (G - 1 - s) / S + 1 : 0;
+  const int nmerge = s < gi ? (gi - 1 - s) / S + 1 : 0;
   bool ok = true;
   for (int t0 = 0; t0 < nmerge * D; t0 += kThreads) {
     const int t = t0 + threadIdx.x;
     const bool act = t < nmerge * D;
     const int j = s + (t / D) * S, dd = t % D;
-    const int h = g * G + (act ? j : 0);
+    const int h = h0 + (act ? j : 0);
     float M = -INFINITY, Ls = 0.f, acc = 0.f;
     for (int q0 = 0; q0 < S && ok; q0 += 8) {
       uint64_t em[8], el[8], eo[8];
@@ -593,50 +863,62 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, Smem& sm, int l) {
   return !sm.abort_flag;
 }
 
-// LM head: rows wave, wave + 8, ... of this CU's vocabulary slice (first batch
-// in rg), logits out, per-CU argmax (ties -> lowest id) as a tagged pair.
+// LM head: rows wave, wave + 8, ... of this CU's vocabulary slice, logits
+// out, per-CU argmax (ties -> lowest id) as a tagged pair.  The registers
+// loaded ahead hold three batches of kBatch segments (kBatch / HS rows per
+// wave each); each batch, once consumed, is reloaded with the rows three
+// batches on, so two batches stream while one is consumed.
 template <int HS>
-__device__ __forceinline__ void lmhead_phase(const Ctx& c, Smem& sm, Regs& rg, float rs) {
+__device__ __forceinline__ void lmhead_phase(const Ctx& c, Smem& sm, Regs<kFirst>& rg, float rs) {
+  static_assert(kFirst == 3 * kBatch, "three streamed batches");
   const AS4 PersistConst& a = *c.a;
-  constexpr int RB = kBatch / HS;  // rows per batch
-  const int v0 = c.v0, nrows = c.v1 - c.v0, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* h = sm.vec[(5 * a.L) & 1];
-  const uint16_t* E = a.embed + (size_t)v0 * HS * kSeg + lane * 8;
+  const int v0 = c.v0, nrows = c.v1 - c.v0, lane = threadIdx.x & 63, wave = wave_id();
+  const float* h = sm.vec[a.L & 1];
+  const __amdgpu_buffer_rsrc_t E = rsrc_of(a.embed + (size_t)v0 * HS * kSeg);  // this CU's first row
+  constexpr int RB = kBatch / HS;        // rows of a wave in one batch
+  constexpr int step = RB * kWaves;      // rows of one batch (all waves)
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  auto consume = [&](const Regs& src, int rb) {
+  auto run = [&](auto j, int rb) {  // batch j of the three: rows rb, rb + 8, ...
+    constexpr int o = decltype(j)::value * kBatch;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int rr = rb + i * kWaves;
       if (rr < nrows) {  // wave-uniform
         float acc = 0.f;
 #pragma unroll
-        for (int sg = 0; sg < HS; ++sg) acc += dot8(src.R[i * HS + sg], h + sg * kSeg + lane * 8);
+        for (int sg = 0; sg < HS; ++sg) acc += dot8(rg.R[o + i * HS + sg], h + sg * kSeg + lane * 8);
         const float t = wave_total(acc) * rs;
-        if (lane == 0) st_f(a.logits + v0 + rr, t);
+        if (lane == 0) sm.outv[rr] = t;
         if (t > best) {  // a wave's rows increase: ties keep the lowest id
           best = t;
           bi = v0 + rr;
         }
       }
     }
+    const int rn = rb + 3 * step;
+    if (rn < nrows) {  // wave-uniform: reload this batch with the rows three batches on
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int rr = min(rn + i * kWaves, nrows - 1);
+#pragma unroll
+        for (int sg = 0; sg < HS; ++sg)
+          rg.R[o + i * HS + sg] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(E, lane * 16, (rr * HS + sg) * kSeg * 2, 2 /* nt */));
+      }
+    }
   };
-  constexpr int step = RB * kWaves;
-  Regs r2;
-  Addr ad;
-  for (int rb = wave; rb < nrows; rb += 2 * step) {
-    lm_addr<HS>(ad, E, rb + step, nrows);
-    load_regs(r2, ad);
-    consume(rg, rb);
-    lm_addr<HS>(ad, E, rb + 2 * step, nrows);
-    load_regs(rg, ad);
-    consume(r2, rb + step);
+  for (int rb = wave; rb < nrows; rb += 3 * step) {
+    run(std::integral_constant<int, 0>{}, rb);
+    run(std::integral_constant<int, 1>{}, rb + step);
+    run(std::integral_constant<int, 2>{}, rb + 2 * step);
   }
   if (lane == 0) {
     sm.red[32 + wave] = best;
     sm.red[40 + wave] = __int_as_float(bi);
   }
   __syncthreads();
+  for (int rr = threadIdx.x; rr < nrows; rr += kThreads) st_f(a.logits + v0 + rr, sm.outv[rr]);
   if (threadIdx.x == 0) {
     float v = sm.red[32];
     int j = __float_as_int(sm.red[40]);
@@ -657,12 +939,12 @@ __device__ __forceinline__ void lmhead_phase(const Ctx& c, Smem& sm, Regs& rg, f
 // total order, so the scan order does not matter.  Advances the step state.
 __device__ __forceinline__ void final_phase(const Ctx& c, Smem& sm) {
   const AS4 PersistConst& a = *c.a;
-  const int n = gridDim.x, ph = 5 * a.L + 1;
-  float* vals = sm.vec[ph & 1];
+  const int n = gridDim.x, ph = 5 * a.L + 1, slot = a.L + 1;  // the LM head used slot L
+  float* vals = sm.vec[slot & 1];
   float rs;
-  stamp(c, ph, 0, threadIdx.x == 0);
-  if (!poll(c, sm, ph, a.AM, 2 * n, tag_of(c.seq, 255), vals, nullptr, &rs, nullptr, 0, nullptr)) return;
-  stamp(c, ph, 1, threadIdx.x == 0);
+  stamp(c, sm, ph, 0, threadIdx.x == 0);
+  if (!poll(c, sm, slot, a.AM, 2 * n, tag_of(c.seq, 255), vals, nullptr, &rs, nullptr, 0, nullptr)) return;
+  stamp(c, sm, ph, 1, threadIdx.x == 0);
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   float v = -INFINITY;
@@ -691,46 +973,68 @@ __device__ __forceinline__ void final_phase(const Ctx& c, Smem& sm) {
     st->pos = c.pos + 1;
     st->step += 1;
   }
-  stamp(c, ph, 5, lane == 0);
+  stamp(c, sm, ph, 5, lane == 0);
 }
 
 template <int G, int HS>
-__global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const PersistConst* __restrict__ pc, int pos,
-                                                                   uint32_t seq, int S, int chunk) {
+__global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const PersistConst* __restrict__ pc,
+                                                                   PersistStep stp) {
   extern __shared__ __align__(16) char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   if (threadIdx.x == 0) sm.abort_flag = 0;
+  if (pc->trace)
+    for (int i = threadIdx.x; i < (kTraceL + 2) * 8; i += kThreads) sm.ts[i / 8][i % 8] = 0;
   const AS4 PersistConst* ap = (const AS4 PersistConst*)pc;
   const AS4 PersistConst& a = *ap;
-  Ctx c{ap, pos, S, chunk, seq, __builtin_amdgcn_s_memrealtime()};
-  cu_rows(a.nqkv, c.q0, c.q1);
-  cu_rows(a.H, c.h0, c.h1);
-  cu_rows(a.I, c.i0, c.i1);
-  cu_rows(a.V, c.v0, c.v1);
-  stamp(c, 0, 7, threadIdx.x == 0);
+  Ctx c;
+  c.a = ap;
+  c.pos = stp.pos;
+  c.S = stp.S;
+  c.chunk = stp.chunk;
+  c.X = stp.X;
+  c.seq = stp.seq;
+  c.t0 = __builtin_amdgcn_s_memrealtime();
+  int role = 0;
+  while (role < 4 && (int)blockIdx.x >= stp.start[role + 1]) ++role;
+  c.role = role;
+  c.rank = (int)blockIdx.x - stp.start[role];
+  c.nrole = stp.start[role + 1] - stp.start[role];
+  const int N = role == kQKV ? a.nqkv : role == kGateUp ? a.I : role == kAttn ? c.nrole : a.H;
+  c.r0 = (int)(((uint32_t)N * c.rank) / c.nrole);
+  c.r1 = (int)(((uint32_t)N * (c.rank + 1)) / c.nrole);
+  c.v0 = (int)(((uint32_t)a.V * blockIdx.x) / gridDim.x);
+  c.v1 = (int)(((uint32_t)a.V * (blockIdx.x + 1)) / gridDim.x);
   const int L = a.L, H = a.H, tid = threadIdx.x;
   const uint16_t* emb = a.embed + (size_t)gl(a.st)->token * H;
-  Regs rg;
-  load_regs(rg, phase_addr<HS>(c, 0));
+  Regs<kFirst> rg;
+  load_regs(rg, ahead_addr<HS>(c, 0));
   __syncthreads();
-  for (int ph = 0; ph < 5 * L; ++ph) {
-    const int l = ph / 5, kind = ph % 5;
+  for (int l = 0; l < L; ++l) {
+    const int ph = 5 * l + role;
     const AS4 LayerPtrs& Lw = ((const AS4 LayerPtrs*)a.layers)[l];
-    const uint32_t tag = tag_of(seq, l);
-    float* vin = sm.vec[ph & 1];
-    float* xr = sm.xres[ph & 1];
+    const uint32_t tag = tag_of(c.seq, l);
+    float* vin = sm.vec[l & 1];
+    float* xr = sm.xres[l & 1];
     float rs = 1.0f;
-    const bool item = kind != kAttn || has_item(c);
-    stamp(c, ph, 0, tid == 0);
+    stamp(c, sm, ph, 0, tid == 0);
+    AttnPre pre{};
+    if (role == kAttn) pre = attn_pre(c, l);
     // ---- the phase input
     bool ok = true;
-    if (!item) {
-      __syncthreads();  // keeps the workgroup barrier sequence of the other CUs
-    } else if (l == 0 && kind == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
+    if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
       float ss = 0.f;
+      const bool split = whole_segments(c);
       for (int k = tid; k < H; k += kThreads) {
         const float x = bf16_to_f(*gl(emb + k));
-        vin[k] = x * ld_f(Lw.attn_norm + k);
+        const float y = x * ld_f(Lw.attn_norm + k);
+        if (split) {
+          uint16_t* d = reinterpret_cast<uint16_t*>(vin) + (k >> 3) * 16 + (k & 7);
+          const uint32_t hb = bf16_rne(y);
+          d[0] = (uint16_t)hb;
+          d[8] = (uint16_t)bf16_rne(y - __uint_as_float(hb << 16));
+        } else {
+          vin[k] = y;
+        }
         ss += x * x;
       }
       const float wsum = wave_total(ss);
@@ -746,51 +1050,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
       const float* gain = nullptr;
       int n, n2 = 0;
       float* dst = vin;
-      switch (kind) {
+      switch (role) {
         case kQKV: src = a.X0; n = H; gain = Lw.attn_norm; break;
-        case kAttn: src = a.QKV + (size_t)(blockIdx.x / S) * (G + 2) * D; n = (G + 2) * D; dst = sm.qk; break;
+        case kAttn: src = a.QKV + (size_t)(c.rank / (c.X * c.S)) * (G + 2) * D; n = (G + 2) * D; dst = sm.qk; break;
         case kOproj:
           src = a.O;
           n = a.nq * D;
           if (l == 0) {
-            for (int r = tid; r < c.h1 - c.h0; r += kThreads) xr[r] = bf16_to_f(*gl(emb + c.h0 + r));
+            for (int r = tid; r < c.r1 - c.r0; r += kThreads) xr[r] = bf16_to_f(*gl(emb + c.r0 + r));
           } else {
-            src2 = a.X0 + c.h0;
-            n2 = c.h1 - c.h0;
+            src2 = a.X0 + c.r0;
+            n2 = c.r1 - c.r0;
           }
           break;
         case kGateUp: src = a.X1; n = H; gain = Lw.mlp_norm; break;
-        default: src = a.ACT; n = a.I; src2 = a.X1 + c.h0; n2 = c.h1 - c.h0; break;
+        default: src = a.ACT; n = a.I; src2 = a.X1 + c.r0; n2 = c.r1 - c.r0; break;
       }
-      ok = poll(c, sm, ph, src, n, tag, dst, gain, &rs, src2, n2, xr);
+      ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, whole_segments(c));
     }
     if (!ok) return;
-    stamp(c, ph, 1, tid == 0);
-    // ---- compute from the registers loaded at the end of the previous phase
-    if (kind == kAttn) {
-      if (item) attn_phase<G>(c, sm, l, rg);
+    stamp(c, sm, ph, 1, tid == 0);
+    // ---- compute from the registers loaded a layer ahead
+    if (role == kAttn) {
+      attn_phase<G>(c, sm, l, rg, pre);
+      stamp(c, sm, ph, 2, tid == 0);
+      if (!attn_finish<G>(c, sm, l)) return;
     } else {
-      gemv_phase(c, sm, l, kind, rg, rs);
+      gemv_phase(c, sm, l, rg, rs);
     }
-    stamp(c, ph, 3, tid == 0);
-    // the single load site: the next phase's first batch flies during the handshake
-    load_regs(rg, phase_addr<HS>(c, ph + 1));
-    if (kind == kAttn && item && !attn_finish<G>(c, sm, l)) return;
-    stamp(c, ph, 5, tid == 0);
+    stamp(c, sm, ph, 3, tid == 0);
+    // the single load site: the next layer's slice (after the last layer, the
+    // first LM-head rows) streams while the other roles take their phases
+    load_regs(rg, ahead_addr<HS>(c, l + 1));
+    stamp(c, sm, ph, 5, tid == 0);
   }
-  // ---- final norm + LM head
+  // ---- final norm + LM head (every CU)
   {
     const int ph = 5 * L;
     float rs;
-    stamp(c, ph, 0, tid == 0);
-    if (!poll(c, sm, ph, a.X0, H, tag_of(seq, L), sm.vec[ph & 1], a.final_norm, &rs, nullptr, 0, nullptr)) return;
-    stamp(c, ph, 1, tid == 0);
+    stamp(c, sm, ph, 0, tid == 0);
+    if (!poll(c, sm, L, a.X0, H, tag_of(c.seq, L), sm.vec[L & 1], a.final_norm, &rs, nullptr, 0, nullptr)) return;
+    stamp(c, sm, ph, 1, tid == 0);
     if (blockIdx.x == 0 && a.xf_out)
-      for (int k = tid; k < H; k += kThreads) st_f(a.xf_out + k, sm.vec[ph & 1][k] * rs);
+      for (int k = tid; k < H; k += kThreads) st_f(a.xf_out + k, sm.vec[L & 1][k] * rs);
     lmhead_phase<HS>(c, sm, rg, rs);
-    stamp(c, ph, 5, tid == 0);
+    stamp(c, sm, ph, 5, tid == 0);
   }
   if (blockIdx.x == 0) final_phase(c, sm);
+  if (a.trace) {
+    __syncthreads();
+    trace_flush(c, sm);
+  }
 }
 
 template <int G, int HS>
@@ -817,6 +1127,9 @@ void* pick(int G, int hseg) {
   return nullptr;
 }
 
+// Segments one wave of a CU with `units` units (rpu rows of nseg segments) loads.
+int wave_segs(int units, int rpu, int nseg) { return (units + kWaves - 1) / kWaves * rpu * nseg; }
+
 }  // namespace
 
 size_t persist_smem_bytes() { return sizeof(Smem); }
@@ -828,11 +1141,93 @@ int persist_prepare(int G, int hseg) {
   return e == hipSuccess ? 0 : (int)e;
 }
 
-int persist_launch(const PersistConst* dev_const, int G, int hseg, int grid, int pos, uint32_t seq, int S, int chunk,
-                   hipStream_t s) {
+int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, PersistStep* out) {
+  if (grid < 1 || pos < 0 || pos >= pc.max_pos || pc.nkv < 1) return -1;
+  const int ctx = pos + 1;
+  // attention: splits no longer than the K/V rows a CU loads ahead, on at most half the grid
+  const int smax = grid / (2 * pc.nkv);
+  if (smax < 1) return -1;
+  const int span = kFirst / 2 * 16;  // positions in the slice loaded ahead
+  int S = std::min((ctx + span - 1) / span, smax);
+  const int chunk = (ctx + S - 1) / S;
+  S = (ctx + chunk - 1) / chunk;  // every split holds at least one position
+  // short contexts: one item per q head (X = G head groups) instead of one per
+  // kv head, which halves (or better) the serial work of an item; each group
+  // reads the kv head's rows again, which is cheap while they are few
+  const int G = pc.nq / pc.nkv;
+  const int X = (S == 1 && pc.nkv * G <= grid / 4) ? G : 1;
+  const int R = grid - pc.nkv * X * S;
+  // the GEMV roles: Q rows, O rows, gate/up row pairs, D rows
+  const int N[4] = {pc.nqkv, pc.H, pc.I, pc.H};
+  const int rpu[4] = {1, 1, 2, 1};
+  const int ns[4] = {(pc.H + kSeg - 1) / kSeg, (pc.nq * D + kSeg - 1) / kSeg, (pc.H + kSeg - 1) / kSeg,
+                     (pc.I + kSeg - 1) / kSeg};
+  int lo[4];
+  for (int r = 0; r < 4; ++r) lo[r] = 1;
+  lo[1] = (pc.H + kResMax - 1) / kResMax;  // residual rows of a CU fit its LDS slot
+  lo[3] = lo[1];
+  for (int r = 0; r < 4; ++r) lo[r] = std::max(lo[r], (N[r] + kOutMax - 1) / kOutMax);  // outputs fit too
+  if ((pc.V + grid - 1) / grid > kOutMax) return -1;
+  int lo_sum = 0, tmax = 0;
+  for (int r = 0; r < 4; ++r) {
+    if (N[r] < lo[r]) return -1;
+    lo_sum += lo[r];
+    tmax = std::max(tmax, wave_segs((N[r] + lo[r] - 1) / lo[r], rpu[r], ns[r]));
+  }
+  if (lo_sum > R) return -1;
+  // the smallest per-wave slice every role can meet with R CUs, then the
+  // spare CUs to the roles with the most segments per CU
+  int n[4] = {lo[0], lo[1], lo[2], lo[3]};
+  for (int T = 1; T <= tmax; ++T) {
+    int m[4], sum = 0;
+    bool fits = true;
+    for (int r = 0; r < 4 && fits; ++r) {
+      const int per = T / (rpu[r] * ns[r]);  // units per wave
+      if (per == 0) {
+        fits = false;
+        break;
+      }
+      m[r] = std::min(N[r], std::max(lo[r], (N[r] + kWaves * per - 1) / (kWaves * per)));
+      sum += m[r];
+    }
+    if (fits && sum <= R) {
+      for (int r = 0; r < 4; ++r) n[r] = m[r];
+      break;
+    }
+  }
+  for (int sum = n[0] + n[1] + n[2] + n[3]; sum < R; ++sum) {
+    int best = -1;
+    double bw = -1.0;
+    for (int r = 0; r < 4; ++r) {
+      if (n[r] >= N[r]) continue;
+      const double w = (double)N[r] * rpu[r] * ns[r] / n[r];
+      if (w > bw) {
+        bw = w;
+        best = r;
+      }
+    }
+    if (best < 0) break;
+    ++n[best];
+  }
+  out->pos = pos;
+  out->seq = seq;
+  out->S = S;
+  out->chunk = chunk;
+  out->X = X;
+  out->start[0] = 0;
+  out->start[1] = n[0];
+  out->start[2] = n[0] + pc.nkv * X * S;
+  out->start[3] = out->start[2] + n[1];
+  out->start[4] = out->start[3] + n[2];
+  out->start[5] = out->start[4] + n[3];
+  return out->start[5] == grid ? 0 : -1;  // every CU has a role
+}
+
+int persist_launch(const PersistConst* dev_const, int G, int hseg, int grid, const PersistStep& st, hipStream_t s) {
   void* fn = pick(G, hseg);
   if (!fn) return -1;
-  void* args[] = {(void*)&dev_const, (void*)&pos, (void*)&seq, (void*)&S, (void*)&chunk};
+  PersistStep arg = st;
+  void* args[] = {(void*)&dev_const, (void*)&arg};
   hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, sizeof(Smem), s);
   return e == hipSuccess ? 0 : (int)e;
 }
