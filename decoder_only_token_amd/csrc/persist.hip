@@ -136,6 +136,7 @@ enum { kQKV = 0, kAttn = 1, kOproj = 2, kGateUp = 3, kDown = 4 };
 struct Ctx {
   const AS4 PersistConst* a;
   int pos, S, chunk, X;  // X: head groups per kv head (attention items = nkv X S)
+  float eps;
   uint32_t seq;
   uint64_t t0;
   int role, rank, nrole;  // this CU's role, its index among the CUs of the role, their number
@@ -216,7 +217,6 @@ __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint6
         ok = false;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
     }
     if (!ok) break;
 #pragma unroll
@@ -250,7 +250,7 @@ __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint6
     float t = 0.f;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) t += red[i];
-    *rs = rsqrtf(t / (float)n + c.a->eps);
+    *rs = rsqrtf(t / (float)n + c.eps);
   }
   return true;
 }
@@ -524,11 +524,10 @@ __device__ __forceinline__ int gemv_ahead(const Ctx& c, Smem& sm, const Gemv& g,
 
 // GEMV role: this wave's units, the slice loaded ahead first and any rest in
 // streamed batches; each finished row goes straight to its output word.
-__device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, float rs) {
+__device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, float rs,
+                                           const Gemv& g, const float* bias) {
   const AS4 PersistConst& a = *c.a;
-  const AS4 LayerPtrs& Lw = ((const AS4 LayerPtrs*)a.layers)[l];
   const int lane = threadIdx.x & 63, wave = wave_id(), kind = c.role;
-  const Gemv g = gemv_of(c, l);
   const float* h = sm.vec[l & 1];
   const float* xr = sm.xres[l & 1];
   const uint32_t tag = tag_of(c.seq, l);
@@ -597,7 +596,7 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
     const int r = c.r0 + u;
     const float t = sm.outv[u];
     switch (kind) {
-      case kQKV: st_tagged(a.QKV + r, Lw.bqkv ? t + ld_f(Lw.bqkv + r) : t, tag); break;
+      case kQKV: st_tagged(a.QKV + r, bias ? t + ld_f(bias + r) : t, tag); break;
       case kOproj: st_tagged(a.X1 + r, xr[u] + t, tag); break;
       case kGateUp: st_tagged(a.ACT + r, t, tag); break;
       default: st_tagged(a.X0 + r, xr[u] + t, tag_of(c.seq, l + 1)); break;
@@ -992,6 +991,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   c.S = stp.S;
   c.chunk = stp.chunk;
   c.X = stp.X;
+  c.eps = a.eps;
   c.seq = stp.seq;
   c.t0 = __builtin_amdgcn_s_memrealtime();
   int role = 0;
@@ -1017,8 +1017,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
     float* xr = sm.xres[l & 1];
     float rs = 1.0f;
     stamp(c, sm, ph, 0, tid == 0);
+    // everything the phase needs that does not depend on its input is read
+    // before the input poll, so its latency hides behind the handshake
     AttnPre pre{};
-    if (role == kAttn) pre = attn_pre(c, l);
+    Gemv gv{};
+    const float* bias = nullptr;
+    if (role == kAttn) {
+      pre = attn_pre(c, l);
+    } else {
+      gv = gemv_of(c, l);
+      if (role == kQKV) bias = Lw.bqkv;
+    }
     // ---- the phase input
     bool ok = true;
     if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
@@ -1076,7 +1085,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
       stamp(c, sm, ph, 2, tid == 0);
       if (!attn_finish<G>(c, sm, l)) return;
     } else {
-      gemv_phase(c, sm, l, rg, rs);
+      gemv_phase(c, sm, l, rg, rs, gv, bias);
     }
     stamp(c, sm, ph, 3, tid == 0);
     // the single load site: the next layer's slice (after the last layer, the
