@@ -379,17 +379,25 @@ __device__ __forceinline__ void gemv_addr(Addr<N>& ad, const Gemv& g, Walk w) {
   }
 }
 
-// Attention batch b: positions p_begin + hw + 16 (b + i), i < N / 2, for the
-// 16 half-waves hw; K rows in [0, N/2), V in [N/2, N).  Positions past the
+// Attention steps t0 .. t0 + N/8 - 1: lane q8 of group pg reads dims
+// 32 k + 4 q8 .. + 3 (k < 4) of position p_begin + 64 t + 8 wave + pg; K
+// fragment k of step t in slot 4 t + k, V in N/2 + 4 t + k.  Positions past the
 // split are read (inside the cache block or its padding) and not used.
 template <int N>
-__device__ __forceinline__ void kv_addr(Addr<N>& ad, const float* Kg, const float* Vg, int p_begin, int b) {
+__device__ __forceinline__ void kv_addr(Addr<N>& ad, const float* Kg, const float* Vg, int p_begin, int t0) {
   ad.rs[0] = rsrc_of(Kg);
   ad.rs[1] = rsrc_of(Vg);
-  ad.voff = (int)((threadIdx.x >> 5) & 1) * D * 4 + (int)(threadIdx.x & 31) * 16;
-  const int p0 = p_begin + 2 * wave_id();
+  ad.voff = (int)((threadIdx.x & 63) >> 3) * D * 4 + (int)(threadIdx.x & 7) * 16;
+  const int p0 = p_begin + 8 * wave_id();
 #pragma unroll
-  for (int i = 0; i < N / 2; ++i) ad.soff[i] = ad.soff[N / 2 + i] = (p0 + 16 * (b + i)) * D * 4;
+  for (int t = 0; t < N / 8; ++t) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int off = (p0 + 64 * (t0 + t)) * D * 4 + k * 128;
+      ad.soff[4 * t + k] = off;
+      ad.soff[N / 2 + 4 * t + k] = off;
+    }
+  }
 }
 
 // LM head: rows rb, rb + 8, ... (N / HS rows of HS segments) of this CU's
@@ -624,10 +632,68 @@ __device__ __forceinline__ AttnPre attn_pre(const Ctx& c, int l) {
   return p;
 }
 
-// Attention item (kv head g, split s), part 1: QK-norm + RoPE of the q heads
-// and k in LDS, the new cache row, then online softmax over positions
-// p_begin + hw + 16 i (hw = the 16 half-waves; a lane holds 4 of the 128
-// dims), the two half-waves merged, per-wave state into LDS.
+// Sum over the 8 lanes of this lane's group (lanes 8 i .. 8 i + 7), in every
+// lane of the group; the two halves add in mirrored order, which is exact.
+__device__ __forceinline__ float group8_sum(float v) {
+  v += DPPF(v, 0xB1, 0xF);   // quad_perm [1,0,3,2]
+  v += DPPF(v, 0x4E, 0xF);   // quad_perm [2,3,0,1]
+  v += DPPF(v, 0x141, 0xF);  // row_half_mirror
+  return v;
+}
+
+// The values of lanes i and i ^ d as (lower lane's, upper lane's), the same
+// pair in both lanes: d = 8 by a DPP rotation within rows of 16; d = 16 and
+// 32 by the gfx950 row swaps, whose two results are already in that order.
+template <int d>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  if (d == 8) {
+    const float p = DPPF(v, 0x128, 0xF);  // row_ror:8
+    const bool low = (threadIdx.x & 8) == 0;
+    lo = low ? v : p;
+    hi = low ? p : v;
+  } else {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = d == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  }
+}
+
+// Merge this lane's online-softmax state {m, l, o} with lane i ^ d's (equal
+// result in both lanes: the lower lane's state goes first).
+template <int d>
+__device__ __forceinline__ void merge_xor(float& m, float& ls, f32x4 (&o)[4]) {
+  float ma, mb, la, lb;
+  lane_pair<d>(m, ma, mb);
+  lane_pair<d>(ls, la, lb);
+  float oa[16], ob[16];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    lane_pair<d>(o[k].x, oa[4 * k + 0], ob[4 * k + 0]);
+    lane_pair<d>(o[k].y, oa[4 * k + 1], ob[4 * k + 1]);
+    lane_pair<d>(o[k].z, oa[4 * k + 2], ob[4 * k + 2]);
+    lane_pair<d>(o[k].w, oa[4 * k + 3], ob[4 * k + 3]);
+  }
+  const float M = fmaxf(ma, mb);
+  if (M != -INFINITY) {
+    const float fa = __expf(ma - M), fb = __expf(mb - M);
+    ls = la * fa + lb * fb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = f32x4{oa[4 * k] * fa + ob[4 * k] * fb, oa[4 * k + 1] * fa + ob[4 * k + 1] * fb,
+                   oa[4 * k + 2] * fa + ob[4 * k + 2] * fb, oa[4 * k + 3] * fa + ob[4 * k + 3] * fb};
+    m = M;
+  }
+}
+
+// Attention item (kv head g, head group, split s), part 1: QK-norm + RoPE of
+// the item's q heads and k in LDS, the new cache row, then per head an online
+// softmax over the split's positions.  A wave covers 8 positions at a time,
+// 8 lanes each: lane q8 of group pg holds dims 32 k + 4 q8 .. + 3 (k < 4) of
+// position p_begin + 64 t + 8 wave + pg at step t, so one 8-lane sum gives a
+// score.  The 8 group states of a wave are merged in a butterfly and written
+// to LDS per head.
 template <int G>
 __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, const AttnPre& pre) {
   const AS4 PersistConst& a = *c.a;
@@ -636,7 +702,7 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
   const Item it = item_of<G>(c);
   const int g = it.g, gi = it.gi;
   const int p_begin = it.s * c.chunk, p_end = min(p_begin + c.chunk, ctx);
-  const int wave = wave_id(), lane = threadIdx.x & 63, hw = threadIdx.x >> 5, sub = lane & 31;
+  const int wave = wave_id(), lane = threadIdx.x & 63, pg = lane >> 3, q8 = lane & 7;
   float* Kg = k_rows(a, l, g);
   float* Vg = v_rows(a, l, g);
   float* qk = sm.qk;
@@ -662,103 +728,79 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
     st_f(Vg + (size_t)pos * D + threadIdx.x, vnew[threadIdx.x]);
   }
   const float scale = 1.0f / sqrtf((float)D);
-  f32x4 qv[G];  // heads j < gi of the item
+  const int pw = p_begin + 8 * wave + pg;  // this lane's position at step 0
+  for (int j = 0; j < gi; ++j) {  // the item's heads, one at a time (wave-uniform)
+    f32x4 q[4];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
-    qv[j] = j < gi ? *reinterpret_cast<const f32x4*>(qk + (it.j0 + j) * D + sub * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[G], ls[G];
-  f32x4 o[G];
+    for (int k = 0; k < 4; ++k) q[k] = *reinterpret_cast<const f32x4*>(qk + (it.j0 + j) * D + 32 * k + 4 * q8);
+    float m = -INFINITY, ls = 0.f;
+    f32x4 o[4] = {};
+    // steps t0 .. t0 + N/8 - 1 from registers r (K fragments in [0, N/2), V in [N/2, N))
+    auto consume = [&](const auto& r, auto n, int t0) {
+      constexpr int N = decltype(n)::value, NT = N / 8;
+      float sc[NT];
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = -INFINITY;
-    ls[j] = 0.f;
-    o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int wave_first = p_begin + 2 * wave;  // this wave's lower-half position in batch 0
-  // Positions in blocks of 4 per half-wave: the 4 G scores first (their
-  // cross-lane sums overlap), then one online-softmax update per head.
-  auto consume = [&](const auto& r, auto n, int b) {
-    constexpr int NP = decltype(n)::value / 2;
+      for (int t = 0; t < NT; ++t) {
+        const int p = pw + 64 * (t0 + t);
+        float sd = 0.f;
 #pragma unroll
-    for (int i0 = 0; i0 < NP; i0 += 4) {
-      if (wave_first + 16 * (b + i0) < p_end) {  // wave-uniform: the lower half has a position
-        float sc[4][G];
-        f32x4 vv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = i0 + q;
-          const int p = p_begin + hw + 16 * (b + i);
-          // the cache row of the new position was loaded before it was written;
-          // rows past the split were read but are not data (a zero weight
-          // times a stale NaN would still be NaN): their V is replaced by 0
-          const f32x4 kv = p == pos ? *reinterpret_cast<const f32x4*>(knew + sub * 4) : as_f4(r.R[i]);
-          vv[q] = p >= p_end ? f32x4{0.f, 0.f, 0.f, 0.f}
-                  : p == pos ? *reinterpret_cast<const f32x4*>(vnew + sub * 4)
-                             : as_f4(r.R[NP + i]);
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            if (j < gi) {  // wave-uniform
-              const float sd = qv[j].x * kv.x + qv[j].y * kv.y + qv[j].z * kv.z + qv[j].w * kv.w;
-              sc[q][j] = p < p_end ? half_total(sd) * scale : -INFINITY;
-            } else {
-              sc[q][j] = -INFINITY;
-            }
-          }
+        for (int k = 0; k < 4; ++k) {
+          // the cache row of the new position was loaded before it was written
+          const f32x4 kf = p == pos ? *reinterpret_cast<const f32x4*>(knew + 32 * k + 4 * q8) : as_f4(r.R[t * 4 + k]);
+          sd = fmaf(q[k].x, kf.x, sd);
+          sd = fmaf(q[k].y, kf.y, sd);
+          sd = fmaf(q[k].z, kf.z, sd);
+          sd = fmaf(q[k].w, kf.w, sd);
         }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const float mx = fmaxf(fmaxf(m[j], fmaxf(sc[0][j], sc[1][j])), fmaxf(sc[2][j], sc[3][j]));
-          if (mx != -INFINITY) {
-            const float corr = __expf(m[j] - mx);
-            ls[j] *= corr;
-            o[j] = o[j] * corr;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float pw = __expf(sc[q][j] - mx);
-              ls[j] += pw;
-              o[j] = o[j] + vv[q] * pw;
-            }
-            m[j] = mx;
-          }
-        }
+        sd = group8_sum(sd) * scale;
+        sc[t] = p < p_end ? sd : -INFINITY;
       }
-    }
-  };
-  consume(rg, std::integral_constant<int, kFirst>{}, 0);
-  for (int b = kFirst / 2; wave_first + b * 16 < p_end; b += kBatch / 2) {  // a split longer than the slice loaded ahead
-    Addr<kBatch> ad;
-    kv_addr<kBatch>(ad, Kg, Vg, p_begin, b);
-    Regs<kBatch> r2;
-    load_regs(r2, ad);
-    consume(r2, std::integral_constant<int, kBatch>{}, b);
-  }
-  stamp(c, sm, 5 * l + kAttn, 6, threadIdx.x == 0);
-  // merge the two half-waves of this wave, lower half first (same order in both halves)
+      float mx = m;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    if (j >= gi) break;  // wave-uniform
-    const float m2 = __shfl_xor(m[j], 32, 64), l2 = __shfl_xor(ls[j], 32, 64);
-    f32x4 o2;
-    o2.x = __shfl_xor(o[j].x, 32, 64);
-    o2.y = __shfl_xor(o[j].y, 32, 64);
-    o2.z = __shfl_xor(o[j].z, 32, 64);
-    o2.w = __shfl_xor(o[j].w, 32, 64);
-    const float M = fmaxf(m[j], m2);
-    if (M != -INFINITY) {
-      const bool lo = lane < 32;
-      const float fa = __expf((lo ? m[j] : m2) - M), fb = __expf((lo ? m2 : m[j]) - M);
-      const float la = lo ? ls[j] : l2, lb = lo ? l2 : ls[j];
-      const f32x4 oa = lo ? o[j] : o2, ob = lo ? o2 : o[j];
-      ls[j] = la * fa + lb * fb;
-      o[j] = oa * fa + ob * fb;
-      m[j] = M;
+      for (int t = 0; t < NT; ++t) mx = fmaxf(mx, sc[t]);
+      if (mx != -INFINITY) {
+        const float corr = __expf(m - mx);
+        ls *= corr;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = o[k] * corr;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int p = pw + 64 * (t0 + t);
+          const float pwt = __expf(sc[t] - mx);
+          ls += pwt;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            // rows past the split were read but are not data (a zero weight
+            // times a stale NaN would still be NaN): their V is replaced by 0
+            const f32x4 vf = p >= p_end ? f32x4{0.f, 0.f, 0.f, 0.f}
+                             : p == pos ? *reinterpret_cast<const f32x4*>(vnew + 32 * k + 4 * q8)
+                                        : as_f4(r.R[N / 2 + t * 4 + k]);
+            o[k] = o[k] + vf * pwt;
+          }
+        }
+        m = mx;
+      }
+    };
+    consume(rg, std::integral_constant<int, kFirst>{}, 0);
+    for (int t0 = kFirst / 8; p_begin + 64 * t0 + 8 * wave < p_end; ++t0) {  // a split longer than the slice loaded ahead
+      Addr<kBatch> ad;
+      kv_addr<kBatch>(ad, Kg, Vg, p_begin, t0);
+      Regs<kBatch> r2;
+      load_regs(r2, ad);
+      consume(r2, std::integral_constant<int, kBatch>{}, t0);
     }
-    if (lane < 32) {
+    if (j == 0) stamp(c, sm, 5 * l + kAttn, 6, threadIdx.x == 0);
+    // merge the 8 groups of the wave (lanes with equal q8 hold the same dims)
+    merge_xor<8>(m, ls, o);
+    merge_xor<16>(m, ls, o);
+    merge_xor<32>(m, ls, o);
+    if (pg == 0) {  // lanes 0..7: the wave's state of head j
       float* e = sm.att + (wave * G + j) * kAttStride;
-      *reinterpret_cast<f32x4*>(e + 4 + sub * 4) = o[j];
-      if (sub == 0) {
-        e[0] = m[j];
-        e[1] = ls[j];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) *reinterpret_cast<f32x4*>(e + 4 + 32 * k + 4 * q8) = o[k];
+      if (q8 == 0) {
+        e[0] = m;
+        e[1] = ls;
       }
     }
   }
@@ -1156,7 +1198,7 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
   // attention: splits no longer than the K/V rows a CU loads ahead, on at most half the grid
   const int smax = grid / (2 * pc.nkv);
   if (smax < 1) return -1;
-  const int span = kFirst / 2 * 16;  // positions in the slice loaded ahead
+  const int span = kFirst / 8 * 64;  // positions in the slice loaded ahead
   int S = std::min((ctx + span - 1) / span, smax);
   const int chunk = (ctx + S - 1) / S;
   S = (ctx + chunk - 1) / chunk;  // every split holds at least one position

@@ -284,6 +284,25 @@ def test_tiny_long_context_splits(torch_cuda, path):
     assert_records(recs, max_forced=1)
 
 
+def test_tiny_persistent_split_beyond_lookahead(torch_cuda):
+    """Decode past 1600 positions on a tiny model with 16 kv heads (one q head
+    each): the CU budget caps the persistent step at 8 attention splits per kv
+    head, so a split holds more positions (201) than the K/V rows a CU loads
+    ahead (192) and the rest stream in further batches; every step checked."""
+    import dataclasses
+    shape = dataclasses.replace(synth.TINY, n_q_heads=16, n_kv_heads=16, max_pos=1664)
+    log("tiny, 16 kv heads, 1600-token context, persistent")
+    w = synth.make_weights(shape, seed=23)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 1600, path="persistent")
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = synth.make_prompt(shape.vocab, 1600, seed=24)
+    recs = lockstep_greedy(dec, oracle, prompt, 4, log=log)
+    assert_records(recs, max_forced=1)
+
+
 @pytest.mark.parametrize("n", [16, 137])
 def test_tiny_batched_prefill_matrix_cores(torch_cuda, n):
     """Prefills of >= 16 rows run the projections on the matrix cores (bf16 hi/lo
