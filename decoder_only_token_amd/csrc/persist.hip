@@ -723,10 +723,6 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
   stamp(c, sm, 5 * l + kAttn, 4, threadIdx.x == 0);
   const float* knew = qk + G * D;
   const float* vnew = qk + (G + 1) * D;
-  if (it.x == 0 && pos >= p_begin && pos < p_end && threadIdx.x < D) {  // this split holds the new position
-    st_f(Kg + (size_t)pos * D + threadIdx.x, knew[threadIdx.x]);
-    st_f(Vg + (size_t)pos * D + threadIdx.x, vnew[threadIdx.x]);
-  }
   const float scale = 1.0f / sqrtf((float)D);
   const int pw = p_begin + 8 * wave + pg;  // this lane's position at step 0
   for (int j = 0; j < gi; ++j) {  // the item's heads, one at a time (wave-uniform)
@@ -902,6 +898,21 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, Smem& sm, int l) {
   if (!ok) sm.abort_flag = 1;
   __syncthreads();
   return !sm.abort_flag;
+}
+
+// Attention item, part 3: the new position's K/V row into the cache, by the
+// item whose split holds it.  Only later steps read the row (this step uses
+// the LDS copy), so it is written after the outputs: a store still in flight
+// would make the memory waits of the combine wait for it.
+template <int G>
+__device__ __forceinline__ void attn_cache_write(const Ctx& c, Smem& sm, int l) {
+  const AS4 PersistConst& a = *c.a;
+  const Item it = item_of<G>(c);
+  const int pos = c.pos, p_begin = it.s * c.chunk, p_end = min(p_begin + c.chunk, pos + 1);
+  if (it.x == 0 && pos >= p_begin && pos < p_end && threadIdx.x < D) {
+    st_f(k_rows(a, l, it.g) + (size_t)pos * D + threadIdx.x, sm.qk[G * D + threadIdx.x]);
+    st_f(v_rows(a, l, it.g) + (size_t)pos * D + threadIdx.x, sm.qk[(G + 1) * D + threadIdx.x]);
+  }
 }
 
 // LM head: rows wave, wave + 8, ... of this CU's vocabulary slice, logits
@@ -1126,6 +1137,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
       attn_phase<G>(c, sm, l, rg, pre);
       stamp(c, sm, ph, 2, tid == 0);
       if (!attn_finish<G>(c, sm, l)) return;
+      attn_cache_write<G>(c, sm, l);
     } else {
       gemv_phase(c, sm, l, rg, rs, gv, bias);
     }
