@@ -1,5 +1,5 @@
 // Persistent decode step for gfx950: the whole single-token forward in ONE
-// cooperative kernel launch, one 512-thread workgroup (8 waves) per CU.
+// kernel launch, one 512-thread workgroup (8 waves) per CU, all resident.
 //
 // A decode step is a chain of 5 dependent phases per layer.  As separate
 // kernels every dependency costs a launch gap plus the ramp and tail of the
@@ -1201,7 +1201,11 @@ int persist_prepare(int G, int hseg) {
   void* fn = pick(G, hseg);
   if (!fn) return -1;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
-  return e == hipSuccess ? 0 : (int)e;
+  if (e != hipSuccess) return (int)e;
+  int per_cu = 0;  // one workgroup per CU must fit (the grid is one per CU)
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, sizeof(Smem));
+  if (e != hipSuccess) return (int)e;
+  return per_cu >= 1 ? 0 : -1;
 }
 
 int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, PersistStep* out) {
@@ -1286,11 +1290,17 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
   return out->start[5] == grid ? 0 : -1;  // every CU has a role
 }
 
+// The step needs all grid workgroups resident at once (one per CU).  A plain
+// launch gets that on a device that runs nothing else: the previous work on
+// the stream has completed and every CU takes one workgroup.  A cooperative
+// launch would guarantee it, but costs ~19 us more per step here.  If the
+// device is shared and a workgroup cannot start, the resident ones give up
+// after their bounded wait and the step is reported as abandoned.
 int persist_launch(const PersistConst* dev_const, int G, int hseg, int grid, const PersistStep& st, hipStream_t s) {
   void* fn = pick(G, hseg);
   if (!fn) return -1;
   PersistStep arg = st;
   void* args[] = {(void*)&dev_const, (void*)&arg};
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, sizeof(Smem), s);
+  hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, sizeof(Smem), s);
   return e == hipSuccess ? 0 : (int)e;
 }

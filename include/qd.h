@@ -76,7 +76,9 @@ typedef struct {
   int32_t max_pos;        /* KV-cache capacity in positions */
   int32_t max_prefill;    /* largest n accepted by one qd_prefill call */
   int32_t lora_rank_max;  /* 0 disables LoRA; else the largest rank qd_set_lora accepts */
-  int32_t decode_path;    /* QD_DECODE_PERSISTENT (one cooperative kernel per decode step)
+  int32_t decode_path;    /* QD_DECODE_PERSISTENT (one kernel per decode step, one workgroup per CU,
+                             all resident at once: the device must not be running other work
+                             meanwhile, else a step can be abandoned after its bounded wait)
                              or QD_DECODE_GRAPH (one kernel per operation, replayed as a hipGraph) */
 } qd_config;
 
