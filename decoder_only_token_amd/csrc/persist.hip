@@ -28,9 +28,12 @@
 // partials, and CU 0 the argmax over the partials, advancing the step state.
 //
 // Every phase: all 512 threads poll the input (a few values each) into LDS,
-// one workgroup barrier, then each wave computes whole output rows.  RMSNorm
-// is folded in: the LDS input is gain * x and each row sum is scaled by
-// 1/RMS(x) afterwards.
+// one workgroup barrier, then the phase's arithmetic.  A GEMV role multiplies
+// on the matrix cores: its rows form 16 x 32 bf16 tiles, the input enters as
+// the bf16 pair (hi, lo) in two rows of the other operand, and each wave
+// accumulates every eighth column chunk, the 8 partials of a row being added
+// in LDS.  RMSNorm is folded in: the LDS input is gain * x and each row sum is
+// scaled by 1/RMS(x) afterwards.
 //
 // The fused QKV rows are stored group-major ([kv head g][q heads of g | k_g |
 // v_g] x 128), so one attention item reads one contiguous run.
@@ -299,12 +302,35 @@ __device__ __forceinline__ Gemv gemv_of(const Ctx& c, int l) {
   return g;
 }
 
-// Whether this CU's GEMV role takes the whole-segment path (rows of 2, 4 or 6
-// full segments), which stages its input as bf16 halves.
-__device__ __forceinline__ bool whole_segments(const Ctx& c) {
+// Matrix-core geometry of a GEMV role.  The CU's rows (per row set: gate and
+// up rows for pairs) form blocks of 16 (the last block shifted back to end at
+// the last row, overlapping its neighbour); the K columns form chunks of 32,
+// dealt to the 8 waves round robin (chunk w + 8 j goes to wave w).  A register
+// slot holds one 16 x 32 tile: lane i has row i % 16, columns 8 (i / 16) ..
+// + 7.  The tiles of every wave fit in the registers loaded ahead.
+struct Tiles {
+  int nb;   // row blocks per row set
+  int ns;   // row sets: 2 for gate/up pairs, else 1
+  int nkw;  // chunks per wave (K / 256)
+};
+
+__device__ __forceinline__ int gemv_k(const Ctx& c) {
   const AS4 PersistConst& a = *c.a;
-  const int K = c.role == kOproj ? a.nq * D : c.role == kDown ? a.I : a.H;
-  return c.role != kAttn && K % kSeg == 0 && (K == 2 * kSeg || K == 4 * kSeg || K == 6 * kSeg);
+  return c.role == kOproj ? a.nq * D : c.role == kDown ? a.I : a.H;
+}
+
+// Whether this CU's GEMV role runs on the matrix cores (and so stages its
+// input as bf16 halves); the other shapes take the row-segment path.
+__device__ __forceinline__ bool mfma_path(const Ctx& c, Tiles* t = nullptr) {
+  if (c.role == kAttn) return false;
+  const int K = gemv_k(c), n = c.r1 - c.r0;
+  Tiles g;
+  g.nb = (n + 15) >> 4;
+  g.ns = c.role == kGateUp ? 2 : 1;
+  g.nkw = K >> 8;
+  if (t) *t = g;
+  const bool kw = g.nkw == 4 || g.nkw == 6 || g.nkw == 8 || g.nkw == 12;
+  return (K & 255) == 0 && kw && n >= 16 && g.ns * g.nb <= 6 && g.ns * g.nb * g.nkw <= kFirst;
 }
 
 // A wave's walk over its segments: unit u (= wave + 8 j), row-in-unit t, segment sg.
@@ -379,6 +405,25 @@ __device__ __forceinline__ void gemv_addr(Addr<N>& ad, const Gemv& g, Walk w) {
   }
 }
 
+// The tiles of this wave (see Tiles): slot bb nkw + j holds row block bb (row
+// set bb / nb) and chunk wave + 8 j; slots past the tiles repeat the last one.
+// Every row read lies inside the CU's own rows.
+template <int N>
+__device__ __forceinline__ void tile_addr(Addr<N>& ad, const Gemv& g, const Tiles& t, int nrows) {
+  ad.rs[0] = ad.rs[1] = rsrc_of(g.a);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  ad.voff = (lane & 15) * g.K * 2 + (lane >> 4) * 16;
+  const int T = t.ns * t.nb * t.nkw;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int ii = min(i, T - 1);
+    const int bb = ii / t.nkw, j = ii - bb * t.nkw;
+    const int set = bb / t.nb, b = bb - set * t.nb;
+    const int row = min(16 * b, nrows - 16);
+    ad.soff[i] = (int)(((long)set * g.delta + (long)row * g.K + (wave + 8 * j) * 32) * 2);
+  }
+}
+
 // Attention steps t0 .. t0 + N/8 - 1: lane q8 of group pg reads dims
 // 32 k + 4 q8 .. + 3 (k < 4) of position p_begin + 64 t + 8 wave + pg; K
 // fragment k of step t in slot 4 t + k, V in N/2 + 4 t + k.  Positions past the
@@ -434,104 +479,69 @@ __device__ __forceinline__ Addr<kFirst> ahead_addr(const Ctx& c, int l) {
     const int g = c.rank / (c.X * c.S), s = c.rank % c.S;
     kv_addr<kFirst>(ad, k_rows(a, l, g), v_rows(a, l, g), s * c.chunk, 0);
   } else {
-    gemv_addr<kFirst>(ad, gemv_of(c, l), Walk{wave, 0, 0});
+    Tiles t;
+    if (mfma_path(c, &t))
+      tile_addr<kFirst>(ad, gemv_of(c, l), t, c.r1 - c.r0);
+    else
+      gemv_addr<kFirst>(ad, gemv_of(c, l), Walk{wave, 0, 0});
   }
   return ad;
 }
 
 // ------------------------------------------------------------------- phases
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-// Dot of 8 bf16 weights with 8 inputs given as bf16 halves (hi + lo): eight
-// bf16 pair products accumulated in f32.
-__device__ __forceinline__ float dot8_split(u32x4 w, u32x4 hi, u32x4 lo, float acc) {
-// (the vector elements are converted to plain values before the bit cast: a
-// bit cast applied to an element expression itself reads element 0 here)
-#define QD_DOT2(a, b, c) \
-  __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, (uint32_t)(a)), __builtin_bit_cast(bf16x2_t, (uint32_t)(b)), c, false)
-  acc = QD_DOT2(w.x, hi.x, acc);
-  acc = QD_DOT2(w.x, lo.x, acc);
-  acc = QD_DOT2(w.y, hi.y, acc);
-  acc = QD_DOT2(w.y, lo.y, acc);
-  acc = QD_DOT2(w.z, hi.z, acc);
-  acc = QD_DOT2(w.z, lo.z, acc);
-  acc = QD_DOT2(w.w, hi.w, acc);
-  acc = QD_DOT2(w.w, lo.w, acc);
-#undef QD_DOT2
-  return acc;
-}
+constexpr int kTileRed = 96;  // LDS floats per wave for the tile partials (6 blocks of 16 rows)
 
-// GEMV units held in the registers loaded ahead, for rows of exactly NSEG
-// whole segments (input staged as bf16 halves): the wave's NSEG input
-// fragments are read from LDS once, each valid unit's dot products run without
-// further branches, and the row sums of all units are finished together.
-// Returns the units per wave covered (kFirst / (RPU NSEG)).
-template <int RPU, int NSEG>
-__device__ __forceinline__ int gemv_ahead(const Ctx& c, Smem& sm, const Gemv& g, const Regs<kFirst>& rg,
-                                          const float* h, float rs, int l) {
-  const int ph = 5 * l + c.role;
-  constexpr int UPW = kFirst / (RPU * NSEG);
+// GEMV tiles on the matrix cores (see Tiles).  Each 16 x 16 x 32 product takes
+// one input chunk of the wave as operand A, whose rows 0 and 1 are the bf16
+// halves hi and lo of the 32 inputs (the other rows are not used), and one
+// weight tile as operand B; result rows 0 and 1 of lane n < 16 accumulate row
+// n of the block against hi and lo.  Lanes 0..15 then write each block's
+// partial (hi + lo over the wave's chunks) to LDS.
+template <int NKW, int NBT>
+__device__ __forceinline__ void gemv_tiles(const Ctx& c, Smem& sm, const Regs<kFirst>& rg, const float* h, int l) {
+  static_assert(NKW * NBT <= kFirst && NBT * 16 <= kTileRed, "tiles fit the registers and the LDS partials");
   const int lane = threadIdx.x & 63, wave = wave_id();
-  u32x4 hh[NSEG], hl[NSEG];
+  u32x4 xa[NKW];
 #pragma unroll
-  for (int sg = 0; sg < NSEG; ++sg) {
-    const u32x4* blk = reinterpret_cast<const u32x4*>(h + sg * kSeg + lane * 8);  // 32 bytes: hi[8], lo[8]
-    hh[sg] = blk[0];
-    hl[sg] = blk[1];
+  for (int j = 0; j < NKW; ++j)  // 8 inputs as hi[8] then lo[8]: lane 1 of each 16 takes the lo half
+    xa[j] = *reinterpret_cast<const u32x4*>(h + (wave + 8 * j) * 32 + (lane >> 4) * 8 + ((lane & 15) == 1 ? 4 : 0));
+  __builtin_amdgcn_sched_barrier(0);  // every LDS read in flight before the first product
+  f32x4 acc[NBT];
+#pragma unroll
+  for (int bb = 0; bb < NBT; ++bb) acc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NKW; ++j)
+#pragma unroll
+    for (int bb = 0; bb < NBT; ++bb)
+      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[j]),
+                                                        __builtin_bit_cast(bf16x8_t, rg.R[bb * NKW + j]), acc[bb], 0, 0, 0);
+  stamp(c, sm, 5 * l + c.role, 6, threadIdx.x == 0);
+  float* red = sm.att + wave * kTileRed;
+  if (lane < 16) {
+#pragma unroll
+    for (int bb = 0; bb < NBT; ++bb) red[bb * 16 + lane] = acc[bb].x + acc[bb].y;
   }
-  float p[UPW * RPU];
-#pragma unroll
-  for (int j = 0; j < UPW; ++j) {
-#pragma unroll
-    for (int t = 0; t < RPU; ++t) p[j * RPU + t] = 0.f;
-    if (wave + kWaves * j < g.nunits) {  // wave-uniform
-#pragma unroll
-      for (int t = 0; t < RPU; ++t) {
-        float acc = 0.f;
-#pragma unroll
-        for (int sg = 0; sg < NSEG; ++sg) acc = dot8_split(rg.R[(j * RPU + t) * NSEG + sg], hh[sg], hl[sg], acc);
-        p[j * RPU + t] = acc;
-      }
-    }
-  }
-  stamp(c, sm, ph, 6, threadIdx.x == 0);
-  // Row sums through LDS: the wave writes its row partials [row][lane], then
-  // lanes 4r .. 4r + 3 add row r's 64 partials (16 each) and finish with two
-  // quad exchanges; one pass serves every row of the wave.  The attention
-  // scratch is free on CUs that run a GEMV role.
-  constexpr int NR = UPW * RPU;  // rows of the wave, at most 16
-  static_assert(NR <= 16, "one reduction pass covers 16 rows");
-  float* red = sm.att + wave * (16 * kRedStride);
-#pragma unroll
-  for (int i = 0; i < NR; ++i) red[i * kRedStride + lane] = p[i];
-  const int row = lane >> 2;
-  float t = 0.f;
-  if (row < NR) {
-    const float* src = red + row * kRedStride + (lane & 3) * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * q);
-      t += (v.x + v.y) + (v.z + v.w);
-    }
-  }
-  t += DPPF(t, 0xB1, 0xF);  // quad_perm [1,0,3,2]
-  t += DPPF(t, 0x4E, 0xF);  // quad_perm [2,3,0,1]: every lane of the quad holds row `row`
-  t *= rs;
-  if (RPU == 1) {
-    const int u = wave + kWaves * row;
-    if ((lane & 3) == 0 && row < NR && u < g.nunits) sm.outv[u] = t;
-  } else {
-    // unit j: gate row 2j in lanes 8j .. 8j + 3, up row 2j + 1 in lanes 8j + 4 .. 8j + 7
-    const float gate = DPPF(t, 0x114, 0xF);  // row_shr:4
-    const int j = lane >> 3, u = wave + kWaves * j;
-    if ((lane & 7) == 4 && j < UPW && u < g.nunits)
-      sm.outv[u] = t * gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
-  }
-  return UPW;
 }
 
-// GEMV role: this wave's units, the slice loaded ahead first and any rest in
-// streamed batches; each finished row goes straight to its output word.
+__device__ __forceinline__ void gemv_tiles_any(const Ctx& c, Smem& sm, const Tiles& t, const Regs<kFirst>& rg,
+                                               const float* h, int l) {
+#define QD_TILES(K, B) \
+  case K * 8 + B: gemv_tiles<K, B>(c, sm, rg, h, l); break;
+  switch (t.nkw * 8 + t.ns * t.nb) {
+    QD_TILES(4, 1) QD_TILES(4, 2) QD_TILES(4, 3) QD_TILES(4, 4) QD_TILES(4, 5) QD_TILES(4, 6)
+    QD_TILES(6, 1) QD_TILES(6, 2) QD_TILES(6, 3) QD_TILES(6, 4)
+    QD_TILES(8, 1) QD_TILES(8, 2) QD_TILES(8, 3)
+    QD_TILES(12, 1) QD_TILES(12, 2)
+    default: break;  // excluded by mfma_path
+  }
+#undef QD_TILES
+}
+
+// GEMV role: this CU's rows, from the registers loaded ahead (and, on the
+// row-segment path, streamed batches for any rest), published one word per
+// output row.
 __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, float rs,
                                            const Gemv& g, const float* bias) {
   const AS4 PersistConst& a = *c.a;
@@ -540,20 +550,49 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
   const float* xr = sm.xres[l & 1];
   const uint32_t tag = tag_of(c.seq, l);
   stamp(c, sm, 5 * l + kind, 4, threadIdx.x == 0);
+  // Publishing: every unit at once, one word per thread, so a wave's stores
+  // cover whole cache lines (single-word stores spread over lines reach the
+  // pollers much later).
+  auto publish = [&](int u, float t) {
+    const int r = c.r0 + u;
+    switch (kind) {
+      case kQKV: st_tagged(a.QKV + r, bias ? t + ld_f(bias + r) : t, tag); break;
+      case kOproj: st_tagged(a.X1 + r, xr[u] + t, tag); break;
+      case kGateUp: st_tagged(a.ACT + r, t, tag); break;
+      default: st_tagged(a.X0 + r, xr[u] + t, tag_of(c.seq, l + 1)); break;
+    }
+  };
+  Tiles tl;
+  if (mfma_path(c, &tl)) {
+    gemv_tiles_any(c, sm, tl, rg, h, l);
+    __syncthreads();
+    // unit u: the 8 waves' partials of its row (and of its up row for pairs)
+    const int nrows = c.r1 - c.r0;
+    for (int u = threadIdx.x; u < nrows; u += kThreads) {
+      const int b = min(u >> 4, tl.nb - 1);
+      const int n = b * 16 + u - min(16 * b, nrows - 16);
+      float y = 0.f, z = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) y += sm.att[w * kTileRed + n];
+      float t = y * rs;
+      if (tl.ns == 2) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) z += sm.att[w * kTileRed + tl.nb * 16 + n];
+        t = z * rs * t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));  // up * SiLU(gate)
+      }
+      publish(u, t);
+    }
+    stamp(c, sm, 5 * l + kind, 2, threadIdx.x == 0);
+    return;
+  }
   Walk w{wave, 0, 0};
   float acc = 0.f, first = 0.f;
-  const bool split = whole_segments(c);  // the input is staged as bf16 halves
   auto consume = [&](const auto& r, auto n) {
 #pragma unroll
     for (int i = 0; i < decltype(n)::value; ++i) {
       if (walk_valid(g, w)) {  // wave-uniform
         const int k = w.sg * kSeg + lane * 8;
-        if (split) {
-          const u32x4* blk = reinterpret_cast<const u32x4*>(h + k);
-          acc = dot8_split(r.R[i], blk[0], blk[1], acc);
-        } else if (k < g.K) {
-          acc += dot8(r.R[i], h + k);
-        }
+        if (k < g.K) acc += dot8(r.R[i], h + k);
         if (w.sg + 1 == g.nseg) {  // row finished
           const float t = wave_total(acc) * rs;
           acc = 0.f;
@@ -567,26 +606,7 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
       }
     }
   };
-  int upw = 0;  // units per wave taken by the whole-segment path
-  if (split) {
-    if (g.rpu == 1) {
-      switch (g.nseg) {
-        case 2: upw = gemv_ahead<1, 2>(c, sm, g, rg, h, rs, l); break;
-        case 4: upw = gemv_ahead<1, 4>(c, sm, g, rg, h, rs, l); break;
-        case 6: upw = gemv_ahead<1, 6>(c, sm, g, rg, h, rs, l); break;
-      }
-    } else {
-      switch (g.nseg) {
-        case 2: upw = gemv_ahead<2, 2>(c, sm, g, rg, h, rs, l); break;
-        case 4: upw = gemv_ahead<2, 4>(c, sm, g, rg, h, rs, l); break;
-        case 6: upw = gemv_ahead<2, 6>(c, sm, g, rg, h, rs, l); break;
-      }
-    }
-  }
-  if (upw > 0)
-    w.u += kWaves * upw;  // the rest (if any) streams below
-  else
-    consume(rg, std::integral_constant<int, kFirst>{});
+  consume(rg, std::integral_constant<int, kFirst>{});
   while (walk_valid(g, w)) {  // a slice larger than the registers loaded ahead
     Addr<kBatch> ad;
     gemv_addr<kBatch>(ad, g, w);
@@ -595,21 +615,8 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
     consume(r2, std::integral_constant<int, kBatch>{});
   }
   stamp(c, sm, 5 * l + kind, 2, threadIdx.x == 0);
-  // Publish every unit at once, one word per thread, so a wave's stores cover
-  // whole cache lines (single-word stores spread over lines reach the pollers
-  // much later), and no wait on the memory counter follows them inside the
-  // dot products.
   __syncthreads();
-  for (int u = threadIdx.x; u < g.nunits; u += kThreads) {
-    const int r = c.r0 + u;
-    const float t = sm.outv[u];
-    switch (kind) {
-      case kQKV: st_tagged(a.QKV + r, bias ? t + ld_f(bias + r) : t, tag); break;
-      case kOproj: st_tagged(a.X1 + r, xr[u] + t, tag); break;
-      case kGateUp: st_tagged(a.ACT + r, t, tag); break;
-      default: st_tagged(a.X0 + r, xr[u] + t, tag_of(c.seq, l + 1)); break;
-    }
-  }
+  for (int u = threadIdx.x; u < g.nunits; u += kThreads) publish(u, sm.outv[u]);
 }
 
 // The attention item's per-lane constants that do not depend on the phase
@@ -1085,7 +1092,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
     bool ok = true;
     if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
       float ss = 0.f;
-      const bool split = whole_segments(c);
+      const bool split = mfma_path(c);
       for (int k = tid; k < H; k += kThreads) {
         const float x = bf16_to_f(*gl(emb + k));
         const float y = x * ld_f(Lw.attn_norm + k);
@@ -1128,7 +1135,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
         case kGateUp: src = a.X1; n = H; gain = Lw.mlp_norm; break;
         default: src = a.ACT; n = a.I; src2 = a.X1 + c.r0; n2 = c.r1 - c.r0; break;
       }
-      ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, whole_segments(c));
+      ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, mfma_path(c));
     }
     if (!ok) return;
     stamp(c, sm, ph, 1, tid == 0);
