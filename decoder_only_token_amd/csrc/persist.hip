@@ -648,50 +648,33 @@ __device__ __forceinline__ float group8_sum(float v) {
   return v;
 }
 
-// The values of lanes i and i ^ d as (lower lane's, upper lane's), the same
-// pair in both lanes: d = 8 by a DPP rotation within rows of 16; d = 16 and
-// 32 by the gfx950 row swaps, whose two results are already in that order.
+// Reduce-scatter step over lane bit 5 (d = 32) or 4 (d = 16) with the gfx950
+// row swaps: lanes with the bit clear return a + a of the partner lane, lanes
+// with it set b + b of the partner.
 template <int d>
-__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
-  if (d == 8) {
-    const float p = DPPF(v, 0x128, 0xF);  // row_ror:8
-    const bool low = (threadIdx.x & 8) == 0;
-    lo = low ? v : p;
-    hi = low ? p : v;
-  } else {
-    const uint32_t u = __float_as_uint(v);
-    const auto r = d == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
-                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    lo = __uint_as_float(r[0]);
-    hi = __uint_as_float(r[1]);
-  }
+__device__ __forceinline__ float swap_sum(float a, float b) {
+  const auto r = d == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                         : __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Merge this lane's online-softmax state {m, l, o} with lane i ^ d's (equal
-// result in both lanes: the lower lane's state goes first).
-template <int d>
-__device__ __forceinline__ void merge_xor(float& m, float& ls, f32x4 (&o)[4]) {
-  float ma, mb, la, lb;
-  lane_pair<d>(m, ma, mb);
-  lane_pair<d>(ls, la, lb);
-  float oa[16], ob[16];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    lane_pair<d>(o[k].x, oa[4 * k + 0], ob[4 * k + 0]);
-    lane_pair<d>(o[k].y, oa[4 * k + 1], ob[4 * k + 1]);
-    lane_pair<d>(o[k].z, oa[4 * k + 2], ob[4 * k + 2]);
-    lane_pair<d>(o[k].w, oa[4 * k + 3], ob[4 * k + 3]);
-  }
-  const float M = fmaxf(ma, mb);
-  if (M != -INFINITY) {
-    const float fa = __expf(ma - M), fb = __expf(mb - M);
-    ls = la * fa + lb * fb;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      o[k] = f32x4{oa[4 * k] * fa + ob[4 * k] * fb, oa[4 * k + 1] * fa + ob[4 * k + 1] * fb,
-                   oa[4 * k + 2] * fa + ob[4 * k + 2] * fb, oa[4 * k + 3] * fa + ob[4 * k + 3] * fb};
-    m = M;
-  }
+// Maximum / sum over the 8 lanes i ^ {0, 8, 16, ..., 56} (lane bits 3..5), in
+// every lane; the pairs are combined in mirrored order, so every lane gets
+// the same value.
+__device__ __forceinline__ float xor_max3(float v) {
+  v = fmaxf(v, DPPF(v, 0x128, 0xF));  // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor_sum3(float v) {
+  const float p = DPPF(v, 0x128, 0xF);  // row_ror:8
+  v = (threadIdx.x & 8) ? p + v : v + p;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Attention item (kv head g, head group, split s), part 1: QK-norm + RoPE of
@@ -793,17 +776,36 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
       consume(r2, std::integral_constant<int, kBatch>{}, t0);
     }
     if (j == 0) stamp(c, sm, 5 * l + kAttn, 6, threadIdx.x == 0);
-    // merge the 8 groups of the wave (lanes with equal q8 hold the same dims)
-    merge_xor<8>(m, ls, o);
-    merge_xor<16>(m, ls, o);
-    merge_xor<32>(m, ls, o);
-    if (pg == 0) {  // lanes 0..7: the wave's state of head j
-      float* e = sm.att + (wave * G + j) * kAttStride;
+    // Merge the 8 groups of the wave (lanes with equal q8 hold the same dims):
+    // every group is rescaled to the wave's maximum, then the sums run as a
+    // reduce-scatter over lane bits 5 and 4 (each row swap moves two values)
+    // and a plain sum over bit 3, leaving o[r] of the wave in lanes 16 r ..
+    // 16 r + 15.
+    const float M = xor_max3(m);
+    const float f = M == -INFINITY ? 0.f : __expf(m - M);
+    float ov[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) *reinterpret_cast<f32x4*>(e + 4 + 32 * k + 4 * q8) = o[k];
-      if (q8 == 0) {
-        e[0] = m;
-        e[1] = ls;
+    for (int k = 0; k < 4; ++k) {
+      ov[4 * k + 0] = o[k].x * f;
+      ov[4 * k + 1] = o[k].y * f;
+      ov[4 * k + 2] = o[k].z * f;
+      ov[4 * k + 3] = o[k].w * f;
+    }
+    const float lsum = xor_sum3(ls * f);
+    float s8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s8[i] = swap_sum<32>(ov[i], ov[i + 8]);  // bit 5 set: values 8 ..
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] = swap_sum<16>(s8[i], s8[i + 4]);  // bit 4 set: values 4 ..
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] += DPPF(s4[i], 0x128, 0xF);  // row_ror:8: lanes i, i ^ 8
+    if ((lane & 8) == 0) {  // the wave's state of head j: o[r] from row r's lanes 0..7
+      float* e = sm.att + (wave * G + j) * kAttStride;
+      *reinterpret_cast<f32x4*>(e + 4 + 32 * (lane >> 4) + 4 * q8) = f32x4{s4[0], s4[1], s4[2], s4[3]};
+      if (lane == 0) {
+        e[0] = M;
+        e[1] = lsum;
       }
     }
   }
