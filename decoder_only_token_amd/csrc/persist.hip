@@ -677,6 +677,21 @@ __device__ __forceinline__ float xor_sum3(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// This lane's 16 dims of q . k for K fragments kp[0], kp[stride], kp[2 stride],
+// kp[3 stride] (16 bytes each: dims 32 k + 4 q8 .. + 3).
+__device__ __forceinline__ float dot16(const f32x4 (&q)[4], const u32x4* kp, int stride = 1) {
+  float sd = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x4 kf = as_f4(kp[k * stride]);
+    sd = fmaf(q[k].x, kf.x, sd);
+    sd = fmaf(q[k].y, kf.y, sd);
+    sd = fmaf(q[k].z, kf.z, sd);
+    sd = fmaf(q[k].w, kf.w, sd);
+  }
+  return sd;
+}
+
 // Attention item (kv head g, head group, split s), part 1: QK-norm + RoPE of
 // the item's q heads and k in LDS, the new cache row, then per head an online
 // softmax over the split's positions.  A wave covers 8 positions at a time,
@@ -727,16 +742,14 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
       float sc[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        sc[t] = -INFINITY;
+        const int pf = p_begin + 8 * wave + 64 * (t0 + t);  // the wave's first position of the step
+        if (pf >= p_end) continue;  // wave-uniform: no position of the split in this step
         const int p = pw + 64 * (t0 + t);
-        float sd = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // the cache row of the new position was loaded before it was written
-          const f32x4 kf = p == pos ? *reinterpret_cast<const f32x4*>(knew + 32 * k + 4 * q8) : as_f4(r.R[t * 4 + k]);
-          sd = fmaf(q[k].x, kf.x, sd);
-          sd = fmaf(q[k].y, kf.y, sd);
-          sd = fmaf(q[k].z, kf.z, sd);
-          sd = fmaf(q[k].w, kf.w, sd);
+        float sd = dot16(q, r.R + t * 4);
+        if (pf <= pos && pos < pf + 8) {  // wave-uniform: the new position, whose row was loaded before it was written
+          const float sn = dot16(q, reinterpret_cast<const u32x4*>(knew + 4 * q8), 8);
+          sd = p == pos ? sn : sd;
         }
         sd = group8_sum(sd) * scale;
         sc[t] = p < p_end ? sd : -INFINITY;
@@ -751,17 +764,24 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
         for (int k = 0; k < 4; ++k) o[k] = o[k] * corr;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+          const int pf = p_begin + 8 * wave + 64 * (t0 + t);
+          if (pf >= p_end) continue;  // wave-uniform, as above
           const int p = pw + 64 * (t0 + t);
           const float pwt = __expf(sc[t] - mx);
           ls += pwt;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
+          if (pf + 8 > p_end || (pf <= pos && pos < pf + 8)) {  // wave-uniform
             // rows past the split were read but are not data (a zero weight
             // times a stale NaN would still be NaN): their V is replaced by 0
-            const f32x4 vf = p >= p_end ? f32x4{0.f, 0.f, 0.f, 0.f}
-                             : p == pos ? *reinterpret_cast<const f32x4*>(vnew + 32 * k + 4 * q8)
-                                        : as_f4(r.R[N / 2 + t * 4 + k]);
-            o[k] = o[k] + vf * pwt;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const f32x4 vf = p >= p_end ? f32x4{0.f, 0.f, 0.f, 0.f}
+                               : p == pos ? *reinterpret_cast<const f32x4*>(vnew + 32 * k + 4 * q8)
+                                          : as_f4(r.R[N / 2 + t * 4 + k]);
+              o[k] = o[k] + vf * pwt;
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = o[k] + as_f4(r.R[N / 2 + t * 4 + k]) * pwt;
           }
         }
         m = mx;
