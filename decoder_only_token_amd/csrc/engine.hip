@@ -533,10 +533,12 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
         (rc = dev_alloc(h, &h->err_dev, 4)) || (rc = dev_alloc(h, &h->pconst, 1)) ||
         (rc = dev_alloc(h, &h->layer_ptrs, (size_t)c.n_layers)))
       return fail(rc);
-    // tags start at 0; every step uses seq >= 1, so stale words never match
+    // tags start at 0; every step uses seq >= 1, so stale words never match.
+    // The activation pairs carry only 16 tag bits (8 of the step): they start
+    // as all ones (layer 255, never a decoder layer), and a reset refills them.
     if (hipMemset(h->X0, 0, H * 8) || hipMemset(h->X1, 0, H * 8) || hipMemset(h->QKVx, 0, qkv_rows(c) * 8) ||
         hipMemset(h->PART, 0, (size_t)c.n_q_heads * smax * (d + 2) * 8) || hipMemset(h->Ox, 0, c.n_q_heads * d * 8) ||
-        hipMemset(h->ACT, 0, I * 8) || hipMemset(h->AM, 0, h->grid * 16) ||
+        hipMemset(h->ACT, 0xFF, I * 8) || hipMemset(h->AM, 0, h->grid * 16) ||
         hipMemset(h->err_dev, 0, 16))
       return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
   }
@@ -682,6 +684,7 @@ int qd_reset_kv(qd_handle* h) {
   if (!h) return QD_E_ARG;
   HIP_TRY(h, hipMemsetAsync(h->st, 0, sizeof(DevState), h->stream));
   if (h->err_dev) HIP_TRY(h, hipMemsetAsync(h->err_dev, 0, 16, h->stream));
+  if (h->ACT) HIP_TRY(h, hipMemsetAsync(h->ACT, 0xFF, (size_t)h->cfg.intermediate * 8, h->stream));
   h->failed = false;
   h->pos = 0;
   h->have_token = false;

@@ -94,6 +94,20 @@ __device__ __forceinline__ float ld_f(const float* p) { return *gl(p); }
 __device__ __forceinline__ void st_f(float* p, float v) { *gl(p) = v; }
 __device__ __forceinline__ uint32_t tag_of(uint32_t seq, int l) { return (seq << 8) | (uint32_t)l; }
 
+// Value pairs: a 64-bit word {tag16 << 48 | a24 << 24 | b24} carries two
+// values rounded to 16 significant bits (the top 24 bits of the float, to
+// nearest even) for a consumer that multiplies them as bf16 halves anyway, and
+// the low 16 bits of the tag (8 bits of the step, the layer).
+__device__ __forceinline__ uint64_t f24(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint64_t)((u + 0x7Fu + ((u >> 8) & 1u)) >> 8);
+}
+__device__ __forceinline__ float unf24(uint64_t b) { return __uint_as_float((uint32_t)(b & 0xFFFFFFu) << 8); }
+__device__ __forceinline__ void st_pair(uint64_t* p, float a, float b, uint32_t tag) {
+  __hip_atomic_store(gl(p), ((uint64_t)(tag & 0xFFFFu) << 48) | (f24(a) << 24) | f24(b), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ f32x4 as_f4(u32x4 u) {
   return f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
 }
@@ -173,6 +187,10 @@ __device__ __forceinline__ void trace_flush(const Ctx& c, Smem& sm) {
   }
 }
 
+// Workgroup barrier ordering LDS only: the waves wait for their own LDS
+// operations, not for global loads still in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ bool timed_out(const Ctx& c) {
   return ld_u32(&c.a->err[0]) != 0 || __builtin_amdgcn_s_memrealtime() - c.t0 > kTimeoutTicks;
 }
@@ -187,11 +205,57 @@ __device__ __forceinline__ bool timed_out(const Ctx& c) {
 // about 16 significant bits, stored per 8 values as hi[8] then lo[8] (the
 // same 32 bytes as 8 floats), for the bf16 dot-product path.
 __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint64_t* src, int n, uint32_t tag, float* dst,
-                     const float* gain, float* rs, const uint64_t* src2, int n2, float* dst2, bool split = false) {
+                     const float* gain, float* rs, const uint64_t* src2, int n2, float* dst2, bool split = false,
+                     bool packed = false) {
   const int tid = threadIdx.x;
   bool ok = !sm.abort_flag;
   float ss = 0.f;
-  for (int base = 0; ok && base < n; base += kPE * kThreads) {
+  if (packed) {  // n / 2 words of value pairs (no gain)
+    const int nw = n >> 1;
+    const uint32_t t16 = tag & 0xFFFFu;
+    for (int base = 0; ok && base < nw; base += kPE * kThreads) {
+      uint64_t v[kPE], v2 = (uint64_t)tag << 32;
+      uint32_t spin = 0;
+      for (;;) {
+        bool done = true;
+#pragma unroll
+        for (int e = 0; e < kPE; ++e) {
+          const int w = base + e * kThreads + tid;
+          v[e] = w < nw ? ld_tagged(src + w) : (uint64_t)t16 << 48;
+        }
+        if (base == 0 && tid < n2) v2 = ld_tagged(src2 + tid);
+#pragma unroll
+        for (int e = 0; e < kPE; ++e) done &= (uint32_t)(v[e] >> 48) == t16;
+        done &= (uint32_t)(v2 >> 32) == tag;
+        if (done) break;
+        if ((++spin & 31) == 0 && timed_out(c)) {
+          st_u32(&c.a->err[0], 1);
+          ok = false;
+          break;
+        }
+      }
+      if (!ok) break;
+#pragma unroll
+      for (int e = 0; e < kPE; ++e) {
+        const int w = base + e * kThreads + tid;
+        if (w < nw) {
+          const float x0 = unf24(v[e] >> 24), x1 = unf24(v[e]);
+          if (split) {  // values 2w, 2w + 1: adjacent halves of the same 8-value block
+            uint32_t* d = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(dst) + (w >> 2) * 16 + ((2 * w) & 7));
+            const uint32_t h0 = bf16_rne(x0), h1 = bf16_rne(x1);
+            d[0] = (h0 & 0xFFFFu) | (h1 << 16);
+            d[4] = (bf16_rne(x0 - __uint_as_float(h0 << 16)) & 0xFFFFu) | (bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
+          } else {
+            dst[2 * w] = x0;
+            dst[2 * w + 1] = x1;
+          }
+          ss += x0 * x0 + x1 * x1;
+        }
+      }
+      if (base == 0 && tid < n2) dst2[tid] = __uint_as_float((uint32_t)v2);
+    }
+  }
+  for (int base = 0; ok && !packed && base < n; base += kPE * kThreads) {
     float gv[kPE];
     if (gain) {
 #pragma unroll
@@ -558,7 +622,6 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
     switch (kind) {
       case kQKV: st_tagged(a.QKV + r, bias ? t + ld_f(bias + r) : t, tag); break;
       case kOproj: st_tagged(a.X1 + r, xr[u] + t, tag); break;
-      case kGateUp: st_tagged(a.ACT + r, t, tag); break;
       default: st_tagged(a.X0 + r, xr[u] + t, tag_of(c.seq, l + 1)); break;
     }
   };
@@ -568,7 +631,7 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
     __syncthreads();
     // unit u: the 8 waves' partials of its row (and of its up row for pairs)
     const int nrows = c.r1 - c.r0;
-    for (int u = threadIdx.x; u < nrows; u += kThreads) {
+    auto unit = [&](int u) {
       const int b = min(u >> 4, tl.nb - 1);
       const int n = b * 16 + u - min(16 * b, nrows - 16);
       float y = 0.f, z = 0.f;
@@ -580,7 +643,12 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
         for (int w = 0; w < kWaves; ++w) z += sm.att[w * kTileRed + tl.nb * 16 + n];
         t = z * rs * t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));  // up * SiLU(gate)
       }
-      publish(u, t);
+      return t;
+    };
+    if (kind == kGateUp) {  // value pairs (the CU's units start at an even unit)
+      for (int u = 2 * threadIdx.x; u < nrows; u += 2 * kThreads) st_pair(a.ACT + ((c.r0 + u) >> 1), unit(u), unit(u + 1), tag);
+    } else {
+      for (int u = threadIdx.x; u < nrows; u += kThreads) publish(u, unit(u));
     }
     stamp(c, sm, 5 * l + kind, 2, threadIdx.x == 0);
     return;
@@ -616,7 +684,12 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
   }
   stamp(c, sm, 5 * l + kind, 2, threadIdx.x == 0);
   __syncthreads();
-  for (int u = threadIdx.x; u < g.nunits; u += kThreads) publish(u, sm.outv[u]);
+  if (kind == kGateUp) {
+    for (int u = 2 * threadIdx.x; u < g.nunits; u += 2 * kThreads)
+      st_pair(a.ACT + ((c.r0 + u) >> 1), sm.outv[u], sm.outv[u + 1], tag);
+  } else {
+    for (int u = threadIdx.x; u < g.nunits; u += kThreads) publish(u, sm.outv[u]);
+  }
 }
 
 // The attention item's per-lane constants that do not depend on the phase
@@ -1057,6 +1130,27 @@ __device__ __forceinline__ void final_phase(const Ctx& c, Smem& sm) {
   stamp(c, sm, ph, 5, lane == 0);
 }
 
+// Gate before a poll: lane 0 of wave 0 watches one word of the producer's own
+// input, sleeping between reads, while the other waves wait at the barrier;
+// once it carries tag `gtag` (or a later one) the producer is at work and the
+// full poll starts, so the input vector is not polled at full rate through
+// the whole wait.  Returns false when the step is abandoned.
+__device__ __forceinline__ bool gate(const Ctx& c, Smem& sm, const uint64_t* w, uint32_t gtag) {
+  if (threadIdx.x == 0) {
+    uint32_t spin = 0;
+    while ((int32_t)((uint32_t)(ld_tagged(w) >> 32) - gtag) < 0) {
+      if ((++spin & 7) == 0 && timed_out(c)) {
+        st_u32(&c.a->err[0], 1);
+        sm.abort_flag = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  lds_barrier();
+  return !sm.abort_flag;
+}
+
 template <int G, int HS>
 __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const PersistConst* __restrict__ pc,
                                                                    PersistStep stp) {
@@ -1082,8 +1176,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   c.rank = (int)blockIdx.x - stp.start[role];
   c.nrole = stp.start[role + 1] - stp.start[role];
   const int N = role == kQKV ? a.nqkv : role == kGateUp ? a.I : role == kAttn ? c.nrole : a.H;
-  c.r0 = (int)(((uint32_t)N * c.rank) / c.nrole);
-  c.r1 = (int)(((uint32_t)N * (c.rank + 1)) / c.nrole);
+  if (role == kGateUp) {  // even boundaries: the units are published as value pairs
+    c.r0 = 2 * (int)(((uint32_t)(N / 2) * c.rank) / c.nrole);
+    c.r1 = 2 * (int)(((uint32_t)(N / 2) * (c.rank + 1)) / c.nrole);
+  } else {
+    c.r0 = (int)(((uint32_t)N * c.rank) / c.nrole);
+    c.r1 = (int)(((uint32_t)N * (c.rank + 1)) / c.nrole);
+  }
   c.v0 = (int)(((uint32_t)a.V * blockIdx.x) / gridDim.x);
   c.v1 = (int)(((uint32_t)a.V * (blockIdx.x + 1)) / gridDim.x);
   const int L = a.L, H = a.H, tid = threadIdx.x;
@@ -1112,6 +1211,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
     }
     // ---- the phase input
     bool ok = true;
+    {  // the word the gate watches: the producer's input (f32 vectors only)
+      const uint64_t* gw = nullptr;
+      uint32_t gt = tag;
+      switch (role) {
+        case kQKV: if (l > 0) { gw = a.X1; gt = tag_of(c.seq, l - 1); } break;
+        case kAttn: if (l > 0) gw = a.X0; break;
+        case kOproj: gw = a.QKV; break;
+        case kGateUp: gw = a.O; break;
+        default: gw = a.X1; break;
+      }
+      if (gw && !gate(c, sm, gw, gt)) return;
+    }
     if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
       float ss = 0.f;
       const bool split = mfma_path(c);
@@ -1157,7 +1268,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
         case kGateUp: src = a.X1; n = H; gain = Lw.mlp_norm; break;
         default: src = a.ACT; n = a.I; src2 = a.X1 + c.r0; n2 = c.r1 - c.r0; break;
       }
-      ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, mfma_path(c));
+      ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, mfma_path(c), role == kDown);
     }
     if (!ok) return;
     stamp(c, sm, ph, 1, tid == 0);
@@ -1181,6 +1292,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
     const int ph = 5 * L;
     float rs;
     stamp(c, sm, ph, 0, tid == 0);
+    if (!gate(c, sm, a.X1, tag_of(c.seq, L - 1))) return;
     if (!poll(c, sm, L, a.X0, H, tag_of(c.seq, L), sm.vec[L & 1], a.final_norm, &rs, nullptr, 0, nullptr)) return;
     stamp(c, sm, ph, 1, tid == 0);
     if (blockIdx.x == 0 && a.xf_out)
@@ -1239,6 +1351,7 @@ int persist_prepare(int G, int hseg) {
 
 int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, PersistStep* out) {
   if (grid < 1 || pos < 0 || pos >= pc.max_pos || pc.nkv < 1) return -1;
+  if (pc.I % 2 != 0) return -1;  // the SwiGLU activations travel as value pairs
   const int ctx = pos + 1;
   // attention: splits no longer than the K/V rows a CU loads ahead, on at most half the grid
   const int smax = grid / (2 * pc.nkv);
