@@ -31,7 +31,7 @@
 // one workgroup barrier, then the phase's arithmetic.  A GEMV role multiplies
 // on the matrix cores: its rows form 16 x 32 bf16 tiles, the input enters as
 // the bf16 pair (hi, lo) in two rows of the other operand, and each wave
-// accumulates every eighth column chunk, the 8 partials of a row being added
+// accumulates its own column chunks, the 8 partials of a row being added
 // in LDS.  RMSNorm is folded in: the LDS input is gain * x and each row sum is
 // scaled by 1/RMS(x) afterwards.
 //
@@ -369,7 +369,7 @@ __device__ __forceinline__ Gemv gemv_of(const Ctx& c, int l) {
 // Matrix-core geometry of a GEMV role.  The CU's rows (per row set: gate and
 // up rows for pairs) form blocks of 16 (the last block shifted back to end at
 // the last row, overlapping its neighbour); the K columns form chunks of 32,
-// dealt to the 8 waves round robin (chunk w + 8 j goes to wave w).  A register
+// dealt to the 8 waves in pairs (see tile_chunk).  A register
 // slot holds one 16 x 32 tile: lane i has row i % 16, columns 8 (i / 16) ..
 // + 7.  The tiles of every wave fit in the registers loaded ahead.
 struct Tiles {
@@ -377,6 +377,10 @@ struct Tiles {
   int ns;   // row sets: 2 for gate/up pairs, else 1
   int nkw;  // chunks per wave (K / 256)
 };
+
+// The j-th chunk of wave w: chunk pairs 2 w, 2 w + 1 (both halves of a row's
+// 128-byte line), then 2 w + 16, 2 w + 17, ...
+__device__ __forceinline__ int tile_chunk(int w, int j) { return 16 * (j >> 1) + 2 * w + (j & 1); }
 
 __device__ __forceinline__ int gemv_k(const Ctx& c) {
   const AS4 PersistConst& a = *c.a;
@@ -470,7 +474,7 @@ __device__ __forceinline__ void gemv_addr(Addr<N>& ad, const Gemv& g, Walk w) {
 }
 
 // The tiles of this wave (see Tiles): slot bb nkw + j holds row block bb (row
-// set bb / nb) and chunk wave + 8 j; slots past the tiles repeat the last one.
+// set bb / nb) and chunk tile_chunk(wave, j); slots past the tiles repeat the last one.
 // Every row read lies inside the CU's own rows.
 template <int N>
 __device__ __forceinline__ void tile_addr(Addr<N>& ad, const Gemv& g, const Tiles& t, int nrows) {
@@ -484,7 +488,7 @@ __device__ __forceinline__ void tile_addr(Addr<N>& ad, const Gemv& g, const Tile
     const int bb = ii / t.nkw, j = ii - bb * t.nkw;
     const int set = bb / t.nb, b = bb - set * t.nb;
     const int row = min(16 * b, nrows - 16);
-    ad.soff[i] = (int)(((long)set * g.delta + (long)row * g.K + (wave + 8 * j) * 32) * 2);
+    ad.soff[i] = (int)(((long)set * g.delta + (long)row * g.K + tile_chunk(wave, j) * 32) * 2);
   }
 }
 
@@ -570,7 +574,7 @@ __device__ __forceinline__ void gemv_tiles(const Ctx& c, Smem& sm, const Regs<kF
   u32x4 xa[NKW];
 #pragma unroll
   for (int j = 0; j < NKW; ++j)  // 8 inputs as hi[8] then lo[8]: lane 1 of each 16 takes the lo half
-    xa[j] = *reinterpret_cast<const u32x4*>(h + (wave + 8 * j) * 32 + (lane >> 4) * 8 + ((lane & 15) == 1 ? 4 : 0));
+    xa[j] = *reinterpret_cast<const u32x4*>(h + tile_chunk(wave, j) * 32 + (lane >> 4) * 8 + ((lane & 15) == 1 ? 4 : 0));
   __builtin_amdgcn_sched_barrier(0);  // every LDS read in flight before the first product
   f32x4 acc[NBT];
 #pragma unroll
@@ -1176,7 +1180,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   c.rank = (int)blockIdx.x - stp.start[role];
   c.nrole = stp.start[role + 1] - stp.start[role];
   const int N = role == kQKV ? a.nqkv : role == kGateUp ? a.I : role == kAttn ? c.nrole : a.H;
-  if (role == kGateUp) {  // even boundaries: the units are published as value pairs
+  if (role != kAttn && N % 16 == 0 && N / 16 >= c.nrole) {  // whole 16-row tile blocks (no overlapping block)
+    c.r0 = 16 * (int)(((uint32_t)(N / 16) * c.rank) / c.nrole);
+    c.r1 = 16 * (int)(((uint32_t)(N / 16) * (c.rank + 1)) / c.nrole);
+  } else if (role == kGateUp) {  // even boundaries: the units are published as value pairs
     c.r0 = 2 * (int)(((uint32_t)(N / 2) * c.rank) / c.nrole);
     c.r1 = 2 * (int)(((uint32_t)(N / 2) * (c.rank + 1)) / c.nrole);
   } else {
