@@ -303,6 +303,27 @@ def test_tiny_persistent_split_beyond_lookahead(torch_cuda):
     assert_records(recs, max_forced=1)
 
 
+def test_tiny_persistent_row_segment_roles(torch_cuda):
+    """A shape whose o_proj (4 q heads: 512 columns) and down projection (1408
+    columns) do not form the matrix-core tiles, so those roles multiply on the
+    row-segment path with f32 inputs (the down role unpacking the activation
+    pairs to f32) while QKV and gate/up use the tiles; QKV bias on, no QK-norm.
+    8-token prompt, 16 greedy steps, every step checked."""
+    import dataclasses
+    shape = dataclasses.replace(synth.TINY, name="tiny-rowseg", n_q_heads=4, n_kv_heads=2, intermediate=1408,
+                                qk_norm=False, qkv_bias=True)
+    log("tiny, row-segment o_proj and down roles, persistent")
+    w = synth.make_weights(shape, seed=25, random_gains=True)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 16, path="persistent")
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = synth.make_prompt(shape.vocab, 8, seed=26)
+    recs = lockstep_greedy(dec, oracle, prompt, 16, log=log)
+    assert_records(recs)
+
+
 @pytest.mark.parametrize("n", [16, 137])
 def test_tiny_batched_prefill_matrix_cores(torch_cuda, n):
     """Prefills of >= 16 rows run the projections on the matrix cores (bf16 hi/lo
