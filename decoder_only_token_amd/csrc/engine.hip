@@ -447,6 +447,20 @@ size_t qd_sizeof_lora(void) { return sizeof(qd_lora); }
 
 const char* qd_last_error(const qd_handle* h) { return h ? h->err.c_str() : "NULL handle"; }
 
+// The persistent step's value-pair buffers (16-bit tags) to all ones: a tag
+// of layer 255, which no decoder layer uses, so no stale word matches.  A
+// null stream fills synchronously.
+static int fill_pairs(qd_handle* h, hipStream_t st) {
+  const qd_config& c = h->cfg;
+  struct { uint64_t* p; size_t words; } bufs[] = {{h->ACT, (size_t)c.intermediate},
+                                                  {h->Ox, (size_t)c.n_q_heads * c.head_dim}};
+  for (auto& b : bufs) {
+    const hipError_t e = st ? hipMemsetAsync(b.p, 0xFF, b.words * 8, st) : hipMemset(b.p, 0xFF, b.words * 8);
+    if (e != hipSuccess) return QD_E_HIP;
+  }
+  return QD_OK;
+}
+
 int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if (!out) return QD_E_ARG;
   *out = nullptr;
@@ -534,12 +548,11 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
         (rc = dev_alloc(h, &h->layer_ptrs, (size_t)c.n_layers)))
       return fail(rc);
     // tags start at 0; every step uses seq >= 1, so stale words never match.
-    // The activation pairs carry only 16 tag bits (8 of the step): they start
+    // The value-pair buffers carry only 16 tag bits (8 of the step): they start
     // as all ones (layer 255, never a decoder layer), and a reset refills them.
     if (hipMemset(h->X0, 0, H * 8) || hipMemset(h->X1, 0, H * 8) || hipMemset(h->QKVx, 0, qkv_rows(c) * 8) ||
-        hipMemset(h->PART, 0, (size_t)c.n_q_heads * smax * (d + 2) * 8) || hipMemset(h->Ox, 0, c.n_q_heads * d * 8) ||
-        hipMemset(h->ACT, 0xFF, I * 8) || hipMemset(h->AM, 0, h->grid * 16) ||
-        hipMemset(h->err_dev, 0, 16))
+        hipMemset(h->PART, 0, (size_t)c.n_q_heads * smax * (d + 2) * 8) || hipMemset(h->AM, 0, h->grid * 16) ||
+        hipMemset(h->err_dev, 0, 16) || fill_pairs(h, nullptr) != QD_OK)
       return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
   }
   if (hipMemset(h->st, 0, sizeof(DevState)) != hipSuccess) return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
@@ -684,7 +697,8 @@ int qd_reset_kv(qd_handle* h) {
   if (!h) return QD_E_ARG;
   HIP_TRY(h, hipMemsetAsync(h->st, 0, sizeof(DevState), h->stream));
   if (h->err_dev) HIP_TRY(h, hipMemsetAsync(h->err_dev, 0, 16, h->stream));
-  if (h->ACT) HIP_TRY(h, hipMemsetAsync(h->ACT, 0xFF, (size_t)h->cfg.intermediate * 8, h->stream));
+  if (h->ACT && fill_pairs(h, h->stream) != QD_OK)
+    return h->set_err(QD_E_HIP, "hipMemsetAsync of the value-pair buffers failed");
   h->failed = false;
   h->pos = 0;
   h->have_token = false;

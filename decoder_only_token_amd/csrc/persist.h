@@ -35,8 +35,8 @@ struct PersistConst {
   uint64_t* X1;    // [H] residual after attention
   uint64_t* QKV;   // [nqkv]
   uint64_t* PART;  // [nq][S][130] split partials {m, l, o[128]}
-  uint64_t* O;     // [nq * 128] attention output
-  uint64_t* ACT;   // [I]
+  uint64_t* O;     // [nq * 64] attention output, value pairs
+  uint64_t* ACT;   // [I / 2] SwiGLU activations, value pairs
   uint64_t* AM;    // [grid][2] per-CU {best logit, best id (bit pattern)}
   float* logits;   // [V]
   float* xf_out;   // [H] final-normed row (optional)

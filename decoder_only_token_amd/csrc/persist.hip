@@ -940,8 +940,10 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, Smem& sm, int l) {
       acc += ow[w] * f;
     }
     const int h = h0 + j;
-    if (S == 1) {
-      st_tagged(a.O + h * D + dd, acc / Ls, tag);
+    if (S == 1) {  // value pairs: the even lane stores its own and its neighbour's (dd ^ 1) value
+      const float v = acc / Ls;
+      const float vn = DPPF(v, 0xB1, 0xF);
+      if ((dd & 1) == 0) st_pair(a.O + ((h * D + dd) >> 1), v, vn, tag);
     } else {
       uint64_t* dst = a.PART + ((size_t)h * S + s) * (D + 2);
       st_tagged(dst + 2 + dd, acc, tag);
@@ -999,7 +1001,9 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, Smem& sm, int l) {
         }
       }
     }
-    if (ok && act) st_tagged(a.O + h * D + dd, acc / Ls, tag);
+    const float v = acc / Ls;
+    const float vn = DPPF(v, 0xB1, 0xF);  // dims dd, dd ^ 1 sit in neighbouring lanes
+    if (ok && act && (dd & 1) == 0) st_pair(a.O + ((h * D + dd) >> 1), v, vn, tag);
   }
   if (!ok) sm.abort_flag = 1;
   __syncthreads();
@@ -1139,10 +1143,13 @@ __device__ __forceinline__ void final_phase(const Ctx& c, Smem& sm) {
 // once it carries tag `gtag` (or a later one) the producer is at work and the
 // full poll starts, so the input vector is not polled at full rate through
 // the whole wait.  Returns false when the step is abandoned.
-__device__ __forceinline__ bool gate(const Ctx& c, Smem& sm, const uint64_t* w, uint32_t gtag) {
+__device__ __forceinline__ bool gate(const Ctx& c, Smem& sm, const uint64_t* w, uint32_t gtag, bool packed = false) {
   if (threadIdx.x == 0) {
     uint32_t spin = 0;
-    while ((int32_t)((uint32_t)(ld_tagged(w) >> 32) - gtag) < 0) {
+    auto early = [&](uint64_t v) {  // tag before gtag (packed words: 16-bit tags)
+      return packed ? (int16_t)(uint16_t)((uint32_t)(v >> 48) - gtag) < 0 : (int32_t)((uint32_t)(v >> 32) - gtag) < 0;
+    };
+    while (early(ld_tagged(w))) {
       if ((++spin & 7) == 0 && timed_out(c)) {
         st_u32(&c.a->err[0], 1);
         sm.abort_flag = 1;
@@ -1183,7 +1190,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   if (role != kAttn && N % 16 == 0 && N / 16 >= c.nrole) {  // whole 16-row tile blocks (no overlapping block)
     c.r0 = 16 * (int)(((uint32_t)(N / 16) * c.rank) / c.nrole);
     c.r1 = 16 * (int)(((uint32_t)(N / 16) * (c.rank + 1)) / c.nrole);
-  } else if (role == kGateUp) {  // even boundaries: the units are published as value pairs
+  } else if (role == kGateUp) {  // even boundaries: the activations travel as value pairs
     c.r0 = 2 * (int)(((uint32_t)(N / 2) * c.rank) / c.nrole);
     c.r1 = 2 * (int)(((uint32_t)(N / 2) * (c.rank + 1)) / c.nrole);
   } else {
@@ -1225,10 +1232,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
         case kQKV: if (l > 0) { gw = a.X1; gt = tag_of(c.seq, l - 1); } break;
         case kAttn: if (l > 0) gw = a.X0; break;
         case kOproj: gw = a.QKV; break;
-        case kGateUp: gw = a.O; break;
+        case kGateUp: gw = a.O; break;  // value pairs
         default: gw = a.X1; break;
       }
-      if (gw && !gate(c, sm, gw, gt)) return;
+      if (gw && !gate(c, sm, gw, gt, role == kGateUp)) return;
     }
     if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
       float ss = 0.f;
@@ -1275,7 +1282,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
         case kGateUp: src = a.X1; n = H; gain = Lw.mlp_norm; break;
         default: src = a.ACT; n = a.I; src2 = a.X1 + c.r0; n2 = c.r1 - c.r0; break;
       }
-      ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, mfma_path(c), role == kDown);
+      ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, mfma_path(c), role == kOproj || role == kDown);
     }
     if (!ok) return;
     stamp(c, sm, ph, 1, tid == 0);
@@ -1384,9 +1391,11 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
   lo[3] = lo[1];
   for (int r = 0; r < 4; ++r) lo[r] = std::max(lo[r], (N[r] + kOutMax - 1) / kOutMax);  // outputs fit too
   if ((pc.V + grid - 1) / grid > kOutMax) return -1;
+  // gate/up publishes value pairs: every CU of it owns at least one pair
+  const int cap[4] = {N[0], N[1], N[2] / 2, N[3]};
   int lo_sum = 0, tmax = 0;
   for (int r = 0; r < 4; ++r) {
-    if (N[r] < lo[r]) return -1;
+    if (cap[r] < lo[r]) return -1;
     lo_sum += lo[r];
     tmax = std::max(tmax, wave_segs((N[r] + lo[r] - 1) / lo[r], rpu[r], ns[r]));
   }
@@ -1403,7 +1412,7 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
         fits = false;
         break;
       }
-      m[r] = std::min(N[r], std::max(lo[r], (N[r] + kWaves * per - 1) / (kWaves * per)));
+      m[r] = std::min(cap[r], std::max(lo[r], (N[r] + kWaves * per - 1) / (kWaves * per)));
       sum += m[r];
     }
     if (fits && sum <= R) {
@@ -1415,7 +1424,7 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
     int best = -1;
     double bw = -1.0;
     for (int r = 0; r < 4; ++r) {
-      if (n[r] >= N[r]) continue;
+      if (n[r] >= cap[r]) continue;
       const double w = (double)N[r] * rpu[r] * ns[r] / n[r];
       if (w > bw) {
         bw = w;
