@@ -440,6 +440,7 @@ struct Addr {
   __amdgpu_buffer_rsrc_t rs[2];
   int voff;
   int soff[N];
+  int n = N;  // slots to load (wave-uniform); the others keep stale values and are not used
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
@@ -450,8 +451,9 @@ template <int N>
 __device__ __forceinline__ void load_regs(Regs<N>& rg, const Addr<N>& ad) {
 #pragma unroll
   for (int i = 0; i < N; ++i)
-    rg.R[i] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.rs[i < N / 2 ? 0 : 1], ad.voff, ad.soff[i], 2 /* nt */));
+    if (i < ad.n)
+      rg.R[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.rs[i < N / 2 ? 0 : 1], ad.voff, ad.soff[i], 2 /* nt */));
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
@@ -474,7 +476,7 @@ __device__ __forceinline__ void gemv_addr(Addr<N>& ad, const Gemv& g, Walk w) {
 }
 
 // The tiles of this wave (see Tiles): slot bb nkw + j holds row block bb (row
-// set bb / nb) and chunk tile_chunk(wave, j); slots past the tiles repeat the last one.
+// set bb / nb) and chunk tile_chunk(wave, j); slots past the tiles are not loaded.
 // Every row read lies inside the CU's own rows.
 template <int N>
 __device__ __forceinline__ void tile_addr(Addr<N>& ad, const Gemv& g, const Tiles& t, int nrows) {
@@ -482,6 +484,7 @@ __device__ __forceinline__ void tile_addr(Addr<N>& ad, const Gemv& g, const Tile
   const int lane = threadIdx.x & 63, wave = wave_id();
   ad.voff = (lane & 15) * g.K * 2 + (lane >> 4) * 16;
   const int T = t.ns * t.nb * t.nkw;
+  ad.n = T;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int ii = min(i, T - 1);
