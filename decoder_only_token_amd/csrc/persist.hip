@@ -562,7 +562,7 @@ __device__ __forceinline__ Addr<kFirst> ahead_addr(const Ctx& c, int l) {
 // ------------------------------------------------------------------- phases
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kTileRed = 96;  // LDS floats per wave for the tile partials (6 blocks of 16 rows)
+constexpr int kTileRed = 96;  // tile rows a CU's partials cover (6 blocks of 16 rows)
 
 // GEMV tiles on the matrix cores (see Tiles).  Each 16 x 16 x 32 product takes
 // one input chunk of the wave as operand A, whose rows 0 and 1 are the bf16
@@ -573,6 +573,7 @@ constexpr int kTileRed = 96;  // LDS floats per wave for the tile partials (6 bl
 template <int NKW, int NBT>
 __device__ __forceinline__ void gemv_tiles(const Ctx& c, Smem& sm, const Regs<kFirst>& rg, const float* h, int l) {
   static_assert(NKW * NBT <= kFirst && NBT * 16 <= kTileRed, "tiles fit the registers and the LDS partials");
+  static_assert(kTileRed * kWaves <= sizeof(Smem::att) / sizeof(float), "the partials fit the scratch");
   const int lane = threadIdx.x & 63, wave = wave_id();
   u32x4 xa[NKW];
 #pragma unroll
@@ -589,10 +590,9 @@ __device__ __forceinline__ void gemv_tiles(const Ctx& c, Smem& sm, const Regs<kF
       acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[j]),
                                                         __builtin_bit_cast(bf16x8_t, rg.R[bb * NKW + j]), acc[bb], 0, 0, 0);
   stamp(c, sm, 5 * l + c.role, 6, threadIdx.x == 0);
-  float* red = sm.att + wave * kTileRed;
-  if (lane < 16) {
+  if (lane < 16) {  // partial of row bb * 16 + lane at [row][wave]: a row's 8 partials are contiguous
 #pragma unroll
-    for (int bb = 0; bb < NBT; ++bb) red[bb * 16 + lane] = acc[bb].x + acc[bb].y;
+    for (int bb = 0; bb < NBT; ++bb) sm.att[(bb * 16 + lane) * kWaves + wave] = acc[bb].x + acc[bb].y;
   }
 }
 
@@ -638,18 +638,16 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
     __syncthreads();
     // unit u: the 8 waves' partials of its row (and of its up row for pairs)
     const int nrows = c.r1 - c.r0;
+    auto sum8 = [&](int row) {  // the 8 wave partials of a tile row, in a fixed order
+      const f32x4 p = *reinterpret_cast<const f32x4*>(sm.att + row * kWaves);
+      const f32x4 q = *reinterpret_cast<const f32x4*>(sm.att + row * kWaves + 4);
+      return ((p.x + p.y) + (p.z + p.w)) + ((q.x + q.y) + (q.z + q.w));
+    };
     auto unit = [&](int u) {
       const int b = min(u >> 4, tl.nb - 1);
       const int n = b * 16 + u - min(16 * b, nrows - 16);
-      float y = 0.f, z = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) y += sm.att[w * kTileRed + n];
-      float t = y * rs;
-      if (tl.ns == 2) {
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) z += sm.att[w * kTileRed + tl.nb * 16 + n];
-        t = z * rs * t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));  // up * SiLU(gate)
-      }
+      float t = sum8(n) * rs;
+      if (tl.ns == 2) t = sum8(tl.nb * 16 + n) * rs * t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));  // up * SiLU(gate)
       return t;
     };
     if (kind == kGateUp) {  // value pairs (the CU's units start at an even unit)
