@@ -610,33 +610,28 @@ __device__ __forceinline__ void gemv_tiles_any(const Ctx& c, Smem& sm, const Til
 #undef QD_TILES
 }
 
-// GEMV role: this CU's rows, from the registers loaded ahead (and, on the
-// row-segment path, streamed batches for any rest), published one word per
-// output row.
-__device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, float rs,
-                                           const Gemv& g, const float* bias) {
+// Output row u of a GEMV role: publishing is every unit at once, one word
+// per thread, so a wave's stores cover whole cache lines (single-word stores
+// spread over lines reach the pollers much later).
+__device__ __forceinline__ void publish_row(const Ctx& c, Smem& sm, int l, int u, float t, const float* bias) {
   const AS4 PersistConst& a = *c.a;
-  const int lane = threadIdx.x & 63, wave = wave_id(), kind = c.role;
-  const float* h = sm.vec[l & 1];
   const float* xr = sm.xres[l & 1];
+  const int r = c.r0 + u;
+  switch (c.role) {
+    case kQKV: st_tagged(a.QKV + r, bias ? t + ld_f(bias + r) : t, tag_of(c.seq, l)); break;
+    case kOproj: st_tagged(a.X1 + r, xr[u] + t, tag_of(c.seq, l)); break;
+    default: st_tagged(a.X0 + r, xr[u] + t, tag_of(c.seq, l + 1)); break;
+  }
+}
+
+// Matrix-core GEMV, after the barrier that follows the products: unit u sums
+// the 8 waves' partials of its row (and of its up row for pairs) and
+// publishes.
+__device__ __forceinline__ void tiles_finish(const Ctx& c, Smem& sm, int l, const Tiles& tl, float rs, const float* bias) {
+  const AS4 PersistConst& a = *c.a;
+  const int kind = c.role;
   const uint32_t tag = tag_of(c.seq, l);
-  stamp(c, sm, 5 * l + kind, 4, threadIdx.x == 0);
-  // Publishing: every unit at once, one word per thread, so a wave's stores
-  // cover whole cache lines (single-word stores spread over lines reach the
-  // pollers much later).
-  auto publish = [&](int u, float t) {
-    const int r = c.r0 + u;
-    switch (kind) {
-      case kQKV: st_tagged(a.QKV + r, bias ? t + ld_f(bias + r) : t, tag); break;
-      case kOproj: st_tagged(a.X1 + r, xr[u] + t, tag); break;
-      default: st_tagged(a.X0 + r, xr[u] + t, tag_of(c.seq, l + 1)); break;
-    }
-  };
-  Tiles tl;
-  if (mfma_path(c, &tl)) {
-    gemv_tiles_any(c, sm, tl, rg, h, l);
-    __syncthreads();
-    // unit u: the 8 waves' partials of its row (and of its up row for pairs)
+  {
     const int nrows = c.r1 - c.r0;
     auto sum8 = [&](int row) {  // the 8 wave partials of a tile row, in a fixed order
       const f32x4 p = *reinterpret_cast<const f32x4*>(sm.att + row * kWaves);
@@ -653,9 +648,27 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
     if (kind == kGateUp) {  // value pairs (the CU's units start at an even unit)
       for (int u = 2 * threadIdx.x; u < nrows; u += 2 * kThreads) st_pair(a.ACT + ((c.r0 + u) >> 1), unit(u), unit(u + 1), tag);
     } else {
-      for (int u = threadIdx.x; u < nrows; u += kThreads) publish(u, unit(u));
+      for (int u = threadIdx.x; u < nrows; u += kThreads) publish_row(c, sm, l, u, unit(u), bias);
     }
     stamp(c, sm, 5 * l + kind, 2, threadIdx.x == 0);
+  }
+}
+
+// GEMV role: this CU's rows, from the registers loaded ahead (and, on the
+// row-segment path, streamed batches for any rest), published one word per
+// output row.
+__device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, float rs,
+                                           const Gemv& g, const float* bias) {
+  const AS4 PersistConst& a = *c.a;
+  const int lane = threadIdx.x & 63, wave = wave_id(), kind = c.role;
+  const float* h = sm.vec[l & 1];
+  const uint32_t tag = tag_of(c.seq, l);
+  stamp(c, sm, 5 * l + kind, 4, threadIdx.x == 0);
+  Tiles tl;
+  if (mfma_path(c, &tl)) {
+    gemv_tiles_any(c, sm, tl, rg, h, l);
+    __syncthreads();
+    tiles_finish(c, sm, l, tl, rs, bias);
     return;
   }
   Walk w{wave, 0, 0};
@@ -693,8 +706,133 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const 
     for (int u = 2 * threadIdx.x; u < g.nunits; u += 2 * kThreads)
       st_pair(a.ACT + ((c.r0 + u) >> 1), sm.outv[u], sm.outv[u + 1], tag);
   } else {
-    for (int u = threadIdx.x; u < g.nunits; u += kThreads) publish(u, sm.outv[u]);
+    for (int u = threadIdx.x; u < g.nunits; u += kThreads) publish_row(c, sm, l, u, sm.outv[u], bias);
   }
+}
+
+// Matrix-core GEMV role with a per-wave input (QKV from layer 1, o_proj,
+// gate/up, down): no workgroup barrier between the poll and the products.
+// Every wave watches its own gate word, polls only the input words of its
+// column chunks (value pairs for o_proj and down, f32 for the normed QKV and
+// gate/up inputs), stages them as bf16 halves for its own A operands and
+// multiplies; it also polls its share of the residual rows and keeps its part
+// of the input's sum of squares.  One barrier, then the rows are finished.
+// Returns false when the step is abandoned.
+constexpr int kWE = 6;  // input words per lane at most (12 chunks of 32 f32 values over 64 lanes)
+
+__device__ __forceinline__ bool gemv_waves(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, const Tiles& tl,
+                                           const float* bias) {
+  const AS4 PersistConst& a = *c.a;
+  const AS4 LayerPtrs& Lw = ((const AS4 LayerPtrs*)a.layers)[l];
+  const int lane = threadIdx.x & 63, wave = wave_id(), kind = c.role, nrows = c.r1 - c.r0;
+  const uint32_t tag = tag_of(c.seq, l), t16 = tag & 0xFFFFu;
+  float* h = sm.vec[l & 1];
+  float* xr = sm.xres[l & 1];
+  const uint64_t* src;
+  const uint64_t* gw;
+  const float* gain = nullptr;
+  const uint64_t* src2 = nullptr;
+  uint32_t gt = tag;
+  bool packed = true, gpk = false;
+  switch (kind) {
+    case kQKV: src = a.X0; gain = Lw.attn_norm; packed = false; gw = a.X1; gt = tag_of(c.seq, l - 1); break;
+    case kOproj: src = a.O; gw = a.QKV; if (l > 0) src2 = a.X0 + c.r0; break;
+    case kGateUp: src = a.X1; gain = Lw.mlp_norm; packed = false; gw = a.O; gpk = true; break;
+    default: src = a.ACT; gw = a.X1; src2 = a.X1 + c.r0; break;
+  }
+  if (kind == kOproj && l == 0)  // layer 0: the residual is the embedding row
+    for (int r = threadIdx.x; r < nrows; r += kThreads) xr[r] = bf16_to_f(*gl(a.embed + (size_t)gl(a.st)->token * a.H + c.r0 + r));
+  bool ok = true;
+  if (lane == 0) {  // the wave's gate (the other lanes wait for lane 0)
+    uint32_t spin = 0;
+    for (;;) {
+      const uint64_t v = ld_tagged(gw);
+      if (gpk ? (int16_t)(uint16_t)((uint32_t)(v >> 48) - gt) >= 0 : (int32_t)((uint32_t)(v >> 32) - gt) >= 0) break;
+      if ((++spin & 7) == 0 && timed_out(c)) {
+        st_u32(&c.a->err[0], 1);
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+  // the wave's words: q = 64 e + lane < W; chunk j = q / per, word per * tile_chunk(wave, j) + q % per
+  const int per = packed ? 16 : 32, W = tl.nkw * per;
+  int widx[kWE];
+  float gv[kWE];
+#pragma unroll
+  for (int e = 0; e < kWE; ++e) {
+    const int q = 64 * e + lane;
+    widx[e] = q < W ? per * tile_chunk(wave, q / per) + q % per : -1;
+    gv[e] = gain && widx[e] >= 0 ? ld_f(gain + widx[e]) : 1.f;
+  }
+  const int ri = wave * 64 + lane;  // residual row of this thread (rows per CU <= 512)
+  const bool has2 = src2 && ri < nrows;
+  uint64_t v[kWE], v2 = 0;
+  uint32_t spin = 0;
+  while (ok) {
+    bool done = true;
+#pragma unroll
+    for (int e = 0; e < kWE; ++e) {
+      if (widx[e] >= 0) {
+        v[e] = ld_tagged(src + widx[e]);
+        done &= packed ? (uint32_t)(v[e] >> 48) == t16 : (uint32_t)(v[e] >> 32) == tag;
+      }
+    }
+    if (has2) {
+      v2 = ld_tagged(src2 + ri);
+      done &= (uint32_t)(v2 >> 32) == tag;
+    }
+    if (__all(done)) break;
+    if ((++spin & 31) == 0 && timed_out(c)) {
+      st_u32(&c.a->err[0], 1);
+      ok = false;
+    }
+  }
+  float ss = 0.f;
+  if (ok) {
+#pragma unroll
+    for (int e = 0; e < kWE; ++e) {
+      if (widx[e] < 0) continue;
+      if (packed) {  // values 2w, 2w + 1: adjacent halves of the same 8-value block
+        const int w = widx[e];
+        const float x0 = unf24(v[e] >> 24), x1 = unf24(v[e]);
+        uint32_t* d = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(h) + (w >> 2) * 16 + ((2 * w) & 7));
+        const uint32_t h0 = bf16_rne(x0), h1 = bf16_rne(x1);
+        d[0] = (h0 & 0xFFFFu) | (h1 << 16);
+        d[4] = (bf16_rne(x0 - __uint_as_float(h0 << 16)) & 0xFFFFu) | (bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
+      } else {  // bf16 halves of gain * x: hi[8] then lo[8] per 8 values
+        const int i = widx[e];
+        const float x = __uint_as_float((uint32_t)v[e]);
+        const float y = x * gv[e];
+        uint16_t* d = reinterpret_cast<uint16_t*>(h) + (i >> 3) * 16 + (i & 7);
+        const uint32_t hb = bf16_rne(y);
+        d[0] = (uint16_t)hb;
+        d[8] = (uint16_t)bf16_rne(y - __uint_as_float(hb << 16));
+        ss += x * x;
+      }
+    }
+    if (has2) xr[ri] = __uint_as_float((uint32_t)v2);
+  } else {
+    sm.abort_flag = 1;
+  }
+  stamp(c, sm, 5 * l + kind, 1, threadIdx.x == 0);
+  Tiles t2 = tl;
+  if (ok) gemv_tiles_any(c, sm, t2, rg, h, l);
+  const float wsum = wave_total(ss);
+  if (lane == 0) sm.red[((5 * l + kind) & 1) * 8 + wave] = wsum;
+  __syncthreads();
+  if (sm.abort_flag) return false;
+  float rs = 1.f;
+  if (gain) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) t += sm.red[((5 * l + kind) & 1) * 8 + i];
+    rs = rsqrtf(t / (float)a.H + c.eps);
+  }
+  tiles_finish(c, sm, l, tl, rs, bias);
+  return true;
 }
 
 // The attention item's per-lane constants that do not depend on the phase
@@ -1224,77 +1362,82 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
       gv = gemv_of(c, l);
       if (role == kQKV) bias = Lw.bqkv;
     }
-    // ---- the phase input
-    bool ok = true;
-    {  // the word the gate watches: the producer's input (f32 vectors only)
-      const uint64_t* gw = nullptr;
-      uint32_t gt = tag;
-      switch (role) {
-        case kQKV: if (l > 0) { gw = a.X1; gt = tag_of(c.seq, l - 1); } break;
-        case kAttn: if (l > 0) gw = a.X0; break;
-        case kOproj: gw = a.QKV; break;
-        case kGateUp: gw = a.O; break;  // value pairs
-        default: gw = a.X1; break;
-      }
-      if (gw && !gate(c, sm, gw, gt, role == kGateUp)) return;
-    }
-    if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
-      float ss = 0.f;
-      const bool split = mfma_path(c);
-      for (int k = tid; k < H; k += kThreads) {
-        const float x = bf16_to_f(*gl(emb + k));
-        const float y = x * ld_f(Lw.attn_norm + k);
-        if (split) {
-          uint16_t* d = reinterpret_cast<uint16_t*>(vin) + (k >> 3) * 16 + (k & 7);
-          const uint32_t hb = bf16_rne(y);
-          d[0] = (uint16_t)hb;
-          d[8] = (uint16_t)bf16_rne(y - __uint_as_float(hb << 16));
-        } else {
-          vin[k] = y;
+    // ---- the phase input and the compute
+    Tiles tw;
+    if (role != kAttn && !(l == 0 && role == kQKV) && mfma_path(c, &tw)) {
+      if (!gemv_waves(c, sm, l, rg, tw, bias)) return;  // per-wave input, matrix-core rows
+    } else {
+      bool ok = true;
+      {  // the word the gate watches: the producer's input (f32 vectors only)
+        const uint64_t* gw = nullptr;
+        uint32_t gt = tag;
+        switch (role) {
+          case kQKV: if (l > 0) { gw = a.X1; gt = tag_of(c.seq, l - 1); } break;
+          case kAttn: if (l > 0) gw = a.X0; break;
+          case kOproj: gw = a.QKV; break;
+          case kGateUp: gw = a.O; break;  // value pairs
+          default: gw = a.X1; break;
         }
-        ss += x * x;
+        if (gw && !gate(c, sm, gw, gt, role == kGateUp)) return;
       }
-      const float wsum = wave_total(ss);
-      if ((tid & 63) == 0) sm.red[tid >> 6] = wsum;
-      __syncthreads();
-      float t = 0.f;
-#pragma unroll
-      for (int i = 0; i < kWaves; ++i) t += sm.red[i];
-      rs = rsqrtf(t / (float)H + a.eps);
-    } else {
-      const uint64_t* src;
-      const uint64_t* src2 = nullptr;
-      const float* gain = nullptr;
-      int n, n2 = 0;
-      float* dst = vin;
-      switch (role) {
-        case kQKV: src = a.X0; n = H; gain = Lw.attn_norm; break;
-        case kAttn: src = a.QKV + (size_t)(c.rank / (c.X * c.S)) * (G + 2) * D; n = (G + 2) * D; dst = sm.qk; break;
-        case kOproj:
-          src = a.O;
-          n = a.nq * D;
-          if (l == 0) {
-            for (int r = tid; r < c.r1 - c.r0; r += kThreads) xr[r] = bf16_to_f(*gl(emb + c.r0 + r));
+      if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
+        float ss = 0.f;
+        const bool split = mfma_path(c);
+        for (int k = tid; k < H; k += kThreads) {
+          const float x = bf16_to_f(*gl(emb + k));
+          const float y = x * ld_f(Lw.attn_norm + k);
+          if (split) {
+            uint16_t* d = reinterpret_cast<uint16_t*>(vin) + (k >> 3) * 16 + (k & 7);
+            const uint32_t hb = bf16_rne(y);
+            d[0] = (uint16_t)hb;
+            d[8] = (uint16_t)bf16_rne(y - __uint_as_float(hb << 16));
           } else {
-            src2 = a.X0 + c.r0;
-            n2 = c.r1 - c.r0;
+            vin[k] = y;
           }
-          break;
-        case kGateUp: src = a.X1; n = H; gain = Lw.mlp_norm; break;
-        default: src = a.ACT; n = a.I; src2 = a.X1 + c.r0; n2 = c.r1 - c.r0; break;
+          ss += x * x;
+        }
+        const float wsum = wave_total(ss);
+        if ((tid & 63) == 0) sm.red[tid >> 6] = wsum;
+        __syncthreads();
+        float t = 0.f;
+  #pragma unroll
+        for (int i = 0; i < kWaves; ++i) t += sm.red[i];
+        rs = rsqrtf(t / (float)H + a.eps);
+      } else {
+        const uint64_t* src;
+        const uint64_t* src2 = nullptr;
+        const float* gain = nullptr;
+        int n, n2 = 0;
+        float* dst = vin;
+        switch (role) {
+          case kQKV: src = a.X0; n = H; gain = Lw.attn_norm; break;
+          case kAttn: src = a.QKV + (size_t)(c.rank / (c.X * c.S)) * (G + 2) * D; n = (G + 2) * D; dst = sm.qk; break;
+          case kOproj:
+            src = a.O;
+            n = a.nq * D;
+            if (l == 0) {
+              for (int r = tid; r < c.r1 - c.r0; r += kThreads) xr[r] = bf16_to_f(*gl(emb + c.r0 + r));
+            } else {
+              src2 = a.X0 + c.r0;
+              n2 = c.r1 - c.r0;
+            }
+            break;
+          case kGateUp: src = a.X1; n = H; gain = Lw.mlp_norm; break;
+          default: src = a.ACT; n = a.I; src2 = a.X1 + c.r0; n2 = c.r1 - c.r0; break;
+        }
+        ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, mfma_path(c), role == kOproj || role == kDown);
       }
-      ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, mfma_path(c), role == kOproj || role == kDown);
-    }
-    if (!ok) return;
-    stamp(c, sm, ph, 1, tid == 0);
-    // ---- compute from the registers loaded a layer ahead
-    if (role == kAttn) {
-      attn_phase<G>(c, sm, l, rg, pre);
-      stamp(c, sm, ph, 2, tid == 0);
-      if (!attn_finish<G>(c, sm, l)) return;
-      attn_cache_write<G>(c, sm, l);
-    } else {
-      gemv_phase(c, sm, l, rg, rs, gv, bias);
+      if (!ok) return;
+      stamp(c, sm, ph, 1, tid == 0);
+      // ---- compute from the registers loaded a layer ahead
+      if (role == kAttn) {
+        attn_phase<G>(c, sm, l, rg, pre);
+        stamp(c, sm, ph, 2, tid == 0);
+        if (!attn_finish<G>(c, sm, l)) return;
+        attn_cache_write<G>(c, sm, l);
+      } else {
+        gemv_phase(c, sm, l, rg, rs, gv, bias);
+      }
     }
     stamp(c, sm, ph, 3, tid == 0);
     // the single load site: the next layer's slice (after the last layer, the
