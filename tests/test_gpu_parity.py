@@ -13,7 +13,7 @@ import pytest
 import synth
 from oracle import OracleModel
 
-from gpu_util import lockstep_greedy, logits_within_tol, sampling_mismatch_explained, to_device
+from gpu_util import lockstep_greedy, logits_within_tol, near_tie, sampling_mismatch_explained, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -322,6 +322,44 @@ def test_tiny_persistent_row_segment_roles(torch_cuda):
     prompt = synth.make_prompt(shape.vocab, 8, seed=26)
     recs = lockstep_greedy(dec, oracle, prompt, 16, log=log)
     assert_records(recs)
+
+
+def test_tiny_persistent_300_steps_across_tag_wrap(torch_cuda):
+    """300 persistent decode steps: the value-pair buffers (SwiGLU activations,
+    attention output) carry only 8 bits of the step number in their tags, so
+    the step count wraps past 256 here, and past 192 positions the attention
+    splits in two.  The GPU's own greedy tokens are fed to the oracle as one
+    sequence: every token must be the argmax of the oracle's logits at its
+    step (near-ties allowed), and the last three steps' logits are checked."""
+    import torch
+    shape = dataclasses.replace(synth.TINY, max_pos=320)
+    log("tiny, 300 persistent decode steps")
+    w = synth.make_weights(shape, seed=27, random_gains=True)
+    dec = make_decoder(torch_cuda, shape, 16, path="persistent")
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = synth.make_prompt(shape.vocab, 8, seed=28)
+    buf = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    dec.prefill(prompt, token_out=tok)
+    torch.cuda.synchronize()
+    toks = [int(tok.item())]
+    last = []
+    for step in range(300):
+        dec.decode_step(logits_out=buf, token_out=tok)
+        torch.cuda.synchronize()
+        toks.append(int(tok.item()))
+        if step >= 297:
+            last.append(buf.cpu().numpy().astype(np.float64))
+    seq = list(prompt) + toks[:-1]  # every token the GPU consumed, in order
+    want = OracleModel(shape, w).forward(seq)  # one logits row per consumed token
+    bad = [k for k, t in enumerate(toks) if not near_tie(want[len(prompt) - 1 + k], t)]
+    assert not bad, f"tokens that are not their step's argmax at steps {bad[:8]}"
+    for i, got in enumerate(last):
+        ok, ratio, nbad = logits_within_tol(got, want[len(seq) - 3 + i])
+        log(f"step {297 + i}: err/tol {ratio:.3f}")
+        assert ok, (297 + i, ratio, nbad)
 
 
 @pytest.mark.parametrize("n", [16, 137])
