@@ -748,12 +748,12 @@ __device__ __forceinline__ bool gemv_waves(const Ctx& c, Smem& sm, int l, const 
     for (;;) {
       const uint64_t v = ld_tagged(gw);
       if (gpk ? (int16_t)(uint16_t)((uint32_t)(v >> 48) - gt) >= 0 : (int32_t)((uint32_t)(v >> 32) - gt) >= 0) break;
-      if ((++spin & 7) == 0 && timed_out(c)) {
+      if ((++spin & 3) == 0 && timed_out(c)) {
         st_u32(&c.a->err[0], 1);
         ok = false;
         break;
       }
-      __builtin_amdgcn_s_sleep(8);
+      __builtin_amdgcn_s_sleep(32);
     }
   }
   ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
@@ -1289,12 +1289,12 @@ __device__ __forceinline__ bool gate(const Ctx& c, Smem& sm, const uint64_t* w, 
       return packed ? (int16_t)(uint16_t)((uint32_t)(v >> 48) - gtag) < 0 : (int32_t)((uint32_t)(v >> 32) - gtag) < 0;
     };
     while (early(ld_tagged(w))) {
-      if ((++spin & 7) == 0 && timed_out(c)) {
+      if ((++spin & 3) == 0 && timed_out(c)) {
         st_u32(&c.a->err[0], 1);
         sm.abort_flag = 1;
         break;
       }
-      __builtin_amdgcn_s_sleep(8);
+      __builtin_amdgcn_s_sleep(32);
     }
   }
   lds_barrier();
