@@ -27,13 +27,20 @@
 // then all CUs take the final RMSNorm + tied LM head with per-CU argmax
 // partials, and CU 0 the argmax over the partials, advancing the step state.
 //
-// Every phase: all 512 threads poll the input (a few values each) into LDS,
-// one workgroup barrier, then the phase's arithmetic.  A GEMV role multiplies
-// on the matrix cores: its rows form 16 x 32 bf16 tiles, the input enters as
-// the bf16 pair (hi, lo) in two rows of the other operand, and each wave
-// accumulates its own column chunks, the 8 partials of a row being added
-// in LDS.  RMSNorm is folded in: the LDS input is gain * x and each row sum is
-// scaled by 1/RMS(x) afterwards.
+// Inputs.  Before polling at full rate a CU watches one word of its
+// producer's own input (a gate).  The attention role (and shapes that do not
+// form matrix-core tiles) then polls its whole input with all 512 threads
+// into LDS, followed by one workgroup barrier.  A matrix-core GEMV role polls
+// per wave instead: each wave takes only the input words of its own column
+// chunks, so no barrier separates the input from the products.  The SwiGLU
+// activations and the attention output travel as value pairs (two values to
+// 16 significant bits per word), halving the words those consumers poll.
+//
+// GEMV on the matrix cores: a role's rows form 16 x 32 bf16 tiles, the input
+// enters as the bf16 pair (hi, lo) in two rows of the other operand, and each
+// wave accumulates its own column chunks, the 8 partials of a row being added
+// in LDS after the one barrier.  RMSNorm is folded in: the LDS input is
+// gain * x and each row sum is scaled by 1/RMS(x) afterwards.
 //
 // The fused QKV rows are stored group-major ([kv head g][q heads of g | k_g |
 // v_g] x 128), so one attention item reads one contiguous run.
