@@ -208,11 +208,9 @@ __device__ __forceinline__ bool timed_out(const Ctx& c) {
 // LDS copy is gain[k] * x[k] and *rs receives 1 / sqrt(mean(x^2) + eps), the
 // RMSNorm scale, applied to the row sums later.  Ends with a workgroup
 // barrier; returns false on every thread when the step is abandoned.  With
-// `split`, the LDS copy is the bf16 pair (hi, lo) with hi + lo = the value to
-// about 16 significant bits, stored per 8 values as hi[8] then lo[8] (the
-// same 32 bytes as 8 floats), for the bf16 dot-product path.
+// `packed`, src holds n / 2 words of value pairs.
 __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint64_t* src, int n, uint32_t tag, float* dst,
-                     const float* gain, float* rs, const uint64_t* src2, int n2, float* dst2, bool split = false,
+                     const float* gain, float* rs, const uint64_t* src2, int n2, float* dst2,
                      bool packed = false) {
   const int tid = threadIdx.x;
   bool ok = !sm.abort_flag;
@@ -247,15 +245,8 @@ __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint6
         const int w = base + e * kThreads + tid;
         if (w < nw) {
           const float x0 = unf24(v[e] >> 24), x1 = unf24(v[e]);
-          if (split) {  // values 2w, 2w + 1: adjacent halves of the same 8-value block
-            uint32_t* d = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(dst) + (w >> 2) * 16 + ((2 * w) & 7));
-            const uint32_t h0 = bf16_rne(x0), h1 = bf16_rne(x1);
-            d[0] = (h0 & 0xFFFFu) | (h1 << 16);
-            d[4] = (bf16_rne(x0 - __uint_as_float(h0 << 16)) & 0xFFFFu) | (bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
-          } else {
-            dst[2 * w] = x0;
-            dst[2 * w + 1] = x1;
-          }
+          dst[2 * w] = x0;
+          dst[2 * w + 1] = x1;
           ss += x0 * x0 + x1 * x1;
         }
       }
@@ -299,14 +290,7 @@ __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint6
       if (i < n) {
         const float x = __uint_as_float((uint32_t)v[e]);
         const float y = gain ? x * gv[e] : x;
-        if (split) {  // bf16 halves y = hi + lo; 8 values per 32 bytes: hi[8] then lo[8]
-          uint16_t* d = reinterpret_cast<uint16_t*>(dst) + (i >> 3) * 16 + (i & 7);
-          const uint32_t hb = bf16_rne(y);
-          d[0] = (uint16_t)hb;
-          d[8] = (uint16_t)bf16_rne(y - __uint_as_float(hb << 16));
-        } else {
-          dst[i] = y;
-        }
+        dst[i] = y;
         ss += x * x;
       }
     }
@@ -803,18 +787,20 @@ __device__ __forceinline__ bool gemv_waves(const Ctx& c, Smem& sm, int l, const 
     for (int e = 0; e < kWE; ++e) {
       if (widx[e] < 0) continue;
       if (packed) {  // values 2w, 2w + 1: adjacent halves of the same 8-value block
+        // 16 significant bits: hi = the top 16 bits, lo = x - hi, both exact in bf16
         const int w = widx[e];
-        const float x0 = unf24(v[e] >> 24), x1 = unf24(v[e]);
+        const uint32_t u0 = (uint32_t)((v[e] >> 24) & 0xFFFFFFu) << 8, u1 = (uint32_t)(v[e] & 0xFFFFFFu) << 8;
+        const uint32_t l0 = __float_as_uint(__uint_as_float(u0) - __uint_as_float(u0 & 0xFFFF0000u));
+        const uint32_t l1 = __float_as_uint(__uint_as_float(u1) - __uint_as_float(u1 & 0xFFFF0000u));
         uint32_t* d = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(h) + (w >> 2) * 16 + ((2 * w) & 7));
-        const uint32_t h0 = bf16_rne(x0), h1 = bf16_rne(x1);
-        d[0] = (h0 & 0xFFFFu) | (h1 << 16);
-        d[4] = (bf16_rne(x0 - __uint_as_float(h0 << 16)) & 0xFFFFu) | (bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
-      } else {  // bf16 halves of gain * x: hi[8] then lo[8] per 8 values
+        d[0] = (u0 >> 16) | (u1 & 0xFFFF0000u);
+        d[4] = (l0 >> 16) | (l1 & 0xFFFF0000u);
+      } else {  // bf16 halves of gain * x: hi[8] then lo[8] per 8 values (hi truncated, lo rounded)
         const int i = widx[e];
         const float x = __uint_as_float((uint32_t)v[e]);
         const float y = x * gv[e];
         uint16_t* d = reinterpret_cast<uint16_t*>(h) + (i >> 3) * 16 + (i & 7);
-        const uint32_t hb = bf16_rne(y);
+        const uint32_t hb = __float_as_uint(y) >> 16;
         d[0] = (uint16_t)hb;
         d[8] = (uint16_t)bf16_rne(y - __uint_as_float(hb << 16));
         ss += x * x;
@@ -1432,7 +1418,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
           case kGateUp: src = a.X1; n = H; gain = Lw.mlp_norm; break;
           default: src = a.ACT; n = a.I; src2 = a.X1 + c.r0; n2 = c.r1 - c.r0; break;
         }
-        ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, mfma_path(c), role == kOproj || role == kDown);
+        ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, role == kOproj || role == kDown);
       }
       if (!ok) return;
       stamp(c, sm, ph, 1, tid == 0);
