@@ -134,13 +134,6 @@ __device__ __forceinline__ float wave_total(float v) {  // the sum of all 64 lan
   v += DPPF(v, 0x143, 0xC);  // row_bcast:31 -> rows 2, 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-__device__ __forceinline__ float half_total(float v) {  // the sum of this lane's half-wave (32 lanes)
-  v = row16_sum(v);
-  v += DPPF(v, 0x142, 0xA);
-  const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
-  const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  return (threadIdx.x & 32) ? hi : lo;
-}
 
 struct Smem {
   float vec[2][kVecMax];    // phase inputs (gain * x for normed phases), slot = layer & 1
