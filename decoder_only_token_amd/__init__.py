@@ -8,8 +8,11 @@ without the built library raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 from typing import Dict, List, Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,7 +58,7 @@ class QdLora(ctypes.Structure):
 
 EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_decode_step", "qd_set_lora",
            "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_enable_phase_trace", "qd_get_phase_trace",
-           "qd_get_quantized", "qd_sync_token", "qd_get_position",
+           "qd_get_quantized", "qd_sync_token", "qd_get_abandoned", "qd_get_position",
            "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
            "qd_sizeof_lora"]
 
@@ -88,6 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qd_get_quantized": (i32, [H, i32, i32, ctypes.POINTER(ctypes.c_int8), sz, ctypes.POINTER(ctypes.c_uint16),
                                    sz]),
         "qd_sync_token": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
+        "qd_get_abandoned": (i32, [H, ctypes.POINTER(ctypes.c_int64)]),
         "qd_get_position": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
         "qd_last_error": (ctypes.c_char_p, [H]),
         "qd_destroy": (None, [H]),
@@ -150,6 +154,28 @@ def _ptr_array(ts: Sequence) -> ctypes.Array:
     return (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
 
 
+_live = weakref.WeakSet()  # open decoders, closed before the interpreter exits
+
+
+@atexit.register
+def _close_all():
+    """Release every open handle (and torch's cached device memory) while the
+    HIP runtime and any attached profiler are still up: process-exit handlers
+    of those run after the interpreter's own exit handlers."""
+    for d in list(_live):
+        try:
+            d.close()
+        except Exception:
+            pass
+    torch = sys.modules.get("torch")
+    try:
+        if torch is not None and torch.cuda.is_initialized():
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+    except Exception:
+        pass
+
+
 class Decoder:
     """One model on the current GPU behind the C ABI.
 
@@ -167,6 +193,7 @@ class Decoder:
         if rc != 0:
             raise QdError(rc, "qd_create failed (reason printed on stderr)")
         self.h = h
+        _live.add(self)
 
     def _check(self, rc: int):
         if rc != 0:
@@ -178,6 +205,8 @@ class Decoder:
             self.h = None
 
     def __del__(self):
+        if sys.is_finalizing():  # the HIP runtime may already be gone; _close_all ran earlier
+            return
         try:
             self.close()
         except Exception:
@@ -267,6 +296,12 @@ class Decoder:
         t = ctypes.c_int32()
         self._check(self.lib.qd_sync_token(self.h, ctypes.byref(t)))
         return t.value
+
+    def abandoned(self) -> int:
+        """Cache episodes since creation in which a persistent decode step was abandoned (synchronises)."""
+        n = ctypes.c_int64()
+        self._check(self.lib.qd_get_abandoned(self.h, ctypes.byref(n)))
+        return n.value
 
     @property
     def position(self) -> int:

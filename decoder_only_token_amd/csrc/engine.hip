@@ -49,6 +49,16 @@ struct LoraLayer {
   uint16_t* bv = nullptr;
 };
 
+// Keeps the persistent step's abandon flag err[0] as a sticky count err[1] of
+// the cache episodes in which a step was abandoned, then clears the flag
+// (stream-ordered: no host synchronisation).
+__global__ void k_fold_err(uint32_t* err) {
+  if (threadIdx.x == 0 && err[0] != 0) {
+    err[1] += 1;
+    err[0] = 0;
+  }
+}
+
 __global__ void k_widen_bf16(const uint16_t* __restrict__ src, float* __restrict__ dst, size_t n) {
   size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   if (i < n) dst[i] = __uint_as_float(((uint32_t)src[i]) << 16);
@@ -187,6 +197,8 @@ int validate_config(const qd_config* c, std::string& why) {
   if (c->lora_rank_max < 0 || c->lora_rank_max > 64) { why = "lora_rank_max must be in [0, 64]"; return QD_E_ARG; }
   if (c->decode_path != QD_DECODE_PERSISTENT && c->decode_path != QD_DECODE_GRAPH) { why = "unknown decode_path"; return QD_E_ARG; }
   if (c->decode_path == QD_DECODE_PERSISTENT) {
+    // handshake tags carry the layer in 8 bits; 255 marks the argmax words and the unset value pairs
+    if (c->n_layers > 254) { why = "the persistent decode step supports at most 254 layers"; return QD_E_ARG; }
     if (c->lora_rank_max != 0) { why = "LoRA needs decode_path QD_DECODE_GRAPH"; return QD_E_ARG; }
     if (c->weight_format != QD_W_BF16) { why = "int4 weights need decode_path QD_DECODE_GRAPH"; return QD_E_ARG; }
     if (c->hidden != 1024 && c->hidden != 2048) { why = "the persistent decode step needs hidden 1024 or 2048"; return QD_E_ARG; }
@@ -696,7 +708,10 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
 int qd_reset_kv(qd_handle* h) {
   if (!h) return QD_E_ARG;
   HIP_TRY(h, hipMemsetAsync(h->st, 0, sizeof(DevState), h->stream));
-  if (h->err_dev) HIP_TRY(h, hipMemsetAsync(h->err_dev, 0, 16, h->stream));
+  if (h->err_dev) {  // an abandoned step of the episode that ends here stays counted in err[1]
+    hipLaunchKernelGGL(k_fold_err, dim3(1), dim3(64), 0, h->stream, h->err_dev);
+    HIP_TRY(h, hipGetLastError());
+  }
   if (h->ACT && fill_pairs(h, h->stream) != QD_OK)
     return h->set_err(QD_E_HIP, "hipMemsetAsync of the value-pair buffers failed");
   h->failed = false;
@@ -938,6 +953,19 @@ int qd_sync_token(qd_handle* h, int32_t* token_host) {
   DevState st;
   HIP_TRY(h, hipMemcpy(&st, h->st, sizeof(st), hipMemcpyDeviceToHost));
   *token_host = st.token;
+  return QD_OK;
+}
+
+int qd_get_abandoned(qd_handle* h, int64_t* count_out) {
+  if (!h) return QD_E_ARG;
+  if (!count_out) return h->set_err(QD_E_ARG, "count_out is NULL");
+  *count_out = 0;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  if (h->err_dev) {
+    uint32_t e[2] = {0, 0};
+    HIP_TRY(h, hipMemcpy(e, h->err_dev, 8, hipMemcpyDeviceToHost));
+    *count_out = (int64_t)e[1] + (e[0] != 0 ? 1 : 0);
+  }
   return QD_OK;
 }
 

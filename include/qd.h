@@ -77,6 +77,7 @@ typedef struct {
   int32_t max_prefill;    /* largest n accepted by one qd_prefill call */
   int32_t lora_rank_max;  /* 0 disables LoRA; else the largest rank qd_set_lora accepts */
   int32_t decode_path;    /* QD_DECODE_PERSISTENT (one kernel per decode step, one workgroup per CU,
+                             at most 254 layers,
                              all resident at once: the device must not be running other work
                              meanwhile, else a step can be abandoned after its bounded wait)
                              or QD_DECODE_GRAPH (one kernel per operation, replayed as a hipGraph) */
@@ -236,8 +237,19 @@ enum { QD_PROJ_Q = 0, QD_PROJ_K = 1, QD_PROJ_V = 2, QD_PROJ_O = 3, QD_PROJ_GATE 
 int qd_get_quantized(qd_handle* h, int32_t layer, int32_t which, int8_t* codes_host, size_t codes_capacity,
                      uint16_t* scales_host, size_t scales_capacity);
 
-/* Synchronise the stream and read the device-resident last token. */
+/* Synchronise the stream and read the device-resident last token.
+ * Errors: QD_E_HIP when a persistent decode step since the last qd_reset_kv was
+ * abandoned (its bounded device-side wait timed out: the device was shared);
+ * later decode steps then fail with QD_E_STATE until qd_reset_kv. */
 int qd_sync_token(qd_handle* h, int32_t* token_host);
+
+/* Synchronise the stream and report in *count_out the number of cache
+ * episodes (spans between qd_reset_kv calls, the current one included) in
+ * which a persistent decode step was abandoned since qd_create.  qd_reset_kv
+ * does not clear this count, so a caller can check a whole run of episodes
+ * once, outside its timed work.  Always 0 for QD_DECODE_GRAPH.
+ * Errors: QD_E_ARG (NULL count_out), QD_E_HIP. */
+int qd_get_abandoned(qd_handle* h, int64_t* count_out);
 
 /* Current position (number of tokens in the KV cache), host-side mirror. */
 int qd_get_position(const qd_handle* h, int32_t* pos_out);

@@ -98,3 +98,21 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.qd_prefill(None, None, 0, None, None, None) == -1
     assert lib.qd_last_error(None) == b"NULL handle"
     lib.qd_destroy(None)
+
+
+def test_persistent_path_rejects_more_than_254_layers():
+    # the persistent step's handshake tags hold the layer in 8 bits (255 is reserved)
+    cfg = qd.make_config(synth.TINY, max_prefill=16, decode_path=qd.QD_DECODE_PERSISTENT)
+    cfg.n_layers = 255
+    rc, h = _create(cfg)
+    assert rc == -1 and not h.value
+    cfg.n_layers = 254
+    rc, h = _create(cfg)
+    assert rc != -1  # passes validation (no GPU here: fails later, at the first HIP call)
+    if rc == 0:
+        qd.load_library().qd_destroy(h)
+
+
+def test_abandoned_count_needs_an_output_pointer():
+    lib = qd.load_library()
+    assert lib.qd_get_abandoned(None, None) == -1

@@ -1,0 +1,139 @@
+"""Oracle parity on the code paths the full-size workloads take.
+
+The full models are too large for a float64 oracle run per step, so each test
+here builds a model small enough for the oracle that still drives the exact
+kernel instantiation or launch branch that a full-size workload runs:
+
+* top-k / top-p sampling over the real 151,936-entry vocabulary (every slice
+  list of the final merge in use), on both decode paths;
+* the persistent step's attention merge with 9 to 11 position splits, which
+  the 0.6B long-context workload runs past 1536 positions;
+* the 3B-width int4 model (hidden 2048, intermediate 11008, 16/2 heads), whose
+  down projection runs the 8-pass int4 GEMV and whose decode step is the
+  captured 3B-width graph.
+
+Every logit of every step is compared with the oracle; tokens follow the
+greedy / sampled near-tie rules of gpu_util.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import OracleModel
+
+from gpu_util import lockstep_greedy, sampling_mismatch_explained, to_device
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"persistent": 0, "graph": 1}
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def make_decoder(torch_cuda, shape, max_prefill, path, lora_rank_max=0):
+    import decoder_only_token_amd as qd
+    cfg = qd.make_config(shape, max_prefill=max_prefill, lora_rank_max=lora_rank_max, decode_path=PATHS[path])
+    return qd.Decoder(cfg, torch_cuda.cuda.current_stream().cuda_stream)
+
+
+def assert_records(recs, max_forced=0):
+    bad = [r for r in recs if r.n_bad]
+    assert not bad, f"logits out of tolerance at steps {[(r.step, r.max_err_ratio, r.n_bad) for r in bad[:5]]}"
+    forced = [r for r in recs if r.forced]
+    assert len(forced) <= max_forced, f"near-tie mismatches at {[(r.step, r.gpu_token, r.oracle_token) for r in forced]}"
+
+
+# the 0.6B shape cut to 2 layers: same vocabulary (151,936), hidden, heads and MLP
+QWEN3_2L = dataclasses.replace(synth.QWEN3_06B, name="qwen3-0.6b-2layer", n_layers=2, max_pos=64)
+# the 3B int4 shape cut to 2 layers and a 4096-entry vocabulary
+QWEN25_INT4_2L = dataclasses.replace(synth.QWEN25_3B_INT4, name="qwen2.5-3b-int4-2layer", n_layers=2, vocab=4096,
+                                     max_pos=64)
+
+
+@pytest.mark.parametrize("path", ["persistent", "graph"])
+def test_sampling_full_vocabulary(torch_cuda, path):
+    """T 0.7 / top-k 40 / top-p 0.9 with a fixed seed over V = 151,936 (149
+    slice lists, so the final merge runs every list of every lane), 2-layer
+    0.6B-width model, 8-token prompt and 28 steps: every logit checked, every
+    draw equal to the oracle's or explained by the near-boundary rule."""
+    import decoder_only_token_amd as qd
+    shape = QWEN3_2L
+    params = (0.7, 40, 0.9, synth.SEED_SAMPLING)
+    log(f"full-vocabulary sampling path={path}")
+    w = synth.make_weights(shape, seed=41)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 16, path)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    del dw
+    sp = qd.make_sampling(*params)
+    prompt = synth.make_prompt(shape.vocab, 8, seed=42)
+    wants = {}
+    recs = lockstep_greedy(dec, oracle, prompt, 28, sampling=sp, sampling_params=params, log=log, want_log=wants)
+    bad = [r for r in recs if r.n_bad]
+    assert not bad, [(r.step, r.max_err_ratio) for r in bad]
+    assert len({r.oracle_token for r in recs}) > 10, "too few distinct draws to exercise the sampler"
+    for r in recs:
+        if r.forced:
+            assert sampling_mismatch_explained(wants[r.step], params, r.step, r.gpu_token), \
+                f"step {r.step}: gpu drew {r.gpu_token}, oracle {r.oracle_token}"
+    assert sum(r.forced for r in recs) <= 2
+    dec.close()
+
+
+@pytest.mark.parametrize("prompt_len,splits", [(1700, 9), (1930, 11)])
+def test_persistent_attention_merge_beyond_eight_splits(torch_cuda, prompt_len, splits):
+    """Tiny model (16 q / 8 kv heads) with a 2048-position cache, as the 0.6B
+    long-context workload: past 1536 positions the persistent step splits each
+    kv head's positions into ceil(ctx / 192) = 9 .. 11 parts, and the merge
+    folds them in two batches of up to 8.  Prompt of `prompt_len` tokens (one
+    batched prefill), then 12 persistent decode steps, every logit checked."""
+    shape = dataclasses.replace(synth.TINY, max_pos=2048)
+    ctx = prompt_len + 1
+    assert -(-ctx // 192) == splits
+    log(f"persistent merge, prompt {prompt_len}: {splits} splits per kv head")
+    w = synth.make_weights(shape, seed=43, random_gains=True)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 2048, "persistent")
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = synth.make_prompt(shape.vocab, prompt_len, seed=44)
+    recs = lockstep_greedy(dec, oracle, prompt, 12, log=log)
+    assert_records(recs, max_forced=1)
+    dec.close()
+
+
+@pytest.mark.parametrize("path", ["graph"])
+def test_int4_3b_width_decode(torch_cuda, path):
+    """2-layer model at the 3B int4 widths (hidden 2048, intermediate 11008,
+    16 q / 2 kv heads, q/k/v bias, no QK-norm, int4 group-128, V 4096): the
+    down projection (K = 11008) runs the 8-pass int4 GEMV, and the decode step
+    is the 3B-width step replayed 16 times.  8-token prompt, every step's
+    logits checked."""
+    shape = QWEN25_INT4_2L
+    log(f"3B-width int4, path={path}")
+    w = synth.make_weights(shape, seed=45, random_gains=True)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 16, path)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    del dw
+    prompt = synth.make_prompt(shape.vocab, 8, seed=46)
+    recs = lockstep_greedy(dec, oracle, prompt, 16, log=log)
+    assert_records(recs, max_forced=1)
+    dec.close()

@@ -308,6 +308,73 @@ def test_qk_norm_makes_logits_invariant_to_scaling_q_and_k_weights():
     assert np.max(np.abs(a - b)) > 1e-4
 
 
+def _qk_layer_by_hand(w, shape, toks, order="norm_then_rope", swap=False):
+    """One layer with a zero MLP at two positions, written out from the block
+    figure of "Failed Star / fs — Forward pass → logits" (QK-norm, then RoPE,
+    then causal GQA attention) with RoPE as a complex rotation of
+    a_j + i b_j (half-split pairs) and a two-entry softmax; returns the layer
+    output of position 1.  `order` / `swap` build deliberately wrong variants."""
+    f = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    lw = w["layers"][0]
+    d, nq, nkv, eps = shape.head_dim, shape.n_q_heads, shape.n_kv_heads, shape.rms_eps
+    gq, gk = f(lw["q_norm"]), f(lw["k_norm"])
+    if swap:
+        gq, gk = gk, gq
+    xs = [f(w["embed"])[t] for t in toks]
+    qs, ks, vs = [], [], []
+    for p, x in enumerate(xs):
+        h = f(lw["attn_norm"]) * x / math.sqrt(float(np.dot(x, x)) / x.size + eps)
+        q = (f(lw["wq"]) @ h).reshape(nq, d)
+        k = (f(lw["wk"]) @ h).reshape(nkv, d)
+        vs.append((f(lw["wv"]) @ h).reshape(nkv, d))
+
+        def rot(u):
+            z = u[:d // 2] + 1j * u[d // 2:]
+            z = z * np.exp(1j * p * (shape.rope_theta ** (-2.0 * np.arange(d // 2) / d)))
+            return np.concatenate([z.real, z.imag])
+
+        def nrm(u, g):
+            return g * u / math.sqrt(float(np.dot(u, u)) / d + eps)
+
+        if order == "norm_then_rope":
+            qs.append(np.stack([rot(nrm(q[i], gq)) for i in range(nq)]))
+            ks.append(np.stack([rot(nrm(k[i], gk)) for i in range(nkv)]))
+        else:
+            qs.append(np.stack([nrm(rot(q[i]), gq) for i in range(nq)]))
+            ks.append(np.stack([nrm(rot(k[i]), gk) for i in range(nkv)]))
+    o = np.zeros((nq, d))
+    for hh in range(nq):
+        g = hh // (nq // nkv)
+        s0 = float(np.dot(qs[1][hh], ks[0][g])) / math.sqrt(d)
+        s1 = float(np.dot(qs[1][hh], ks[1][g])) / math.sqrt(d)
+        p1 = 1.0 / (1.0 + math.exp(s0 - s1))
+        o[hh] = (1.0 - p1) * vs[0][g] + p1 * vs[1][g]
+    return xs[1] + f(lw["wo"]) @ o.reshape(-1)
+
+
+def test_qk_norm_gains_and_order_closed_form():
+    # Distinct random q_norm / k_norm gains; the hand-written layer (complex
+    # RoPE, explicit two-entry softmax) must equal the oracle, and swapping the
+    # gains or rotating before normalising must not.
+    shape = tiny_shape(n_layers=1, qk_norm=True)
+    w = synth.make_weights(shape, seed=31, random_gains=True)
+    lw = w["layers"][0]
+    rng = np.random.default_rng(32)
+    lw["q_norm"] = synth.bf16_round(rng.uniform(0.3, 2.5, shape.head_dim).astype(np.float32))
+    lw["k_norm"] = synth.bf16_round(rng.uniform(0.3, 2.5, shape.head_dim).astype(np.float32))
+    for name in ("w_gate", "w_up", "w_down"):
+        lw[name] = np.zeros_like(lw[name])
+    toks = [11, 42]
+    cap = {}
+    _model(shape, w).forward(toks, capture=cap)
+    got = cap["layer_out"][0][1]
+    want = _qk_layer_by_hand(w, shape, toks)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    for variant in (dict(swap=True), dict(order="rope_then_norm")):
+        wrong = _qk_layer_by_hand(w, shape, toks, **variant)
+        assert np.max(np.abs(wrong - got)) > 1e-6, variant
+
+
 def test_incremental_equals_cacheless_prefill():
     shape = tiny_shape(qkv_bias=True)
     w = synth.make_weights(shape, seed=18, random_gains=True)
@@ -380,6 +447,14 @@ def test_splitmix64_published_vectors():
     assert got == [int(h, 16) for h in g["outputs_hex"]]
     u = [uniform_for_step(2, s) for s in range(1000)]
     assert min(u) >= 0.0 and max(u) < 1.0 and abs(np.mean(u) - 0.5) < 0.03
+
+
+def test_uniform_for_step_published_vectors():
+    # u for step s is output s+1's top 24 bits over 2^24, derived by hand from
+    # the published outputs: pins the counter offset and the bit window.
+    g = golden("uniform_vectors.json")
+    for s, (top, u) in enumerate(zip(g["top24"], g["u"])):
+        assert uniform_for_step(g["seed"], s) == u == top / float(1 << 24), s
 
 
 def test_sampling_worked_examples():
