@@ -11,6 +11,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -200,7 +201,6 @@ int validate_config(const qd_config* c, std::string& why) {
     // handshake tags carry the layer in 8 bits; 255 marks the argmax words and the unset value pairs
     if (c->n_layers > 254) { why = "the persistent decode step supports at most 254 layers"; return QD_E_ARG; }
     if (c->lora_rank_max != 0) { why = "LoRA needs decode_path QD_DECODE_GRAPH"; return QD_E_ARG; }
-    if (c->weight_format != QD_W_BF16) { why = "int4 weights need decode_path QD_DECODE_GRAPH"; return QD_E_ARG; }
     if (c->hidden != 1024 && c->hidden != 2048) { why = "the persistent decode step needs hidden 1024 or 2048"; return QD_E_ARG; }
     if (c->intermediate > 11264 || c->n_q_heads * c->head_dim > 11264) { why = "model too wide for the persistent decode step"; return QD_E_ARG; }
   }
@@ -538,11 +538,17 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || ncu < 1)
       return fail(h->set_err(QD_E_HIP, "cannot query the CU count"));
     h->grid = ncu > 1024 ? 1024 : ncu;
+    if (const char* e = getenv("QD_PERSIST_CUS")) {  // fewer workgroups (diagnostics, tests)
+      const int n = atoi(e);
+      if (n >= 1 && n < h->grid) h->grid = n;
+    }
     h->hseg = c.hidden / 512;
     const int G = c.n_q_heads / c.n_kv_heads;
-    if (persist_prepare(G, h->hseg) != 0) return fail(h->set_err(QD_E_HIP, "persistent decode kernel unavailable"));
+    const int q4 = c.weight_format == QD_W_INT4_G128;
+    if (persist_prepare(G, h->hseg, q4) != 0) return fail(h->set_err(QD_E_HIP, "persistent decode kernel unavailable"));
     {  // the role plan must exist at the shortest and the longest context
       PersistConst shape{};
+      shape.q4 = q4;
       shape.H = c.hidden; shape.nq = c.n_q_heads; shape.nkv = c.n_kv_heads; shape.I = c.intermediate;
       shape.nqkv = (int)qkv_rows(c); shape.max_pos = c.max_pos; shape.V = c.vocab;
       PersistStep st;
@@ -614,10 +620,11 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
       if (q4) {
         if ((rc = dev_alloc(h, &L.cqkv, NQKV * H / 2)) || (rc = dev_alloc(h, &L.sqkv, NQKV * H / 128)) ||
             (rc = dev_alloc(h, &L.co, H * nq * d / 2)) || (rc = dev_alloc(h, &L.so, H * nq * d / 128)) ||
-            (rc = dev_alloc(h, &L.cg, I * H / 2)) || (rc = dev_alloc(h, &L.sg, I * H / 128)) ||
-            (rc = dev_alloc(h, &L.cu, I * H / 2)) || (rc = dev_alloc(h, &L.su, I * H / 128)) ||
+            (rc = dev_alloc(h, &L.cg, 2 * I * H / 2)) || (rc = dev_alloc(h, &L.sg, 2 * I * H / 128)) ||
             (rc = dev_alloc(h, &L.cd, H * I / 2)) || (rc = dev_alloc(h, &L.sd, H * I / 128)))
           return rc;
+        L.cu = L.cg + I * H / 2;  // up rows follow the gate rows (codes and scales)
+        L.su = L.sg + I * H / 128;
       } else if ((rc = dev_alloc(h, &L.wqkv, NQKV * H)) || (rc = dev_alloc(h, &L.wo, H * nq * d)) ||
                  (rc = dev_alloc(h, &L.wg, 2 * I * H)) || (rc = dev_alloc(h, &L.wd, H * I))) {
         return rc;
@@ -686,11 +693,12 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
     std::vector<LayerPtrs> lp(c.n_layers);
     for (int l = 0; l < c.n_layers; ++l) {
       const Layer& L = h->layers[l];
-      lp[l] = LayerPtrs{L.wqkv, L.bqkv, L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm, L.wo, L.wg, L.wu, L.wd};
+      lp[l] = LayerPtrs{L.wqkv, L.bqkv, L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm, L.wo,  L.wg,  L.wu,
+                        L.wd,   L.cqkv, L.co,        L.cg,       L.cd,     L.sqkv,   L.so, L.sg, L.sd};
     }
     PersistConst pc{};
     pc.L = c.n_layers; pc.H = c.hidden; pc.nq = c.n_q_heads; pc.nkv = c.n_kv_heads; pc.I = c.intermediate;
-    pc.V = c.vocab; pc.nqkv = (int)NQKV; pc.max_pos = c.max_pos; pc.eps = c.rms_eps;
+    pc.V = c.vocab; pc.nqkv = (int)NQKV; pc.max_pos = c.max_pos; pc.eps = c.rms_eps; pc.q4 = q4;
     pc.embed = h->embed; pc.final_norm = h->final_norm; pc.layers = h->layer_ptrs;
     pc.Kc = h->Kc; pc.Vc = h->Vc; pc.rope_cos = h->rope_cos; pc.rope_sin = h->rope_sin;
     pc.X0 = h->X0; pc.X1 = h->X1; pc.QKV = h->QKVx; pc.PART = h->PART; pc.O = h->Ox; pc.ACT = h->ACT;
@@ -763,7 +771,7 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
     const int G = h->cfg.n_q_heads / h->cfg.n_kv_heads;
     if (h->trace_on)  // a traced step writes only the stamps of its CUs' phases
       HIP_TRY(h, hipMemsetAsync(h->trace, 0, (size_t)h->grid * persist_trace_slots(h->cfg.n_layers) * 8, h->stream));
-    int e = persist_launch(h->pconst, G, h->hseg, h->grid, st, h->stream);
+    int e = persist_launch(h->pconst, G, h->hseg, h->cfg.weight_format == QD_W_INT4_G128, h->grid, st, h->stream);
     if (e != 0) return h->set_err(QD_E_HIP, "persistent decode launch failed: " + std::to_string(e));
     if ((rc = maybe_sample(h, sampling))) return rc;
     h->pos += 1;

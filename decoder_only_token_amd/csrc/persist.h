@@ -17,12 +17,24 @@ struct LayerPtrs {
   const uint16_t* wg;  // [I][H]
   const uint16_t* wu;  // [I][H]
   const uint16_t* wd;  // [H][I]
+  // int4 group-128 weights (codes u8 [rows][in / 2], fp16 scales [rows][in / 128],
+  // same row order as the bf16 matrices above, which are then null); the up
+  // rows' codes and scales follow the gate rows' in one allocation each
+  const uint8_t* cqkv;
+  const uint8_t* co;
+  const uint8_t* cg;
+  const uint8_t* cd;
+  const uint16_t* sqkv;
+  const uint16_t* so;
+  const uint16_t* sg;
+  const uint16_t* sd;
 };
 
 // Everything the decode kernel needs that does not change from step to step.
 // The exchange buffers hold 64-bit words {f32 value | tag << 32}.
 struct PersistConst {
   int L, H, nq, nkv, I, V, nqkv, max_pos;
+  int q4;  // 1: the projections are int4 group-128 (LayerPtrs c* / s*)
   float eps;
   const uint16_t* embed;
   const float* final_norm;
@@ -65,8 +77,9 @@ struct PersistStep {
 };
 
 size_t persist_smem_bytes();
-int persist_prepare(int G, int hseg);
+int persist_prepare(int G, int hseg, int q4);
 // Plans the step at position pos for `grid` CUs; 0 on success, -1 if the
 // grid cannot hold the five roles.
 int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, PersistStep* out);
-int persist_launch(const PersistConst* dev_const, int G, int hseg, int grid, const PersistStep& st, hipStream_t s);
+int persist_launch(const PersistConst* dev_const, int G, int hseg, int q4, int grid, const PersistStep& st,
+                   hipStream_t s);

@@ -52,6 +52,8 @@
 // only after a workgroup barrier that all waves reach after their last read
 // of it (slots alternate by layer).
 
+#include <hip/hip_fp16.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -202,6 +204,7 @@ __device__ __forceinline__ bool timed_out(const Ctx& c) {
 // RMSNorm scale, applied to the row sums later.  Ends with a workgroup
 // barrier; returns false on every thread when the step is abandoned.  With
 // `packed`, src holds n / 2 words of value pairs.
+template <int PE = kPE>
 __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint64_t* src, int n, uint32_t tag, float* dst,
                      const float* gain, float* rs, const uint64_t* src2, int n2, float* dst2,
                      bool packed = false) {
@@ -211,19 +214,19 @@ __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint6
   if (packed) {  // n / 2 words of value pairs (no gain)
     const int nw = n >> 1;
     const uint32_t t16 = tag & 0xFFFFu;
-    for (int base = 0; ok && base < nw; base += kPE * kThreads) {
-      uint64_t v[kPE], v2 = (uint64_t)tag << 32;
+    for (int base = 0; ok && base < nw; base += PE * kThreads) {
+      uint64_t v[PE], v2 = (uint64_t)tag << 32;
       uint32_t spin = 0;
       for (;;) {
         bool done = true;
 #pragma unroll
-        for (int e = 0; e < kPE; ++e) {
+        for (int e = 0; e < PE; ++e) {
           const int w = base + e * kThreads + tid;
           v[e] = w < nw ? ld_tagged(src + w) : (uint64_t)t16 << 48;
         }
         if (base == 0 && tid < n2) v2 = ld_tagged(src2 + tid);
 #pragma unroll
-        for (int e = 0; e < kPE; ++e) done &= (uint32_t)(v[e] >> 48) == t16;
+        for (int e = 0; e < PE; ++e) done &= (uint32_t)(v[e] >> 48) == t16;
         done &= (uint32_t)(v2 >> 32) == tag;
         if (done) break;
         if ((++spin & 31) == 0 && timed_out(c)) {
@@ -234,7 +237,7 @@ __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint6
       }
       if (!ok) break;
 #pragma unroll
-      for (int e = 0; e < kPE; ++e) {
+      for (int e = 0; e < PE; ++e) {
         const int w = base + e * kThreads + tid;
         if (w < nw) {
           const float x0 = unf24(v[e] >> 24), x1 = unf24(v[e]);
@@ -246,28 +249,28 @@ __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint6
       if (base == 0 && tid < n2) dst2[tid] = __uint_as_float((uint32_t)v2);
     }
   }
-  for (int base = 0; ok && !packed && base < n; base += kPE * kThreads) {
-    float gv[kPE];
+  for (int base = 0; ok && !packed && base < n; base += PE * kThreads) {
+    float gv[PE];
     if (gain) {
 #pragma unroll
-      for (int e = 0; e < kPE; ++e) {
+      for (int e = 0; e < PE; ++e) {
         const int i = base + e * kThreads + tid;
         gv[e] = i < n ? ld_f(gain + i) : 0.f;
       }
     }
     const uint64_t want = (uint64_t)tag << 32;
-    uint64_t v[kPE], v2 = want;
+    uint64_t v[PE], v2 = want;
     uint32_t spin = 0;
     for (;;) {
       bool done = true;
 #pragma unroll
-      for (int e = 0; e < kPE; ++e) {
+      for (int e = 0; e < PE; ++e) {
         const int i = base + e * kThreads + tid;
         v[e] = i < n ? ld_tagged(src + i) : want;
       }
       if (base == 0 && tid < n2) v2 = ld_tagged(src2 + tid);
 #pragma unroll
-      for (int e = 0; e < kPE; ++e) done &= (uint32_t)(v[e] >> 32) == tag;
+      for (int e = 0; e < PE; ++e) done &= (uint32_t)(v[e] >> 32) == tag;
       done &= (uint32_t)(v2 >> 32) == tag;
       if (done) break;
       if ((++spin & 31) == 0 && timed_out(c)) {
@@ -278,7 +281,7 @@ __device__ __forceinline__ bool poll(const Ctx& c, Smem& sm, int ph, const uint6
     }
     if (!ok) break;
 #pragma unroll
-    for (int e = 0; e < kPE; ++e) {
+    for (int e = 0; e < PE; ++e) {
       const int i = base + e * kThreads + tid;
       if (i < n) {
         const float x = __uint_as_float((uint32_t)v[e]);
@@ -427,6 +430,16 @@ struct Addr {
   int n = N;  // slots to load (wave-uniform); the others keep stale values and are not used
 };
 
+// int4 roles: the slots' fp16 group scales, one per lane and slot (record,
+// lane part, uniform parts, count).
+template <int N>
+struct SAddr {
+  __amdgpu_buffer_rsrc_t rs;
+  int voff;
+  int soff[N];
+  int n;
+};
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
@@ -441,6 +454,15 @@ __device__ __forceinline__ void load_regs(Regs<N>& rg, const Addr<N>& ad) {
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// The group scales of an int4 role's slots (fp16 bit patterns, one per lane
+// and slot), into registers sc[H0 ..]; issued beside the codes' loads.
+template <int H0, int N, int M>
+__device__ __forceinline__ void load_scales(uint32_t (&sc)[M], const SAddr<N>& ad) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i < ad.n) sc[H0 + i] = __builtin_amdgcn_raw_buffer_load_b16(ad.rs, ad.voff, ad.soff[i], 2 /* nt */);
+}
 
 // The next N segments from walk position w (the last valid segment repeats
 // past the end, so every register is loaded).  A row's last segment may run
@@ -514,6 +536,95 @@ __device__ __forceinline__ void lm_addr(Addr<N>& ad, const uint16_t* E, int rb, 
   }
 }
 
+// ---------------------------------------------------------- int4 GEMV roles
+// A role's rows in int4 group-128 form (codes u8 [rows][K / 2], byte b of a
+// row = columns 2b (low nibble) and 2b + 1 (high nibble) as code + 8; fp16
+// scales [rows][K / 128]) are read in slots of one 16-row block by one group
+// of 128 columns: lane i loads the 16 bytes of row i % 16, columns
+// 32 (i / 16) .. + 31, and one scale (its row's, of the slot's group).  Groups
+// are dealt to the waves round robin (wave w: groups w, w + 8, ...); a wave's
+// slots run row block by row block, its groups inner.  The first kFirst slots
+// are loaded a layer ahead, the rest stream in during the phase.
+struct Q4Geo {
+  const uint8_t* c;   // codes of the CU's first row (gate rows for pairs)
+  const uint16_t* s;  // scales of the CU's first row
+  int dc, ds;         // up rows - gate rows: codes (bytes), scales (elements)
+  int K, ng;          // columns, groups of 128
+  int nb, ns, nrows;  // row blocks per row set, row sets, rows per set
+  int cnt, nslots;    // groups and slots of this wave
+};
+
+__device__ __forceinline__ Q4Geo q4_geo(const Ctx& c, int l) {
+  const AS4 PersistConst& a = *c.a;
+  const AS4 LayerPtrs& L = ((const AS4 LayerPtrs*)a.layers)[l];
+  Q4Geo q;
+  q.ns = 1;
+  q.dc = q.ds = 0;
+  switch (c.role) {
+    case kQKV: q.K = a.H; q.c = L.cqkv; q.s = L.sqkv; break;
+    case kOproj: q.K = a.nq * D; q.c = L.co; q.s = L.so; break;
+    case kGateUp:
+      q.K = a.H; q.c = L.cg; q.s = L.sg; q.ns = 2;
+      q.dc = a.I * (a.H >> 1);
+      q.ds = a.I * (a.H >> 7);
+      break;
+    default: q.K = a.I; q.c = L.cd; q.s = L.sd; break;
+  }
+  q.ng = q.K >> 7;
+  q.nrows = c.r1 - c.r0;
+  q.nb = (q.nrows + 15) >> 4;
+  q.c += (size_t)c.r0 * (q.K >> 1);
+  q.s += (size_t)c.r0 * q.ng;
+  const int w = wave_id();
+  q.cnt = __builtin_amdgcn_readfirstlane(w < q.ng ? (q.ng - 1 - w) / kWaves + 1 : 0);
+  q.nslots = __builtin_amdgcn_readfirstlane(q.ns * q.nb * q.cnt);
+  return q;
+}
+
+// Addresses of this wave's slots i0 .. i0 + N - 1 (those past its last slot
+// are not loaded).  Every row read lies inside the CU's own rows.
+// Row block and group of the wave's slot ii: {set, first row, group}.
+struct Q4Slot {
+  int set, row, g;
+};
+__device__ __forceinline__ Q4Slot q4_slot_of(const Q4Geo& q, int ii) {
+  const int cnt = max(q.cnt, 1);
+  const int bb = ii / cnt, j = ii - bb * cnt;
+  Q4Slot t;
+  t.set = bb / q.nb;
+  t.row = min(16 * (bb - t.set * q.nb), q.nrows - 16);
+  t.g = wave_id() + kWaves * j;
+  return t;
+}
+
+template <int N>
+__device__ __forceinline__ void q4_addr(Addr<N>& ad, const Q4Geo& q, int i0) {
+  const int lane = threadIdx.x & 63;
+  const int n = max(0, min(N, q.nslots - i0));
+  ad.rs[0] = ad.rs[1] = rsrc_of(q.c);
+  ad.voff = (lane & 15) * (q.K >> 1) + (lane >> 4) * 16;
+  ad.n = n;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const Q4Slot t = q4_slot_of(q, i0 + min(i, max(n - 1, 0)));
+    ad.soff[i] = __builtin_amdgcn_readfirstlane(t.set * q.dc + t.row * (q.K >> 1) + t.g * 64);  // wave-uniform
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void q4_saddr(SAddr<N>& sa, const Q4Geo& q, int i0) {
+  const int lane = threadIdx.x & 63;
+  const int n = max(0, min(N, q.nslots - i0));
+  sa.rs = rsrc_of(q.s);
+  sa.voff = (lane & 15) * q.ng * 2;
+  sa.n = n;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const Q4Slot t = q4_slot_of(q, i0 + min(i, max(n - 1, 0)));
+    sa.soff[i] = __builtin_amdgcn_readfirstlane((t.set * q.ds + t.row * q.ng + t.g) * 2);
+  }
+}
+
 // K and V cache rows of (layer l, kv head g).
 __device__ __forceinline__ float* k_rows(const AS4 PersistConst& a, int l, int g) {
   return a.Kc + ((size_t)l * a.nkv + g) * a.max_pos * D;
@@ -523,7 +634,7 @@ __device__ __forceinline__ float* v_rows(const AS4 PersistConst& a, int l, int g
 }
 
 // The slice this CU loads ahead for layer l (l == L: its first LM-head rows).
-template <int HS>
+template <int HS, bool Q4>
 __device__ __forceinline__ Addr<kFirst> ahead_addr(const Ctx& c, int l) {
   const AS4 PersistConst& a = *c.a;
   const int wave = wave_id();
@@ -533,6 +644,8 @@ __device__ __forceinline__ Addr<kFirst> ahead_addr(const Ctx& c, int l) {
   } else if (c.role == kAttn) {
     const int g = c.rank / (c.X * c.S), s = c.rank % c.S;
     kv_addr<kFirst>(ad, k_rows(a, l, g), v_rows(a, l, g), s * c.chunk, 0);
+  } else if (Q4) {
+    q4_addr<kFirst>(ad, q4_geo(c, l), 0);
   } else {
     Tiles t;
     if (mfma_path(c, &t))
@@ -638,16 +751,177 @@ __device__ __forceinline__ void tiles_finish(const Ctx& c, Smem& sm, int l, cons
   }
 }
 
+// int4 roles' input as int8 pieces for the matrix cores.  The phase input h
+// (f32, gain * x for normed phases) of each 128-column group g is written as
+// y = u (a + b / 128 + c / 16384) with a power of two u per group (the group's
+// largest |y| lies in [64 u, 128 u)), a = trunc(y / u), b and c the next
+// seven-bit digits (c rounded to nearest): |error| <= u / 32768, i.e. 2^-21 of
+// the group's largest input.  The pieces a, b, c go to rows 0, 4 and 8 of the
+// A operand of v_mfma_i32_16x16x64_i8 (the other rows are zero), so the three
+// products land in lanes 0-15, 16-31 and 32-47 of one result.  LDS layout per
+// group: [parity e][piece p][quarter q][16 bytes], byte 4 m + t of quarter q
+// being column 128 g + 32 q + 8 m + 2 t + e (the order in which the codes'
+// nibbles unpack); u / 16 per group follows the pieces.  Each 16-lane team of
+// a wave converts one of the wave's groups (lane: quarter q, dword m).
+constexpr int kQ4Group = 384;  // LDS bytes of one group's pieces
+
+__device__ __forceinline__ void q4_stage(const float* h, uint8_t* q8, const Q4Geo& q) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int t = lane >> 4, l16 = lane & 15, qq = l16 >> 2, m = l16 & 3;
+  float* ug = reinterpret_cast<float*>(q8 + q.ng * kQ4Group);
+  for (int j0 = 0; j0 < q.cnt; j0 += 4) {  // wave-uniform
+    const int j = j0 + t;
+    const bool act = j < q.cnt;
+    const int g = wave + kWaves * j;
+    const int col = 128 * g + 32 * qq + 8 * m;
+    f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0;
+    if (act) {
+      y0 = *reinterpret_cast<const f32x4*>(h + col);
+      y1 = *reinterpret_cast<const f32x4*>(h + col + 4);
+    }
+    const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(y[k]));
+    mx = group_max<16>(mx);  // the team's group
+    const int E = (int)((__float_as_uint(mx) >> 23) & 0xFF);  // mx in [2^(E-127), 2^(E-126))
+    const bool live = E >= 6;  // a group below 2^-121 (or all zero) is taken as zero
+    const float up = __uint_as_float((uint32_t)(live ? 260 - E : 127) << 23);  // 1 / u = 2^(133 - E)
+    uint32_t pk[6] = {0u, 0u, 0u, 0u, 0u, 0u};  // [parity][piece]
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float v = live ? y[k] * up : 0.f;  // |v| < 128, exact
+      const float a = truncf(v);
+      const float r = (v - a) * 128.0f;
+      const float b = truncf(r);
+      const float cc = fminf(fmaxf(rintf((r - b) * 128.0f), -127.0f), 127.0f);
+      const int sh = 8 * (k >> 1), e3 = 3 * (k & 1);
+      pk[e3 + 0] |= ((uint32_t)(int)a & 0xFFu) << sh;
+      pk[e3 + 1] |= ((uint32_t)(int)b & 0xFFu) << sh;
+      pk[e3 + 2] |= ((uint32_t)(int)cc & 0xFFu) << sh;
+    }
+    if (act) {
+      uint8_t* d = q8 + g * kQ4Group + qq * 16 + m * 4;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        *reinterpret_cast<uint32_t*>(d + p * 64) = pk[p];
+        *reinterpret_cast<uint32_t*>(d + 192 + p * 64) = pk[3 + p];
+      }
+      if (l16 == 0) ug[g] = live ? ldexpf(1.0f, E - 137) : 0.f;  // u / 16 (the codes enter as 16 code)
+    }
+  }
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// int4 GEMV role: stage the pieces, then every slot of the wave (the
+// registers loaded ahead, then streamed halves of kFirst / 2 slots, each half
+// reloaded as soon as it is consumed) as two int8 products (even and odd
+// columns of the group: the code nibbles become 16 code in the bytes' high
+// halves, exact), the slot's integer result scaled by its group scale and
+// u / 16 into a per-lane f32 sum; at the end of each row block the three
+// piece sums are weighted (1, 2^-7, 2^-14) and added across lanes in a fixed
+// order, and lanes 0-15 leave the wave's partial of each row in LDS for
+// tiles_finish.
+__device__ __forceinline__ void q4_phase(const Ctx& c, Smem& sm, int l, Regs<kFirst>& rg, uint32_t (&sc)[kFirst],
+                                         float rs, const float* bias) {
+  const Q4Geo q = q4_geo(c, l);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  uint8_t* q8 = reinterpret_cast<uint8_t*>(sm.vec[(l + 1) & 1]);  // the slot of the previous layer's input
+  q4_stage(sm.vec[l & 1], q8, q);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back its own pieces
+  const float* ug = reinterpret_cast<const float*>(q8 + q.ng * kQ4Group);
+  const int l16 = lane & 15;
+  const bool plane = (l16 & 3) == 0 && l16 < 12;  // A rows 0, 4, 8 hold the pieces
+  const int aoff = (l16 >> 2) * 64 + (lane >> 4) * 16;
+  const float pw = lane < 16 ? 1.0f : lane < 32 ? 0.0078125f : lane < 48 ? 6.103515625e-05f : 0.0f;
+  const int nbb = q.ns * q.nb, cnt = max(q.cnt, 1);
+  float tot = 0.f;
+  int cur = 0;
+  auto flush = [&]() {
+    float v = tot * pw;
+    v += __shfl_xor(v, 32, 64);
+    v += __shfl_xor(v, 16, 64);
+    if (lane < 16) sm.att[(cur * 16 + lane) * kWaves + wave] = v;
+    tot = 0.f;
+    ++cur;
+  };
+  auto slot = [&](const u32x4 w, uint32_t s16, int i) {
+    const int bb = i / cnt, j = i - bb * cnt;
+    while (cur < bb) flush();  // wave-uniform
+    const int g = wave + kWaves * j;
+    u32x4 ae = {0u, 0u, 0u, 0u}, ao = ae;
+    if (plane) {
+      ae = *reinterpret_cast<const u32x4*>(q8 + g * kQ4Group + aoff);
+      ao = *reinterpret_cast<const u32x4*>(q8 + g * kQ4Group + 192 + aoff);
+    }
+    u32x4 be, bo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x = w[k] ^ 0x88888888u;  // code + 8 -> the code's 4-bit two's complement
+      be[k] = (x << 4) & 0xF0F0F0F0u;
+      bo[k] = x & 0xF0F0F0F0u;
+    }
+    i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, ae), __builtin_bit_cast(i32x4, be),
+                                                      i32x4{0, 0, 0, 0}, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, ao), __builtin_bit_cast(i32x4, bo), acc, 0, 0,
+                                                0);
+    const float sv = __half2float(__ushort_as_half((uint16_t)s16)) * ug[g];
+    tot = fmaf((float)acc.x, sv, tot);
+  };
+  constexpr int HN = kFirst / 2;
+  for (int base = 0; base < q.nslots; base += kFirst) {  // wave-uniform
+#pragma unroll
+    for (int r = 0; r < HN; ++r)
+      if (base + r < q.nslots) slot(rg.R[r], sc[r], base + r);
+    if (base + kFirst < q.nslots) {
+      Addr<HN> ad;
+      SAddr<HN> sa;
+      q4_addr<HN>(ad, q, base + kFirst);
+      q4_saddr<HN>(sa, q, base + kFirst);
+#pragma unroll
+      for (int i = 0; i < HN; ++i)
+        if (i < ad.n)
+          rg.R[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.rs[0], ad.voff, ad.soff[i], 2));
+      load_scales<0>(sc, sa);
+    }
+#pragma unroll
+    for (int r = 0; r < HN; ++r)
+      if (base + HN + r < q.nslots) slot(rg.R[HN + r], sc[HN + r], base + HN + r);
+    if (base + kFirst + HN < q.nslots) {
+      Addr<HN> ad;
+      SAddr<HN> sa;
+      q4_addr<HN>(ad, q, base + kFirst + HN);
+      q4_saddr<HN>(sa, q, base + kFirst + HN);
+#pragma unroll
+      for (int i = 0; i < HN; ++i)
+        if (i < ad.n)
+          rg.R[HN + i] =
+              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.rs[0], ad.voff, ad.soff[i], 2));
+      load_scales<HN>(sc, sa);
+    }
+  }
+  while (cur < nbb) flush();
+  stamp(c, sm, 5 * l + c.role, 2, threadIdx.x == 0);
+  __syncthreads();
+  tiles_finish(c, sm, l, Tiles{q.nb, q.ns, 0}, rs, bias);
+}
+
 // GEMV role: this CU's rows, from the registers loaded ahead (and, on the
 // row-segment path, streamed batches for any rest), published one word per
 // output row.
-__device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, float rs,
-                                           const Gemv& g, const float* bias) {
+template <bool Q4>
+__device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, Regs<kFirst>& rg, uint32_t (&sc)[kFirst],
+                                           float rs, const Gemv& g, const float* bias) {
   const AS4 PersistConst& a = *c.a;
   const int lane = threadIdx.x & 63, wave = wave_id(), kind = c.role;
   const float* h = sm.vec[l & 1];
   const uint32_t tag = tag_of(c.seq, l);
   stamp(c, sm, 5 * l + kind, 4, threadIdx.x == 0);
+  if (Q4) {
+    q4_phase(c, sm, l, rg, sc, rs, bias);
+    return;
+  }
   Tiles tl;
   if (mfma_path(c, &tl)) {
     gemv_tiles_any(c, sm, tl, rg, h, l);
@@ -1287,7 +1561,7 @@ __device__ __forceinline__ bool gate(const Ctx& c, Smem& sm, const uint64_t* w, 
   return !sm.abort_flag;
 }
 
-template <int G, int HS>
+template <int G, int HS, bool Q4>
 __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const PersistConst* __restrict__ pc,
                                                                    PersistStep stp) {
   extern __shared__ __align__(16) char smem_raw[];
@@ -1327,7 +1601,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   const int L = a.L, H = a.H, tid = threadIdx.x;
   const uint16_t* emb = a.embed + (size_t)gl(a.st)->token * H;
   Regs<kFirst> rg;
-  load_regs(rg, ahead_addr<HS>(c, 0));
+  load_regs(rg, ahead_addr<HS, Q4>(c, 0));
   __syncthreads();
   for (int l = 0; l < L; ++l) {
     const int ph = 5 * l + role;
@@ -1345,15 +1619,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
     if (role == kAttn) {
       pre = attn_pre(c, l);
     } else {
-      gv = gemv_of(c, l);
+      if (!Q4) gv = gemv_of(c, l);
       if (role == kQKV) bias = Lw.bqkv;
     }
     // ---- the phase input and the compute
     Tiles tw;
-    if (role != kAttn && !(l == 0 && role == kQKV) && mfma_path(c, &tw)) {
+    if (!Q4 && role != kAttn && !(l == 0 && role == kQKV) && mfma_path(c, &tw)) {
       if (!gemv_waves(c, sm, l, rg, tw, bias)) return;  // per-wave input, matrix-core rows
     } else {
       bool ok = true;
+      // int4 roles: the group scales of the slots loaded ahead, requested
+      // before the input wait (1/64 of the codes' bytes)
+      uint32_t sc[kFirst];
+      if (Q4 && role != kAttn) {
+        SAddr<kFirst> sa;
+        q4_saddr<kFirst>(sa, q4_geo(c, l), 0);
+        load_scales<0>(sc, sa);
+      }
       {  // the word the gate watches: the producer's input (f32 vectors only)
         const uint64_t* gw = nullptr;
         uint32_t gt = tag;
@@ -1368,7 +1650,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
       }
       if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
         float ss = 0.f;
-        const bool split = mfma_path(c);
+        const bool split = !Q4 && mfma_path(c);
         for (int k = tid; k < H; k += kThreads) {
           const float x = bf16_to_f(*gl(emb + k));
           const float y = x * ld_f(Lw.attn_norm + k);
@@ -1411,7 +1693,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
           case kGateUp: src = a.X1; n = H; gain = Lw.mlp_norm; break;
           default: src = a.ACT; n = a.I; src2 = a.X1 + c.r0; n2 = c.r1 - c.r0; break;
         }
-        ok = poll(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, role == kOproj || role == kDown);
+        // (int4 roles hold their slots' scales meanwhile: a narrower poll keeps
+        // the registers within one wave per SIMD half)
+        ok = poll<Q4 ? 4 : kPE>(c, sm, l, src, n, tag, dst, gain, &rs, src2, n2, xr, role == kOproj || role == kDown);
       }
       if (!ok) return;
       stamp(c, sm, ph, 1, tid == 0);
@@ -1422,13 +1706,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
         if (!attn_finish<G>(c, sm, l)) return;
         attn_cache_write<G>(c, sm, l);
       } else {
-        gemv_phase(c, sm, l, rg, rs, gv, bias);
+        gemv_phase<Q4>(c, sm, l, rg, sc, rs, gv, bias);
       }
     }
     stamp(c, sm, ph, 3, tid == 0);
     // the single load site: the next layer's slice (after the last layer, the
     // first LM-head rows) streams while the other roles take their phases
-    load_regs(rg, ahead_addr<HS>(c, l + 1));
+    load_regs(rg, ahead_addr<HS, Q4>(c, l + 1));
     stamp(c, sm, ph, 5, tid == 0);
   }
   // ---- final norm + LM head (every CU)
@@ -1451,29 +1735,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   }
 }
 
-template <int G, int HS>
+template <int G, int HS, bool Q4>
 void* kernel_ptr() {
-  return (void*)k_decode_persistent<G, HS>;
+  return (void*)k_decode_persistent<G, HS, Q4>;
 }
 
-void* pick(int G, int hseg) {
+template <bool Q4>
+void* pick_fmt(int G, int hseg) {
   if (hseg == 2) {
     switch (G) {
-      case 1: return kernel_ptr<1, 2>();
-      case 2: return kernel_ptr<2, 2>();
-      case 4: return kernel_ptr<4, 2>();
-      case 8: return kernel_ptr<8, 2>();
+      case 1: return kernel_ptr<1, 2, Q4>();
+      case 2: return kernel_ptr<2, 2, Q4>();
+      case 4: return kernel_ptr<4, 2, Q4>();
+      case 8: return kernel_ptr<8, 2, Q4>();
     }
   } else if (hseg == 4) {
     switch (G) {
-      case 1: return kernel_ptr<1, 4>();
-      case 2: return kernel_ptr<2, 4>();
-      case 4: return kernel_ptr<4, 4>();
-      case 8: return kernel_ptr<8, 4>();
+      case 1: return kernel_ptr<1, 4, Q4>();
+      case 2: return kernel_ptr<2, 4, Q4>();
+      case 4: return kernel_ptr<4, 4, Q4>();
+      case 8: return kernel_ptr<8, 4, Q4>();
     }
   }
   return nullptr;
 }
+
+void* pick(int G, int hseg, int q4) { return q4 ? pick_fmt<true>(G, hseg) : pick_fmt<false>(G, hseg); }
 
 // Segments one wave of a CU with `units` units (rpu rows of nseg segments) loads.
 int wave_segs(int units, int rpu, int nseg) { return (units + kWaves - 1) / kWaves * rpu * nseg; }
@@ -1482,8 +1769,8 @@ int wave_segs(int units, int rpu, int nseg) { return (units + kWaves - 1) / kWav
 
 size_t persist_smem_bytes() { return sizeof(Smem); }
 
-int persist_prepare(int G, int hseg) {
-  void* fn = pick(G, hseg);
+int persist_prepare(int G, int hseg, int q4) {
+  void* fn = pick(G, hseg, q4);
   if (!fn) return -1;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
   if (e != hipSuccess) return (int)e;
@@ -1510,6 +1797,48 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
   const int G = pc.nq / pc.nkv;
   const int X = (S == 1 && pc.nkv * G <= grid / 4) ? G : 1;
   const int R = grid - pc.nkv * X * S;
+  if (pc.q4) {  // int4 roles: whole 16-row blocks, CUs in proportion to the slots (16 rows x 128 columns)
+    const int NB[4] = {pc.nqkv / 16, pc.H / 16, pc.I / 16, pc.H / 16};
+    const int NG[4] = {pc.H / 128, pc.nq * D / 128, pc.H / 128, pc.I / 128};
+    const int sets[4] = {1, 1, 2, 1};
+    const int att_rows = (int)(sizeof(Smem::att) / sizeof(float)) / kWaves;  // LDS partial rows of a CU
+    int n[4], lo_sum = 0;
+    for (int r = 0; r < 4; ++r) {
+      int lo = 1;
+      if (r == 1 || r == 3) lo = std::max(lo, (pc.H + kResMax - 1) / kResMax);  // residual rows fit the LDS slot
+      while ((NB[r] + lo - 1) / lo * 16 * sets[r] > att_rows) ++lo;
+      if (lo > NB[r]) return -1;
+      n[r] = lo;
+      lo_sum += lo;
+    }
+    if (lo_sum > R) return -1;
+    for (int sum = lo_sum; sum < R; ++sum) {
+      int best = -1;
+      double bw = -1.0;
+      for (int r = 0; r < 4; ++r) {
+        if (n[r] >= NB[r]) continue;
+        const double w = (double)NB[r] * NG[r] * sets[r] / n[r];
+        if (w > bw) {
+          bw = w;
+          best = r;
+        }
+      }
+      if (best < 0) break;
+      ++n[best];
+    }
+    out->pos = pos;
+    out->seq = seq;
+    out->S = S;
+    out->chunk = chunk;
+    out->X = X;
+    out->start[0] = 0;
+    out->start[1] = n[0];
+    out->start[2] = n[0] + pc.nkv * X * S;
+    out->start[3] = out->start[2] + n[1];
+    out->start[4] = out->start[3] + n[2];
+    out->start[5] = out->start[4] + n[3];
+    return out->start[5] == grid ? 0 : -1;
+  }
   // the GEMV roles: Q rows, O rows, gate/up row pairs, D rows
   const int N[4] = {pc.nqkv, pc.H, pc.I, pc.H};
   const int rpu[4] = {1, 1, 2, 1};
@@ -1584,8 +1913,9 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
 // launch would guarantee it, but costs ~19 us more per step here.  If the
 // device is shared and a workgroup cannot start, the resident ones give up
 // after their bounded wait and the step is reported as abandoned.
-int persist_launch(const PersistConst* dev_const, int G, int hseg, int grid, const PersistStep& st, hipStream_t s) {
-  void* fn = pick(G, hseg);
+int persist_launch(const PersistConst* dev_const, int G, int hseg, int q4, int grid, const PersistStep& st,
+                   hipStream_t s) {
+  void* fn = pick(G, hseg, q4);
   if (!fn) return -1;
   PersistStep arg = st;
   void* args[] = {(void*)&dev_const, (void*)&arg};

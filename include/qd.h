@@ -152,6 +152,13 @@ enum {
 
 /* Validate *cfg (before any HIP call), then allocate the KV cache
  * ([n_layers][n_kv_heads][max_pos][head_dim] f32 for K and for V), workspaces
+ * and RoPE tables on the current HIP device (see below).  The persistent decode
+ * step runs one workgroup per compute unit; the environment variable
+ * QD_PERSIST_CUS = n (read here) limits it to n workgroups (diagnostics and
+ * tests: more rows per CU, slices larger than the registers loaded ahead).
+ *
+ * Validate *cfg (before any HIP call), then allocate the KV cache
+ * ([n_layers][n_kv_heads][max_pos][head_dim] f32 for K and for V), workspaces
  * and RoPE tables on the current HIP device.  hip_stream is a hipStream_t
  * that all later work is enqueued on; NULL makes the handle create (and own)
  * a non-blocking stream of its own, which the legacy default stream does not

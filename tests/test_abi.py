@@ -66,10 +66,7 @@ def test_create_rejects_bad_config_before_any_hip_call(mutate, code):
     assert not h.value
 
 
-def test_int4_needs_the_graph_decode_path():
-    cfg = qd.make_config(synth.TINY_INT4, max_prefill=16, decode_path=qd.QD_DECODE_PERSISTENT)
-    rc, h = _create(cfg)
-    assert rc == -1 and not h.value
+def test_unknown_weight_format_is_rejected():
     cfg = qd.make_config(synth.TINY_INT4, max_prefill=16)
     cfg.weight_format = 7
     rc, h = _create(cfg)

@@ -10,7 +10,8 @@ kernel instantiation or launch branch that a full-size workload runs:
   the 0.6B long-context workload runs past 1536 positions;
 * the 3B-width int4 model (hidden 2048, intermediate 11008, 16/2 heads), whose
   down projection runs the 8-pass int4 GEMV and whose decode step is the
-  captured 3B-width graph.
+  captured 3B-width graph, or the persistent step with int4 slots (also on
+  64 CUs, where the slots stream in during each phase).
 
 Every logit of every step is compared with the oracle; tokens follow the
 greedy / sampled near-tie rules of gpu_util.
@@ -117,18 +118,24 @@ def test_persistent_attention_merge_beyond_eight_splits(torch_cuda, prompt_len, 
     dec.close()
 
 
-@pytest.mark.parametrize("path", ["graph"])
-def test_int4_3b_width_decode(torch_cuda, path):
+@pytest.mark.parametrize("path", ["graph", "persistent", "persistent-64cu"])
+def test_int4_3b_width_decode(torch_cuda, path, monkeypatch):
     """2-layer model at the 3B int4 widths (hidden 2048, intermediate 11008,
     16 q / 2 kv heads, q/k/v bias, no QK-norm, int4 group-128, V 4096): the
-    down projection (K = 11008) runs the 8-pass int4 GEMV, and the decode step
-    is the 3B-width step replayed 16 times.  8-token prompt, every step's
-    logits checked."""
+    down projection (K = 11008) runs the 8-pass int4 GEMV on the graph path and
+    86 groups over 8 waves (ragged) with streamed slots on the persistent path;
+    the decode step is the 3B-width step run 16 times.  With the persistent
+    step on 64 CUs, every GEMV CU holds more slots than it loads ahead (up to
+    ~170 per wave), so most of its weights stream in during the phase, as at
+    the 16K-context shape.  8-token prompt, every step's logits checked."""
     shape = QWEN25_INT4_2L
     log(f"3B-width int4, path={path}")
     w = synth.make_weights(shape, seed=45, random_gains=True)
     oracle = OracleModel(shape, w)
-    dec = make_decoder(torch_cuda, shape, 16, path)
+    if path == "persistent-64cu":
+        monkeypatch.setenv("QD_PERSIST_CUS", "64")
+    dec = make_decoder(torch_cuda, shape, 16, path.split("-")[0])
+    monkeypatch.delenv("QD_PERSIST_CUS", raising=False)
     dw = to_device(w)
     torch_cuda.cuda.synchronize()
     dec.load_weights(dw)

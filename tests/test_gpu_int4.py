@@ -34,9 +34,10 @@ def torch_cuda():
     return torch
 
 
-def make_decoder(torch_cuda, shape, max_prefill):
+def make_decoder(torch_cuda, shape, max_prefill, path="graph"):
     import decoder_only_token_amd as qd
-    cfg = qd.make_config(shape, max_prefill=max_prefill, decode_path=qd.QD_DECODE_GRAPH)
+    cfg = qd.make_config(shape, max_prefill=max_prefill,
+                         decode_path=qd.QD_DECODE_GRAPH if path == "graph" else qd.QD_DECODE_PERSISTENT)
     return qd.Decoder(cfg, torch_cuda.cuda.current_stream().cuda_stream)
 
 
@@ -80,14 +81,18 @@ def test_int4_quantiser_matches_oracle_encoding(torch_cuda, shape_name):
     assert list(c[2, :9]) == [7, 2, -2, 0, 0, 2, -2, 4, -7] and s[2, 0] == np.float16(0.25)
 
 
+@pytest.mark.parametrize("path", ["graph", "persistent"])
 @pytest.mark.parametrize("shape_name", ["TINY_INT4", "TINY_INT4_WIDE"])
-def test_tiny_int4_prefill_and_decode(torch_cuda, shape_name):
-    """8-token prompt (int4 GEMVs, two row tiles), then 16 greedy steps, every step checked."""
+def test_tiny_int4_prefill_and_decode(torch_cuda, shape_name, path):
+    """8-token prompt (int4 GEMVs, two row tiles), then 16 greedy steps, every
+    step checked; the decode steps run as the per-operation graph or as the
+    persistent kernel (int4 slots on the int8 matrix cores; the 1408-column
+    down projection of TINY_INT4 leaves 3 of the 8 waves a second group)."""
     shape = getattr(synth, shape_name)
-    log(f"int4 decode {shape.name}")
+    log(f"int4 decode {shape.name} path={path}")
     w = synth.make_weights(shape, seed=42, random_gains=True)
     oracle = OracleModel(shape, w)
-    dec = make_decoder(torch_cuda, shape, 16)
+    dec = make_decoder(torch_cuda, shape, 16, path)
     dw = to_device(w)
     torch_cuda.cuda.synchronize()
     dec.load_weights(dw)
