@@ -22,6 +22,7 @@ QD_ABI_VERSION = 1
 QD_W_BF16, QD_W_INT4_G128 = 0, 1
 QD_DECODE_PERSISTENT, QD_DECODE_GRAPH = 0, 1
 QD_CAP_EMBED, QD_CAP_LAYER_OUT, QD_CAP_FINAL_NORM, QD_CAP_LOGITS = 0, 1, 2, 3
+QD_XCH = {"x0": 0, "x1": 1, "qkv": 2, "attn": 3, "act": 4}
 QD_PROJ = {"wq": 0, "wk": 1, "wv": 2, "wo": 3, "w_gate": 4, "w_up": 5, "w_down": 6}
 STATUS = {0: "QD_OK", -1: "QD_E_ARG", -2: "QD_E_ABI", -3: "QD_E_STATE", -4: "QD_E_RANGE", -5: "QD_E_OOM",
           -6: "QD_E_HIP"}
@@ -58,7 +59,7 @@ class QdLora(ctypes.Structure):
 
 EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_decode_step", "qd_set_lora",
            "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_enable_phase_trace", "qd_get_phase_trace",
-           "qd_get_quantized", "qd_sync_token", "qd_get_abandoned", "qd_get_position",
+           "qd_get_quantized", "qd_get_exchange", "qd_sync_token", "qd_get_abandoned", "qd_get_position",
            "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
            "qd_sizeof_lora"]
 
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_int32)]),
         "qd_get_quantized": (i32, [H, i32, i32, ctypes.POINTER(ctypes.c_int8), sz, ctypes.POINTER(ctypes.c_uint16),
                                    sz]),
+        "qd_get_exchange": (i32, [H, i32, ctypes.POINTER(ctypes.c_float), sz, ctypes.POINTER(sz)]),
         "qd_sync_token": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
         "qd_get_abandoned": (i32, [H, ctypes.POINTER(ctypes.c_int64)]),
         "qd_get_position": (i32, [H, ctypes.POINTER(ctypes.c_int32)]),
@@ -205,9 +207,9 @@ class Decoder:
             self.h = None
 
     def __del__(self):
-        if sys.is_finalizing():  # the HIP runtime may already be gone; _close_all ran earlier
-            return
         try:
+            if sys.is_finalizing():  # the HIP runtime may already be gone; _close_all ran earlier
+                return
             self.close()
         except Exception:
             pass
@@ -291,6 +293,15 @@ class Decoder:
                                               codes.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), codes.size,
                                               scales.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), scales.size))
         return codes, scales.view(np.float16)
+
+    def get_exchange(self, name: str, n: int):
+        """A persistent-step exchange buffer ("x0", "x1", "qkv", "attn", "act") after the last step."""
+        import numpy as np
+        out = np.empty(n, dtype=np.float32)
+        written = ctypes.c_size_t()
+        self._check(self.lib.qd_get_exchange(self.h, QD_XCH[name], out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                             n, ctypes.byref(written)))
+        return out[:written.value]
 
     def sync_token(self) -> int:
         t = ctypes.c_int32()

@@ -693,8 +693,8 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
     std::vector<LayerPtrs> lp(c.n_layers);
     for (int l = 0; l < c.n_layers; ++l) {
       const Layer& L = h->layers[l];
-      lp[l] = LayerPtrs{L.wqkv, L.bqkv, L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm, L.wo,  L.wg,  L.wu,
-                        L.wd,   L.cqkv, L.co,        L.cg,       L.cd,     L.sqkv,   L.so, L.sg, L.sd};
+      lp[l] = LayerPtrs{L.wqkv, L.bqkv, L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm, L.wo, L.wg, L.wu, L.wd,
+                        {L.cqkv, L.co, L.cg, L.cd}, {L.sqkv, L.so, L.sg, L.sd}};
     }
     PersistConst pc{};
     pc.L = c.n_layers; pc.H = c.hidden; pc.nq = c.n_q_heads; pc.nkv = c.n_kv_heads; pc.I = c.intermediate;
@@ -899,6 +899,40 @@ int qd_get_phase_trace(qd_handle* h, uint64_t* out_host, size_t capacity_elems, 
   HIP_TRY(h, hipMemcpy(out_host, h->trace, n * 8, hipMemcpyDeviceToHost));
   if (written_elems) *written_elems = n;
   if (n_cu) *n_cu = h->grid;
+  return QD_OK;
+}
+
+int qd_get_exchange(qd_handle* h, int32_t which, float* out_host, size_t capacity_elems, size_t* written_elems) {
+  if (!h) return QD_E_ARG;
+  if (!out_host) return h->set_err(QD_E_ARG, "out_host is NULL");
+  if (!h->persistent) return h->set_err(QD_E_STATE, "exchange buffers belong to the persistent decode step");
+  const qd_config& c = h->cfg;
+  const uint64_t* src = nullptr;
+  size_t n = 0;
+  bool pairs = false;
+  switch (which) {
+    case QD_XCH_X0: src = h->X0; n = c.hidden; break;
+    case QD_XCH_X1: src = h->X1; n = c.hidden; break;
+    case QD_XCH_QKV: src = h->QKVx; n = (size_t)qkv_rows(c); break;
+    case QD_XCH_ATTN: src = h->Ox; n = (size_t)c.n_q_heads * c.head_dim; pairs = true; break;
+    case QD_XCH_ACT: src = h->ACT; n = c.intermediate; pairs = true; break;
+    default: return h->set_err(QD_E_ARG, "unknown exchange buffer");
+  }
+  if (capacity_elems < n) return h->set_err(QD_E_ARG, "capacity smaller than the buffer");
+  std::vector<uint64_t> words(pairs ? n / 2 : n);
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipMemcpy(words.data(), src, words.size() * 8, hipMemcpyDeviceToHost));
+  for (size_t i = 0; i < words.size(); ++i) {
+    if (pairs) {  // {tag16 | a24 | b24}: the top 24 bits of two floats
+      const uint32_t a = (uint32_t)((words[i] >> 24) & 0xFFFFFFu) << 8, b = (uint32_t)(words[i] & 0xFFFFFFu) << 8;
+      memcpy(out_host + 2 * i, &a, 4);
+      memcpy(out_host + 2 * i + 1, &b, 4);
+    } else {
+      const uint32_t a = (uint32_t)words[i];
+      memcpy(out_host + i, &a, 4);
+    }
+  }
+  if (written_elems) *written_elems = n;
   return QD_OK;
 }
 

@@ -17,17 +17,12 @@ struct LayerPtrs {
   const uint16_t* wg;  // [I][H]
   const uint16_t* wu;  // [I][H]
   const uint16_t* wd;  // [H][I]
-  // int4 group-128 weights (codes u8 [rows][in / 2], fp16 scales [rows][in / 128],
-  // same row order as the bf16 matrices above, which are then null); the up
-  // rows' codes and scales follow the gate rows' in one allocation each
-  const uint8_t* cqkv;
-  const uint8_t* co;
-  const uint8_t* cg;
-  const uint8_t* cd;
-  const uint16_t* sqkv;
-  const uint16_t* so;
-  const uint16_t* sg;
-  const uint16_t* sd;
+  // int4 group-128 weights of the four projections q|k|v, o, gate (+ up), down,
+  // in that order (codes u8 [rows][in / 2], fp16 scales [rows][in / 128], same
+  // row order as the bf16 matrices above, which are then null); the up rows'
+  // codes and scales follow the gate rows' in one allocation each
+  const uint8_t* qcode[4];
+  const uint16_t* qscale[4];
 };
 
 // Everything the decode kernel needs that does not change from step to step.

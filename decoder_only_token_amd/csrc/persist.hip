@@ -558,18 +558,15 @@ __device__ __forceinline__ Q4Geo q4_geo(const Ctx& c, int l) {
   const AS4 PersistConst& a = *c.a;
   const AS4 LayerPtrs& L = ((const AS4 LayerPtrs*)a.layers)[l];
   Q4Geo q;
-  q.ns = 1;
-  q.dc = q.ds = 0;
-  switch (c.role) {
-    case kQKV: q.K = a.H; q.c = L.cqkv; q.s = L.sqkv; break;
-    case kOproj: q.K = a.nq * D; q.c = L.co; q.s = L.so; break;
-    case kGateUp:
-      q.K = a.H; q.c = L.cg; q.s = L.sg; q.ns = 2;
-      q.dc = a.I * (a.H >> 1);
-      q.ds = a.I * (a.H >> 7);
-      break;
-    default: q.K = a.I; q.c = L.cd; q.s = L.sd; break;
-  }
+  // the projection of the role (q|k|v 0, o 1, gate/up 2, down 3), selected by
+  // index rather than by a branch per role
+  const int p = c.role - (c.role > kAttn ? 1 : 0);
+  q.c = L.qcode[p];
+  q.s = L.qscale[p];
+  q.K = c.role == kOproj ? a.nq * D : c.role == kDown ? a.I : a.H;
+  q.ns = c.role == kGateUp ? 2 : 1;
+  q.dc = c.role == kGateUp ? a.I * (a.H >> 1) : 0;
+  q.ds = c.role == kGateUp ? a.I * (a.H >> 7) : 0;
   q.ng = q.K >> 7;
   q.nrows = c.r1 - c.r0;
   q.nb = (q.nrows + 15) >> 4;

@@ -227,6 +227,20 @@ int qd_enable_phase_trace(qd_handle* h, int32_t enable);
 int qd_get_phase_trace(qd_handle* h, uint64_t* out_host, size_t capacity_elems, size_t* written_elems,
                        int32_t* n_cu);
 
+/* Exchange buffers of the persistent decode step (diagnostics): after a step
+ * they hold the LAST layer's values of that step (which argument):
+ *   QD_XCH_X0   f32 [hidden]        residual after the last layer (the final norm's input)
+ *   QD_XCH_X1   f32 [hidden]        residual after the last layer's attention block
+ *   QD_XCH_QKV  f32 [(nq+2nkv) d]   raw q|k|v projection (+bias, +LoRA), kv-group-major
+ *                                   ([kv head g][q heads of g | k_g | v_g] x d)
+ *   QD_XCH_ATTN f32 [nq d]          attention output, 16 significant bits
+ *   QD_XCH_ACT  f32 [intermediate]  SiLU(gate) * up, 16 significant bits
+ * qd_get_exchange synchronises the stream and copies one of them into
+ * out_host.  Errors: QD_E_STATE (not the persistent path), QD_E_ARG (NULL
+ * output, unknown buffer, capacity too small), QD_E_HIP. */
+enum { QD_XCH_X0 = 0, QD_XCH_X1 = 1, QD_XCH_QKV = 2, QD_XCH_ATTN = 3, QD_XCH_ACT = 4 };
+int qd_get_exchange(qd_handle* h, int32_t which, float* out_host, size_t capacity_elems, size_t* written_elems);
+
 /* Projections of a layer, for qd_get_quantized. */
 enum { QD_PROJ_Q = 0, QD_PROJ_K = 1, QD_PROJ_V = 2, QD_PROJ_O = 3, QD_PROJ_GATE = 4, QD_PROJ_UP = 5, QD_PROJ_DOWN = 6 };
 

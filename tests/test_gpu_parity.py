@@ -428,3 +428,21 @@ def test_chunked_prefill_attention(torch_cuda, shape_name, chunks):
         log(f"after {at} rows: err/tol {ratio:.3f}")
         assert ok, (at, ratio, nbad)
     assert dec.position == at
+
+
+@pytest.mark.parametrize("path", ["persistent", "graph"])
+def test_tiny_eight_query_heads_per_kv_head(torch_cuda, path):
+    """bf16 model of the 3B family's structure (16 q / 2 kv heads: 8 query
+    heads per kv head, q/k/v bias, no QK-norm) at 2 layers: 8-token prompt,
+    16 greedy steps, every step checked on both decode paths."""
+    shape = dataclasses.replace(synth.TINY_INT4, name="tiny-g8-bf16", weight_format=synth.W_BF16)
+    log(f"tiny G=8 bf16 path={path}")
+    w = synth.make_weights(shape, seed=29, random_gains=True)
+    oracle = OracleModel(shape, w)
+    dec = make_decoder(torch_cuda, shape, 16, path=path)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    prompt = synth.make_prompt(shape.vocab, 8, seed=30)
+    recs = lockstep_greedy(dec, oracle, prompt, 16, log=log)
+    assert_records(recs, max_forced=1)
