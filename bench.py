@@ -1,14 +1,23 @@
-"""Benchmark: single-sequence decode (and prefill) of a Qwen3-style decoder on one MI355X.
+"""Benchmark: single-sequence decode (and prefill) of a Qwen-style decoder on one MI355X.
 
-One timed step = one whole generation job of the workload: reset the KV cache,
-batched prefill of the prompt, then the workload's greedy decode steps, all
-through the C ABI on one HIP stream, with weights and inputs resident in HBM.
+Headline workload (default): qwen2.5-3b-int4-lora, the largest one-GPU
+configuration (36 layers, hidden 2048, 16/2 heads, int4 group-128 projection
+weights, rank-16 LoRA on q/v, 16,384-position f32 KV cache).  One timed step
+is one decode token at the end of the context: the cache is filled untimed
+(the workload's 8192-token prompt as one batched prefill, then batched
+prefills of random tokens) to 16384 - warmup - steps positions, then `warmup`
+untimed and `steps` timed decode steps run back to back on one HIP stream
+(device-resident token feedback, one host synchronisation at the end), the
+last one reaching position 16383.  Weights, prompt and cache are resident in
+HBM before timing starts.
 
-Prints ONE JSON line.  `value` = generated tokens per second over the whole
-job (prefill token + decode tokens); decode-only and prefill rates, the
-effective HBM bandwidth and the dominant kernel's roofline fraction are
-reported beside it.  The CPU oracle is timed on a bounded sample of the same
-workload on the host cores (`cpu_baseline`).
+Prints ONE JSON line: `value` = decode tokens / second over the timed steps;
+beside it the roofline of the decode kernel (algorithmic bytes per step =
+weights + LoRA factors + tied LM head + one embedding row + KV read and
+write, over the step's measured time), the workload's batched prefill
+(tokens / s, projection TFLOP/s, MFMA use), the qwen3-0.6b decode job of the
+previous measurements as extra keys, and the CPU oracle timed on a bounded
+sample of the same decode step (`cpu_baseline`).
 """
 from __future__ import annotations
 
@@ -28,18 +37,15 @@ MFMA_PEAK_BF16_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="qwen3-0.6b")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-rows", type=int, default=512,
-                    help="also time one batched prefill of this many random tokens (0: skip)")
-    ap.add_argument("--cpu-sample-steps", type=int, default=128)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen2.5-3b-int4-lora")
     ap.add_argument("--path", choices=["auto", "persistent", "graph"], default="auto",
                     help="decode step as one persistent kernel, or as per-operation kernels in a hipGraph "
-                         "(auto: persistent where the model allows it: bf16 weights, no adapter)")
-    ap.add_argument("--decode-steps", type=int, default=0,
-                    help="decode steps per job (0: the workload's own count)")
+                         "(auto: the persistent kernel)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the qwen3-0.6b job and the prefill timing")
+    ap.add_argument("--only-decode", action="store_true", help="decode timing only (for profiler runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 launches): the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -94,54 +100,97 @@ def calibrate_copy(mib: int):
                       "bytes_written_per_launch": n * 4, "launches": 5}), flush=True)
 
 
-def blas_threads() -> int:
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
-    except Exception:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
         pass
-    return len(os.sched_getaffinity(0))
+    return "unknown"
 
 
-def cpu_baseline(wl, weights, prompt, n_steps, min_seconds=10.0, max_jobs=8):
-    """Time the oracle (as it stands) on the host: jobs of prompt + n_steps
-    incremental greedy steps, repeated until about min_seconds of CPU work."""
-    from oracle import OracleModel, argmax_lowest
-    t_build = time.perf_counter()
-    m = OracleModel(wl.shape, weights)
-    t_build = time.perf_counter() - t_build
-    toks, jobs = 0, 0
-    t0 = time.perf_counter()
-    while jobs < max_jobs and (jobs == 0 or time.perf_counter() - t0 < min_seconds):
-        cache = m.new_cache(len(prompt) + n_steps + 1)
-        logits = m.forward(prompt, cache, logits_rows="last")[-1]
-        toks += 1
-        for _ in range(n_steps):
-            logits = m.forward([argmax_lowest(logits)], cache, logits_rows="last")[-1]
-            toks += 1
-        jobs += 1
-    dt = time.perf_counter() - t0
-    cores = blas_threads()
-    return {"value": toks / dt, "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{wl.name}: float64 numpy oracle, {jobs} job(s) of prefill {len(prompt)} tokens + {n_steps} "
-                      f"greedy decode steps with its own KV cache ({toks} tokens in {dt:.1f} s; weight widening "
-                      f"{t_build:.1f} s not counted); {cores} BLAS threads"}
-
-
-def measure_long_prefill(dec, stream, shape, wl, args):
-    """Time a batched prefill of args.prefill_rows seeded random tokens on the
-    same model (the projections run on the matrix cores).  FLOP counts are the
-    algorithmic ones: 2 per weight per row for the projections, plus the causal
-    attention products (2 * 2 * d per visible key per q head)."""
-    import numpy as np
-    import torch
+def step_bytes(shape, lora_rank, ctx):
+    """Algorithmic HBM bytes of one decode step whose context after the step is
+    ctx: every weight once (layers, LoRA factors, tied head, one gathered row),
+    the KV read of ctx - 1 cached positions and the write of the new one."""
     import synth
-    n = args.prefill_rows
-    if n > wl.max_prefill or n > shape.max_pos:
-        return None
-    toks = synth.make_prompt(shape.vocab, n, seed=7)
+    wb = synth.weight_bytes(shape, lora_rank)
+    return wb["layers"] + wb["lora"] + wb["lm_head"] + wb["embed_row"] + synth.kv_bytes_per_position(shape) * ctx
+
+
+def make_decoder(wl, path, stream, dw, dl=None):
+    import torch
+    import decoder_only_token_amd as qd
+    cfg = qd.make_config(wl.shape, max_prefill=wl.max_prefill, lora_rank_max=wl.lora_rank,
+                         decode_path=qd.QD_DECODE_PERSISTENT if path == "persistent" else qd.QD_DECODE_GRAPH)
+    dec = qd.Decoder(cfg, stream.cuda_stream)
+    dec.load_weights(dw)
+    if dl is not None:
+        dec.set_lora(dl, wl.lora_rank, wl.lora_alpha)
+    torch.cuda.synchronize()
+    return dec
+
+
+def fill_to(dec, wl, stream, target):
+    """Untimed: reset, the workload's prompt as one batched prefill, then
+    batched prefills of random tokens until `target` positions are cached."""
+    import synth
+    import torch
+    shape = wl.shape
+    with torch.cuda.stream(stream):
+        dec.reset_kv()
+        prompt = synth.make_prompt(shape.vocab, min(wl.prompt_len, target))
+        dec.prefill(prompt)
+        at, k = len(prompt), 0
+        while at < target:
+            n = min(wl.max_prefill, target - at)
+            dec.prefill(synth.make_prompt(shape.vocab, n, seed=100 + k))
+            at += n
+            k += 1
+    dec.sync_token()
+    assert dec.position == target
+
+
+def decode_at_end(dec, wl, stream, steps, warmup):
+    """`warmup` untimed and `steps` timed decode steps ending at the last
+    cache position; HIP events on the library's stream bracket the timed steps."""
+    import torch
+    end = wl.shape.max_pos
+    start = end - steps - warmup
+    fill_to(dec, wl, stream, start)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            dec.decode_step()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(steps):
+            dec.decode_step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    if dec.abandoned():
+        raise RuntimeError("a persistent decode step was abandoned (device shared with other work)")
+    ms = a.elapsed_time(b)
+    ctx0 = start + warmup + 1  # context after the first timed step
+    byts = [step_bytes(wl.shape, wl.lora_rank, ctx0 + i) for i in range(steps)]
+    return {"steps": steps, "wall_s": wall, "event_ms": ms, "ctx_first": ctx0, "ctx_last": ctx0 + steps - 1,
+            "bytes_per_step": sum(byts) / steps}
+
+
+def prefill_rate(dec, wl, stream, rows):
+    """Median of 3 batched prefills of `rows` tokens from an empty cache; FLOPs
+    are the algorithmic ones (2 per weight per row for the projections, the
+    LoRA products, and 2 * 2 * d per visible key per q head for attention)."""
+    import numpy as np
+    import synth
+    import torch
+    shape = wl.shape
+    toks = synth.make_prompt(shape.vocab, rows, seed=7)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     times = []
     with torch.cuda.stream(stream):
@@ -159,13 +208,112 @@ def measure_long_prefill(dec, stream, shape, wl, args):
     H, d, I, L = shape.hidden, shape.head_dim, shape.intermediate, shape.n_layers
     nq, nkv = shape.n_q_heads, shape.n_kv_heads
     lin = (nq * d + 2 * nkv * d) * H + H * nq * d + 2 * I * H + H * I
-    proj = 2.0 * n * lin * L
-    attn = 2.0 * 2.0 * d * nq * L * (n * (n + 1) / 2)
-    return {"rows": n, "ms": round(ms, 3), "tok_s": round(n / (ms * 1e-3), 1),
+    lora = wl.lora_rank * (2 * H + nq * d + nkv * d)
+    proj = 2.0 * rows * (lin + lora) * L
+    attn = 2.0 * 2.0 * d * nq * L * (rows * (rows + 1) / 2)
+    return {"rows": rows, "ms": round(ms, 3), "tok_s": round(rows / (ms * 1e-3), 1),
             "projection_tflops": round(proj / (ms * 1e-3) / 1e12, 2),
-            "mfma_util_lower_bound": round(proj / (ms * 1e-3) / (MFMA_PEAK_BF16_TFLOPS * 1e12), 4),
-            "note": "whole prefill time (projections, attention, norms, LM head row); projection FLOPs "
-                    "counted once although the hi/lo input split issues each product twice"}
+            "attention_tflops": round(attn / (ms * 1e-3) / 1e12, 2),
+            "mfma_util_lower_bound": round((proj + attn) / (ms * 1e-3) / (MFMA_PEAK_BF16_TFLOPS * 1e12), 4),
+            "note": "whole prefill time (projections on the matrix cores, attention, norms, LM head row); "
+                    "algorithmic FLOPs over the bf16 dense peak (the hi/lo input split issues each product twice)"}
+
+
+def job_06b(stream, path):
+    """qwen3-0.6b: jobs of reset + 5-token prefill + 128 greedy decode steps
+    (the configuration of the earlier measurements), decode roofline."""
+    import numpy as np
+    import synth
+    import torch
+    wl = synth.WORKLOADS["qwen3-0.6b"]
+    dw = synth.make_weights_device(wl.shape)
+    dec = make_decoder(wl, path, stream, dw)
+    del dw
+    prompt = synth.make_prompt(wl.shape.vocab, wl.prompt_len)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    dts = []
+    with torch.cuda.stream(stream):
+        for i in range(4):
+            dec.reset_kv()
+            dec.prefill(prompt)
+            a, b = ev(), ev()
+            a.record(stream)
+            for _ in range(wl.decode_steps):
+                dec.decode_step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                dts.append(a.elapsed_time(b))
+    if dec.abandoned():
+        raise RuntimeError("a persistent decode step was abandoned")
+    dec.close()
+    ms = float(np.median(dts))
+    n = wl.decode_steps
+    byts = sum(step_bytes(wl.shape, 0, wl.prompt_len + 1 + i) for i in range(n)) / n
+    us = ms * 1e3 / n
+    ach = byts / (us * 1e-6) / 1e9
+    return {"workload": wl.name, "decode_tok_s": round(n / (ms * 1e-3), 1), "decode_step_us": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name)}}
+
+
+def cpu_baseline(wl, dw, dl, ctx):
+    """The float64 oracle on a bounded sample of the timed step: one decode
+    token at context `ctx`, on the model cut to 1 and to 2 layers (its KV cache
+    filled with seeded random keys and values for ctx - 1 positions: the
+    arithmetic does not depend on their values), plus the tied head; the
+    36-layer time is t(1) + 35 (t(2) - t(1)).  Timed with all host threads and
+    with one thread."""
+    import dataclasses
+    import numpy as np
+    import synth
+    from oracle import OracleModel
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    shape = wl.shape
+    host = synth.device_to_host(dw, layers=[0, 1])
+    lora = None
+    if dl is not None:
+        lora = [{k: v.cpu().numpy().view(np.uint16) for k, v in dl[i].items()} for i in (0, 1)]
+    t_build = time.perf_counter()
+    models = {}
+    for nl in (1, 2):
+        s = dataclasses.replace(shape, n_layers=nl)
+        sub = {"embed": host["embed"], "final_norm": host["final_norm"], "layers": host["layers"][:nl]}
+        models[nl] = OracleModel(s, sub, lora=lora[:nl] if lora else None, lora_alpha=wl.lora_alpha)
+    t_build = time.perf_counter() - t_build
+    rng = np.random.default_rng(11)
+
+    def one_token(m):
+        cache = m.new_cache(ctx)
+        for li in range(m.shape.n_layers):
+            cache.k[li][:ctx - 1] = rng.standard_normal((ctx - 1, shape.n_kv_heads, shape.head_dim))
+            cache.v[li][:ctx - 1] = rng.standard_normal((ctx - 1, shape.n_kv_heads, shape.head_dim))
+        cache.length = ctx - 1
+        t = time.perf_counter()
+        m.forward([1234], cache, logits_rows="last")
+        return time.perf_counter() - t
+
+    def estimate(reps):
+        t1 = min(one_token(models[1]) for _ in range(reps))
+        t2 = min(one_token(models[2]) for _ in range(reps))
+        return t1 + (shape.n_layers - 1) * max(t2 - t1, 0.0), t1, t2
+
+    cores = len(os.sched_getaffinity(0))
+    t_all, t1, t2 = estimate(3)
+    t_one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t_one = estimate(1)[0]
+    return {"value": round(1.0 / t_all, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "one_thread_tok_s": round(1.0 / t_one, 5) if t_one else None,
+            "sample": f"{wl.name}: float64 numpy oracle, one decode token at context {ctx} on the model cut to "
+                      f"1 and 2 layers (KV cache filled with seeded random values), 36-layer time = t1 + 35 (t2 - t1) "
+                      f"= {t_all:.3f} s (t1 {t1:.3f} s, t2 {t2:.3f} s, best of 3; weight widening {t_build:.1f} s "
+                      f"not counted); {cores} host threads"}
 
 
 def main():
@@ -176,92 +324,22 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
-    import numpy as np
     import torch
     import synth
-    import decoder_only_token_amd as qd
 
     wl = synth.WORKLOADS[args.workload]
     shape = wl.shape
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
-    weights = synth.make_weights(shape)
-    prompt = synth.make_prompt(shape.vocab, wl.prompt_len)
-    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
-    dw = {"embed": to_dev(weights["embed"]), "final_norm": to_dev(weights["final_norm"]),
-          "layers": [{k: to_dev(v) for k, v in lw.items()} for lw in weights["layers"]]}
+    path = ("graph" if wl.lora_rank else "persistent") if args.path == "auto" else args.path
+    dw = synth.make_weights_device(shape)
+    dl = synth.make_lora_device(shape, wl.lora_rank) if wl.lora_rank else None
     torch.cuda.synchronize()
-    if args.path == "auto":
-        args.path = "persistent" if shape.weight_format == synth.W_BF16 and not wl.lora_rank else "graph"
-    path = qd.QD_DECODE_PERSISTENT if args.path == "persistent" else qd.QD_DECODE_GRAPH
-    dec = qd.Decoder(qd.make_config(shape, max_prefill=wl.max_prefill, lora_rank_max=wl.lora_rank,
-                                    decode_path=path), stream.cuda_stream)
-    dec.load_weights(dw)
-    del dw
-    if wl.lora_rank:
-        lora = synth.make_lora(shape, wl.lora_rank)
-        dl = [{k: to_dev(v) for k, v in lw.items()} for lw in lora]
-        torch.cuda.synchronize()
-        dec.set_lora(dl, wl.lora_rank, wl.lora_alpha)
-        del dl
-    torch.cuda.synchronize()
-    n_dec = args.decode_steps or wl.decode_steps
-    sampling = (qd.make_sampling(wl.temperature, wl.top_k, wl.top_p, synth.SEED_SAMPLING)
-                if wl.temperature > 0 else None)
-
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-
-    def job(marks=None, samp=None):
-        dec.reset_kv()
-        if marks:
-            marks[0].record(stream)
-        dec.prefill(prompt, sampling=samp)
-        if marks:
-            marks[1].record(stream)
-        for _ in range(n_dec):
-            dec.decode_step(sampling=samp)
-        if marks:
-            marks[2].record(stream)
-
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            job()
-        torch.cuda.synchronize()
-        marks = [[ev(), ev(), ev()] for _ in range(args.steps)]
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            job(marks[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    dec.sync_token()  # raises if any decode step was abandoned
-    sampled = None
-    if sampling is not None:
-        with torch.cuda.stream(stream):
-            m = [ev(), ev(), ev()]
-            job(m, sampling)
-            torch.cuda.synchronize()
-        dec.sync_token()
-        s_ms = m[1].elapsed_time(m[2])
-        sampled = {"temperature": wl.temperature, "top_k": wl.top_k, "top_p": wl.top_p, "seed": synth.SEED_SAMPLING,
-                   "decode_tok_s": round(n_dec / (s_ms * 1e-3), 2), "decode_step_us": round(s_ms * 1e3 / n_dec, 2),
-                   "note": "one job with on-GPU top-k / temperature / top-p draws (greedy is the headline)"}
-    long_prefill = measure_long_prefill(dec, stream, shape, wl, args) if args.prefill_rows else None
-    prefill_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
-    decode_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-    tokens_per_job = 1 + n_dec
-    value = tokens_per_job * args.steps / wall
-
-    kvp = synth.kv_bytes_per_position(shape)
-    # algorithmic HBM bytes of one decode step at context c: all weights once
-    # (layers + tied head + one gathered row), KV read for c positions, KV write of one position
-    ctx0 = wl.prompt_len
-    wb = synth.weight_bytes(shape, wl.lora_rank)
-    dec_bytes = sum((wb["layers"] + wb["lora"] + wb["lm_head"] + wb["embed_row"]) + kvp * (ctx0 + i + 1)
-                    for i in range(n_dec))
-    decode_step_us = decode_ms * 1e3 / n_dec
-    achieved = dec_bytes / n_dec / (decode_step_us * 1e-6) / 1e9
-    traffic = measured_traffic(wl.name) if args.path == "persistent" else None
+    dec = make_decoder(wl, path, stream, dw, dl)
+    d = decode_at_end(dec, wl, stream, args.steps, args.warmup)
+    us = d["event_ms"] * 1e3 / args.steps
+    achieved = d["bytes_per_step"] / (us * 1e-6) / 1e9
+    value = args.steps / d["wall_s"]
     out = {
         "metric": "decode tok/s + achieved HBM GB/s (% of peak); prefill tok/s, 1 MI355X",
         "value": round(value, 2),
@@ -269,37 +347,43 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step": round(d["wall_s"] * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("int4-g128 projection weights with fp16 scales, bf16 tied embedding"
-                  if shape.weight_format == synth.W_INT4_G128 else "bf16 weights") +
-                 ", f32 activations/accumulation/KV",
-        "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform random prompt ids)",
-        "config": {"workload": wl.name, "model": shape.name, "layers": shape.n_layers, "hidden": shape.hidden,
-                   "heads": [shape.n_q_heads, shape.n_kv_heads], "vocab": shape.vocab,
-                   "prompt_len": wl.prompt_len, "decode_steps": n_dec, "global_batch": 1,
-                   "parallelism": "single GPU", "decode_path": args.path,
+        "dtype": ("int4 group-128 projection weights x fp16 scales, int8 matrix-core products against the input "
+                  "split into three 7-bit pieces (2^-21 of the group maximum)" if shape.weight_format == synth.W_INT4_G128
+                  else "bf16 weights, matrix-core GEMV with the input as bf16 hi/lo halves (16 significant bits)") +
+                 "; bf16 tied embedding and LoRA factors; f32 accumulation, residual and KV cache; attention output "
+                 "and SwiGLU activations exchanged at 16 significant bits",
+        "data": "synthetic (seeded N(0,0.02) weights drawn on the GPU and rounded to bf16, uniform random token ids)",
+        "config": {"workload": wl.name, "layers": shape.n_layers, "hidden": shape.hidden,
+                   "heads": [shape.n_q_heads, shape.n_kv_heads], "intermediate": shape.intermediate,
+                   "vocab": shape.vocab, "prompt_len": wl.prompt_len, "max_pos": shape.max_pos,
+                   "decode_context": [d["ctx_first"], d["ctx_last"]], "global_batch": 1,
+                   "parallelism": "single GPU", "decode_path": path,
                    "lora": {"rank": wl.lora_rank, "alpha": wl.lora_alpha} if wl.lora_rank else None},
-        "decode_tok_s": round(n_dec / (decode_ms * 1e-3), 2),
-        "decode_step_us": round(decode_step_us, 2),
-        "prefill_tok_s": round(wl.prompt_len / (prefill_ms * 1e-3), 2),
-        "prefill_ms": round(prefill_ms, 3),
+        "decode_tok_s": round(args.steps / (d["event_ms"] * 1e-3), 2),
+        "decode_step_us": round(us, 2),
         "decode_hbm_gbs_effective": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("k_decode_persistent (one launch = one decode step)" if args.path == "persistent"
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name) if path == "persistent" else None,
+                     "kernel": ("k_decode_persistent (one launch = one decode step)" if path == "persistent"
                                 else "decode step (captured graph of per-operation kernels)") +
-                               "; algorithmic bytes = weights + KV read + KV write"},
+                               f"; algorithmic bytes per step = {d['bytes_per_step']:.4g} (weights + LoRA + tied "
+                               "head + one embedding row + KV read and write at the step's context)"},
     }
-    if long_prefill:
-        out["prefill_batched"] = long_prefill
-    if sampled:
-        out["sampled"] = sampled
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, weights, prompt, args.cpu_sample_steps)
+    if not args.only_decode and not args.no_extra:
+        out["prefill_batched"] = prefill_rate(dec, wl, stream, wl.prompt_len)
+    if not args.only_decode and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, dw, dl, shape.max_pos)
     dec.close()
+    del dw, dl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.only_decode and not args.no_extra and wl.name != "qwen3-0.6b":
+        out["qwen3_0_6b"] = job_06b(stream, "persistent" if args.path == "auto" else args.path)
     print(json.dumps(out), flush=True)
 
 

@@ -225,3 +225,56 @@ def weight_bytes(shape: ModelShape, lora_rank: int = 0) -> Dict[str, int]:
 def kv_bytes_per_position(shape: ModelShape) -> int:
     """f32 K and V for one position across all layers."""
     return shape.n_layers * 2 * shape.n_kv_heads * shape.head_dim * 4
+
+
+def make_weights_device(shape: ModelShape, seed: int = SEED_WEIGHTS, std: float = 0.02, device: str = "cuda"):
+    """The same weight set structure drawn on the GPU (torch's counter-based
+    Philox generator seeded with `seed`, N(0, std) in float32 rounded to bf16
+    by torch's round-to-nearest-even conversion), returned as int16 device
+    tensors holding the bf16 bit patterns; gains 1.0.  Same draw order as
+    make_weights.  Used where only the shapes matter (benchmark inputs); the
+    parity tests use make_weights, whose draws the oracle also sees."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def normal(*shp):
+        t = torch.randn(*shp, generator=g, device=device, dtype=torch.float32) * std
+        return t.to(torch.bfloat16).view(torch.int16)
+
+    ones = lambda n: torch.ones(n, device=device, dtype=torch.bfloat16).view(torch.int16)  # noqa: E731
+    out = {"embed": normal(shape.vocab, shape.hidden)}
+    layers = []
+    for _ in range(shape.n_layers):
+        lw = {}
+        for name in layer_tensor_names(shape):
+            shp = tensor_shape(shape, name)
+            lw[name] = ones(shp[0]) if name.endswith("_norm") else normal(*shp)
+        layers.append(lw)
+    out["layers"] = layers
+    out["final_norm"] = ones(shape.hidden)
+    return out
+
+
+def make_lora_device(shape: ModelShape, rank: int, seed: int = SEED_LORA, std: float = 0.01, device: str = "cuda"):
+    """LoRA factors as in make_lora, drawn on the GPU (see make_weights_device)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    H, d = shape.hidden, shape.head_dim
+
+    def normal(*shp):
+        t = torch.randn(*shp, generator=g, device=device, dtype=torch.float32) * std
+        return t.to(torch.bfloat16).view(torch.int16)
+
+    return [{"a_q": normal(rank, H), "b_q": normal(shape.n_q_heads * d, rank), "a_v": normal(rank, H),
+             "b_v": normal(shape.n_kv_heads * d, rank)} for _ in range(shape.n_layers)]
+
+
+def device_to_host(weights_dev, layers=None):
+    """bf16 bit patterns (numpy uint16) of a device weight set, all layers or the given ones."""
+    import numpy as np
+    h = lambda t: t.cpu().numpy().view(np.uint16)  # noqa: E731
+    idx = range(len(weights_dev["layers"])) if layers is None else layers
+    return {"embed": h(weights_dev["embed"]), "final_norm": h(weights_dev["final_norm"]),
+            "layers": [{k: h(v) for k, v in weights_dev["layers"][i].items()} for i in idx]}
