@@ -61,7 +61,7 @@ EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_deco
            "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_enable_phase_trace", "qd_get_phase_trace",
            "qd_get_quantized", "qd_get_exchange", "qd_sync_token", "qd_get_abandoned", "qd_get_position",
            "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
-           "qd_sizeof_lora"]
+           "qd_sizeof_lora", "qd_sample_workspace_bytes", "qd_sample_logits"]
 
 _lib = None
 
@@ -101,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qd_sizeof_weights": (sz, []),
         "qd_sizeof_sampling": (sz, []),
         "qd_sizeof_lora": (sz, []),
+        "qd_sample_workspace_bytes": (sz, [i32, ctypes.POINTER(QdSampling)]),
+        "qd_sample_logits": (i32, [_P, i32, ctypes.POINTER(QdSampling), u64, _P, _P, sz, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -319,3 +321,25 @@ class Decoder:
         p = ctypes.c_int32()
         self._check(self.lib.qd_get_position(self.h, ctypes.byref(p)))
         return p.value
+
+
+def _sp_ref(sampling: Optional[QdSampling]):
+    return None if sampling is None else ctypes.byref(sampling)
+
+
+def sample_workspace_bytes(vocab: int, sampling: Optional[QdSampling] = None) -> int:
+    """Device scratch bytes qd_sample_logits needs for `vocab` logits (0: invalid arguments)."""
+    return int(load_library().qd_sample_workspace_bytes(int(vocab), _sp_ref(sampling)))
+
+
+def sample_logits(logits, sampling: Optional[QdSampling], step: int, token_out, workspace, stream_ptr: int = 0):
+    """Choose a token from `logits` (f32 device tensor, 1-D) into `token_out`
+    (int32 device tensor, 1 element) with the caller's `workspace` (device
+    tensor of at least sample_workspace_bytes(...) bytes), enqueued on the
+    stream `stream_ptr`."""
+    L = load_library()
+    rc = L.qd_sample_logits(_ptr(logits), int(logits.numel()), _sp_ref(sampling), int(step), _ptr(token_out),
+                            _ptr(workspace), int(workspace.numel() * workspace.element_size()), stream_ptr)
+    if rc != 0:
+        raise QdError(rc, L.qd_last_error(None).decode())
+

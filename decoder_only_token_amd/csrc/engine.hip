@@ -443,7 +443,7 @@ int check_sampling(qd_handle* h, const qd_sampling* sp) {
 int maybe_sample(qd_handle* h, const qd_sampling* sp) {
   if (!sp || sp->temperature <= 0.f || sp->top_k == 1) return QD_OK;
   launch_sample(h->stream, h->logits, h->cfg.vocab, sp->top_k, sp->temperature, sp->top_p, sp->seed, h->spv, h->spi,
-                h->st, nullptr);
+                h->st, 0, nullptr);
   HIP_TRY(h, hipGetLastError());
   return QD_OK;
 }
@@ -457,7 +457,7 @@ size_t qd_sizeof_weights(void) { return sizeof(qd_weights); }
 size_t qd_sizeof_sampling(void) { return sizeof(qd_sampling); }
 size_t qd_sizeof_lora(void) { return sizeof(qd_lora); }
 
-const char* qd_last_error(const qd_handle* h) { return h ? h->err.c_str() : "NULL handle"; }
+const char* qd_last_error(const qd_handle* h) { return h ? h->err.c_str() : sample_free_error(); }
 
 // The persistent step's value-pair buffers (16-bit tags) to all ones: a tag
 // of layer 255, which no decoder layer uses, so no stale word matches.  A
@@ -530,7 +530,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   if (hipHostMalloc((void**)&h->tokens_pinned, rows * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
     return fail(h->set_err(QD_E_OOM, "hipHostMalloc failed"));
   if ((rc = build_rope_tables(h))) return fail(rc);
-  if (sample_supported(c.vocab, 1) && sample_prepare(c.vocab, c.vocab < 64 ? c.vocab : 64) != 0)
+  if (sample_supported(c.vocab, 1) && sample_prepare() != 0)
     return fail(h->set_err(QD_E_HIP, "sampling kernel unavailable"));
   if (c.decode_path == QD_DECODE_PERSISTENT) {
     h->persistent = true;

@@ -48,9 +48,10 @@ void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int 
 // goes to the device step state, which the greedy pass has already advanced.
 int sample_lists(int V);
 bool sample_supported(int V, int K);
-int sample_prepare(int V, int K);
+int sample_prepare();  // with the device current
 void launch_sample(hipStream_t s, const float* logits, int V, int K, float temperature, float top_p, uint64_t seed,
-                   float* part_val, int32_t* part_idx, DevState* st, int32_t* token_out);
+                   float* part_val, int32_t* part_idx, DevState* st, uint64_t step, int32_t* token_out);
+const char* sample_free_error();
 
 // Batched prefill projections on the matrix cores (gemm.hip).  X rows are
 // split into bf16 hi/lo halves (after RMSNorm with gains when `gain` is set),

@@ -27,7 +27,8 @@
  *
  * Conventions
  *   - Every call returns an int status: QD_OK (0) or a negative QD_E_* code.
- *     qd_last_error() returns a text reason for the last failure on a handle.
+ *     qd_last_error() returns a text reason for the last failure on a handle
+ *     (qd_last_error(NULL): of the last failed handle-free call).
  *   - Arguments are checked before any state change or GPU work; a failed
  *     call leaves the handle as it was.
  *   - "device pointer" = memory allocated on the handle's GPU (hipMalloc or
@@ -275,6 +276,37 @@ int qd_get_abandoned(qd_handle* h, int64_t* count_out);
 /* Current position (number of tokens in the KV cache), host-side mirror. */
 int qd_get_position(const qd_handle* h, int32_t* pos_out);
 
+/* Token choice over logits the caller already holds, without a handle: the
+ * same greedy / top-k / temperature / top-p rule as qd_sampling above
+ * ("flashmoon demo/README.md — Qwen3-0.6B inference", Quick start: greedy at
+ * temperature 0, else temperature, top-k and top-p; "EMBERGLASS
+ * (qwen-webgpu-lora)" decoding notes: the choice stays on the GPU).
+ *   logits_dev     device pointer, `vocab` f32 logits.
+ *   vocab          1 .. 524288 entries; top_k must not exceed it, and the
+ *                  merge's lists must fit its LDS: (ceil(vocab / 1024) + 1)
+ *                  * top_k <= 20480 (top_k <= 39 at the largest vocab).
+ *   sampling       NULL or temperature <= 0: greedy (ties to the lowest id);
+ *                  else top_k in [1, 64], top_p in (0, 1].
+ *   step           draw counter: u comes from SplitMix64 output number
+ *                  (step + 1) from state sampling->seed (ignored when greedy).
+ *   token_dev      device pointer, receives the chosen id (int32).
+ *   workspace_dev  device scratch of at least qd_sample_workspace_bytes()
+ *                  bytes, 4-byte aligned, owned by the caller; it holds the
+ *                  per-slice top-k lists and needs no initial contents.
+ *   hip_stream     the hipStream_t to enqueue on (NULL: the null stream), on
+ *                  the device current at the call.
+ * Asynchronous: two kernels on hip_stream; allocates nothing.  Calls that
+ * share a workspace must be ordered on one stream.
+ * Errors (nothing enqueued): QD_E_ARG (NULL pointer, bad vocab / top_k /
+ * top_p / temperature, workspace too small or misaligned), QD_E_ABI
+ * (sampling->struct_size), QD_E_HIP; the reason is qd_last_error(NULL) on the
+ * calling thread. */
+size_t qd_sample_workspace_bytes(int32_t vocab, const qd_sampling* sampling); /* 0: invalid arguments */
+int qd_sample_logits(const float* logits_dev, int32_t vocab, const qd_sampling* sampling, uint64_t step,
+                     int32_t* token_dev, void* workspace_dev, size_t workspace_bytes, void* hip_stream);
+
+/* Reason of the handle's last failure; with h == NULL, of the last failed
+ * handle-free call (qd_sample_*) on the calling thread. */
 const char* qd_last_error(const qd_handle* h);
 void qd_destroy(qd_handle* h);
 

@@ -192,6 +192,15 @@ def make_prompt(vocab: int, n: int, seed: int = SEED_PROMPT) -> np.ndarray:
     return np.random.default_rng(seed).integers(0, vocab, n).astype(np.int32)
 
 
+def make_logits(vocab: int, seed: int, scale: float = 3.0, step: Optional[float] = None) -> np.ndarray:
+    """f32 logits ~ N(0, scale^2); with `step`, rounded to multiples of it so
+    that many entries tie (for the lowest-id tie rule)."""
+    x = np.random.default_rng(seed).standard_normal(vocab) * scale
+    if step:
+        x = np.round(x / step) * step
+    return x.astype(np.float32)
+
+
 def scaled_shape(shape: ModelShape, **kw) -> ModelShape:
     return dataclasses.replace(shape, **kw)
 

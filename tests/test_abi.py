@@ -93,7 +93,7 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.qd_reset_kv(None) == -1
     assert lib.qd_decode_step(None, None, None, None) == -1
     assert lib.qd_prefill(None, None, 0, None, None, None) == -1
-    assert lib.qd_last_error(None) == b"NULL handle"
+    assert isinstance(lib.qd_last_error(None), bytes)  # the handle-free calls' last reason
     lib.qd_destroy(None)
 
 
@@ -113,3 +113,47 @@ def test_persistent_path_rejects_more_than_254_layers():
 def test_abandoned_count_needs_an_output_pointer():
     lib = qd.load_library()
     assert lib.qd_get_abandoned(None, None) == -1
+
+
+def _sample_call(logits=1 << 20, vocab=1000, sampling=None, token=1 << 21, ws=1 << 22, ws_bytes=1 << 20):
+    lib = qd.load_library()
+    return lib.qd_sample_logits(logits, vocab, None if sampling is None else ctypes.byref(sampling), 0, token, ws,
+                                ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), -1),
+    (dict(token=None), -1),
+    (dict(ws=None), -1),
+    (dict(vocab=0), -1),
+    (dict(vocab=524289), -1),
+    (dict(ws_bytes=7), -1),
+    (dict(ws=(1 << 22) + 2), -1),
+    (dict(sampling=qd.make_sampling(0.7, 0, 0.9, 1)), -1),
+    (dict(sampling=qd.make_sampling(0.7, 65, 0.9, 1)), -1),
+    (dict(sampling=qd.make_sampling(0.7, 40, 0.0, 1)), -1),
+    (dict(sampling=qd.make_sampling(float("inf"), 40, 0.9, 1)), -1),
+    (dict(vocab=16, sampling=qd.make_sampling(0.7, 40, 0.9, 1)), -1),
+])
+def test_handle_free_sampler_checks_arguments_before_any_hip_call(kw, code):
+    """Every bad argument is refused (with a reason) before the library
+    touches the device, so these run without a GPU."""
+    assert _sample_call(**kw) == code
+    assert qd.load_library().qd_last_error(None)
+
+
+def test_handle_free_sampler_rejects_a_foreign_struct_size():
+    s = qd.make_sampling(0.7, 40, 0.9, 1)
+    s.struct_size -= 4
+    assert _sample_call(sampling=s) == -2
+
+
+def test_sampler_workspace_size():
+    """K lists of (value, id) per 1024-logit slice: greedy keeps one entry."""
+    assert qd.sample_workspace_bytes(151936) == 149 * 1 * 8
+    assert qd.sample_workspace_bytes(151936, qd.make_sampling(0.7, 40, 0.9, 1)) == 149 * 40 * 8
+    assert qd.sample_workspace_bytes(1025, qd.make_sampling(0.0, 0, 0.0, 1)) == 2 * 8
+    assert qd.sample_workspace_bytes(0) == 0
+    assert qd.sample_workspace_bytes(8, qd.make_sampling(0.7, 9, 0.9, 1)) == 0
+    assert qd.sample_workspace_bytes(524288, qd.make_sampling(0.7, 39, 0.9, 1)) == 512 * 39 * 8
+    assert qd.sample_workspace_bytes(524288, qd.make_sampling(0.7, 40, 0.9, 1)) == 0  # merge LDS bound
