@@ -61,7 +61,7 @@ EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_deco
            "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_enable_phase_trace", "qd_get_phase_trace",
            "qd_get_quantized", "qd_get_exchange", "qd_sync_token", "qd_get_abandoned", "qd_get_position",
            "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
-           "qd_sizeof_lora", "qd_sample_workspace_bytes", "qd_sample_logits"]
+           "qd_sizeof_lora", "qd_sample_workspace_bytes", "qd_sample_logits", "qd_sample_logits_static"]
 
 _lib = None
 
@@ -103,6 +103,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qd_sizeof_lora": (sz, []),
         "qd_sample_workspace_bytes": (sz, [i32, ctypes.POINTER(QdSampling)]),
         "qd_sample_logits": (i32, [_P, i32, ctypes.POINTER(QdSampling), u64, _P, _P, sz, _P]),
+        "qd_sample_logits_static": (i32, [_P, i32, ctypes.POINTER(QdSampling), u64, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -343,3 +344,11 @@ def sample_logits(logits, sampling: Optional[QdSampling], step: int, token_out, 
     if rc != 0:
         raise QdError(rc, L.qd_last_error(None).decode())
 
+
+def sample_logits_static(logits, sampling: Optional[QdSampling], step: int, token_out, stream_ptr: int = 0):
+    """sample_logits with the library's static per-device scratch (no workspace)."""
+    L = load_library()
+    rc = L.qd_sample_logits_static(_ptr(logits), int(logits.numel()), _sp_ref(sampling), int(step), _ptr(token_out),
+                                   stream_ptr)
+    if rc != 0:
+        raise QdError(rc, L.qd_last_error(None).decode())

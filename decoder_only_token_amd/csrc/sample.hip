@@ -265,6 +265,47 @@ int launch_checked(const float* logits, int V, int K, const qd_sampling* sp, uin
 
 const char* sample_free_error() { return t_err.c_str(); }
 
+// ------------------------------------------- handle-free sampling, no workspace
+namespace {
+
+// Scratch of qd_sample_logits_static: the per-slice lists (f32 value, i32
+// id) of any supported call, whose lists and merged list fit the merge's
+// 160 KiB of LDS, so 160 KiB always suffice; one copy per device, kept until
+// the process ends.  Host code never passes
+// this name to a kernel (on the host it is only a stand-in): it uses the
+// device address that hipGetSymbolAddress returns, per device.
+constexpr size_t kStaticScratch = kSampleMaxLds;
+__device__ __align__(256) uint8_t scratch[kStaticScratch];
+
+void* g_scratch[kMaxDevices];  // device address of `scratch`, per device (guarded by g_prep_mu)
+
+// Once per device, with that device current: the symbol's device address.
+int static_scratch(int dev, void** out) {
+  std::lock_guard<std::mutex> g(g_prep_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail(QD_E_HIP, "hipGetSymbolAddress(scratch) failed");
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return QD_OK;
+}
+
+}  // namespace
+
+extern "C" int qd_sample_logits_static(const float* logits_dev, int32_t vocab, const qd_sampling* sampling,
+                                       uint64_t step, int32_t* token_dev, void* hip_stream) {
+  if (!logits_dev || !token_dev) return fail(QD_E_ARG, "NULL logits or token pointer");
+  int K = 0, rc = sample_k(sampling, vocab, &K), dev = 0;
+  if (rc != QD_OK) return rc;
+  if ((size_t)sample_lists(vocab) * K * 8 > kStaticScratch)
+    return fail(QD_E_ARG, "vocab x top_k beyond the static scratch (160 KiB)");
+  void* ws = nullptr;
+  if ((rc = prepare_device(&dev)) != QD_OK || (rc = static_scratch(dev, &ws)) != QD_OK) return rc;
+  return launch_checked(logits_dev, vocab, K, sampling, step, token_dev, ws, static_cast<hipStream_t>(hip_stream));
+}
+
 extern "C" {
 
 size_t qd_sample_workspace_bytes(int32_t vocab, const qd_sampling* sampling) {

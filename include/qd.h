@@ -305,6 +305,18 @@ size_t qd_sample_workspace_bytes(int32_t vocab, const qd_sampling* sampling); /*
 int qd_sample_logits(const float* logits_dev, int32_t vocab, const qd_sampling* sampling, uint64_t step,
                      int32_t* token_dev, void* workspace_dev, size_t workspace_bytes, void* hip_stream);
 
+/* qd_sample_logits without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Its scratch is a file-scope device array
+ * of 160 KiB per GPU (enough for every supported vocab and top_k), which the
+ * library keeps until the process ends; the first call on a device looks up
+ * its address.  Calls on one GPU share that array, and it keeps the last
+ * call's contents (no call needs it cleared): calls that overlap on one GPU
+ * (different streams, or different threads without ordering) race.
+ * Arguments, results and errors as qd_sample_logits; allocates nothing. */
+int qd_sample_logits_static(const float* logits_dev, int32_t vocab, const qd_sampling* sampling, uint64_t step,
+                            int32_t* token_dev, void* hip_stream);
+
 /* Reason of the handle's last failure; with h == NULL, of the last failed
  * handle-free call (qd_sample_*) on the calling thread. */
 const char* qd_last_error(const qd_handle* h);
