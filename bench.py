@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--workload", default="qwen2.5-3b-int4-lora")
     ap.add_argument("--path", choices=["auto", "persistent", "graph"], default="auto",
                     help="decode step as one persistent kernel, or as per-operation kernels in a hipGraph "
-                         "(auto: the persistent kernel)")
+                         "(auto: the persistent kernel without an adapter, the graph with one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the qwen3-0.6b job and the prefill timing")
     ap.add_argument("--only-decode", action="store_true", help="decode timing only (for profiler runs)")
@@ -331,6 +331,8 @@ def main():
     shape = wl.shape
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
+    # auto: the persistent step, except with an adapter at the long context,
+    # where the captured graph's split-K attention over every CU is faster
     path = ("graph" if wl.lora_rank else "persistent") if args.path == "auto" else args.path
     dw = synth.make_weights_device(shape)
     dl = synth.make_lora_device(shape, wl.lora_rank) if wl.lora_rank else None

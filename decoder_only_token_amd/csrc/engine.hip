@@ -200,7 +200,18 @@ int validate_config(const qd_config* c, std::string& why) {
   if (c->decode_path == QD_DECODE_PERSISTENT) {
     // handshake tags carry the layer in 8 bits; 255 marks the argmax words and the unset value pairs
     if (c->n_layers > 254) { why = "the persistent decode step supports at most 254 layers"; return QD_E_ARG; }
-    if (c->lora_rank_max != 0) { why = "LoRA needs decode_path QD_DECODE_GRAPH"; return QD_E_ARG; }
+    if (c->lora_rank_max != 0) {
+      // the LoRA-down CU holds [A_q; A_v] in the 24 registers slots per lane it
+      // loads ahead (rows over 8 waves, 512 columns a slot), and an attention
+      // item stages its heads' B rows (bf16) in the 2 x 11264 floats of the
+      // phase-input slots
+      const int G = c->n_kv_heads > 0 ? c->n_q_heads / c->n_kv_heads : 0;
+      if ((2 * c->lora_rank_max + 7) / 8 * ((c->hidden + 511) / 512) > 24 ||
+          (size_t)(G + 1) * c->head_dim * c->lora_rank_max * 2 > 2 * 11264 * 4) {
+        why = "lora_rank_max too large for the persistent decode step (ceil(r / 4) * hidden / 512 must be <= 24)";
+        return QD_E_ARG;
+      }
+    }
     if (c->hidden != 1024 && c->hidden != 2048) { why = "the persistent decode step needs hidden 1024 or 2048"; return QD_E_ARG; }
     if (c->intermediate > 11264 || c->n_q_heads * c->head_dim > 11264) { why = "model too wide for the persistent decode step"; return QD_E_ARG; }
   }
@@ -545,12 +556,14 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     h->hseg = c.hidden / 512;
     const int G = c.n_q_heads / c.n_kv_heads;
     const int q4 = c.weight_format == QD_W_INT4_G128;
-    if (persist_prepare(G, h->hseg, q4) != 0) return fail(h->set_err(QD_E_HIP, "persistent decode kernel unavailable"));
+    if (persist_prepare(G, h->hseg, q4, 0) != 0 || (c.lora_rank_max && persist_prepare(G, h->hseg, q4, 1) != 0))
+      return fail(h->set_err(QD_E_HIP, "persistent decode kernel unavailable"));
     {  // the role plan must exist at the shortest and the longest context
       PersistConst shape{};
       shape.q4 = q4;
       shape.H = c.hidden; shape.nq = c.n_q_heads; shape.nkv = c.n_kv_heads; shape.I = c.intermediate;
       shape.nqkv = (int)qkv_rows(c); shape.max_pos = c.max_pos; shape.V = c.vocab;
+      shape.lora_r = c.lora_rank_max;  // the plan with the LoRA-down CU, if an adapter may come
       PersistStep st;
       if (c.vocab < h->grid || persist_plan(shape, h->grid, 0, 1, &st) != 0 ||
           persist_plan(shape, h->grid, c.max_pos - 1, 1, &st) != 0)
@@ -558,7 +571,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     }
     const size_t smax = (size_t)h->grid / c.n_kv_heads;
     if ((rc = dev_alloc(h, &h->X0, H)) || (rc = dev_alloc(h, &h->X1, H)) ||
-        (rc = dev_alloc(h, &h->QKVx, (size_t)qkv_rows(c))) ||
+        (rc = dev_alloc(h, &h->QKVx, (size_t)qkv_rows(c) + 2 * c.lora_rank_max)) ||
         (rc = dev_alloc(h, &h->PART, (size_t)c.n_q_heads * smax * (d + 2))) ||
         (rc = dev_alloc(h, &h->Ox, (size_t)c.n_q_heads * d)) || (rc = dev_alloc(h, &h->ACT, I)) ||
         (rc = dev_alloc(h, &h->AM, (size_t)2 * h->grid)) ||
@@ -568,7 +581,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     // tags start at 0; every step uses seq >= 1, so stale words never match.
     // The value-pair buffers carry only 16 tag bits (8 of the step): they start
     // as all ones (layer 255, never a decoder layer), and a reset refills them.
-    if (hipMemset(h->X0, 0, H * 8) || hipMemset(h->X1, 0, H * 8) || hipMemset(h->QKVx, 0, qkv_rows(c) * 8) ||
+    if (hipMemset(h->X0, 0, H * 8) || hipMemset(h->X1, 0, H * 8) || hipMemset(h->QKVx, 0, (qkv_rows(c) + 2 * c.lora_rank_max) * 8) ||
         hipMemset(h->PART, 0, (size_t)c.n_q_heads * smax * (d + 2) * 8) || hipMemset(h->AM, 0, h->grid * 16) ||
         hipMemset(h->err_dev, 0, 16) || fill_pairs(h, nullptr) != QD_OK)
       return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
@@ -693,12 +706,15 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
     std::vector<LayerPtrs> lp(c.n_layers);
     for (int l = 0; l < c.n_layers; ++l) {
       const Layer& L = h->layers[l];
+      const bool lo = !h->lora.empty();
       lp[l] = LayerPtrs{L.wqkv, L.bqkv, L.attn_norm, L.mlp_norm, L.q_norm, L.k_norm, L.wo, L.wg, L.wu, L.wd,
-                        {L.cqkv, L.co, L.cg, L.cd}, {L.sqkv, L.so, L.sg, L.sd}};
+                        {L.cqkv, L.co, L.cg, L.cd}, {L.sqkv, L.so, L.sg, L.sd},
+                        lo ? h->lora[l].a : nullptr, lo ? h->lora[l].bq : nullptr, lo ? h->lora[l].bv : nullptr};
     }
     PersistConst pc{};
     pc.L = c.n_layers; pc.H = c.hidden; pc.nq = c.n_q_heads; pc.nkv = c.n_kv_heads; pc.I = c.intermediate;
     pc.V = c.vocab; pc.nqkv = (int)NQKV; pc.max_pos = c.max_pos; pc.eps = c.rms_eps; pc.q4 = q4;
+    pc.lora_r = h->lora_rank; pc.lora_scale = h->lora_scale;
     pc.embed = h->embed; pc.final_norm = h->final_norm; pc.layers = h->layer_ptrs;
     pc.Kc = h->Kc; pc.Vc = h->Vc; pc.rope_cos = h->rope_cos; pc.rope_sin = h->rope_sin;
     pc.X0 = h->X0; pc.X1 = h->X1; pc.QKV = h->QKVx; pc.PART = h->PART; pc.O = h->Ox; pc.ACT = h->ACT;
@@ -771,7 +787,8 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
     const int G = h->cfg.n_q_heads / h->cfg.n_kv_heads;
     if (h->trace_on)  // a traced step writes only the stamps of its CUs' phases
       HIP_TRY(h, hipMemsetAsync(h->trace, 0, (size_t)h->grid * persist_trace_slots(h->cfg.n_layers) * 8, h->stream));
-    int e = persist_launch(h->pconst, G, h->hseg, h->cfg.weight_format == QD_W_INT4_G128, h->grid, st, h->stream);
+    int e = persist_launch(h->pconst, G, h->hseg, h->cfg.weight_format == QD_W_INT4_G128, h->pc_host.lora_r > 0,
+                           h->grid, st, h->stream);
     if (e != 0) return h->set_err(QD_E_HIP, "persistent decode launch failed: " + std::to_string(e));
     if ((rc = maybe_sample(h, sampling))) return rc;
     h->pos += 1;
@@ -791,6 +808,18 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
   if ((rc = maybe_sample(h, sampling))) return rc;
   h->pos += 1;
   return copy_outputs(h, logits_dev, token_dev);
+}
+
+// The persistent step's copy of the adapter's rank and scale (its plan gives
+// the LoRA-down CU only while one is installed); ordered on the stream before
+// the next step.
+static int sync_persist_lora(qd_handle* h) {
+  if (!h->persistent || !h->weights) return QD_OK;
+  h->pc_host.lora_r = h->lora_rank;
+  h->pc_host.lora_scale = h->lora_scale;
+  HIP_TRY(h, hipMemcpyAsync(h->pconst, &h->pc_host, sizeof(PersistConst), hipMemcpyHostToDevice, h->stream));
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  return QD_OK;
 }
 
 int qd_set_lora(qd_handle* h, const qd_lora* lora) {
@@ -818,7 +847,7 @@ int qd_set_lora(qd_handle* h, const qd_lora* lora) {
   h->lora_rank = (int)r;
   h->lora_scale = lora->alpha / (float)r;
   drop_decode_graph(h);  // the next decode step captures the adapter's kernels
-  return QD_OK;
+  return sync_persist_lora(h);
 }
 
 int qd_clear_lora(qd_handle* h) {
@@ -827,6 +856,7 @@ int qd_clear_lora(qd_handle* h) {
     HIP_TRY(h, hipStreamSynchronize(h->stream));  // the captured step may still be running
     h->lora_rank = 0;
     drop_decode_graph(h);
+    return sync_persist_lora(h);
   }
   return QD_OK;
 }

@@ -23,6 +23,11 @@ struct LayerPtrs {
   // codes and scales follow the gate rows' in one allocation each
   const uint8_t* qcode[4];
   const uint16_t* qscale[4];
+  // LoRA factors (bf16, rank r = PersistConst::lora_r): down rows [A_q; A_v]
+  // [2 r][H], up rows B_q [nq d][r] and B_v [nkv d][r] (original head order)
+  const uint16_t* lora_a;
+  const uint16_t* lora_bq;
+  const uint16_t* lora_bv;
 };
 
 // Everything the decode kernel needs that does not change from step to step.
@@ -30,6 +35,8 @@ struct LayerPtrs {
 struct PersistConst {
   int L, H, nq, nkv, I, V, nqkv, max_pos;
   int q4;  // 1: the projections are int4 group-128 (LayerPtrs c* / s*)
+  int lora_r;        // 0: no adapter; else its rank (one more CU in the QKV role)
+  float lora_scale;  // alpha / r
   float eps;
   const uint16_t* embed;
   const float* final_norm;
@@ -40,7 +47,7 @@ struct PersistConst {
   const float* rope_sin;
   uint64_t* X0;    // [H] residual entering a layer
   uint64_t* X1;    // [H] residual after attention
-  uint64_t* QKV;   // [nqkv]
+  uint64_t* QKV;   // [nqkv + 2 lora_r]: q|k|v rows, then the LoRA down products u_q, u_v
   uint64_t* PART;  // [nq][S][130] split partials {m, l, o[128]}
   uint64_t* O;     // [nq * 64] attention output, value pairs
   uint64_t* ACT;   // [I / 2] SwiGLU activations, value pairs
@@ -60,7 +67,8 @@ constexpr int kTraceSlots = 8;
 __host__ __device__ inline int persist_trace_slots(int L) { return (5 * L + 2) * kTraceSlots; }
 
 // One decode step's launch plan: the attention splits and the CU ranges of
-// the five roles (role r runs on blocks [start[r], start[r + 1]): QKV rows,
+// the five roles (role r runs on blocks [start[r], start[r + 1]): QKV rows
+// (with an adapter, the role's last CU computes the LoRA down products),
 // attention items (kv head, head group, split), o_proj rows, gate/up row
 // pairs, down rows).
 struct PersistStep {
@@ -72,9 +80,9 @@ struct PersistStep {
 };
 
 size_t persist_smem_bytes();
-int persist_prepare(int G, int hseg, int q4);
+int persist_prepare(int G, int hseg, int q4, int lora);  // lora: the instantiation with an adapter
 // Plans the step at position pos for `grid` CUs; 0 on success, -1 if the
 // grid cannot hold the five roles.
 int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, PersistStep* out);
-int persist_launch(const PersistConst* dev_const, int G, int hseg, int q4, int grid, const PersistStep& st,
+int persist_launch(const PersistConst* dev_const, int G, int hseg, int q4, int lora, int grid, const PersistStep& st,
                    hipStream_t s);

@@ -353,6 +353,22 @@ __device__ __forceinline__ Gemv gemv_of(const Ctx& c, int l) {
   return g;
 }
 
+// The LoRA-down CU ("EMBERGLASS (qwen-webgpu-lora) README", LoRA sections: a
+// live rank-r adapter on q_proj and v_proj): rows [A_q; A_v] of layer l, 2 r
+// rows of H, as a row-segment GEMV whose outputs go to QKV[nqkv ..].
+__device__ __forceinline__ Gemv lora_of(const Ctx& c, int l) {
+  const AS4 PersistConst& a = *c.a;
+  const AS4 LayerPtrs& L = ((const AS4 LayerPtrs*)a.layers)[l];
+  Gemv g;
+  g.a = L.lora_a;
+  g.delta = 0;
+  g.K = a.H;
+  g.nseg = (a.H + kSeg - 1) / kSeg;
+  g.rpu = 1;
+  g.nunits = 2 * a.lora_r;
+  return g;
+}
+
 // Matrix-core geometry of a GEMV role.  The CU's rows (per row set: gate and
 // up rows for pairs) form blocks of 16 (the last block shifted back to end at
 // the last row, overlapping its neighbour); the K columns form chunks of 32,
@@ -631,8 +647,8 @@ __device__ __forceinline__ float* v_rows(const AS4 PersistConst& a, int l, int g
 }
 
 // The slice this CU loads ahead for layer l (l == L: its first LM-head rows).
-template <int HS, bool Q4>
-__device__ __forceinline__ Addr<kFirst> ahead_addr(const Ctx& c, int l) {
+template <int HS, bool Q4, bool LORA>
+__device__ __forceinline__ Addr<kFirst> ahead_addr(const Ctx& c, int l, bool lora) {
   const AS4 PersistConst& a = *c.a;
   const int wave = wave_id();
   Addr<kFirst> ad;
@@ -641,6 +657,8 @@ __device__ __forceinline__ Addr<kFirst> ahead_addr(const Ctx& c, int l) {
   } else if (c.role == kAttn) {
     const int g = c.rank / (c.X * c.S), s = c.rank % c.S;
     kv_addr<kFirst>(ad, k_rows(a, l, g), v_rows(a, l, g), s * c.chunk, 0);
+  } else if (LORA && lora) {
+    gemv_addr<kFirst>(ad, lora_of(c, l), Walk{wave, 0, 0});
   } else if (Q4) {
     q4_addr<kFirst>(ad, q4_geo(c, l), 0);
   } else {
@@ -975,6 +993,36 @@ __device__ __forceinline__ void gemv_phase(const Ctx& c, Smem& sm, int l, Regs<k
 // Returns false when the step is abandoned.
 constexpr int kWE = 6;  // input words per lane at most (12 chunks of 32 f32 values over 64 lanes)
 
+// LoRA-down CU: u = rs [A_q; A_v] (gain * x), 2 r rows from the registers
+// loaded ahead (row u on wave u % 8, its segments in slot order), published
+// with the layer's tag after the q|k|v rows, where the attention items poll
+// them beside their q|k|v.
+__device__ __forceinline__ void lora_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, float rs) {
+  const AS4 PersistConst& a = *c.a;
+  const Gemv g = lora_of(c, l);
+  const int lane = threadIdx.x & 63;
+  const float* h = sm.vec[l & 1];
+  Walk w{wave_id(), 0, 0};
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kFirst; ++i) {
+    if (walk_valid(g, w)) {  // wave-uniform
+      const int k = w.sg * kSeg + lane * 8;
+      if (k < g.K) acc += dot8(rg.R[i], h + k);
+      if (w.sg + 1 == g.nseg) {
+        const float t = wave_total(acc) * rs;
+        acc = 0.f;
+        if (lane == 0) sm.outv[w.u] = t;
+      }
+      walk_next(g, w);
+    }
+  }
+  stamp(c, sm, 5 * l + kQKV, 2, threadIdx.x == 0);
+  __syncthreads();
+  const uint32_t tag = tag_of(c.seq, l);
+  for (int u = threadIdx.x; u < g.nunits; u += kThreads) st_tagged(a.QKV + a.nqkv + u, sm.outv[u], tag);
+}
+
 __device__ __forceinline__ bool gemv_waves(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, const Tiles& tl,
                                            const float* bias) {
   const AS4 PersistConst& a = *c.a;
@@ -1112,6 +1160,23 @@ __device__ __forceinline__ AttnPre attn_pre(const Ctx& c, int l) {
   return p;
 }
 
+// With an adapter: the attention item's LoRA up rows, copied to LDS before
+// the input poll (the phase inputs' slots are free in the attention role):
+// B_q rows of the item's gi q heads [gi D][r], then B_v rows of its kv head
+// [D][r], bf16.
+template <int G>
+__device__ __forceinline__ void lora_stage(const Ctx& c, Smem& sm, int l) {
+  const AS4 PersistConst& a = *c.a;
+  const AS4 LayerPtrs& Lw = ((const AS4 LayerPtrs*)a.layers)[l];
+  const Item it = item_of<G>(c);
+  const int r = a.lora_r;
+  const int nq16 = it.gi * D * r / 8, nv16 = D * r / 8;  // 16-byte pieces (D r is a multiple of 8)
+  const u32x4* bq = reinterpret_cast<const u32x4*>(Lw.lora_bq + (size_t)(it.g * G + it.j0) * D * r);
+  const u32x4* bv = reinterpret_cast<const u32x4*>(Lw.lora_bv + (size_t)it.g * D * r);
+  u32x4* dst = reinterpret_cast<u32x4*>(&sm.vec[0][0]);
+  for (int i = threadIdx.x; i < nq16 + nv16; i += kThreads) dst[i] = i < nq16 ? *gl(bq + i) : *gl(bv + i - nq16);
+}
+
 // Sum over the 8 lanes of this lane's group (lanes 8 i .. 8 i + 7), in every
 // lane of the group; the two halves add in mirrored order, which is exact.
 __device__ __forceinline__ float group8_sum(float v) {
@@ -1172,7 +1237,7 @@ __device__ __forceinline__ float dot16(const f32x4 (&q)[4], const u32x4* kp, int
 // position p_begin + 64 t + 8 wave + pg at step t, so one 8-lane sum gives a
 // score.  The 8 group states of a wave are merged in a butterfly and written
 // to LDS per head.
-template <int G>
+template <int G, bool LORA>
 __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const Regs<kFirst>& rg, const AttnPre& pre) {
   const AS4 PersistConst& a = *c.a;
   const AS4 LayerPtrs& Lw = ((const AS4 LayerPtrs*)a.layers)[l];
@@ -1184,6 +1249,21 @@ __device__ __forceinline__ void attn_phase(const Ctx& c, Smem& sm, int l, const 
   float* Kg = k_rows(a, l, g);
   float* Vg = v_rows(a, l, g);
   float* qk = sm.qk;
+  if (LORA && a.lora_r) {  // q += s B_q u_q on the item's heads, v += s B_v u_v (before QK-norm and RoPE)
+    const int r = a.lora_r;
+    const uint16_t* bq = reinterpret_cast<const uint16_t*>(&sm.vec[0][0]);
+    const uint16_t* bv = bq + gi * D * r;
+    const float* u = sm.xres[0];  // u_q, then u_v (polled beside q|k|v)
+    for (int row = threadIdx.x; row < (gi + 1) * D; row += kThreads) {
+      const bool isq = row < gi * D;
+      const uint16_t* b = isq ? bq + row * r : bv + (row - gi * D) * r;
+      const float* uu = isq ? u : u + r;
+      float t = 0.f;
+      for (int k = 0; k < r; ++k) t = fmaf(bf16_to_f(b[k]), uu[k], t);
+      qk[isq ? it.j0 * D + row : (G + 1) * D + row - gi * D] += a.lora_scale * t;
+    }
+    __syncthreads();
+  }
   // QK-norm (optional) and RoPE of the item's q heads and k; wave hd handles
   // one of them (lane j: the pair (j, j + 64))
   for (int hd = wave; hd < gi + 1; hd += kWaves) {
@@ -1558,7 +1638,7 @@ __device__ __forceinline__ bool gate(const Ctx& c, Smem& sm, const uint64_t* w, 
   return !sm.abort_flag;
 }
 
-template <int G, int HS, bool Q4>
+template <int G, int HS, bool Q4, bool LORA>
 __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const PersistConst* __restrict__ pc,
                                                                    PersistStep stp) {
   extern __shared__ __align__(16) char smem_raw[];
@@ -1583,22 +1663,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   c.rank = (int)blockIdx.x - stp.start[role];
   c.nrole = stp.start[role + 1] - stp.start[role];
   const int N = role == kQKV ? a.nqkv : role == kGateUp ? a.I : role == kAttn ? c.nrole : a.H;
-  if (role != kAttn && N % 16 == 0 && N / 16 >= c.nrole) {  // whole 16-row tile blocks (no overlapping block)
-    c.r0 = 16 * (int)(((uint32_t)(N / 16) * c.rank) / c.nrole);
-    c.r1 = 16 * (int)(((uint32_t)(N / 16) * (c.rank + 1)) / c.nrole);
+  // with an adapter the QKV role's last CU computes the LoRA down products
+  const int nr = c.nrole - (LORA && role == kQKV && a.lora_r > 0 ? 1 : 0);
+  const bool lora = LORA && c.rank >= nr;
+  if (lora) {
+    c.r0 = a.nqkv;
+    c.r1 = a.nqkv + 2 * a.lora_r;
+  } else if (role != kAttn && N % 16 == 0 && N / 16 >= nr) {  // whole 16-row tile blocks (no overlapping block)
+    c.r0 = 16 * (int)(((uint32_t)(N / 16) * c.rank) / nr);
+    c.r1 = 16 * (int)(((uint32_t)(N / 16) * (c.rank + 1)) / nr);
   } else if (role == kGateUp) {  // even boundaries: the activations travel as value pairs
-    c.r0 = 2 * (int)(((uint32_t)(N / 2) * c.rank) / c.nrole);
-    c.r1 = 2 * (int)(((uint32_t)(N / 2) * (c.rank + 1)) / c.nrole);
+    c.r0 = 2 * (int)(((uint32_t)(N / 2) * c.rank) / nr);
+    c.r1 = 2 * (int)(((uint32_t)(N / 2) * (c.rank + 1)) / nr);
   } else {
-    c.r0 = (int)(((uint32_t)N * c.rank) / c.nrole);
-    c.r1 = (int)(((uint32_t)N * (c.rank + 1)) / c.nrole);
+    c.r0 = (int)(((uint32_t)N * c.rank) / nr);
+    c.r1 = (int)(((uint32_t)N * (c.rank + 1)) / nr);
   }
   c.v0 = (int)(((uint32_t)a.V * blockIdx.x) / gridDim.x);
   c.v1 = (int)(((uint32_t)a.V * (blockIdx.x + 1)) / gridDim.x);
   const int L = a.L, H = a.H, tid = threadIdx.x;
   const uint16_t* emb = a.embed + (size_t)gl(a.st)->token * H;
   Regs<kFirst> rg;
-  load_regs(rg, ahead_addr<HS, Q4>(c, 0));
+  load_regs(rg, ahead_addr<HS, Q4, LORA>(c, 0, lora));
   __syncthreads();
   for (int l = 0; l < L; ++l) {
     const int ph = 5 * l + role;
@@ -1615,20 +1701,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
     const float* bias = nullptr;
     if (role == kAttn) {
       pre = attn_pre(c, l);
-    } else {
+      if (LORA && a.lora_r) lora_stage<G>(c, sm, l);
+    } else if (!lora) {
       if (!Q4) gv = gemv_of(c, l);
       if (role == kQKV) bias = Lw.bqkv;
     }
     // ---- the phase input and the compute
     Tiles tw;
-    if (!Q4 && role != kAttn && !(l == 0 && role == kQKV) && mfma_path(c, &tw)) {
+    if (!Q4 && role != kAttn && !lora && !(l == 0 && role == kQKV) && mfma_path(c, &tw)) {
       if (!gemv_waves(c, sm, l, rg, tw, bias)) return;  // per-wave input, matrix-core rows
     } else {
       bool ok = true;
       // int4 roles: the group scales of the slots loaded ahead, requested
       // before the input wait (1/64 of the codes' bytes)
       uint32_t sc[kFirst];
-      if (Q4 && role != kAttn) {
+      if (Q4 && role != kAttn && !lora) {
         SAddr<kFirst> sa;
         q4_saddr<kFirst>(sa, q4_geo(c, l), 0);
         load_scales<0>(sc, sa);
@@ -1647,7 +1734,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
       }
       if (l == 0 && role == kQKV) {  // layer 0: x0 is the embedding row (nothing to wait for)
         float ss = 0.f;
-        const bool split = !Q4 && mfma_path(c);
+        const bool split = !Q4 && !lora && mfma_path(c);
         for (int k = tid; k < H; k += kThreads) {
           const float x = bf16_to_f(*gl(emb + k));
           const float y = x * ld_f(Lw.attn_norm + k);
@@ -1676,7 +1763,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
         float* dst = vin;
         switch (role) {
           case kQKV: src = a.X0; n = H; gain = Lw.attn_norm; break;
-          case kAttn: src = a.QKV + (size_t)(c.rank / (c.X * c.S)) * (G + 2) * D; n = (G + 2) * D; dst = sm.qk; break;
+          case kAttn:
+            src = a.QKV + (size_t)(c.rank / (c.X * c.S)) * (G + 2) * D;
+            n = (G + 2) * D;
+            dst = sm.qk;
+            if (LORA && a.lora_r) {  // the LoRA down products u_q, u_v
+              src2 = a.QKV + a.nqkv;
+              n2 = 2 * a.lora_r;
+              xr = sm.xres[0];
+            }
+            break;
           case kOproj:
             src = a.O;
             n = a.nq * D;
@@ -1698,10 +1794,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
       stamp(c, sm, ph, 1, tid == 0);
       // ---- compute from the registers loaded a layer ahead
       if (role == kAttn) {
-        attn_phase<G>(c, sm, l, rg, pre);
+        attn_phase<G, LORA>(c, sm, l, rg, pre);
         stamp(c, sm, ph, 2, tid == 0);
         if (!attn_finish<G>(c, sm, l)) return;
         attn_cache_write<G>(c, sm, l);
+      } else if (LORA && lora) {
+        lora_phase(c, sm, l, rg, rs);
       } else {
         gemv_phase<Q4>(c, sm, l, rg, sc, rs, gv, bias);
       }
@@ -1709,7 +1807,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
     stamp(c, sm, ph, 3, tid == 0);
     // the single load site: the next layer's slice (after the last layer, the
     // first LM-head rows) streams while the other roles take their phases
-    load_regs(rg, ahead_addr<HS, Q4>(c, l + 1));
+    load_regs(rg, ahead_addr<HS, Q4, LORA>(c, l + 1, lora));
     stamp(c, sm, ph, 5, tid == 0);
   }
   // ---- final norm + LM head (every CU)
@@ -1732,32 +1830,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   }
 }
 
-template <int G, int HS, bool Q4>
+template <int G, int HS, bool Q4, bool LORA>
 void* kernel_ptr() {
-  return (void*)k_decode_persistent<G, HS, Q4>;
+  return (void*)k_decode_persistent<G, HS, Q4, LORA>;
 }
 
-template <bool Q4>
+template <bool Q4, bool LORA>
 void* pick_fmt(int G, int hseg) {
   if (hseg == 2) {
     switch (G) {
-      case 1: return kernel_ptr<1, 2, Q4>();
-      case 2: return kernel_ptr<2, 2, Q4>();
-      case 4: return kernel_ptr<4, 2, Q4>();
-      case 8: return kernel_ptr<8, 2, Q4>();
+      case 1: return kernel_ptr<1, 2, Q4, LORA>();
+      case 2: return kernel_ptr<2, 2, Q4, LORA>();
+      case 4: return kernel_ptr<4, 2, Q4, LORA>();
+      case 8: return kernel_ptr<8, 2, Q4, LORA>();
     }
   } else if (hseg == 4) {
     switch (G) {
-      case 1: return kernel_ptr<1, 4, Q4>();
-      case 2: return kernel_ptr<2, 4, Q4>();
-      case 4: return kernel_ptr<4, 4, Q4>();
-      case 8: return kernel_ptr<8, 4, Q4>();
+      case 1: return kernel_ptr<1, 4, Q4, LORA>();
+      case 2: return kernel_ptr<2, 4, Q4, LORA>();
+      case 4: return kernel_ptr<4, 4, Q4, LORA>();
+      case 8: return kernel_ptr<8, 4, Q4, LORA>();
     }
   }
   return nullptr;
 }
 
-void* pick(int G, int hseg, int q4) { return q4 ? pick_fmt<true>(G, hseg) : pick_fmt<false>(G, hseg); }
+// The kernels with the LoRA-down CU and the attention items' up products are
+// separate instantiations, so that the adapter's code takes no registers from
+// the kernels without one.
+void* pick(int G, int hseg, int q4, int lora) {
+  if (lora) return q4 ? pick_fmt<true, true>(G, hseg) : pick_fmt<false, true>(G, hseg);
+  return q4 ? pick_fmt<true, false>(G, hseg) : pick_fmt<false, false>(G, hseg);
+}
 
 // Segments one wave of a CU with `units` units (rpu rows of nseg segments) loads.
 int wave_segs(int units, int rpu, int nseg) { return (units + kWaves - 1) / kWaves * rpu * nseg; }
@@ -1766,8 +1870,8 @@ int wave_segs(int units, int rpu, int nseg) { return (units + kWaves - 1) / kWav
 
 size_t persist_smem_bytes() { return sizeof(Smem); }
 
-int persist_prepare(int G, int hseg, int q4) {
-  void* fn = pick(G, hseg, q4);
+int persist_prepare(int G, int hseg, int q4, int lora) {
+  void* fn = pick(G, hseg, q4, lora);
   if (!fn) return -1;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
   if (e != hipSuccess) return (int)e;
@@ -1793,7 +1897,8 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
   // reads the kv head's rows again, which is cheap while they are few
   const int G = pc.nq / pc.nkv;
   const int X = (S == 1 && pc.nkv * G <= grid / 4) ? G : 1;
-  const int R = grid - pc.nkv * X * S;
+  const int nl = pc.lora_r > 0 ? 1 : 0;  // the LoRA-down CU (last of the QKV role)
+  const int R = grid - pc.nkv * X * S - nl;
   if (pc.q4) {  // int4 roles: whole 16-row blocks, CUs in proportion to the slots (16 rows x 128 columns)
     const int NB[4] = {pc.nqkv / 16, pc.H / 16, pc.I / 16, pc.H / 16};
     const int NG[4] = {pc.H / 128, pc.nq * D / 128, pc.H / 128, pc.I / 128};
@@ -1829,8 +1934,8 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
     out->chunk = chunk;
     out->X = X;
     out->start[0] = 0;
-    out->start[1] = n[0];
-    out->start[2] = n[0] + pc.nkv * X * S;
+    out->start[1] = n[0] + nl;
+    out->start[2] = out->start[1] + pc.nkv * X * S;
     out->start[3] = out->start[2] + n[1];
     out->start[4] = out->start[3] + n[2];
     out->start[5] = out->start[4] + n[3];
@@ -1896,8 +2001,8 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
   out->chunk = chunk;
   out->X = X;
   out->start[0] = 0;
-  out->start[1] = n[0];
-  out->start[2] = n[0] + pc.nkv * X * S;
+  out->start[1] = n[0] + nl;
+  out->start[2] = out->start[1] + pc.nkv * X * S;
   out->start[3] = out->start[2] + n[1];
   out->start[4] = out->start[3] + n[2];
   out->start[5] = out->start[4] + n[3];
@@ -1910,9 +2015,9 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
 // launch would guarantee it, but costs ~19 us more per step here.  If the
 // device is shared and a workgroup cannot start, the resident ones give up
 // after their bounded wait and the step is reported as abandoned.
-int persist_launch(const PersistConst* dev_const, int G, int hseg, int q4, int grid, const PersistStep& st,
-                   hipStream_t s) {
-  void* fn = pick(G, hseg, q4);
+int persist_launch(const PersistConst* dev_const, int G, int hseg, int q4, int lora, int grid,
+                   const PersistStep& st, hipStream_t s) {
+  void* fn = pick(G, hseg, q4, lora);
   if (!fn) return -1;
   PersistStep arg = st;
   void* args[] = {(void*)&dev_const, (void*)&arg};

@@ -76,7 +76,8 @@ typedef struct {
   uint8_t weight_format;  /* QD_W_BF16 or QD_W_INT4_G128 (projections only; E stays bf16) */
   int32_t max_pos;        /* KV-cache capacity in positions */
   int32_t max_prefill;    /* largest n accepted by one qd_prefill call */
-  int32_t lora_rank_max;  /* 0 disables LoRA; else the largest rank qd_set_lora accepts */
+  int32_t lora_rank_max;  /* 0 disables LoRA; else the largest rank qd_set_lora accepts (<= 64;
+                             QD_DECODE_PERSISTENT: ceil(r / 4) * ceil(hidden / 512) <= 24) */
   int32_t decode_path;    /* QD_DECODE_PERSISTENT (one kernel per decode step, one workgroup per CU,
                              at most 254 layers,
                              all resident at once: the device must not be running other work
@@ -195,8 +196,9 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
 
 /* Install (copy) a LoRA adapter ("EMBERGLASS (qwen-webgpu-lora) README", LoRA
  * sections: a live low-rank adapter on q_proj and v_proj).  Needs
- * lora_rank_max in 1..64 at qd_create (and decode_path QD_DECODE_GRAPH); rank
- * must be in 1..lora_rank_max and alpha finite.  The adapter applies to every
+ * lora_rank_max >= 1 at qd_create; rank must be in 1..lora_rank_max and alpha
+ * finite.  On the persistent decode step one more CU computes the down
+ * products A h and the attention items add the up products.  The adapter applies to every
  * later prefill and decode step; the KV cache is kept.  Synchronises the
  * stream.  qd_clear_lora removes it: the adapter's kernels no longer run, so
  * outputs are bit-for-bit those of the base model.
@@ -232,7 +234,8 @@ int qd_get_phase_trace(qd_handle* h, uint64_t* out_host, size_t capacity_elems, 
  * they hold the LAST layer's values of that step (which argument):
  *   QD_XCH_X0   f32 [hidden]        residual after the last layer (the final norm's input)
  *   QD_XCH_X1   f32 [hidden]        residual after the last layer's attention block
- *   QD_XCH_QKV  f32 [(nq+2nkv) d]   raw q|k|v projection (+bias, +LoRA), kv-group-major
+ *   QD_XCH_QKV  f32 [(nq+2nkv) d]   raw q|k|v projection (+bias; an adapter's up products are
+ *                                   added later, by the attention items), kv-group-major
  *                                   ([kv head g][q heads of g | k_g | v_g] x d)
  *   QD_XCH_ATTN f32 [nq d]          attention output, 16 significant bits
  *   QD_XCH_ACT  f32 [intermediate]  SiLU(gate) * up, 16 significant bits

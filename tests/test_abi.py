@@ -2,6 +2,7 @@
 include/qd.h declares, the ctypes mirrors match the C struct sizes, and
 qd_create rejects bad configurations before making any HIP call."""
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -73,13 +74,20 @@ def test_unknown_weight_format_is_rejected():
     assert rc == -1 and not h.value
 
 
-def test_lora_needs_the_graph_decode_path_and_a_bounded_rank():
-    cfg = qd.make_config(synth.TINY, max_prefill=16, lora_rank_max=16, decode_path=qd.QD_DECODE_PERSISTENT)
-    rc, h = _create(cfg)
-    assert rc == -1 and not h.value
+def test_lora_rank_bounds_per_decode_path():
+    """The persistent step's LoRA-down CU holds [A_q; A_v] in its 24 register
+    slots per lane: ceil(r / 4) * hidden / 512 <= 24 (r <= 48 at hidden 1024,
+    r <= 24 at 2048); the graph path takes r <= 64.  Rejected before any HIP call."""
+    big = dataclasses.replace(synth.TINY, hidden=2048)
+    for shape, r in ((synth.TINY, 49), (big, 25)):
+        cfg = qd.make_config(shape, max_prefill=16, lora_rank_max=r, decode_path=qd.QD_DECODE_PERSISTENT)
+        rc, h = _create(cfg)
+        assert rc == -1 and not h.value, (shape.hidden, r)
     cfg = qd.make_config(synth.TINY, max_prefill=16, lora_rank_max=65, decode_path=qd.QD_DECODE_GRAPH)
     rc, h = _create(cfg)
     assert rc == -1 and not h.value
+    err = qd.load_library().qd_last_error(None)
+    assert isinstance(err, bytes)
 
 
 def test_create_rejects_null_config():

@@ -118,7 +118,7 @@ def test_persistent_attention_merge_beyond_eight_splits(torch_cuda, prompt_len, 
     dec.close()
 
 
-@pytest.mark.parametrize("path", ["graph", "persistent", "persistent-64cu"])
+@pytest.mark.parametrize("path", ["graph", "persistent", "persistent-64cu", "persistent-lora"])
 def test_int4_3b_width_decode(torch_cuda, path, monkeypatch):
     """2-layer model at the 3B int4 widths (hidden 2048, intermediate 11008,
     16 q / 2 kv heads, q/k/v bias, no QK-norm, int4 group-128, V 4096): the
@@ -127,19 +127,25 @@ def test_int4_3b_width_decode(torch_cuda, path, monkeypatch):
     the decode step is the 3B-width step run 16 times.  With the persistent
     step on 64 CUs, every GEMV CU holds more slots than it loads ahead (up to
     ~170 per wave), so most of its weights stream in during the phase, as at
-    the 16K-context shape.  8-token prompt, every step's logits checked."""
+    the 16K-context shape.  With the rank-16 adapter of the LoRA workload
+    (alpha 32) the persistent step adds its LoRA-down CU.  8-token prompt,
+    every step's logits checked."""
+    from gpu_util import lora_to_device
     shape = QWEN25_INT4_2L
     log(f"3B-width int4, path={path}")
     w = synth.make_weights(shape, seed=45, random_gains=True)
-    oracle = OracleModel(shape, w)
+    lora = synth.make_lora(shape, 16, seed=47) if path.endswith("lora") else None
+    oracle = OracleModel(shape, w, lora=lora, lora_alpha=32.0)
     if path == "persistent-64cu":
         monkeypatch.setenv("QD_PERSIST_CUS", "64")
-    dec = make_decoder(torch_cuda, shape, 16, path.split("-")[0])
+    dec = make_decoder(torch_cuda, shape, 16, path.split("-")[0], lora_rank_max=16 if lora else 0)
     monkeypatch.delenv("QD_PERSIST_CUS", raising=False)
     dw = to_device(w)
     torch_cuda.cuda.synchronize()
     dec.load_weights(dw)
     del dw
+    if lora:
+        dec.set_lora(lora_to_device(lora), 16, 32.0)
     prompt = synth.make_prompt(shape.vocab, 8, seed=46)
     recs = lockstep_greedy(dec, oracle, prompt, 16, log=log)
     assert_records(recs, max_forced=1)

@@ -27,10 +27,10 @@ def torch_cuda():
     return torch
 
 
-def make_decoder(torch_cuda, shape, max_prefill, lora_rank_max=RANK):
+def make_decoder(torch_cuda, shape, max_prefill, lora_rank_max=RANK, path="graph"):
     import decoder_only_token_amd as qd
     cfg = qd.make_config(shape, max_prefill=max_prefill, lora_rank_max=lora_rank_max,
-                         decode_path=qd.QD_DECODE_GRAPH)
+                         decode_path=qd.QD_DECODE_GRAPH if path == "graph" else qd.QD_DECODE_PERSISTENT)
     return qd.Decoder(cfg, torch_cuda.cuda.current_stream().cuda_stream)
 
 
@@ -54,13 +54,15 @@ def run_logits(torch_cuda, dec, prompt, steps):
     return out
 
 
+@pytest.mark.parametrize("path", ["graph", "persistent"])
 @pytest.mark.parametrize("fmt", ["bf16", "int4"])
-def test_lora_decode_parity(torch_cuda, fmt):
+def test_lora_decode_parity(torch_cuda, fmt, path):
     """8-token prompt and 12 greedy steps with a rank-16 adapter (alpha 32); the
     adapter moves the oracle's logits far beyond the tolerance, and the GPU
-    follows the adapted oracle."""
+    follows the adapted oracle.  On the persistent step one more CU computes
+    the adapter's down products and the attention items add the up products."""
     shape = SHAPES[fmt]
-    log(f"lora decode {shape.name}")
+    log(f"lora decode {shape.name} path={path}")
     w = synth.make_weights(shape, seed=51, random_gains=True)
     lora = synth.make_lora(shape, RANK, seed=52)
     base = OracleModel(shape, w)
@@ -68,7 +70,7 @@ def test_lora_decode_parity(torch_cuda, fmt):
     prompt = synth.make_prompt(shape.vocab, 8, seed=53)
     moved = np.max(np.abs(oracle.forward(prompt)[-1] - base.forward(prompt)[-1]))
     assert moved > 10 * (ATOL + RTOL), moved
-    dec = make_decoder(torch_cuda, shape, 16)
+    dec = make_decoder(torch_cuda, shape, 16, path=path)
     dw, dl = to_device(w), lora_to_device(lora)
     torch_cuda.cuda.synchronize()
     dec.load_weights(dw)
@@ -108,16 +110,21 @@ def test_lora_batched_prefill(torch_cuda, fmt, n):
     assert ok, (ratio, nbad)
 
 
+@pytest.mark.parametrize("path", ["graph", "persistent"])
 @pytest.mark.parametrize("fmt", ["bf16", "int4"])
-def test_lora_cleared_is_bit_exact_base(torch_cuda, fmt):
+def test_lora_cleared_is_bit_exact_base(torch_cuda, fmt, path):
     """Base run; adapter set (outputs change); adapter cleared: the logits of
     every step equal the base run's bit for bit.  An adapter with B = 0 also
-    leaves every logit unchanged."""
+    leaves every logit unchanged: bit for bit on the graph path and in the
+    prefill; on the persistent step, whose plan gives the adapter's down
+    products a CU of their own (the other roles' rows are split otherwise, so
+    their sums run in another order), within the logit tolerance."""
     import torch
     shape = SHAPES[fmt]
+    log(f"lora cleared {shape.name} path={path}")
     w = synth.make_weights(shape, seed=57)
     lora = synth.make_lora(shape, RANK, seed=58)
-    dec = make_decoder(torch_cuda, shape, 32)
+    dec = make_decoder(torch_cuda, shape, 32, path=path)
     dw, dl = to_device(w), lora_to_device(lora)
     torch_cuda.cuda.synchronize()
     dec.load_weights(dw)
@@ -136,7 +143,11 @@ def test_lora_cleared_is_bit_exact_base(torch_cuda, fmt):
         zb = run_logits(torch_cuda, dec, prompt, 6)
         dec.clear_lora()
         for i, (a, b) in enumerate(zip(base, zb)):
-            assert np.array_equal(a, b), (len(prompt), i, float(np.max(np.abs(a - b))))
+            if path == "graph" or i == 0:
+                assert np.array_equal(a, b), (len(prompt), i, float(np.max(np.abs(a - b))))
+            else:  # the adapter's persistent step gives one CU to the down products: other row splits
+                ok, ratio, nbad = logits_within_tol(a, b.astype(np.float64))
+                assert ok, (len(prompt), i, ratio, nbad)
 
 
 def test_lora_argument_errors(torch_cuda):
