@@ -767,41 +767,46 @@ __device__ __forceinline__ void tiles_finish(const Ctx& c, Smem& sm, int l, cons
 }
 
 // int4 roles' input as int8 pieces for the matrix cores.  The phase input h
-// (f32, gain * x for normed phases) of each 128-column group g is written as
-// y = u (a + b / 128 + c / 16384) with a power of two u per group (the group's
-// largest |y| lies in [64 u, 128 u)), a = trunc(y / u), b and c the next
-// seven-bit digits (c rounded to nearest): |error| <= u / 32768, i.e. 2^-21 of
-// the group's largest input.  The pieces a, b, c go to rows 0, 4 and 8 of the
-// A operand of v_mfma_i32_16x16x64_i8 (the other rows are zero), so the three
-// products land in lanes 0-15, 16-31 and 32-47 of one result.  LDS layout per
-// group: [parity e][piece p][quarter q][16 bytes], byte 4 m + t of quarter q
-// being column 128 g + 32 q + 8 m + 2 t + e (the order in which the codes'
-// nibbles unpack); u / 16 per group follows the pieces.  Each 16-lane team of
-// a wave converts one of the wave's groups (lane: quarter q, dword m).
+// (f32, gain * x for normed phases) over the wave's groups (128 columns each;
+// group g belongs to wave g % 8) is written as y = u (a + b / 128 + c / 16384)
+// with one power of two u per wave (its largest |y| lies in [64 u, 128 u)),
+// a = trunc(y / u), b and c the next seven-bit digits (c rounded to nearest):
+// |error| <= u / 32768, i.e. 2^-21 of the wave's largest input.  The pieces
+// a, b, c go to rows 0, 4 and 8 of the A operand of v_mfma_i32_16x16x64_i8, so
+// the three products land in lanes 0-15, 16-31 and 32-47 of one result; the
+// other rows read a record of zeros after the groups.  LDS layout per group:
+// [parity e][piece p][quarter q][16 bytes], byte 4 m + t of quarter q being
+// column 128 g + 32 q + 8 m + 2 t + e (the order in which the codes' nibbles
+// unpack).  Each 16-lane team of a wave converts one of the wave's groups
+// (lane: quarter q, dword m).  Returns u / 16 (the codes enter as 16 code).
 constexpr int kQ4Group = 384;  // LDS bytes of one group's pieces
 
-__device__ __forceinline__ void q4_stage(const float* h, uint8_t* q8, const Q4Geo& q) {
+__device__ __forceinline__ float q4_stage(const float* h, uint8_t* q8, const Q4Geo& q) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int t = lane >> 4, l16 = lane & 15, qq = l16 >> 2, m = l16 & 3;
-  float* ug = reinterpret_cast<float*>(q8 + q.ng * kQ4Group);
+  float mx = 0.f;  // the wave's largest |y|
   for (int j0 = 0; j0 < q.cnt; j0 += 4) {  // wave-uniform
     const int j = j0 + t;
-    const bool act = j < q.cnt;
+    if (j < q.cnt) {
+      const int col = 128 * (wave + kWaves * j) + 32 * qq + 8 * m;
+      const f32x4 y0 = *reinterpret_cast<const f32x4*>(h + col);
+      const f32x4 y1 = *reinterpret_cast<const f32x4*>(h + col + 4);
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(y0.x), fabsf(y0.y)), fmaxf(fabsf(y0.z), fabsf(y0.w))));
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(y1.x), fabsf(y1.y)), fmaxf(fabsf(y1.z), fabsf(y1.w))));
+    }
+  }
+  mx = wave_max(mx);
+  const int E = (int)((__float_as_uint(mx) >> 23) & 0xFF);  // mx in [2^(E-127), 2^(E-126))
+  const bool live = E >= 6;  // inputs below 2^-121 (or all zero) are taken as zero
+  const float up = __uint_as_float((uint32_t)(live ? 260 - E : 127) << 23);  // 1 / u = 2^(133 - E)
+  for (int j0 = 0; j0 < q.cnt; j0 += 4) {  // wave-uniform
+    const int j = j0 + t;
+    if (j >= q.cnt) continue;
     const int g = wave + kWaves * j;
     const int col = 128 * g + 32 * qq + 8 * m;
-    f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0;
-    if (act) {
-      y0 = *reinterpret_cast<const f32x4*>(h + col);
-      y1 = *reinterpret_cast<const f32x4*>(h + col + 4);
-    }
+    const f32x4 y0 = *reinterpret_cast<const f32x4*>(h + col);
+    const f32x4 y1 = *reinterpret_cast<const f32x4*>(h + col + 4);
     const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-    float mx = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(y[k]));
-    mx = group_max<16>(mx);  // the team's group
-    const int E = (int)((__float_as_uint(mx) >> 23) & 0xFF);  // mx in [2^(E-127), 2^(E-126))
-    const bool live = E >= 6;  // a group below 2^-121 (or all zero) is taken as zero
-    const float up = __uint_as_float((uint32_t)(live ? 260 - E : 127) << 23);  // 1 / u = 2^(133 - E)
     uint32_t pk[6] = {0u, 0u, 0u, 0u, 0u, 0u};  // [parity][piece]
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -815,80 +820,89 @@ __device__ __forceinline__ void q4_stage(const float* h, uint8_t* q8, const Q4Ge
       pk[e3 + 1] |= ((uint32_t)(int)b & 0xFFu) << sh;
       pk[e3 + 2] |= ((uint32_t)(int)cc & 0xFFu) << sh;
     }
-    if (act) {
-      uint8_t* d = q8 + g * kQ4Group + qq * 16 + m * 4;
+    uint8_t* d = q8 + g * kQ4Group + qq * 16 + m * 4;
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        *reinterpret_cast<uint32_t*>(d + p * 64) = pk[p];
-        *reinterpret_cast<uint32_t*>(d + 192 + p * 64) = pk[3 + p];
-      }
-      if (l16 == 0) ug[g] = live ? ldexpf(1.0f, E - 137) : 0.f;  // u / 16 (the codes enter as 16 code)
+    for (int p = 0; p < 3; ++p) {
+      *reinterpret_cast<uint32_t*>(d + p * 64) = pk[p];
+      *reinterpret_cast<uint32_t*>(d + 192 + p * 64) = pk[3 + p];
     }
   }
+  if (lane < kQ4Group / 16)  // the record of zeros read by the A rows that hold no piece
+    reinterpret_cast<u32x4*>(q8 + q.ng * kQ4Group)[lane] = u32x4{0u, 0u, 0u, 0u};
+  return live ? ldexpf(1.0f, E - 137) : 0.f;
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// int4 GEMV role: stage the pieces, then every slot of the wave (the
-// registers loaded ahead, then streamed halves of kFirst / 2 slots, each half
-// reloaded as soon as it is consumed) as two int8 products (even and odd
-// columns of the group: the code nibbles become 16 code in the bytes' high
-// halves, exact), the slot's integer result scaled by its group scale and
-// u / 16 into a per-lane f32 sum; at the end of each row block the three
-// piece sums are weighted (1, 2^-7, 2^-14) and added across lanes in a fixed
-// order, and lanes 0-15 leave the wave's partial of each row in LDS for
+// int4 GEMV role: stage the pieces, then every slot of the wave in the order
+// (row block, group) (the registers loaded ahead, then streamed halves of
+// kFirst / 2 slots, each half reloaded as soon as it is consumed).  A slot is
+// two int8 products (even and odd columns of the group: the code nibbles
+// become 16 code in the bytes' high halves, exact) into one integer result,
+// which, scaled by the slot's group scale, joins a per-lane f32 sum one slot
+// later, so that the products' latency hides behind the next slot's work.
+// At the end of each row block the three piece sums are weighted (1, 2^-7,
+// 2^-14, times the wave's u / 16) and added across lanes in a fixed order,
+// and lanes 0-15 leave the wave's partial of each row in LDS for
 // tiles_finish.
 __device__ __forceinline__ void q4_phase(const Ctx& c, Smem& sm, int l, Regs<kFirst>& rg, uint32_t (&sc)[kFirst],
                                          float rs, const float* bias) {
   const Q4Geo q = q4_geo(c, l);
   const int lane = threadIdx.x & 63, wave = wave_id();
   uint8_t* q8 = reinterpret_cast<uint8_t*>(sm.vec[(l + 1) & 1]);  // the slot of the previous layer's input
-  q4_stage(sm.vec[l & 1], q8, q);
+  const float u16 = q4_stage(sm.vec[l & 1], q8, q);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave reads back its own pieces
-  const float* ug = reinterpret_cast<const float*>(q8 + q.ng * kQ4Group);
   const int l16 = lane & 15;
   const bool plane = (l16 & 3) == 0 && l16 < 12;  // A rows 0, 4, 8 hold the pieces
-  const int aoff = (l16 >> 2) * 64 + (lane >> 4) * 16;
-  const float pw = lane < 16 ? 1.0f : lane < 32 ? 0.0078125f : lane < 48 ? 6.103515625e-05f : 0.0f;
+  // A of the wave's group j at a0 + j astep (even columns; odd at + 192); the
+  // other rows read the record of zeros after the groups
+  const int a0 = plane ? wave * kQ4Group + (l16 >> 2) * 64 + (lane >> 4) * 16 : q.ng * kQ4Group;
+  const int astep = plane ? kWaves * kQ4Group : 0;
+  const float pw = (lane < 16 ? 1.0f : lane < 32 ? 0.0078125f : lane < 48 ? 6.103515625e-05f : 0.0f) * u16;
   const int nbb = q.ns * q.nb, cnt = max(q.cnt, 1);
-  float tot = 0.f;
+  int sb = 0, sj = 0;  // row block and group of the next slot
+  float tot = 0.f, ps = 0.f;
   int cur = 0;
+  i32x4 pp = {0, 0, 0, 0};  // the previous slot's result (scale ps)
   auto flush = [&]() {
-    float v = tot * pw;
-    v += __shfl_xor(v, 32, 64);
-    v += __shfl_xor(v, 16, 64);
-    if (lane < 16) sm.att[(cur * 16 + lane) * kWaves + wave] = v;
+    const float v = tot * pw;
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float v2 = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2), false, false);
+    const float v4 = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    if (lane < 16) sm.att[(cur * 16 + lane) * kWaves + wave] = v4;
     tot = 0.f;
     ++cur;
   };
-  auto slot = [&](const u32x4 w, uint32_t s16, int i) {
-    const int bb = i / cnt, j = i - bb * cnt;
-    while (cur < bb) flush();  // wave-uniform
-    const int g = wave + kWaves * j;
-    u32x4 ae = {0u, 0u, 0u, 0u}, ao = ae;
-    if (plane) {
-      ae = *reinterpret_cast<const u32x4*>(q8 + g * kQ4Group + aoff);
-      ao = *reinterpret_cast<const u32x4*>(q8 + g * kQ4Group + 192 + aoff);
+  auto slot = [&](const u32x4 w, uint32_t s16) {
+    const int bb = sb, j = sj;
+    if (++sj == cnt) {  // wave-uniform cursor of the next slot
+      sj = 0;
+      ++sb;
     }
+    const int aa = a0 + j * astep;
+    const u32x4 ae = *reinterpret_cast<const u32x4*>(q8 + aa);
+    const u32x4 ao = *reinterpret_cast<const u32x4*>(q8 + aa + 192);
     u32x4 be, bo;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t x = w[k] ^ 0x88888888u;  // code + 8 -> the code's 4-bit two's complement
-      be[k] = (x << 4) & 0xF0F0F0F0u;
-      bo[k] = x & 0xF0F0F0F0u;
+      be[k] = ((w[k] << 4) ^ 0x88888880u) & 0xF0F0F0F0u;
+      bo[k] = (w[k] ^ 0x88888888u) & 0xF0F0F0F0u;
     }
     i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, ae), __builtin_bit_cast(i32x4, be),
                                                       i32x4{0, 0, 0, 0}, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, ao), __builtin_bit_cast(i32x4, bo), acc, 0, 0,
                                                 0);
-    const float sv = __half2float(__ushort_as_half((uint16_t)s16)) * ug[g];
-    tot = fmaf((float)acc.x, sv, tot);
+    tot = fmaf((float)pp.x, ps, tot);  // the previous slot (its products are ready by now)
+    while (cur < bb) flush();  // wave-uniform
+    pp = acc;
+    ps = __half2float(__ushort_as_half((uint16_t)s16));
   };
   constexpr int HN = kFirst / 2;
   for (int base = 0; base < q.nslots; base += kFirst) {  // wave-uniform
 #pragma unroll
     for (int r = 0; r < HN; ++r)
-      if (base + r < q.nslots) slot(rg.R[r], sc[r], base + r);
+      if (base + r < q.nslots) slot(rg.R[r], sc[r]);
     if (base + kFirst < q.nslots) {
       Addr<HN> ad;
       SAddr<HN> sa;
@@ -902,7 +916,7 @@ __device__ __forceinline__ void q4_phase(const Ctx& c, Smem& sm, int l, Regs<kFi
     }
 #pragma unroll
     for (int r = 0; r < HN; ++r)
-      if (base + HN + r < q.nslots) slot(rg.R[HN + r], sc[HN + r], base + HN + r);
+      if (base + HN + r < q.nslots) slot(rg.R[HN + r], sc[HN + r]);
     if (base + kFirst + HN < q.nslots) {
       Addr<HN> ad;
       SAddr<HN> sa;
@@ -916,6 +930,7 @@ __device__ __forceinline__ void q4_phase(const Ctx& c, Smem& sm, int l, Regs<kFi
       load_scales<HN>(sc, sa);
     }
   }
+  tot = fmaf((float)pp.x, ps, tot);
   while (cur < nbb) flush();
   stamp(c, sm, 5 * l + c.role, 2, threadIdx.x == 0);
   __syncthreads();
