@@ -1929,19 +1929,45 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
       lo_sum += lo;
     }
     if (lo_sum > R) return -1;
-    for (int sum = lo_sum; sum < R; ++sum) {
-      int best = -1;
-      double bw = -1.0;
+    // the phases run one after another, so the spare CUs go where they cut
+    // the most slots per wave (the busiest wave of a CU: ceil(NB / n) blocks
+    // per row set, ceil(NG / 8) groups each), slots beyond the registers
+    // loaded ahead (which stream in during the phase, their load latency
+    // exposed) counted seven times; whole steps only, as a block count per CU
+    // drops at certain n
+    auto cost = [&](int r, int m) {
+      const int spw = sets[r] * ((NB[r] + m - 1) / m) * ((NG[r] + kWaves - 1) / kWaves);
+      return spw + 6 * std::max(0, spw - kFirst);
+    };
+    int left = R - lo_sum;
+    while (left > 0) {
+      int best = -1, bk = 0;
+      double bg = 0.0;
       for (int r = 0; r < 4; ++r) {
-        if (n[r] >= NB[r]) continue;
-        const double w = (double)NB[r] * NG[r] * sets[r] / n[r];
-        if (w > bw) {
-          bw = w;
-          best = r;
+        const int c0 = cost(r, n[r]);
+        for (int k = 1; k <= left && n[r] + k <= NB[r]; ++k) {
+          const int c1 = cost(r, n[r] + k);
+          if (c1 < c0) {
+            const double g = (double)(c0 - c1) / k;
+            if (g > bg) {
+              bg = g;
+              best = r;
+              bk = k;
+            }
+            break;
+          }
         }
       }
-      if (best < 0) break;
-      ++n[best];
+      if (best < 0) {  // no step left that helps: the rest to the busiest role that can take them
+        int r1 = -1;
+        for (int r = 0; r < 4; ++r)
+          if (n[r] < NB[r] && (r1 < 0 || cost(r, n[r]) > cost(r1, n[r1]))) r1 = r;
+        if (r1 < 0) break;
+        best = r1;
+        bk = 1;
+      }
+      n[best] += bk;
+      left -= bk;
     }
     out->pos = pos;
     out->seq = seq;
