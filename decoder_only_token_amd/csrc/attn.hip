@@ -131,8 +131,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
       const size_t off = (size_t)(t0 + pl) * D + sub * 32;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Kg + off) + i);
-        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Vg + off) + i);
+        kr[i] = reinterpret_cast<const f32x4*>(Kg + off)[i];
+        vr[i] = reinterpret_cast<const f32x4*>(Vg + off)[i];
       }
     } else {
 #pragma unroll
