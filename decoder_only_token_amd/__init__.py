@@ -57,7 +57,7 @@ class QdLora(ctypes.Structure):
                 ("a_q", _PP), ("b_q", _PP), ("a_v", _PP), ("b_v", _PP)]
 
 
-EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_decode_step", "qd_set_lora",
+EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_decode_step", "qd_decode_steps", "qd_set_lora",
            "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_enable_phase_trace", "qd_get_phase_trace",
            "qd_get_quantized", "qd_get_exchange", "qd_sync_token", "qd_get_abandoned", "qd_get_position",
            "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qd_reset_kv": (i32, [H]),
         "qd_prefill": (i32, [H, ctypes.POINTER(ctypes.c_int32), i32, ctypes.POINTER(QdSampling), _P, _P]),
         "qd_decode_step": (i32, [H, ctypes.POINTER(QdSampling), _P, _P]),
+        "qd_decode_steps": (i32, [H, i32, ctypes.POINTER(QdSampling), _P, _P]),
         "qd_set_lora": (i32, [H, ctypes.POINTER(QdLora)]),
         "qd_clear_lora": (i32, [H]),
         "qd_enable_capture": (i32, [H, i32]),
@@ -245,6 +246,11 @@ class Decoder:
     def decode_step(self, sampling: Optional[QdSampling] = None, logits_out=None, token_out=None):
         self._check(self.lib.qd_decode_step(self.h, ctypes.byref(sampling) if sampling else None,
                                             ctypes.c_void_p(_ptr(logits_out)), ctypes.c_void_p(_ptr(token_out))))
+
+    def decode_steps(self, n: int, sampling: Optional[QdSampling] = None, logits_out=None, tokens_out=None):
+        """n decode steps with device-resident token feedback (tokens_out: int32 device tensor of n)."""
+        self._check(self.lib.qd_decode_steps(self.h, int(n), None if sampling is None else ctypes.byref(sampling),
+                                             _ptr(logits_out), _ptr(tokens_out)))
 
     def set_lora(self, lora_layers: List[Dict], rank: int, alpha: float):
         q = QdLora()

@@ -23,6 +23,7 @@
 namespace {
 
 constexpr int kDecodeMinSplit = 16;  // shortest split of the decode attention
+constexpr int kMaxStepsPerLaunch = 64;  // decode steps in one persistent launch (8-bit step tags, 200 ms waits)
 constexpr int kGemmMinRows = 16;  // prefills of at least this many rows use the matrix-core projections
 
 struct Layer {
@@ -126,6 +127,7 @@ struct qd_handle {
   LayerPtrs* layer_ptrs = nullptr; // device array [L]
   uint64_t *X0 = nullptr, *X1 = nullptr, *QKVx = nullptr, *PART = nullptr, *Ox = nullptr, *ACT = nullptr;
   uint64_t* AM = nullptr;
+  uint64_t* TOK = nullptr;  // the persistent step's token word (multi-step launches)
   uint32_t* err_dev = nullptr;
   bool failed = false;  // a decode step was abandoned; needs qd_reset_kv
   PersistConst pc_host{};
@@ -574,7 +576,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
         (rc = dev_alloc(h, &h->QKVx, (size_t)qkv_rows(c) + 2 * c.lora_rank_max)) ||
         (rc = dev_alloc(h, &h->PART, (size_t)c.n_q_heads * smax * (d + 2))) ||
         (rc = dev_alloc(h, &h->Ox, (size_t)c.n_q_heads * d)) || (rc = dev_alloc(h, &h->ACT, I)) ||
-        (rc = dev_alloc(h, &h->AM, (size_t)2 * h->grid)) ||
+        (rc = dev_alloc(h, &h->AM, (size_t)2 * h->grid)) || (rc = dev_alloc(h, &h->TOK, 1)) ||
         (rc = dev_alloc(h, &h->err_dev, 4)) || (rc = dev_alloc(h, &h->pconst, 1)) ||
         (rc = dev_alloc(h, &h->layer_ptrs, (size_t)c.n_layers)))
       return fail(rc);
@@ -582,7 +584,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     // The value-pair buffers carry only 16 tag bits (8 of the step): they start
     // as all ones (layer 255, never a decoder layer), and a reset refills them.
     if (hipMemset(h->X0, 0, H * 8) || hipMemset(h->X1, 0, H * 8) || hipMemset(h->QKVx, 0, (qkv_rows(c) + 2 * c.lora_rank_max) * 8) ||
-        hipMemset(h->PART, 0, (size_t)c.n_q_heads * smax * (d + 2) * 8) || hipMemset(h->AM, 0, h->grid * 16) ||
+        hipMemset(h->PART, 0, (size_t)c.n_q_heads * smax * (d + 2) * 8) || hipMemset(h->AM, 0, h->grid * 16) || hipMemset(h->TOK, 0, 8) ||
         hipMemset(h->err_dev, 0, 16) || fill_pairs(h, nullptr) != QD_OK)
       return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
   }
@@ -718,7 +720,7 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
     pc.embed = h->embed; pc.final_norm = h->final_norm; pc.layers = h->layer_ptrs;
     pc.Kc = h->Kc; pc.Vc = h->Vc; pc.rope_cos = h->rope_cos; pc.rope_sin = h->rope_sin;
     pc.X0 = h->X0; pc.X1 = h->X1; pc.QKV = h->QKVx; pc.PART = h->PART; pc.O = h->Ox; pc.ACT = h->ACT;
-    pc.AM = h->AM; pc.logits = h->logits; pc.xf_out = nullptr; pc.st = h->st; pc.err = h->err_dev;
+    pc.AM = h->AM; pc.TOK = h->TOK; pc.logits = h->logits; pc.xf_out = nullptr; pc.st = h->st; pc.err = h->err_dev;
     pc.trace = h->trace_on ? h->trace : nullptr;
     h->pc_host = pc;
     HIP_TRY(h, hipMemcpyAsync(h->layer_ptrs, lp.data(), lp.size() * sizeof(LayerPtrs), hipMemcpyHostToDevice, s));
@@ -808,6 +810,44 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
   if ((rc = maybe_sample(h, sampling))) return rc;
   h->pos += 1;
   return copy_outputs(h, logits_dev, token_dev);
+}
+
+int qd_decode_steps(qd_handle* h, int32_t n, const qd_sampling* sampling, float* logits_dev, int32_t* tokens_dev) {
+  if (!h) return QD_E_ARG;
+  if (n < 1) return h->set_err(QD_E_ARG, "n must be >= 1");
+  if (!h->weights) return h->set_err(QD_E_STATE, "weights not loaded");
+  if (!h->have_token) return h->set_err(QD_E_STATE, "decode before prefill");
+  if ((int64_t)h->pos + n > h->cfg.max_pos) return h->set_err(QD_E_RANGE, "position would exceed max_pos");
+  int rc = check_sampling(h, sampling);
+  if (rc) return rc;
+  if (h->failed) return h->set_err(QD_E_STATE, "an earlier decode step was abandoned; call qd_reset_kv");
+  const bool greedy = !sampling || sampling->temperature <= 0.f || sampling->top_k == 1;
+  if (!h->persistent || !greedy || h->trace_on) {  // one step per launch, all enqueued without a host wait
+    for (int i = 0; i < n; ++i) {
+      if ((rc = qd_decode_step(h, sampling, i + 1 == n ? logits_dev : nullptr, tokens_dev ? tokens_dev + i : nullptr)))
+        return rc;
+    }
+    return QD_OK;
+  }
+  // greedy persistent: runs of steps with one split count per launch
+  const int G = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+  for (int done = 0; done < n;) {
+    const int m = persist_batch_len(h->pc_host, h->grid, h->pos, std::min(n - done, kMaxStepsPerLaunch));
+    if (h->seq + m >= (1u << 24)) h->seq = 0;  // tags of the launch's steps: seq + 1 .. seq + m
+    PersistStep st;
+    if (persist_plan(h->pc_host, h->grid, h->pos, h->seq + 1, &st) != 0)
+      return h->set_err(QD_E_HIP, "no CU role plan for this decode step");
+    st.nsteps = m;
+    st.tokens_out = tokens_dev ? tokens_dev + done : nullptr;
+    int e = persist_launch(h->pconst, G, h->hseg, h->cfg.weight_format == QD_W_INT4_G128, h->pc_host.lora_r > 0,
+                           h->grid, st, h->stream);
+    if (e != 0) return h->set_err(QD_E_HIP, "persistent decode launch failed: " + std::to_string(e));
+    h->seq += m;
+    h->pos += m;
+    done += m;
+  }
+  h->traced_step = false;
+  return copy_outputs(h, logits_dev, nullptr);
 }
 
 // The persistent step's copy of the adapter's rank and scale (its plan gives

@@ -52,6 +52,7 @@ struct PersistConst {
   uint64_t* O;     // [nq * 64] attention output, value pairs
   uint64_t* ACT;   // [I / 2] SwiGLU activations, value pairs
   uint64_t* AM;    // [grid][2] per-CU {best logit, best id (bit pattern)}
+  uint64_t* TOK;   // [1] the token a step chose, for the launch's next step
   float* logits;   // [V]
   float* xf_out;   // [H] final-normed row (optional)
   DevState* st;
@@ -77,6 +78,12 @@ struct PersistStep {
   int S, chunk;  // splits per kv head, positions per split
   int X;         // head groups per kv head: attention items = nkv X S
   int start[6];
+  // decode steps in this launch (positions pos .. pos + nsteps - 1, tags seq
+  // .. seq + nsteps - 1), all with this plan's CU roles and split count S
+  // (each step's splits one position longer, as its own plan would cut them);
+  // tokens_out (device, optional) receives the nsteps tokens
+  int nsteps;
+  int32_t* tokens_out;
 };
 
 size_t persist_smem_bytes();
@@ -84,5 +91,8 @@ int persist_prepare(int G, int hseg, int q4, int lora);  // lora: the instantiat
 // Plans the step at position pos for `grid` CUs; 0 on success, -1 if the
 // grid cannot hold the five roles.
 int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, PersistStep* out);
+// The number of steps from position pos (at most nmax) whose plans have the
+// same split count S, so one launch can run them with one plan.
+int persist_batch_len(const PersistConst& pc, int grid, int pos, int nmax);
 int persist_launch(const PersistConst* dev_const, int G, int hseg, int q4, int lora, int grid, const PersistStep& st,
                    hipStream_t s);

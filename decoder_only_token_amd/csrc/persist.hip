@@ -102,6 +102,24 @@ __device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ float ld_f(const float* p) { return *gl(p); }
 __device__ __forceinline__ void st_f(float* p, float v) { *gl(p) = v; }
 __device__ __forceinline__ uint32_t tag_of(uint32_t seq, int l) { return (seq << 8) | (uint32_t)l; }
+constexpr int kTokLayer = 254;  // tag "layer" of the token word (unique to that word)
+
+// Positions per attention split at context ctx, as the step plan cuts them:
+// splits no longer than the rows a CU loads ahead, on at most half the grid.
+__host__ __device__ inline int split_plan(int ctx, int grid, int nkv, int* chunk) {
+  const int span = kFirst / 8 * 64;
+  const int smax = grid / (2 * nkv);
+  int S = (ctx + span - 1) / span;
+  S = S < smax ? S : smax;
+  const int ch = (ctx + S - 1) / S;
+  *chunk = ch;
+  return (ctx + ch - 1) / ch;  // every split holds at least one position
+}
+__device__ __forceinline__ int step_chunk(int ctx, int grid, int nkv) {
+  int ch;
+  (void)split_plan(ctx, grid, nkv, &ch);
+  return ch;
+}
 
 // Value pairs: a 64-bit word {tag16 << 48 | a24 << 24 | b24} carries two
 // values rounded to 16 significant bits (the top 24 bits of the float, to
@@ -1590,7 +1608,7 @@ __device__ __forceinline__ void lmhead_phase(const Ctx& c, Smem& sm, Regs<kFirst
 
 // CU 0: argmax over the per-CU {value, id} pairs; (value desc, id asc) is a
 // total order, so the scan order does not matter.  Advances the step state.
-__device__ __forceinline__ void final_phase(const Ctx& c, Smem& sm) {
+__device__ __forceinline__ void final_phase(const Ctx& c, Smem& sm, int k, int32_t* tokens_out) {
   const AS4 PersistConst& a = *c.a;
   const int n = gridDim.x, ph = 5 * a.L + 1, slot = a.L + 1;  // the LM head used slot L
   float* vals = sm.vec[slot & 1];
@@ -1625,6 +1643,11 @@ __device__ __forceinline__ void final_phase(const Ctx& c, Smem& sm) {
     st->token = j;
     st->pos = c.pos + 1;
     st->step += 1;
+    if (tokens_out) *gl(tokens_out + k) = j;
+    // the token for the launch's next step, after the step state
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(gl(a.TOK), ((uint64_t)tag_of(c.seq, kTokLayer) << 32) | (uint32_t)j, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
   stamp(c, sm, ph, 5, lane == 0);
 }
@@ -1697,8 +1720,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
   c.v0 = (int)(((uint32_t)a.V * blockIdx.x) / gridDim.x);
   c.v1 = (int)(((uint32_t)a.V * (blockIdx.x + 1)) / gridDim.x);
   const int L = a.L, H = a.H, tid = threadIdx.x;
-  const uint16_t* emb = a.embed + (size_t)gl(a.st)->token * H;
   Regs<kFirst> rg;
+  for (int k = 0; k < stp.nsteps; ++k) {  // decode steps of this launch, each one's token feeding the next
+  int token;
+  if (k == 0) {
+    token = gl(a.st)->token;
+  } else {
+    // the next position: the same splits, each one position longer (as the
+    // per-step plan would cut them), and the token the last step chose
+    c.pos = stp.pos + k;
+    c.seq = stp.seq + k;
+    c.t0 = __builtin_amdgcn_s_memrealtime();
+    c.chunk = step_chunk(c.pos + 1, (int)gridDim.x, a.nkv);
+    if (tid == 0) {
+      const uint64_t want = (uint64_t)tag_of(c.seq - 1, kTokLayer) << 32;
+      uint64_t v;
+      uint32_t spin = 0;
+      while (((v = ld_tagged(a.TOK)) >> 32) != (want >> 32)) {
+        if ((++spin & 31) == 0 && timed_out(c)) {
+          st_u32(&c.a->err[0], 1);
+          sm.abort_flag = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      sm.red[47] = __int_as_float((int)(uint32_t)v);
+    }
+    __syncthreads();
+    if (sm.abort_flag) return;
+    token = __float_as_int(sm.red[47]);
+    // every row the last step wrote (the K/V cache rows) is read afresh
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  const uint16_t* emb = a.embed + (size_t)token * H;
   load_regs(rg, ahead_addr<HS, Q4, LORA>(c, 0, lora));
   __syncthreads();
   for (int l = 0; l < L; ++l) {
@@ -1813,6 +1867,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
         stamp(c, sm, ph, 2, tid == 0);
         if (!attn_finish<G>(c, sm, l)) return;
         attn_cache_write<G>(c, sm, l);
+        if (stp.nsteps > 1) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the row before later steps read it
       } else if (LORA && lora) {
         lora_phase(c, sm, l, rg, rs);
       } else {
@@ -1838,7 +1893,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_persistent(const Persist
     lmhead_phase<HS>(c, sm, rg, rs);
     stamp(c, sm, ph, 5, tid == 0);
   }
-  if (blockIdx.x == 0) final_phase(c, sm);
+  if (blockIdx.x == 0) final_phase(c, sm, k, stp.tokens_out);
+  if (sm.abort_flag) return;
+  }  // decode steps
   if (a.trace) {
     __syncthreads();
     trace_flush(c, sm);
@@ -1901,12 +1958,9 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
   if (pc.I % 2 != 0) return -1;  // the SwiGLU activations travel as value pairs
   const int ctx = pos + 1;
   // attention: splits no longer than the K/V rows a CU loads ahead, on at most half the grid
-  const int smax = grid / (2 * pc.nkv);
-  if (smax < 1) return -1;
-  const int span = kFirst / 8 * 64;  // positions in the slice loaded ahead
-  int S = std::min((ctx + span - 1) / span, smax);
-  const int chunk = (ctx + S - 1) / S;
-  S = (ctx + chunk - 1) / chunk;  // every split holds at least one position
+  if (grid / (2 * pc.nkv) < 1) return -1;
+  int chunk;
+  const int S = split_plan(ctx, grid, pc.nkv, &chunk);
   // short contexts: one item per q head (X = G head groups) instead of one per
   // kv head, which halves (or better) the serial work of an item; each group
   // reads the kv head's rows again, which is cheap while they are few
@@ -1969,6 +2023,8 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
       n[best] += bk;
       left -= bk;
     }
+    out->nsteps = 1;
+    out->tokens_out = nullptr;
     out->pos = pos;
     out->seq = seq;
     out->S = S;
@@ -2036,6 +2092,8 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
     if (best < 0) break;
     ++n[best];
   }
+  out->nsteps = 1;
+  out->tokens_out = nullptr;
   out->pos = pos;
   out->seq = seq;
   out->S = S;
@@ -2056,6 +2114,14 @@ int persist_plan(const PersistConst& pc, int grid, int pos, uint32_t seq, Persis
 // launch would guarantee it, but costs ~19 us more per step here.  If the
 // device is shared and a workgroup cannot start, the resident ones give up
 // after their bounded wait and the step is reported as abandoned.
+int persist_batch_len(const PersistConst& pc, int grid, int pos, int nmax) {
+  int ch;
+  const int S = split_plan(pos + 1, grid, pc.nkv, &ch);
+  int m = 1;
+  while (m < nmax && pos + m < pc.max_pos && split_plan(pos + m + 1, grid, pc.nkv, &ch) == S) ++m;
+  return m;
+}
+
 int persist_launch(const PersistConst* dev_const, int G, int hseg, int q4, int lora, int grid,
                    const PersistStep& st, hipStream_t s) {
   void* fn = pick(G, hseg, q4, lora);

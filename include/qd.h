@@ -194,6 +194,19 @@ int qd_prefill(qd_handle* h, const int32_t* tokens_host, int32_t n, const qd_sam
  * Errors: QD_E_STATE, QD_E_RANGE, QD_E_ARG (bad sampling). */
 int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev, int32_t* token_dev);
 
+/* n decode steps in one call, the token each step chooses feeding the next on
+ * the device, with no host wait in between ("EMBERGLASS (qwen-webgpu-lora)
+ * README", why it is fast: a GPU-resident batched decode loop, argmax to
+ * embedding on the GPU, one sync per batch).  tokens_dev (device int32[n],
+ * optional) receives the n tokens in order; logits_dev (optional) the last
+ * step's logits.  Greedy on QD_DECODE_PERSISTENT: one kernel launch runs the
+ * steps whose plans share one attention split count (a launch runs up to 64
+ * steps; a longer or split-count-crossing run takes a few launches); each
+ * step's results are bit for bit those of qd_decode_step.  Sampling,
+ * QD_DECODE_GRAPH or an enabled phase trace: one launch per step.
+ * Errors: as qd_decode_step; QD_E_ARG (n < 1), QD_E_RANGE (pos + n > max_pos). */
+int qd_decode_steps(qd_handle* h, int32_t n, const qd_sampling* sampling, float* logits_dev, int32_t* tokens_dev);
+
 /* Install (copy) a LoRA adapter ("EMBERGLASS (qwen-webgpu-lora) README", LoRA
  * sections: a live low-rank adapter on q_proj and v_proj).  Needs
  * lora_rank_max >= 1 at qd_create; rank must be in 1..lora_rank_max and alpha
