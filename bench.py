@@ -182,6 +182,36 @@ def decode_at_end(dec, wl, stream, steps, warmup):
             "bytes_per_step": sum(byts) / steps}
 
 
+def multistep_rate(dec, wl, stream, n=16, batches=3):
+    """qd_decode_steps with n tokens per call (one host synchronisation per
+    call), `batches` timed calls after one untimed, ending at the last cache
+    position; HIP events on the library's stream bracket the timed calls."""
+    import torch
+    end = wl.shape.max_pos
+    fill_to(dec, wl, stream, end - n * (batches + 1))
+    toks = torch.empty(n, dtype=torch.int32, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    with torch.cuda.stream(stream):
+        dec.decode_steps(n, tokens_out=toks)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(batches):
+            dec.decode_steps(n, tokens_out=toks)
+            stream.synchronize()  # one host synchronisation per call
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    if dec.abandoned():
+        raise RuntimeError("a persistent decode step was abandoned")
+    steps = n * batches
+    return {"tokens_per_call": n, "calls": batches, "tok_s": round(steps / wall, 2),
+            "step_us": round(a.elapsed_time(b) * 1e3 / steps, 2),
+            "note": "greedy; one launch per run of steps with one attention split count on the persistent "
+                    "path, one launch per step on the graph path"}
+
+
 def prefill_rate(dec, wl, stream, rows):
     """Median of 3 batched prefills of `rows` tokens from an empty cache; FLOPs
     are the algorithmic ones (2 per weight per row for the projections, the
@@ -377,6 +407,7 @@ def main():
                                "head + one embedding row + KV read and write at the step's context)"},
     }
     if not args.only_decode and not args.no_extra:
+        out["decode_steps_16"] = multistep_rate(dec, wl, stream)
         out["prefill_batched"] = prefill_rate(dec, wl, stream, wl.prompt_len)
     if not args.only_decode and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, dw, dl, shape.max_pos)
