@@ -287,6 +287,28 @@ def job_06b(stream, path):
                          "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name)}}
 
 
+def job_c4(stream, steps=20, warmup=5):
+    """qwen2.5-3b-int4 (4096 positions): decode at the end of the context on
+    the persistent step, with its roofline and measured traffic."""
+    import synth
+    import torch
+    wl = synth.WORKLOADS["qwen2.5-3b-int4"]
+    dw = synth.make_weights_device(wl.shape)
+    dec = make_decoder(wl, "persistent", stream, dw)
+    del dw
+    d = decode_at_end(dec, wl, stream, steps, warmup)
+    dec.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    us = d["event_ms"] * 1e3 / steps
+    ach = d["bytes_per_step"] / (us * 1e-6) / 1e9
+    return {"workload": wl.name, "decode_path": "persistent", "decode_tok_s": round(steps / d["wall_s"], 2),
+            "decode_step_us": round(us, 2), "decode_context": [d["ctx_first"], d["ctx_last"]],
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
+                         "kernel": "k_decode_persistent (one launch = one decode step)"}}
+
+
 def cpu_baseline(wl, dw, dl, ctx):
     """The float64 oracle on a bounded sample of the timed step: one decode
     token at context `ctx`, on the model cut to 1 and to 2 layers (its KV cache
@@ -346,6 +368,19 @@ def cpu_baseline(wl, dw, dl, ctx):
                       f"not counted); {cores} host threads"}
 
 
+def dtype_of(shape, path):
+    import synth
+    if shape.weight_format == synth.W_INT4_G128:
+        w = ("int4 group-128 projection weights x fp16 scales; " +
+             ("int8 matrix-core products against the input split into three 7-bit pieces (error <= 2^-21 of the "
+              "largest input of a wave's groups)" if path == "persistent" else
+              "codes widened in registers, f32 products (GEMV); bf16 hi/lo matrix-core products (prefill)"))
+    else:
+        w = "bf16 weights, matrix-core GEMV with the input as bf16 hi/lo halves (16 significant bits)"
+    return (w + "; bf16 tied embedding and LoRA factors; f32 accumulation, residual and KV cache" +
+            ("; attention output and SwiGLU activations exchanged at 16 significant bits" if path == "persistent" else ""))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -383,11 +418,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("int4 group-128 projection weights x fp16 scales, int8 matrix-core products against the input "
-                  "split into three 7-bit pieces (2^-21 of the group maximum)" if shape.weight_format == synth.W_INT4_G128
-                  else "bf16 weights, matrix-core GEMV with the input as bf16 hi/lo halves (16 significant bits)") +
-                 "; bf16 tied embedding and LoRA factors; f32 accumulation, residual and KV cache; attention output "
-                 "and SwiGLU activations exchanged at 16 significant bits",
+        "dtype": dtype_of(shape, path),
         "data": "synthetic (seeded N(0,0.02) weights drawn on the GPU and rounded to bf16, uniform random token ids)",
         "config": {"workload": wl.name, "layers": shape.n_layers, "hidden": shape.hidden,
                    "heads": [shape.n_q_heads, shape.n_kv_heads], "intermediate": shape.intermediate,
@@ -417,6 +448,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.only_decode and not args.no_extra and wl.name != "qwen3-0.6b":
         out["qwen3_0_6b"] = job_06b(stream, "persistent" if args.path == "auto" else args.path)
+    if not args.only_decode and not args.no_extra and wl.name != "qwen2.5-3b-int4":
+        out["qwen2_5_3b_int4"] = job_c4(stream)
     print(json.dumps(out), flush=True)
 
 
