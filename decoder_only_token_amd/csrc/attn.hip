@@ -68,13 +68,25 @@ __device__ __forceinline__ void norm_rope_head(const float* __restrict__ src, co
   out[l + 64] = b * c + a * s;
 }
 
-template <int G>
+// With an adapter (LORA), the block first adds the up products of its heads:
+// q_j += s B_q u_q and v += s B_v u_v ("EMBERGLASS (qwen-webgpu-lora) README",
+// LoRA sections), u = [A_q; A_v] h from the down-product GEMV, before QK-norm
+// and RoPE; one thread per adapted row, its row of B read as 16-byte pieces.
+struct LoraUp {
+  const float* u;      // [2 r]: u_q, u_v
+  const uint16_t* bq;  // [nq d][r] bf16
+  const uint16_t* bv;  // [nkv d][r] bf16
+  int r;
+  float scale;
+};
+
+template <int G, bool LORA>
 __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ qkv, const float* __restrict__ qn,
                                                      const float* __restrict__ kn, float eps,
                                                      const float* __restrict__ cos_t, const float* __restrict__ sin_t,
                                                      float* __restrict__ Kc, float* __restrict__ Vc, int max_pos,
                                                      const DevState* __restrict__ st, int S, int cmin, float scale,
-                                                     float* __restrict__ part) {
+                                                     float* __restrict__ part, LoraUp lu) {
   const int g = blockIdx.x, sp = blockIdx.y;
   const int ctx = st->pos + 1, pos = ctx - 1;
   const int C = split_len(ctx, S, cmin);
@@ -91,12 +103,36 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // group-major projection rows: [q heads g G .. g G + G - 1 | k_g | v_g] x D
   const float* grp = qkv + (size_t)g * (G + 2) * D;
-  for (int j = wave; j < G; j += 4) norm_rope_head(grp + j * D, qn, eps, cos_t, sin_t, pos, qs + j * D);
+  const float* qsrc = grp;          // the q heads' raw rows
+  const float* vsrc = grp + (G + 1) * D;  // and v's
+  if (LORA) {  // q and v with the adapter, into the V tile's LDS (free until the first tile)
+    float* raw = vs;  // [G D | D]
+    const int r = lu.r;
+    for (int row = tid; row < (G + 1) * D; row += 256) {
+      const bool isq = row < G * D;
+      const uint16_t* b = isq ? lu.bq + ((size_t)g * G * D + row) * r : lu.bv + ((size_t)g * D + row - G * D) * r;
+      const float* u = lu.u + (isq ? 0 : r);
+      float a = 0.f;
+      for (int k0 = 0; k0 < r; k0 += 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(b + k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a = fmaf(__uint_as_float(w[i] << 16), u[k0 + 2 * i], a);
+          a = fmaf(__uint_as_float(w[i] & 0xFFFF0000u), u[k0 + 2 * i + 1], a);
+        }
+      }
+      raw[row] = (isq ? grp[row] : grp[(G + 1) * D + row - G * D]) + lu.scale * a;
+    }
+    __syncthreads();
+    qsrc = raw;
+    vsrc = raw + G * D;
+  }
+  for (int j = wave; j < G; j += 4) norm_rope_head(qsrc + j * D, qn, eps, cos_t, sin_t, pos, qs + j * D);
   const bool owns_new = p_end == ctx;
   if (owns_new && wave == 3) {  // wave 3 has the fewest q heads
     norm_rope_head(grp + G * D, kn, eps, cos_t, sin_t, pos, kv_new);
-    kv_new[D + lane] = grp[(G + 1) * D + lane];
-    kv_new[D + 64 + lane] = grp[(G + 1) * D + 64 + lane];
+    kv_new[D + lane] = vsrc[lane];
+    kv_new[D + 64 + lane] = vsrc[64 + lane];
     float* kr = Kc + ((size_t)g * max_pos + pos) * D;
     float* vr = Vc + ((size_t)g * max_pos + pos) * D;
     kr[lane] = kv_new[lane];
@@ -459,12 +495,19 @@ int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin) {
 
 void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, const float* kn, float eps,
                              const float* cos_t, const float* sin_t, int nq, int nkv, float* Kc, float* Vc,
-                             int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out) {
+                             int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out,
+                             const float* lora_u, const uint16_t* lora_bq, const uint16_t* lora_bv, int lora_r,
+                             float lora_scale) {
   const float scale = 1.0f / sqrtf((float)D);
   const dim3 grid(nkv, S);
-#define QD_ATTN_DECODE(G_)                                                                                          \
-  hipLaunchKernelGGL(k_attn_decode<G_>, grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, Kc, Vc, max_pos, st, \
-                     S, cmin, scale, part)
+  const LoraUp lu{lora_u, lora_bq, lora_bv, lora_r, lora_scale};
+#define QD_ATTN_DECODE(G_)                                                                                         \
+  if (lora_u)                                                                                                      \
+    hipLaunchKernelGGL((k_attn_decode<G_, true>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, Kc, Vc,    \
+                       max_pos, st, S, cmin, scale, part, lu);                                                     \
+  else                                                                                                             \
+    hipLaunchKernelGGL((k_attn_decode<G_, false>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, Kc, Vc,   \
+                       max_pos, st, S, cmin, scale, part, lu)
   switch (nq / nkv) {
     case 1: QD_ATTN_DECODE(1); break;
     case 2: QD_ATTN_DECODE(2); break;

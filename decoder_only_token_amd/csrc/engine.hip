@@ -305,10 +305,12 @@ void enqueue_attention(qd_handle* h, int l, int T) {
   const int d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const size_t layer_kv = (size_t)nkv * c.max_pos * d;
   const Layer& L = h->layers[l];
-  if (T == 1) {  // QK-norm, RoPE and the cache write happen inside the decode attention
+  if (T == 1) {  // QK-norm, RoPE, the adapter's up products and the cache write happen inside the decode attention
+    const bool lo = h->lora_rank > 0;
     launch_attention_decode(s, h->qkv, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin, nq, nkv,
                             h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, h->dec_splits,
-                            kDecodeMinSplit, h->part, h->o);
+                            kDecodeMinSplit, h->part, h->o, lo ? h->lu : nullptr, lo ? h->lora[l].bq : nullptr,
+                            lo ? h->lora[l].bv : nullptr, h->lora_rank, h->lora_scale);
   } else {
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
                       h->st, h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
@@ -394,8 +396,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
         launch_gemv_bf16(s, h->lora[l].a, r2, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, nullptr,
                          h->lu + (size_t)t0 * r2, r2, 0, h->ncu);
       }
-      launch_lora_up(s, h->lu, r2, T, h->lora_rank, h->lora[l].bq, h->lora[l].bv, nq, c.n_kv_heads, d,
-                     h->lora_scale, h->qkv, NQKV);
+      if (T > 1)  // a decode step's up products are added by the attention blocks
+        launch_lora_up(s, h->lu, r2, T, h->lora_rank, h->lora[l].bq, h->lora[l].bv, nq, c.n_kv_heads, d,
+                       h->lora_scale, h->qkv, NQKV);
     }
     enqueue_attention(h, l, T);
     for (int t0 = 0, tt = tile(nq * d); t0 < T; t0 += tt) {

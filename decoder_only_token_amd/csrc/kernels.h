@@ -38,7 +38,9 @@ void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq
 int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin);
 void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, const float* kn, float eps,
                              const float* cos_t, const float* sin_t, int nq, int nkv, float* Kc, float* Vc,
-                             int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out);
+                             int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out,
+                             const float* lora_u = nullptr, const uint16_t* lora_bq = nullptr,
+                             const uint16_t* lora_bv = nullptr, int lora_r = 0, float lora_scale = 0.f);
 
 // Causal attention of T >= 2 new rows (attn.hip), rows at positions pos .. pos + T - 1.
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const float* Kc, const float* Vc,
