@@ -382,16 +382,17 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
     const Layer& L = h->layers[l];
     for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      if (q4)
+      if (q4)  // with an adapter, its down products u = [A_q; A_v] h ride along as bf16 rows
         launch_gemv_q4(s, L.cqkv, L.sqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
-                       h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
+                       h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu, h->lora_rank ? h->lora[l].a : nullptr,
+                       2 * h->lora_rank, h->lu + (size_t)t0 * 2 * h->lora_rank, 2 * h->lora_rank);
       else
         launch_gemv_bf16(s, L.wqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
                          h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
     }
     if (h->lora_rank) {
       const int r2 = 2 * h->lora_rank;
-      for (int t0 = 0, tt = gemv_t_tile(H); t0 < T; t0 += tt) {
+      for (int t0 = 0, tt = gemv_t_tile(H); t0 < T && !q4; t0 += tt) {  // (int4: inside the q|k|v GEMV)
         const int tn = std::min(tt, T - t0);
         launch_gemv_bf16(s, h->lora[l].a, r2, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, nullptr,
                          h->lu + (size_t)t0 * r2, r2, 0, h->ncu);

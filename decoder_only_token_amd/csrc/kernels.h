@@ -81,7 +81,8 @@ void launch_quantize_q4(hipStream_t s, const uint16_t* src, int nrows, int K, ui
 int q4_gemv_t_tile(int K);
 void launch_gemv_q4(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
                     int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate,
-                    int ncu);
+                    int ncu,
+                    const uint16_t* xw = nullptr, int xn = 0, float* xy = nullptr, int ldxy = 0);
 void launch_gemv_gateup_q4(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su,
                            int N, int K, const float* x, int ldx, int T, const float* gain, float eps, float* a,
                            int lda, int ncu);

@@ -49,6 +49,15 @@ __device__ __forceinline__ float f16_bits_to_f(uint16_t b) { return __half2float
 // without bank conflicts: within each 2048-column pass, lane l owns columns
 // 32 l .. 32 l + 31 (its 16 bytes of codes), and its j-th quadruple of inputs
 // (columns 32 l + 4 j .. + 3) sits at float offset (64 j + l) 4 of the pass.
+// Extra bf16 rows of a GEMV launch (see gemv_extra_bf16).
+struct XRows {
+  const uint16_t* W;  // [N][K] bf16, or null
+  int N;
+  float* y;
+  int ldy;
+  int blk0;  // first block of the extra rows
+};
+
 // Rows of the staged block are q4_stride(K) floats apart.
 __host__ __device__ inline int q4_stride(int K) { return (K + 2047) / 2048 * 2048; }
 
@@ -131,15 +140,79 @@ __device__ __forceinline__ void load_x32(const float* hp, f32x4* v, float& sx) {
 // requested together (the first NP before the input is staged), so a row of
 // up to NP * 2048 columns costs one HBM round trip.  TM = 1 (decode) keeps
 // the register count low enough for several waves per SIMD.
+// Blocks blk0 .. of the launch: bf16 rows W [N][K] against the same staged
+// input (one row per wave), yx[t][n] = row n . h[t] — the adapter's down
+// products beside the q|k|v rows, so they cost no launch of their own.
+template <int TM, int NP>
+__device__ __forceinline__ void gemv_extra_bf16(const XRows& xr, int K, const float* __restrict__ x, int ldx, int T,
+                                                const float* __restrict__ gain, float eps, float* h, float* red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = ((int)blockIdx.x - xr.blk0) * 4 + wave, ks = q4_stride(K), np = (K + 2047) / 2048;
+  const bool live = n < xr.N;
+  u32x4 w[NP][4];
+  auto load = [&](int pb) {  // 32 columns (64 bytes) of the row per lane and pass
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int k = (pb + p) * 2048 + lane * 32;
+      if (live && pb + p < np && k < K) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[p][m] = *reinterpret_cast<const u32x4*>(xr.W + (size_t)n * K + k + 8 * m);
+      }
+    }
+  };
+  load(0);
+  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  if (!live) return;
+  float acc[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) acc[t] = 0.f;
+  for (int pb = 0; pb < np; pb += NP) {
+    if (pb) load(pb);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (pb + p >= np || (pb + p) * 2048 + lane * 32 >= K) continue;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        if (t >= T) continue;
+        f32x4 v[8];
+        float sx;
+        load_x32(h + t * ks + (pb + p) * 2048 + lane * 4, v, sx);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {  // dword i of piece m: columns 8 m + 2 i, + 1
+            const uint32_t b = w[p][m][i];
+            const f32x4 a = v[2 * m + i / 2];
+            const float x0 = (i & 1) ? a.z : a.x, x1 = (i & 1) ? a.w : a.y;
+            acc[t] = fmaf(__uint_as_float(b << 16), x0, acc[t]);
+            acc[t] = fmaf(__uint_as_float(b & 0xFFFF0000u), x1, acc[t]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t < T) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0) xr.y[(size_t)t * xr.ldy + n] = s;
+    }
+  }
+}
+
 template <int RPW, int TM, int NP>
 __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4, const uint16_t* __restrict__ S4,
                                                  int N, int K, const float* __restrict__ x, int ldx, int T,
                                                  const float* __restrict__ gain, float eps,
                                                  const float* __restrict__ bias, float* __restrict__ y, int ldy,
-                                                 int accumulate) {
+                                                 int accumulate, XRows xr) {
   extern __shared__ float smem[];
   float* red = smem;
   float* h = smem + 8;
+  if (xr.W && (int)blockIdx.x >= xr.blk0) {  // block-uniform
+    gemv_extra_bf16<TM, NP>(xr, K, x, ldx, T, gain, eps, h, red);
+    return;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
   const int groups = K / 128, ks = q4_stride(K), np = (K + 2047) / 2048;
@@ -294,24 +367,27 @@ int q4_np(int K) {
 template <int RPW, int NP>
 void gemv_q4_np(hipStream_t s, dim3 grid, size_t lds, const uint8_t* codes, const uint16_t* scales, int N, int K,
                 const float* x, int ldx, int T, const float* gain, float eps, const float* bias, float* y, int ldy,
-                int accumulate) {
+                int accumulate, const XRows& xr0) {
+  XRows xr = xr0;
+  xr.blk0 = (int)grid.x;
+  const dim3 g2(grid.x + (xr.W ? (xr.N + 3) / 4 : 0));
   if (T == 1)
-    hipLaunchKernelGGL((k_gemv_q4<RPW, 1, NP>), grid, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain, eps,
-                       bias, y, ldy, accumulate);
+    hipLaunchKernelGGL((k_gemv_q4<RPW, 1, NP>), g2, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain, eps,
+                       bias, y, ldy, accumulate, xr);
   else
-    hipLaunchKernelGGL((k_gemv_q4<RPW, GEMV_MAX_T, 1>), grid, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain,
-                       eps, bias, y, ldy, accumulate);
+    hipLaunchKernelGGL((k_gemv_q4<RPW, GEMV_MAX_T, 1>), g2, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain,
+                       eps, bias, y, ldy, accumulate, xr);
 }
 
 template <int RPW>
 void gemv_q4_t(hipStream_t s, dim3 grid, size_t lds, const uint8_t* codes, const uint16_t* scales, int N, int K,
                const float* x, int ldx, int T, const float* gain, float eps, const float* bias, float* y, int ldy,
-               int accumulate) {
+               int accumulate, const XRows& xr) {
   switch (q4_np(K)) {
-    case 1: gemv_q4_np<RPW, 1>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
-    case 2: gemv_q4_np<RPW, 2>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
-    case 4: gemv_q4_np<RPW, 4>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
-    default: gemv_q4_np<RPW, 8>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate); break;
+    case 1: gemv_q4_np<RPW, 1>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate, xr); break;
+    case 2: gemv_q4_np<RPW, 2>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate, xr); break;
+    case 4: gemv_q4_np<RPW, 4>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate, xr); break;
+    default: gemv_q4_np<RPW, 8>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate, xr); break;
   }
 }
 
@@ -354,16 +430,17 @@ void launch_quantize_q4(hipStream_t s, const uint16_t* src, int nrows, int K, ui
 
 void launch_gemv_q4(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
                     int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate,
-                    int ncu) {
+                    int ncu, const uint16_t* xw, int xn, float* xy, int ldxy) {
   const size_t lds = (8 + (size_t)T * q4_stride(K)) * sizeof(float);
   const int r = q4_rpw(N, ncu, 4);
   const dim3 grid((N + 4 * r - 1) / (4 * r));
+  const XRows xr{xw, xn, xy, ldxy, 0};
   if (r == 4)
-    gemv_q4_t<4>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+    gemv_q4_t<4>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate, xr);
   else if (r == 2)
-    gemv_q4_t<2>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+    gemv_q4_t<2>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate, xr);
   else
-    gemv_q4_t<1>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+    gemv_q4_t<1>(s, grid, lds, codes, scales, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate, xr);
 }
 
 void launch_gemv_gateup_q4(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su,
