@@ -107,11 +107,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
   const float* vsrc = grp + (G + 1) * D;  // and v's
   if (LORA) {  // q and v with the adapter, into the V tile's LDS (free until the first tile)
     float* raw = vs;  // [G D | D]
+    float* us = vs + (G + 1) * D;  // u_q | u_v, after them
     const int r = lu.r;
+    if (tid < 2 * r) us[tid] = lu.u[tid];
+    __syncthreads();
     for (int row = tid; row < (G + 1) * D; row += 256) {
       const bool isq = row < G * D;
       const uint16_t* b = isq ? lu.bq + ((size_t)g * G * D + row) * r : lu.bv + ((size_t)g * D + row - G * D) * r;
-      const float* u = lu.u + (isq ? 0 : r);
+      const float* u = us + (isq ? 0 : r);
       float a = 0.f;
       for (int k0 = 0; k0 < r; k0 += 8) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(b + k0);
