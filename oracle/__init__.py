@@ -18,11 +18,13 @@ Sources followed (cited by page title and section in each function):
   * "flashmoon demo/README.md — Qwen3-0.6B inference": f32 KV cache, greedy
     (temp = 0) and temperature/top-k/top-p sampling.
   * "EMBERGLASS (qwen-webgpu-lora) README": int4 group-128 weights, rank-r
-    LoRA on the projections, batched prefill equal to sequential decode.
+    LoRA on the projections, batched prefill equal to sequential decode, and
+    the optional reduced-precision (bf16) KV cache.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, hand-worked examples (``tests/golden/``), invariants and special cases.
 """
 from .model import OracleModel, rmsnorm, rope_rotate, causal_gqa_attention, silu, swiglu_mlp, argmax_lowest  # noqa: F401
+from .model import round_bf16  # noqa: F401
 from .quant import quantize_int4_g128, dequantize_int4_g128  # noqa: F401
 from .sampling import splitmix64_output, uniform_for_step, sample_top_k_top_p  # noqa: F401

@@ -32,6 +32,17 @@ def widen_bf16_f32(bits) -> np.ndarray:
     return u.view(np.float32)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 value (8 significant bits), ties to even, as
+    float64.  A reduced-precision KV cache ("EMBERGLASS (qwen-webgpu-lora)
+    README", Context window & prefill sizes: the f32 KV could be quantised)
+    stores every key and value this way.  Written with frexp/ldexp: x = m 2^e
+    with m in [0.5, 1), and m is rounded to a multiple of 2^-8."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     """Row-wise RMSNorm over the last axis: g_j * x_j / sqrt(mean_k x_k^2 + eps).
 
@@ -133,8 +144,12 @@ class OracleModel:
     depends on a later one.
     """
 
-    def __init__(self, shape, weights: Dict, lora: Optional[List[Dict]] = None, lora_alpha: float = 0.0):
+    def __init__(self, shape, weights: Dict, lora: Optional[List[Dict]] = None, lora_alpha: float = 0.0,
+                 kv_bf16: bool = False):
         self.shape = shape
+        # kv_bf16: the cache keeps keys (after RoPE) and values rounded to bf16,
+        # and attention reads them back from it (the current rows included)
+        self.kv_store = round_bf16 if kv_bf16 else (lambda a: a)
         self.E = widen_bf16(weights["embed"])
         self.final_norm = widen_bf16(weights["final_norm"])
         self.layers = []
@@ -190,7 +205,8 @@ class OracleModel:
             q = rmsnorm(q, w["q_norm"], s.rms_eps)
             k = rmsnorm(k, w["k_norm"], s.rms_eps)
         q = rope_rotate(q, rows, s.rope_theta)
-        k = rope_rotate(k, pos, s.rope_theta)
+        k = self.kv_store(rope_rotate(k, pos, s.rope_theta))
+        v = self.kv_store(v)
         o = causal_gqa_attention(q, k, v, rows)
         xr = x[rows] + o.reshape(len(rows), nq * d) @ w["wo"].T
         h2 = rmsnorm(xr, w["mlp_norm"], s.rms_eps)
@@ -240,8 +256,8 @@ class OracleModel:
                 k = rmsnorm(k, w["k_norm"], s.rms_eps)
             q = rope_rotate(q, pos, s.rope_theta)
             k = rope_rotate(k, pos, s.rope_theta)
-            cache.k[li][p0:p0 + n] = k
-            cache.v[li][p0:p0 + n] = v
+            cache.k[li][p0:p0 + n] = self.kv_store(k)
+            cache.v[li][p0:p0 + n] = self.kv_store(v)
             o = causal_gqa_attention(q, cache.k[li][:p0 + n], cache.v[li][:p0 + n], pos)
             x = x + o.reshape(n, nq * d) @ w["wo"].T
             h2 = rmsnorm(x, w["mlp_norm"], s.rms_eps)

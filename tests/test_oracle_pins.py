@@ -545,3 +545,61 @@ def test_layer_rows_matches_the_full_forward(shape_name, lora):
         x_in = cap["embed"] if li == 0 else cap["layer_out"][li - 1]
         got = m.layer_rows(li, x_in, rows)
         np.testing.assert_allclose(got, cap["layer_out"][li][rows], rtol=1e-12, atol=1e-12)
+
+
+def test_round_bf16_hand_values():
+    """bf16 keeps 8 significant bits: 1 + 2^-8 is a tie between 1 and 1 + 2^-7
+    and goes to the even one (1); 1 + 3 2^-9 rounds up to 1 + 2^-7; signs and
+    powers of two pass through; the step doubles with each binade (2^-6 in
+    [2, 4), 8 in [1024, 2048))."""
+    from oracle import round_bf16
+    cases = {1.0: 1.0, 1.0 + 2 ** -8: 1.0, 1.0 + 3 * 2 ** -9: 1.0 + 2 ** -7, 1.0 + 2 ** -7: 1.0 + 2 ** -7,
+             1.0 + 3 * 2 ** -8: 1.0 + 2 ** -6, -1.0 - 2 ** -8: -1.0, 2.0 + 2 ** -7: 2.0,
+             3.0 + 2 ** -7: 3.0,  # half a step (2^-6 in [2, 4)) above 3, whose last bit is even
+             3.0 + 3 * 2 ** -8: 3.0 + 2 ** -6, 1024.0 + 3.0: 1024.0, 1024.0 + 5.0: 1032.0,  # steps of 8
+             0.0: 0.0, -0.5: -0.5, 2 ** -100: 2 ** -100}
+    for x, want in cases.items():
+        assert round_bf16(np.array([x]))[0] == want, x
+
+
+def test_round_bf16_matches_the_float32_bit_rule():
+    """On float32 inputs, round_bf16 equals rounding the float32 bit pattern to
+    its top 16 bits (round half to even on the dropped 16 bits) — an integer
+    rule independent of the frexp form used by the oracle."""
+    from oracle import round_bf16
+    rng = np.random.default_rng(40)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    x[:4] = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 65504.0], dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    want = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(round_bf16(x.astype(np.float64)), want)
+
+
+def test_kv_bf16_model_reads_back_rounded_keys_and_values():
+    """With a bf16 cache the decode step's output equals the f32-cache model's
+    exactly when every cached key and value is already a bf16 value (here:
+    zero q/k/v weights and k bias, so k = 0 and v is its bf16 bias);
+    and a decode from a cache filled at prefill equals the cache-less forward
+    (the rounding happens once, at the store)."""
+    shape = tiny_shape(qkv_bias=True)
+    w = synth.make_weights(shape, seed=41, random_gains=True)
+    toks = synth.make_prompt(shape.vocab, 9, seed=42)
+    m = OracleModel(shape, w, kv_bf16=True)
+    full = m.forward(toks)
+    cache = m.new_cache()
+    inc = np.concatenate([m.forward(toks[:4], cache)] + [m.forward([t], cache) for t in toks[4:]], axis=0)
+    np.testing.assert_allclose(inc, full, rtol=1e-12, atol=1e-13)
+    # the rounding is actually applied, and it is small
+    f32 = OracleModel(shape, w).forward(toks)
+    d = np.max(np.abs(f32 - full))
+    assert 0 < d < 0.05 * np.max(np.abs(f32))
+    # keys and values that are bf16 already: identical to the f32 cache
+    w2 = synth.make_weights(shape, seed=43)
+    for lw in w2["layers"]:  # k = 0 and v = its bf16 bias on every row
+        for nm in ("wq", "wk", "wv", "bk"):
+            lw[nm] = np.zeros_like(lw[nm])
+    a = OracleModel(shape, w2, kv_bf16=True).forward(toks)
+    b = OracleModel(shape, w2).forward(toks)
+    np.testing.assert_array_equal(a, b)
