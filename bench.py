@@ -111,20 +111,22 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def step_bytes(shape, lora_rank, ctx):
+def step_bytes(shape, lora_rank, ctx, kv_elem_bytes=4):
     """Algorithmic HBM bytes of one decode step whose context after the step is
     ctx: every weight once (layers, LoRA factors, tied head, one gathered row),
     the KV read of ctx - 1 cached positions and the write of the new one."""
     import synth
     wb = synth.weight_bytes(shape, lora_rank)
-    return wb["layers"] + wb["lora"] + wb["lm_head"] + wb["embed_row"] + synth.kv_bytes_per_position(shape) * ctx
+    kv = synth.kv_bytes_per_position(shape) * kv_elem_bytes // 4
+    return wb["layers"] + wb["lora"] + wb["lm_head"] + wb["embed_row"] + kv * ctx
 
 
-def make_decoder(wl, path, stream, dw, dl=None):
+def make_decoder(wl, path, stream, dw, dl=None, kv_bf16=False):
     import torch
     import decoder_only_token_amd as qd
     cfg = qd.make_config(wl.shape, max_prefill=wl.max_prefill, lora_rank_max=wl.lora_rank,
-                         decode_path=qd.QD_DECODE_PERSISTENT if path == "persistent" else qd.QD_DECODE_GRAPH)
+                         decode_path=qd.QD_DECODE_PERSISTENT if path == "persistent" else qd.QD_DECODE_GRAPH,
+                         kv_format=qd.QD_KV_BF16 if kv_bf16 else qd.QD_KV_F32)
     dec = qd.Decoder(cfg, stream.cuda_stream)
     dec.load_weights(dw)
     if dl is not None:
@@ -153,7 +155,7 @@ def fill_to(dec, wl, stream, target):
     assert dec.position == target
 
 
-def decode_at_end(dec, wl, stream, steps, warmup):
+def decode_at_end(dec, wl, stream, steps, warmup, kv_elem_bytes=4):
     """`warmup` untimed and `steps` timed decode steps ending at the last
     cache position; HIP events on the library's stream bracket the timed steps."""
     import torch
@@ -177,7 +179,7 @@ def decode_at_end(dec, wl, stream, steps, warmup):
         raise RuntimeError("a persistent decode step was abandoned (device shared with other work)")
     ms = a.elapsed_time(b)
     ctx0 = start + warmup + 1  # context after the first timed step
-    byts = [step_bytes(wl.shape, wl.lora_rank, ctx0 + i) for i in range(steps)]
+    byts = [step_bytes(wl.shape, wl.lora_rank, ctx0 + i, kv_elem_bytes) for i in range(steps)]
     return {"steps": steps, "wall_s": wall, "event_ms": ms, "ctx_first": ctx0, "ctx_last": ctx0 + steps - 1,
             "bytes_per_step": sum(byts) / steps}
 
@@ -307,6 +309,25 @@ def job_c4(stream, steps=20, warmup=5):
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
                          "kernel": "k_decode_persistent (one launch = one decode step)"}}
+
+
+def job_kv_bf16(wl, stream, dw, dl, steps=20, warmup=5):
+    """The headline workload with a bf16 KV cache (graph path): half the cache
+    bytes; the rounding of keys and values is part of that model variant."""
+    import torch
+    dec = make_decoder(wl, "graph", stream, dw, dl, kv_bf16=True)
+    d = decode_at_end(dec, wl, stream, steps, warmup, kv_elem_bytes=2)
+    dec.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    us = d["event_ms"] * 1e3 / steps
+    ach = d["bytes_per_step"] / (us * 1e-6) / 1e9
+    return {"workload": wl.name, "kv_format": "bf16", "decode_path": "graph",
+            "decode_tok_s": round(steps / d["wall_s"], 2), "decode_step_us": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": f"decode step (captured graph); algorithmic bytes per step = {d['bytes_per_step']:.4g} "
+                                   "(KV at 2 bytes per element)"}}
 
 
 def cpu_baseline(wl, dw, dl, ctx):
@@ -442,6 +463,11 @@ def main():
         out["prefill_batched"] = prefill_rate(dec, wl, stream, wl.prompt_len)
     if not args.only_decode and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, dw, dl, shape.max_pos)
+    if not args.only_decode and not args.no_extra and wl.name == "qwen2.5-3b-int4-lora":
+        dec.close()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["kv_bf16"] = job_kv_bf16(wl, stream, dw, dl)
     dec.close()
     del dw, dl
     torch.cuda.synchronize()

@@ -18,9 +18,10 @@ from typing import Dict, List, Optional, Sequence
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqd.so")
 
-QD_ABI_VERSION = 1
+QD_ABI_VERSION = 2
 QD_W_BF16, QD_W_INT4_G128 = 0, 1
 QD_DECODE_PERSISTENT, QD_DECODE_GRAPH = 0, 1
+QD_KV_F32, QD_KV_BF16 = 0, 1
 QD_CAP_EMBED, QD_CAP_LAYER_OUT, QD_CAP_FINAL_NORM, QD_CAP_LOGITS = 0, 1, 2, 3
 QD_XCH = {"x0": 0, "x1": 1, "qkv": 2, "attn": 3, "act": 4}
 QD_PROJ = {"wq": 0, "wk": 1, "wv": 2, "wo": 3, "w_gate": 4, "w_up": 5, "w_down": 6}
@@ -38,7 +39,7 @@ class QdConfig(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("qk_norm", ctypes.c_uint8), ("qkv_bias", ctypes.c_uint8), ("tie_embeddings", ctypes.c_uint8),
                 ("weight_format", ctypes.c_uint8), ("max_pos", ctypes.c_int32), ("max_prefill", ctypes.c_int32),
-                ("lora_rank_max", ctypes.c_int32), ("decode_path", ctypes.c_int32)]
+                ("lora_rank_max", ctypes.c_int32), ("decode_path", ctypes.c_int32), ("kv_format", ctypes.c_int32)]
 
 
 class QdWeights(ctypes.Structure):
@@ -125,7 +126,7 @@ class QdError(RuntimeError):
 
 
 def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Optional[int] = None,
-                decode_path: int = QD_DECODE_PERSISTENT) -> QdConfig:
+                decode_path: int = QD_DECODE_PERSISTENT, kv_format: int = QD_KV_F32) -> QdConfig:
     """Fill a QdConfig from any object with the model-shape attribute names."""
     c = QdConfig()
     c.struct_size = ctypes.sizeof(QdConfig)
@@ -142,6 +143,7 @@ def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Option
     c.max_prefill = int(max_prefill)
     c.lora_rank_max = int(lora_rank_max)
     c.decode_path = int(decode_path)
+    c.kv_format = int(kv_format)
     return c
 
 

@@ -80,11 +80,11 @@ struct LoraUp {
   float scale;
 };
 
-template <int G, bool LORA>
+template <int G, bool LORA, typename KVT>
 __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ qkv, const float* __restrict__ qn,
                                                      const float* __restrict__ kn, float eps,
                                                      const float* __restrict__ cos_t, const float* __restrict__ sin_t,
-                                                     float* __restrict__ Kc, float* __restrict__ Vc, int max_pos,
+                                                     KVT* __restrict__ Kc, KVT* __restrict__ Vc, int max_pos,
                                                      const DevState* __restrict__ st, int S, int cmin, float scale,
                                                      float* __restrict__ part, LoraUp lu) {
   const int g = blockIdx.x, sp = blockIdx.y;
@@ -134,14 +134,19 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
   const bool owns_new = p_end == ctx;
   if (owns_new && wave == 3) {  // wave 3 has the fewest q heads
     norm_rope_head(grp + G * D, kn, eps, cos_t, sin_t, pos, kv_new);
-    kv_new[D + lane] = vsrc[lane];
-    kv_new[D + 64 + lane] = vsrc[64 + lane];
-    float* kr = Kc + ((size_t)g * max_pos + pos) * D;
-    float* vr = Vc + ((size_t)g * max_pos + pos) * D;
-    kr[lane] = kv_new[lane];
-    kr[lane + 64] = kv_new[lane + 64];
-    vr[lane] = kv_new[D + lane];
-    vr[lane + 64] = kv_new[D + 64 + lane];
+    // the new row as the cache stores it (bf16 cache: rounded), for this step too
+    const float k0 = kv_round<KVT>(kv_new[lane]), k1 = kv_round<KVT>(kv_new[lane + 64]);
+    const float v0 = kv_round<KVT>(vsrc[lane]), v1 = kv_round<KVT>(vsrc[64 + lane]);
+    kv_new[lane] = k0;
+    kv_new[lane + 64] = k1;
+    kv_new[D + lane] = v0;
+    kv_new[D + 64 + lane] = v1;
+    KVT* kr = Kc + ((size_t)g * max_pos + pos) * D;
+    KVT* vr = Vc + ((size_t)g * max_pos + pos) * D;
+    st_kv(kr + lane, k0);
+    st_kv(kr + lane + 64, k1);
+    st_kv(vr + lane, v0);
+    st_kv(vr + lane + 64, v1);
   }
 
   const int pl = tid >> 2, sub = tid & 3;  // load / score mapping: position, quarter of the dims
@@ -160,8 +165,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
 #pragma unroll
   for (int r = 0; r < HPW; ++r) { M[r] = -INFINITY; L[r] = 0.f; }
 
-  const float* Kg = Kc + (size_t)g * max_pos * D;
-  const float* Vg = Vc + (size_t)g * max_pos * D;
+  const KVT* Kg = Kc + (size_t)g * max_pos * D;
+  const KVT* Vg = Vc + (size_t)g * max_pos * D;
   for (int t0 = p_begin; t0 < p_end; t0 += TP) {
     const int n = min(TP, p_end - t0);
     f32x4 kr[8], vr[8];
@@ -170,8 +175,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
       const size_t off = (size_t)(t0 + pl) * D + sub * 32;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        kr[i] = reinterpret_cast<const f32x4*>(Kg + off)[i];
-        vr[i] = reinterpret_cast<const f32x4*>(Vg + off)[i];
+        kr[i] = ld_kv4(Kg + off + 4 * i);
+        vr[i] = ld_kv4(Vg + off + 4 * i);
       }
     } else {
 #pragma unroll
@@ -323,10 +328,10 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
 // (row maxima and sums over the 16 lanes that hold a row, by DPP), writes
 // P's halves to its own LDS slice in the A-operand layout, and accumulates
 // its 16 x 128 output tile.
-template <int G>
+template <int G, typename KVT>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restrict__ q, int T, int nq,
-                                                           const float* __restrict__ Kc,
-                                                           const float* __restrict__ Vc, int max_pos,
+                                                           const KVT* __restrict__ Kc,
+                                                           const KVT* __restrict__ Vc, int max_pos,
                                                            const DevState* __restrict__ st, float scale,
                                                            float* __restrict__ o_out, int ldo) {
   constexpr int QV = 64, R = QV / G, BK = 32;
@@ -380,8 +385,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* Kg = Kc + (size_t)g * max_pos * D;
-  const float* Vg = Vc + (size_t)g * max_pos * D;
+  const KVT* Kg = Kc + (size_t)g * max_pos * D;
+  const KVT* Vg = Vc + (size_t)g * max_pos * D;
   // staging map: positions 4 p4 .. + 3, dims 4 c4 .. + 3
   const int p4 = tid & 7, c4 = tid >> 3;
 
@@ -393,8 +398,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
       const int p = 4 * p4 + pp;
       kr[pp] = vr[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (p < nk) {
-        kr[pp] = *reinterpret_cast<const f32x4*>(Kg + (size_t)(k0 + p) * D + 4 * c4);
-        vr[pp] = *reinterpret_cast<const f32x4*>(Vg + (size_t)(k0 + p) * D + 4 * c4);
+        kr[pp] = ld_kv4(Kg + (size_t)(k0 + p) * D + 4 * c4);
+        vr[pp] = ld_kv4(Vg + (size_t)(k0 + p) * D + 4 * c4);
       }
     }
     __syncthreads();  // the previous tile's K, V and P are consumed
@@ -497,20 +502,24 @@ int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin) {
 }
 
 void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, const float* kn, float eps,
-                             const float* cos_t, const float* sin_t, int nq, int nkv, float* Kc, float* Vc,
-                             int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out,
+                             const float* cos_t, const float* sin_t, int nq, int nkv, void* Kc, void* Vc,
+                             int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out,
                              const float* lora_u, const uint16_t* lora_bq, const uint16_t* lora_bv, int lora_r,
                              float lora_scale) {
   const float scale = 1.0f / sqrtf((float)D);
   const dim3 grid(nkv, S);
   const LoraUp lu{lora_u, lora_bq, lora_bv, lora_r, lora_scale};
-#define QD_ATTN_DECODE(G_)                                                                                         \
-  if (lora_u)                                                                                                      \
-    hipLaunchKernelGGL((k_attn_decode<G_, true>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, Kc, Vc,    \
-                       max_pos, st, S, cmin, scale, part, lu);                                                     \
-  else                                                                                                             \
-    hipLaunchKernelGGL((k_attn_decode<G_, false>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, Kc, Vc,   \
-                       max_pos, st, S, cmin, scale, part, lu)
+#define QD_ATTN_DECODE_T(G_, L_, T_)                                                                                 \
+  hipLaunchKernelGGL((k_attn_decode<G_, L_, T_>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, (T_*)Kc,   \
+                     (T_*)Vc, max_pos, st, S, cmin, scale, part, lu)
+#define QD_ATTN_DECODE(G_)                                     \
+  if (kv_bf16) {                                               \
+    if (lora_u) QD_ATTN_DECODE_T(G_, true, uint16_t);          \
+    else QD_ATTN_DECODE_T(G_, false, uint16_t);                \
+  } else {                                                     \
+    if (lora_u) QD_ATTN_DECODE_T(G_, true, float);             \
+    else QD_ATTN_DECODE_T(G_, false, float);                   \
+  }
   switch (nq / nkv) {
     case 1: QD_ATTN_DECODE(1); break;
     case 2: QD_ATTN_DECODE(2); break;
@@ -519,17 +528,22 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
     default: return;  // rejected by the host before any launch
   }
 #undef QD_ATTN_DECODE
+#undef QD_ATTN_DECODE_T
   hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32), dim3(256), 0, s, part, S, cmin, st, o_out);
 }
 
-void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const float* Kc, const float* Vc,
-                              int max_pos, const DevState* st, float* o_out, int ldo, int ncu) {
+void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
+                              int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu) {
   const float scale = 1.0f / sqrtf((float)D);
   const int G = nq / nkv;
   const dim3 grid(nkv, (T + 64 / G - 1) / (64 / G));
-#define QD_ATTN_PREFILL(G_)                                                                                   \
-  hipLaunchKernelGGL(k_attn_prefill_mfma<G_>, grid, dim3(256), 0, s, q, T, nq, Kc, Vc, max_pos, st, scale, o_out, \
-                     ldo)
+#define QD_ATTN_PREFILL(G_)                                                                                        \
+  if (kv_bf16)                                                                                                     \
+    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, uint16_t>), grid, dim3(256), 0, s, q, T, nq, (const uint16_t*)Kc,  \
+                       (const uint16_t*)Vc, max_pos, st, scale, o_out, ldo);                                        \
+  else                                                                                                             \
+    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, float>), grid, dim3(256), 0, s, q, T, nq, (const float*)Kc,        \
+                       (const float*)Vc, max_pos, st, scale, o_out, ldo)
   switch (G) {
     case 1: QD_ATTN_PREFILL(1); break;
     case 2: QD_ATTN_PREFILL(2); break;

@@ -22,6 +22,22 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// KV-cache elements: f32 as computed, or bf16 (nearest, ties to even) for the
+// half-size cache.  ld_kv4 reads 4 consecutive elements as f32; st_kv stores
+// one; kv_round is the value a store then a load gives back.
+__device__ __forceinline__ f32x4 ld_kv4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld_kv4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+}
+__device__ __forceinline__ void st_kv(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st_kv(uint16_t* p, float v) { *p = (uint16_t)bf16_rne(v); }
+template <typename KVT>
+__device__ __forceinline__ float kv_round(float v) {
+  if constexpr (sizeof(KVT) == 2) return __uint_as_float(bf16_rne(v) << 16);
+  return v;
+}
+
 // Lane exchange within rows of 16 lanes through DPP (no LDS round trip).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

@@ -87,7 +87,7 @@ struct qd_handle {
   float lora_scale = 0.f;       // alpha / rank
   float* lu = nullptr;          // [rows][2 lora_rank_max] down products
 
-  float* Kc = nullptr;  // [L][nkv][max_pos][d]
+  float* Kc = nullptr;  // [L][nkv][max_pos][d] f32, or bf16 (kv_format QD_KV_BF16) in the same allocation
   float* Vc = nullptr;
   float* rope_cos = nullptr;  // [max_pos][d/2]
   float* rope_sin = nullptr;
@@ -199,6 +199,11 @@ int validate_config(const qd_config* c, std::string& why) {
   if (c->max_prefill < 1 || c->max_prefill > c->max_pos) { why = "max_prefill must be in [1, max_pos]"; return QD_E_ARG; }
   if (c->lora_rank_max < 0 || c->lora_rank_max > 64) { why = "lora_rank_max must be in [0, 64]"; return QD_E_ARG; }
   if (c->decode_path != QD_DECODE_PERSISTENT && c->decode_path != QD_DECODE_GRAPH) { why = "unknown decode_path"; return QD_E_ARG; }
+  if (c->kv_format != QD_KV_F32 && c->kv_format != QD_KV_BF16) { why = "unknown kv_format"; return QD_E_ARG; }
+  if (c->kv_format == QD_KV_BF16 && c->decode_path != QD_DECODE_GRAPH) {
+    why = "a bf16 KV cache needs decode_path QD_DECODE_GRAPH";
+    return QD_E_ARG;
+  }
   if (c->decode_path == QD_DECODE_PERSISTENT) {
     // handshake tags carry the layer in 8 bits; 255 marks the argmax words and the unset value pairs
     if (c->n_layers > 254) { why = "the persistent decode step supports at most 254 layers"; return QD_E_ARG; }
@@ -299,23 +304,30 @@ void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
 }
 
 // Attention for T new rows (shared by both projection paths).
+// Layer l's block of a KV cache (elements of 4 or 2 bytes).
+void* kv_layer(qd_handle* h, float* base, int l) {
+  const qd_config& c = h->cfg;
+  const size_t layer_kv = (size_t)c.n_kv_heads * c.max_pos * c.head_dim;
+  return reinterpret_cast<char*>(base) + l * layer_kv * (c.kv_format == QD_KV_BF16 ? 2 : 4);
+}
+
 void enqueue_attention(qd_handle* h, int l, int T) {
   const qd_config& c = h->cfg;
   hipStream_t s = h->stream;
   const int d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
-  const size_t layer_kv = (size_t)nkv * c.max_pos * d;
+  const int kv16 = c.kv_format == QD_KV_BF16;
   const Layer& L = h->layers[l];
   if (T == 1) {  // QK-norm, RoPE, the adapter's up products and the cache write happen inside the decode attention
     const bool lo = h->lora_rank > 0;
     launch_attention_decode(s, h->qkv, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin, nq, nkv,
-                            h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, h->dec_splits,
+                            kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos, h->st, h->dec_splits,
                             kDecodeMinSplit, h->part, h->o, lo ? h->lu : nullptr, lo ? h->lora[l].bq : nullptr,
                             lo ? h->lora[l].bv : nullptr, h->lora_rank, h->lora_scale);
   } else {
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
-                      h->st, h->q, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos);
-    launch_attention_prefill(s, h->q, T, nq, nkv, h->Kc + l * layer_kv, h->Vc + l * layer_kv, c.max_pos, h->st, h->o,
-                             nq * d, h->ncu);
+                      h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16);
+    launch_attention_prefill(s, h->q, T, nq, nkv, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos, h->st,
+                             h->o, nq * d, h->ncu);
   }
 }
 
@@ -519,12 +531,14 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     h->own_stream = true;
   }
   const size_t H = c.hidden, d = c.head_dim, I = c.intermediate, rows = c.max_prefill;
-  const size_t kv = (size_t)c.n_layers * c.n_kv_heads * c.max_pos * d;
+  // KV elements as floats: a bf16 cache takes half (rounded up)
+  const size_t kv_elems = (size_t)c.n_layers * c.n_kv_heads * c.max_pos * d + 256 * d;
+  const size_t kvf = c.kv_format == QD_KV_BF16 ? (kv_elems + 1) / 2 : kv_elems;
   h->dec_splits = attn_decode_splits(c.max_pos, c.n_kv_heads, h->ncu, kDecodeMinSplit);
   h->part_floats = (size_t)c.n_q_heads * h->dec_splits * (d + 2);
   // the caches carry 256 rows of tail padding: the persistent decode step reads
   // (and ignores) up to 192 positions past the end of a split
-  if ((rc = dev_alloc(h, &h->Kc, kv + 256 * d)) || (rc = dev_alloc(h, &h->Vc, kv + 256 * d)) ||
+  if ((rc = dev_alloc(h, &h->Kc, kvf)) || (rc = dev_alloc(h, &h->Vc, kvf)) ||
       (rc = dev_alloc(h, &h->rope_cos, (size_t)c.max_pos * d / 2)) ||
       (rc = dev_alloc(h, &h->rope_sin, (size_t)c.max_pos * d / 2)) || (rc = dev_alloc(h, &h->x, rows * H)) ||
       (rc = dev_alloc(h, &h->qkv, rows * qkv_rows(c))) || (rc = dev_alloc(h, &h->q, rows * c.n_q_heads * d)) ||
@@ -541,8 +555,8 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
     return fail(rc);
   // caches start as zeros, padding included (rows are read past a split's end
   // and discarded; zeros keep even the discarded values finite)
-  if (hipMemset(h->Kc, 0, (kv + 256 * d) * sizeof(float)) != hipSuccess ||
-      hipMemset(h->Vc, 0, (kv + 256 * d) * sizeof(float)) != hipSuccess)
+  if (hipMemset(h->Kc, 0, kvf * sizeof(float)) != hipSuccess ||
+      hipMemset(h->Vc, 0, kvf * sizeof(float)) != hipSuccess)
     return fail(h->set_err(QD_E_HIP, "hipMemset failed"));
   if (hipHostMalloc((void**)&h->tokens_pinned, rows * sizeof(int32_t), hipHostMallocDefault) != hipSuccess)
     return fail(h->set_err(QD_E_OOM, "hipHostMalloc failed"));

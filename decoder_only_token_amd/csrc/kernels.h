@@ -30,21 +30,21 @@ void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* pa
                          int advance, int32_t* token_out);
 void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq, int nkv, int d, const float* qn,
                        const float* kn, float eps, const float* cos_t, const float* sin_t, const DevState* st,
-                       float* q_out, float* Kc, float* Vc, int max_pos);
+                       float* q_out, void* Kc, void* Vc, int max_pos, int kv_bf16);
 // Decode attention for one new row (attn.hip), from the raw q|k|v projection
 // row (group-major): QK-norm (gains may be null), RoPE, the cache write of the
 // new k / v, then S splits of length max(cmin, ceil(ctx / S)); part holds
 // nq * S * (d + 2) floats.
 int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin);
 void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, const float* kn, float eps,
-                             const float* cos_t, const float* sin_t, int nq, int nkv, float* Kc, float* Vc,
-                             int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out,
+                             const float* cos_t, const float* sin_t, int nq, int nkv, void* Kc, void* Vc,
+                             int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out,
                              const float* lora_u = nullptr, const uint16_t* lora_bq = nullptr,
                              const uint16_t* lora_bv = nullptr, int lora_r = 0, float lora_scale = 0.f);
 
 // Causal attention of T >= 2 new rows (attn.hip), rows at positions pos .. pos + T - 1.
-void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const float* Kc, const float* Vc,
-                              int max_pos, const DevState* st, float* o_out, int ldo, int ncu);
+void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
+                              int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu);
 
 // Top-k / temperature / top-p sampling over the logits (sample.hip); the token
 // goes to the device step state, which the greedy pass has already advanced.

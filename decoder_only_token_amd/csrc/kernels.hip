@@ -416,11 +416,12 @@ void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* pa
 // group-major: [kv head g][q heads of g | k_g | v_g].  "Failed Star / fs" block figure:
 // QK-norm comes before RoPE.  Pairs are (j, j + d/2).
 // grid (T, nq + nkv), block d/2 threads (one per rotation pair).
+template <typename KVT>
 __global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, int nkv, int d,
                              const float* __restrict__ qn, const float* __restrict__ kn, float eps,
                              const float* __restrict__ cos_t, const float* __restrict__ sin_t,
                              const DevState* __restrict__ st, float* __restrict__ q_out,
-                             float* __restrict__ Kc, float* __restrict__ Vc, int max_pos) {
+                             KVT* __restrict__ Kc, KVT* __restrict__ Vc, int max_pos) {
   const int t = blockIdx.x, head = blockIdx.y, j = threadIdx.x, half = d >> 1;
   const int pos = st->pos + t;
   const float* row = qkv + (size_t)t * ldqkv;
@@ -453,20 +454,24 @@ __global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, i
     qo[j] = ra;
     qo[j + half] = rb;
   } else {
-    float* kr = Kc + ((size_t)g * max_pos + pos) * d;
-    kr[j] = ra;
-    kr[j + half] = rb;
+    KVT* kr = Kc + ((size_t)g * max_pos + pos) * d;
+    st_kv(kr + j, ra);
+    st_kv(kr + j + half, rb);
     const float* vsrc = grp + (G + 1) * d;
-    float* vr = Vc + ((size_t)g * max_pos + pos) * d;
-    vr[j] = vsrc[j];
-    vr[j + half] = vsrc[j + half];
+    KVT* vr = Vc + ((size_t)g * max_pos + pos) * d;
+    st_kv(vr + j, vsrc[j]);
+    st_kv(vr + j + half, vsrc[j + half]);
   }
 }
 
 void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq, int nkv, int d, const float* qn,
                        const float* kn, float eps, const float* cos_t, const float* sin_t, const DevState* st,
-                       float* q_out, float* Kc, float* Vc, int max_pos) {
-  hipLaunchKernelGGL(k_qk_rope_kv, dim3(T, nq + nkv), dim3(d / 2), 0, s, qkv, ldqkv, nq, nkv, d, qn, kn, eps, cos_t,
-                     sin_t, st, q_out, Kc, Vc, max_pos);
+                       float* q_out, void* Kc, void* Vc, int max_pos, int kv_bf16) {
+  if (kv_bf16)
+    hipLaunchKernelGGL(k_qk_rope_kv<uint16_t>, dim3(T, nq + nkv), dim3(d / 2), 0, s, qkv, ldqkv, nq, nkv, d, qn, kn,
+                       eps, cos_t, sin_t, st, q_out, (uint16_t*)Kc, (uint16_t*)Vc, max_pos);
+  else
+    hipLaunchKernelGGL(k_qk_rope_kv<float>, dim3(T, nq + nkv), dim3(d / 2), 0, s, qkv, ldqkv, nq, nkv, d, qn, kn, eps,
+                       cos_t, sin_t, st, q_out, (float*)Kc, (float*)Vc, max_pos);
 }
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QD_ABI_VERSION 1
+#define QD_ABI_VERSION 2
 
 typedef struct qd_handle qd_handle; /* opaque; owns every device buffer it allocates */
 
@@ -83,9 +83,16 @@ typedef struct {
                              all resident at once: the device must not be running other work
                              meanwhile, else a step can be abandoned after its bounded wait)
                              or QD_DECODE_GRAPH (one kernel per operation, replayed as a hipGraph) */
+  int32_t kv_format;      /* QD_KV_F32 (keys and values as computed) or QD_KV_BF16 ("EMBERGLASS
+                             (qwen-webgpu-lora) README", Context window & prefill sizes: a quantised
+                             KV cache would roughly halve its size): every key (after RoPE) and value
+                             is rounded to bf16 (nearest, ties to even) when it is stored, and
+                             attention reads it back from the cache, the new rows included.  Half
+                             the cache bytes; QD_DECODE_GRAPH only. */
 } qd_config;
 
 enum { QD_DECODE_PERSISTENT = 0, QD_DECODE_GRAPH = 1 };
+enum { QD_KV_F32 = 0, QD_KV_BF16 = 1 };
 
 /* Weights: device pointers to bf16 (uint16 bit patterns), row-major [out, in].
  * Per-layer fields are HOST arrays of n_layers device pointers.  Shapes:

@@ -165,3 +165,14 @@ def test_sampler_workspace_size():
     assert qd.sample_workspace_bytes(8, qd.make_sampling(0.7, 9, 0.9, 1)) == 0
     assert qd.sample_workspace_bytes(524288, qd.make_sampling(0.7, 39, 0.9, 1)) == 512 * 39 * 8
     assert qd.sample_workspace_bytes(524288, qd.make_sampling(0.7, 40, 0.9, 1)) == 0  # merge LDS bound
+
+
+def test_bf16_kv_cache_needs_the_graph_path():
+    """kv_format QD_KV_BF16 runs on the graph decode path only, and unknown
+    formats are refused; both before any HIP call."""
+    cfg = qd.make_config(synth.TINY, max_prefill=16, decode_path=qd.QD_DECODE_PERSISTENT, kv_format=qd.QD_KV_BF16)
+    rc, h = _create(cfg)
+    assert rc == -1 and not h.value
+    cfg = qd.make_config(synth.TINY, max_prefill=16, decode_path=qd.QD_DECODE_GRAPH, kv_format=2)
+    rc, h = _create(cfg)
+    assert rc == -1 and not h.value
