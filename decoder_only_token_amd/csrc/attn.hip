@@ -71,7 +71,7 @@ __device__ __forceinline__ void norm_rope_head(const float* __restrict__ src, co
 // With an adapter (LORA), the block first adds the up products of its heads:
 // q_j += s B_q u_q and v += s B_v u_v ("EMBERGLASS (qwen-webgpu-lora) README",
 // LoRA sections), u = [A_q; A_v] h from the down-product GEMV, before QK-norm
-// and RoPE; one thread per adapted row, its row of B read as 16-byte pieces.
+// and RoPE; one thread per adapted row.
 struct LoraUp {
   const float* u;      // [2 r]: u_q, u_v
   const uint16_t* bq;  // [nq d][r] bf16
@@ -115,15 +115,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
       const bool isq = row < G * D;
       const uint16_t* b = isq ? lu.bq + ((size_t)g * G * D + row) * r : lu.bv + ((size_t)g * D + row - G * D) * r;
       const float* u = us + (isq ? 0 : r);
-      float a = 0.f;
-      for (int k0 = 0; k0 < r; k0 += 8) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(b + k0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a = fmaf(__uint_as_float(w[i] << 16), u[k0 + 2 * i], a);
-          a = fmaf(__uint_as_float(w[i] & 0xFFFF0000u), u[k0 + 2 * i + 1], a);
-        }
-      }
+      float a = 0.f;  // (rows of B are r values apart, any r)
+      for (int k = 0; k < r; ++k) a = fmaf(bf16_to_f(b[k]), u[k], a);
       raw[row] = (isq ? grp[row] : grp[(G + 1) * D + row - G * D]) + lu.scale * a;
     }
     __syncthreads();
@@ -267,6 +260,297 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
     if (j < G && lane == 0) {
       base[(size_t)j * S * (D + 2)] = M[r];
       base[(size_t)j * S * (D + 2) + 1] = L[r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The same split-K decode attention for G = 8 query heads per kv head, with a
+// tile layout that keeps the operands of both products in registers.  Lane
+// bits 0, 1, 4, 5 give the dim group dg (dims 4 dg .. + 3 and 64 + 4 dg ..
+// + 3), lane bits 2, 3 and the wave give the position group pg (positions
+// pg, pg + 16, pg + 32, pg + 48 of a 64-position tile).  A thread holds its
+// 8 dims of q for all 8 heads, and of K and V for its 4 positions:
+//   * QK: 8 heads x 4 positions partial dots over 8 dims, then a reduce-
+//     scatter over the 16 dim groups (row swaps over lane bits 5 and 4, DPP
+//     over bits 1 and 0) leaves each lane 2 complete scores;
+//   * softmax per head as in the generic kernel (one position per lane);
+//   * PV: o[8 heads][8 dims] += p * V from the thread's own V registers, the
+//     probabilities read as [position][head] rows;
+// and at the split's end the 16 position groups' partial outputs are added
+// (DPP within a wave, then the 4 waves through LDS, in a fixed order).  The
+// next tile's K is requested after QK and its V after PV, as buffer loads
+// bounded by the split (zeros past it).
+
+// Reduce-scatter step over lane bit 5 (d = 32) or 4 (d = 16) with the gfx950
+// row swaps: lanes with the bit clear return a + a of the partner lane, lanes
+// with it set b + b of the partner.
+template <int d>
+__device__ __forceinline__ float swap_add(float a, float b) {
+  const auto r = d == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                         : __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The same step over lane bit 1 (CTRL = xor 2) or 0 (xor 1) through DPP.
+template <int CTRL>
+__device__ __forceinline__ float quad_add(float a, float b, bool bit) {
+  return (bit ? b : a) + dpp_f<CTRL>(bit ? a : b);
+}
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b, float c) {
+  c = fmaf(a.x, b.x, c);
+  c = fmaf(a.y, b.y, c);
+  c = fmaf(a.z, b.z, c);
+  return fmaf(a.w, b.w, c);
+}
+
+// A buffer record over `bytes` bytes at `base` (both the same in every lane;
+// taken from lane 0 so the record lives in scalar registers rather than being
+// rebuilt lane by lane around every load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_record(const void* base, int bytes) {
+  const uint64_t v = (uint64_t)base;
+  const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// 4 values of one K or V row at byte offset `off` of the split's record
+template <typename KVT>
+__device__ __forceinline__ f32x4 kv_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (sizeof(KVT) == 4) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  } else {
+    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return f32x4{bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y)};
+  }
+}
+
+template <bool LORA, typename KVT>
+__global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ qkv, const float* __restrict__ qn,
+                                                      const float* __restrict__ kn, float eps,
+                                                      const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+                                                      KVT* __restrict__ Kc, KVT* __restrict__ Vc, int max_pos,
+                                                      const DevState* __restrict__ st, int S, int cmin, float scale,
+                                                      float* __restrict__ part, LoraUp lu) {
+  constexpr int G = 8;
+  const int g = blockIdx.x, sp = blockIdx.y;
+  const int ctx = st->pos + 1, pos = ctx - 1;
+  const int C = split_len(ctx, S, cmin);
+  const int p_begin = sp * C;
+  if (p_begin >= ctx) return;  // the merge reads only the splits that hold positions
+  const int p_end = min(p_begin + C, ctx);
+
+  __shared__ __align__(16) float qs[G * D];
+  __shared__ __align__(16) float ps[G * TP];  // scores [head][position]
+  __shared__ __align__(16) float pt[TP * G];  // probabilities [position][head]
+  __shared__ __align__(16) float cs[G];       // per-head rescale of this tile
+  __shared__ __align__(16) float kv_new[2 * D];
+  __shared__ __align__(16) float ored[4 * 16 * 64];  // the waves' partial outputs (first: adapter scratch)
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* grp = qkv + (size_t)g * (G + 2) * D;
+  const float* qsrc = grp;
+  const float* vsrc = grp + (G + 1) * D;
+  if (LORA) {  // q and v with the adapter, in the output scratch (free until the split's end)
+    float* raw = ored;             // [G D | D]
+    float* us = ored + (G + 1) * D;  // u_q | u_v
+    const int r = lu.r;
+    if (tid < 2 * r) us[tid] = lu.u[tid];
+    __syncthreads();
+    for (int row = tid; row < (G + 1) * D; row += 256) {
+      const bool isq = row < G * D;
+      const uint16_t* b = isq ? lu.bq + ((size_t)g * G * D + row) * r : lu.bv + ((size_t)g * D + row - G * D) * r;
+      const float* u = us + (isq ? 0 : r);
+      float a = 0.f;
+      for (int k = 0; k < r; ++k) a = fmaf(bf16_to_f(b[k]), u[k], a);
+      raw[row] = (isq ? grp[row] : grp[(G + 1) * D + row - G * D]) + lu.scale * a;
+    }
+    __syncthreads();
+    qsrc = raw;
+    vsrc = raw + G * D;
+  }
+  for (int j = wave; j < G; j += 4) norm_rope_head(qsrc + j * D, qn, eps, cos_t, sin_t, pos, qs + j * D);
+  const bool owns_new = p_end == ctx;
+  if (owns_new && wave == 3) {
+    norm_rope_head(grp + G * D, kn, eps, cos_t, sin_t, pos, kv_new);
+    const float k0 = kv_round<KVT>(kv_new[lane]), k1 = kv_round<KVT>(kv_new[lane + 64]);
+    const float v0 = kv_round<KVT>(vsrc[lane]), v1 = kv_round<KVT>(vsrc[64 + lane]);
+    kv_new[lane] = k0;
+    kv_new[lane + 64] = k1;
+    kv_new[D + lane] = v0;
+    kv_new[D + 64 + lane] = v1;
+    KVT* kr = Kc + ((size_t)g * max_pos + pos) * D;
+    KVT* vr = Vc + ((size_t)g * max_pos + pos) * D;
+    st_kv(kr + lane, k0);
+    st_kv(kr + lane + 64, k1);
+    st_kv(vr + lane, v0);
+    st_kv(vr + lane + 64, v1);
+  }
+
+  const int dg = (lane & 3) | ((lane >> 4) << 2);
+  const int pg = wave * 4 + ((lane >> 2) & 3);
+  const bool b0 = lane & 1, b1 = lane & 2;
+  const int isel = (lane >> 4) & 3;  // which of the lane's 4 positions its two final scores belong to
+  const int jsel = 4 * (int)b1 + 2 * (int)b0;  // and their heads: jsel, jsel + 1
+  const int kv_bytes = (p_end - p_begin) * D * (int)sizeof(KVT);
+  const __amdgpu_buffer_rsrc_t rk = kv_record(Kc + ((size_t)g * max_pos + p_begin) * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = kv_record(Vc + ((size_t)g * max_pos + p_begin) * D, kv_bytes);
+  const int esz = (int)sizeof(KVT);
+  // byte offset of (tile-relative row r, half h) in the split's record
+  auto off = [&](int r, int h) { return (r * D + 64 * h + 4 * dg) * esz; };
+  f32x4 kk[4][2], vv[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kk[i][h] = kv_load4<KVT>(rk, off(pg + 16 * i, h));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vv[i][h] = kv_load4<KVT>(rv, off(pg + 16 * i, h));
+
+  __syncthreads();  // q and the new row staged
+  f32x4 qq[G][2];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qq[j][h] = *reinterpret_cast<const f32x4*>(qs + j * D + 64 * h + 4 * dg);
+  f32x4 acc[G][2];
+#pragma unroll
+  for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float M[2], L[2];
+  M[0] = M[1] = -INFINITY;
+  L[0] = L[1] = 0.f;
+
+  for (int t0 = p_begin; t0 < p_end; t0 += TP) {
+    const int n = min(TP, p_end - t0);
+    if (owns_new) {  // the new row: from LDS, not the cache
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (t0 + pg + 16 * i == pos) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            kk[i][h] = *reinterpret_cast<const f32x4*>(kv_new + 64 * h + 4 * dg);
+            vv[i][h] = *reinterpret_cast<const f32x4*>(kv_new + D + 64 * h + 4 * dg);
+          }
+        }
+      }
+    }
+    // ---- scores: partial dots, then the reduce-scatter over the dim groups
+    float sc[32];  // [position i][head j] = sc[8 i + j]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < G; ++j) sc[8 * i + j] = dot4(kk[i][1], qq[j][1], dot4(kk[i][0], qq[j][0], 0.f));
+    const int tn = t0 + TP - p_begin;  // the next tile's first row in the record
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) kk[i][h] = kv_load4<KVT>(rk, off(tn + pg + 16 * i, h));
+    float r1[16], r2[8], r3[4];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) r1[k] = swap_add<32>(sc[k], sc[k + 16]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r2[k] = swap_add<16>(r1[k], r1[k + 8]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r3[k] = quad_add<kDppQuadSwap2>(r2[k], r2[k + 4], b1);
+    const float s0 = quad_add<kDppQuadSwap1>(r3[0], r3[2], b0);
+    const float s1 = quad_add<kDppQuadSwap1>(r3[1], r3[3], b0);
+    {
+      const int pr = pg + 16 * isel;
+      const bool ok = pr < n;
+      ps[jsel * TP + pr] = ok ? s0 * scale : -INFINITY;
+      ps[(jsel + 1) * TP + pr] = ok ? s1 * scale : -INFINITY;
+    }
+    __syncthreads();
+    // ---- online softmax, heads wave and wave + 4 (one position per lane)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int j = wave + 4 * rr;
+      const float sv = ps[j * TP + lane];
+      const float mn = fmaxf(M[rr], wave_max(sv));
+      const float p = __expf(sv - mn);
+      const float c = __expf(M[rr] - mn);
+      L[rr] = L[rr] * c + wave_sum(p);
+      M[rr] = mn;
+      pt[lane * G + j] = p;
+      if (lane == 0) cs[j] = c;
+    }
+    __syncthreads();
+    // ---- PV from the thread's own V rows
+    {
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs), c1 = *reinterpret_cast<const f32x4*>(cs + 4);
+      const float cj[G] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        acc[j][0] *= cj[j];
+        acc[j][1] *= cj[j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float* pp = pt + (pg + 16 * i) * G;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(pp), p1 = *reinterpret_cast<const f32x4*>(pp + 4);
+        const float pj[G] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          acc[j][0] += pj[j] * vv[i][0];
+          acc[j][1] += pj[j] * vv[i][1];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) vv[i][h] = kv_load4<KVT>(rv, off(tn + pg + 16 * i, h));
+  }
+
+  // ---- the 16 position groups' outputs: the 4 of a wave by DPP (row
+  // rotations by 8 and 4 stay on lanes with the same dim group), then the
+  // waves in order through LDS
+  __syncthreads();  // the adapter scratch is no longer read
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 v = acc[j][h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = v[e];
+        x += dpp_f<0x128>(x);  // row_ror:8
+        x += dpp_f<0x124>(x);  // row_ror:4
+        v[e] = x;
+      }
+      acc[j][h] = v;
+    }
+  }
+  if (((lane >> 2) & 3) == 0) {
+    float* dst = ored + (wave * 16 + dg) * 64;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) *reinterpret_cast<f32x4*>(dst + j * 8 + h * 4) = acc[j][h];
+  }
+  __syncthreads();
+  float* base = part + ((size_t)g * G * S + sp) * (D + 2);
+  {
+    const int j = tid >> 5, d0 = (tid & 31) * 4;  // head j, dims d0 .. d0 + 3
+    const int h = d0 >> 6, dgo = (d0 & 63) >> 2;
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o += *reinterpret_cast<const f32x4*>(ored + (w * 16 + dgo) * 64 + j * 8 + h * 4);
+    float* dst = base + (size_t)j * S * (D + 2) + 2 + d0;
+    dst[0] = o.x;
+    dst[1] = o.y;
+    dst[2] = o.z;
+    dst[3] = o.w;
+  }
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int j = wave + 4 * rr;
+    if (lane == 0) {
+      base[(size_t)j * S * (D + 2)] = M[rr];
+      base[(size_t)j * S * (D + 2) + 1] = L[rr];
     }
   }
 }
@@ -510,8 +794,12 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
   const dim3 grid(nkv, S);
   const LoraUp lu{lora_u, lora_bq, lora_bv, lora_r, lora_scale};
 #define QD_ATTN_DECODE_T(G_, L_, T_)                                                                                 \
-  hipLaunchKernelGGL((k_attn_decode<G_, L_, T_>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, (T_*)Kc,   \
-                     (T_*)Vc, max_pos, st, S, cmin, scale, part, lu)
+  if (G_ == 8)                                                                                                       \
+    hipLaunchKernelGGL((k_attn_decode8<L_, T_>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, (T_*)Kc,    \
+                       (T_*)Vc, max_pos, st, S, cmin, scale, part, lu);                                              \
+  else                                                                                                               \
+    hipLaunchKernelGGL((k_attn_decode<G_, L_, T_>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, (T_*)Kc, \
+                       (T_*)Vc, max_pos, st, S, cmin, scale, part, lu)
 #define QD_ATTN_DECODE(G_)                                     \
   if (kv_bf16) {                                               \
     if (lora_u) QD_ATTN_DECODE_T(G_, true, uint16_t);          \

@@ -11,7 +11,10 @@ kernel instantiation or launch branch that a full-size workload runs:
 * the 3B-width int4 model (hidden 2048, intermediate 11008, 16/2 heads), whose
   down projection runs the 8-pass int4 GEMV and whose decode step is the
   captured 3B-width graph, or the persistent step with int4 slots (also on
-  64 CUs, where the slots stream in during each phase).
+  64 CUs, where the slots stream in during each phase);
+* the graph path's decode attention for 8 q heads per kv head with several
+  64-position tiles per split (16 kv heads, ~2100 positions), f32 and bf16
+  cache, with an adapter whose rank is not a multiple of 8.
 
 Every logit of every step is compared with the oracle; tokens follow the
 greedy / sampled near-tie rules of gpu_util.
@@ -148,5 +151,42 @@ def test_int4_3b_width_decode(torch_cuda, path, monkeypatch):
         dec.set_lora(lora_to_device(lora), 16, 32.0)
     prompt = synth.make_prompt(shape.vocab, 8, seed=46)
     recs = lockstep_greedy(dec, oracle, prompt, 16, log=log)
+    assert_records(recs, max_forced=1)
+    dec.close()
+
+
+# 16 kv heads of 8 q heads each: the decode attention cuts each kv head's
+# positions into 256 / 16 = 16 splits, so near 2100 positions a split holds
+# 132 positions, two full 64-position tiles and a ragged one
+G8_WIDE = dataclasses.replace(synth.TINY, name="tiny-128q-16kv", n_q_heads=128, n_kv_heads=16, max_pos=2304)
+
+
+@pytest.mark.parametrize("kv,rank", [("f32", 0), ("bf16", 12)])
+def test_graph_attention_g8_several_tiles_per_split(torch_cuda, kv, rank):
+    """Tiny model with 8 q heads per kv head and 16 kv heads on the graph path:
+    past 2048 positions every split of the decode attention spans three
+    64-position tiles (the last one ragged), so the kernel's tile loop, its
+    next-tile requests and the new row's patch in a later tile all run.  With
+    the bf16 cache and a rank-12 adapter (rank not a multiple of 8: B rows are
+    not 16-byte aligned).  2100-token prompt (one batched prefill), then 10
+    decode steps, every logit checked."""
+    import decoder_only_token_amd as qd
+    from gpu_util import lora_to_device
+    shape = G8_WIDE
+    log(f"graph G=8 attention, several tiles per split, kv={kv}, rank={rank}")
+    w = synth.make_weights(shape, seed=48, random_gains=True)
+    lora = synth.make_lora(shape, rank, seed=49) if rank else None
+    oracle = OracleModel(shape, w, lora=lora, lora_alpha=24.0, kv_bf16=kv == "bf16")
+    cfg = qd.make_config(shape, max_prefill=2112, lora_rank_max=rank, decode_path=PATHS["graph"],
+                         kv_format=qd.QD_KV_BF16 if kv == "bf16" else qd.QD_KV_F32)
+    dec = qd.Decoder(cfg, torch_cuda.cuda.current_stream().cuda_stream)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    del dw
+    if lora:
+        dec.set_lora(lora_to_device(lora), rank, 24.0)
+    prompt = synth.make_prompt(shape.vocab, 2100, seed=50)
+    recs = lockstep_greedy(dec, oracle, prompt, 10, log=log)
     assert_records(recs, max_forced=1)
     dec.close()
