@@ -102,6 +102,77 @@ __device__ __forceinline__ void stage_input_q4(const float* __restrict__ x, int 
   __syncthreads();
 }
 
+// Single input row (decode): its pieces (and the norm gains) are requested
+// into registers before the weights, so the wait for them does not also wait
+// for the weights (loads complete in order); then h[perm(k)] = x[k]
+// (* g[k] / rms(x)) is written once.  Thread t holds columns 4 (t + 256 i) ..
+// + 3 for i < NI; reads past K come back as zeros (buffer record of K floats).
+template <int NI>
+struct RowIn {
+  f32x4 x[NI], g[NI];
+};
+
+// A buffer record over `bytes` bytes at `p` (the same in every lane; taken
+// from lane 0 so it lives in scalar registers).  Loads at offsets past it
+// read zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_record(const void* p, int bytes) {
+  const uint64_t v = (uint64_t)p;
+  const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f32_record(const float* p, int n) { return byte_record(p, n * 4); }
+constexpr int kPastRecord = 0x7FFFFFF0;  // an offset past every record here
+
+// 16 bytes of codes (32 columns) of row n from column k, and the fp16 scale
+// bits of its group; zeros when k >= K.  No branch, so the waits for earlier
+// loads keep their in-order counts.
+__device__ __forceinline__ void q4_piece(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int n, int k, int K,
+                                         u32x4& c, uint16_t& sc) {
+  const bool in = k < K;
+  int oc = in ? n * (K / 2) + k / 2 : kPastRecord, os = in ? (n * (K / 128) + k / 128) * 2 : kPastRecord;
+  // (an opaque register value: otherwise the select is turned into two loads
+  // under a branch)
+  asm volatile("" : "+v"(oc), "+v"(os));
+  c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 2 /* streamed */));
+  sc = __builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0);
+}
+
+template <int NI>
+__device__ __forceinline__ void row_in_load(RowIn<NI>& in, const float* x, const float* gain, int K) {
+  const __amdgpu_buffer_rsrc_t rx = f32_record(x, K);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    in.x[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (threadIdx.x + i * 256) * 16, 0, 0));
+  if (gain) {
+    const __amdgpu_buffer_rsrc_t rg = f32_record(gain, K);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      in.g[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (threadIdx.x + i * 256) * 16, 0, 0));
+  }
+}
+
+template <int NI>
+__device__ __forceinline__ void row_in_stage(const RowIn<NI>& in, bool gain, int K, float eps, float* h, float* red) {
+  float r = 1.f;
+  if (gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const f32x4 v = in.x[i];
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    r = 1.0f / sqrtf(block_sum_256(ss, red) / (float)K + eps);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int k = (threadIdx.x + i * 256) * 4;
+    if (k < K) *reinterpret_cast<f32x4*>(h + q4_perm(k)) = gain ? in.x[i] * r * in.g[i] : in.x[i];
+  }
+  __syncthreads();
+}
+
 // sum over one lane's 32 columns of code * x, with u = code + 8 in the nibbles:
 // sum u x - 8 sum x.  Dword m holds columns 8 m .. 8 m + 7; v[2 m], v[2 m + 1]
 // are their inputs.
@@ -160,8 +231,15 @@ __device__ __forceinline__ void gemv_extra_bf16(const XRows& xr, int K, const fl
       }
     }
   };
-  load(0);
-  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  if (TM == 1) {
+    RowIn<2 * NP> in;
+    row_in_load(in, x, gain, K);
+    load(0);
+    row_in_stage(in, gain != nullptr, K, eps, h, red);
+  } else {
+    load(0);
+    stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  }
   if (!live) return;
   float acc[TM];
 #pragma unroll
@@ -200,7 +278,9 @@ __device__ __forceinline__ void gemv_extra_bf16(const XRows& xr, int K, const fl
   }
 }
 
-template <int RPW, int TM, int NP>
+// XR: the launch has extra bf16 rows (a separate instantiation, so launches
+// without them do not carry that path's registers)
+template <int RPW, int TM, int NP, bool XR>
 __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4, const uint16_t* __restrict__ S4,
                                                  int N, int K, const float* __restrict__ x, int ldx, int T,
                                                  const float* __restrict__ gain, float eps,
@@ -209,7 +289,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
   extern __shared__ float smem[];
   float* red = smem;
   float* h = smem + 8;
-  if (xr.W && (int)blockIdx.x >= xr.blk0) {  // block-uniform
+  if (XR && (int)blockIdx.x >= xr.blk0) {  // block-uniform
     gemv_extra_bf16<TM, NP>(xr, K, x, ldx, T, gain, eps, h, red);
     return;
   }
@@ -217,23 +297,23 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
   const int groups = K / 128, ks = q4_stride(K), np = (K + 2047) / 2048;
   u32x4 c[NP][RPW];
-  float sc[NP][RPW];
+  uint16_t sc[NP][RPW];  // fp16 bits, widened where used (a conversion here would wait for the load)
+  const __amdgpu_buffer_rsrc_t rc = byte_record(C4, N * (K / 2)), rs = byte_record(S4, N * groups * 2);
   auto load = [&](int pb) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int k = (pb + p) * 2048 + lane * 32;
-      if (k < K) {
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-          const int n = min(n0 + i, N - 1);
-          c[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(C4 + (size_t)n * (K / 2) + k / 2));
-          sc[p][i] = f16_bits_to_f(S4[(size_t)n * groups + k / 128]);
-        }
-      }
-    }
+      for (int i = 0; i < RPW; ++i) q4_piece(rc, rs, min(n0 + i, N - 1), (pb + p) * 2048 + lane * 32, K, c[p][i], sc[p][i]);
   };
-  if (n0 < N) load(0);
-  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  if (TM == 1) {
+    RowIn<2 * NP> in;
+    row_in_load(in, x, gain, K);
+    load(0);  // (rows past N repeat row N - 1; their waves return after the staging)
+    row_in_stage(in, gain != nullptr, K, eps, h, red);
+  } else {
+    if (n0 < N) load(0);
+    stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  }
   if (n0 >= N) return;
   float acc[RPW][TM];
 #pragma unroll
@@ -252,10 +332,13 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
             float sx;
             load_x32(h + t * ks + (pb + p) * 2048 + lane * 4, v, sx);
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) acc[i][t] = fmaf(sc[p][i], dot32_q4(c[p][i], v, sx), acc[i][t]);
+            for (int i = 0; i < RPW; ++i) acc[i][t] = fmaf(f16_bits_to_f(sc[p][i]), dot32_q4(c[p][i], v, sx), acc[i][t]);
           }
         }
       }
+      // one pass's inputs in registers at a time (hoisting every pass's LDS
+      // reads would cost the occupancy)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
@@ -290,25 +373,28 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restric
   const int n0 = (blockIdx.x * 4 + wave) * RPW;
   const int groups = K / 128, ks = q4_stride(K), np = (K + 2047) / 2048;
   u32x4 cg[NP][RPW], cu[NP][RPW];
-  float sg[NP][RPW], su[NP][RPW];
+  uint16_t sg[NP][RPW], su[NP][RPW];  // fp16 bits, widened where used
+  const __amdgpu_buffer_rsrc_t rcg = byte_record(Cg, N * (K / 2)), rsg = byte_record(Sg, N * groups * 2);
+  const __amdgpu_buffer_rsrc_t rcu = byte_record(Cu, N * (K / 2)), rsu = byte_record(Su, N * groups * 2);
   auto load = [&](int pb) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int k = (pb + p) * 2048 + lane * 32;
-      if (k < K) {
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-          const int n = min(n0 + i, N - 1);
-          cg[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cg + (size_t)n * (K / 2) + k / 2));
-          cu[p][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Cu + (size_t)n * (K / 2) + k / 2));
-          sg[p][i] = f16_bits_to_f(Sg[(size_t)n * groups + k / 128]);
-          su[p][i] = f16_bits_to_f(Su[(size_t)n * groups + k / 128]);
-        }
+      for (int i = 0; i < RPW; ++i) {
+        const int n = min(n0 + i, N - 1), k = (pb + p) * 2048 + lane * 32;
+        q4_piece(rcg, rsg, n, k, K, cg[p][i], sg[p][i]);
+        q4_piece(rcu, rsu, n, k, K, cu[p][i], su[p][i]);
       }
-    }
   };
-  if (n0 < N) load(0);
-  stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  if (TM == 1) {
+    RowIn<2 * NP> in;
+    row_in_load(in, x, gain, K);
+    load(0);  // (rows past N repeat row N - 1; their waves return after the staging)
+    row_in_stage(in, gain != nullptr, K, eps, h, red);
+  } else {
+    if (n0 < N) load(0);
+    stage_input_q4(x, ldx, T, K, gain, eps, h, red);
+  }
   if (n0 >= N) return;
   float ag[RPW][TM], au[RPW][TM];
 #pragma unroll
@@ -328,8 +414,8 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restric
             load_x32(h + t * ks + (pb + p) * 2048 + lane * 4, v, sx);
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
-              ag[i][t] = fmaf(sg[p][i], dot32_q4(cg[p][i], v, sx), ag[i][t]);
-              au[i][t] = fmaf(su[p][i], dot32_q4(cu[p][i], v, sx), au[i][t]);
+              ag[i][t] = fmaf(f16_bits_to_f(sg[p][i]), dot32_q4(cg[p][i], v, sx), ag[i][t]);
+              au[i][t] = fmaf(f16_bits_to_f(su[p][i]), dot32_q4(cu[p][i], v, sx), au[i][t]);
             }
           }
         }
@@ -371,12 +457,17 @@ void gemv_q4_np(hipStream_t s, dim3 grid, size_t lds, const uint8_t* codes, cons
   XRows xr = xr0;
   xr.blk0 = (int)grid.x;
   const dim3 g2(grid.x + (xr.W ? (xr.N + 3) / 4 : 0));
-  if (T == 1)
-    hipLaunchKernelGGL((k_gemv_q4<RPW, 1, NP>), g2, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain, eps,
-                       bias, y, ldy, accumulate, xr);
-  else
-    hipLaunchKernelGGL((k_gemv_q4<RPW, GEMV_MAX_T, 1>), g2, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain,
-                       eps, bias, y, ldy, accumulate, xr);
+#define QD_GEMV_Q4(TM_, NP_, XR_)                                                                                   \
+  hipLaunchKernelGGL((k_gemv_q4<RPW, TM_, NP_, XR_>), g2, dim3(256), lds, s, codes, scales, N, K, x, ldx, T, gain, \
+                     eps, bias, y, ldy, accumulate, xr)
+  if (T == 1) {
+    if (xr.W) QD_GEMV_Q4(1, NP, true);
+    else QD_GEMV_Q4(1, NP, false);
+  } else {
+    if (xr.W) QD_GEMV_Q4(GEMV_MAX_T, 1, true);
+    else QD_GEMV_Q4(GEMV_MAX_T, 1, false);
+  }
+#undef QD_GEMV_Q4
 }
 
 template <int RPW>
