@@ -327,6 +327,56 @@ __device__ __forceinline__ f32x4 kv_load4(__amdgpu_buffer_rsrc_t r, int off) {
   }
 }
 
+// dot of 8 bf16 (one 16-byte piece of a B row) with 8 floats
+__device__ __forceinline__ float dot8_bf16(u32x4 w, f32x4 u0, f32x4 u1) {
+  float a = 0.f;
+  a = fmaf(bf16_lo(w.x), u0.x, a);
+  a = fmaf(bf16_hi(w.x), u0.y, a);
+  a = fmaf(bf16_lo(w.y), u0.z, a);
+  a = fmaf(bf16_hi(w.y), u0.w, a);
+  a = fmaf(bf16_lo(w.z), u1.x, a);
+  a = fmaf(bf16_hi(w.z), u1.y, a);
+  a = fmaf(bf16_lo(w.w), u1.z, a);
+  a = fmaf(bf16_hi(w.w), u1.w, a);
+  return a;
+}
+
+// One row of an adapter's up product, B[row] . u over r columns.  Rows of B
+// are r bf16 apart, so they are 16-byte aligned only when r is a multiple of
+// 8: then the first NPRE 8-column pieces come from registers loaded ahead and
+// the rest are read here in pieces; any other r is read value by value.
+template <int NPRE>
+__device__ __forceinline__ float lora_row(const u32x4* pre, const f32x4* upre, const uint16_t* brow, const float* u,
+                                          int r) {
+  float a = 0.f;
+  if ((r & 7) == 0) {
+#pragma unroll
+    for (int c = 0; c < NPRE; ++c)
+      if (8 * c < r) a += dot8_bf16(pre[c], upre[2 * c], upre[2 * c + 1]);
+    for (int k0 = 8 * NPRE; k0 < r; k0 += 8)
+      a += dot8_bf16(*reinterpret_cast<const u32x4*>(brow + k0), *reinterpret_cast<const f32x4*>(u + k0),
+                     *reinterpret_cast<const f32x4*>(u + k0 + 4));
+  } else {
+    for (int k = 0; k < r; ++k) a = fmaf(bf16_to_f(brow[k]), u[k], a);
+  }
+  return a;
+}
+
+// One head of the new row from registers (lane: dims lane and lane + 64):
+// optional RMSNorm over the head's D values (gain), then RoPE with the
+// half-split pairing (j, j + D/2); the results go to out[lane], out[lane + 64].
+__device__ __forceinline__ void norm_rope_regs(float a, float b, bool gain, float ga, float gb, float eps, float c,
+                                               float s, float* out) {
+  const int l = threadIdx.x & 63;
+  if (gain) {
+    const float r = 1.0f / sqrtf(wave_sum(a * a + b * b) / (float)D + eps);
+    a = a * r * ga;
+    b = b * r * gb;
+  }
+  out[l] = a * c - b * s;
+  out[l + 64] = b * c + a * s;
+}
+
 template <bool LORA, typename KVT>
 __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ qkv, const float* __restrict__ qn,
                                                       const float* __restrict__ kn, float eps,
@@ -347,36 +397,104 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
   __shared__ __align__(16) float pt[TP * G];  // probabilities [position][head]
   __shared__ __align__(16) float cs[G];       // per-head rescale of this tile
   __shared__ __align__(16) float kv_new[2 * D];
-  __shared__ __align__(16) float ored[4 * 16 * 64];  // the waves' partial outputs (first: adapter scratch)
+  __shared__ __align__(16) float ored[4 * 16 * 64];  // the waves' partial outputs
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float* grp = qkv + (size_t)g * (G + 2) * D;
-  const float* qsrc = grp;
-  const float* vsrc = grp + (G + 1) * D;
-  if (LORA) {  // q and v with the adapter, in the output scratch (free until the split's end)
-    float* raw = ored;             // [G D | D]
-    float* us = ored + (G + 1) * D;  // u_q | u_v
-    const int r = lu.r;
-    if (tid < 2 * r) us[tid] = lu.u[tid];
-    __syncthreads();
-    for (int row = tid; row < (G + 1) * D; row += 256) {
-      const bool isq = row < G * D;
-      const uint16_t* b = isq ? lu.bq + ((size_t)g * G * D + row) * r : lu.bv + ((size_t)g * D + row - G * D) * r;
-      const float* u = us + (isq ? 0 : r);
-      float a = 0.f;
-      for (int k = 0; k < r; ++k) a = fmaf(bf16_to_f(b[k]), u[k], a);
-      raw[row] = (isq ? grp[row] : grp[(G + 1) * D + row - G * D]) + lu.scale * a;
-    }
-    __syncthreads();
-    qsrc = raw;
-    vsrc = raw + G * D;
-  }
-  for (int j = wave; j < G; j += 4) norm_rope_head(qsrc + j * D, qn, eps, cos_t, sin_t, pos, qs + j * D);
   const bool owns_new = p_end == ctx;
-  if (owns_new && wave == 3) {
-    norm_rope_head(grp + G * D, kn, eps, cos_t, sin_t, pos, kv_new);
+  const bool kvw = owns_new && wave == 3;  // wave 3 finishes the new row's k and v
+
+  // ---- 1. everything the q side reads (lane: dims lane and lane + 64 of q
+  // heads wave and wave + 4; wave 3 also of the new k and v), requested
+  // before the K/V rows so that waiting for it never waits for them
+  float qa[2], qb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave + 4 * i;
+    qa[i] = grp[j * D + lane];
+    qb[i] = grp[j * D + lane + 64];
+  }
+  float ka = 0.f, kb = 0.f, va = 0.f, vb = 0.f;
+  if (kvw) {
+    ka = grp[G * D + lane];
+    kb = grp[G * D + lane + 64];
+    va = grp[(G + 1) * D + lane];
+    vb = grp[(G + 1) * D + lane + 64];
+  }
+  const float cth = cos_t[(size_t)pos * (D / 2) + lane], sth = sin_t[(size_t)pos * (D / 2) + lane];
+  const float gq0 = qn ? qn[lane] : 1.f, gq1 = qn ? qn[lane + 64] : 1.f;
+  const float gk0 = kn ? kn[lane] : 1.f, gk1 = kn ? kn[lane + 64] : 1.f;
+  // adapter (q += s B_q u_q, v += s B_v u_v, "EMBERGLASS (qwen-webgpu-lora)
+  // README", LoRA sections): with r a multiple of 8, the first 16 columns of
+  // this lane's B rows and of u, ahead
+  constexpr int NPRE = LORA ? 2 : 1;
+  u32x4 bqa[2][NPRE], bqb[2][NPRE], bva[NPRE], bvb[NPRE];
+  f32x4 uq[2 * NPRE], uv[2 * NPRE];
+  const int r = lu.r;
+  const bool r8 = (r & 7) == 0;
+  if (LORA && r8) {
+#pragma unroll
+    for (int c = 0; c < NPRE; ++c) {
+      if (8 * c < r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const size_t row = (size_t)(g * G + wave + 4 * i) * D + lane;
+          bqa[i][c] = *reinterpret_cast<const u32x4*>(lu.bq + row * r + 8 * c);
+          bqb[i][c] = *reinterpret_cast<const u32x4*>(lu.bq + (row + 64) * r + 8 * c);
+        }
+        if (kvw) {
+          bva[c] = *reinterpret_cast<const u32x4*>(lu.bv + ((size_t)g * D + lane) * r + 8 * c);
+          bvb[c] = *reinterpret_cast<const u32x4*>(lu.bv + ((size_t)g * D + lane + 64) * r + 8 * c);
+        }
+        uq[2 * c] = *reinterpret_cast<const f32x4*>(lu.u + 8 * c);
+        uq[2 * c + 1] = *reinterpret_cast<const f32x4*>(lu.u + 8 * c + 4);
+        uv[2 * c] = *reinterpret_cast<const f32x4*>(lu.u + r + 8 * c);
+        uv[2 * c + 1] = *reinterpret_cast<const f32x4*>(lu.u + r + 8 * c + 4);
+      }
+    }
+  }
+
+  // ---- 2. the split's first tile of K and V rows
+  const int dg = (lane & 3) | ((lane >> 4) << 2);
+  const int pg = wave * 4 + ((lane >> 2) & 3);
+  const int kv_bytes = (p_end - p_begin) * D * (int)sizeof(KVT);
+  const __amdgpu_buffer_rsrc_t rk = kv_record(Kc + ((size_t)g * max_pos + p_begin) * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = kv_record(Vc + ((size_t)g * max_pos + p_begin) * D, kv_bytes);
+  const int esz = (int)sizeof(KVT);
+  // byte offset of (tile-relative row rr, half h) in the split's record
+  auto off = [&](int rr, int h) { return (rr * D + 64 * h + 4 * dg) * esz; };
+  f32x4 kk[4][2], vv[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kk[i][h] = kv_load4<KVT>(rk, off(pg + 16 * i, h));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vv[i][h] = kv_load4<KVT>(rv, off(pg + 16 * i, h));
+
+  // ---- 3. q heads (adapter, QK-norm, RoPE) into LDS; the new k and v
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave + 4 * i;
+    float a = qa[i], b = qb[i];
+    if (LORA) {
+      const uint16_t* b0 = lu.bq + ((size_t)(g * G + j) * D + lane) * r;
+      a += lu.scale * lora_row<NPRE>(bqa[i], uq, b0, lu.u, r);
+      b += lu.scale * lora_row<NPRE>(bqb[i], uq, b0 + 64 * (size_t)r, lu.u, r);
+    }
+    norm_rope_regs(a, b, qn != nullptr, gq0, gq1, eps, cth, sth, qs + j * D);
+  }
+  if (kvw) {
+    if (LORA) {
+      const uint16_t* b0 = lu.bv + ((size_t)g * D + lane) * r;
+      va += lu.scale * lora_row<NPRE>(bva, uv, b0, lu.u + r, r);
+      vb += lu.scale * lora_row<NPRE>(bvb, uv, b0 + 64 * (size_t)r, lu.u + r, r);
+    }
+    norm_rope_regs(ka, kb, kn != nullptr, gk0, gk1, eps, cth, sth, kv_new);
+    // the new row as the cache stores it (bf16 cache: rounded), for this step too
     const float k0 = kv_round<KVT>(kv_new[lane]), k1 = kv_round<KVT>(kv_new[lane + 64]);
-    const float v0 = kv_round<KVT>(vsrc[lane]), v1 = kv_round<KVT>(vsrc[64 + lane]);
+    const float v0 = kv_round<KVT>(va), v1 = kv_round<KVT>(vb);
     kv_new[lane] = k0;
     kv_new[lane + 64] = k1;
     kv_new[D + lane] = v0;
@@ -389,27 +507,9 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
     st_kv(vr + lane + 64, v1);
   }
 
-  const int dg = (lane & 3) | ((lane >> 4) << 2);
-  const int pg = wave * 4 + ((lane >> 2) & 3);
   const bool b0 = lane & 1, b1 = lane & 2;
   const int isel = (lane >> 4) & 3;  // which of the lane's 4 positions its two final scores belong to
   const int jsel = 4 * (int)b1 + 2 * (int)b0;  // and their heads: jsel, jsel + 1
-  const int kv_bytes = (p_end - p_begin) * D * (int)sizeof(KVT);
-  const __amdgpu_buffer_rsrc_t rk = kv_record(Kc + ((size_t)g * max_pos + p_begin) * D, kv_bytes);
-  const __amdgpu_buffer_rsrc_t rv = kv_record(Vc + ((size_t)g * max_pos + p_begin) * D, kv_bytes);
-  const int esz = (int)sizeof(KVT);
-  // byte offset of (tile-relative row r, half h) in the split's record
-  auto off = [&](int r, int h) { return (r * D + 64 * h + 4 * dg) * esz; };
-  f32x4 kk[4][2], vv[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) kk[i][h] = kv_load4<KVT>(rk, off(pg + 16 * i, h));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) vv[i][h] = kv_load4<KVT>(rv, off(pg + 16 * i, h));
-
   __syncthreads();  // q and the new row staged
   f32x4 qq[G][2];
 #pragma unroll
