@@ -15,10 +15,11 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-from .quant import quantize_int4_g128, dequantize_int4_g128
+from .quant import quantize_int4_g128, dequantize_int4_g128, quantize_q8_0, dequantize_q8_0
 
 _PROJ = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 _W_INT4_G128 = 1
+_W_Q8_0 = 2
 
 
 def widen_bf16(bits) -> np.ndarray:
@@ -159,6 +160,9 @@ class OracleModel:
                 if shape.weight_format == _W_INT4_G128 and name in _PROJ:
                     codes, scales = quantize_int4_g128(widen_bf16_f32(bits))
                     layer[name] = dequantize_int4_g128(codes, scales)
+                elif shape.weight_format == _W_Q8_0 and name in _PROJ:
+                    codes, scales = quantize_q8_0(widen_bf16_f32(bits))
+                    layer[name] = dequantize_q8_0(codes, scales)
                 else:
                     layer[name] = widen_bf16(bits)
             self.layers.append(layer)

@@ -26,6 +26,7 @@ SEED_LORA = 3
 
 W_BF16 = 0
 W_INT4_G128 = 1
+W_Q8_0 = 2  # int8 blocks of 32 with an fp16 scale
 
 
 @dataclasses.dataclass(frozen=True)
@@ -73,6 +74,13 @@ TINY_INT4 = ModelShape("tiny-int4g128", 2, 1024, 16, 2, 128, 1408, 4096, qk_norm
 TINY_INT4_WIDE = ModelShape("tiny-int4g128-wide", 2, 2048, 16, 2, 128, 2432, 4096, qk_norm=False, qkv_bias=True,
                             weight_format=W_INT4_G128, max_pos=256)
 
+# Q8_0 models: the 0.6B shape and a tiny one whose widths end partway into a
+# 1024-column pass (1408) or run one pass and a ragged rest (2432)
+QWEN3_06B_Q8 = dataclasses.replace(QWEN3_06B, name="qwen3-0.6b-q8_0", weight_format=W_Q8_0)
+TINY_Q8 = ModelShape("tiny-q8_0", 2, 1024, 16, 8, 128, 1408, 4096, weight_format=W_Q8_0, max_pos=256)
+TINY_Q8_WIDE = ModelShape("tiny-q8_0-wide", 2, 2048, 16, 2, 128, 2432, 4096, qk_norm=False, qkv_bias=True,
+                          weight_format=W_Q8_0, max_pos=256)
+
 WORKLOADS: Dict[str, Workload] = {
     # 8-token prompt, 16 greedy decode steps
     "tiny": Workload("tiny", TINY, 8, 16, 64),
@@ -84,6 +92,8 @@ WORKLOADS: Dict[str, Workload] = {
                                 temperature=0.7, top_k=40, top_p=0.9),
     # 256-token prompt, decode to context 4096
     "qwen2.5-3b-int4": Workload("qwen2.5-3b-int4", QWEN25_3B_INT4, 256, 4096 - 256, 512),
+    # the 0.6B model with Q8_0 projection weights: 5-token prompt, 128 greedy steps
+    "qwen3-0.6b-q8_0": Workload("qwen3-0.6b-q8_0", QWEN3_06B_Q8, 5, 128, 512),
     # 8192-token prefill with rank-16 LoRA on q/v, decode to context 16384
     "qwen2.5-3b-int4-lora": Workload("qwen2.5-3b-int4-lora", QWEN25_3B_INT4_16K, 8192, 16384 - 8192, 8192,
                                      lora_rank=16, lora_alpha=32.0),
@@ -209,7 +219,8 @@ def weight_bytes(shape: ModelShape, lora_rank: int = 0) -> Dict[str, int]:
     """Algorithmic bytes one decode step reads from the weights, by kind.
 
     bf16 matrices: 2 bytes per element.  int4 group-128: half a byte per code plus
-    a 2-byte fp16 scale per 128 codes.  Norm gains and biases are bf16.  The tied
+    a 2-byte fp16 scale per 128 codes.  Q8_0: one byte per code plus a 2-byte
+    fp16 scale per 32 codes.  Norm gains and biases are bf16.  The tied
     embedding table is bf16 and read once for the LM head (plus one row gathered).
     """
     H, d, I, L = shape.hidden, shape.head_dim, shape.intermediate, shape.n_layers
@@ -217,6 +228,8 @@ def weight_bytes(shape: ModelShape, lora_rank: int = 0) -> Dict[str, int]:
     lin = (nq * d + 2 * nkv * d) * H + H * nq * d + 2 * I * H + H * I
     if shape.weight_format == W_BF16:
         mat = 2 * lin
+    elif shape.weight_format == W_Q8_0:
+        mat = lin + 2 * (lin // 32)
     else:
         mat = lin // 2 + 2 * (lin // 128)
     small = 2 * (2 * H) + (2 * 2 * d if shape.qk_norm else 0) + (2 * (nq * d + 2 * nkv * d) if shape.qkv_bias else 0)

@@ -16,6 +16,7 @@ import pytest
 import synth
 from oracle import (OracleModel, rmsnorm, rope_rotate, causal_gqa_attention, silu, swiglu_mlp,
                     argmax_lowest, quantize_int4_g128, dequantize_int4_g128, splitmix64_output,
+                    quantize_q8_0, dequantize_q8_0,
                     uniform_for_step, sample_top_k_top_p)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -525,6 +526,61 @@ def test_int4_properties():
     # idempotent: quantising the dequantised weights returns the same codes and scales
     c2, s2 = quantize_int4_g128(what.astype(np.float32))
     assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+
+
+# ---------------------------------------------------------------- Q8_0 (int8 blocks of 32)
+
+def test_q8_0_worked_example():
+    g = golden("q8_0_worked.json")
+    w = np.zeros((2, 64), dtype=np.float32)
+    w[0, :len(g["values"])] = np.array(g["values"], dtype=np.float32)
+    w[0, 32:] = np.float32(0.5)  # a second block of the row: its own scale
+    codes, scales = quantize_q8_0(w)
+    assert float(scales[0, 0]) == g["scale"]
+    assert scales[0, 0].view(np.uint16) == 0x211F
+    assert list(codes[0, :len(g["codes"])]) == g["codes"]
+    assert np.all(codes[0, len(g["codes"]):32] == 0)
+    assert np.all(codes[0, 32:] == 127)  # the block's largest magnitude -> 127
+    assert float(scales[1, 0]) == 0.0 and np.all(codes[1] == 0)
+
+
+def test_q8_0_properties():
+    rng = np.random.default_rng(29)
+    w = synth.bf16_to_f32(synth.bf16_round(rng.standard_normal((48, 256)).astype(np.float32) * 0.02))
+    w[3, 64:96] = 0.0  # an all-zero block
+    codes, scales = quantize_q8_0(w)
+    assert codes.dtype == np.int8 and codes.min() >= -127 and codes.max() <= 127
+    assert scales.shape == (48, 8)
+    s = np.repeat(scales.astype(np.float32), 32, axis=1)
+    what = dequantize_q8_0(codes, scales)
+    # error within half a step (plus the float32 rounding of the division)
+    assert np.all(np.abs(w - what) <= s * (0.5 + 1e-3))
+    # the largest magnitude of every non-zero block maps to +-127
+    blk = np.abs(codes.reshape(48, 8, 32)).max(axis=2)
+    nz = scales.astype(np.float32) > 0
+    assert np.all(blk[nz] == 127) and np.all(blk[~nz] == 0) and not nz[3, 2]
+    # idempotent: quantising the dequantised weights returns the same codes and scales
+    c2, s2 = quantize_q8_0(what.astype(np.float32))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
+    # blocks are independent: changing one block leaves the others' codes alone
+    w2 = w.copy()
+    w2[5, 0:32] *= 3.0
+    c3, s3 = quantize_q8_0(w2)
+    assert np.array_equal(c3[:, 32:], codes[:, 32:]) and np.array_equal(c3[:5], codes[:5])
+
+
+def test_q8_0_model_uses_dequantised_projections():
+    shape = tiny_shape(qk_norm=True, qkv_bias=False, hidden=128, intermediate=256, head_dim=32,
+                       weight_format=synth.W_Q8_0)
+    w = synth.make_weights(shape, seed=26)
+    m = _model(shape, w)
+    f32 = lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)  # noqa: E731
+    for name in ("wq", "wo", "w_down"):
+        codes, scales = quantize_q8_0(f32(w["layers"][0][name]))
+        np.testing.assert_array_equal(m.layers[0][name], codes.astype(np.float64) *
+                                      np.repeat(scales.astype(np.float64), 32, axis=1))
+    # norms and the embedding stay bf16
+    np.testing.assert_array_equal(m.layers[0]["attn_norm"], f32(w["layers"][0]["attn_norm"]).astype(np.float64))
 
 
 @pytest.mark.parametrize("shape_name,lora", [("TINY", False), ("TINY_INT4", True)])
