@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqd.so")
 
 QD_ABI_VERSION = 2
-QD_W_BF16, QD_W_INT4_G128 = 0, 1
+QD_W_BF16, QD_W_INT4_G128, QD_W_Q8_0 = 0, 1, 2
 QD_DECODE_PERSISTENT, QD_DECODE_GRAPH = 0, 1
 QD_KV_F32, QD_KV_BF16 = 0, 1
 QD_CAP_EMBED, QD_CAP_LAYER_OUT, QD_CAP_FINAL_NORM, QD_CAP_LOGITS = 0, 1, 2, 3
@@ -126,8 +126,12 @@ class QdError(RuntimeError):
 
 
 def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Optional[int] = None,
-                decode_path: int = QD_DECODE_PERSISTENT, kv_format: int = QD_KV_F32) -> QdConfig:
-    """Fill a QdConfig from any object with the model-shape attribute names."""
+                decode_path: Optional[int] = None, kv_format: int = QD_KV_F32) -> QdConfig:
+    """Fill a QdConfig from any object with the model-shape attribute names.
+    decode_path None: the persistent step, or the graph for Q8_0 weights (the
+    only path they run on)."""
+    if decode_path is None:
+        decode_path = QD_DECODE_GRAPH if int(shape.weight_format) == QD_W_Q8_0 else QD_DECODE_PERSISTENT
     c = QdConfig()
     c.struct_size = ctypes.sizeof(QdConfig)
     c.abi_version = QD_ABI_VERSION
@@ -294,12 +298,14 @@ class Decoder:
         return out[:written.value].reshape(ncu.value, -1)
 
     def get_quantized(self, layer: int, name: str, shape):
-        """int4 encoding of projection `name` ("wq", ..., "w_down") of `layer`:
-        (codes int8 [N, K], scales float16 [N, K / 128])."""
+        """int4 / Q8_0 encoding of projection `name` ("wq", ..., "w_down") of
+        `layer`: (codes int8 [N, K], scales float16 [N, K / B]), B = 128 (int4)
+        or 32 (Q8_0)."""
         import numpy as np
         n, k = shape
+        b = 32 if self.cfg.weight_format == QD_W_Q8_0 else 128
         codes = np.empty((n, k), dtype=np.int8)
-        scales = np.empty((n, k // 128), dtype=np.uint16)
+        scales = np.empty((n, k // b), dtype=np.uint16)
         self._check(self.lib.qd_get_quantized(self.h, layer, QD_PROJ[name],
                                               codes.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), codes.size,
                                               scales.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)), scales.size))

@@ -41,6 +41,9 @@ struct Layer {
   // of the same five matrices (the bf16 pointers above stay null)
   uint8_t *cqkv = nullptr, *co = nullptr, *cg = nullptr, *cu = nullptr, *cd = nullptr;
   uint16_t *sqkv = nullptr, *so = nullptr, *sg = nullptr, *su = nullptr, *sd = nullptr;
+  // Q8_0 format: int8 codes [rows][in] of the five matrices; their fp16 scales
+  // [rows][in / 32] use the s* pointers above
+  int8_t *qqkv = nullptr, *qo = nullptr, *qg = nullptr, *qu = nullptr, *qd = nullptr;
 };
 
 // Adapter of one layer: stacked down matrices [A_q; A_v] [2 r, H] and the up
@@ -194,7 +197,14 @@ int validate_config(const qd_config* c, std::string& why) {
   }
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) { why = "rope_theta must be > 0 and rms_eps >= 0"; return QD_E_ARG; }
   if (c->tie_embeddings != 1) { why = "only tied embeddings are supported (tie_embeddings must be 1)"; return QD_E_ARG; }
-  if (c->weight_format != QD_W_BF16 && c->weight_format != QD_W_INT4_G128) { why = "unknown weight_format"; return QD_E_ARG; }
+  if (c->weight_format != QD_W_BF16 && c->weight_format != QD_W_INT4_G128 && c->weight_format != QD_W_Q8_0) {
+    why = "unknown weight_format";
+    return QD_E_ARG;
+  }
+  if (c->weight_format == QD_W_Q8_0 && c->decode_path != QD_DECODE_GRAPH) {
+    why = "Q8_0 weights need decode_path QD_DECODE_GRAPH";
+    return QD_E_ARG;
+  }
   if (c->max_pos < 1 || c->max_pos > (1 << 20)) { why = "max_pos out of range"; return QD_E_ARG; }
   if (c->max_prefill < 1 || c->max_prefill > c->max_pos) { why = "max_prefill must be in [1, max_pos]"; return QD_E_ARG; }
   if (c->lora_rank_max < 0 || c->lora_rank_max > 64) { why = "lora_rank_max must be in [0, 64]"; return QD_E_ARG; }
@@ -290,7 +300,7 @@ void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
   const int H = c.hidden;
   launch_embed(s, h->embed, tok, T, H, h->x);
   if (capture) (void)hipMemcpyAsync(h->cap, h->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice, s);
-  if (T >= kGemmMinRows) {
+  if (T >= kGemmMinRows && c.weight_format != QD_W_Q8_0) {  // (Q8_0: the GEMVs on row tiles)
     enqueue_layers_gemm(h, T, capture);
   } else {
     enqueue_layers_gemv(h, T, capture);
@@ -388,8 +398,8 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
   hipStream_t s = h->stream;
   const int H = c.hidden, d = c.head_dim, nq = c.n_q_heads, I = c.intermediate;
   const int NQKV = qkv_rows(c);
-  const bool q4 = c.weight_format == QD_W_INT4_G128;
-  auto tile = [&](int K) { return q4 ? q4_gemv_t_tile(K) : gemv_t_tile(K); };
+  const bool q4 = c.weight_format == QD_W_INT4_G128, q8 = c.weight_format == QD_W_Q8_0;
+  auto tile = [&](int K) { return q4 ? q4_gemv_t_tile(K) : q8 ? q8_gemv_t_tile(K) : gemv_t_tile(K); };
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = h->layers[l];
     for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
@@ -398,6 +408,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
         launch_gemv_q4(s, L.cqkv, L.sqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
                        h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu, h->lora_rank ? h->lora[l].a : nullptr,
                        2 * h->lora_rank, h->lu + (size_t)t0 * 2 * h->lora_rank, 2 * h->lora_rank);
+      else if (q8)
+        launch_gemv_q8(s, L.qqkv, L.sqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
+                       h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
       else
         launch_gemv_bf16(s, L.wqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
                          h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
@@ -419,6 +432,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
       if (q4)
         launch_gemv_q4(s, L.co, L.so, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
                        h->x + (size_t)t0 * H, H, 1, h->ncu);
+      else if (q8)
+        launch_gemv_q8(s, L.qo, L.so, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
+                       h->x + (size_t)t0 * H, H, 1, h->ncu);
       else
         launch_gemv_bf16(s, L.wo, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
                          h->x + (size_t)t0 * H, H, 1, h->ncu);
@@ -428,6 +444,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
       if (q4)
         launch_gemv_gateup_q4(s, L.cg, L.sg, L.cu, L.su, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
                               h->act + (size_t)t0 * I, I, h->ncu);
+      else if (q8)
+        launch_gemv_gateup_q8(s, L.qg, L.sg, L.qu, L.su, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
+                              h->act + (size_t)t0 * I, I, h->ncu);
       else
         launch_gemv_gateup_bf16(s, L.wg, L.wu, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
                                 h->act + (size_t)t0 * I, I, h->ncu);
@@ -436,6 +455,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
       const int tn = std::min(tt, T - t0);
       if (q4)
         launch_gemv_q4(s, L.cd, L.sd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
+                       h->x + (size_t)t0 * H, H, 1, h->ncu);
+      else if (q8)
+        launch_gemv_q8(s, L.qd, L.sd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
                        h->x + (size_t)t0 * H, H, 1, h->ncu);
       else
         launch_gemv_bf16(s, L.wd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
@@ -645,7 +667,7 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
   auto widen = [&](const void* src, float* dst, size_t n) {
     hipLaunchKernelGGL(k_widen_bf16, dim3((n + 255) / 256), dim3(256), 0, s, (const uint16_t*)src, dst, n);
   };
-  const bool q4 = c.weight_format == QD_W_INT4_G128;
+  const bool q4 = c.weight_format == QD_W_INT4_G128, q8 = c.weight_format == QD_W_Q8_0;
   if (!h->weights) {  // first load: allocate engine-owned weight buffers
     if ((rc = dev_alloc(h, &h->embed, (size_t)c.vocab * H)) || (rc = dev_alloc(h, &h->final_norm, H))) return rc;
     for (auto& L : h->layers) {
@@ -658,6 +680,14 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
           return rc;
         L.cu = L.cg + I * H / 2;  // up rows follow the gate rows (codes and scales)
         L.su = L.sg + I * H / 128;
+      } else if (q8) {
+        if ((rc = dev_alloc(h, &L.qqkv, NQKV * H)) || (rc = dev_alloc(h, &L.sqkv, NQKV * H / 32)) ||
+            (rc = dev_alloc(h, &L.qo, H * nq * d)) || (rc = dev_alloc(h, &L.so, H * nq * d / 32)) ||
+            (rc = dev_alloc(h, &L.qg, 2 * I * H)) || (rc = dev_alloc(h, &L.sg, 2 * I * H / 32)) ||
+            (rc = dev_alloc(h, &L.qd, H * I)) || (rc = dev_alloc(h, &L.sd, H * I / 32)))
+          return rc;
+        L.qu = L.qg + I * H;  // up rows follow the gate rows (codes and scales)
+        L.su = L.sg + I * H / 32;
       } else if ((rc = dev_alloc(h, &L.wqkv, NQKV * H)) || (rc = dev_alloc(h, &L.wo, H * nq * d)) ||
                  (rc = dev_alloc(h, &L.wg, 2 * I * H)) || (rc = dev_alloc(h, &L.wd, H * I))) {
         return rc;
@@ -689,9 +719,25 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
       quant(w->w_gate[l], 0, I, H, L.cg, L.sg, 0);
       quant(w->w_up[l], 0, I, H, L.cu, L.su, 0);
       quant(w->w_down[l], 0, H, I, L.cd, L.sd, 0);
+    } else if (q8) {
+      auto quant = [&](const void* src, size_t row0, size_t nrows, size_t K, int8_t* codes, uint16_t* scales,
+                       size_t dst_row) {
+        launch_quantize_q8(s, (const uint16_t*)src + row0 * K, (int)nrows, (int)K, codes + dst_row * K,
+                           scales + dst_row * (K / 32));
+      };
+      for (size_t g = 0; g < nkv; ++g) {
+        const size_t r = g * (G + 2) * d;
+        quant(w->wq[l], g * G * d, G * d, H, L.qqkv, L.sqkv, r);
+        quant(w->wk[l], g * d, d, H, L.qqkv, L.sqkv, r + G * d);
+        quant(w->wv[l], g * d, d, H, L.qqkv, L.sqkv, r + (G + 1) * d);
+      }
+      quant(w->wo[l], 0, H, nq * d, L.qo, L.so, 0);
+      quant(w->w_gate[l], 0, I, H, L.qg, L.sg, 0);
+      quant(w->w_up[l], 0, I, H, L.qu, L.su, 0);
+      quant(w->w_down[l], 0, H, I, L.qd, L.sd, 0);
     }
     // fused q|k|v rows, group-major: [kv head g][q heads g*G .. g*G+G-1 | k_g | v_g] x d rows
-    for (size_t g = 0; !q4 && g < nkv; ++g) {
+    for (size_t g = 0; !q4 && !q8 && g < nkv; ++g) {
       uint16_t* dst = L.wqkv + g * (G + 2) * d * H;
       HIP_TRY(h, hipMemcpyAsync(dst, (const uint16_t*)w->wq[l] + g * G * d * H, G * d * H * 2,
                                 hipMemcpyDeviceToDevice, s));
@@ -700,7 +746,7 @@ int qd_load_weights(qd_handle* h, const qd_weights* w) {
       HIP_TRY(h, hipMemcpyAsync(dst + (G + 1) * d * H, (const uint16_t*)w->wv[l] + g * d * H, d * H * 2,
                                 hipMemcpyDeviceToDevice, s));
     }
-    if (!q4) {
+    if (!q4 && !q8) {
       HIP_TRY(h, hipMemcpyAsync(L.wo, w->wo[l], H * nq * d * 2, hipMemcpyDeviceToDevice, s));
       HIP_TRY(h, hipMemcpyAsync(L.wg, w->w_gate[l], I * H * 2, hipMemcpyDeviceToDevice, s));
       HIP_TRY(h, hipMemcpyAsync(L.wu, w->w_up[l], I * H * 2, hipMemcpyDeviceToDevice, s));
@@ -1028,42 +1074,49 @@ int qd_get_quantized(qd_handle* h, int32_t layer, int32_t which, int8_t* codes_h
                      uint16_t* scales_host, size_t scales_capacity) {
   if (!h) return QD_E_ARG;
   const qd_config& c = h->cfg;
-  if (c.weight_format != QD_W_INT4_G128) return h->set_err(QD_E_STATE, "the handle does not hold int4 weights");
+  const bool q4 = c.weight_format == QD_W_INT4_G128;
+  if (!q4 && c.weight_format != QD_W_Q8_0) return h->set_err(QD_E_STATE, "the handle does not hold quantised weights");
   if (!h->weights) return h->set_err(QD_E_STATE, "weights not loaded");
   if (!codes_host || !scales_host) return h->set_err(QD_E_ARG, "output pointer is NULL");
   if (layer < 0 || layer >= c.n_layers) return h->set_err(QD_E_ARG, "layer out of range");
   const size_t H = c.hidden, d = c.head_dim, I = c.intermediate, nq = c.n_q_heads, nkv = c.n_kv_heads;
-  const size_t G = nq / nkv;
+  const size_t G = nq / nkv, gs = q4 ? 128 : 32;  // columns per scale
   const Layer& L = h->layers[layer];
   // (source matrix, its rows, K) and, for q/k/v, where each kv group's rows sit in the fused matrix
   const uint8_t* cs = nullptr;
   const uint16_t* ss = nullptr;
   size_t N = 0, K = 0, src_rows = 0, per_group = 0, group_off = 0;
+  auto codes_of = [&](const uint8_t* c4, const int8_t* c8) { return q4 ? c4 : reinterpret_cast<const uint8_t*>(c8); };
   switch (which) {
-    case QD_PROJ_Q: cs = L.cqkv; ss = L.sqkv; N = nq * d; K = H; per_group = G * d; group_off = 0; break;
-    case QD_PROJ_K: cs = L.cqkv; ss = L.sqkv; N = nkv * d; K = H; per_group = d; group_off = G * d; break;
-    case QD_PROJ_V: cs = L.cqkv; ss = L.sqkv; N = nkv * d; K = H; per_group = d; group_off = (G + 1) * d; break;
-    case QD_PROJ_O: cs = L.co; ss = L.so; N = H; K = nq * d; break;
-    case QD_PROJ_GATE: cs = L.cg; ss = L.sg; N = I; K = H; break;
-    case QD_PROJ_UP: cs = L.cu; ss = L.su; N = I; K = H; break;
-    case QD_PROJ_DOWN: cs = L.cd; ss = L.sd; N = H; K = I; break;
+    case QD_PROJ_Q: cs = codes_of(L.cqkv, L.qqkv); ss = L.sqkv; N = nq * d; K = H; per_group = G * d; group_off = 0; break;
+    case QD_PROJ_K: cs = codes_of(L.cqkv, L.qqkv); ss = L.sqkv; N = nkv * d; K = H; per_group = d; group_off = G * d; break;
+    case QD_PROJ_V: cs = codes_of(L.cqkv, L.qqkv); ss = L.sqkv; N = nkv * d; K = H; per_group = d; group_off = (G + 1) * d; break;
+    case QD_PROJ_O: cs = codes_of(L.co, L.qo); ss = L.so; N = H; K = nq * d; break;
+    case QD_PROJ_GATE: cs = codes_of(L.cg, L.qg); ss = L.sg; N = I; K = H; break;
+    case QD_PROJ_UP: cs = codes_of(L.cu, L.qu); ss = L.su; N = I; K = H; break;
+    case QD_PROJ_DOWN: cs = codes_of(L.cd, L.qd); ss = L.sd; N = H; K = I; break;
     default: return h->set_err(QD_E_ARG, "unknown projection");
   }
-  if (codes_capacity < N * K || scales_capacity < N * (K / 128))
+  if (codes_capacity < N * K || scales_capacity < N * (K / gs))
     return h->set_err(QD_E_ARG, "capacity smaller than the matrix");
   src_rows = per_group ? (size_t)qkv_rows(c) : N;
-  std::vector<uint8_t> codes(src_rows * K / 2);
-  std::vector<uint16_t> scales(src_rows * K / 128);
+  const size_t row_bytes = q4 ? K / 2 : K;
+  std::vector<uint8_t> codes(src_rows * row_bytes);
+  std::vector<uint16_t> scales(src_rows * K / gs);
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   HIP_TRY(h, hipMemcpy(codes.data(), cs, codes.size(), hipMemcpyDeviceToHost));
   HIP_TRY(h, hipMemcpy(scales.data(), ss, scales.size() * 2, hipMemcpyDeviceToHost));
   for (size_t n = 0; n < N; ++n) {
     const size_t r = per_group ? (n / per_group) * (G + 2) * d + group_off + n % per_group : n;
     for (size_t k = 0; k < K; ++k) {
-      const uint8_t b = codes[r * (K / 2) + k / 2];
-      codes_host[n * K + k] = (int8_t)((k & 1 ? b >> 4 : b & 15) - 8);
+      if (q4) {
+        const uint8_t b = codes[r * row_bytes + k / 2];
+        codes_host[n * K + k] = (int8_t)((k & 1 ? b >> 4 : b & 15) - 8);
+      } else {
+        codes_host[n * K + k] = (int8_t)codes[r * row_bytes + k];
+      }
     }
-    for (size_t g = 0; g < K / 128; ++g) scales_host[n * (K / 128) + g] = scales[r * (K / 128) + g];
+    for (size_t g = 0; g < K / gs; ++g) scales_host[n * (K / gs) + g] = scales[r * (K / gs) + g];
   }
   return QD_OK;
 }

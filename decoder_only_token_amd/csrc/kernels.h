@@ -87,6 +87,18 @@ void launch_gemv_gateup_q4(hipStream_t s, const uint8_t* cg, const uint16_t* sg,
                            int N, int K, const float* x, int ldx, int T, const float* gain, float eps, float* a,
                            int lda, int ncu);
 
+// Q8_0 weights (q8.hip): int8 codes [N][K] and fp16 scales [N][K / 32]; the
+// quantiser run at weight load and the GEMVs of decode and short prefills
+// (same contracts as the int4 GEMVs).
+void launch_quantize_q8(hipStream_t s, const uint16_t* src, int nrows, int K, int8_t* codes, uint16_t* scales);
+int q8_gemv_t_tile(int K);
+void launch_gemv_q8(hipStream_t s, const int8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
+                    int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate,
+                    int ncu);
+void launch_gemv_gateup_q8(hipStream_t s, const int8_t* cg, const uint16_t* sg, const int8_t* cu, const uint16_t* su,
+                           int N, int K, const float* x, int ldx, int T, const float* gain, float eps, float* a,
+                           int lda, int ncu);
+
 // LoRA up products (lora.hip): for rows t < T, q rows of the fused q|k|v
 // output += scale B_q u[t][0, r), v rows += scale B_v u[t][r, 2 r).
 void launch_lora_up(hipStream_t s, const float* u, int ldu, int T, int r, const uint16_t* Bq, const uint16_t* Bv,

@@ -231,7 +231,7 @@ __device__ __forceinline__ void gemv_extra_bf16(const XRows& xr, int K, const fl
       }
     }
   };
-  if (TM == 1) {
+  if (TM == 1 && K <= 2048 * NP) {  // (the input pieces cover 2048 NP columns)
     RowIn<2 * NP> in;
     row_in_load(in, x, gain, K);
     load(0);
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const uint8_t* __restrict__ C4,
 #pragma unroll
       for (int i = 0; i < RPW; ++i) q4_piece(rc, rs, min(n0 + i, N - 1), (pb + p) * 2048 + lane * 32, K, c[p][i], sc[p][i]);
   };
-  if (TM == 1) {
+  if (TM == 1 && K <= 2048 * NP) {  // (the input pieces cover 2048 NP columns)
     RowIn<2 * NP> in;
     row_in_load(in, x, gain, K);
     load(0);  // (rows past N repeat row N - 1; their waves return after the staging)
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restric
         q4_piece(rcu, rsu, n, k, K, cu[p][i], su[p][i]);
       }
   };
-  if (TM == 1) {
+  if (TM == 1 && K <= 2048 * NP) {  // (the input pieces cover 2048 NP columns)
     RowIn<2 * NP> in;
     row_in_load(in, x, gain, K);
     load(0);  // (rows past N repeat row N - 1; their waves return after the staging)

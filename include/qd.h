@@ -61,7 +61,7 @@ enum {
   QD_E_HIP = -6    /* a HIP runtime call failed */
 };
 
-enum { QD_W_BF16 = 0, QD_W_INT4_G128 = 1 };
+enum { QD_W_BF16 = 0, QD_W_INT4_G128 = 1, QD_W_Q8_0 = 2 };
 
 /* Model and engine shape.  Copied by qd_create. */
 typedef struct {
@@ -73,7 +73,11 @@ typedef struct {
   uint8_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE */
   uint8_t qkv_bias;       /* 1: q/k/v projections carry a bias */
   uint8_t tie_embeddings; /* must be 1: the LM head is the embedding table */
-  uint8_t weight_format;  /* QD_W_BF16 or QD_W_INT4_G128 (projections only; E stays bf16) */
+  uint8_t weight_format;  /* QD_W_BF16, QD_W_INT4_G128 or QD_W_Q8_0 (projections only; E stays bf16).
+                             QD_W_Q8_0 ("SuperKittens pull request #7", the Q8_0 commit: int8 in
+                             blocks of 32 columns with an fp16 scale, quantised at qd_load_weights)
+                             needs decode_path QD_DECODE_GRAPH; its prefills run the GEMV kernels
+                             on tiles of up to 8 rows */
   int32_t max_pos;        /* KV-cache capacity in positions */
   int32_t max_prefill;    /* largest n accepted by one qd_prefill call */
   int32_t lora_rank_max;  /* 0 disables LoRA; else the largest rank qd_set_lora accepts (<= 64;
@@ -268,17 +272,18 @@ int qd_get_exchange(qd_handle* h, int32_t which, float* out_host, size_t capacit
 /* Projections of a layer, for qd_get_quantized. */
 enum { QD_PROJ_Q = 0, QD_PROJ_K = 1, QD_PROJ_V = 2, QD_PROJ_O = 3, QD_PROJ_GATE = 4, QD_PROJ_UP = 5, QD_PROJ_DOWN = 6 };
 
-/* Read back the int4 group-128 encoding that qd_load_weights made of one
- * projection of layer `layer` ("EMBERGLASS (qwen-webgpu-lora) README", "Note
- * on weights": int4 in groups of 128, quantised on the way to the GPU), in the
- * caller's [out, in] order whatever the library's own layout:
- *   codes_host  int8 [N][K], values in [-7, 7]            (codes_capacity >= N K)
- *   scales_host fp16 bit patterns [N][K / 128]           (scales_capacity >= N K / 128)
+/* Read back the encoding that qd_load_weights made of one projection of layer
+ * `layer`, in the caller's [out, in] order whatever the library's own layout.
+ * QD_W_INT4_G128 ("EMBERGLASS (qwen-webgpu-lora) README", "Note on weights":
+ * int4 in groups of 128, quantised on the way to the GPU): B = 128, codes in
+ * [-7, 7]; QD_W_Q8_0 ("SuperKittens pull request #7", the Q8_0 commit): B =
+ * 32, codes in [-127, 127].
+ *   codes_host  int8 [N][K]                              (codes_capacity >= N K)
+ *   scales_host fp16 bit patterns [N][K / B]             (scales_capacity >= N K / B)
  * with N x K the shape of that projection (qd_weights); the weight of row n,
- * column k is codes[n][k] * scale[n][k / 128].  Synchronises the stream.
- * Errors: QD_E_STATE (weights not loaded, or weight_format is not
- * QD_W_INT4_G128), QD_E_ARG (NULL output, bad layer or projection, capacity
- * too small), QD_E_HIP. */
+ * column k is codes[n][k] * scale[n][k / B].  Synchronises the stream.
+ * Errors: QD_E_STATE (weights not loaded, or bf16 weights), QD_E_ARG (NULL
+ * output, bad layer or projection, capacity too small), QD_E_HIP. */
 int qd_get_quantized(qd_handle* h, int32_t layer, int32_t which, int8_t* codes_host, size_t codes_capacity,
                      uint16_t* scales_host, size_t scales_capacity);
 

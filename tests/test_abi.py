@@ -167,6 +167,20 @@ def test_sampler_workspace_size():
     assert qd.sample_workspace_bytes(524288, qd.make_sampling(0.7, 40, 0.9, 1)) == 0  # merge LDS bound
 
 
+def test_q8_0_weights_need_the_graph_path():
+    """QD_W_Q8_0 runs on the graph decode path only (refused on the persistent
+    step before any HIP call); make_config picks the graph for it by default."""
+    cfg = qd.make_config(synth.TINY_Q8, max_prefill=16, decode_path=qd.QD_DECODE_PERSISTENT)
+    rc, h = _create(cfg)
+    assert rc == -1 and not h.value
+    assert qd.make_config(synth.TINY_Q8, max_prefill=16).decode_path == qd.QD_DECODE_GRAPH
+    assert qd.make_config(synth.TINY, max_prefill=16).decode_path == qd.QD_DECODE_PERSISTENT
+    cfg = qd.make_config(synth.TINY, max_prefill=16)
+    cfg.weight_format = 3
+    rc, h = _create(cfg)
+    assert rc == -1 and not h.value
+
+
 def test_bf16_kv_cache_needs_the_graph_path():
     """kv_format QD_KV_BF16 runs on the graph decode path only, and unknown
     formats are refused; both before any HIP call."""
