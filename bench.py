@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--workload", default="qwen2.5-3b-int4-lora")
     ap.add_argument("--path", choices=["auto", "persistent", "graph"], default="auto",
                     help="decode step as one persistent kernel, or as per-operation kernels in a hipGraph "
-                         "(auto: the persistent kernel without an adapter, the graph with one)")
+                         "(auto: the persistent kernel without an adapter, the graph with one or with Q8_0 weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the qwen3-0.6b job and the prefill timing")
     ap.add_argument("--only-decode", action="store_true", help="decode timing only (for profiler runs)")
@@ -251,13 +251,14 @@ def prefill_rate(dec, wl, stream, rows):
                     "algorithmic FLOPs over the bf16 dense peak (the hi/lo input split issues each product twice)"}
 
 
-def job_06b(stream, path):
-    """qwen3-0.6b: jobs of reset + 5-token prefill + 128 greedy decode steps
-    (the configuration of the earlier measurements), decode roofline."""
+def job_06b(stream, path, workload="qwen3-0.6b"):
+    """qwen3-0.6b (or its Q8_0 form): jobs of reset + 5-token prefill + 128
+    greedy decode steps (the configuration of the earlier measurements),
+    decode roofline."""
     import numpy as np
     import synth
     import torch
-    wl = synth.WORKLOADS["qwen3-0.6b"]
+    wl = synth.WORKLOADS[workload]
     dw = synth.make_weights_device(wl.shape)
     dec = make_decoder(wl, path, stream, dw)
     del dw
@@ -284,9 +285,27 @@ def job_06b(stream, path):
     byts = sum(step_bytes(wl.shape, 0, wl.prompt_len + 1 + i) for i in range(n)) / n
     us = ms * 1e3 / n
     ach = byts / (us * 1e-6) / 1e9
-    return {"workload": wl.name, "decode_tok_s": round(n / (ms * 1e-3), 1), "decode_step_us": round(us, 2),
+    return {"workload": wl.name, "decode_path": path, "decode_tok_s": round(n / (ms * 1e-3), 1),
+            "decode_step_us": round(us, 2), "bytes_per_step": round(byts),
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name)}}
+                         "frac": round(ach / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(wl.name) if path == "persistent" else None}}
+
+
+def job_q8(stream):
+    """The Q8_0 weight format on qwen3-0.6b ("SuperKittens pull request #7"
+    compares Q8_0 with fp16 weights on this model): the same decode job with
+    Q8_0 and with bf16 projection weights, both on the per-operation graph
+    (Q8_0 runs there only), and the ratio."""
+    q8 = job_06b(stream, "graph", "qwen3-0.6b-q8_0")
+    bf = job_06b(stream, "graph", "qwen3-0.6b")
+    return {"q8_0": q8, "bf16": bf, "q8_0_over_bf16": round(q8["decode_tok_s"] / bf["decode_tok_s"], 3),
+            "dtype": dtype_of(synth_shape("qwen3-0.6b-q8_0"), "graph")}
+
+
+def synth_shape(name):
+    import synth
+    return synth.WORKLOADS[name].shape
 
 
 def job_c4(stream, steps=20, warmup=5):
@@ -391,7 +410,9 @@ def cpu_baseline(wl, dw, dl, ctx):
 
 def dtype_of(shape, path):
     import synth
-    if shape.weight_format == synth.W_INT4_G128:
+    if shape.weight_format == synth.W_Q8_0:
+        w = "Q8_0 projection weights (int8 blocks of 32 x fp16 scales); codes widened in registers, f32 products (GEMV)"
+    elif shape.weight_format == synth.W_INT4_G128:
         w = ("int4 group-128 projection weights x fp16 scales; " +
              ("int8 matrix-core products against the input split into three 7-bit pieces (error <= 2^-21 of the "
               "largest input of a wave's groups)" if path == "persistent" else
@@ -419,7 +440,8 @@ def main():
     stream = torch.cuda.Stream()
     # auto: the persistent step, except with an adapter at the long context,
     # where the captured graph's split-K attention over every CU is faster
-    path = ("graph" if wl.lora_rank else "persistent") if args.path == "auto" else args.path
+    path = ("graph" if wl.lora_rank or wl.shape.weight_format == 2 else "persistent") if args.path == "auto" \
+        else args.path
     dw = synth.make_weights_device(shape)
     dl = synth.make_lora_device(shape, wl.lora_rank) if wl.lora_rank else None
     torch.cuda.synchronize()
@@ -476,6 +498,8 @@ def main():
         out["qwen3_0_6b"] = job_06b(stream, "persistent" if args.path == "auto" else args.path)
     if not args.only_decode and not args.no_extra and wl.name != "qwen2.5-3b-int4":
         out["qwen2_5_3b_int4"] = job_c4(stream)
+    if not args.only_decode and not args.no_extra:
+        out["q8_0_qwen3_0_6b"] = job_q8(stream)
     print(json.dumps(out), flush=True)
 
 
