@@ -62,7 +62,8 @@ EXPORTS = ["qd_create", "qd_load_weights", "qd_reset_kv", "qd_prefill", "qd_deco
            "qd_clear_lora", "qd_enable_capture", "qd_get_capture", "qd_enable_phase_trace", "qd_get_phase_trace",
            "qd_get_quantized", "qd_get_exchange", "qd_sync_token", "qd_get_abandoned", "qd_get_position",
            "qd_last_error", "qd_destroy", "qd_sizeof_config", "qd_sizeof_weights", "qd_sizeof_sampling",
-           "qd_sizeof_lora", "qd_sample_workspace_bytes", "qd_sample_logits", "qd_sample_logits_static"]
+           "qd_sizeof_lora", "qd_sample_workspace_bytes", "qd_sample_logits", "qd_sample_logits_static",
+           "qd_verify", "qd_rewind"]
 
 _lib = None
 
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qd_prefill": (i32, [H, ctypes.POINTER(ctypes.c_int32), i32, ctypes.POINTER(QdSampling), _P, _P]),
         "qd_decode_step": (i32, [H, ctypes.POINTER(QdSampling), _P, _P]),
         "qd_decode_steps": (i32, [H, i32, ctypes.POINTER(QdSampling), _P, _P]),
+        "qd_verify": (i32, [H, ctypes.POINTER(ctypes.c_int32), i32, _P, _P]),
+        "qd_rewind": (i32, [H, i32, i32]),
         "qd_set_lora": (i32, [H, ctypes.POINTER(QdLora)]),
         "qd_clear_lora": (i32, [H]),
         "qd_enable_capture": (i32, [H, i32]),
@@ -149,6 +152,18 @@ def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Option
     c.decode_path = int(decode_path)
     c.kv_format = int(kv_format)
     return c
+
+
+QD_VERIFY_MAX = 16
+
+
+def accepted_drafts(drafts: Sequence[int], choices: Sequence[int]) -> int:
+    """Greedy acceptance: the number of leading drafts d[i] that equal the
+    choice made before them (choices[i] follows the i-th verified row)."""
+    a = 0
+    while a < len(drafts) and int(drafts[a]) == int(choices[a]):
+        a += 1
+    return a
 
 
 def make_sampling(temperature: float, top_k: int, top_p: float, seed: int) -> QdSampling:
@@ -257,6 +272,32 @@ class Decoder:
         """n decode steps with device-resident token feedback (tokens_out: int32 device tensor of n)."""
         self._check(self.lib.qd_decode_steps(self.h, int(n), None if sampling is None else ctypes.byref(sampling),
                                              _ptr(logits_out), _ptr(tokens_out)))
+
+    def verify(self, tokens: Sequence[int], logits_out=None, choices_out=None):
+        """Speculative verification of len(tokens) <= QD_VERIFY_MAX tokens: the
+        greedy choice after every row into choices_out (int32 device tensor),
+        the rows' logits into logits_out (float32 device tensor [m, V])."""
+        arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+        self._check(self.lib.qd_verify(self.h, arr, len(tokens), ctypes.c_void_p(_ptr(logits_out)),
+                                       ctypes.c_void_p(_ptr(choices_out))))
+
+    def rewind(self, n: int, next_token: int):
+        """Drop the last n positions and make next_token the next input token."""
+        self._check(self.lib.qd_rewind(self.h, int(n), int(next_token)))
+
+    def speculative_step(self, next_token: int, drafts: Sequence[int], choices_out):
+        """One greedy speculative step: verify [next_token, *drafts], accept the
+        leading drafts that equal the choice before them, rewind the rest.
+        Returns the new tokens (the accepted drafts and one more choice), which
+        are those of as many greedy decode steps.  choices_out: an int32 device
+        tensor of at least len(drafts) + 1 entries (read back here)."""
+        m = len(drafts) + 1
+        self.verify([next_token, *drafts], choices_out=choices_out)
+        self.sync_token()  # the library's stream, which need not be torch's current one
+        c = [int(v) for v in choices_out[:m].cpu().tolist()]
+        a = accepted_drafts(drafts, c)
+        self.rewind(m - 1 - a, c[a])
+        return list(drafts[:a]) + [c[a]]
 
     def set_lora(self, lora_layers: List[Dict], rank: int, alpha: float):
         q = QdLora()

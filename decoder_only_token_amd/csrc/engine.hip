@@ -112,6 +112,12 @@ struct qd_handle {
   float* logits = nullptr;  // [V]
   float* pval = nullptr;
   int32_t* pidx = nullptr;
+  // speculative verification: logits [QD_VERIFY_MAX][V], argmax partials
+  // [QD_VERIFY_MAX][lmhead_blocks(V)], choices [QD_VERIFY_MAX]
+  float* vlogits = nullptr;
+  float* vpval = nullptr;
+  int32_t* vpidx = nullptr;
+  int32_t* vchoice = nullptr;
   float* spv = nullptr;      // sampling: per-slice sorted top-k lists
   int32_t* spi = nullptr;
   int32_t* tokens_dev = nullptr;  // [max_prefill]
@@ -571,6 +577,10 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
       (rc = dev_alloc(h, &h->part, h->part_floats)) || (rc = dev_alloc(h, &h->logits, (size_t)c.vocab)) ||
       (rc = dev_alloc(h, &h->pval, (size_t)lmhead_blocks(c.vocab))) ||
       (rc = dev_alloc(h, &h->pidx, (size_t)lmhead_blocks(c.vocab))) ||
+      (rc = dev_alloc(h, &h->vlogits, (size_t)QD_VERIFY_MAX * c.vocab)) ||
+      (rc = dev_alloc(h, &h->vpval, (size_t)QD_VERIFY_MAX * lmhead_blocks(c.vocab))) ||
+      (rc = dev_alloc(h, &h->vpidx, (size_t)QD_VERIFY_MAX * lmhead_blocks(c.vocab))) ||
+      (rc = dev_alloc(h, &h->vchoice, (size_t)QD_VERIFY_MAX)) ||
       (rc = dev_alloc(h, &h->spv, (size_t)sample_lists(c.vocab) * 64)) ||
       (rc = dev_alloc(h, &h->spi, (size_t)sample_lists(c.vocab) * 64)) ||
       (rc = dev_alloc(h, &h->tokens_dev, rows)) || (rc = dev_alloc(h, &h->st, 1)))
@@ -874,6 +884,57 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
   if ((rc = maybe_sample(h, sampling))) return rc;
   h->pos += 1;
   return copy_outputs(h, logits_dev, token_dev);
+}
+
+int qd_verify(qd_handle* h, const int32_t* tokens_host, int32_t m, float* logits_dev, int32_t* choices_dev) {
+  if (!h) return QD_E_ARG;
+  const qd_config& c = h->cfg;
+  if (!h->weights) return h->set_err(QD_E_STATE, "weights not loaded");
+  if (!tokens_host) return h->set_err(QD_E_ARG, "tokens is NULL");
+  if (m < 1 || m > QD_VERIFY_MAX) return h->set_err(QD_E_ARG, "m must be in [1, QD_VERIFY_MAX]");
+  if (m > c.max_prefill) return h->set_err(QD_E_RANGE, "m exceeds max_prefill");
+  if ((int64_t)h->pos + m > c.max_pos) return h->set_err(QD_E_RANGE, "position would exceed max_pos");
+  for (int i = 0; i < m; ++i)
+    if (tokens_host[i] < 0 || tokens_host[i] >= c.vocab) return h->set_err(QD_E_ARG, "token id out of range");
+  if (h->failed) return h->set_err(QD_E_STATE, "an earlier decode step was abandoned; call qd_reset_kv");
+  hipStream_t s = h->stream;
+  HIP_TRY(h, hipStreamSynchronize(s));  // the pinned staging buffer may still feed an earlier copy
+  memcpy(h->tokens_pinned, tokens_host, (size_t)m * sizeof(int32_t));
+  HIP_TRY(h, hipMemcpyAsync(h->tokens_dev, h->tokens_pinned, (size_t)m * sizeof(int32_t), hipMemcpyHostToDevice, s));
+  // the m rows through the layers (a prefill of m rows), then the final norm
+  // and LM head of every row, up to lmhead_rows_per_pass rows per E pass
+  const int H = c.hidden, V = c.vocab, nblk = lmhead_blocks(V);
+  launch_embed(s, h->embed, h->tokens_dev, m, H, h->x);
+  if (m >= kGemmMinRows && c.weight_format != QD_W_Q8_0)
+    enqueue_layers_gemm(h, m, false);
+  else
+    enqueue_layers_gemv(h, m, false);
+  for (int t0 = 0, tr = lmhead_rows_per_pass(H); t0 < m; t0 += tr) {
+    const int tn = std::min(tr, m - t0);
+    launch_lmhead_rows_bf16(s, h->embed, V, H, h->x + (size_t)t0 * H, tn, h->final_norm, c.rms_eps,
+                            h->vlogits + (size_t)t0 * V, h->vpval + (size_t)t0 * nblk, h->vpidx + (size_t)t0 * nblk);
+  }
+  launch_argmax_rows(s, h->vpval, h->vpidx, nblk, m, h->st, h->vchoice);
+  HIP_TRY(h, hipGetLastError());
+  h->pos += m;
+  h->have_token = true;
+  h->cap_rows = 0;
+  if (logits_dev)
+    HIP_TRY(h, hipMemcpyAsync(logits_dev, h->vlogits, (size_t)m * V * 4, hipMemcpyDeviceToDevice, s));
+  if (choices_dev) HIP_TRY(h, hipMemcpyAsync(choices_dev, h->vchoice, (size_t)m * 4, hipMemcpyDeviceToDevice, s));
+  return QD_OK;
+}
+
+int qd_rewind(qd_handle* h, int32_t n, int32_t next_token) {
+  if (!h) return QD_E_ARG;
+  if (n < 0 || n > h->pos) return h->set_err(QD_E_ARG, "n must be in [0, position]");
+  if (next_token < 0 || next_token >= h->cfg.vocab) return h->set_err(QD_E_ARG, "token id out of range");
+  launch_rewind_state(h->stream, h->st, n, next_token);
+  HIP_TRY(h, hipGetLastError());
+  h->pos -= n;
+  h->have_token = h->pos > 0;
+  h->cap_rows = 0;
+  return QD_OK;
 }
 
 int qd_decode_steps(qd_handle* h, int32_t n, const qd_sampling* sampling, float* logits_dev, int32_t* tokens_dev) {

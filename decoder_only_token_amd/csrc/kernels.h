@@ -16,6 +16,7 @@ struct DevState {
 #define GEMV_RPW 4     // output rows per wave (plain GEMV)
 #define GATEUP_RPW 2   // output rows per wave (gate/up pair)
 #define LMHEAD_RPW 4   // vocabulary rows per wave (LM head)
+#define LMHEAD_ROWS 8  // input rows of one multi-row LM head pass
 
 void launch_embed(hipStream_t s, const uint16_t* E, const int32_t* tok, int T, int H, float* x);
 // (ncu = compute units of the GPU, used to size the grid)
@@ -26,6 +27,15 @@ void launch_gemv_gateup_bf16(hipStream_t s, const uint16_t* Wg, const uint16_t* 
 int lmhead_blocks(int V);
 void launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
                         float* logits, float* part_val, int32_t* part_idx, float* xf_out);
+// Speculative verification: final norm + LM head for T <= lmhead_rows_per_pass(H)
+// rows with per-row logits [T][V] and argmax partials [T][lmhead_blocks(V)];
+// the per-row choices (advancing the step state by T); dropping positions.
+int lmhead_rows_per_pass(int H);
+void launch_lmhead_rows_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, int T, const float* gain,
+                             float eps, float* logits, float* part_val, int32_t* part_idx);
+void launch_argmax_rows(hipStream_t s, const float* part_val, const int32_t* part_idx, int nblk, int T, DevState* st,
+                        int32_t* choice);
+void launch_rewind_state(hipStream_t s, DevState* st, int n, int32_t token);
 void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* part_idx, int nparts, DevState* st,
                          int advance, int32_t* token_out);
 void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq, int nkv, int d, const float* qn,

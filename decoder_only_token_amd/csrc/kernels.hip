@@ -409,6 +409,147 @@ void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* pa
 }
 
 // ---------------------------------------------------------------------------
+// Final RMSNorm + tied LM head for T <= LMHEAD_ROWS rows at once (speculative
+// verification): every E row is read once for all T rows, so the bytes of a
+// T-row pass are those of one row.  logits[t][v] (t-th row, ld V) and per-block
+// argmax partials part_val / part_idx [t][nblk] (lowest id on ties).
+__global__ __launch_bounds__(256) void k_lmhead_rows_bf16(const uint16_t* __restrict__ E, int V, int H,
+                                                          const float* __restrict__ x, int T,
+                                                          const float* __restrict__ gain, float eps,
+                                                          float* __restrict__ logits, float* __restrict__ part_val,
+                                                          int32_t* __restrict__ part_idx, int nblk) {
+  extern __shared__ float smem[];
+  float* red = smem;
+  float* h = smem + 8;
+  __shared__ float bval[LMHEAD_ROWS][4];
+  __shared__ int32_t bidx[LMHEAD_ROWS][4];
+  stage_input(x, H, T, H, gain, eps, h, red);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * LMHEAD_RPW;
+  float acc[LMHEAD_RPW][LMHEAD_ROWS];
+#pragma unroll
+  for (int i = 0; i < LMHEAD_RPW; ++i)
+#pragma unroll
+    for (int t = 0; t < LMHEAD_ROWS; ++t) acc[i][t] = 0.f;
+  if (n0 < V) {
+    for (int k = lane * 8; k < H; k += 512) {
+      u32x4 w[LMHEAD_RPW];
+#pragma unroll
+      for (int i = 0; i < LMHEAD_RPW; ++i) {
+        const int n = min(n0 + i, V - 1);
+        w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(E + (size_t)n * H + k));
+      }
+#pragma unroll
+      for (int t = 0; t < LMHEAD_ROWS; ++t)
+        if (t < T) {
+#pragma unroll
+          for (int i = 0; i < LMHEAD_RPW; ++i) acc[i][t] += dot8(w[i], h + (size_t)t * H + k);
+        }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < LMHEAD_ROWS; ++t) {
+    if (t >= T) break;
+    float best = -INFINITY;
+    int32_t bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < LMHEAD_RPW; ++i) {
+      const float sv = wave_sum(acc[i][t]);
+      const int n = n0 + i;
+      if (n < V) {
+        if (lane == 0) logits[(size_t)t * V + n] = sv;
+        if (sv > best) { best = sv; bi = n; }  // rows visited in increasing id: ties keep the lowest
+      }
+    }
+    if (lane == 0) { bval[t][wave] = best; bidx[t][wave] = bi; }
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    float bv = bval[t][0];
+    int32_t bj = bidx[t][0];
+    for (int w = 1; w < 4; ++w)
+      if (bval[t][w] > bv || (bval[t][w] == bv && bidx[t][w] < bj)) { bv = bval[t][w]; bj = bidx[t][w]; }
+    part_val[(size_t)t * nblk + blockIdx.x] = bv;
+    part_idx[(size_t)t * nblk + blockIdx.x] = bj;
+  }
+}
+
+// Greedy choice of each of T rows from its per-block partials (block t: row
+// t), into choice[t]; the block of the last row then advances the step state
+// as T decode steps would: token := its choice, pos += T, step += T.
+__global__ __launch_bounds__(256) void k_argmax_rows(const float* __restrict__ part_val,
+                                                     const int32_t* __restrict__ part_idx, int nblk, int T,
+                                                     DevState* st, int32_t* __restrict__ choice) {
+  __shared__ float sv[256];
+  __shared__ int32_t si[256];
+  const int t = blockIdx.x;
+  float bv = -INFINITY;
+  int32_t bj = 0x7fffffff;
+  for (int i = threadIdx.x; i < nblk; i += 256) {
+    const float v = part_val[(size_t)t * nblk + i];
+    const int32_t j = part_idx[(size_t)t * nblk + i];
+    if (v > bv || (v == bv && j < bj)) { bv = v; bj = j; }
+  }
+  sv[threadIdx.x] = bv;
+  si[threadIdx.x] = bj;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) {
+      const float v = sv[threadIdx.x + off];
+      const int32_t j = si[threadIdx.x + off];
+      if (v > sv[threadIdx.x] || (v == sv[threadIdx.x] && j < si[threadIdx.x])) {
+        sv[threadIdx.x] = v;
+        si[threadIdx.x] = j;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int32_t tok = si[0];
+    if (tok == 0x7fffffff) tok = 0;  // only if every logit was NaN
+    choice[t] = tok;
+    if (t == T - 1) {
+      st->token = tok;
+      st->pos += T;
+      st->step += T;
+    }
+  }
+}
+
+// Drop the last n positions: pos -= n, step -= n, the next input token set.
+__global__ void k_rewind_state(DevState* st, int n, int32_t token) {
+  if (threadIdx.x == 0) {
+    st->pos -= n;
+    st->step = st->step >= n ? st->step - n : 0;
+    st->token = token;
+  }
+}
+
+int lmhead_rows_per_pass(int H) {
+  int r = (40960 - 8 - 256) / H;  // staged rows (and the block's partials) within 160 KiB of LDS
+  if (r > LMHEAD_ROWS) r = LMHEAD_ROWS;
+  return r < 1 ? 1 : r;
+}
+
+void launch_lmhead_rows_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, int T, const float* gain,
+                             float eps, float* logits, float* part_val, int32_t* part_idx) {
+  const int nblk = lmhead_blocks(V);
+  const size_t lds = (8 + (size_t)T * H) * sizeof(float);
+  hipLaunchKernelGGL(k_lmhead_rows_bf16, dim3(nblk), dim3(256), lds, s, E, V, H, x, T, gain, eps, logits, part_val,
+                     part_idx, nblk);
+}
+
+void launch_argmax_rows(hipStream_t s, const float* part_val, const int32_t* part_idx, int nblk, int T, DevState* st,
+                        int32_t* choice) {
+  hipLaunchKernelGGL(k_argmax_rows, dim3(T), dim3(256), 0, s, part_val, part_idx, nblk, T, st, choice);
+}
+
+void launch_rewind_state(hipStream_t s, DevState* st, int n, int32_t token) {
+  hipLaunchKernelGGL(k_rewind_state, dim3(1), dim3(64), 0, s, st, n, token);
+}
+
+// ---------------------------------------------------------------------------
 // Per-head QK-RMSNorm, RoPE and the KV-cache write for T rows at positions
 // pos .. pos+T-1 (pos read from the device state).
 // "flashmoon demo/README.md", decode invariants: RoPE is applied as K is

@@ -218,6 +218,34 @@ int qd_decode_step(qd_handle* h, const qd_sampling* sampling, float* logits_dev,
  * Errors: as qd_decode_step; QD_E_ARG (n < 1), QD_E_RANGE (pos + n > max_pos). */
 int qd_decode_steps(qd_handle* h, int32_t n, const qd_sampling* sampling, float* logits_dev, int32_t* tokens_dev);
 
+/* Speculative verification ("flashmoon demo/README.md", Known limitations:
+ * no speculative decode, a single sequence; here for that one sequence).
+ * Consumes the m host tokens tokens_host[0 .. m) at positions pos .. pos + m - 1,
+ * as a prefill of m rows, and makes the greedy choice after every row:
+ * choices_dev[i] (device int32[m], optional) = argmax of the logits after
+ * tokens[0 .. i] (lowest id on ties), the choice a greedy decode step would
+ * make there; logits_dev (device f32[m][vocab], optional) receives the rows'
+ * logits.  The projections run as for a prefill of m rows (GEMV kernels that
+ * read each weight once for up to 8 rows; matrix cores from 16 rows) and the
+ * LM head reads the embedding table once for up to 8 rows.  Afterwards the
+ * position is pos + m and the next input token is choices[m - 1], as after m
+ * decode steps.  With tokens = [the next input token, d1, .., d(m-1)] (drafts)
+ * and a = the number of leading drafts equal to the choice before them
+ * (d(i) == choices[i - 1]), the a + 1 tokens d1 .. da, choices[a] are exactly
+ * those of a + 1 greedy decode steps; qd_rewind(h, m - 1 - a, choices[a])
+ * then drops the rejected rows.
+ * Errors: QD_E_STATE (no weights), QD_E_ARG (NULL tokens, m outside
+ * [1, QD_VERIFY_MAX], token out of range), QD_E_RANGE (m > max_prefill or
+ * pos + m > max_pos). */
+#define QD_VERIFY_MAX 16
+int qd_verify(qd_handle* h, const int32_t* tokens_host, int32_t m, float* logits_dev, int32_t* choices_dev);
+
+/* Drop the last n positions of the cache (position -= n; their K/V rows are
+ * overwritten by later steps) and make next_token the next input token.
+ * Stream-ordered, no synchronisation.
+ * Errors: QD_E_ARG (n outside [0, position], token out of range). */
+int qd_rewind(qd_handle* h, int32_t n, int32_t next_token);
+
 /* Install (copy) a LoRA adapter ("EMBERGLASS (qwen-webgpu-lora) README", LoRA
  * sections: a live low-rank adapter on q_proj and v_proj).  Needs
  * lora_rank_max >= 1 at qd_create; rank must be in 1..lora_rank_max and alpha

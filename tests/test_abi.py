@@ -190,3 +190,11 @@ def test_bf16_kv_cache_needs_the_graph_path():
     cfg = qd.make_config(synth.TINY, max_prefill=16, decode_path=qd.QD_DECODE_GRAPH, kv_format=2)
     rc, h = _create(cfg)
     assert rc == -1 and not h.value
+
+
+def test_greedy_acceptance_rule():
+    """Leading drafts equal to the choice before them are accepted."""
+    assert qd.accepted_drafts([5, 6, 7], [5, 6, 7, 8]) == 3
+    assert qd.accepted_drafts([5, 6, 7], [5, 9, 7, 8]) == 1
+    assert qd.accepted_drafts([5, 6, 7], [4, 6, 7, 8]) == 0
+    assert qd.accepted_drafts([], [3]) == 0
