@@ -184,6 +184,39 @@ def decode_at_end(dec, wl, stream, steps, warmup, kv_elem_bytes=4):
             "bytes_per_step": sum(byts) / steps}
 
 
+def verify_rate(dec, wl, stream, ms_rows=(4, 8, 16), reps=5):
+    """Speculative verification at the end of the context: qd_verify of m rows
+    then qd_rewind(m), so every call runs at the same context; the median time
+    per call and the tokens/s it gives when every draft is accepted (m tokens
+    per call)."""
+    import numpy as np
+    import synth
+    import torch
+    start = wl.shape.max_pos - 16 - 1
+    fill_to(dec, wl, stream, start)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out = {"context": start}
+    with torch.cuda.stream(stream):
+        for m in ms_rows:
+            if m > wl.max_prefill:
+                continue
+            toks = synth.make_prompt(wl.shape.vocab, m, seed=300 + m)
+            dts = []
+            for r in range(reps + 1):
+                torch.cuda.synchronize()
+                a, b = ev(), ev()
+                a.record(stream)
+                dec.verify(toks)
+                dec.rewind(m, int(toks[0]))
+                b.record(stream)
+                torch.cuda.synchronize()
+                if r:
+                    dts.append(a.elapsed_time(b))
+            t = float(np.median(dts))
+            out[f"m{m}"] = {"us_per_call": round(t * 1e3, 1), "tok_s_all_accepted": round(m / (t * 1e-3), 1)}
+    return out
+
+
 def multistep_rate(dec, wl, stream, n=16, batches=3):
     """qd_decode_steps with n tokens per call (one host synchronisation per
     call), `batches` timed calls after one untimed, ending at the last cache
@@ -482,6 +515,7 @@ def main():
     }
     if not args.only_decode and not args.no_extra:
         out["decode_steps_16"] = multistep_rate(dec, wl, stream)
+        out["speculative_verify"] = verify_rate(dec, wl, stream)
         out["prefill_batched"] = prefill_rate(dec, wl, stream, wl.prompt_len)
     if not args.only_decode and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, dw, dl, shape.max_pos)

@@ -85,10 +85,10 @@ __global__ __launch_bounds__(256) void k_attn_decode(const float* __restrict__ q
                                                      const float* __restrict__ kn, float eps,
                                                      const float* __restrict__ cos_t, const float* __restrict__ sin_t,
                                                      KVT* __restrict__ Kc, KVT* __restrict__ Vc, int max_pos,
-                                                     const DevState* __restrict__ st, int S, int cmin, float scale,
+                                                     const DevState* __restrict__ st, int row, int S, int cmin, float scale,
                                                      float* __restrict__ part, LoraUp lu) {
   const int g = blockIdx.x, sp = blockIdx.y;
-  const int ctx = st->pos + 1, pos = ctx - 1;
+  const int ctx = st->pos + row + 1, pos = ctx - 1;  // (row: of a batch of new rows)
   const int C = split_len(ctx, S, cmin);
   const int p_begin = sp * C;
   if (p_begin >= ctx) return;  // the merge reads only the splits that hold positions
@@ -382,11 +382,11 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
                                                       const float* __restrict__ kn, float eps,
                                                       const float* __restrict__ cos_t, const float* __restrict__ sin_t,
                                                       KVT* __restrict__ Kc, KVT* __restrict__ Vc, int max_pos,
-                                                      const DevState* __restrict__ st, int S, int cmin, float scale,
+                                                      const DevState* __restrict__ st, int row, int S, int cmin, float scale,
                                                       float* __restrict__ part, LoraUp lu) {
   constexpr int G = 8;
   const int g = blockIdx.x, sp = blockIdx.y;
-  const int ctx = st->pos + 1, pos = ctx - 1;
+  const int ctx = st->pos + row + 1, pos = ctx - 1;  // (row: of a batch of new rows)
   const int C = split_len(ctx, S, cmin);
   const int p_begin = sp * C;
   if (p_begin >= ctx) return;  // the merge reads only the splits that hold positions
@@ -661,12 +661,13 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
 constexpr int kMaxSplits = 1024;
 
 __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restrict__ part, int S, int cmin,
-                                                           const DevState* __restrict__ st, float* __restrict__ o_out) {
+                                                           const DevState* __restrict__ st, int row,
+                                                           float* __restrict__ o_out) {
   __shared__ float f[kMaxSplits];
   __shared__ float red[8];
   __shared__ float acc_s[8][33];
   const int h = blockIdx.x, tid = threadIdx.x;
-  const int ctx = st->pos + 1;
+  const int ctx = st->pos + row + 1;
   const int C = split_len(ctx, S, cmin);
   const int s_act = min(S, (ctx + C - 1) / C);
   const float* base = part + (size_t)h * S * (D + 2);
@@ -889,17 +890,17 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
                              const float* cos_t, const float* sin_t, int nq, int nkv, void* Kc, void* Vc,
                              int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out,
                              const float* lora_u, const uint16_t* lora_bq, const uint16_t* lora_bv, int lora_r,
-                             float lora_scale) {
+                             float lora_scale, int row) {
   const float scale = 1.0f / sqrtf((float)D);
   const dim3 grid(nkv, S);
   const LoraUp lu{lora_u, lora_bq, lora_bv, lora_r, lora_scale};
 #define QD_ATTN_DECODE_T(G_, L_, T_)                                                                                 \
   if (G_ == 8)                                                                                                       \
     hipLaunchKernelGGL((k_attn_decode8<L_, T_>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, (T_*)Kc,    \
-                       (T_*)Vc, max_pos, st, S, cmin, scale, part, lu);                                              \
+                       (T_*)Vc, max_pos, st, row, S, cmin, scale, part, lu);                                              \
   else                                                                                                               \
     hipLaunchKernelGGL((k_attn_decode<G_, L_, T_>), grid, dim3(256), 0, s, qkv, qn, kn, eps, cos_t, sin_t, (T_*)Kc, \
-                       (T_*)Vc, max_pos, st, S, cmin, scale, part, lu)
+                       (T_*)Vc, max_pos, st, row, S, cmin, scale, part, lu)
 #define QD_ATTN_DECODE(G_)                                     \
   if (kv_bf16) {                                               \
     if (lora_u) QD_ATTN_DECODE_T(G_, true, uint16_t);          \
@@ -917,7 +918,7 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
   }
 #undef QD_ATTN_DECODE
 #undef QD_ATTN_DECODE_T
-  hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32), dim3(256), 0, s, part, S, cmin, st, o_out);
+  hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32), dim3(256), 0, s, part, S, cmin, st, row, o_out);
 }
 
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,

@@ -23,6 +23,11 @@
 namespace {
 
 constexpr int kDecodeMinSplit = 16;  // shortest split of the decode attention
+// batches of at most this many rows at positions from kRowAttnMinPos on run
+// the decode attention once per row instead of the prefill attention (which
+// spreads a batch over its query rows, few here, not over the positions)
+constexpr int kRowAttnMaxRows = 16;
+constexpr int kRowAttnMinPos = 512;
 constexpr int kMaxStepsPerLaunch = 64;  // decode steps in one persistent launch (8-bit step tags, 200 ms waits)
 constexpr int kGemmMinRows = 16;  // prefills of at least this many rows use the matrix-core projections
 
@@ -339,6 +344,16 @@ void enqueue_attention(qd_handle* h, int l, int T) {
                             kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos, h->st, h->dec_splits,
                             kDecodeMinSplit, h->part, h->o, lo ? h->lu : nullptr, lo ? h->lora[l].bq : nullptr,
                             lo ? h->lora[l].bv : nullptr, h->lora_rank, h->lora_scale);
+  } else if (T <= kRowAttnMaxRows && h->pos >= kRowAttnMinPos) {
+    // a few rows at a long context (speculative verification, short prefills):
+    // the split-K decode attention once per row, in order, so that every row
+    // is spread over the CUs and sees the rows before it (the adapter's up
+    // products are already in the q|k|v rows)
+    for (int t = 0; t < T; ++t)
+      launch_attention_decode(s, h->qkv + (size_t)t * qkv_rows(c), L.q_norm, L.k_norm, c.rms_eps, h->rope_cos,
+                              h->rope_sin, nq, nkv, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos, h->st,
+                              h->dec_splits, kDecodeMinSplit, h->part, h->o + (size_t)t * nq * d, nullptr, nullptr,
+                              nullptr, 0, 0.f, t);
   } else {
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
                       h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16);

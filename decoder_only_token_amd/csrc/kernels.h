@@ -44,13 +44,14 @@ void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq
 // Decode attention for one new row (attn.hip), from the raw q|k|v projection
 // row (group-major): QK-norm (gains may be null), RoPE, the cache write of the
 // new k / v, then S splits of length max(cmin, ceil(ctx / S)); part holds
-// nq * S * (d + 2) floats.
+// nq * S * (d + 2) floats.  The row sits at position st->pos + row (row > 0:
+// the rows of a short batch, one launch each, in order).
 int attn_decode_splits(int max_pos, int nkv, int ncu, int cmin);
 void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, const float* kn, float eps,
                              const float* cos_t, const float* sin_t, int nq, int nkv, void* Kc, void* Vc,
                              int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part, float* o_out,
                              const float* lora_u = nullptr, const uint16_t* lora_bq = nullptr,
-                             const uint16_t* lora_bv = nullptr, int lora_r = 0, float lora_scale = 0.f);
+                             const uint16_t* lora_bv = nullptr, int lora_r = 0, float lora_scale = 0.f, int row = 0);
 
 // Causal attention of T >= 2 new rows (attn.hip), rows at positions pos .. pos + T - 1.
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,

@@ -9,7 +9,9 @@ projections as GEMVs over up to 8 rows), the tiny int4 model with 16 rows
 Q8_0 weights.  A greedy speculative loop (drafts taken from the oracle's
 greedy continuation, some planted wrong) must produce the oracle's greedy
 tokens, and a decode step after its rewinds must see exactly the accepted
-prefix in the cache.
+prefix in the cache.  Past 512 cached positions the rows of a batch run the
+split-K decode attention one by one (cases at 600-700 positions, with an
+adapter and the bf16 cache).
 """
 import dataclasses
 
@@ -38,36 +40,49 @@ def torch_cuda():
     return torch
 
 
-def make(torch, shape, path, max_prefill=32):
+def make(torch, shape, path, max_prefill=32, lora_rank_max=0, kv_format=0):
     import decoder_only_token_amd as qd
-    cfg = qd.make_config(shape, max_prefill=max_prefill,
+    cfg = qd.make_config(shape, max_prefill=max_prefill, lora_rank_max=lora_rank_max, kv_format=kv_format,
                          decode_path=None if path == "auto" else
                          (qd.QD_DECODE_PERSISTENT if path == "persistent" else qd.QD_DECODE_GRAPH))
     dec = qd.Decoder(cfg, torch.cuda.current_stream().cuda_stream)
     return dec
 
 
+TINY_LONG = dataclasses.replace(synth.TINY, max_pos=1024)
+INT4_LONG = dataclasses.replace(synth.TINY_INT4, max_pos=1024)
+
 CASES = {
-    # name: (shape, decode path, prompt length, m)
-    "tiny-graph-5": (TINY, "graph", 9, 5),
-    "tiny-persistent-8": (TINY, "persistent", 9, 8),
-    "tiny-int4-16": (synth.TINY_INT4, "graph", 7, 16),
-    "tiny-int4-1": (synth.TINY_INT4, "persistent", 7, 1),
-    "tiny-q8-6": (synth.TINY_Q8, "auto", 5, 6),
+    # name: (shape, decode path, prompt length, m, adapter rank, bf16 cache)
+    "tiny-graph-5": (TINY, "graph", 9, 5, 0, False),
+    "tiny-persistent-8": (TINY, "persistent", 9, 8, 0, False),
+    "tiny-int4-16": (synth.TINY_INT4, "graph", 7, 16, 0, False),
+    "tiny-int4-1": (synth.TINY_INT4, "persistent", 7, 1, 0, False),
+    "tiny-q8-6": (synth.TINY_Q8, "auto", 5, 6, 0, False),
+    # past 512 cached positions each row runs the split-K decode attention
+    "tiny-long-7": (TINY_LONG, "graph", 600, 7, 0, False),
+    "int4-long-lora-bf16kv-9": (INT4_LONG, "graph", 700, 9, 8, True),
+    "int4-long-persistent-16": (INT4_LONG, "persistent", 650, 16, 0, False),
 }
 
 
 @pytest.mark.parametrize("case", list(CASES))
 def test_verify_rows_against_oracle(torch_cuda, case):
+    import decoder_only_token_amd as qd
+    from gpu_util import lora_to_device
     torch = torch_cuda
-    shape, path, plen, m = CASES[case]
+    shape, path, plen, m, rank, kv16 = CASES[case]
     log(f"verify {case}")
     w = synth.make_weights(shape, seed=61, random_gains=True)
-    oracle = OracleModel(shape, w)
-    dec = make(torch, shape, path)
+    lora = synth.make_lora(shape, rank, seed=68) if rank else None
+    oracle = OracleModel(shape, w, lora=lora, lora_alpha=16.0, kv_bf16=kv16)
+    dec = make(torch, shape, path, max_prefill=max(32, plen), lora_rank_max=rank,
+               kv_format=qd.QD_KV_BF16 if kv16 else qd.QD_KV_F32)
     dw = to_device(w)
     torch.cuda.synchronize()
     dec.load_weights(dw)
+    if lora:
+        dec.set_lora(lora_to_device(lora), rank, 16.0)
     prompt = synth.make_prompt(shape.vocab, plen, seed=62)
     toks = synth.make_prompt(shape.vocab, m, seed=63)
     V = shape.vocab
