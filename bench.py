@@ -449,7 +449,9 @@ def dtype_of(shape, path):
         w = ("int4 group-128 projection weights x fp16 scales; " +
              ("int8 matrix-core products against the input split into three 7-bit pieces (error <= 2^-21 of the "
               "largest input of a wave's groups)" if path == "persistent" else
-              "codes widened in registers, f32 products (GEMV); bf16 hi/lo matrix-core products (prefill)"))
+              "int8 matrix-core products against the input split into three 7-bit pieces (error <= 2^-20 of the "
+              "row's largest input) for o_proj, gate/up and down, codes widened in registers with f32 products for "
+              "q|k|v (GEMV); bf16 hi/lo matrix-core products (prefill)"))
     else:
         w = "bf16 weights, matrix-core GEMV with the input as bf16 hi/lo halves (16 significant bits)"
     return (w + "; bf16 tied embedding and LoRA factors; f32 accumulation, residual and KV cache" +

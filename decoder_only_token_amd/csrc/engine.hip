@@ -450,7 +450,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
     enqueue_attention(h, l, T);
     for (int t0 = 0, tt = tile(nq * d); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      if (q4)
+      if (q4 && tn == 1 &&
+          q4m_gemv(s, L.co, L.so, H, nq * d, h->o + (size_t)t0 * nq * d, nullptr, 0.f, nullptr, h->x + (size_t)t0 * H, 1)) {
+      } else if (q4)
         launch_gemv_q4(s, L.co, L.so, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
                        h->x + (size_t)t0 * H, H, 1, h->ncu);
       else if (q8)
@@ -462,7 +464,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
     }
     for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      if (q4)
+      if (q4 && tn == 1 &&
+          q4m_gateup(s, L.cg, L.sg, L.cu, L.su, I, H, h->x + (size_t)t0 * H, L.mlp_norm, c.rms_eps, h->act + (size_t)t0 * I)) {
+      } else if (q4)
         launch_gemv_gateup_q4(s, L.cg, L.sg, L.cu, L.su, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
                               h->act + (size_t)t0 * I, I, h->ncu);
       else if (q8)
@@ -474,7 +478,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
     }
     for (int t0 = 0, tt = tile(I); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      if (q4)
+      if (q4 && tn == 1 &&
+          q4m_gemv(s, L.cd, L.sd, H, I, h->act + (size_t)t0 * I, nullptr, 0.f, nullptr, h->x + (size_t)t0 * H, 1)) {
+      } else if (q4)
         launch_gemv_q4(s, L.cd, L.sd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
                        h->x + (size_t)t0 * H, H, 1, h->ncu);
       else if (q8)

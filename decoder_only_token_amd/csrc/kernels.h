@@ -90,6 +90,14 @@ void launch_gemm_q4(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* 
 // ncu = compute units, used to size the grid).
 void launch_quantize_q4(hipStream_t s, const uint16_t* src, int nrows, int K, uint8_t* codes, uint16_t* scales);
 int q4_gemv_t_tile(int K);
+// Single-row (decode) int4 GEMVs on the int8 matrix cores, the input split into
+// three 7-bit pieces (error <= 2^-20 of the row's largest input); false when
+// the shape is not covered (K not a multiple of 128 or above 12288; gate/up:
+// K above 2048).
+bool q4m_gemv(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x,
+              const float* gain, float eps, const float* bias, float* y, int accumulate);
+bool q4m_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su, int N,
+                int K, const float* x, const float* gain, float eps, float* a);
 void launch_gemv_q4(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
                     int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate,
                     int ncu,

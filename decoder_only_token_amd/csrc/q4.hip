@@ -436,6 +436,238 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_q4(const uint8_t* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Single-row int4 GEMV on the int8 matrix cores (decode).  A block owns R =
+// 16 / RG output rows of NS matrices (1, or 2 for gate and up); its W waves
+// take the rows' 128-column groups RG at a time (a super-slot; super-slot gs to
+// wave gs % W).  The input row h (gain * x / rms(x) for the normed
+// projections) is written as y = u (a + b / 128 + c / 16384) with one power of
+// two u per block (its largest |y| lies in [32 u, 64 u)) and a, b, c the
+// rounded seven-bit digits: |error| <= u / 32768, at most 2^-20 of the row's
+// largest input.  In v_mfma_i32_16x16x64_i8, B column n is row n % R of the
+// block over group RG gs + n / R (its codes, 16 q, exact), and A row 4 p + j
+// is piece p of the input over group RG gs + j (rows with p = 3 or j >= RG,
+// and groups past K, read a record of zeros); so D[4 p + n / R][n] is piece
+// p's dot product for column n, in lanes 16 p + n.  A super-slot is two such
+// products, over the even and the odd columns.  The pieces' sums are weighted
+// (1, 2^-7, 2^-14, times u / 16), added across lanes with the row swaps, and
+// the W waves' and RG sub-groups' partials of each row added in a fixed order.
+// LDS layout per group: [parity e][piece p][quarter q][16 bytes], byte 4 m + t
+// of quarter q being column 128 g + 32 q + 8 m + 2 t + e.
+constexpr int kGroupBytes = 384;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Low bytes of four words, packed (w0 in byte 0).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u);  // [w0.b0, w1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(w3, w2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+template <int NS, int W, int MS, int MI, int RG>
+__global__ __launch_bounds__(64 * W) void k_gemv_q4m(const uint8_t* __restrict__ C0, const uint16_t* __restrict__ S0,
+                                                      const uint8_t* __restrict__ C1, const uint16_t* __restrict__ S1,
+                                                      int N, int K, const float* __restrict__ x,
+                                                      const float* __restrict__ gain, float eps,
+                                                      const float* __restrict__ bias, float* __restrict__ y,
+                                                      int accumulate) {
+  constexpr int NT = 64 * W, R = 16 / RG;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float red[W];
+  __shared__ float part[W][NS][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, quarter = lane >> 4;
+  const int ng = K / 128, nss = (ng + RG - 1) / RG, r0 = blockIdx.x * R;
+  const int row = min(r0 + l16 % R, N - 1), sub = l16 / R;
+  // ---- 1. the input (and gains): items of 8 columns, item i = tid + NT j,
+  // requested before the codes (reads past K are zeros)
+  f32x4 xv[MI][2], gv[MI][2];
+  {
+    const __amdgpu_buffer_rsrc_t rx = byte_record(x, K * 4);
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const int off = (tid + NT * j) * 32;
+      xv[j][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+      xv[j][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0));
+    }
+    if (gain) {
+      const __amdgpu_buffer_rsrc_t rg = byte_record(gain, K * 4);
+#pragma unroll
+      for (int j = 0; j < MI; ++j) {
+        const int off = (tid + NT * j) * 32;
+        gv[j][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+        gv[j][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, off + 16, 0, 0));
+      }
+    }
+  }
+  // ---- 2. the lane's codes and scales: row `row`, quarter `quarter` of
+  // group RG gs + sub (past K: the record's zeros)
+  u32x4 cw[NS][MS];
+  uint16_t sw[NS][MS];
+  {
+    const __amdgpu_buffer_rsrc_t rc0 = byte_record(C0, N * (K / 2)), rs0 = byte_record(S0, N * ng * 2);
+    const __amdgpu_buffer_rsrc_t rc1 = byte_record(NS == 2 ? C1 : C0, N * (K / 2));
+    const __amdgpu_buffer_rsrc_t rs1 = byte_record(NS == 2 ? S1 : S0, N * ng * 2);
+#pragma unroll
+    for (int j = 0; j < MS; ++j) {
+      const int g = (wave + W * j) * RG + sub;
+      int oc = g < ng ? row * (K / 2) + g * 64 + quarter * 16 : kPastRecord;
+      int os = g < ng ? (row * ng + g) * 2 : kPastRecord;
+      asm volatile("" : "+v"(oc), "+v"(os));  // (opaque: one load each, no branch)
+      cw[0][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc0, oc, 0, 2 /* streamed */));
+      sw[0][j] = __builtin_amdgcn_raw_buffer_load_b16(rs0, os, 0, 0);
+      if (NS == 2) {
+        cw[NS - 1][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc1, oc, 0, 2));
+        sw[NS - 1][j] = __builtin_amdgcn_raw_buffer_load_b16(rs1, os, 0, 0);
+      }
+    }
+  }
+  // ---- 3. the row's RMS scale, h, its largest magnitude and u
+  float r = 1.f;
+  if (gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < MI; ++j)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 v = xv[j][hh];
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+    float t = wave_sum(ss);
+    if (lane == 0) red[wave] = t;
+    __syncthreads();
+    t = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) t += red[w];
+    r = 1.0f / sqrtf(t / (float)K + eps);
+    __syncthreads();
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int j = 0; j < MI; ++j)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4 v = xv[j][hh];
+      if (gain) v = v * r * gv[j][hh];
+      xv[j][hh] = v;
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) mx = fmaxf(mx, red[w]);
+  const int E = (int)((__float_as_uint(mx) >> 23) & 0xFF);  // mx in [2^(E-127), 2^(E-126))
+  const bool live = E >= 6;  // inputs below 2^-121 (or all zero) are taken as zero
+  const float up = __uint_as_float((uint32_t)(live ? 259 - E : 127) << 23);  // 1 / u = 2^(132 - E)
+  const float u16 = live ? ldexpf(1.0f, E - 136) : 0.f;                    // u / 16
+  // ---- 4. the pieces into LDS.  v + 1.5 * 2^23 holds rint(v) in its low
+  // mantissa bits (|v| <= 64), so its low byte is the digit, two's complement.
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    const int it = tid + NT * j, col = it * 8;
+    if (col < K) {
+      const float kMagic = 12582912.0f;
+      const float yv[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                           xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+      uint32_t dg[3][8];  // [piece][column]: the digit in the low byte
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float v = live ? yv[k] * up : 0.f;  // |v| < 64, exact
+        const float ta = v + kMagic, ra = (v - (ta - kMagic)) * 128.0f;
+        const float tb = ra + kMagic, rb = (ra - (tb - kMagic)) * 128.0f;
+        const float tc = rb + kMagic;
+        dg[0][k] = __float_as_uint(ta);
+        dg[1][k] = __float_as_uint(tb);
+        dg[2][k] = __float_as_uint(tc);
+      }
+      const int g = col >> 7, qq = (col >> 5) & 3, m = (col >> 3) & 3;
+      uint8_t* d = lds + g * kGroupBytes + qq * 16 + m * 4;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        *reinterpret_cast<uint32_t*>(d + p * 64) = pack_low_bytes(dg[p][0], dg[p][2], dg[p][4], dg[p][6]);
+        *reinterpret_cast<uint32_t*>(d + 192 + p * 64) = pack_low_bytes(dg[p][1], dg[p][3], dg[p][5], dg[p][7]);
+      }
+    }
+  }
+  if (tid < kGroupBytes / 16)  // the record of zeros
+    reinterpret_cast<u32x4*>(lds + ng * kGroupBytes)[tid] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  // ---- 5. the super-slots on the matrix cores
+  const int ap = l16 >> 2, aj = l16 & 3;  // this lane's A row: piece ap of sub-group aj
+  const bool plane = ap < 3 && aj < RG;
+  const int abase = ap * 64 + quarter * 16, azero = ng * kGroupBytes;
+  float tot[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) tot[s] = 0.f;
+#pragma unroll
+  for (int j = 0; j < MS; ++j) {
+    const int gs = wave + W * j;
+    if (gs < nss) {  // wave-uniform
+      const int ga = gs * RG + aj;
+      const int ao = plane && ga < ng ? ga * kGroupBytes + abase : azero;
+      const u32x4 ae = *reinterpret_cast<const u32x4*>(lds + ao);
+      const u32x4 aod = *reinterpret_cast<const u32x4*>(lds + ao + 192);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 w = cw[s][j];
+        u32x4 be, bo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          be[k] = ((w[k] << 4) ^ 0x88888880u) & 0xF0F0F0F0u;
+          bo[k] = (w[k] ^ 0x88888888u) & 0xF0F0F0F0u;
+        }
+        i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, ae),
+                                                          __builtin_bit_cast(i32x4, be), i32x4{0, 0, 0, 0}, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, aod), __builtin_bit_cast(i32x4, bo),
+                                                    acc, 0, 0, 0);
+        const int dv = RG == 1 ? acc.x : RG == 2 ? (sub ? acc.y : acc.x)
+                                                 : (sub == 0 ? acc.x : sub == 1 ? acc.y : sub == 2 ? acc.z : acc.w);
+        tot[s] = fmaf((float)dv, f16_bits_to_f(sw[s][j]), tot[s]);
+      }
+    }
+  }
+  // ---- 6. pieces weighted and added across the lane groups; the partials
+  const float pw = (lane < 16 ? 1.0f : lane < 32 ? 0.0078125f : lane < 48 ? 6.103515625e-05f : 0.0f) * u16;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float v = tot[s] * pw;
+    auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float v2 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2), false, false);
+    const float v4 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    if (lane < 16) part[wave][s][lane] = v4;
+  }
+  __syncthreads();
+  if (tid < R && r0 + tid < N) {
+    float t[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      t[s] = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w)
+#pragma unroll
+        for (int jj = 0; jj < RG; ++jj) t[s] += part[w][s][tid + R * jj];
+    }
+    const int n = r0 + tid;
+    if (NS == 2) {
+      y[n] = silu_f(t[0]) * t[NS - 1];
+    } else {
+      const float v = t[0] + (bias ? bias[n] : 0.f);
+      y[n] = accumulate ? y[n] + v : v;
+    }
+  }
+}
+
+template <int NS, int W, int MS, int MI, int RG>
+void launch_q4m(hipStream_t s, const uint8_t* c0, const uint16_t* s0, const uint8_t* c1, const uint16_t* s1, int N,
+                int K, const float* x, const float* gain, float eps, const float* bias, float* y, int accumulate) {
+  const size_t lds = (size_t)(K / 128 + 1) * kGroupBytes;
+  hipLaunchKernelGGL((k_gemv_q4m<NS, W, MS, MI, RG>), dim3((N + 16 / RG - 1) / (16 / RG)), dim3(64 * W), lds, s, c0,
+                     s0, c1, s1, N, K, x, gain, eps, bias, y, accumulate);
+}
+
 // Output rows per wave: as many as max_rpw while the grid (four waves per
 // block) still gives every CU at least two blocks.
 int q4_rpw(int N, int ncu, int max_rpw) {
@@ -506,6 +738,29 @@ void gateup_q4_t(hipStream_t s, dim3 grid, size_t lds, const uint8_t* cg, const 
 }
 
 }  // namespace
+
+// Single-row GEMVs on the matrix cores: false when the shape is not covered
+// (the caller then uses the f32 GEMV).  Rows per block: 8 when that gives
+// every CU a block or K is long, else 4 (more blocks for short matrices).
+bool q4m_gemv(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x,
+              const float* gain, float eps, const float* bias, float* y, int accumulate) {
+  const int ng = K / 128;
+  if (K % 128 || ng > 96) return false;
+  if (ng > 16)
+    launch_q4m<1, 8, 6, 3, 2>(s, codes, scales, nullptr, nullptr, N, K, x, gain, eps, bias, y, accumulate);
+  else if ((N + 7) / 8 >= 256)
+    launch_q4m<1, 8, 1, 1, 2>(s, codes, scales, nullptr, nullptr, N, K, x, gain, eps, bias, y, accumulate);
+  else
+    launch_q4m<1, 4, 1, 1, 4>(s, codes, scales, nullptr, nullptr, N, K, x, gain, eps, bias, y, accumulate);
+  return true;
+}
+
+bool q4m_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su, int N,
+                int K, const float* x, const float* gain, float eps, float* a) {
+  if (K % 128 || K > 2048) return false;
+  launch_q4m<2, 4, 4, 1, 1>(s, cg, sg, cu, su, N, K, x, gain, eps, nullptr, a, 0);
+  return true;
+}
 
 int q4_gemv_t_tile(int K) {
   int t = (16384 - 64) / q4_stride(K);  // staged rows (plus the reduction slots) within 64 KiB of LDS
