@@ -656,45 +656,78 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
 }
 
 // o_h = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M} over the splits that hold
-// positions, in split order.  grid (nq, D / 32), block 256: 32 dims x 8 split
-// classes (s mod 8), summed in class order at the end.
+// positions.  grid (nq, D / 32), block 256: 32 dims x 8 split classes (s mod 8).
+// Every thread requests its splits' m, l and o in one go (indices clamped to
+// the S written splits, so no load waits on the step state), keeps those
+// that hold positions, and merges them in registers, 8 U splits per pass;
+// the classes are then merged in class order.
 constexpr int kMaxSplits = 1024;
+
+// (m, l, o) <- the merge of (m, l, o) and (mc, lc, oc); a side with no
+// position (m = -inf, l = o = 0) weighs e^-inf = 0, with no branch.
+__device__ __forceinline__ void merge_into(float& m, float& l, float& o, float mc, float lc, float oc) {
+  const float mn = fmaxf(m, mc), mr = fmaxf(mn, -3.0e38f);
+  const float a = __expf(m - mr), b = __expf(mc - mr);
+  l = l * a + lc * b;
+  o = o * a + oc * b;
+  m = mn;
+}
 
 __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restrict__ part, int S, int cmin,
                                                            const DevState* __restrict__ st, int row,
                                                            float* __restrict__ o_out) {
-  __shared__ float f[kMaxSplits];
-  __shared__ float red[8];
-  __shared__ float acc_s[8][33];
+  constexpr int U = 16;
+  __shared__ float mm[8], ll[8], oo[8][33];
   const int h = blockIdx.x, tid = threadIdx.x;
-  const int ctx = st->pos + row + 1;
-  const int C = split_len(ctx, S, cmin);
-  const int s_act = min(S, (ctx + C - 1) / C);
-  const float* base = part + (size_t)h * S * (D + 2);
-  float m = -INFINITY;
-  for (int s = tid; s < s_act; s += 256) m = fmaxf(m, base[(size_t)s * (D + 2)]);
-  const float M = block_max_256(m, red);
-  float lsum = 0.f;
-  for (int s = tid; s < s_act; s += 256) {
-    const float e = __expf(base[(size_t)s * (D + 2)] - M);
-    f[s] = e;
-    lsum = fmaf(base[(size_t)s * (D + 2) + 1], e, lsum);
-  }
-  const float Lt = block_sum_256(lsum, red);  // its barrier also publishes f[]
   const int d = blockIdx.y * 32 + (tid & 31), sg = tid >> 5;
-  float a = 0.f;
-#pragma unroll 4
-  for (int s = sg; s < s_act; s += 8) a = fmaf(f[s], base[(size_t)s * (D + 2) + 2 + d], a);
-  acc_s[sg][tid & 31] = a;
+  const float* base = part + (size_t)h * S * (D + 2);
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8 * U) {  // uniform
+    float mv[U], lv[U], ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* ps = base + (size_t)min(s0 + sg + 8 * u, S - 1) * (D + 2);
+      mv[u] = ps[0];
+      lv[u] = ps[1];
+      ov[u] = ps[2 + d];
+    }
+    // (read here, after the loads are requested: the step state is not
+    // waited for before them)
+    const int ctx = *reinterpret_cast<const volatile int*>(&st->pos) + row + 1;
+    const int C = split_len(ctx, S, cmin);
+    const int s_act = min(S, (ctx + C - 1) / C);
+    float mc = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + sg + 8 * u >= s_act) {  // a split with no position: its words are stale, not read
+        mv[u] = -INFINITY;
+        lv[u] = ov[u] = 0.f;
+      }
+      mc = fmaxf(mc, mv[u]);
+    }
+    float lc = 0.f, oc = 0.f;
+    const float mref = fmaxf(mc, -3.0e38f);  // finite: a masked split weighs e^-inf = 0, with no branch
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float e = __expf(mv[u] - mref);
+      lc = fmaf(lv[u], e, lc);
+      oc = fmaf(ov[u], e, oc);
+    }
+    merge_into(m, l, o, mc, lc, oc);
+  }
+  if ((tid & 31) == 0) {
+    mm[sg] = m;
+    ll[sg] = l;
+  }
+  oo[sg][tid & 31] = o;
   __syncthreads();
   if (sg == 0) {
-    float o = 0.f;
+    float M = mm[0], L = ll[0], O = oo[0][tid];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o += acc_s[k][tid & 31];
-    o_out[(size_t)h * D + d] = o / Lt;
+    for (int k = 1; k < 8; ++k) merge_into(M, L, O, mm[k], ll[k], oo[k][tid]);
+    o_out[(size_t)h * D + d] = O / L;
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Causal attention for a prefill of T >= 2 rows (flash style).  Query row t
