@@ -343,24 +343,33 @@ def synth_shape(name):
 
 def job_c4(stream, steps=20, warmup=5):
     """qwen2.5-3b-int4 (4096 positions): decode at the end of the context on
-    the persistent step, with its roofline and measured traffic."""
+    the captured graph (its default path) and on the persistent step (with
+    its measured traffic), each with its roofline."""
     import synth
     import torch
     wl = synth.WORKLOADS["qwen2.5-3b-int4"]
     dw = synth.make_weights_device(wl.shape)
-    dec = make_decoder(wl, "persistent", stream, dw)
+    res = {}
+    for path in ("graph", "persistent"):
+        dec = make_decoder(wl, path, stream, dw)
+        d = decode_at_end(dec, wl, stream, steps, warmup)
+        dec.close()
+        torch.cuda.synchronize()
+        us = d["event_ms"] * 1e3 / steps
+        ach = d["bytes_per_step"] / (us * 1e-6) / 1e9
+        res[path] = {"decode_path": path, "decode_tok_s": round(steps / d["wall_s"], 2),
+                     "decode_step_us": round(us, 2), "decode_context": [d["ctx_first"], d["ctx_last"]],
+                     "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(ach / HBM_PEAK_GBS, 4),
+                                  "traffic": measured_traffic(wl.name) if path == "persistent" else None,
+                                  "kernel": ("k_decode_persistent (one launch = one decode step)"
+                                             if path == "persistent" else "decode step (captured graph)")}}
     del dw
-    d = decode_at_end(dec, wl, stream, steps, warmup)
-    dec.close()
-    torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    us = d["event_ms"] * 1e3 / steps
-    ach = d["bytes_per_step"] / (us * 1e-6) / 1e9
-    return {"workload": wl.name, "decode_path": "persistent", "decode_tok_s": round(steps / d["wall_s"], 2),
-            "decode_step_us": round(us, 2), "decode_context": [d["ctx_first"], d["ctx_last"]],
-            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
-                         "kernel": "k_decode_persistent (one launch = one decode step)"}}
+    out = {"workload": wl.name}
+    out.update(res["graph"])
+    out["persistent"] = res["persistent"]
+    return out
 
 
 def job_kv_bf16(wl, stream, dw, dl, steps=20, warmup=5):
@@ -473,9 +482,10 @@ def main():
     shape = wl.shape
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
-    # auto: the persistent step, except with an adapter at the long context,
-    # where the captured graph's split-K attention over every CU is faster
-    path = ("graph" if wl.lora_rank or wl.shape.weight_format == 2 else "persistent") if args.path == "auto" \
+    # auto: the persistent step for bf16 weights without an adapter; the
+    # captured graph otherwise (int4 single-row projections on the int8
+    # matrix cores, split-K attention over every CU; Q8_0 runs only there)
+    path = ("graph" if wl.lora_rank or wl.shape.weight_format != 0 else "persistent") if args.path == "auto" \
         else args.path
     dw = synth.make_weights_device(shape)
     dl = synth.make_lora_device(shape, wl.lora_rank) if wl.lora_rank else None

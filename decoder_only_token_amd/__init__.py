@@ -131,10 +131,12 @@ class QdError(RuntimeError):
 def make_config(shape, max_prefill: int, lora_rank_max: int = 0, max_pos: Optional[int] = None,
                 decode_path: Optional[int] = None, kv_format: int = QD_KV_F32) -> QdConfig:
     """Fill a QdConfig from any object with the model-shape attribute names.
-    decode_path None: the persistent step, or the graph for Q8_0 weights (the
-    only path they run on)."""
+    decode_path None: the persistent step for bf16 weights; the graph for int4
+    weights (faster on the graph, where their single-row projections run on
+    the int8 matrix cores over every CU) and for Q8_0 weights (the only path
+    they run on)."""
     if decode_path is None:
-        decode_path = QD_DECODE_GRAPH if int(shape.weight_format) == QD_W_Q8_0 else QD_DECODE_PERSISTENT
+        decode_path = QD_DECODE_PERSISTENT if int(shape.weight_format) == QD_W_BF16 else QD_DECODE_GRAPH
     c = QdConfig()
     c.struct_size = ctypes.sizeof(QdConfig)
     c.abi_version = QD_ABI_VERSION
