@@ -377,6 +377,10 @@ __device__ __forceinline__ void norm_rope_regs(float a, float b, bool gain, floa
   out[l + 64] = b * c + a * s;
 }
 
+// Row stride (floats) of the waves' partial outputs in LDS: 64 values and 4 of
+// padding, so that the 16 rows written or read at once fall on distinct banks.
+constexpr int kOredStride = 68;
+
 template <bool LORA, typename KVT>
 __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ qkv, const float* __restrict__ qn,
                                                       const float* __restrict__ kn, float eps,
@@ -386,27 +390,21 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
                                                       float* __restrict__ part, LoraUp lu) {
   constexpr int G = 8;
   const int g = blockIdx.x, sp = blockIdx.y;
-  const int ctx = st->pos + row + 1, pos = ctx - 1;  // (row: of a batch of new rows)
-  const int C = split_len(ctx, S, cmin);
-  const int p_begin = sp * C;
-  if (p_begin >= ctx) return;  // the merge reads only the splits that hold positions
-  const int p_end = min(p_begin + C, ctx);
 
   __shared__ __align__(16) float qs[G * D];
   __shared__ __align__(16) float ps[G * TP];  // scores [head][position]
   __shared__ __align__(16) float pt[TP * G];  // probabilities [position][head]
   __shared__ __align__(16) float cs[G];       // per-head rescale of this tile
   __shared__ __align__(16) float kv_new[2 * D];
-  __shared__ __align__(16) float ored[4 * 16 * 64];  // the waves' partial outputs
+  __shared__ __align__(16) float ored[4 * 16 * kOredStride];  // the waves' partial outputs
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float* grp = qkv + (size_t)g * (G + 2) * D;
-  const bool owns_new = p_end == ctx;
-  const bool kvw = owns_new && wave == 3;  // wave 3 finishes the new row's k and v
 
-  // ---- 1. everything the q side reads (lane: dims lane and lane + 64 of q
-  // heads wave and wave + 4; wave 3 also of the new k and v), requested
-  // before the K/V rows so that waiting for it never waits for them
+  // ---- 1. what the q side reads that does not depend on the step's position
+  // (lane: dims lane and lane + 64 of q heads wave and wave + 4; wave 3 also
+  // of the new k and v), requested first: the step state is read after it and
+  // the K/V rows after both, so that no wait for one waits for a later one
   float qa[2], qb[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -415,13 +413,12 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
     qb[i] = grp[j * D + lane + 64];
   }
   float ka = 0.f, kb = 0.f, va = 0.f, vb = 0.f;
-  if (kvw) {
+  if (wave == 3) {
     ka = grp[G * D + lane];
     kb = grp[G * D + lane + 64];
     va = grp[(G + 1) * D + lane];
     vb = grp[(G + 1) * D + lane + 64];
   }
-  const float cth = cos_t[(size_t)pos * (D / 2) + lane], sth = sin_t[(size_t)pos * (D / 2) + lane];
   const float gq0 = qn ? qn[lane] : 1.f, gq1 = qn ? qn[lane + 64] : 1.f;
   const float gk0 = kn ? kn[lane] : 1.f, gk1 = kn ? kn[lane + 64] : 1.f;
   // adapter (q += s B_q u_q, v += s B_v u_v, "EMBERGLASS (qwen-webgpu-lora)
@@ -432,6 +429,9 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
   f32x4 uq[2 * NPRE], uv[2 * NPRE];
   const int r = lu.r;
   const bool r8 = (r & 7) == 0;
+  int zoff = 0;
+  asm volatile("" : "+v"(zoff));  // (u through a per-lane address: vector loads, no scalar wait)
+  const float* uu = lu.u + zoff;
   if (LORA && r8) {
 #pragma unroll
     for (int c = 0; c < NPRE; ++c) {
@@ -442,17 +442,28 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
           bqa[i][c] = *reinterpret_cast<const u32x4*>(lu.bq + row * r + 8 * c);
           bqb[i][c] = *reinterpret_cast<const u32x4*>(lu.bq + (row + 64) * r + 8 * c);
         }
-        if (kvw) {
+        if (wave == 3) {
           bva[c] = *reinterpret_cast<const u32x4*>(lu.bv + ((size_t)g * D + lane) * r + 8 * c);
           bvb[c] = *reinterpret_cast<const u32x4*>(lu.bv + ((size_t)g * D + lane + 64) * r + 8 * c);
         }
-        uq[2 * c] = *reinterpret_cast<const f32x4*>(lu.u + 8 * c);
-        uq[2 * c + 1] = *reinterpret_cast<const f32x4*>(lu.u + 8 * c + 4);
-        uv[2 * c] = *reinterpret_cast<const f32x4*>(lu.u + r + 8 * c);
-        uv[2 * c + 1] = *reinterpret_cast<const f32x4*>(lu.u + r + 8 * c + 4);
+        uq[2 * c] = *reinterpret_cast<const f32x4*>(uu + 8 * c);
+        uq[2 * c + 1] = *reinterpret_cast<const f32x4*>(uu + 8 * c + 4);
+        uv[2 * c] = *reinterpret_cast<const f32x4*>(uu + r + 8 * c);
+        uv[2 * c + 1] = *reinterpret_cast<const f32x4*>(uu + r + 8 * c + 4);
       }
     }
   }
+
+  // ---- the split and what depends on the position.  A split past the
+  // context holds no position: an empty record, no tile, and a partial the
+  // merge does not read.
+  const int ctx = st->pos + row + 1, pos = ctx - 1;  // (row: of a batch of new rows)
+  const int C = split_len(ctx, S, cmin);
+  const int p_begin = sp * C;
+  const int p_end = max(p_begin, min(p_begin + C, ctx));
+  const bool owns_new = p_begin < ctx && p_end == ctx;
+  const bool kvw = owns_new && wave == 3;  // wave 3 finishes the new row's k and v
+  const float cth = cos_t[(size_t)pos * (D / 2) + lane], sth = sin_t[(size_t)pos * (D / 2) + lane];
 
   // ---- 2. the split's first tile of K and V rows
   const int dg = (lane & 3) | ((lane >> 4) << 2);
@@ -625,7 +636,7 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
     }
   }
   if (((lane >> 2) & 3) == 0) {
-    float* dst = ored + (wave * 16 + dg) * 64;
+    float* dst = ored + (wave * 16 + dg) * kOredStride;
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
@@ -638,7 +649,7 @@ __global__ __launch_bounds__(256) void k_attn_decode8(const float* __restrict__ 
     const int h = d0 >> 6, dgo = (d0 & 63) >> 2;
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) o += *reinterpret_cast<const f32x4*>(ored + (w * 16 + dgo) * 64 + j * 8 + h * 4);
+    for (int w = 0; w < 4; ++w) o += *reinterpret_cast<const f32x4*>(ored + (w * 16 + dgo) * kOredStride + j * 8 + h * 4);
     float* dst = base + (size_t)j * S * (D + 2) + 2 + d0;
     dst[0] = o.x;
     dst[1] = o.y;
