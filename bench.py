@@ -58,29 +58,44 @@ KERNEL_SOURCES = ["decoder_only_token_amd/csrc/persist.hip", "decoder_only_token
                   "decoder_only_token_amd/csrc/common.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=None) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files or KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the persistent decode kernel from the committed
-    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor),
-    or None when there is none for this workload or the kernel has changed since."""
-    path = os.path.join(ROOT, "profiles", f"k_decode_persistent.{workload}.traffic.txt")
-    if not os.path.exists(path):
+def library_sources():
+    """Every source of the HIP library (the graph path's kernels), sorted."""
+    d = os.path.join(ROOT, "decoder_only_token_amd", "csrc")
+    return sorted(os.path.join("decoder_only_token_amd", "csrc", f) for f in os.listdir(d)
+                  if f.endswith((".hip", ".h")))
+
+
+def measured_traffic(workload: str, path: str = "persistent"):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel factor): per launch of the
+    persistent decode kernel, or per decode step (every kernel of the captured
+    graph) on the graph path; None when there is none for this workload or the
+    sources have changed since."""
+    if path == "graph":
+        fname, key, want = f"decode_graph.{workload}.traffic.txt", "library_source_sha256_16", \
+            kernel_source_hash(library_sources())
+    else:
+        fname, key, want = f"k_decode_persistent.{workload}.traffic.txt", "kernel_source_sha256_16", \
+            kernel_source_hash()
+    fpath = os.path.join(ROOT, "profiles", fname)
+    if not os.path.exists(fpath):
         return None
     kv = {}
-    with open(path) as fh:
+    with open(fpath) as fh:
         for line in fh:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get(key) != want:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -322,7 +337,7 @@ def job_06b(stream, path, workload="qwen3-0.6b"):
             "decode_step_us": round(us, 2), "bytes_per_step": round(byts),
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(wl.name) if path == "persistent" else None}}
+                         "traffic": measured_traffic(wl.name, path)}}
 
 
 def job_q8(stream):
@@ -361,7 +376,7 @@ def job_c4(stream, steps=20, warmup=5):
                      "decode_step_us": round(us, 2), "decode_context": [d["ctx_first"], d["ctx_last"]],
                      "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(ach / HBM_PEAK_GBS, 4),
-                                  "traffic": measured_traffic(wl.name) if path == "persistent" else None,
+                                  "traffic": measured_traffic(wl.name, path),
                                   "kernel": ("k_decode_persistent (one launch = one decode step)"
                                              if path == "persistent" else "decode step (captured graph)")}}
     del dw
@@ -519,7 +534,7 @@ def main():
         "decode_hbm_gbs_effective": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(wl.name) if path == "persistent" else None,
+                     "traffic": measured_traffic(wl.name, path),
                      "kernel": ("k_decode_persistent (one launch = one decode step)" if path == "persistent"
                                 else "decode step (captured graph of per-operation kernels)") +
                                f"; algorithmic bytes per step = {d['bytes_per_step']:.4g} (weights + LoRA + tied "
