@@ -131,6 +131,10 @@ struct qd_handle {
 
   hipGraphExec_t decode_exec = nullptr;
   hipGraph_t decode_graph = nullptr;
+  // speculative verification of m rows, captured per [attention mode][m]
+  // (mode 1: the split-K decode attention once per row, chosen by position)
+  hipGraphExec_t verify_exec[2][QD_VERIFY_MAX + 1] = {};
+  hipGraph_t verify_graph[2][QD_VERIFY_MAX + 1] = {};
 
   // persistent single-kernel decode step
   bool persistent = false;
@@ -287,6 +291,13 @@ void drop_decode_graph(qd_handle* h) {
   if (h->decode_graph) (void)hipGraphDestroy(h->decode_graph);
   h->decode_exec = nullptr;
   h->decode_graph = nullptr;
+  for (int a = 0; a < 2; ++a)
+    for (int m = 0; m <= QD_VERIFY_MAX; ++m) {
+      if (h->verify_exec[a][m]) (void)hipGraphExecDestroy(h->verify_exec[a][m]);
+      if (h->verify_graph[a][m]) (void)hipGraphDestroy(h->verify_graph[a][m]);
+      h->verify_exec[a][m] = nullptr;
+      h->verify_graph[a][m] = nullptr;
+    }
 }
 
 void free_all(qd_handle* h) {
@@ -421,6 +432,9 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
   const int NQKV = qkv_rows(c);
   const bool q4 = c.weight_format == QD_W_INT4_G128, q8 = c.weight_format == QD_W_Q8_0;
   auto tile = [&](int K) { return q4 ? q4_gemv_t_tile(K) : q8 ? q8_gemv_t_tile(K) : gemv_t_tile(K); };
+  // int4 o_proj, gate/up and down: row tiles of the matrix-core forms where
+  // they cover the width (one row: the single-row form)
+  auto tile4 = [&](int K, bool gu) { return q4 && q4mr_rows(K, gu) ? q4mr_rows(K, gu) : tile(K); };
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = h->layers[l];
     for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
@@ -448,10 +462,13 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
                        h->lora_scale, h->qkv, NQKV);
     }
     enqueue_attention(h, l, T);
-    for (int t0 = 0, tt = tile(nq * d); t0 < T; t0 += tt) {
+    for (int t0 = 0, tt = tile4(nq * d, false); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
       if (q4 && tn == 1 &&
           q4m_gemv(s, L.co, L.so, H, nq * d, h->o + (size_t)t0 * nq * d, nullptr, 0.f, nullptr, h->x + (size_t)t0 * H, 1)) {
+      } else if (q4 && tn > 1 &&
+                 q4mr_gemv(s, L.co, L.so, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
+                           h->x + (size_t)t0 * H, H, 1)) {
       } else if (q4)
         launch_gemv_q4(s, L.co, L.so, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
                        h->x + (size_t)t0 * H, H, 1, h->ncu);
@@ -462,9 +479,12 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
         launch_gemv_bf16(s, L.wo, H, nq * d, h->o + (size_t)t0 * nq * d, nq * d, tn, nullptr, 0.f, nullptr,
                          h->x + (size_t)t0 * H, H, 1, h->ncu);
     }
-    for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
+    for (int t0 = 0, tt = tile4(H, true); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      if (q4 && tn == 1 &&
+      if (q4 && tn > 1 &&
+          q4mr_gateup(s, L.cg, L.sg, L.cu, L.su, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
+                      h->act + (size_t)t0 * I, I)) {
+      } else if (q4 && tn == 1 &&
           q4m_gateup(s, L.cg, L.sg, L.cu, L.su, I, H, h->x + (size_t)t0 * H, L.mlp_norm, c.rms_eps, h->act + (size_t)t0 * I)) {
       } else if (q4)
         launch_gemv_gateup_q4(s, L.cg, L.sg, L.cu, L.su, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
@@ -476,10 +496,13 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
         launch_gemv_gateup_bf16(s, L.wg, L.wu, I, H, h->x + (size_t)t0 * H, H, tn, L.mlp_norm, c.rms_eps,
                                 h->act + (size_t)t0 * I, I, h->ncu);
     }
-    for (int t0 = 0, tt = tile(I); t0 < T; t0 += tt) {
+    for (int t0 = 0, tt = tile4(I, false); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
       if (q4 && tn == 1 &&
           q4m_gemv(s, L.cd, L.sd, H, I, h->act + (size_t)t0 * I, nullptr, 0.f, nullptr, h->x + (size_t)t0 * H, 1)) {
+      } else if (q4 && tn > 1 &&
+                 q4mr_gemv(s, L.cd, L.sd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
+                           h->x + (size_t)t0 * H, H, 1)) {
       } else if (q4)
         launch_gemv_q4(s, L.cd, L.sd, H, I, h->act + (size_t)t0 * I, I, tn, nullptr, 0.f, nullptr,
                        h->x + (size_t)t0 * H, H, 1, h->ncu);
@@ -923,20 +946,32 @@ int qd_verify(qd_handle* h, const int32_t* tokens_host, int32_t m, float* logits
   memcpy(h->tokens_pinned, tokens_host, (size_t)m * sizeof(int32_t));
   HIP_TRY(h, hipMemcpyAsync(h->tokens_dev, h->tokens_pinned, (size_t)m * sizeof(int32_t), hipMemcpyHostToDevice, s));
   // the m rows through the layers (a prefill of m rows), then the final norm
-  // and LM head of every row, up to lmhead_rows_per_pass rows per E pass
+  // and LM head of every row, up to lmhead_rows_per_pass rows per E pass; as
+  // one captured graph per (attention mode, m), every position read from the
+  // step state
   const int H = c.hidden, V = c.vocab, nblk = lmhead_blocks(V);
-  launch_embed(s, h->embed, h->tokens_dev, m, H, h->x);
-  if (m >= kGemmMinRows && c.weight_format != QD_W_Q8_0)
-    enqueue_layers_gemm(h, m, false);
-  else
-    enqueue_layers_gemv(h, m, false);
-  for (int t0 = 0, tr = lmhead_rows_per_pass(H); t0 < m; t0 += tr) {
-    const int tn = std::min(tr, m - t0);
-    launch_lmhead_rows_bf16(s, h->embed, V, H, h->x + (size_t)t0 * H, tn, h->final_norm, c.rms_eps,
-                            h->vlogits + (size_t)t0 * V, h->vpval + (size_t)t0 * nblk, h->vpidx + (size_t)t0 * nblk);
+  const int mode = m > 1 && m <= kRowAttnMaxRows && h->pos >= kRowAttnMinPos ? 1 : 0;
+  hipGraphExec_t& ex = h->verify_exec[mode][m];
+  if (!ex) {
+    HIP_TRY(h, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    launch_embed(s, h->embed, h->tokens_dev, m, H, h->x);
+    if (m >= kGemmMinRows && c.weight_format != QD_W_Q8_0)
+      enqueue_layers_gemm(h, m, false);
+    else
+      enqueue_layers_gemv(h, m, false);
+    for (int t0 = 0, tr = lmhead_rows_per_pass(H); t0 < m; t0 += tr) {
+      const int tn = std::min(tr, m - t0);
+      launch_lmhead_rows_bf16(s, h->embed, V, H, h->x + (size_t)t0 * H, tn, h->final_norm, c.rms_eps,
+                              h->vlogits + (size_t)t0 * V, h->vpval + (size_t)t0 * nblk, h->vpidx + (size_t)t0 * nblk);
+    }
+    launch_argmax_rows(s, h->vpval, h->vpidx, nblk, m, h->st, h->vchoice);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(s, &g);
+    if (e != hipSuccess) return h->set_err(QD_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    h->verify_graph[mode][m] = g;
+    HIP_TRY(h, hipGraphInstantiate(&ex, g, nullptr, nullptr, 0));
   }
-  launch_argmax_rows(s, h->vpval, h->vpidx, nblk, m, h->st, h->vchoice);
-  HIP_TRY(h, hipGetLastError());
+  HIP_TRY(h, hipGraphLaunch(ex, s));
   h->pos += m;
   h->have_token = true;
   h->cap_rows = 0;

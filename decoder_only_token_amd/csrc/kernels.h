@@ -98,6 +98,14 @@ bool q4m_gemv(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N
               const float* gain, float eps, const float* bias, float* y, int accumulate);
 bool q4m_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su, int N,
                 int K, const float* x, const float* gain, float eps, float* a);
+// The same for 2 to 4 rows at once (row strides ldx, ldy / lda); the codes are
+// read once for every row; false when the shape or T is not covered.
+// q4mr_rows: rows per launch for K columns (4), or 0 when not covered.
+int q4mr_rows(int K, bool gateup);
+bool q4mr_gemv(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
+               int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate);
+bool q4mr_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su, int N,
+                 int K, const float* x, int ldx, int T, const float* gain, float eps, float* a, int lda);
 void launch_gemv_q4(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
                     int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate,
                     int ncu,

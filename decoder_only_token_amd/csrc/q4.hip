@@ -668,6 +668,259 @@ void launch_q4m(hipStream_t s, const uint8_t* c0, const uint16_t* s0, const uint
                      s0, c1, s1, N, K, x, gain, eps, bias, y, accumulate);
 }
 
+// Multi-row form (2 to 4 input rows; speculative verification, short
+// prefills): the rows' digits sit side by side in LDS (input row t at
+// t * ng * 384 bytes) and every code and scale is requested once and serves
+// every row.  A row 4 p + j holds digit p of input row tg * TG + j % TG over
+// group RG s + j / TG (TG = 4 / RG rows per product, tg the product's row
+// pass), so D[4 p + (n / R) TG + i][n] is digit p's dot product of input
+// row tg TG + i with column n.  One power of two u per input row.
+template <int NS, int W, int MS, int MI, int RG>
+__global__ __launch_bounds__(64 * W) void k_gemv_q4mr(const uint8_t* __restrict__ C0, const uint16_t* __restrict__ S0,
+                                                       const uint8_t* __restrict__ C1, const uint16_t* __restrict__ S1,
+                                                       int N, int K, const float* __restrict__ x, int ldx, int T,
+                                                       const float* __restrict__ gain, float eps,
+                                                       const float* __restrict__ bias, float* __restrict__ y, int ldy,
+                                                       int accumulate) {
+  constexpr int NT = 64 * W, R = 16 / RG, TG = 4 / RG, TM = 4;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float red[W][TM];
+  __shared__ float part[W][NS][TM][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, quarter = lane >> 4;
+  const int ng = K / 128, nss = (ng + RG - 1) / RG, r0 = blockIdx.x * R;
+  const int row = min(r0 + l16 % R, N - 1), sub = l16 / R;
+  const int rstride = ng * kGroupBytes;  // LDS bytes of one input row's digits
+  // ---- 1. the T input rows (rows past T: an empty record, zeros) and gains
+  f32x4 xv[TM][MI][2], gv[MI][2];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    const __amdgpu_buffer_rsrc_t rx = byte_record(x + (size_t)min(t, T - 1) * ldx, t < T ? K * 4 : 0);
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const int off = (tid + NT * j) * 32;
+      xv[t][j][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+      xv[t][j][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0));
+    }
+  }
+  if (gain) {
+    const __amdgpu_buffer_rsrc_t rg = byte_record(gain, K * 4);
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const int off = (tid + NT * j) * 32;
+      gv[j][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+      gv[j][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, off + 16, 0, 0));
+    }
+  }
+  // ---- 2. the lane's codes and scales, as in the single-row form
+  u32x4 cw[NS][MS];
+  uint16_t sw[NS][MS];
+  {
+    const __amdgpu_buffer_rsrc_t rc0 = byte_record(C0, N * (K / 2)), rs0 = byte_record(S0, N * ng * 2);
+    const __amdgpu_buffer_rsrc_t rc1 = byte_record(NS == 2 ? C1 : C0, N * (K / 2));
+    const __amdgpu_buffer_rsrc_t rs1 = byte_record(NS == 2 ? S1 : S0, N * ng * 2);
+#pragma unroll
+    for (int j = 0; j < MS; ++j) {
+      const int g = (wave + W * j) * RG + sub;
+      int oc = g < ng ? row * (K / 2) + g * 64 + quarter * 16 : kPastRecord;
+      int os = g < ng ? (row * ng + g) * 2 : kPastRecord;
+      asm volatile("" : "+v"(oc), "+v"(os));  // (opaque: one load each, no branch)
+      cw[0][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc0, oc, 0, 2 /* streamed */));
+      sw[0][j] = __builtin_amdgcn_raw_buffer_load_b16(rs0, os, 0, 0);
+      if (NS == 2) {
+        cw[NS - 1][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc1, oc, 0, 2));
+        sw[NS - 1][j] = __builtin_amdgcn_raw_buffer_load_b16(rs1, os, 0, 0);
+      }
+    }
+  }
+  // ---- 3. every row's RMS scale, h, largest magnitude and u
+  float rr[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) rr[t] = 1.f;
+  if (gain) {
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < MI; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const f32x4 v = xv[t][j][hh];
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+      ss = wave_sum(ss);
+      if (lane == 0) red[wave][t] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      float q = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) q += red[w][t];
+      rr[t] = 1.0f / sqrtf(q / (float)K + eps);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < MI; ++j)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        f32x4 v = xv[t][j][hh];
+        if (gain) v = v * rr[t] * gv[j][hh];
+        xv[t][j][hh] = v;
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      }
+    mx = wave_max(mx);
+    if (lane == 0) red[wave][t] = mx;
+  }
+  __syncthreads();
+  float up[TM], u16[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    float mx = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) mx = fmaxf(mx, red[w][t]);
+    const int E = (int)((__float_as_uint(mx) >> 23) & 0xFF);
+    const bool live = E >= 6 && t < T;
+    up[t] = __uint_as_float((uint32_t)(live ? 259 - E : 127) << 23);
+    u16[t] = live ? ldexpf(1.0f, E - 136) : 0.f;
+    if (!live) up[t] = 0.f;
+  }
+  // ---- 4. every row's digits into LDS (as in the single-row form)
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t >= T) break;  // uniform
+#pragma unroll
+    for (int j = 0; j < MI; ++j) {
+      const int it = tid + NT * j, col = it * 8;
+      if (col < K) {
+        const float kMagic = 12582912.0f;
+        const float yv[8] = {xv[t][j][0].x, xv[t][j][0].y, xv[t][j][0].z, xv[t][j][0].w,
+                             xv[t][j][1].x, xv[t][j][1].y, xv[t][j][1].z, xv[t][j][1].w};
+        uint32_t dg[3][8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float v = yv[k] * up[t];  // |v| < 64, exact
+          const float ta = v + kMagic, ra = (v - (ta - kMagic)) * 128.0f;
+          const float tb = ra + kMagic, rb = (ra - (tb - kMagic)) * 128.0f;
+          const float tc = rb + kMagic;
+          dg[0][k] = __float_as_uint(ta);
+          dg[1][k] = __float_as_uint(tb);
+          dg[2][k] = __float_as_uint(tc);
+        }
+        const int g = col >> 7, qq = (col >> 5) & 3, m = (col >> 3) & 3;
+        uint8_t* d = lds + t * rstride + g * kGroupBytes + qq * 16 + m * 4;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          *reinterpret_cast<uint32_t*>(d + p * 64) = pack_low_bytes(dg[p][0], dg[p][2], dg[p][4], dg[p][6]);
+          *reinterpret_cast<uint32_t*>(d + 192 + p * 64) = pack_low_bytes(dg[p][1], dg[p][3], dg[p][5], dg[p][7]);
+        }
+      }
+    }
+  }
+  if (tid < kGroupBytes / 16)  // the record of zeros, after the T rows
+    reinterpret_cast<u32x4*>(lds + T * rstride)[tid] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  // ---- 5. the super-slots on the matrix cores, TG input rows per product
+  const int ap = l16 >> 2, aj = l16 & 3;  // A row: digit ap, sub-group aj / TG, row aj % TG of the pass
+  const int asub = aj / TG, at = aj % TG;
+  const int abase = ap * 64 + quarter * 16, azero = T * rstride;
+  float tot[NS][TM];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) tot[s][t] = 0.f;
+#pragma unroll
+  for (int j = 0; j < MS; ++j) {
+    const int gs = wave + W * j;
+    if (gs < nss) {  // wave-uniform
+      u32x4 be[NS], bo[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          be[s][k] = ((cw[s][j][k] << 4) ^ 0x88888880u) & 0xF0F0F0F0u;
+          bo[s][k] = (cw[s][j][k] ^ 0x88888888u) & 0xF0F0F0F0u;
+        }
+      const int ga = gs * RG + asub;
+#pragma unroll
+      for (int tg = 0; tg < TM / TG; ++tg) {
+        if (tg * TG >= T) break;  // uniform
+        const int ta = tg * TG + at;
+        const int ao = ap < 3 && ta < T && ga < ng ? ta * rstride + ga * kGroupBytes + abase : azero;
+        const u32x4 ae = *reinterpret_cast<const u32x4*>(lds + ao);
+        const u32x4 aod = *reinterpret_cast<const u32x4*>(lds + ao + 192);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, ae),
+                                                            __builtin_bit_cast(i32x4, be[s]), i32x4{0, 0, 0, 0}, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, aod), __builtin_bit_cast(i32x4, bo[s]),
+                                                      acc, 0, 0, 0);
+          const float sc = f16_bits_to_f(sw[s][j]);
+#pragma unroll
+          for (int i = 0; i < TG; ++i) {
+            const int c = sub * TG + i;  // this lane's column's result for row tg TG + i
+            const int dv = RG == 1 ? acc[i] : c == 0 ? acc.x : c == 1 ? acc.y : c == 2 ? acc.z : acc.w;
+            tot[s][tg * TG + i] = fmaf((float)dv, sc, tot[s][tg * TG + i]);
+          }
+        }
+      }
+    }
+  }
+  // ---- 6. digits weighted and added across the lane groups; the partials
+  const float pd = lane < 16 ? 1.0f : lane < 32 ? 0.0078125f : lane < 48 ? 6.103515625e-05f : 0.0f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t >= T) break;  // uniform
+      const float v = tot[s][t] * pd * u16[t];
+      auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      const float v2 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+      q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2), false, false);
+      const float v4 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+      if (lane < 16) part[wave][s][t][lane] = v4;
+    }
+  __syncthreads();
+  if (tid < R * T) {
+    const int t = tid / R, rr2 = tid % R, n = r0 + rr2;
+    if (n < N) {
+      float v[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        v[s] = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+#pragma unroll
+          for (int jj = 0; jj < RG; ++jj) v[s] += part[w][s][t][rr2 + R * jj];
+      }
+      float* yo = y + (size_t)t * ldy + n;
+      if (NS == 2) {
+        *yo = silu_f(v[0]) * v[NS - 1];
+      } else {
+        const float o = v[0] + (bias ? bias[n] : 0.f);
+        *yo = accumulate ? *yo + o : o;
+      }
+    }
+  }
+}
+
+template <int NS, int W, int MS, int MI, int RG>
+void launch_q4mr(hipStream_t s, const uint8_t* c0, const uint16_t* s0, const uint8_t* c1, const uint16_t* s1, int N,
+                 int K, const float* x, int ldx, int T, const float* gain, float eps, const float* bias, float* y,
+                 int ldy, int accumulate) {
+  const size_t lds = ((size_t)T * (K / 128) + 1) * kGroupBytes;
+  // (more than 64 KiB of LDS for the longest rows: allowed once per kernel)
+  static const bool big_lds = hipFuncSetAttribute((const void*)k_gemv_q4mr<NS, W, MS, MI, RG>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)(((size_t)4 * 96 + 1) * kGroupBytes)) == hipSuccess;
+  (void)big_lds;
+  hipLaunchKernelGGL((k_gemv_q4mr<NS, W, MS, MI, RG>), dim3((N + 16 / RG - 1) / (16 / RG)), dim3(64 * W), lds, s, c0,
+                     s0, c1, s1, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+}
+
 // Output rows per wave: as many as max_rpw while the grid (four waves per
 // block) still gives every CU at least two blocks.
 int q4_rpw(int N, int ncu, int max_rpw) {
@@ -759,6 +1012,30 @@ bool q4m_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint
                 int K, const float* x, const float* gain, float eps, float* a) {
   if (K % 128 || K > 2048) return false;
   launch_q4m<2, 4, 4, 1, 1>(s, cg, sg, cu, su, N, K, x, gain, eps, nullptr, a, 0);
+  return true;
+}
+
+// Rows per launch of the multi-row forms for K columns (0: not covered).
+int q4mr_rows(int K, bool gateup) { return K % 128 == 0 && K / 128 <= (gateup ? 16 : 96) ? 4 : 0; }
+
+// Multi-row forms (2 <= T <= 4 rows): false when the shape is not covered.
+bool q4mr_gemv(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
+               int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate) {
+  const int ng = K / 128;
+  if (!q4mr_rows(K, false) || T < 2 || T > 4) return false;
+  if (ng > 16)
+    launch_q4mr<1, 8, 6, 3, 2>(s, codes, scales, nullptr, nullptr, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+  else if ((N + 7) / 8 >= 256)
+    launch_q4mr<1, 8, 1, 1, 2>(s, codes, scales, nullptr, nullptr, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+  else
+    launch_q4mr<1, 4, 1, 1, 4>(s, codes, scales, nullptr, nullptr, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+  return true;
+}
+
+bool q4mr_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su, int N,
+                 int K, const float* x, int ldx, int T, const float* gain, float eps, float* a, int lda) {
+  if (!q4mr_rows(K, true) || T < 2 || T > 4) return false;
+  launch_q4mr<2, 4, 4, 1, 1>(s, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, nullptr, a, lda, 0);
   return true;
 }
 
