@@ -689,8 +689,12 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
                                                            float* __restrict__ o_out) {
   constexpr int U = 16;
   __shared__ float mm[8], ll[8], oo[8][33];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int h = blockIdx.x, tid = threadIdx.x, nqh = gridDim.x;
   const int d = blockIdx.y * 32 + (tid & 31), sg = tid >> 5;
+  // (grid z: the rows of a batch, their partials and outputs one after the
+  // other; the split geometry is that of the batch's last row, `row`)
+  part += (size_t)blockIdx.z * nqh * S * (D + 2);
+  o_out += (size_t)blockIdx.z * nqh * D;
   const float* base = part + (size_t)h * S * (D + 2);
   float m = -INFINITY, l = 0.f, o = 0.f;
   for (int s0 = 0; s0 < S; s0 += 8 * U) {  // uniform
@@ -749,7 +753,12 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
 // nearest even) and three products (hi.hi + hi.lo + lo.hi, the lo.lo term is
 // below f32 rounding of the result); accumulation is f32.
 //
-// grid (nkv, ceil(T / (64 / G))), block 256 = 4 waves.  A block owns 64 query
+// grid (nkv, ceil(T / (64 / G))), block 256 = 4 waves.  Split form (SPLIT,
+// short batches at long contexts): grid (nkv, ceil(T / (64 / G)) S), the
+// positions 0 .. pos + T - 1 cut into S splits of split_len(pos + T, S, cmin)
+// as the decode attention cuts them, and each block writes the partials
+// {m, l, o} of its query vectors over its split (part[(row nq + head) S +
+// split]) for k_attn_merge_decode.  A block owns 64 query
 // vectors of kv head g; wave w owns 16 of them (the A operand of S, kept in
 // registers for the whole kernel).  Per tile of 32 cache positions the block
 // stages K (row-major) and V (transposed) as bf16 halves in LDS; each wave
@@ -757,12 +766,13 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
 // (row maxima and sums over the 16 lanes that hold a row, by DPP), writes
 // P's halves to its own LDS slice in the A-operand layout, and accumulates
 // its 16 x 128 output tile.
-template <int G, typename KVT>
+template <int G, typename KVT, bool SPLIT>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restrict__ q, int T, int nq,
                                                            const KVT* __restrict__ Kc,
                                                            const KVT* __restrict__ Vc, int max_pos,
                                                            const DevState* __restrict__ st, float scale,
-                                                           float* __restrict__ o_out, int ldo) {
+                                                           float* __restrict__ o_out, int ldo, int S, int cmin,
+                                                           float* __restrict__ part) {
   constexpr int QV = 64, R = QV / G, BK = 32;
   constexpr int KS = D + 8;   // K row stride (bf16)
   constexpr int VS = BK + 8;  // V^T row stride (bf16)
@@ -773,10 +783,18 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;  // fragment row / column, k-quarter
   const int g = blockIdx.x;
-  const int t0 = (gridDim.y - 1 - blockIdx.y) * R;
+  const int tile = SPLIT ? blockIdx.y / S : gridDim.y - 1 - blockIdx.y, sp = SPLIT ? blockIdx.y % S : 0;
+  const int t0 = tile * R;
   const int pos0 = st->pos;
   const int nrows = min(R, T - t0);
   const int kv_end = pos0 + t0 + nrows;  // one past the last row's position
+  // positions of this block: all it sees, or its split of the batch's positions
+  int k_begin = 0, k_end = kv_end;
+  if (SPLIT) {
+    const int C = split_len(pos0 + T, S, cmin);
+    k_begin = min(sp * C, kv_end);
+    k_end = min(sp * C + C, kv_end);
+  }
 
   // this lane's query fragment: vector wave*16 + lr, dims 32 ks + 8 lq .. + 8
   bf16x8 qh[4], ql[4];
@@ -819,9 +837,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
   // staging map: positions 4 p4 .. + 3, dims 4 c4 .. + 3
   const int p4 = tid & 7, c4 = tid >> 3;
 
-  for (int k0 = 0; k0 < kv_end; k0 += BK) {
-    const int nk = min(BK, kv_end - k0);
-    f32x4 kr[4], vr[4];
+  // a tile's K and V rows are requested while the previous tile is computed
+  f32x4 kr[4], vr[4];
+  auto load_tile = [&](int k0) {
+    const int nk = min(BK, k_end - k0);
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
       const int p = 4 * p4 + pp;
@@ -831,6 +850,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
         vr[pp] = ld_kv4(Vg + (size_t)(k0 + p) * D + 4 * c4);
       }
     }
+  };
+  if (k_begin < k_end) load_tile(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += BK) {
+    const int nk = min(BK, k_end - k0);
     __syncthreads();  // the previous tile's K, V and P are consumed
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
@@ -856,6 +879,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
       *reinterpret_cast<u32x2*>(&Vth[(4 * c4 + i) * VS + 4 * p4]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
       *reinterpret_cast<u32x2*>(&Vtl[(4 * c4 + i) * VS + 4 * p4]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     }
+    if (k0 + BK < k_end) load_tile(k0 + BK);  // (kr, vr are staged: free)
     __syncthreads();
     // S = Q K^T: 16 queries x 32 positions (two 16 x 16 tiles)
     f32x4 sc[2];
@@ -909,6 +933,22 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
     }
   }
   // element e of oacc[dt]: row 4 lq + e, dim dt * 16 + lr
+  if (SPLIT) {  // the partials: m, l and o not divided by l
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = wave * 16 + 4 * lq + e, r = v / G, j = v % G;
+      if (r < nrows) {
+        float* dst = part + ((size_t)(t0 + r) * nq + g * G + j) * S * (D + 2) + (size_t)sp * (D + 2);
+        if (lr == 0) {
+          dst[0] = m[e];
+          dst[1] = l[e];
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) dst[2 + dt * 16 + lr] = oacc[dt][e];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int v = wave * 16 + 4 * lq + e, r = v / G, j = v % G;
@@ -972,11 +1012,11 @@ void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int 
   const dim3 grid(nkv, (T + 64 / G - 1) / (64 / G));
 #define QD_ATTN_PREFILL(G_)                                                                                        \
   if (kv_bf16)                                                                                                     \
-    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, uint16_t>), grid, dim3(256), 0, s, q, T, nq, (const uint16_t*)Kc,  \
-                       (const uint16_t*)Vc, max_pos, st, scale, o_out, ldo);                                        \
+    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, uint16_t, false>), grid, dim3(256), 0, s, q, T, nq,               \
+                       (const uint16_t*)Kc, (const uint16_t*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr);    \
   else                                                                                                             \
-    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, float>), grid, dim3(256), 0, s, q, T, nq, (const float*)Kc,        \
-                       (const float*)Vc, max_pos, st, scale, o_out, ldo)
+    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, float, false>), grid, dim3(256), 0, s, q, T, nq, (const float*)Kc, \
+                       (const float*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr)
   switch (G) {
     case 1: QD_ATTN_PREFILL(1); break;
     case 2: QD_ATTN_PREFILL(2); break;
@@ -986,4 +1026,29 @@ void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int 
   }
 #undef QD_ATTN_PREFILL
   (void)ncu;
+}
+
+void launch_attention_rows_split(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
+                                 int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part,
+                                 float* o_out) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const int G = nq / nkv;
+  const dim3 grid(nkv, ((T + 64 / G - 1) / (64 / G)) * S);
+#define QD_ATTN_ROWS(G_)                                                                                           \
+  if (kv_bf16)                                                                                                     \
+    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, uint16_t, true>), grid, dim3(256), 0, s, q, T, nq,                \
+                       (const uint16_t*)Kc, (const uint16_t*)Vc, max_pos, st, scale, nullptr, 0, S, cmin, part);   \
+  else                                                                                                             \
+    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, float, true>), grid, dim3(256), 0, s, q, T, nq, (const float*)Kc,  \
+                       (const float*)Vc, max_pos, st, scale, nullptr, 0, S, cmin, part)
+  switch (G) {
+    case 1: QD_ATTN_ROWS(1); break;
+    case 2: QD_ATTN_ROWS(2); break;
+    case 4: QD_ATTN_ROWS(4); break;
+    case 8: QD_ATTN_ROWS(8); break;
+    default: return;  // rejected by the host before any launch
+  }
+#undef QD_ATTN_ROWS
+  // the rows' merges (their split geometry: that of the last row)
+  hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32, T), dim3(256), 0, s, part, S, cmin, st, T - 1, o_out);
 }

@@ -24,8 +24,9 @@ namespace {
 
 constexpr int kDecodeMinSplit = 16;  // shortest split of the decode attention
 // batches of at most this many rows at positions from kRowAttnMinPos on run
-// the decode attention once per row instead of the prefill attention (which
-// spreads a batch over its query rows, few here, not over the positions)
+// the split form of the batch attention (its positions cut as the decode
+// attention cuts them) instead of the plain one (which spreads a batch over
+// its query rows, few here, not over the positions)
 constexpr int kRowAttnMaxRows = 16;
 constexpr int kRowAttnMinPos = 512;
 constexpr int kMaxStepsPerLaunch = 64;  // decode steps in one persistent launch (8-bit step tags, 200 ms waits)
@@ -357,14 +358,14 @@ void enqueue_attention(qd_handle* h, int l, int T) {
                             lo ? h->lora[l].bv : nullptr, h->lora_rank, h->lora_scale);
   } else if (T <= kRowAttnMaxRows && h->pos >= kRowAttnMinPos) {
     // a few rows at a long context (speculative verification, short prefills):
-    // the split-K decode attention once per row, in order, so that every row
-    // is spread over the CUs and sees the rows before it (the adapter's up
-    // products are already in the q|k|v rows)
-    for (int t = 0; t < T; ++t)
-      launch_attention_decode(s, h->qkv + (size_t)t * qkv_rows(c), L.q_norm, L.k_norm, c.rms_eps, h->rope_cos,
-                              h->rope_sin, nq, nkv, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos, h->st,
-                              h->dec_splits, kDecodeMinSplit, h->part, h->o + (size_t)t * nq * d, nullptr, nullptr,
-                              nullptr, 0, 0.f, t);
+    // QK-norm, RoPE and the cache rows of all of them, then one split-K pass
+    // over the positions for every row at once (the decode attention's splits,
+    // so the batch is spread over the CUs) and the rows' merges (the adapter's
+    // up products are already in the q|k|v rows)
+    launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
+                      h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16);
+    launch_attention_rows_split(s, h->q, T, nq, nkv, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos,
+                                h->st, h->dec_splits, kDecodeMinSplit, h->part, h->o);
   } else {
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
                       h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16);
@@ -607,7 +608,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   const size_t kv_elems = (size_t)c.n_layers * c.n_kv_heads * c.max_pos * d + 256 * d;
   const size_t kvf = c.kv_format == QD_KV_BF16 ? (kv_elems + 1) / 2 : kv_elems;
   h->dec_splits = attn_decode_splits(c.max_pos, c.n_kv_heads, h->ncu, kDecodeMinSplit);
-  h->part_floats = (size_t)c.n_q_heads * h->dec_splits * (d + 2);
+  h->part_floats = (size_t)kRowAttnMaxRows * c.n_q_heads * h->dec_splits * (d + 2);  // a short batch's rows
   // the caches carry 256 rows of tail padding: the persistent decode step reads
   // (and ignores) up to 192 positions past the end of a split
   if ((rc = dev_alloc(h, &h->Kc, kvf)) || (rc = dev_alloc(h, &h->Vc, kvf)) ||

@@ -54,6 +54,12 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
                              const uint16_t* lora_bv = nullptr, int lora_r = 0, float lora_scale = 0.f, int row = 0);
 
 // Causal attention of T >= 2 new rows (attn.hip), rows at positions pos .. pos + T - 1.
+// Split form for short batches at long contexts: the positions cut into S
+// splits as the decode attention cuts them, partials part[T][nq][S][D + 2],
+// merged into o_out[T][nq D]; q and the new rows' K/V already in place.
+void launch_attention_rows_split(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
+                                 int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part,
+                                 float* o_out);
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
                               int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu);
 
