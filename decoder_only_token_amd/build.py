@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqd.so")
-SOURCES = ["kernels.hip", "gemm.hip", "q4.hip", "q8.hip", "attn.hip", "lora.hip", "persist.hip", "sample.hip", "engine.hip"]
+SOURCES = ["kernels.hip", "gemm.hip", "q4.hip", "q8.hip", "attn.hip", "persist.hip", "sample.hip", "engine.hip"]
 ARCH = "gfx950"
 
 

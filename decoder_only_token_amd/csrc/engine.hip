@@ -350,6 +350,15 @@ void enqueue_attention(qd_handle* h, int l, int T) {
   const int d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
   const int kv16 = c.kv_format == QD_KV_BF16;
   const Layer& L = h->layers[l];
+  LoraRows lr;  // a batch's adapter up products: added by the QK-norm / RoPE pass
+  if (h->lora_rank) {
+    lr.u = h->lu;
+    lr.ldu = 2 * h->lora_rank;
+    lr.bq = h->lora[l].bq;
+    lr.bv = h->lora[l].bv;
+    lr.r = h->lora_rank;
+    lr.scale = h->lora_scale;
+  }
   if (T == 1) {  // QK-norm, RoPE, the adapter's up products and the cache write happen inside the decode attention
     const bool lo = h->lora_rank > 0;
     launch_attention_decode(s, h->qkv, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin, nq, nkv,
@@ -358,17 +367,17 @@ void enqueue_attention(qd_handle* h, int l, int T) {
                             lo ? h->lora[l].bv : nullptr, h->lora_rank, h->lora_scale);
   } else if (T <= kRowAttnMaxRows && h->pos >= kRowAttnMinPos) {
     // a few rows at a long context (speculative verification, short prefills):
-    // QK-norm, RoPE and the cache rows of all of them, then one split-K pass
-    // over the positions for every row at once (the decode attention's splits,
-    // so the batch is spread over the CUs) and the rows' merges (the adapter's
-    // up products are already in the q|k|v rows)
+    // the adapter, QK-norm, RoPE and the cache rows of all of them, then one
+    // split-K pass over the positions for every row at once (the decode
+    // attention's splits, so the batch is spread over the CUs) and the rows'
+    // merges
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
-                      h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16);
+                      h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16, lr);
     launch_attention_rows_split(s, h->q, T, nq, nkv, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos,
                                 h->st, h->dec_splits, kDecodeMinSplit, h->part, h->o);
   } else {
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
-                      h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16);
+                      h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16, lr);
     launch_attention_prefill(s, h->q, T, nq, nkv, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos, h->st,
                              h->o, nq * d, h->ncu);
   }
@@ -390,12 +399,10 @@ void enqueue_layers_gemm(qd_handle* h, int T, bool capture) {
     else
       launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, L.wqkv, nullptr, NQKV, L.bqkv, h->qkv, NQKV, h->gws,
                        h->gws_floats, h->ncu);
-    if (h->lora_rank) {  // the normed input halves are still in xh / xl
+    if (h->lora_rank) {  // the down products (the normed input halves are still in xh / xl)
       const int r2 = 2 * h->lora_rank;
       launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, h->lora[l].a, nullptr, r2, nullptr, h->lu, r2, h->gws,
                        h->gws_floats, h->ncu);
-      launch_lora_up(s, h->lu, r2, T, h->lora_rank, h->lora[l].bq, h->lora[l].bv, nq, c.n_kv_heads, d,
-                     h->lora_scale, h->qkv, NQKV);
     }
     enqueue_attention(h, l, T);
     launch_split_rows(s, h->o, nq * d, T, nq * d, nullptr, 0.f, h->xh, h->xl);
@@ -436,14 +443,22 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
   // int4 o_proj, gate/up and down: row tiles of the matrix-core forms where
   // they cover the width (one row: the single-row form)
   auto tile4 = [&](int K, bool gu) { return q4 && q4mr_rows(K, gu) ? q4mr_rows(K, gu) : tile(K); };
+  // int4 q|k|v of a batch on the matrix cores (the adapter's down products
+  // then run as their own bf16 GEMV); of a single row, the VALU GEMV with the
+  // down products riding along as bf16 rows
+  const bool qkv_mr = q4 && T > 1 && q4mr_rows(H, false);
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& L = h->layers[l];
-    for (int t0 = 0, tt = tile(H); t0 < T; t0 += tt) {
+    for (int t0 = 0, tt = qkv_mr ? q4mr_rows(H, false) : tile(H); t0 < T; t0 += tt) {
       const int tn = std::min(tt, T - t0);
-      if (q4)  // with an adapter, its down products u = [A_q; A_v] h ride along as bf16 rows
+      const bool xr = h->lora_rank && !qkv_mr;
+      if (qkv_mr && tn > 1 &&
+          q4mr_gemv(s, L.cqkv, L.sqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
+                    h->qkv + (size_t)t0 * NQKV, NQKV, 0)) {
+      } else if (q4)
         launch_gemv_q4(s, L.cqkv, L.sqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
-                       h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu, h->lora_rank ? h->lora[l].a : nullptr,
-                       2 * h->lora_rank, h->lu + (size_t)t0 * 2 * h->lora_rank, 2 * h->lora_rank);
+                       h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu, xr ? h->lora[l].a : nullptr, xr ? 2 * h->lora_rank : 0,
+                       h->lu + (size_t)t0 * 2 * h->lora_rank, 2 * h->lora_rank);
       else if (q8)
         launch_gemv_q8(s, L.qqkv, L.sqkv, NQKV, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, L.bqkv,
                        h->qkv + (size_t)t0 * NQKV, NQKV, 0, h->ncu);
@@ -453,14 +468,13 @@ void enqueue_layers_gemv(qd_handle* h, int T, bool capture) {
     }
     if (h->lora_rank) {
       const int r2 = 2 * h->lora_rank;
-      for (int t0 = 0, tt = gemv_t_tile(H); t0 < T && !q4; t0 += tt) {  // (int4: inside the q|k|v GEMV)
+      const bool own = qkv_mr && launch_lora_down_rows(s, h->lora[l].a, r2, H, h->x, H, T, L.attn_norm, c.rms_eps,
+                                                       h->lu, r2);
+      for (int t0 = 0, tt = gemv_t_tile(H); t0 < T && (!q4 || qkv_mr) && !own; t0 += tt) {  // (else inside the q|k|v GEMV)
         const int tn = std::min(tt, T - t0);
         launch_gemv_bf16(s, h->lora[l].a, r2, H, h->x + (size_t)t0 * H, H, tn, L.attn_norm, c.rms_eps, nullptr,
                          h->lu + (size_t)t0 * r2, r2, 0, h->ncu);
       }
-      if (T > 1)  // a decode step's up products are added by the attention blocks
-        launch_lora_up(s, h->lu, r2, T, h->lora_rank, h->lora[l].bq, h->lora[l].bv, nq, c.n_kv_heads, d,
-                       h->lora_scale, h->qkv, NQKV);
     }
     enqueue_attention(h, l, T);
     for (int t0 = 0, tt = tile4(nq * d, false); t0 < T; t0 += tt) {

@@ -38,9 +38,23 @@ void launch_argmax_rows(hipStream_t s, const float* part_val, const int32_t* par
 void launch_rewind_state(hipStream_t s, DevState* st, int n, int32_t token);
 void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* part_idx, int nparts, DevState* st,
                          int advance, int32_t* token_out);
+// The adapter's up products of a batch of rows: u [T][ldu] (u_q then u_v),
+// B_q [nq d][r], B_v [nkv d][r] bf16; u == nullptr: no adapter.
+struct LoraRows {
+  const float* u = nullptr;
+  int ldu = 0;
+  const uint16_t* bq = nullptr;
+  const uint16_t* bv = nullptr;
+  int r = 0;
+  float scale = 0.f;
+};
+// The adapter's down products of a batch (T <= 16 rows, K a multiple of 1024):
+// u[t][o] = A[o] . (gain * x_t / rms(x_t)), A bf16 [n][K]; false when not covered.
+bool launch_lora_down_rows(hipStream_t s, const uint16_t* A, int n, int K, const float* x, int ldx, int T,
+                           const float* gain, float eps, float* u, int ldu);
 void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq, int nkv, int d, const float* qn,
                        const float* kn, float eps, const float* cos_t, const float* sin_t, const DevState* st,
-                       float* q_out, void* Kc, void* Vc, int max_pos, int kv_bf16);
+                       float* q_out, void* Kc, void* Vc, int max_pos, int kv_bf16, const LoraRows& lr);
 // Decode attention for one new row (attn.hip), from the raw q|k|v projection
 // row (group-major): QK-norm (gains may be null), RoPE, the cache write of the
 // new k / v, then S splits of length max(cmin, ceil(ctx / S)); part holds
@@ -104,9 +118,9 @@ bool q4m_gemv(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N
               const float* gain, float eps, const float* bias, float* y, int accumulate);
 bool q4m_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su, int N,
                 int K, const float* x, const float* gain, float eps, float* a);
-// The same for 2 to 4 rows at once (row strides ldx, ldy / lda); the codes are
-// read once for every row; false when the shape or T is not covered.
-// q4mr_rows: rows per launch for K columns (4), or 0 when not covered.
+// The same for 2 to q4mr_rows(K) rows at once (row strides ldx, ldy / lda); the
+// codes are read once for every row; false when the shape or T is not covered.
+// q4mr_rows: rows per launch for K columns (8 or 4), or 0 when not covered.
 int q4mr_rows(int K, bool gateup);
 bool q4mr_gemv(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
                int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate);
@@ -132,7 +146,3 @@ void launch_gemv_gateup_q8(hipStream_t s, const int8_t* cg, const uint16_t* sg, 
                            int N, int K, const float* x, int ldx, int T, const float* gain, float eps, float* a,
                            int lda, int ncu);
 
-// LoRA up products (lora.hip): for rows t < T, q rows of the fused q|k|v
-// output += scale B_q u[t][0, r), v rows += scale B_v u[t][r, 2 r).
-void launch_lora_up(hipStream_t s, const float* u, int ldu, int T, int r, const uint16_t* Bq, const uint16_t* Bv,
-                    int nq, int nkv, int d, float scale, float* qkv, int ldqkv);

@@ -557,12 +557,67 @@ void launch_rewind_state(hipStream_t s, DevState* st, int n, int32_t token) {
 // group-major: [kv head g][q heads of g | k_g | v_g].  "Failed Star / fs" block figure:
 // QK-norm comes before RoPE.  Pairs are (j, j + d/2).
 // grid (T, nq + nkv), block d/2 threads (one per rotation pair).
+// The adapter's down products of a batch: u[t][o] = A[o] . (g * x_t / rms(x_t))
+// for rows o < n of A (bf16 [n][K]) and input rows t < T (T <= 16).  One
+// workgroup per row of A: every thread requests its columns of the A row,
+// the gains and every input row at once, then the T dot products and sums
+// of squares are reduced together.
+constexpr int kLoraDownMaxT = 16;
+__global__ __launch_bounds__(256) void k_lora_down_rows(const uint16_t* __restrict__ A, int K,
+                                                        const float* __restrict__ x, int ldx, int T,
+                                                        const float* __restrict__ gain, float eps,
+                                                        float* __restrict__ u, int ldu) {
+  __shared__ float red[4][2 * kLoraDownMaxT];
+  const int o = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float dot[kLoraDownMaxT], ss[kLoraDownMaxT];
+#pragma unroll
+  for (int t = 0; t < kLoraDownMaxT; ++t) dot[t] = ss[t] = 0.f;
+  for (int c0 = tid * 4; c0 < K; c0 += 1024) {  // 4 columns per thread and pass
+    const uint2 a2 = *reinterpret_cast<const uint2*>(A + (size_t)o * K + c0);
+    const f32x4 g4 = gain ? *reinterpret_cast<const f32x4*>(gain + c0) : f32x4{1.f, 1.f, 1.f, 1.f};
+    const f32x4 ag = f32x4{__uint_as_float(a2.x << 16), __uint_as_float(a2.x & 0xFFFF0000u),
+                           __uint_as_float(a2.y << 16), __uint_as_float(a2.y & 0xFFFF0000u)} * g4;
+#pragma unroll
+    for (int t = 0; t < kLoraDownMaxT; ++t) {
+      if (t >= T) break;  // uniform
+      const f32x4 v = *reinterpret_cast<const f32x4*>(x + (size_t)t * ldx + c0);
+      dot[t] += ag.x * v.x + ag.y * v.y + ag.z * v.z + ag.w * v.w;
+      ss[t] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kLoraDownMaxT; ++t) {
+    if (t >= T) break;
+    const float dsum = wave_sum(dot[t]), ssum = wave_sum(ss[t]);
+    if (lane == 0) {
+      red[wave][2 * t] = dsum;
+      red[wave][2 * t + 1] = ssum;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    float dsum = 0.f, ssum = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      dsum += red[w][2 * tid];
+      ssum += red[w][2 * tid + 1];
+    }
+    u[(size_t)tid * ldu + o] = dsum / sqrtf(ssum / (float)K + eps);
+  }
+}
+
+// sum_i B[i] u[i] over an adapter row of r bf16 values, in index order
+__device__ __forceinline__ float lora_dot(const uint16_t* __restrict__ B, const float* __restrict__ u, int r) {
+  float a = 0.f;
+  for (int i = 0; i < r; ++i) a = fmaf(bf16_to_f(B[i]), u[i], a);
+  return a;
+}
+
 template <typename KVT>
 __global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, int nkv, int d,
                              const float* __restrict__ qn, const float* __restrict__ kn, float eps,
                              const float* __restrict__ cos_t, const float* __restrict__ sin_t,
                              const DevState* __restrict__ st, float* __restrict__ q_out,
-                             KVT* __restrict__ Kc, KVT* __restrict__ Vc, int max_pos) {
+                             KVT* __restrict__ Kc, KVT* __restrict__ Vc, int max_pos, LoraRows lr) {
   const int t = blockIdx.x, head = blockIdx.y, j = threadIdx.x, half = d >> 1;
   const int pos = st->pos + t;
   const float* row = qkv + (size_t)t * ldqkv;
@@ -573,6 +628,13 @@ __global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, i
   const float* grp = row + (size_t)g * (G + 2) * d;
   const float* src = is_q ? grp + (head % G) * d : grp + G * d;
   float a = src[j], b = src[j + half];
+  // adapter (q += s B_q u_q, v += s B_v u_v, before QK-norm and RoPE;
+  // "EMBERGLASS (qwen-webgpu-lora) README", LoRA sections)
+  const float* ut = lr.u ? lr.u + (size_t)t * lr.ldu : nullptr;
+  if (ut && is_q) {
+    a += lr.scale * lora_dot(lr.bq + ((size_t)head * d + j) * lr.r, ut, lr.r);
+    b += lr.scale * lora_dot(lr.bq + ((size_t)head * d + j + half) * lr.r, ut, lr.r);
+  }
   const float* gain = is_q ? qn : kn;
   if (gain) {
     __shared__ float red[4];
@@ -599,20 +661,31 @@ __global__ void k_qk_rope_kv(const float* __restrict__ qkv, int ldqkv, int nq, i
     st_kv(kr + j, ra);
     st_kv(kr + j + half, rb);
     const float* vsrc = grp + (G + 1) * d;
+    float va = vsrc[j], vb = vsrc[j + half];
+    if (ut) {
+      va += lr.scale * lora_dot(lr.bv + ((size_t)g * d + j) * lr.r, ut + lr.r, lr.r);
+      vb += lr.scale * lora_dot(lr.bv + ((size_t)g * d + j + half) * lr.r, ut + lr.r, lr.r);
+    }
     KVT* vr = Vc + ((size_t)g * max_pos + pos) * d;
-    st_kv(vr + j, vsrc[j]);
-    st_kv(vr + j + half, vsrc[j + half]);
+    st_kv(vr + j, va);
+    st_kv(vr + j + half, vb);
   }
 }
 
 void launch_qk_rope_kv(hipStream_t s, const float* qkv, int ldqkv, int T, int nq, int nkv, int d, const float* qn,
                        const float* kn, float eps, const float* cos_t, const float* sin_t, const DevState* st,
-                       float* q_out, void* Kc, void* Vc, int max_pos, int kv_bf16) {
+                       float* q_out, void* Kc, void* Vc, int max_pos, int kv_bf16, const LoraRows& lr) {
   if (kv_bf16)
     hipLaunchKernelGGL(k_qk_rope_kv<uint16_t>, dim3(T, nq + nkv), dim3(d / 2), 0, s, qkv, ldqkv, nq, nkv, d, qn, kn,
-                       eps, cos_t, sin_t, st, q_out, (uint16_t*)Kc, (uint16_t*)Vc, max_pos);
+                       eps, cos_t, sin_t, st, q_out, (uint16_t*)Kc, (uint16_t*)Vc, max_pos, lr);
   else
     hipLaunchKernelGGL(k_qk_rope_kv<float>, dim3(T, nq + nkv), dim3(d / 2), 0, s, qkv, ldqkv, nq, nkv, d, qn, kn, eps,
-                       cos_t, sin_t, st, q_out, (float*)Kc, (float*)Vc, max_pos);
+                       cos_t, sin_t, st, q_out, (float*)Kc, (float*)Vc, max_pos, lr);
 }
 
+bool launch_lora_down_rows(hipStream_t s, const uint16_t* A, int n, int K, const float* x, int ldx, int T,
+                           const float* gain, float eps, float* u, int ldu) {
+  if (T < 1 || T > kLoraDownMaxT || K % 1024) return false;
+  hipLaunchKernelGGL(k_lora_down_rows, dim3(n), dim3(256), 0, s, A, K, x, ldx, T, gain, eps, u, ldu);
+  return true;
+}

@@ -668,21 +668,22 @@ void launch_q4m(hipStream_t s, const uint8_t* c0, const uint16_t* s0, const uint
                      s0, c1, s1, N, K, x, gain, eps, bias, y, accumulate);
 }
 
-// Multi-row form (2 to 4 input rows; speculative verification, short
-// prefills): the rows' digits sit side by side in LDS (input row t at
+// Multi-row form (2 to TM input rows, TM = 8, or 4 for the longest rows;
+// speculative verification, short prefills): the rows' digits sit side by
+// side in LDS (input row t at
 // t * ng * 384 bytes) and every code and scale is requested once and serves
 // every row.  A row 4 p + j holds digit p of input row tg * TG + j % TG over
 // group RG s + j / TG (TG = 4 / RG rows per product, tg the product's row
 // pass), so D[4 p + (n / R) TG + i][n] is digit p's dot product of input
 // row tg TG + i with column n.  One power of two u per input row.
-template <int NS, int W, int MS, int MI, int RG>
+template <int NS, int W, int MS, int MI, int RG, int TM>
 __global__ __launch_bounds__(64 * W) void k_gemv_q4mr(const uint8_t* __restrict__ C0, const uint16_t* __restrict__ S0,
                                                        const uint8_t* __restrict__ C1, const uint16_t* __restrict__ S1,
                                                        int N, int K, const float* __restrict__ x, int ldx, int T,
                                                        const float* __restrict__ gain, float eps,
                                                        const float* __restrict__ bias, float* __restrict__ y, int ldy,
                                                        int accumulate) {
-  constexpr int NT = 64 * W, R = 16 / RG, TG = 4 / RG, TM = 4;
+  constexpr int NT = 64 * W, R = 16 / RG, TG = 4 / RG;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ float red[W][TM];
   __shared__ float part[W][NS][TM][16];
@@ -907,17 +908,18 @@ __global__ __launch_bounds__(64 * W) void k_gemv_q4mr(const uint8_t* __restrict_
   }
 }
 
-template <int NS, int W, int MS, int MI, int RG>
+template <int NS, int W, int MS, int MI, int RG, int TM>
 void launch_q4mr(hipStream_t s, const uint8_t* c0, const uint16_t* s0, const uint8_t* c1, const uint16_t* s1, int N,
                  int K, const float* x, int ldx, int T, const float* gain, float eps, const float* bias, float* y,
                  int ldy, int accumulate) {
   const size_t lds = ((size_t)T * (K / 128) + 1) * kGroupBytes;
-  // (more than 64 KiB of LDS for the longest rows: allowed once per kernel)
-  static const bool big_lds = hipFuncSetAttribute((const void*)k_gemv_q4mr<NS, W, MS, MI, RG>,
+  // (more than 64 KiB of LDS for the longest rows: allowed once per kernel;
+  // at most 4 rows of 96 groups or 8 rows of 16)
+  static const bool big_lds = hipFuncSetAttribute((const void*)k_gemv_q4mr<NS, W, MS, MI, RG, TM>,
                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                                   (int)(((size_t)4 * 96 + 1) * kGroupBytes)) == hipSuccess;
   (void)big_lds;
-  hipLaunchKernelGGL((k_gemv_q4mr<NS, W, MS, MI, RG>), dim3((N + 16 / RG - 1) / (16 / RG)), dim3(64 * W), lds, s, c0,
+  hipLaunchKernelGGL((k_gemv_q4mr<NS, W, MS, MI, RG, TM>), dim3((N + 16 / RG - 1) / (16 / RG)), dim3(64 * W), lds, s, c0,
                      s0, c1, s1, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
 }
 
@@ -1015,27 +1017,37 @@ bool q4m_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint
   return true;
 }
 
-// Rows per launch of the multi-row forms for K columns (0: not covered).
-int q4mr_rows(int K, bool gateup) { return K % 128 == 0 && K / 128 <= (gateup ? 16 : 96) ? 4 : 0; }
+// Rows per launch of the multi-row forms for K columns: 8 up to 2048 columns,
+// 4 up to 12288 (not gate/up: LDS), 0 when not covered.
+int q4mr_rows(int K, bool gateup) {
+  if (K % 128) return 0;
+  return K / 128 <= 16 ? 8 : !gateup && K / 128 <= 96 ? 4 : 0;
+}
 
-// Multi-row forms (2 <= T <= 4 rows): false when the shape is not covered.
+// Multi-row forms (2 <= T <= q4mr_rows(K) rows): false when the shape is not covered.
 bool q4mr_gemv(hipStream_t s, const uint8_t* codes, const uint16_t* scales, int N, int K, const float* x, int ldx,
                int T, const float* gain, float eps, const float* bias, float* y, int ldy, int accumulate) {
   const int ng = K / 128;
-  if (!q4mr_rows(K, false) || T < 2 || T > 4) return false;
-  if (ng > 16)
-    launch_q4mr<1, 8, 6, 3, 2>(s, codes, scales, nullptr, nullptr, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
-  else if ((N + 7) / 8 >= 256)
-    launch_q4mr<1, 8, 1, 1, 2>(s, codes, scales, nullptr, nullptr, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
-  else
-    launch_q4mr<1, 4, 1, 1, 4>(s, codes, scales, nullptr, nullptr, N, K, x, ldx, T, gain, eps, bias, y, ldy, accumulate);
+  if (T < 2 || T > q4mr_rows(K, false)) return false;
+  // (the 8-row forms hold more registers: fewer workgroups per CU; up to 4
+  // rows the 4-row forms)
+#define QD_Q4MR(W_, MS_, MI_, RG_, TM_)                                                                          \
+  launch_q4mr<1, W_, MS_, MI_, RG_, TM_>(s, codes, scales, nullptr, nullptr, N, K, x, ldx, T, gain, eps, bias, y, \
+                                         ldy, accumulate)
+  if (ng > 16) QD_Q4MR(8, 6, 3, 2, 4);
+  else if ((N + 7) / 8 >= 256 && T <= 4) QD_Q4MR(8, 1, 1, 2, 4);
+  else if ((N + 7) / 8 >= 256) QD_Q4MR(8, 1, 1, 2, 8);
+  else if (T <= 4) QD_Q4MR(4, 1, 1, 4, 4);
+  else QD_Q4MR(4, 1, 1, 4, 8);
+#undef QD_Q4MR
   return true;
 }
 
 bool q4mr_gateup(hipStream_t s, const uint8_t* cg, const uint16_t* sg, const uint8_t* cu, const uint16_t* su, int N,
                  int K, const float* x, int ldx, int T, const float* gain, float eps, float* a, int lda) {
-  if (!q4mr_rows(K, true) || T < 2 || T > 4) return false;
-  launch_q4mr<2, 4, 4, 1, 1>(s, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, nullptr, a, lda, 0);
+  if (T < 2 || T > q4mr_rows(K, true)) return false;
+  if (T <= 4) launch_q4mr<2, 4, 4, 1, 1, 4>(s, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, nullptr, a, lda, 0);
+  else launch_q4mr<2, 4, 4, 1, 1, 8>(s, cg, sg, cu, su, N, K, x, ldx, T, gain, eps, nullptr, a, lda, 0);
   return true;
 }
 
