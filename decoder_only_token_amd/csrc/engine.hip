@@ -329,9 +329,9 @@ void enqueue_forward(qd_handle* h, int T, const int32_t* tok, bool capture) {
     enqueue_layers_gemv(h, T, capture);
   }
   float* xf_cap = capture ? h->cap + (size_t)(c.n_layers + 1) * c.max_prefill * H : nullptr;
-  launch_lmhead_bf16(s, h->embed, c.vocab, H, h->x + (size_t)(T - 1) * H, h->final_norm, c.rms_eps, h->logits,
-                     h->pval, h->pidx, xf_cap);
-  launch_argmax_final(s, h->pval, h->pidx, lmhead_blocks(c.vocab), h->st, T, nullptr);
+  const int nparts = launch_lmhead_bf16(s, h->embed, c.vocab, H, h->x + (size_t)(T - 1) * H, h->final_norm,
+                                       c.rms_eps, h->logits, h->pval, h->pidx, xf_cap);
+  launch_argmax_final(s, h->pval, h->pidx, nparts, h->st, T, nullptr);
   if (capture)
     (void)hipMemcpyAsync(xf_cap + H, h->logits, (size_t)c.vocab * 4, hipMemcpyDeviceToDevice, s);
 }

@@ -25,8 +25,10 @@ void launch_gemv_bf16(hipStream_t s, const uint16_t* W, int N, int K, const floa
 void launch_gemv_gateup_bf16(hipStream_t s, const uint16_t* Wg, const uint16_t* Wu, int N, int K, const float* x,
                              int ldx, int T, const float* gain, float eps, float* a, int lda, int ncu);
 int lmhead_blocks(int V);
-void launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
-                        float* logits, float* part_val, int32_t* part_idx, float* xf_out);
+// Final norm + tied LM head of one row with per-workgroup argmax partials;
+// returns the number of partials written (<= lmhead_blocks(V)).
+int launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
+                       float* logits, float* part_val, int32_t* part_idx, float* xf_out);
 // Speculative verification: final norm + LM head for T <= lmhead_rows_per_pass(H)
 // rows with per-row logits [T][V] and argmax partials [T][lmhead_blocks(V)];
 // the per-row choices (advancing the step state by T); dropping positions.

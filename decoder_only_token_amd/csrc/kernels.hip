@@ -352,14 +352,114 @@ __global__ __launch_bounds__(256) void k_lmhead_bf16(const uint16_t* __restrict_
   }
 }
 
+// Streaming form of the LM head (hidden a multiple of 512, HP = hidden / 512):
+// a fixed grid of at most 512 workgroups, each staging the normed row once and
+// owning RB contiguous vocabulary rows (RB a multiple of 16); wave w takes
+// the 4-row chunks w, w + 4, ... of them, the next chunk's rows requested
+// while the current one is reduced (rows past the workgroup's range read
+// zeros from a bounded buffer record, without memory traffic, so every
+// chunk issues the same loads and no wait is forced at a branch).
+constexpr int kLmPastRecord = 0x7FFFFFF0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lm_record(const void* p, int bytes) {
+  const uint64_t v = (uint64_t)p;
+  const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+template <int HP>
+__global__ __launch_bounds__(256) void k_lmhead_stream(const uint16_t* __restrict__ E, int V, int H, int RB,
+                                                       const float* __restrict__ x, const float* __restrict__ gain,
+                                                       float eps, float* __restrict__ logits,
+                                                       float* __restrict__ part_val, int32_t* __restrict__ part_idx,
+                                                       float* __restrict__ xf_out) {
+  extern __shared__ float smem[];
+  float* red = smem;
+  float* h = smem + 8;
+  __shared__ float bval[4];
+  __shared__ int32_t bidx[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int base = blockIdx.x * RB, rowend = min(V, base + RB), nrow = max(0, rowend - base);
+  const __amdgpu_buffer_rsrc_t re = lm_record(E + (size_t)min(base, V) * H, nrow * H * 2);
+  const int nch = RB / 16;  // 4-row chunks per wave
+  u32x4 wa[4][HP], wb[4][HP];
+  auto load = [&](u32x4 (&w)[4][HP], int j) {
+    const int r0 = (wave + 4 * j) * 4;  // first row of the chunk, in the workgroup's range
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int off = r0 + i < nrow ? ((r0 + i) * H + lane * 8) * 2 : kLmPastRecord;
+      asm volatile("" : "+v"(off));  // (opaque: one load each, no branch)
+#pragma unroll
+      for (int p = 0; p < HP; ++p)
+        w[i][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(re, off, p * 1024, 2 /* streamed */));
+    }
+  };
+  if (nch > 0) load(wa, 0);  // requested before the input is staged
+  stage_input(x, H, 1, H, gain, eps, h, red);
+  if (xf_out && blockIdx.x == 0)
+    for (int k = threadIdx.x; k < H; k += 256) xf_out[k] = h[k];
+  float best = -INFINITY;
+  int32_t bi = 0x7fffffff;
+  auto reduce = [&](u32x4 (&w)[4][HP], int j) {
+    const int r0 = (wave + 4 * j) * 4;
+    float acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = 0.f;
+#pragma unroll
+      for (int p = 0; p < HP; ++p) acc[i] += dot8(w[i][p], h + p * 512 + lane * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float sc = wave_sum(acc[i]);
+      if (r0 + i < nrow) {
+        const int n = base + r0 + i;
+        if (lane == 0) logits[n] = sc;
+        if (sc > best) { best = sc; bi = n; }  // rows visited in increasing id: ties keep the lowest
+      }
+    }
+  };
+  for (int j = 0; j < nch; j += 2) {  // uniform; chunks j (in wa) and j + 1 (in wb)
+    load(wb, j + 1);
+    reduce(wa, j);
+    load(wa, j + 2);
+    reduce(wb, j + 1);
+  }
+  if (lane == 0) { bval[wave] = best; bidx[wave] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bv = bval[0];
+    int32_t bj = bidx[0];
+    for (int w = 1; w < 4; ++w)
+      if (bval[w] > bv || (bval[w] == bv && bidx[w] < bj)) { bv = bval[w]; bj = bidx[w]; }
+    part_val[blockIdx.x] = bv;
+    part_idx[blockIdx.x] = bj;
+  }
+}
+
 int lmhead_blocks(int V) { return (V + 4 * LMHEAD_RPW - 1) / (4 * LMHEAD_RPW); }
 
-void launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
-                        float* logits, float* part_val, int32_t* part_idx, float* xf_out) {
-  dim3 grid(lmhead_blocks(V));
-  size_t lds = (8 + (size_t)H) * sizeof(float);
-  hipLaunchKernelGGL(k_lmhead_bf16, grid, dim3(256), lds, s, E, V, H, x, gain, eps, logits, part_val, part_idx,
-                     xf_out);
+int launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
+                       float* logits, float* part_val, int32_t* part_idx, float* xf_out) {
+  const size_t lds = (8 + (size_t)H) * sizeof(float);
+  const int hp = H / 512;
+  if (H % 512 == 0 && (hp == 1 || hp == 2 || hp == 4 || hp == 8) && (size_t)V * H * 2 < ((size_t)1 << 31)) {
+    const int grid = std::min(512, (V + 15) / 16);
+    const int RB = (V + grid * 16 - 1) / (grid * 16) * 16;
+#define QD_LM(HP_)                                                                                                \
+  hipLaunchKernelGGL(k_lmhead_stream<HP_>, dim3(grid), dim3(256), lds, s, E, V, H, RB, x, gain, eps, logits,     \
+                     part_val, part_idx, xf_out)
+    if (hp == 1) QD_LM(1);
+    else if (hp == 2) QD_LM(2);
+    else if (hp == 4) QD_LM(4);
+    else QD_LM(8);
+#undef QD_LM
+    return grid;
+  }
+  hipLaunchKernelGGL(k_lmhead_bf16, dim3(lmhead_blocks(V)), dim3(256), lds, s, E, V, H, x, gain, eps, logits, part_val,
+                     part_idx, xf_out);
+  return lmhead_blocks(V);
 }
 
 // ---------------------------------------------------------------------------
