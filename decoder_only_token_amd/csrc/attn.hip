@@ -744,6 +744,27 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
   }
 }
 
+// The batch attention's split partials merged: one thread per (row, head,
+// dim), over all S splits (every split's partials are written, those with no
+// visible position as m = -inf, l = o = 0), in split order.
+__global__ __launch_bounds__(256) void k_attn_merge_rows(const float* __restrict__ part, int S, int total,
+                                                         float* __restrict__ o_out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int d = i % D, th = i / D;  // th = row nq + head
+  const float* base = part + (size_t)th * S * (D + 2);
+  float M = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, base[(size_t)sp * (D + 2)]);
+  float L = 0.f, O = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    const float* ps = base + (size_t)sp * (D + 2);
+    const float e = __expf(ps[0] - M);
+    L = fmaf(ps[1], e, L);
+    O = fmaf(ps[2 + d], e, O);
+  }
+  o_out[(size_t)th * D + d] = O / L;
+}
+
 // ---------------------------------------------------------------------------
 // Causal attention for a prefill of T >= 2 rows (flash style).  Query row t
 // sits at position pos + t (pos = the step state's position) and sees cache
@@ -1005,10 +1026,28 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
   hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32), dim3(256), 0, s, part, S, cmin, st, row, o_out);
 }
 
+void launch_attention_rows_split_only(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc,
+                                      const void* Vc, int kv_bf16, int max_pos, const DevState* st, int S, int cmin,
+                                      float* part);
+
+int attn_prefill_splits(int T, int nq, int nkv, int ncu) {
+  const int blocks = nkv * ((T + 64 / (nq / nkv) - 1) / (64 / (nq / nkv)));
+  if (blocks >= ncu) return 1;
+  return std::min(16, (2 * ncu + blocks - 1) / blocks);
+}
+
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
-                              int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu) {
+                              int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu,
+                              float* part, int cmin) {
   const float scale = 1.0f / sqrtf((float)D);
   const int G = nq / nkv;
+  const int S = part ? attn_prefill_splits(T, nq, nkv, ncu) : 1;
+  if (S > 1 && ldo == nq * D) {  // fewer query tiles than CUs: the split form, then the merge
+    launch_attention_rows_split_only(s, q, T, nq, nkv, Kc, Vc, kv_bf16, max_pos, st, S, cmin, part);
+    const int total = T * nq * D;
+    hipLaunchKernelGGL(k_attn_merge_rows, dim3((total + 255) / 256), dim3(256), 0, s, part, S, total, o_out);
+    return;
+  }
   const dim3 grid(nkv, (T + 64 / G - 1) / (64 / G));
 #define QD_ATTN_PREFILL(G_)                                                                                        \
   if (kv_bf16)                                                                                                     \
@@ -1028,9 +1067,9 @@ void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int 
   (void)ncu;
 }
 
-void launch_attention_rows_split(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
-                                 int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part,
-                                 float* o_out) {
+void launch_attention_rows_split_only(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc,
+                                      const void* Vc, int kv_bf16, int max_pos, const DevState* st, int S, int cmin,
+                                      float* part) {
   const float scale = 1.0f / sqrtf((float)D);
   const int G = nq / nkv;
   const dim3 grid(nkv, ((T + 64 / G - 1) / (64 / G)) * S);
@@ -1049,6 +1088,12 @@ void launch_attention_rows_split(hipStream_t s, const float* q, int T, int nq, i
     default: return;  // rejected by the host before any launch
   }
 #undef QD_ATTN_ROWS
+}
+
+void launch_attention_rows_split(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
+                                 int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part,
+                                 float* o_out) {
+  launch_attention_rows_split_only(s, q, T, nq, nkv, Kc, Vc, kv_bf16, max_pos, st, S, cmin, part);
   // the rows' merges (their split geometry: that of the last row)
   hipLaunchKernelGGL(k_attn_merge_decode, dim3(nq, D / 32, T), dim3(256), 0, s, part, S, cmin, st, T - 1, o_out);
 }

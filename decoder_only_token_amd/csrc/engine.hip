@@ -379,7 +379,7 @@ void enqueue_attention(qd_handle* h, int l, int T) {
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
                       h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16, lr);
     launch_attention_prefill(s, h->q, T, nq, nkv, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos, h->st,
-                             h->o, nq * d, h->ncu);
+                             h->o, nq * d, h->ncu, h->part, kDecodeMinSplit);
   }
 }
 
@@ -622,7 +622,12 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
   const size_t kv_elems = (size_t)c.n_layers * c.n_kv_heads * c.max_pos * d + 256 * d;
   const size_t kvf = c.kv_format == QD_KV_BF16 ? (kv_elems + 1) / 2 : kv_elems;
   h->dec_splits = attn_decode_splits(c.max_pos, c.n_kv_heads, h->ncu, kDecodeMinSplit);
-  h->part_floats = (size_t)kRowAttnMaxRows * c.n_q_heads * h->dec_splits * (d + 2);  // a short batch's rows
+  // attention partials: a short batch's rows over the decode splits, or a
+  // prefill's rows over its splits (batches whose query tiles leave CUs idle)
+  size_t part_rows = (size_t)kRowAttnMaxRows * h->dec_splits;
+  for (int t = 2; t <= c.max_prefill; ++t)
+    part_rows = std::max(part_rows, (size_t)t * attn_prefill_splits(t, c.n_q_heads, c.n_kv_heads, h->ncu));
+  h->part_floats = part_rows * c.n_q_heads * (d + 2);
   // the caches carry 256 rows of tail padding: the persistent decode step reads
   // (and ignores) up to 192 positions past the end of a split
   if ((rc = dev_alloc(h, &h->Kc, kvf)) || (rc = dev_alloc(h, &h->Vc, kvf)) ||

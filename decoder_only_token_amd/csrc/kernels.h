@@ -76,8 +76,13 @@ void launch_attention_decode(hipStream_t s, const float* qkv, const float* qn, c
 void launch_attention_rows_split(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
                                  int kv_bf16, int max_pos, const DevState* st, int S, int cmin, float* part,
                                  float* o_out);
+// With `part`, batches whose query tiles do not fill the CUs run the split
+// form over attn_prefill_splits(T, ...) splits (partials part[T][nq][S][D + 2])
+// and a merge.
+int attn_prefill_splits(int T, int nq, int nkv, int ncu);
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
-                              int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu);
+                              int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu,
+                              float* part = nullptr, int cmin = 16);
 
 // Top-k / temperature / top-p sampling over the logits (sample.hip); the token
 // goes to the device step state, which the greedy pass has already advanced.
