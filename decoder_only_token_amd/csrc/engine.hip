@@ -258,8 +258,8 @@ int alloc_gemm_workspace(qd_handle* h) {
   if (c.max_prefill < kGemmMinRows) return QD_OK;
   size_t need = 0;
   const int NQKV = qkv_rows(c);
-  // the need s(T) * T * N peaks at the end of each 128-row tile count
-  for (int T = std::min(128, c.max_prefill); T <= c.max_prefill; T = T < c.max_prefill ? std::min(T + 128, c.max_prefill) : T + 1) {
+  // the need s(T) * T * N peaks at the end of each row-tile count (64 or 128 rows)
+  for (int T = std::min(64, c.max_prefill); T <= c.max_prefill; T = T < c.max_prefill ? std::min(T + 64, c.max_prefill) : T + 1) {
     need = std::max(need, gemm_workspace_floats(T, c.hidden, NQKV, h->ncu));
     need = std::max(need, gemm_workspace_floats(T, c.n_q_heads * c.head_dim, c.hidden, h->ncu));
     need = std::max(need, gemm_workspace_floats(T, c.hidden, c.intermediate, h->ncu));

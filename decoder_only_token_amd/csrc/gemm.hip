@@ -71,25 +71,26 @@ enum { EPI_STORE = 0, EPI_ADD = 1, EPI_GATEUP = 2 };
 //
 // Q4: B / B2 are int4 codes [N][K / 2] with fp16 scales SB / SB2 [N][K / 128]
 // (the layout of the int4 GEMVs); Kc is then a multiple of 128.
-template <int EPI, bool Q4>
+template <int EPI, bool Q4, int BMT>
 __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al,
                                                         int T, int K, const void* __restrict__ B,
                                                         const void* __restrict__ B2, const uint16_t* __restrict__ SB,
                                                         const uint16_t* __restrict__ SB2, int N,
                                                         const float* __restrict__ bias, float* __restrict__ C,
                                                         int ldc, int Kc, float* __restrict__ part) {
-  __shared__ __align__(16) uint16_t sA[2][BM * LDR];  // [hi, lo]
+  constexpr int MI = BMT / 32, JA = BMT / 32;  // 16-row tiles per wave, A chunks per thread
+  __shared__ __align__(16) uint16_t sA[2][BMT * LDR];  // [hi, lo]
   __shared__ __align__(16) uint16_t sB[BN * LDR];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.x * BM;
+  const int m0 = blockIdx.x * BMT;
   const int n0 = blockIdx.y * (EPI == EPI_GATEUP ? BN / 2 : BN);
 
-  // global -> register staging: each tile is 128 rows x 8 chunks of 16 bytes,
-  // 4 chunks per thread (row = idx / 8, chunk = idx % 8)
-  // (an int4 W tile is 128 rows x 32 bytes: one 16-byte load per thread,
-  // row = tid / 2, columns 32 (tid % 2) .. + 31)
-  u32x4 ra[2][4], rb[Q4 ? 1 : 4];
+  // global -> register staging: each tile is BMT (A) or 128 (B) rows x 8
+  // chunks of 16 bytes, BMT / 32 or 4 chunks per thread (row = idx / 8,
+  // chunk = idx % 8) (an int4 W tile is 128 rows x 32 bytes: one 16-byte load
+  // per thread, row = tid / 2, columns 32 (tid % 2) .. + 31)
+  u32x4 ra[2][JA], rb[Q4 ? 1 : 4];
   auto b_row = [&](int row, int& n) -> const void* {
     if (EPI == EPI_GATEUP) {
       n = min(n0 + (row & 63), N - 1);
@@ -100,12 +101,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   };
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JA; ++j) {
       const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
       const int t = min(m0 + row, T - 1);
       const size_t off = (size_t)t * K + k0 + ch * 8;
       ra[0][j] = *reinterpret_cast<const u32x4*>(Ah + off);
       ra[1][j] = *reinterpret_cast<const u32x4*>(Al + off);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
       if (!Q4) {
         int n;
         const uint16_t* src = static_cast<const uint16_t*>(b_row(row, n));
@@ -121,10 +126,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   };
   auto sstore = [&]() {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JA; ++j) {
       const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
       *reinterpret_cast<u32x4*>(&sA[0][row * LDR + ch * 8]) = ra[0][j];
       *reinterpret_cast<u32x4*>(&sA[1][row * LDR + ch * 8]) = ra[1][j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
       if (!Q4) *reinterpret_cast<u32x4*>(&sB[row * LDR + ch * 8]) = rb[j];
     }
     if (Q4) {
@@ -148,9 +157,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   // Q4: acc holds sum_groups code.x * e_g / e_cur, where e_g is the group's
   // scale (a zero scale keeps the previous one: its codes are all zero);
   // entering a group multiplies acc by e_prev / e_new, and the end by e_last.
-  f32x4 acc[4][4];
+  f32x4 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
         if (e > 0.f) {
           const float r = scl[j] / e;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][j] *= r;
+          for (int i = 0; i < MI; ++i) acc[i][j] *= r;
           scl[j] = e;
         }
       }
@@ -199,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
 #pragma unroll
       for (int j = 0; j < 4; ++j) bh[j] = *reinterpret_cast<const bf16x8*>(&sB[(brow[j] + fr) * LDR + fk]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ar = wm * 64 + i * 16 + fr;
+      for (int i = 0; i < MI; ++i) {
+        const int ar = wm * (BMT / 2) + i * 16 + fr;
         const bf16x8 a_hi = *reinterpret_cast<const bf16x8*>(&sA[0][ar * LDR + fk]);
         const bf16x8 a_lo = *reinterpret_cast<const bf16x8*>(&sA[1][ar * LDR + fk]);
 #pragma unroll
@@ -218,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   }
   if (Q4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] *= scl[j];
   }
@@ -229,10 +238,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
     const int ldp = EPI == EPI_GATEUP ? 2 * N : N;
     float* P = part + (size_t)blockIdx.z * T * ldp;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        const int t = m0 + wm * (BMT / 2) + i * 16 + (lane >> 4) * 4 + e;
         if (t >= T) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -250,10 +259,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+      const int t = m0 + wm * (BMT / 2) + i * 16 + (lane >> 4) * 4 + e;
       if (t >= T) continue;
       if (EPI == EPI_GATEUP) {
 #pragma unroll
@@ -308,11 +317,18 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float* __restrict
   }
 }
 
-// K splits for a T x N product: enough blocks to cover the GPU twice, each
-// split at least two K-steps long, at most 8 splits.
+// Row tile of a T-row product: 64 rows for short batches (twice the
+// workgroups, so fewer K splits), 128 otherwise.
+int gemm_bm(int T) { return T <= 2048 ? 64 : BM; }
+
+// K splits for a T x N product: none when the tiles give every CU a
+// workgroup, else enough to do so, each split at least two K-steps long, at
+// most 8 splits.
 int splits_for(int T, int K, int N, int epi, int ncu) {
-  const int tiles = ((T + BM - 1) / BM) * (epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN);
-  int s = (2 * ncu + tiles - 1) / tiles;
+  const int bm = gemm_bm(T);
+  const int tiles = ((T + bm - 1) / bm) * (epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN);
+  if (tiles >= ncu) return 1;
+  int s = (ncu + tiles - 1) / tiles;
   s = std::min(s, std::max(1, K / BK / 2));
   return std::max(1, std::min(s, 8));
 }
@@ -346,21 +362,26 @@ void launch_gemm(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl,
   const int step = Q4 ? 128 : BK;  // an int4 split holds whole groups
   const int Kc = (K / step + S - 1) / S * step;
   S = (K + Kc - 1) / Kc;  // every split holds at least one K-step
-  const dim3 grid((T + BM - 1) / BM, epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN, S);
+  const int bm = gemm_bm(T);
+  const dim3 grid((T + bm - 1) / bm, epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN, S);
+#define QD_GEMM(EPI_, BM_)                                                                                          \
+  hipLaunchKernelGGL((k_gemm_hilo<EPI_, Q4, BM_>), grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, SW, SW2, N, bias, \
+                     C, ldc, Kc, ws)
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL((k_gemm_hilo<EPI_STORE, Q4>), grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, SW, SW2, N,
-                         bias, C, ldc, Kc, ws);
+      if (bm == 64) QD_GEMM(EPI_STORE, 64);
+      else QD_GEMM(EPI_STORE, BM);
       break;
     case EPI_ADD:
-      hipLaunchKernelGGL((k_gemm_hilo<EPI_ADD, Q4>), grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, SW, SW2, N,
-                         bias, C, ldc, Kc, ws);
+      if (bm == 64) QD_GEMM(EPI_ADD, 64);
+      else QD_GEMM(EPI_ADD, BM);
       break;
     default:
-      hipLaunchKernelGGL((k_gemm_hilo<EPI_GATEUP, Q4>), grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, SW, SW2, N,
-                         bias, C, ldc, Kc, ws);
+      if (bm == 64) QD_GEMM(EPI_GATEUP, 64);
+      else QD_GEMM(EPI_GATEUP, BM);
       break;
   }
+#undef QD_GEMM
   if (S == 1) return;
   const int blocks = (int)std::min<size_t>(((size_t)T * N + 255) / 256, 4096);
   switch (epi) {
