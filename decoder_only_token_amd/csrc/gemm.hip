@@ -90,7 +90,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   // chunks of 16 bytes, BMT / 32 or 4 chunks per thread (row = idx / 8,
   // chunk = idx % 8) (an int4 W tile is 128 rows x 32 bytes: one 16-byte load
   // per thread, row = tid / 2, columns 32 (tid % 2) .. + 31)
-  u32x4 ra[2][JA], rb[Q4 ? 1 : 4];
+  constexpr int NB = Q4 ? 1 : 4;
+  // two register sets, so that two K-steps' loads are in flight: set X holds
+  // A hi / lo, B and (int4, even steps) the 4 group scales of this lane's
+  // output columns, requested with the step's tiles
+  u32x4 raX[2][JA], rbX[NB], raY[2][JA], rbY[NB];
+  uint16_t scX[4], scY[4];
   auto b_row = [&](int row, int& n) -> const void* {
     if (EPI == EPI_GATEUP) {
       n = min(n0 + (row & 63), N - 1);
@@ -99,7 +104,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
     n = min(n0 + row, N - 1);
     return B;
   };
-  auto gload = [&](int k0) {
+  const int kbeg = blockIdx.z * Kc;
+  const int nk = min(Kc, K - kbeg) / BK;
+  auto gload = [&](u32x4 (&ra)[2][JA], u32x4 (&rb)[NB], uint16_t (&sc)[4], int kt) {
+    const int k0 = kbeg + kt * BK;
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
       const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
@@ -108,35 +116,48 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
       ra[0][j] = *reinterpret_cast<const u32x4*>(Ah + off);
       ra[1][j] = *reinterpret_cast<const u32x4*>(Al + off);
     }
+    if (!Q4) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
-      if (!Q4) {
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
         int n;
         const uint16_t* src = static_cast<const uint16_t*>(b_row(row, n));
         rb[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)n * K + k0 + ch * 8));
       }
-    }
-    if (Q4) {
+    } else {
       int n;
       const uint8_t* src = static_cast<const uint8_t*>(b_row(tid >> 1, n));
       rb[0] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(src + (size_t)n * (K / 2) + k0 / 2 + (tid & 1) * 16));
+      const int g = k0 / 128;  // (read on every step; used on even ones, where a group starts)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint16_t* S;
+        if (EPI == EPI_GATEUP) {
+          n = n0 + wn * 32 + (j & 1) * 16 + (lane & 15);
+          S = j < 2 ? SB : SB2;
+        } else {
+          n = n0 + wn * 64 + j * 16 + (lane & 15);
+          S = SB;
+        }
+        sc[j] = S[(size_t)min(n, N - 1) * (K / 128) + g];
+      }
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](const u32x4 (&ra)[2][JA], const u32x4 (&rb)[NB]) {
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
       const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
       *reinterpret_cast<u32x4*>(&sA[0][row * LDR + ch * 8]) = ra[0][j];
       *reinterpret_cast<u32x4*>(&sA[1][row * LDR + ch * 8]) = ra[1][j];
     }
+    if (!Q4) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
-      if (!Q4) *reinterpret_cast<u32x4*>(&sB[row * LDR + ch * 8]) = rb[j];
-    }
-    if (Q4) {
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + j * kThreads, row = idx >> 3, ch = idx & 7;
+        *reinterpret_cast<u32x4*>(&sB[row * LDR + ch * 8]) = rb[j];
+      }
+    } else {
       // byte b of dword m: columns 8 m + 2 b (low nibble) and 8 m + 2 b + 1
       // (high nibble), each code + 8; bf16 of a small integer is exact
 #pragma unroll
@@ -169,29 +190,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
   for (int j = 0; j < 4; ++j)
     brow[j] = EPI == EPI_GATEUP ? (j < 2 ? 0 : 64) + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16;
 
-  const int kbeg = blockIdx.z * Kc;
-  const int nk = min(Kc, K - kbeg) / BK;
-  auto gload_k = [&](int kt) { gload(kbeg + kt * BK); };
-  gload_k(0);
-  sstore();
-  __syncthreads();
   float scl[4] = {1.f, 1.f, 1.f, 1.f};  // Q4: current scale e of this lane's 4 output columns
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload_k(kt + 1);  // the next K-step flies during this one
+  // one K-step from the tiles in LDS (scales of its register set)
+  auto step = [&](int kt, const uint16_t (&sc)[4]) {
     if (Q4 && (kt & 1) == 0) {
-      const int g = (kbeg + kt * BK) / 128;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        int n;
-        const uint16_t* S;
-        if (EPI == EPI_GATEUP) {
-          n = n0 + wn * 32 + (j & 1) * 16 + (lane & 15);
-          S = j < 2 ? SB : SB2;
-        } else {
-          n = n0 + wn * 64 + j * 16 + (lane & 15);
-          S = SB;
-        }
-        const float e = __half2float(__ushort_as_half(S[(size_t)min(n, N - 1) * (K / 128) + g]));
+        const float e = __half2float(__ushort_as_half(sc[j]));
         if (e > 0.f) {
           const float r = scl[j] / e;
 #pragma unroll
@@ -219,10 +224,78 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
         }
       }
     }
-    if (kt + 1 < nk) {
-      __syncthreads();  // every wave is done with this K-step's tiles
-      sstore();
+  };
+
+  if constexpr (BMT == 128) {
+    // the 128-row tile (long batches, many workgroups): one register set,
+    // the next K-step in flight during this one (a second set would cost
+    // occupancy)
+    gload(raX, rbX, scX, 0);
+    sstore(raX, rbX);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {  // uniform
+      uint16_t scc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) scc[j] = scX[j];
+      if (kt + 1 < nk) gload(raX, rbX, scX, kt + 1);
+      step(kt, scc);
+      if (kt + 1 < nk) {
+        __syncthreads();  // every wave is done with this K-step's tiles
+        sstore(raX, rbX);
+        __syncthreads();
+      }
+    }
+  } else {
+    // K-steps: step kt computes from LDS while the registers of steps kt + 1
+    // and kt + 2 are in flight.  The steady part issues the same loads in every
+    // pass (no load under a branch, so no wait for a later load is forced);
+    // the last (up to three) steps follow.  (With one step, set Y re-reads it.)
+    gload(raX, rbX, scX, 0);
+    sstore(raX, rbX);
+    __syncthreads();
+    uint16_t sc0[4];
+  #pragma unroll
+    for (int j = 0; j < 4; ++j) sc0[j] = scX[j];
+    gload(raY, rbY, scY, min(1, nk - 1));
+    int kt = 0;
+    for (; kt + 3 < nk; kt += 2) {  // uniform
+      uint16_t scc[4];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) scc[j] = kt == 0 ? sc0[j] : scX[j];
+      gload(raX, rbX, scX, kt + 2);
+      step(kt, scc);
+      __syncthreads();  // every wave is done with step kt's tiles
+      sstore(raY, rbY);
       __syncthreads();
+      uint16_t scn[4];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) scn[j] = scY[j];
+      gload(raY, rbY, scY, kt + 3);
+      step(kt + 1, scn);
+      __syncthreads();
+      sstore(raX, rbX);
+      __syncthreads();
+    }
+    // the tail: step kt in LDS (its scales: sc0 at kt = 0, else set X's),
+    // kt + 1 in set Y when it exists, kt + 2 not requested yet
+    {
+      uint16_t scc[4];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) scc[j] = kt == 0 ? sc0[j] : scX[j];
+      if (kt + 2 < nk) gload(raX, rbX, scX, kt + 2);
+      step(kt, scc);
+      if (kt + 1 < nk) {
+        __syncthreads();
+        sstore(raY, rbY);
+        __syncthreads();
+        step(kt + 1, scY);
+      }
+      if (kt + 2 < nk) {
+        __syncthreads();
+        sstore(raX, rbX);
+        __syncthreads();
+        step(kt + 2, scX);
+      }
     }
   }
   if (Q4) {
