@@ -979,12 +979,13 @@ int qd_verify(qd_handle* h, const int32_t* tokens_host, int32_t m, float* logits
       enqueue_layers_gemm(h, m, false);
     else
       enqueue_layers_gemv(h, m, false);
+    int np = nblk;  // partials per row (row stride nblk)
     for (int t0 = 0, tr = lmhead_rows_per_pass(H); t0 < m; t0 += tr) {
       const int tn = std::min(tr, m - t0);
-      launch_lmhead_rows_bf16(s, h->embed, V, H, h->x + (size_t)t0 * H, tn, h->final_norm, c.rms_eps,
+      np = launch_lmhead_rows_bf16(s, h->embed, V, H, h->x + (size_t)t0 * H, tn, h->final_norm, c.rms_eps,
                               h->vlogits + (size_t)t0 * V, h->vpval + (size_t)t0 * nblk, h->vpidx + (size_t)t0 * nblk);
     }
-    launch_argmax_rows(s, h->vpval, h->vpidx, nblk, m, h->st, h->vchoice);
+    launch_argmax_rows(s, h->vpval, h->vpidx, nblk, np, m, h->st, h->vchoice);
     hipGraph_t g = nullptr;
     const hipError_t e = hipStreamEndCapture(s, &g);
     if (e != hipSuccess) return h->set_err(QD_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));

@@ -30,13 +30,14 @@ int lmhead_blocks(int V);
 int launch_lmhead_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, const float* gain, float eps,
                        float* logits, float* part_val, int32_t* part_idx, float* xf_out);
 // Speculative verification: final norm + LM head for T <= lmhead_rows_per_pass(H)
-// rows with per-row logits [T][V] and argmax partials [T][lmhead_blocks(V)];
+// rows with per-row logits [T][V] and argmax partials at row stride
+// lmhead_blocks(V) (the count per row is returned);
 // the per-row choices (advancing the step state by T); dropping positions.
 int lmhead_rows_per_pass(int H);
-void launch_lmhead_rows_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, int T, const float* gain,
+int launch_lmhead_rows_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, int T, const float* gain,
                              float eps, float* logits, float* part_val, int32_t* part_idx);
-void launch_argmax_rows(hipStream_t s, const float* part_val, const int32_t* part_idx, int nblk, int T, DevState* st,
-                        int32_t* choice);
+void launch_argmax_rows(hipStream_t s, const float* part_val, const int32_t* part_idx, int nblk, int nparts, int T,
+                        DevState* st, int32_t* choice);
 void launch_rewind_state(hipStream_t s, DevState* st, int n, int32_t token);
 void launch_argmax_final(hipStream_t s, const float* part_val, const int32_t* part_idx, int nparts, DevState* st,
                          int advance, int32_t* token_out);

@@ -579,14 +579,14 @@ __global__ __launch_bounds__(256) void k_lmhead_rows_bf16(const uint16_t* __rest
 // t), into choice[t]; the block of the last row then advances the step state
 // as T decode steps would: token := its choice, pos += T, step += T.
 __global__ __launch_bounds__(256) void k_argmax_rows(const float* __restrict__ part_val,
-                                                     const int32_t* __restrict__ part_idx, int nblk, int T,
-                                                     DevState* st, int32_t* __restrict__ choice) {
+                                                     const int32_t* __restrict__ part_idx, int nblk, int nparts,
+                                                     int T, DevState* st, int32_t* __restrict__ choice) {
   __shared__ float sv[256];
   __shared__ int32_t si[256];
   const int t = blockIdx.x;
   float bv = -INFINITY;
   int32_t bj = 0x7fffffff;
-  for (int i = threadIdx.x; i < nblk; i += 256) {
+  for (int i = threadIdx.x; i < nparts; i += 256) {  // (row t's partials at stride nblk)
     const float v = part_val[(size_t)t * nblk + i];
     const int32_t j = part_idx[(size_t)t * nblk + i];
     if (v > bv || (v == bv && j < bj)) { bv = v; bj = j; }
@@ -626,23 +626,176 @@ __global__ void k_rewind_state(DevState* st, int n, int32_t token) {
   }
 }
 
+// The LM head of up to 8 rows on the matrix cores: at most 512 workgroups,
+// each staging the rows' final-normed values once as bf16 halves (A rows
+// 0-7: hi of rows 0-7, A rows 8-15: lo; rows past T are zeros) and owning RB
+// contiguous vocabulary rows (a multiple of 64); wave w takes the 16-row
+// chunks w, w + 4, ... of them as the B operand of v_mfma_f32_16x16x32_bf16
+// (lane l: vocabulary row l % 16, columns 8 (l / 16) .. + 7 of each 32-column
+// K-step), 16 K-steps of loads per group, the next group in flight.  D rows
+// t and 8 + t are row t's hi and lo products: added across lanes l, l + 32.
+// Each row keeps a running argmax (ties to the lowest id); partials
+// part[t][pstride] for the workgroups.
+constexpr int kLmKg = 16;  // K-steps per load group
+__global__ __launch_bounds__(256) void k_lmhead_rows_mfma(const uint16_t* __restrict__ E, int V, int H, int RB,
+                                                          const float* __restrict__ x, int T,
+                                                          const float* __restrict__ gain, float eps,
+                                                          float* __restrict__ logits, float* __restrict__ part_val,
+                                                          int32_t* __restrict__ part_idx, int pstride) {
+  extern __shared__ __align__(16) uint16_t sa[];  // [16][H + 8] bf16
+  __shared__ float red[4][LMHEAD_ROWS];
+  __shared__ float bval[LMHEAD_ROWS][4];
+  __shared__ int32_t bidx[LMHEAD_ROWS][4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int LS = H + 8;
+  // ---- the rows' RMS scales, then their hi / lo halves into LDS
+  float ss[LMHEAD_ROWS];
+#pragma unroll
+  for (int t = 0; t < LMHEAD_ROWS; ++t) {
+    ss[t] = 0.f;
+    if (t < T)
+      for (int k = tid * 4; k < H; k += 1024) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(x + (size_t)t * H + k);
+        ss[t] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+    ss[t] = wave_sum(ss[t]);
+    if (lane == 0) red[wave][t] = ss[t];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < LMHEAD_ROWS; ++t) {
+    const float r = 1.0f / sqrtf((red[0][t] + red[1][t] + red[2][t] + red[3][t]) / (float)H + eps);
+    for (int k = tid * 4; k < H; k += 1024) {
+      uint32_t hi[4], lo[4];
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < T) {
+        v = *reinterpret_cast<const f32x4*>(x + (size_t)t * H + k) * r;
+        if (gain) v = v * *reinterpret_cast<const f32x4*>(gain + k);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = bf16_rne(v[i]);
+        lo[i] = bf16_rne(v[i] - __uint_as_float(hi[i] << 16));
+      }
+      *reinterpret_cast<uint2*>(sa + (size_t)t * LS + k) = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+      *reinterpret_cast<uint2*>(sa + (size_t)(8 + t) * LS + k) = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    }
+  }
+  __syncthreads();
+  // ---- the workgroup's vocabulary rows, 16 per chunk
+  const int base = blockIdx.x * RB, rowend = min(V, base + RB), nrow = max(0, rowend - base);
+  const __amdgpu_buffer_rsrc_t re = lm_record(E + (size_t)min(base, V) * H, nrow * H * 2);
+  const int nl = lane & 15, q = lane >> 4;
+  const int ng = H / (32 * kLmKg);          // load groups per chunk
+  const int nch = RB / 64;                  // chunks per wave
+  const int nu = nch * ng;                  // load groups per wave
+  u32x4 bX[kLmKg], bY[kLmKg];
+  auto load = [&](u32x4 (&b)[kLmKg], int u) {
+    const int j = u / ng, g = u % ng;
+    const int row = (wave + 4 * j) * 16 + nl;
+    int off = row < nrow && u < nu ? (row * H + g * 32 * kLmKg + 8 * q) * 2 : kLmPastRecord;
+    asm volatile("" : "+v"(off));  // (opaque: one load each, no branch)
+#pragma unroll
+    for (int s2 = 0; s2 < kLmKg; ++s2)
+      b[s2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(re, off, s2 * 64, 2 /* streamed */));
+  };
+  float best[4];
+  int32_t bi[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    best[e] = -INFINITY;
+    bi[e] = 0x7fffffff;
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4 (&b)[kLmKg], int u) {
+    const int j = u / ng, g = u % ng;
+#pragma unroll
+    for (int s2 = 0; s2 < kLmKg; ++s2) {
+      const int k = (g * kLmKg + s2) * 32 + 8 * q;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sa + (size_t)nl * LS + k);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b[s2]), acc, 0, 0, 0);
+    }
+    if (g == ng - 1) {  // uniform: the chunk is done
+      const int row = (wave + 4 * j) * 16 + nl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[e]), __float_as_uint(acc[e]), false, false);
+        const float v = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // hi + lo products of row 4 q + e
+        const int t = 4 * (q & 1) + e;
+        if (lane < 32 && t < T && row < nrow) {
+          const int n = base + row;
+          logits[(size_t)t * V + n] = v;
+          if (v > best[e]) { best[e] = v; bi[e] = n; }  // chunks in increasing id: ties keep the lowest
+        }
+      }
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load(bX, 0);
+  for (int u = 0; u < nu; u += 2) {  // uniform
+    load(bY, u + 1);
+    compute(bX, u);
+    load(bX, u + 2);
+    if (u + 1 < nu) compute(bY, u + 1);
+  }
+  // ---- row maxima over the 16 lanes of a row group, then over the waves
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float v = best[e];
+    int32_t id = bi[e];
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const float ov = __shfl_xor(v, m, 64);
+      const int32_t oi = __shfl_xor(id, m, 64);
+      if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+    }
+    const int t = 4 * (q & 1) + e;
+    if (lane < 32 && nl == 0 && t < T) {
+      bval[t][wave] = v;
+      bidx[t][wave] = id;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    float bv = bval[tid][0];
+    int32_t bj = bidx[tid][0];
+    for (int w = 1; w < 4; ++w)
+      if (bval[tid][w] > bv || (bval[tid][w] == bv && bidx[tid][w] < bj)) { bv = bval[tid][w]; bj = bidx[tid][w]; }
+    part_val[(size_t)tid * pstride + blockIdx.x] = bv;
+    part_idx[(size_t)tid * pstride + blockIdx.x] = bj;
+  }
+}
+
 int lmhead_rows_per_pass(int H) {
   int r = (40960 - 8 - 256) / H;  // staged rows (and the block's partials) within 160 KiB of LDS
   if (r > LMHEAD_ROWS) r = LMHEAD_ROWS;
   return r < 1 ? 1 : r;
 }
 
-void launch_lmhead_rows_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, int T, const float* gain,
-                             float eps, float* logits, float* part_val, int32_t* part_idx) {
+int launch_lmhead_rows_bf16(hipStream_t s, const uint16_t* E, int V, int H, const float* x, int T, const float* gain,
+                            float eps, float* logits, float* part_val, int32_t* part_idx) {
   const int nblk = lmhead_blocks(V);
+  if (H % (32 * kLmKg) == 0 && H <= 4096 && (size_t)V * H * 2 < ((size_t)1 << 31) && T <= LMHEAD_ROWS) {
+    static const bool big_lds = hipFuncSetAttribute((const void*)k_lmhead_rows_mfma,
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                    (int)(16 * (4096 + 8) * sizeof(uint16_t))) == hipSuccess;
+    (void)big_lds;
+    const int grid = std::min(512, (V + 63) / 64);
+    const int RB = (V + grid * 64 - 1) / (grid * 64) * 64;
+    const size_t lds = (size_t)16 * (H + 8) * sizeof(uint16_t);
+    hipLaunchKernelGGL(k_lmhead_rows_mfma, dim3(grid), dim3(256), lds, s, E, V, H, RB, x, T, gain, eps, logits,
+                       part_val, part_idx, nblk);
+    return grid;
+  }
   const size_t lds = (8 + (size_t)T * H) * sizeof(float);
   hipLaunchKernelGGL(k_lmhead_rows_bf16, dim3(nblk), dim3(256), lds, s, E, V, H, x, T, gain, eps, logits, part_val,
                      part_idx, nblk);
+  return nblk;
 }
 
-void launch_argmax_rows(hipStream_t s, const float* part_val, const int32_t* part_idx, int nblk, int T, DevState* st,
-                        int32_t* choice) {
-  hipLaunchKernelGGL(k_argmax_rows, dim3(T), dim3(256), 0, s, part_val, part_idx, nblk, T, st, choice);
+void launch_argmax_rows(hipStream_t s, const float* part_val, const int32_t* part_idx, int nblk, int nparts, int T,
+                        DevState* st, int32_t* choice) {
+  hipLaunchKernelGGL(k_argmax_rows, dim3(T), dim3(256), 0, s, part_val, part_idx, nblk, nparts, T, st, choice);
 }
 
 void launch_rewind_state(hipStream_t s, DevState* st, int n, int32_t token) {
