@@ -744,11 +744,19 @@ __global__ __launch_bounds__(256) void k_attn_merge_decode(const float* __restri
   }
 }
 
+// The bf16 halves of v (as the projection input split makes them).
+__device__ __forceinline__ void store_hilo_o(uint16_t* __restrict__ h, uint16_t* __restrict__ l, size_t i, float v) {
+  const uint32_t hb = bf16_rne(v);
+  h[i] = (uint16_t)hb;
+  l[i] = (uint16_t)bf16_rne(v - __uint_as_float(hb << 16));
+}
+
 // The batch attention's split partials merged: one thread per (row, head,
 // dim), over all S splits (every split's partials are written, those with no
 // visible position as m = -inf, l = o = 0), in split order.
 __global__ __launch_bounds__(256) void k_attn_merge_rows(const float* __restrict__ part, int S, int total,
-                                                         float* __restrict__ o_out) {
+                                                         float* __restrict__ o_out, uint16_t* __restrict__ oh,
+                                                         uint16_t* __restrict__ ol) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   const int d = i % D, th = i / D;  // th = row nq + head
@@ -762,7 +770,9 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(const float* __restrict
     L = fmaf(ps[1], e, L);
     O = fmaf(ps[2 + d], e, O);
   }
-  o_out[(size_t)th * D + d] = O / L;
+  const float o = O / L;
+  o_out[(size_t)th * D + d] = o;
+  if (oh) store_hilo_o(oh, ol, (size_t)th * D + d, o);  // (optional: the o_proj input halves too)
 }
 
 // ---------------------------------------------------------------------------
@@ -793,7 +803,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
                                                            const KVT* __restrict__ Vc, int max_pos,
                                                            const DevState* __restrict__ st, float scale,
                                                            float* __restrict__ o_out, int ldo, int S, int cmin,
-                                                           float* __restrict__ part) {
+                                                           float* __restrict__ part, uint16_t* __restrict__ oh,
+                                                           uint16_t* __restrict__ ol) {
   constexpr int QV = 64, R = QV / G, BK = 32;
   constexpr int KS = D + 8;   // K row stride (bf16)
   constexpr int VS = BK + 8;  // V^T row stride (bf16)
@@ -975,9 +986,13 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
     const int v = wave * 16 + 4 * lq + e, r = v / G, j = v % G;
     if (r < nrows) {
       const float inv = 1.0f / l[e];
-      float* dst = o_out + (size_t)(t0 + r) * ldo + (g * G + j) * D + lr;
+      const size_t o0 = (size_t)(t0 + r) * ldo + (g * G + j) * D + lr;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) dst[dt * 16] = oacc[dt][e] * inv;
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const float o = oacc[dt][e] * inv;
+        o_out[o0 + dt * 16] = o;
+        if (oh) store_hilo_o(oh, ol, o0 + dt * 16, o);  // (optional: the o_proj input halves too)
+      }
     }
   }
 }
@@ -1038,24 +1053,25 @@ int attn_prefill_splits(int T, int nq, int nkv, int ncu) {
 
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
                               int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu,
-                              float* part, int cmin) {
+                              float* part, int cmin, uint16_t* oh, uint16_t* ol) {
   const float scale = 1.0f / sqrtf((float)D);
   const int G = nq / nkv;
   const int S = part ? attn_prefill_splits(T, nq, nkv, ncu) : 1;
   if (S > 1 && ldo == nq * D) {  // fewer query tiles than CUs: the split form, then the merge
     launch_attention_rows_split_only(s, q, T, nq, nkv, Kc, Vc, kv_bf16, max_pos, st, S, cmin, part);
     const int total = T * nq * D;
-    hipLaunchKernelGGL(k_attn_merge_rows, dim3((total + 255) / 256), dim3(256), 0, s, part, S, total, o_out);
+    hipLaunchKernelGGL(k_attn_merge_rows, dim3((total + 255) / 256), dim3(256), 0, s, part, S, total, o_out, oh, ol);
     return;
   }
   const dim3 grid(nkv, (T + 64 / G - 1) / (64 / G));
 #define QD_ATTN_PREFILL(G_)                                                                                        \
   if (kv_bf16)                                                                                                     \
     hipLaunchKernelGGL((k_attn_prefill_mfma<G_, uint16_t, false>), grid, dim3(256), 0, s, q, T, nq,               \
-                       (const uint16_t*)Kc, (const uint16_t*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr);    \
+                       (const uint16_t*)Kc, (const uint16_t*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr,     \
+                       oh, ol);                                                                                     \
   else                                                                                                             \
     hipLaunchKernelGGL((k_attn_prefill_mfma<G_, float, false>), grid, dim3(256), 0, s, q, T, nq, (const float*)Kc, \
-                       (const float*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr)
+                       (const float*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr, oh, ol)
   switch (G) {
     case 1: QD_ATTN_PREFILL(1); break;
     case 2: QD_ATTN_PREFILL(2); break;
@@ -1076,10 +1092,11 @@ void launch_attention_rows_split_only(hipStream_t s, const float* q, int T, int 
 #define QD_ATTN_ROWS(G_)                                                                                           \
   if (kv_bf16)                                                                                                     \
     hipLaunchKernelGGL((k_attn_prefill_mfma<G_, uint16_t, true>), grid, dim3(256), 0, s, q, T, nq,                \
-                       (const uint16_t*)Kc, (const uint16_t*)Vc, max_pos, st, scale, nullptr, 0, S, cmin, part);   \
+                       (const uint16_t*)Kc, (const uint16_t*)Vc, max_pos, st, scale, nullptr, 0, S, cmin, part,    \
+                       nullptr, nullptr);                                                                           \
   else                                                                                                             \
     hipLaunchKernelGGL((k_attn_prefill_mfma<G_, float, true>), grid, dim3(256), 0, s, q, T, nq, (const float*)Kc,  \
-                       (const float*)Vc, max_pos, st, scale, nullptr, 0, S, cmin, part)
+                       (const float*)Vc, max_pos, st, scale, nullptr, 0, S, cmin, part, nullptr, nullptr)
   switch (G) {
     case 1: QD_ATTN_ROWS(1); break;
     case 2: QD_ATTN_ROWS(2); break;

@@ -109,6 +109,8 @@ struct qd_handle {
   float* act = nullptr;  // [rows][I]
   uint16_t* xh = nullptr;  // [rows][max(H, nq d, I)] bf16 halves of a projection input
   uint16_t* xl = nullptr;
+  uint16_t* xh2 = nullptr;  // [rows][I]: the down projection's input halves (written by gate/up)
+  uint16_t* xl2 = nullptr;
   float* gws = nullptr;  // split-K workspace of the batched projections
   size_t gws_floats = 0;
   int ncu = 0;
@@ -344,7 +346,9 @@ void* kv_layer(qd_handle* h, float* base, int l) {
   return reinterpret_cast<char*>(base) + l * layer_kv * (c.kv_format == QD_KV_BF16 ? 2 : 4);
 }
 
-void enqueue_attention(qd_handle* h, int l, int T) {
+// hilo_o: the batch attention also writes the bf16 halves of its output into
+// xh / xl (the o_proj input of the matrix-core projections); returns whether it did.
+bool enqueue_attention(qd_handle* h, int l, int T, bool hilo_o = false) {
   const qd_config& c = h->cfg;
   hipStream_t s = h->stream;
   const int d = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
@@ -379,8 +383,11 @@ void enqueue_attention(qd_handle* h, int l, int T) {
     launch_qk_rope_kv(s, h->qkv, qkv_rows(c), T, nq, nkv, d, L.q_norm, L.k_norm, c.rms_eps, h->rope_cos, h->rope_sin,
                       h->st, h->q, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), c.max_pos, kv16, lr);
     launch_attention_prefill(s, h->q, T, nq, nkv, kv_layer(h, h->Kc, l), kv_layer(h, h->Vc, l), kv16, c.max_pos, h->st,
-                             h->o, nq * d, h->ncu, h->part, kDecodeMinSplit);
+                             h->o, nq * d, h->ncu, h->part, kDecodeMinSplit, hilo_o ? h->xh : nullptr,
+                             hilo_o ? h->xl : nullptr);
+    return hilo_o;
   }
+  return false;
 }
 
 // Layers with the matrix-core projections (T >= kGemmMinRows).
@@ -404,8 +411,8 @@ void enqueue_layers_gemm(qd_handle* h, int T, bool capture) {
       launch_gemm_hilo(s, GEMM_STORE, h->xh, h->xl, T, H, h->lora[l].a, nullptr, r2, nullptr, h->lu, r2, h->gws,
                        h->gws_floats, h->ncu);
     }
-    enqueue_attention(h, l, T);
-    launch_split_rows(s, h->o, nq * d, T, nq * d, nullptr, 0.f, h->xh, h->xl);
+    if (!enqueue_attention(h, l, T, true))  // (else the attention wrote the o_proj input halves)
+      launch_split_rows(s, h->o, nq * d, T, nq * d, nullptr, 0.f, h->xh, h->xl);
     if (q4)
       launch_gemm_q4(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.co, L.so, nullptr, nullptr, H, nullptr, h->x, H, h->gws,
                      h->gws_floats, h->ncu);
@@ -413,18 +420,18 @@ void enqueue_layers_gemm(qd_handle* h, int T, bool capture) {
       launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, nq * d, L.wo, nullptr, H, nullptr, h->x, H, h->gws,
                        h->gws_floats, h->ncu);
     launch_split_rows(s, h->x, H, T, H, L.mlp_norm, c.rms_eps, h->xh, h->xl);
+    // gate | up writes SiLU(gate) * up and its bf16 halves (the down input)
     if (q4)
       launch_gemm_q4(s, GEMM_GATEUP, h->xh, h->xl, T, H, L.cg, L.sg, L.cu, L.su, I, nullptr, h->act, I, h->gws,
-                     h->gws_floats, h->ncu);
+                     h->gws_floats, h->ncu, h->xh2, h->xl2);
     else
       launch_gemm_hilo(s, GEMM_GATEUP, h->xh, h->xl, T, H, L.wg, L.wu, I, nullptr, h->act, I, h->gws, h->gws_floats,
-                       h->ncu);
-    launch_split_rows(s, h->act, I, T, I, nullptr, 0.f, h->xh, h->xl);
+                       h->ncu, h->xh2, h->xl2);
     if (q4)
-      launch_gemm_q4(s, GEMM_ADD, h->xh, h->xl, T, I, L.cd, L.sd, nullptr, nullptr, H, nullptr, h->x, H, h->gws,
+      launch_gemm_q4(s, GEMM_ADD, h->xh2, h->xl2, T, I, L.cd, L.sd, nullptr, nullptr, H, nullptr, h->x, H, h->gws,
                      h->gws_floats, h->ncu);
     else
-      launch_gemm_hilo(s, GEMM_ADD, h->xh, h->xl, T, I, L.wd, nullptr, H, nullptr, h->x, H, h->gws, h->gws_floats,
+      launch_gemm_hilo(s, GEMM_ADD, h->xh2, h->xl2, T, I, L.wd, nullptr, H, nullptr, h->x, H, h->gws, h->gws_floats,
                        h->ncu);
     if (capture)
       (void)hipMemcpyAsync(h->cap + (size_t)(l + 1) * c.max_prefill * H, h->x, (size_t)T * H * 4,
@@ -637,6 +644,7 @@ int qd_create(const qd_config* cfg, void* hip_stream, qd_handle** out) {
       (rc = dev_alloc(h, &h->o, rows * c.n_q_heads * d)) || (rc = dev_alloc(h, &h->act, rows * I)) ||
       (rc = dev_alloc(h, &h->xh, rows * std::max(std::max(H, (size_t)c.n_q_heads * d), I))) ||
       (rc = dev_alloc(h, &h->xl, rows * std::max(std::max(H, (size_t)c.n_q_heads * d), I))) ||
+      (rc = dev_alloc(h, &h->xh2, rows * I)) || (rc = dev_alloc(h, &h->xl2, rows * I)) ||
       (rc = alloc_gemm_workspace(h)) ||
       (rc = dev_alloc(h, &h->part, h->part_floats)) || (rc = dev_alloc(h, &h->logits, (size_t)c.vocab)) ||
       (rc = dev_alloc(h, &h->pval, (size_t)lmhead_blocks(c.vocab))) ||

@@ -57,6 +57,13 @@ __global__ __launch_bounds__(256) void k_split_rows(const float* __restrict__ x,
   }
 }
 
+// The bf16 halves of v (as k_split_rows makes them, without a gain).
+__device__ __forceinline__ void store_hilo(uint16_t* __restrict__ h, uint16_t* __restrict__ l, size_t i, float v) {
+  const uint32_t hb = bf16_rne(v);
+  h[i] = (uint16_t)hb;
+  l[i] = (uint16_t)bf16_rne(v - __uint_as_float(hb << 16));
+}
+
 enum { EPI_STORE = 0, EPI_ADD = 1, EPI_GATEUP = 2 };
 
 // C tile of block (bm, bn).  EPI_STORE: C = acc (+ bias); EPI_ADD: C += acc;
@@ -77,7 +84,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
                                                         const void* __restrict__ B2, const uint16_t* __restrict__ SB,
                                                         const uint16_t* __restrict__ SB2, int N,
                                                         const float* __restrict__ bias, float* __restrict__ C,
-                                                        int ldc, int Kc, float* __restrict__ part) {
+                                                        int ldc, int Kc, float* __restrict__ part,
+                                                        uint16_t* __restrict__ Ch, uint16_t* __restrict__ Cl) {
   constexpr int MI = BMT / 32, JA = BMT / 32;  // 16-row tiles per wave, A chunks per thread
   __shared__ __align__(16) uint16_t sA[2][BMT * LDR];  // [hi, lo]
   __shared__ __align__(16) uint16_t sB[BN * LDR];
@@ -343,7 +351,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
           const int n = n0 + wn * 32 + j * 16 + (lane & 15);
           if (n < N) {
             const float g = acc[i][j][e], u = acc[i][j + 2][e];
-            C[(size_t)t * ldc + n] = silu_f(g) * u;
+            const float v = silu_f(g) * u;
+            C[(size_t)t * ldc + n] = v;
+            if (Ch) store_hilo(Ch, Cl, (size_t)t * ldc + n, v);
           }
         }
       } else {
@@ -368,7 +378,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_hilo(const uint16_t* __restri
 template <int EPI>
 __global__ __launch_bounds__(256) void k_splitk_epilogue(const float* __restrict__ part, int S, int T, int N,
                                                          const float* __restrict__ bias, float* __restrict__ C,
-                                                         int ldc) {
+                                                         int ldc, uint16_t* __restrict__ Ch,
+                                                         uint16_t* __restrict__ Cl) {
   const size_t total = (size_t)T * N;
   const int ldp = EPI == EPI_GATEUP ? 2 * N : N;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
@@ -381,7 +392,9 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float* __restrict
     }
     float* cp = C + (size_t)t * ldc + n;
     if (EPI == EPI_GATEUP) {
-      *cp = silu_f(a) * b;
+      const float v = silu_f(a) * b;
+      *cp = v;
+      if (Ch) store_hilo(Ch, Cl, (size_t)t * ldc + n, v);
     } else if (EPI == EPI_ADD) {
       *cp += a;
     } else {
@@ -429,7 +442,7 @@ namespace {
 template <bool Q4>
 void launch_gemm(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const void* W,
                  const void* W2, const uint16_t* SW, const uint16_t* SW2, int N, const float* bias, float* C, int ldc,
-                 float* ws, size_t ws_floats, int ncu) {
+                 float* ws, size_t ws_floats, int ncu, uint16_t* ch, uint16_t* cl) {
   int S = splits_for(T, K, N, epi, ncu);
   if ((size_t)S * T * (epi == EPI_GATEUP ? 2 * N : N) > ws_floats || !ws) S = 1;
   const int step = Q4 ? 128 : BK;  // an int4 split holds whole groups
@@ -439,7 +452,7 @@ void launch_gemm(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl,
   const dim3 grid((T + bm - 1) / bm, epi == EPI_GATEUP ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN, S);
 #define QD_GEMM(EPI_, BM_)                                                                                          \
   hipLaunchKernelGGL((k_gemm_hilo<EPI_, Q4, BM_>), grid, dim3(kThreads), 0, s, xh, xl, T, K, W, W2, SW, SW2, N, bias, \
-                     C, ldc, Kc, ws)
+                     C, ldc, Kc, ws, ch, cl)
   switch (epi) {
     case EPI_STORE:
       if (bm == 64) QD_GEMM(EPI_STORE, 64);
@@ -459,13 +472,13 @@ void launch_gemm(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl,
   const int blocks = (int)std::min<size_t>(((size_t)T * N + 255) / 256, 4096);
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL(k_splitk_epilogue<EPI_STORE>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc);
+      hipLaunchKernelGGL(k_splitk_epilogue<EPI_STORE>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc, ch, cl);
       break;
     case EPI_ADD:
-      hipLaunchKernelGGL(k_splitk_epilogue<EPI_ADD>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc);
+      hipLaunchKernelGGL(k_splitk_epilogue<EPI_ADD>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc, ch, cl);
       break;
     default:
-      hipLaunchKernelGGL(k_splitk_epilogue<EPI_GATEUP>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc);
+      hipLaunchKernelGGL(k_splitk_epilogue<EPI_GATEUP>, dim3(blocks), dim3(256), 0, s, ws, S, T, N, bias, C, ldc, ch, cl);
       break;
   }
 }
@@ -474,12 +487,12 @@ void launch_gemm(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl,
 
 void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
                       const uint16_t* W2, int N, const float* bias, float* C, int ldc, float* ws, size_t ws_floats,
-                      int ncu) {
-  launch_gemm<false>(s, epi, xh, xl, T, K, W, W2, nullptr, nullptr, N, bias, C, ldc, ws, ws_floats, ncu);
+                      int ncu, uint16_t* ch, uint16_t* cl) {
+  launch_gemm<false>(s, epi, xh, xl, T, K, W, W2, nullptr, nullptr, N, bias, C, ldc, ws, ws_floats, ncu, ch, cl);
 }
 
 void launch_gemm_q4(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint8_t* W,
                     const uint16_t* SW, const uint8_t* W2, const uint16_t* SW2, int N, const float* bias, float* C,
-                    int ldc, float* ws, size_t ws_floats, int ncu) {
-  launch_gemm<true>(s, epi, xh, xl, T, K, W, W2, SW, SW2, N, bias, C, ldc, ws, ws_floats, ncu);
+                    int ldc, float* ws, size_t ws_floats, int ncu, uint16_t* ch, uint16_t* cl) {
+  launch_gemm<true>(s, epi, xh, xl, T, K, W, W2, SW, SW2, N, bias, C, ldc, ws, ws_floats, ncu, ch, cl);
 }

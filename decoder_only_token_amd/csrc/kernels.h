@@ -79,11 +79,12 @@ void launch_attention_rows_split(hipStream_t s, const float* q, int T, int nq, i
                                  float* o_out);
 // With `part`, batches whose query tiles do not fill the CUs run the split
 // form over attn_prefill_splits(T, ...) splits (partials part[T][nq][S][D + 2])
-// and a merge.
+// and a merge.  oh / ol (optional): the output's bf16 halves too, at the same
+// indices (the o_proj input split).
 int attn_prefill_splits(int T, int nq, int nkv, int ncu);
 void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc, const void* Vc,
                               int kv_bf16, int max_pos, const DevState* st, float* o_out, int ldo, int ncu,
-                              float* part = nullptr, int cmin = 16);
+                              float* part = nullptr, int cmin = 16, uint16_t* oh = nullptr, uint16_t* ol = nullptr);
 
 // Top-k / temperature / top-p sampling over the logits (sample.hip); the token
 // goes to the device step state, which the greedy pass has already advanced.
@@ -104,14 +105,16 @@ void launch_split_rows(hipStream_t s, const float* x, int ldx, int T, int K, con
 // ws: split-K workspace of ws_floats floats (gemm_workspace_floats of the
 // largest product); ncu = compute units of the GPU.
 size_t gemm_workspace_floats(int T, int K, int N, int ncu);
+// ch / cl (gate | up only, optional): the bf16 halves of the output too, as
+// k_split_rows would make them from it.
 void launch_gemm_hilo(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint16_t* W,
                       const uint16_t* W2, int N, const float* bias, float* C, int ldc, float* ws, size_t ws_floats,
-                      int ncu);
+                      int ncu, uint16_t* ch = nullptr, uint16_t* cl = nullptr);
 // W given as int4 group-128 codes [N][K / 2] and fp16 scales [N][K / 128]
 // (q4.hip layout); K a multiple of 128.  W2 / SW2: the up matrix of GEMM_GATEUP.
 void launch_gemm_q4(hipStream_t s, int epi, const uint16_t* xh, const uint16_t* xl, int T, int K, const uint8_t* W,
                     const uint16_t* SW, const uint8_t* W2, const uint16_t* SW2, int N, const float* bias, float* C,
-                    int ldc, float* ws, size_t ws_floats, int ncu);
+                    int ldc, float* ws, size_t ws_floats, int ncu, uint16_t* ch = nullptr, uint16_t* cl = nullptr);
 
 // int4 group-128 weights (q4.hip): quantiser run at weight load, and the
 // GEMVs of decode and short prefills (same contracts as the bf16 GEMVs;
