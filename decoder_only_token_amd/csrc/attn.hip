@@ -784,34 +784,39 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(const float* __restrict
 // nearest even) and three products (hi.hi + hi.lo + lo.hi, the lo.lo term is
 // below f32 rounding of the result); accumulation is f32.
 //
-// grid (nkv, ceil(T / (64 / G))), block 256 = 4 waves.  Split form (SPLIT,
+// grid (nkv, ceil(T / (16 NW / G))), block 64 NW (NW = 4 waves, or 8 for
+// long batches: the same K/V tile then serves twice the queries).  Split form (SPLIT,
 // short batches at long contexts): grid (nkv, ceil(T / (64 / G)) S), the
 // positions 0 .. pos + T - 1 cut into S splits of split_len(pos + T, S, cmin)
 // as the decode attention cuts them, and each block writes the partials
 // {m, l, o} of its query vectors over its split (part[(row nq + head) S +
-// split]) for k_attn_merge_decode.  A block owns 64 query
+// split]) for k_attn_merge_decode.  A block owns 16 NW query
 // vectors of kv head g; wave w owns 16 of them (the A operand of S, kept in
 // registers for the whole kernel).  Per tile of 32 cache positions the block
 // stages K (row-major) and V (transposed) as bf16 halves in LDS; each wave
 // forms its 16 x 32 score tile, updates the online softmax of its rows
-// (row maxima and sums over the 16 lanes that hold a row, by DPP), writes
+// (row maxima and sums over the 16 lanes that hold a row, by DPP; base-2
+// exponentials with log2 e folded into the query scale; the causal and range
+// masks only on tiles that reach them; the output rescale skipped when no
+// row maximum of the wave moved), writes
 // P's halves to its own LDS slice in the A-operand layout, and accumulates
 // its 16 x 128 output tile.
-template <int G, typename KVT, bool SPLIT>
-__global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restrict__ q, int T, int nq,
+template <int G, typename KVT, bool SPLIT, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_attn_prefill_mfma(const float* __restrict__ q, int T, int nq,
                                                            const KVT* __restrict__ Kc,
                                                            const KVT* __restrict__ Vc, int max_pos,
                                                            const DevState* __restrict__ st, float scale,
                                                            float* __restrict__ o_out, int ldo, int S, int cmin,
                                                            float* __restrict__ part, uint16_t* __restrict__ oh,
                                                            uint16_t* __restrict__ ol) {
-  constexpr int QV = 64, R = QV / G, BK = 32;
+  constexpr int QV = 16 * NW, R = QV / G, BK = 32;
+  constexpr int PPT = 4 * 4 / NW, PG = BK / PPT;  // staging: positions per thread, position groups
   constexpr int KS = D + 8;   // K row stride (bf16)
   constexpr int VS = BK + 8;  // V^T row stride (bf16)
   constexpr int PS = BK + 8;  // P row stride (bf16)
   __shared__ __align__(16) uint16_t Kh[BK * KS], Kl[BK * KS];
   __shared__ __align__(16) uint16_t Vth[D * VS], Vtl[D * VS];
-  __shared__ __align__(16) uint16_t Ph[4][16 * PS], Pl[4][16 * PS];
+  __shared__ __align__(16) uint16_t Ph[NW][16 * PS], Pl[NW][16 * PS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;  // fragment row / column, k-quarter
   const int g = blockIdx.x;
@@ -828,7 +833,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
     k_end = min(sp * C + C, kv_end);
   }
 
-  // this lane's query fragment: vector wave*16 + lr, dims 32 ks + 8 lq .. + 8
+  // this lane's query fragment: vector wave*16 + lr, dims 32 ks + 8 lq .. + 8,
+  // scaled by scale log2 e so that the scores are in base-2 exponent units
+  const float qscale = scale * 1.44269504088896341f;
   bf16x8 qh[4], ql[4];
   {
     const int v = wave * 16 + lr, r = v / G, j = v % G;
@@ -837,16 +844,16 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
     for (int ks = 0; ks < 4; ++ks) {
       f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, b = a;
       if (r < nrows) {
-        a = *reinterpret_cast<const f32x4*>(src + 32 * ks) * scale;
-        b = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4) * scale;
+        a = *reinterpret_cast<const f32x4*>(src + 32 * ks) * qscale;
+        b = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4) * qscale;
       }
-      const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t h = bf16_rne(x[i]);
-        qh[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)h);
-        ql[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)bf16_rne(x[i] - __uint_as_float(h << 16)));
-      }
+      uint32_t h[4], lo[4];
+      split_bf16x2(a.x, a.y, h[0], lo[0]);
+      split_bf16x2(a.z, a.w, h[1], lo[1]);
+      split_bf16x2(b.x, b.y, h[2], lo[2]);
+      split_bf16x2(b.z, b.w, h[3], lo[3]);
+      qh[ks] = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+      ql[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
     }
   }
   // softmax state of this lane's 4 rows (rows 4 lq + e of the wave's 16)
@@ -866,16 +873,16 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
   for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const KVT* Kg = Kc + (size_t)g * max_pos * D;
   const KVT* Vg = Vc + (size_t)g * max_pos * D;
-  // staging map: positions 4 p4 .. + 3, dims 4 c4 .. + 3
-  const int p4 = tid & 7, c4 = tid >> 3;
+  // staging map: positions PPT p4 .. + PPT - 1, dims 4 c4 .. + 3
+  const int p4 = tid % PG, c4 = tid / PG;
 
   // a tile's K and V rows are requested while the previous tile is computed
-  f32x4 kr[4], vr[4];
+  f32x4 kr[PPT], vr[PPT];
   auto load_tile = [&](int k0) {
     const int nk = min(BK, k_end - k0);
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int p = 4 * p4 + pp;
+    for (int pp = 0; pp < PPT; ++pp) {
+      const int p = PPT * p4 + pp;
       kr[pp] = vr[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (p < nk) {
         kr[pp] = ld_kv4(Kg + (size_t)(k0 + p) * D + 4 * c4);
@@ -888,28 +895,25 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
     const int nk = min(BK, k_end - k0);
     __syncthreads();  // the previous tile's K, V and P are consumed
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const float x[4] = {kr[pp].x, kr[pp].y, kr[pp].z, kr[pp].w};
-      uint32_t h[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[i] = bf16_rne(x[i]);
-        lo[i] = bf16_rne(x[i] - __uint_as_float(h[i] << 16));
-      }
-      *reinterpret_cast<u32x2*>(&Kh[(4 * p4 + pp) * KS + 4 * c4]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *reinterpret_cast<u32x2*>(&Kl[(4 * p4 + pp) * KS + 4 * c4]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    for (int pp = 0; pp < PPT; ++pp) {
+      uint32_t h[2], lo[2];
+      split_bf16x2(kr[pp].x, kr[pp].y, h[0], lo[0]);
+      split_bf16x2(kr[pp].z, kr[pp].w, h[1], lo[1]);
+      *reinterpret_cast<u32x2*>(&Kh[(PPT * p4 + pp) * KS + 4 * c4]) = u32x2{h[0], h[1]};
+      *reinterpret_cast<u32x2*>(&Kl[(PPT * p4 + pp) * KS + 4 * c4]) = u32x2{lo[0], lo[1]};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // dim 4 c4 + i: its 4 positions 4 p4 .. + 3, transposed
-      uint32_t h[4], lo[4];
+    for (int i = 0; i < 4; ++i) {  // dim 4 c4 + i: its PPT positions, transposed
+      uint32_t h[PPT / 2], lo[PPT / 2];
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const float x = vr[pp][i];
-        h[pp] = bf16_rne(x);
-        lo[pp] = bf16_rne(x - __uint_as_float(h[pp] << 16));
+      for (int pp = 0; pp < PPT; pp += 2) split_bf16x2(vr[pp][i], vr[pp + 1][i], h[pp / 2], lo[pp / 2]);
+      if constexpr (PPT == 4) {
+        *reinterpret_cast<u32x2*>(&Vth[(4 * c4 + i) * VS + 4 * p4]) = u32x2{h[0], h[1]};
+        *reinterpret_cast<u32x2*>(&Vtl[(4 * c4 + i) * VS + 4 * p4]) = u32x2{lo[0], lo[1]};
+      } else {
+        *reinterpret_cast<uint32_t*>(&Vth[(4 * c4 + i) * VS + PPT * p4]) = h[0];
+        *reinterpret_cast<uint32_t*>(&Vtl[(4 * c4 + i) * VS + PPT * p4]) = lo[0];
       }
-      *reinterpret_cast<u32x2*>(&Vth[(4 * c4 + i) * VS + 4 * p4]) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *reinterpret_cast<u32x2*>(&Vtl[(4 * c4 + i) * VS + 4 * p4]) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     }
     if (k0 + BK < k_end) load_tile(k0 + BK);  // (kr, vr are staged: free)
     __syncthreads();
@@ -928,27 +932,41 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
         sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kh, sc[nt], 0, 0, 0);
       }
     }
-    // online softmax; element e of sc[nt] is row 4 lq + e, position nt * 16 + lr
+    // online softmax in base 2 (the scores carry log2 e); element e of
+    // sc[nt] is row 4 lq + e, position nt * 16 + lr.  Masks only on a tile
+    // that reaches past the block's first query position or the range end.
+    const bool edge = nk < BK || k0 + BK - 1 > pos0 + t0;
+    float cs[4];
+    bool moved = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float s0 = sc[0][e], s1 = sc[1][e];
-      if (!live[e] || lr >= nk || k0 + lr > qpos[e]) s0 = -INFINITY;
-      if (!live[e] || 16 + lr >= nk || k0 + 16 + lr > qpos[e]) s1 = -INFINITY;
+      if (edge) {
+        if (!live[e] || lr >= nk || k0 + lr > qpos[e]) s0 = -INFINITY;
+        if (!live[e] || 16 + lr >= nk || k0 + 16 + lr > qpos[e]) s1 = -INFINITY;
+      }
       const float mn = fmaxf(m[e], group_max<16>(fmaxf(s0, s1)));
       const float mref = mn == -INFINITY ? 0.f : mn;  // a row with nothing visible yet
-      const float e0 = __expf(s0 - mref), e1 = __expf(s1 - mref);
-      const float c = __expf(m[e] - mref);
+      const float e0 = __builtin_amdgcn_exp2f(s0 - mref), e1 = __builtin_amdgcn_exp2f(s1 - mref);
+      const float c = __builtin_amdgcn_exp2f(m[e] - mref);
       l[e] = l[e] * c + group_sum<16>(e0 + e1);
+      moved |= mn != m[e];
       m[e] = mn;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) oacc[dt][e] *= c;
-      const uint32_t h0 = bf16_rne(e0), h1 = bf16_rne(e1);
+      cs[e] = c;
+      uint32_t h, lo;  // (e0 in the low halves, e1 in the high)
+      split_bf16x2(e0, e1, h, lo);
       uint16_t* ph = &Ph[wave][(4 * lq + e) * PS];
       uint16_t* pl = &Pl[wave][(4 * lq + e) * PS];
-      ph[lr] = (uint16_t)h0;
-      ph[16 + lr] = (uint16_t)h1;
-      pl[lr] = (uint16_t)bf16_rne(e0 - __uint_as_float(h0 << 16));
-      pl[16 + lr] = (uint16_t)bf16_rne(e1 - __uint_as_float(h1 << 16));
+      ph[lr] = (uint16_t)h;
+      ph[16 + lr] = (uint16_t)(h >> 16);
+      pl[lr] = (uint16_t)lo;
+      pl[16 + lr] = (uint16_t)(lo >> 16);
+    }
+    if (__any(moved)) {  // some row maximum of the wave moved: rescale (c = 1 elsewhere)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) oacc[dt][e] *= cs[e];
     }
     __syncthreads();  // P written (each wave reads back only its own slice)
     // O += P V: A = P (16 queries x 32 positions), B = V^T fragments of 8 dim tiles
@@ -972,7 +990,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* __restri
       if (r < nrows) {
         float* dst = part + ((size_t)(t0 + r) * nq + g * G + j) * S * (D + 2) + (size_t)sp * (D + 2);
         if (lr == 0) {
-          dst[0] = m[e];
+          dst[0] = m[e] * 0.693147180559945309f;  // back to natural-log units for the merge
           dst[1] = l[e];
         }
 #pragma unroll
@@ -1063,15 +1081,25 @@ void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int 
     hipLaunchKernelGGL(k_attn_merge_rows, dim3((total + 255) / 256), dim3(256), 0, s, part, S, total, o_out, oh, ol);
     return;
   }
-  const dim3 grid(nkv, (T + 64 / G - 1) / (64 / G));
-#define QD_ATTN_PREFILL(G_)                                                                                        \
+  // long batches: 8 waves (128 query vectors) per block while that still
+  // leaves two blocks per CU, halving the K/V tiles staged per query
+  const bool wide = nkv * ((T + 128 / G - 1) / (128 / G)) >= 2 * ncu;
+  const int qv = wide ? 128 : 64;
+  const dim3 grid(nkv, (T + qv / G - 1) / (qv / G)), block(wide ? 512 : 256);
+#define QD_ATTN_PREFILL_NW(G_, NW_)                                                                                \
   if (kv_bf16)                                                                                                     \
-    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, uint16_t, false>), grid, dim3(256), 0, s, q, T, nq,               \
+    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, uint16_t, false, NW_>), grid, block, 0, s, q, T, nq,              \
                        (const uint16_t*)Kc, (const uint16_t*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr,     \
                        oh, ol);                                                                                     \
   else                                                                                                             \
-    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, float, false>), grid, dim3(256), 0, s, q, T, nq, (const float*)Kc, \
-                       (const float*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr, oh, ol)
+    hipLaunchKernelGGL((k_attn_prefill_mfma<G_, float, false, NW_>), grid, block, 0, s, q, T, nq,                 \
+                       (const float*)Kc, (const float*)Vc, max_pos, st, scale, o_out, ldo, 1, 0, nullptr, oh, ol)
+#define QD_ATTN_PREFILL(G_)             \
+  if (wide) {                           \
+    QD_ATTN_PREFILL_NW(G_, 8);          \
+  } else {                              \
+    QD_ATTN_PREFILL_NW(G_, 4);          \
+  }
   switch (G) {
     case 1: QD_ATTN_PREFILL(1); break;
     case 2: QD_ATTN_PREFILL(2); break;
@@ -1080,7 +1108,7 @@ void launch_attention_prefill(hipStream_t s, const float* q, int T, int nq, int 
     default: break;  // rejected by the host before any launch
   }
 #undef QD_ATTN_PREFILL
-  (void)ncu;
+#undef QD_ATTN_PREFILL_NW
 }
 
 void launch_attention_rows_split_only(hipStream_t s, const float* q, int T, int nq, int nkv, const void* Kc,

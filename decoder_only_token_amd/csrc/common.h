@@ -17,6 +17,18 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two f32 -> their bf16 patterns packed (a in the low half), round to
+// nearest even; gfx950 does this in one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)a, (__bf16)b});
+}
+// hi/lo split of a pair: h = rne(x), l = rne(x - h), packed as above.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& h, uint32_t& l) {
+  h = bf16x2_rne(a, b);
+  l = bf16x2_rne(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+}
+
 // bf16 bit pattern -> float (exact)
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
