@@ -858,9 +858,27 @@ __global__ __launch_bounds__(256) void k_lora_down_rows(const uint16_t* __restri
   }
 }
 
-// sum_i B[i] u[i] over an adapter row of r bf16 values, in index order
+// sum_i B[i] u[i] over an adapter row of r bf16 values, in index order.
+// Ranks that are multiples of 8 read B in 16-byte and u in 16-byte pieces
+// (rows start at multiples of r elements of 16-byte aligned buffers; the
+// same fused multiply-adds in the same order).
 __device__ __forceinline__ float lora_dot(const uint16_t* __restrict__ B, const float* __restrict__ u, int r) {
   float a = 0.f;
+  if ((r & 7) == 0) {
+    for (int i = 0; i < r; i += 8) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(B + i);
+      const f32x4 u0 = *reinterpret_cast<const f32x4*>(u + i), u1 = *reinterpret_cast<const f32x4*>(u + i + 4);
+      a = fmaf(bf16_lo(w.x), u0.x, a);
+      a = fmaf(bf16_hi(w.x), u0.y, a);
+      a = fmaf(bf16_lo(w.y), u0.z, a);
+      a = fmaf(bf16_hi(w.y), u0.w, a);
+      a = fmaf(bf16_lo(w.z), u1.x, a);
+      a = fmaf(bf16_hi(w.z), u1.y, a);
+      a = fmaf(bf16_lo(w.w), u1.z, a);
+      a = fmaf(bf16_hi(w.w), u1.w, a);
+    }
+    return a;
+  }
   for (int i = 0; i < r; ++i) a = fmaf(bf16_to_f(B[i]), u[i], a);
   return a;
 }
