@@ -190,3 +190,27 @@ def test_graph_attention_g8_several_tiles_per_split(torch_cuda, kv, rank):
     recs = lockstep_greedy(dec, oracle, prompt, 10, log=log)
     assert_records(recs, max_forced=1)
     dec.close()
+
+
+@pytest.mark.parametrize("nq", [32, 64])
+def test_graph_prefill_eight_wave_attention(torch_cuda, nq):
+    """16 kv heads with 2 or 4 q heads each: a 2100-row batched prefill gives
+    at least two 128-query blocks per CU, so the batch attention runs its
+    8-wave form (the last query tile ragged: 2100 = 32 x 65 + 20 rows at
+    G = 2, 16 x 131 + 4 at G = 4); then 4 graph decode steps, every logit
+    checked against the oracle."""
+    import decoder_only_token_amd as qd
+    shape = dataclasses.replace(synth.TINY, name=f"tiny-{nq}q-16kv", n_q_heads=nq, n_kv_heads=16, max_pos=2112)
+    log(f"8-wave batch attention, nq={nq}, nkv=16, 2100-row prefill")
+    w = synth.make_weights(shape, seed=51, random_gains=True)
+    oracle = OracleModel(shape, w)
+    cfg = qd.make_config(shape, max_prefill=2112, decode_path=PATHS["graph"])
+    dec = qd.Decoder(cfg, torch_cuda.cuda.current_stream().cuda_stream)
+    dw = to_device(w)
+    torch_cuda.cuda.synchronize()
+    dec.load_weights(dw)
+    del dw
+    prompt = synth.make_prompt(shape.vocab, 2100, seed=52)
+    recs = lockstep_greedy(dec, oracle, prompt, 4, log=log)
+    assert_records(recs, max_forced=1)
+    dec.close()
