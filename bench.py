@@ -408,11 +408,12 @@ def job_kv_bf16(wl, stream, dw, dl, steps=20, warmup=5):
 
 def cpu_baseline(wl, dw, dl, ctx):
     """The float64 oracle on a bounded sample of the timed step: one decode
-    token at context `ctx`, on the model cut to 1 and to 2 layers (its KV cache
+    token at context `ctx`, on the model cut to 1 and to 4 layers (its KV cache
     filled with seeded random keys and values for ctx - 1 positions: the
     arithmetic does not depend on their values), plus the tied head; the
-    36-layer time is t(1) + 35 (t(2) - t(1)).  Timed with all host threads and
-    with one thread."""
+    36-layer time is t(1) + 35 (t(4) - t(1)) / 3 (three layers' difference, so
+    that timing noise on the head does not swamp one layer's time).  Timed
+    with all host threads and with one thread."""
     import dataclasses
     import numpy as np
     import synth
@@ -422,13 +423,13 @@ def cpu_baseline(wl, dw, dl, ctx):
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     shape = wl.shape
-    host = synth.device_to_host(dw, layers=[0, 1])
+    host = synth.device_to_host(dw, layers=[0, 1, 2, 3])
     lora = None
     if dl is not None:
-        lora = [{k: v.cpu().numpy().view(np.uint16) for k, v in dl[i].items()} for i in (0, 1)]
+        lora = [{k: v.cpu().numpy().view(np.uint16) for k, v in dl[i].items()} for i in range(4)]
     t_build = time.perf_counter()
     models = {}
-    for nl in (1, 2):
+    for nl in (1, 4):
         s = dataclasses.replace(shape, n_layers=nl)
         sub = {"embed": host["embed"], "final_norm": host["final_norm"], "layers": host["layers"][:nl]}
         models[nl] = OracleModel(s, sub, lora=lora[:nl] if lora else None, lora_alpha=wl.lora_alpha)
@@ -447,11 +448,11 @@ def cpu_baseline(wl, dw, dl, ctx):
 
     def estimate(reps):
         t1 = min(one_token(models[1]) for _ in range(reps))
-        t2 = min(one_token(models[2]) for _ in range(reps))
-        return t1 + (shape.n_layers - 1) * max(t2 - t1, 0.0), t1, t2
+        t4 = min(one_token(models[4]) for _ in range(reps))
+        return t1 + (shape.n_layers - 1) * max(t4 - t1, 0.0) / 3, t1, t4
 
     cores = len(os.sched_getaffinity(0))
-    t_all, t1, t2 = estimate(3)
+    t_all, t1, t4 = estimate(3)
     t_one = None
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
@@ -460,8 +461,9 @@ def cpu_baseline(wl, dw, dl, ctx):
             "cpu_model": cpu_model(),
             "one_thread_tok_s": round(1.0 / t_one, 5) if t_one else None,
             "sample": f"{wl.name}: float64 numpy oracle, one decode token at context {ctx} on the model cut to "
-                      f"1 and 2 layers (KV cache filled with seeded random values), 36-layer time = t1 + 35 (t2 - t1) "
-                      f"= {t_all:.3f} s (t1 {t1:.3f} s, t2 {t2:.3f} s, best of 3; weight widening {t_build:.1f} s "
+                      f"1 and 4 layers (KV cache filled with seeded random values), 36-layer time = "
+                      f"t1 + 35 (t4 - t1) / 3 = {t_all:.3f} s (t1 {t1:.3f} s, t4 {t4:.3f} s, best of 3; weight "
+                      f"widening {t_build:.1f} s "
                       f"not counted); {cores} host threads"}
 
 
